@@ -1,0 +1,16 @@
+"""Float64 CPU oracle for the GQA decode step -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The product path (the HIP library and its Python binding)
+never imports or calls it, and it imports nothing from them.
+"""
+from .oracle import (  # noqa: F401
+    append,
+    attend,
+    attend_one,
+    decode,
+    kv_index,
+    kv_rows,
+    softmax_weights,
+    step,
+)

@@ -1,0 +1,140 @@
+"""Seeded synthetic inputs for the GQA decode step.
+
+Shared by the tests, the smoke check and the benchmark, and fed identically to
+the HIP library and to the float64 oracle.  This module holds no attention
+arithmetic: it only draws random numbers, casts them to the storage type and
+writes the stale-slot filler.
+
+The five workloads follow the shapes, distributions and length mixes given for
+this decode step (tiny, Llama-3-8B-like layer, ragged batch, long context,
+large group).  ``lengths`` is always the number of tokens held *before* the
+step's append (the step writes the new key/value at slot ``lengths[b]`` and
+then attends ``lengths[b] + 1`` slots); slots ``>= lengths[b]`` start out
+holding the workload's stale filler, or the plain random draw where none is
+given.
+
+Draw order (one ``torch.Generator`` seeded with the workload's seed, on the
+device the tensors are made on): q, K cache, V cache, new K, new V, stale
+signs.  ``lengths`` comes from a CPU generator with the same seed so it does not
+depend on the device.  fp32 draws are rounded to bf16 to nearest-even by
+``Tensor.to``.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    seed: int
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    capacity: int
+    layout: str            # "BHSD" = (B, Hkv, S, D); "BSHD" = (B, S, Hkv, D)
+    kv_dtype: str          # "f32" | "bf16"
+    qo_dtype: str          # "f32" | "bf16"
+    len_lo: int            # pre-append length range, inclusive
+    len_hi: int
+    key_scale: float = 1.0
+    stale: str = "none"    # "none" | "const:<v>" | "pm:<v>" (random sign)
+    note: str = field(default="", compare=False)
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("tiny", 1, B=2, Hq=4, Hkv=2, D=4, capacity=8, layout="BHSD", kv_dtype="f32", qo_dtype="f32",
+                 len_lo=1, len_hi=7, stale="const:1000",
+                 note="B=2 Hq=4 Hkv=2 D=4 cap=8 fp32, lengths U[1,7], stale 1e3"),
+        Workload("llama3_8b_layer", 2, B=32, Hq=32, Hkv=8, D=128, capacity=4097, layout="BHSD", kv_dtype="bf16",
+                 qo_dtype="bf16", len_lo=4096, len_hi=4096,
+                 note="B=32 Hq=32 Hkv=8 D=128, 4096 cached + 1 new, bf16"),
+        Workload("ragged_batch", 3, B=64, Hq=64, Hkv=8, D=128, capacity=8192, layout="BSHD", kv_dtype="bf16",
+                 qo_dtype="bf16", len_lo=0, len_hi=8191, stale="pm:10000",
+                 note="B=64 Hq=64 Hkv=8 D=128 cap=8192 (B,S,Hkv,D), attended counts U[1,8192], stale +-1e4"),
+        Workload("long_context", 4, B=4, Hq=32, Hkv=8, D=128, capacity=131073, layout="BHSD", kv_dtype="bf16",
+                 qo_dtype="bf16", len_lo=131072, len_hi=131072, key_scale=3.0,
+                 note="B=4 Hq=32 Hkv=8 D=128, 131072 cached + 1 new, keys x3"),
+        Workload("large_group", 5, B=128, Hq=64, Hkv=1, D=128, capacity=2048, layout="BHSD", kv_dtype="bf16",
+                 qo_dtype="bf16", len_lo=1023, len_hi=2047,
+                 note="B=128 Hq=64 Hkv=1 D=128 cap=2048, attended counts U[1024,2048]"),
+    ]
+}
+
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def cache_shape(w: Workload, capacity: int | None = None):
+    S = w.capacity if capacity is None else capacity
+    return (w.B, w.Hkv, S, w.D) if w.layout == "BHSD" else (w.B, S, w.Hkv, w.D)
+
+
+def draw_lengths(w: Workload) -> torch.Tensor:
+    g = torch.Generator().manual_seed(w.seed)
+    return torch.randint(w.len_lo, w.len_hi + 1, (w.B,), generator=g, dtype=torch.int64).to(torch.int32)
+
+
+def make_inputs(w: Workload, device="cpu", lengths: torch.Tensor | None = None) -> dict:
+    """Seeded inputs of workload ``w`` as torch tensors on ``device``.
+
+    Returns a dict with q (B,Hq,D), k_cache / v_cache (layout), k_new / v_new
+    (B,Hkv,D), lengths int32 (B,) (pre-append counts).
+    """
+    g = torch.Generator(device=device).manual_seed(w.seed)
+    L = draw_lengths(w) if lengths is None else lengths.to(torch.int32).cpu()
+    kvt, qot = TORCH_DTYPE[w.kv_dtype], TORCH_DTYPE[w.qo_dtype]
+
+    def randn(shape, scale=1.0):
+        x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        if scale != 1.0:
+            x.mul_(scale)
+        return x
+
+    q = randn((w.B, w.Hq, w.D)).to(qot)
+    k_cache = randn(cache_shape(w), w.key_scale).to(kvt)
+    v_cache = randn(cache_shape(w)).to(kvt)
+    k_new = randn((w.B, w.Hkv, w.D), w.key_scale).to(kvt)
+    v_new = randn((w.B, w.Hkv, w.D)).to(kvt)
+    if w.stale != "none":
+        kind, val = w.stale.split(":")
+        val = float(val)
+        S = w.capacity
+        slot = torch.arange(S, device=device)
+        stale = slot[None, :] >= L.to(device)[:, None].to(torch.int64)          # (B, S)
+        stale = stale[:, None, :, None] if w.layout == "BHSD" else stale[:, :, None, None]
+        for cache in (k_cache, v_cache):
+            if kind == "const":
+                fill = torch.full(cache.shape, val, device=device, dtype=torch.float32)
+            else:
+                sign = torch.randint(0, 2, cache.shape, generator=g, device=device, dtype=torch.int8)
+                fill = (sign.to(torch.float32) * 2 - 1) * val
+            cache.copy_(torch.where(stale, fill.to(kvt), cache))
+            del fill
+    return dict(q=q, k_cache=k_cache, v_cache=v_cache, k_new=k_new, v_new=v_new,
+                lengths=L.to(device))
+
+
+def to_numpy_storage(t: torch.Tensor) -> np.ndarray:
+    """A tensor's stored bits as the oracle takes them: float32, or uint16 bf16 patterns."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float32:
+        return t.numpy()
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def algorithmic_bytes(w: Workload, lengths) -> int:
+    """Bytes one step must move at minimum: valid K+V read (the new token
+    included), Q read, new K/V write, output write."""
+    e_kv = 4 if w.kv_dtype == "f32" else 2
+    e_qo = 4 if w.qo_dtype == "f32" else 2
+    n = np.asarray(lengths, dtype=np.int64) + 1
+    kv_read = int(n.sum()) * w.Hkv * w.D * 2 * e_kv
+    return kv_read + 2 * w.B * w.Hq * w.D * e_qo + 2 * w.B * w.Hkv * w.D * e_kv
