@@ -1,0 +1,190 @@
+"""Benchmark of the GQA decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one gqa_decode_step call (in-place append + length-masked GQA
+attention over every sequence of the batch, i.e. one layer's decode) on
+seeded synthetic inputs already resident in HBM.  W untimed steps, then K
+timed back-to-back on one stream between HIP events.  The cache tensors
+rotate over R copies so the bytes one rotation touches exceed the 256 MB
+Infinity Cache and every step reads K/V from HBM.
+
+Prints ONE JSON line: value = achieved HBM GB/s over the algorithmic bytes
+(valid K+V read incl. the new token, Q read, new K/V write, output write),
+plus steps/s, the fraction of the 8 TB/s peak, and the float64 oracle timed on
+this host's cores over a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+METRIC = "achieved HBM GB/s (% of MI355X peak) + decode steps/sec per config"
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["gqa_decode_attention_amd/csrc/kernels_mfma.hip", "gqa_decode_attention_amd/csrc/kernels_generic.hip",
+                  "gqa_decode_attention_amd/csrc/device_common.h", "gqa_decode_attention_amd/csrc/gqa_decode.cpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the kernels as they are now; otherwise None."""
+    path = os.path.join(PROFILES, f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, inp, budget_s=15.0):
+    """The float64 oracle on this host's cores, on a bounded sample: whole
+    sequences of the same inputs, as many as fit in about budget_s seconds."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    L = inp["lengths"].cpu().numpy()
+
+    def run(bs):
+        sl = slice(bs[0], bs[1])
+        q = W.to_numpy_storage(inp["q"][sl])
+        kc = W.to_numpy_storage(inp["k_cache"][sl])
+        vc = W.to_numpy_storage(inp["v_cache"][sl])
+        kn = W.to_numpy_storage(inp["k_new"][sl])
+        vn = W.to_numpy_storage(inp["v_new"][sl])
+        t0 = time.perf_counter()
+        oracle.step(q, w.qo_dtype, kc, vc, kn, vn, w.kv_dtype, L[sl], w.layout, w.Hq, w.Hkv)
+        return time.perf_counter() - t0
+
+    t1 = run((0, 1))
+    nb = int(max(1, min(w.B, budget_s / max(t1, 1e-6))))
+    if w.name == "tiny":
+        reps = max(1, int(budget_s / 10 / max(t1, 1e-6)))
+        t = sum(run((0, w.B)) for _ in range(min(reps, 1000)))
+        nbytes = W.algorithmic_bytes(w, L) * min(reps, 1000)
+        sample = f"{min(reps, 1000)} whole steps"
+    else:
+        t = run((0, nb)) if nb > 1 else t1
+        sub = W.Workload(**{**w.__dict__, "B": nb})
+        nbytes = W.algorithmic_bytes(sub, L[:nb])
+        sample = f"oracle.step over sequences 0..{nb - 1} of {w.B} (all {w.Hq} query heads), same inputs"
+    gbs = nbytes / t / 1e9
+    return {"value": round(gbs, 6), "unit": "GB/s", "cores": threads, "kind": "oracle", "sample": sample,
+            "seconds": round(t, 3), "steps_per_sec_equiv": round(gbs * 1e9 / W.algorithmic_bytes(w, L), 6),
+            "host_cpus": os.cpu_count(), "affinity": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama3_8b_layer")
+    ap.add_argument("--num-splits", type=int, default=0, help="0 = the library's plan")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gqa_decode_attention_amd as g
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    g.lib()
+    w = W.WORKLOADS[args.workload]
+    dev = "cuda"
+    inp = W.make_inputs(w, dev)
+    L = inp["lengths"].cpu().numpy()
+    nbytes = W.algorithmic_bytes(w, L)
+    kv_bytes = 2 * inp["k_cache"].numel() * inp["k_cache"].element_size()
+    R = max(1, math.ceil(3 * MALL_BYTES / kv_bytes))
+    caches = [(inp["k_cache"], inp["v_cache"])] + [(inp["k_cache"].clone(), inp["v_cache"].clone())
+                                                    for _ in range(R - 1)]
+    desc = g.desc_for(inp["q"], inp["k_cache"], w.layout, args.num_splits)
+    plan = g.get_plan(desc)
+    ws = torch.empty(max(plan["workspace_bytes"], 1), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(inp["q"])
+
+    def step(i):
+        kc, vc = caches[i % R]
+        g.step(inp["q"], kc, vc, inp["k_new"], inp["v_new"], inp["lengths"], layout=w.layout, out=out,
+               workspace=ws, num_splits=args.num_splits)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, inp)
+
+    kv = "bf16" if w.kv_dtype == "bf16" else "f32"
+    line = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "storage_dtype": kv,
+        "data": "synthetic",
+        "steps_per_sec": round(1000.0 / ms, 2),
+        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "config": {"workload": w.name, "batch": w.B, "num_q_heads": w.Hq, "num_kv_heads": w.Hkv, "head_dim": w.D,
+                   "capacity": w.capacity, "layout": w.layout, "kv_dtype": w.kv_dtype, "qo_dtype": w.qo_dtype,
+                   "tokens_attended": int((L + 1).sum()), "algorithmic_bytes_per_step": nbytes,
+                   "cache_rotation": R, "plan": plan},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(w.name),
+                     "per": "one gqa_decode_step call (attention kernel + split combine), HIP events over the "
+                            "timed region"},
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 4),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

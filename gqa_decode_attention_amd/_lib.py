@@ -1,0 +1,208 @@
+"""ctypes binding of libgqa_decode.so (the C ABI declared in include/gqa_decode.h).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+library.  torch tensors supply device memory and the current HIP stream.  If
+the library is not built, every call raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa_decode.so")
+
+GQA_OK = 0
+STATUS_NAMES = {
+    0: "GQA_OK",
+    1: "GQA_ERR_INVALID_ARGUMENT",
+    2: "GQA_ERR_UNSUPPORTED",
+    3: "GQA_ERR_WORKSPACE_TOO_SMALL",
+    4: "GQA_ERR_HIP",
+    5: "GQA_ERR_INTERNAL",
+}
+F32, BF16 = 0, 1
+LAYOUTS = {"BHSD": 0, "BSHD": 1}
+KERNEL_NAMES = {0: "generic", 1: "mfma_qk", 2: "mfma_all"}
+
+
+class GqaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS_NAMES.get(status, status)}")
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("capacity", ctypes.c_int32),
+        ("layout", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("qo_dtype", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32),
+    ]
+
+
+class PlanT(ctypes.Structure):
+    _fields_ = [
+        ("kernel", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32),
+        ("split_tokens", ctypes.c_int32),
+        ("grid", ctypes.c_int32),
+        ("block", ctypes.c_int32),
+        ("combine", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+EXPORTS = (
+    "gqa_decode_workspace_size",
+    "gqa_decode_get_plan",
+    "gqa_decode_append",
+    "gqa_decode_attend",
+    "gqa_decode_step",
+    "gqa_decode_status_string",
+    "gqa_decode_version",
+)
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m gqa_decode_attention_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, S, I32P = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p
+    DP = ctypes.POINTER(Desc)
+    L.gqa_decode_workspace_size.argtypes = [DP, ctypes.POINTER(ctypes.c_size_t)]
+    L.gqa_decode_get_plan.argtypes = [DP, ctypes.POINTER(PlanT)]
+    L.gqa_decode_append.argtypes = [DP, P, P, P, P, I32P, P]
+    L.gqa_decode_attend.argtypes = [DP, P, P, P, I32P, P, P, S, P]
+    L.gqa_decode_step.argtypes = [DP, P, P, P, P, P, I32P, P, P, S, P]
+    for name in ("gqa_decode_workspace_size", "gqa_decode_get_plan", "gqa_decode_append", "gqa_decode_attend",
+                 "gqa_decode_step"):
+        getattr(L, name).restype = ctypes.c_int
+    L.gqa_decode_status_string.argtypes = [ctypes.c_int]
+    L.gqa_decode_status_string.restype = ctypes.c_char_p
+    L.gqa_decode_version.argtypes = []
+    L.gqa_decode_version.restype = ctypes.c_int32
+    _lib = L
+    return L
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return F32
+    if t == torch.bfloat16:
+        return BF16
+    raise ValueError(f"unsupported dtype {t}; float32 or bfloat16")
+
+
+def make_desc(batch, num_q_heads, num_kv_heads, head_dim, capacity, layout="BHSD", kv_dtype=BF16, qo_dtype=BF16,
+              num_splits=0) -> Desc:
+    return Desc(batch, num_q_heads, num_kv_heads, head_dim, capacity, LAYOUTS[layout], kv_dtype, qo_dtype,
+                num_splits)
+
+
+def desc_for(q: torch.Tensor, k_cache: torch.Tensor, layout: str, num_splits: int = 0) -> Desc:
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {list(LAYOUTS)}")
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q is (B, Hq, D); caches are 4-D")
+    B, Hq, D = q.shape
+    if layout == "BHSD":
+        Bc, Hkv, S, Dc = k_cache.shape
+    else:
+        Bc, S, Hkv, Dc = k_cache.shape
+    if Bc != B or Dc != D:
+        raise ValueError("q and cache disagree on batch or head_dim")
+    return make_desc(B, Hq, Hkv, D, S, layout, _dtype_code(k_cache.dtype), _dtype_code(q.dtype), num_splits)
+
+
+def check(status: int, what: str) -> None:
+    if status != GQA_OK:
+        raise GqaError(status, what)
+
+
+def workspace_size(desc: Desc) -> int:
+    n = ctypes.c_size_t(0)
+    check(lib().gqa_decode_workspace_size(ctypes.byref(desc), ctypes.byref(n)), "gqa_decode_workspace_size")
+    return n.value
+
+
+def get_plan(desc: Desc) -> dict:
+    p = PlanT()
+    check(lib().gqa_decode_get_plan(ctypes.byref(desc), ctypes.byref(p)), "gqa_decode_get_plan")
+    return dict(kernel=KERNEL_NAMES.get(p.kernel, p.kernel), num_splits=p.num_splits, split_tokens=p.split_tokens,
+                grid=p.grid, block=p.block, combine=bool(p.combine), workspace_bytes=p.workspace_bytes)
+
+
+def _dev(tensors, lengths):
+    dev = tensors[0].device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    for t in tensors:
+        if t.device != dev:
+            raise ValueError("all tensors must be on one device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    if lengths.dtype != torch.int32 or lengths.device != dev or not lengths.is_contiguous():
+        raise ValueError("lengths must be a contiguous int32 tensor on the same device")
+    return dev
+
+
+def _stream(dev) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _workspace(desc: Desc, dev, workspace):
+    need = workspace_size(desc)
+    if need == 0:
+        return workspace, None, 0
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    return workspace, workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def append(k_cache, v_cache, k_new, v_new, lengths, *, layout="BHSD"):
+    """In-place append of k_new/v_new (B, Hkv, D) at slot lengths[b] of the caches."""
+    dev = _dev([k_cache, v_cache, k_new, v_new], lengths)
+    B, Hkv, D = k_new.shape
+    S = k_cache.shape[2] if layout == "BHSD" else k_cache.shape[1]
+    desc = make_desc(B, Hkv, Hkv, D, S, layout, _dtype_code(k_cache.dtype), _dtype_code(k_cache.dtype))
+    check(lib().gqa_decode_append(ctypes.byref(desc), k_cache.data_ptr(), v_cache.data_ptr(), k_new.data_ptr(),
+                                  v_new.data_ptr(), lengths.data_ptr(), _stream(dev)), "gqa_decode_append")
+
+
+def attend(q, k_cache, v_cache, lengths, *, layout="BHSD", out=None, workspace=None, num_splits=0):
+    """Read-only length-masked GQA attention; lengths[b] = valid slots. Returns out (B, Hq, D)."""
+    dev = _dev([q, k_cache, v_cache], lengths)
+    desc = desc_for(q, k_cache, layout, num_splits)
+    if out is None:
+        out = torch.empty_like(q)
+    workspace, wptr, wbytes = _workspace(desc, dev, workspace)
+    check(lib().gqa_decode_attend(ctypes.byref(desc), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                  lengths.data_ptr(), out.data_ptr(), wptr, wbytes, _stream(dev)),
+          "gqa_decode_attend")
+    return out
+
+
+def step(q, k_cache, v_cache, k_new, v_new, lengths, *, layout="BHSD", out=None, workspace=None, num_splits=0):
+    """Fused decode step: append at lengths[b], then attend lengths[b] + 1 slots. Returns out."""
+    dev = _dev([q, k_cache, v_cache, k_new, v_new], lengths)
+    desc = desc_for(q, k_cache, layout, num_splits)
+    if out is None:
+        out = torch.empty_like(q)
+    workspace, wptr, wbytes = _workspace(desc, dev, workspace)
+    check(lib().gqa_decode_step(ctypes.byref(desc), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                k_new.data_ptr(), v_new.data_ptr(), lengths.data_ptr(), out.data_ptr(), wptr, wbytes,
+                                _stream(dev)), "gqa_decode_step")
+    return out

@@ -1,0 +1,363 @@
+// C ABI of the GQA decode step: argument validation, planning and launch.
+//
+// Every condition the host can check is checked before the first HIP call,
+// so an error return means nothing was enqueued (CLIKA groupQueryAttention
+// page: validate the whole input before any read, refuse with
+// INVALID_ARGUMENT; CANN aclnnMlaPrologV3WeightNz page: the first phase
+// verifies parameters and reports the workspace size).  The plan -- kernel,
+// split of the token axis, grid, workspace -- is a pure function of the
+// descriptor: `lengths` stays on the device and is never read here.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "gqa_decode.h"
+#include "internal.h"
+
+using namespace gqa;
+
+namespace {
+
+constexpr int32_t kVersion = 100;  // 0.1.0
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int elem_bytes(int32_t dt) { return dt == GQA_F32 ? 4 : 2; }
+
+// Checked product of non-negative factors; false on overflow past 2^62.
+bool mul_ok(int64_t a, int64_t b, int64_t* r) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > ((int64_t)1 << 62) / a) return false;
+  *r = a * b;
+  return true;
+}
+
+gqa_status_t check_desc(const gqa_decode_desc_t* d) {
+  if (d == nullptr) return GQA_ERR_INVALID_ARGUMENT;
+  if (d->batch < 0 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->head_dim < 1 || d->capacity < 1)
+    return GQA_ERR_INVALID_ARGUMENT;
+  if (d->num_q_heads % d->num_kv_heads != 0) return GQA_ERR_INVALID_ARGUMENT;
+  if (d->layout != GQA_LAYOUT_BHSD && d->layout != GQA_LAYOUT_BSHD) return GQA_ERR_INVALID_ARGUMENT;
+  if ((d->kv_dtype != GQA_F32 && d->kv_dtype != GQA_BF16) || (d->qo_dtype != GQA_F32 && d->qo_dtype != GQA_BF16))
+    return GQA_ERR_INVALID_ARGUMENT;
+  if (d->num_splits < 0) return GQA_ERR_INVALID_ARGUMENT;
+  if (d->head_dim > 256) return GQA_ERR_UNSUPPORTED;
+  // Sizes must be addressable with 64-bit element offsets and the grids with 32-bit counts.
+  int64_t t;
+  if (!mul_ok(d->batch, d->num_kv_heads, &t) || !mul_ok(t, d->capacity, &t) || !mul_ok(t, d->head_dim, &t) ||
+      !mul_ok(t, 4, &t))
+    return GQA_ERR_UNSUPPORTED;
+  if (!mul_ok(d->batch, d->num_q_heads, &t) || t > INT32_MAX) return GQA_ERR_UNSUPPORTED;
+  return GQA_OK;
+}
+
+// Which attention kernel serves the descriptor (pointer alignment is checked
+// separately: a misaligned call of a fast-path descriptor is refused).
+int32_t choose_kernel(const gqa_decode_desc_t* d) {
+  const int32_t G = d->num_q_heads / d->num_kv_heads;
+  const bool bf16 = d->kv_dtype == GQA_BF16 && d->qo_dtype == GQA_BF16;
+  if (bf16 && d->head_dim == 128 && G <= 16 && kHaveMfmaQk) return GQA_KERNEL_MFMA_QK;
+  if (bf16 && d->head_dim == 128 && G > 16 && kHaveMfmaAll) return GQA_KERNEL_MFMA_ALL;
+  return GQA_KERNEL_GENERIC;
+}
+
+// Plan: a pure function of the descriptor.
+gqa_status_t make_plan(const gqa_decode_desc_t* d, Plan* p) {
+  gqa_status_t st = check_desc(d);
+  if (st != GQA_OK) return st;
+  std::memset(p, 0, sizeof(*p));
+  const int64_t B = d->batch, Hq = d->num_q_heads, Hkv = d->num_kv_heads, S = d->capacity, D = d->head_dim;
+  const int64_t G = Hq / Hkv;
+  p->kernel = choose_kernel(d);
+  p->head_chunks = p->kernel == GQA_KERNEL_GENERIC ? (int32_t)((G + kGenericHeadChunk - 1) / kGenericHeadChunk) : 1;
+  p->block = kBlock;
+  const int64_t units = std::max<int64_t>(1, B * Hkv * p->head_chunks);
+  int64_t split_tokens;
+  if (d->num_splits > 0) {
+    const int64_t ns = std::min<int64_t>(d->num_splits, S);
+    split_tokens = (S + ns - 1) / ns;
+  } else {
+    // Enough workgroups to fill 256 CUs several times over, but never splits
+    // so short that the partials (D + 2 floats per head) cost a visible share
+    // of the K/V bytes.
+    const int64_t want = std::max<int64_t>(1, (2048 + units - 1) / units);
+    split_tokens = (S + want - 1) / want;
+    split_tokens = ((split_tokens + 63) / 64) * 64;
+    split_tokens = std::max<int64_t>(split_tokens, 256);
+  }
+  if (split_tokens >= S) split_tokens = S;
+  const int64_t nsplit = (S + split_tokens - 1) / split_tokens;
+  p->split_tokens = (int32_t)split_tokens;
+  p->nsplit = (int32_t)nsplit;
+  p->combine = nsplit > 1 ? 1 : 0;
+  int64_t grid;
+  if (!mul_ok(units, nsplit, &grid) || grid > INT32_MAX) return GQA_ERR_UNSUPPORTED;
+  p->grid = (int32_t)grid;
+  if (nsplit > 1) {
+    const size_t nparts = (size_t)B * Hq * nsplit;
+    p->off_m = align256(nparts * D * sizeof(float));
+    p->off_l = p->off_m + align256(nparts * sizeof(float));
+    p->workspace_bytes = p->off_l + align256(nparts * sizeof(float));
+  }
+  return GQA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Span {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+Span span(const void* p, size_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Span{lo, lo + bytes};
+}
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
+
+void fill_args(const gqa_decode_desc_t* d, const Plan& p, AttnArgs* a) {
+  std::memset(a, 0, sizeof(*a));
+  a->B = d->batch;
+  a->Hq = d->num_q_heads;
+  a->Hkv = d->num_kv_heads;
+  a->D = d->head_dim;
+  a->S = d->capacity;
+  a->G = d->num_q_heads / d->num_kv_heads;
+  const int64_t S = d->capacity, D = d->head_dim, Hkv = d->num_kv_heads;
+  if (d->layout == GQA_LAYOUT_BHSD) {
+    a->sb = Hkv * S * D;
+    a->sh = S * D;
+    a->st = D;
+  } else {
+    a->sb = S * Hkv * D;
+    a->sh = D;
+    a->st = Hkv * D;
+  }
+  a->nsplit = p.nsplit;
+  a->split_tokens = p.split_tokens;
+  a->head_chunks = p.head_chunks;
+  a->kv_dtype = d->kv_dtype;
+  a->qo_dtype = d->qo_dtype;
+  a->scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d->head_dim));
+}
+
+// Pointer checks shared by attend and step.  `k_new`/`v_new` are null for attend.
+gqa_status_t check_attend_ptrs(const gqa_decode_desc_t* d, const Plan& p, const void* q, const void* kc,
+                               const void* vc, const void* kn, const void* vn, const int32_t* lengths,
+                               const void* out, const void* ws, size_t ws_bytes, bool step) {
+  const size_t ekv = elem_bytes(d->kv_dtype), eqo = elem_bytes(d->qo_dtype);
+  if (!q || !kc || !vc || !lengths || !out) return GQA_ERR_INVALID_ARGUMENT;
+  if (step && (!kn || !vn)) return GQA_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, eqo) || !aligned(out, eqo) || !aligned(kc, ekv) || !aligned(vc, ekv) || !aligned(lengths, 4))
+    return GQA_ERR_INVALID_ARGUMENT;
+  if (step && (!aligned(kn, ekv) || !aligned(vn, ekv))) return GQA_ERR_INVALID_ARGUMENT;
+  if (p.kernel != GQA_KERNEL_GENERIC) {
+    // The matrix-core kernels read q, caches and new K/V with 16-byte loads.
+    if (!aligned(q, 16) || !aligned(kc, 16) || !aligned(vc, 16) || !aligned(out, 16)) return GQA_ERR_INVALID_ARGUMENT;
+    if (step && (!aligned(kn, 16) || !aligned(vn, 16))) return GQA_ERR_INVALID_ARGUMENT;
+  }
+  if (p.workspace_bytes > 0) {
+    if (ws_bytes < p.workspace_bytes) return GQA_ERR_WORKSPACE_TOO_SMALL;
+    if (!ws || !aligned(ws, 256)) return GQA_ERR_INVALID_ARGUMENT;
+  }
+  const size_t B = d->batch, Hq = d->num_q_heads, Hkv = d->num_kv_heads, S = d->capacity, D = d->head_dim;
+  const Span s_out = span(out, B * Hq * D * eqo);
+  const Span s_q = span(q, B * Hq * D * eqo);
+  const Span s_kc = span(kc, B * Hkv * S * D * ekv);
+  const Span s_vc = span(vc, B * Hkv * S * D * ekv);
+  const Span s_len = span(lengths, B * 4);
+  const Span s_ws = span(ws, p.workspace_bytes);
+  if (overlap(s_out, s_q) || overlap(s_out, s_kc) || overlap(s_out, s_vc) || overlap(s_out, s_len) ||
+      (p.workspace_bytes > 0 && (overlap(s_out, s_ws) || overlap(s_ws, s_q) || overlap(s_ws, s_kc) ||
+                                 overlap(s_ws, s_vc) || overlap(s_ws, s_len))))
+    return GQA_ERR_INVALID_ARGUMENT;
+  if (step) {
+    const Span s_kn = span(kn, B * Hkv * D * ekv), s_vn = span(vn, B * Hkv * D * ekv);
+    if (overlap(s_kc, s_vc) || overlap(s_kn, s_kc) || overlap(s_kn, s_vc) || overlap(s_vn, s_kc) ||
+        overlap(s_vn, s_vc) || overlap(s_out, s_kn) || overlap(s_out, s_vn) || overlap(s_len, s_kc) ||
+        overlap(s_len, s_vc) ||
+        (p.workspace_bytes > 0 && (overlap(s_ws, s_kn) || overlap(s_ws, s_vn))))
+      return GQA_ERR_INVALID_ARGUMENT;
+  }
+  return GQA_OK;
+}
+
+gqa_status_t run_attend(const gqa_decode_desc_t* d, const Plan& p, AttnArgs& a, hipStream_t s) {
+  hipError_t e;
+  switch (p.kernel) {
+    case GQA_KERNEL_MFMA_QK: e = launch_attend_mfma_qk(a, p, s); break;
+    case GQA_KERNEL_MFMA_ALL: e = launch_attend_mfma_all(a, p, s); break;
+    default: {
+      const size_t ekv = elem_bytes(d->kv_dtype);
+      const bool vec = (d->head_dim * ekv) % 16 == 0 && aligned(a.k_cache, 16) && aligned(a.v_cache, 16);
+      e = launch_attend_generic(a, p, vec ? 1 : 0, s);
+    }
+  }
+  if (e != hipSuccess) return GQA_ERR_HIP;
+  if (p.combine) {
+    e = launch_combine(a, p, s);
+    if (e != hipSuccess) return GQA_ERR_HIP;
+  }
+  return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gqa_status_t gqa_decode_workspace_size(const gqa_decode_desc_t* desc, size_t* bytes) {
+  try {
+    if (bytes == nullptr) return GQA_ERR_INVALID_ARGUMENT;
+    Plan p;
+    gqa_status_t st = make_plan(desc, &p);
+    if (st != GQA_OK) return st;
+    *bytes = p.workspace_bytes;
+    return GQA_OK;
+  } catch (...) {
+    return GQA_ERR_INTERNAL;
+  }
+}
+
+gqa_status_t gqa_decode_get_plan(const gqa_decode_desc_t* desc, gqa_decode_plan_t* plan) {
+  try {
+    if (plan == nullptr) return GQA_ERR_INVALID_ARGUMENT;
+    Plan p;
+    gqa_status_t st = make_plan(desc, &p);
+    if (st != GQA_OK) return st;
+    plan->kernel = p.kernel;
+    plan->num_splits = p.nsplit;
+    plan->split_tokens = p.split_tokens;
+    plan->grid = p.grid;
+    plan->block = p.block;
+    plan->combine = p.combine;
+    plan->workspace_bytes = p.workspace_bytes;
+    return GQA_OK;
+  } catch (...) {
+    return GQA_ERR_INTERNAL;
+  }
+}
+
+gqa_status_t gqa_decode_append(const gqa_decode_desc_t* desc, void* k_cache, void* v_cache, const void* k_new,
+                               const void* v_new, const int32_t* lengths, void* stream) {
+  try {
+    gqa_status_t st = check_desc(desc);
+    if (st != GQA_OK) return st;
+    if (desc->batch == 0) return GQA_OK;
+    if (!k_cache || !v_cache || !k_new || !v_new || !lengths) return GQA_ERR_INVALID_ARGUMENT;
+    const size_t e = elem_bytes(desc->kv_dtype);
+    if (!aligned(k_cache, e) || !aligned(v_cache, e) || !aligned(k_new, e) || !aligned(v_new, e) ||
+        !aligned(lengths, 4))
+      return GQA_ERR_INVALID_ARGUMENT;
+    const size_t B = desc->batch, Hkv = desc->num_kv_heads, S = desc->capacity, D = desc->head_dim;
+    const Span s_kc = span(k_cache, B * Hkv * S * D * e), s_vc = span(v_cache, B * Hkv * S * D * e);
+    const Span s_kn = span(k_new, B * Hkv * D * e), s_vn = span(v_new, B * Hkv * D * e);
+    const Span s_len = span(lengths, B * 4);
+    if (overlap(s_kc, s_vc) || overlap(s_kn, s_kc) || overlap(s_kn, s_vc) || overlap(s_vn, s_kc) ||
+        overlap(s_vn, s_vc) || overlap(s_len, s_kc) || overlap(s_len, s_vc))
+      return GQA_ERR_INVALID_ARGUMENT;
+    Plan p;
+    std::memset(&p, 0, sizeof(p));
+    p.nsplit = 1;
+    AttnArgs a;
+    fill_args(desc, p, &a);
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.lengths = lengths;
+    if (launch_append(a, k_cache, v_cache, (hipStream_t)stream) != hipSuccess) return GQA_ERR_HIP;
+    return GQA_OK;
+  } catch (...) {
+    return GQA_ERR_INTERNAL;
+  }
+}
+
+gqa_status_t gqa_decode_attend(const gqa_decode_desc_t* desc, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* lengths, void* out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  try {
+    Plan p;
+    gqa_status_t st = make_plan(desc, &p);
+    if (st != GQA_OK) return st;
+    if (desc->batch == 0) return GQA_OK;
+    st = check_attend_ptrs(desc, p, q, k_cache, v_cache, nullptr, nullptr, lengths, out, workspace, workspace_bytes,
+                           false);
+    if (st != GQA_OK) return st;
+    AttnArgs a;
+    fill_args(desc, p, &a);
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.lengths = lengths;
+    a.out = out;
+    a.len_offset = 0;
+    if (p.workspace_bytes > 0) {
+      char* w = static_cast<char*>(workspace);
+      a.part_o = reinterpret_cast<float*>(w);
+      a.part_m = reinterpret_cast<float*>(w + p.off_m);
+      a.part_l = reinterpret_cast<float*>(w + p.off_l);
+    }
+    return run_attend(desc, p, a, (hipStream_t)stream);
+  } catch (...) {
+    return GQA_ERR_INTERNAL;
+  }
+}
+
+gqa_status_t gqa_decode_step(const gqa_decode_desc_t* desc, const void* q, void* k_cache, void* v_cache,
+                             const void* k_new, const void* v_new, const int32_t* lengths, void* out,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    Plan p;
+    gqa_status_t st = make_plan(desc, &p);
+    if (st != GQA_OK) return st;
+    if (desc->batch == 0) return GQA_OK;
+    st = check_attend_ptrs(desc, p, q, k_cache, v_cache, k_new, v_new, lengths, out, workspace, workspace_bytes,
+                           true);
+    if (st != GQA_OK) return st;
+    AttnArgs a;
+    fill_args(desc, p, &a);
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.lengths = lengths;
+    a.out = out;
+    a.len_offset = 1;
+    if (p.workspace_bytes > 0) {
+      char* w = static_cast<char*>(workspace);
+      a.part_o = reinterpret_cast<float*>(w);
+      a.part_m = reinterpret_cast<float*>(w + p.off_m);
+      a.part_l = reinterpret_cast<float*>(w + p.off_l);
+    }
+    if (p.kernel == GQA_KERNEL_GENERIC) {
+      // Generic path: the append kernel, then attention over lengths[b] + 1
+      // slots, ordered by the stream.
+      if (launch_append(a, k_cache, v_cache, (hipStream_t)stream) != hipSuccess) return GQA_ERR_HIP;
+    } else {
+      // Matrix-core paths fuse the append: the workgroup whose split holds
+      // slot lengths[b] takes the new K/V from k_new/v_new and writes it to
+      // the cache; no other workgroup reads that slot.
+      a.k_cache_w = k_cache;
+      a.v_cache_w = v_cache;
+    }
+    return run_attend(desc, p, a, (hipStream_t)stream);
+  } catch (...) {
+    return GQA_ERR_INTERNAL;
+  }
+}
+
+const char* gqa_decode_status_string(gqa_status_t s) {
+  switch (s) {
+    case GQA_OK: return "GQA_OK";
+    case GQA_ERR_INVALID_ARGUMENT: return "GQA_ERR_INVALID_ARGUMENT";
+    case GQA_ERR_UNSUPPORTED: return "GQA_ERR_UNSUPPORTED";
+    case GQA_ERR_WORKSPACE_TOO_SMALL: return "GQA_ERR_WORKSPACE_TOO_SMALL";
+    case GQA_ERR_HIP: return "GQA_ERR_HIP";
+    case GQA_ERR_INTERNAL: return "GQA_ERR_INTERNAL";
+  }
+  return "GQA_ERR_UNKNOWN";
+}
+
+int32_t gqa_decode_version(void) { return kVersion; }
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Host-side interface between the C ABI (gqa_decode.cpp) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gqa_decode.h"
+
+namespace gqa {
+
+// Everything a kernel needs, resolved on the host from the descriptor.
+struct AttnArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  void* k_cache_w;       // fused step: cache written with the new K/V (else null)
+  void* v_cache_w;
+  const void* k_new;     // fused step: new K/V (else null)
+  const void* v_new;
+  const int32_t* lengths;
+  void* out;
+  float* part_o;         // split partials: [B][Hq][nsplit][D] unnormalised sums
+  float* part_m;         // [B][Hq][nsplit] running max (log2 units)
+  float* part_l;         // [B][Hq][nsplit] softmax denominators
+  int32_t B, Hq, Hkv, D, S, G;
+  int64_t sb, sh, st;    // cache element strides of sequence, kv-head, slot
+  int32_t nsplit, split_tokens;
+  int32_t head_chunks;   // generic kernel: query-head chunks per kv-head
+  int32_t len_offset;    // slots attended = lengths[b] + len_offset (1 for a step, 0 for attend)
+  int32_t kv_dtype, qo_dtype;
+  float scale_log2;      // log2(e) / sqrt(D)
+};
+
+struct Plan {
+  int32_t kernel;
+  int32_t nsplit;
+  int32_t split_tokens;
+  int32_t head_chunks;   // generic kernel: query-head chunks per kv-head
+  int32_t grid;
+  int32_t block;
+  int32_t combine;
+  size_t workspace_bytes;
+  size_t off_m, off_l;   // byte offsets of part_m / part_l inside the workspace
+};
+
+// Which matrix-core kernels this build provides (the planner falls back to the
+// generic kernel for the others).
+extern const bool kHaveMfmaQk;
+extern const bool kHaveMfmaAll;
+
+constexpr int kNumCUs = 256;          // MI355X: 8 XCDs x 32 CUs
+constexpr int kGenericHeadChunk = 8;  // query heads per workgroup in the generic kernel
+constexpr int kBlock = 256;
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_append(const AttnArgs& a, void* k_cache, void* v_cache, hipStream_t s);
+hipError_t launch_attend_generic(const AttnArgs& a, const Plan& p, int vec_path, hipStream_t s);
+hipError_t launch_attend_mfma_qk(const AttnArgs& a, const Plan& p, hipStream_t s);
+hipError_t launch_attend_mfma_all(const AttnArgs& a, const Plan& p, hipStream_t s);
+hipError_t launch_combine(const AttnArgs& a, const Plan& p, hipStream_t s);
+
+}  // namespace gqa

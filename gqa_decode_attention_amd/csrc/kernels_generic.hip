@@ -1,0 +1,308 @@
+// Generic kernels of the GQA decode step for gfx950: the in-place append, a
+// vector-ALU split attention that takes any head width D <= 256 in f32 or bf16
+// storage, and the log-sum-exp combine of split partials.
+//
+// Semantics: TensorTonic "Grouped-Query Decode Step" (JAX) page, problem
+// statement -- query head h reads cache head floor(h/G); only slots
+// j < lengths[b] count; s_j = q.K_j/sqrt(D); o = sum_j softmax(s)_j V_j; all in
+// float32.  Append: TensorTonic "KV cache decode step" page -- the new key/value
+// take the position after the cached tokens.
+//
+// The split attention evaluates the same softmax with the online (running
+// maximum) formulation: for a stream of scores it keeps m = max so far,
+// l = sum exp(s - m) and o = sum exp(s - m) V, rescaling l and o by exp(m_old -
+// m_new) whenever the maximum grows.  Partial (m, l, o) triples over disjoint
+// token ranges merge exactly: M = max m_i, l = sum l_i exp(m_i - M), o = sum
+// o_i exp(m_i - M); the output is o / l.  Exponentials are base 2 with log2(e)
+// folded into the score scale.
+#include "device_common.h"
+#include "internal.h"
+
+namespace gqa {
+
+constexpr float kNegInf = -__builtin_inff();
+
+// ---------------------------------------------------------------------------
+// Append: one thread per element of the new K/V; raw copy of the stored bits.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void append_kernel(T* __restrict__ kc, T* __restrict__ vc,
+                                                     const T* __restrict__ kn, const T* __restrict__ vn,
+                                                     const int32_t* __restrict__ lengths, int32_t B,
+                                                     int32_t Hkv, int32_t D, int32_t S, int64_t sb, int64_t sh,
+                                                     int64_t st) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)B * Hkv * D;
+  if (i >= total) return;
+  const int32_t d = (int32_t)(i % D);
+  const int64_t bh = i / D;
+  const int32_t h = (int32_t)(bh % Hkv);
+  const int32_t b = (int32_t)(bh / Hkv);
+  const int32_t pos = lengths[b];
+  if (pos < 0 || pos >= S) return;  // out of contract: nothing written
+  const int64_t off = b * sb + h * sh + (int64_t)pos * st + d;
+  kc[off] = kn[i];
+  vc[off] = vn[i];
+}
+
+hipError_t launch_append(const AttnArgs& a, void* k_cache, void* v_cache, hipStream_t s) {
+  const int64_t total = (int64_t)a.B * a.Hkv * a.D;
+  const unsigned blocks = (unsigned)((total + 255) / 256);
+  const void* kn = a.k_new;
+  const void* vn = a.v_new;
+  const int32_t* lens = a.lengths;
+  int32_t B = a.B, Hkv = a.Hkv, D = a.D, S = a.S;
+  int64_t sb = a.sb, sh = a.sh, st = a.st;
+  void* params[] = {&k_cache, &v_cache, &kn, &vn, &lens, &B, &Hkv, &D, &S, &sb, &sh, &st};
+  const void* fn = a.kv_dtype == GQA_F32 ? reinterpret_cast<const void*>(&append_kernel<uint32_t>)
+                                         : reinterpret_cast<const void*>(&append_kernel<uint16_t>);
+  return hipLaunchKernel(fn, dim3(blocks), dim3(256), params, 0, s);
+}
+
+// ---------------------------------------------------------------------------
+// Generic split attention.
+//
+// Grid: blockIdx.x = ((b * Hkv + h) * head_chunks + c) * nsplit + split; the
+// split index varies fastest so neighbouring workgroups (which the dispatcher
+// deals round-robin to the 8 XCDs) take different token ranges of the same
+// (b, h).  Block: 4 waves.  The lanes of a wave form row groups of LPR lanes;
+// a row group handles one slot at a time and each lane holds NCH chunks of VEC
+// consecutive elements of the row (element d = (c * LPR + lane_in_group) * VEC
+// + e).  A workgroup serves up to kGenericHeadChunk query heads of one kv-head,
+// so each K/V row it loads is used by all of them.
+// ---------------------------------------------------------------------------
+template <int KV, int QO, int VEC, int NCH, int LPR>
+__global__ __launch_bounds__(256) void attend_generic_kernel(AttnArgs a) {
+  constexpr int EPL = VEC * NCH;
+  constexpr int RPW = 64 / LPR;
+  constexpr int NRG = 4 * RPW;
+  constexpr int GC = kGenericHeadChunk;
+  constexpr int KB = Store<KV>::kBytes;
+
+  __shared__ float sm_o[4][GC][256];
+  __shared__ float sm_m[4][GC];
+  __shared__ float sm_l[4][GC];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int rl = lane % LPR;
+  const int rg = wave * RPW + lane / LPR;
+
+  int x = blockIdx.x;
+  const int split = x % a.nsplit;
+  x /= a.nsplit;
+  const int hc = x % a.head_chunks;
+  x /= a.head_chunks;
+  const int h = x % a.Hkv;
+  const int b = x / a.Hkv;
+  const int g0 = hc * GC;
+  const int gc = min(GC, a.G - g0);
+  const int D = a.D;
+
+  int n = a.lengths[b] + a.len_offset;
+  n = n < 0 ? 0 : (n > a.S ? a.S : n);
+  const int t_begin = split * a.split_tokens;
+  const int t_end = min(t_begin + a.split_tokens, n);
+  if (a.nsplit > 1 && t_begin >= n) return;  // inactive split: the combine pass skips it
+
+  const int64_t qrow0 = ((int64_t)b * a.Hq + (int64_t)h * a.G + g0) * D;
+  float qv[GC][EPL];
+#pragma unroll
+  for (int g = 0; g < GC; ++g)
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const int d = (c * LPR + rl) * VEC + e;
+        qv[g][c * VEC + e] = (g < gc && d < D) ? Store<QO>::load1_cached(a.q, qrow0 + (int64_t)g * D + d) : 0.f;
+      }
+
+  float m[GC], l[GC], acc[GC][EPL];
+#pragma unroll
+  for (int g = 0; g < GC; ++g) {
+    m[g] = kNegInf;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
+  }
+
+  const int64_t base = (int64_t)b * a.sb + (int64_t)h * a.sh;
+  const char* kb = reinterpret_cast<const char*>(a.k_cache) + base * KB;
+  const char* vb = reinterpret_cast<const char*>(a.v_cache) + base * KB;
+
+  for (int t = t_begin + rg; t < t_end; t += NRG) {
+    const int64_t row = (int64_t)t * a.st;
+    float kv[EPL], vv[EPL];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int d0 = (c * LPR + rl) * VEC;
+      if constexpr (VEC > 1) {
+        if (d0 < D) {
+          widen16<KV>(load_nt16(kb + (row + d0) * KB), &kv[c * VEC]);
+          widen16<KV>(load_nt16(vb + (row + d0) * KB), &vv[c * VEC]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) kv[c * VEC + e] = vv[c * VEC + e] = 0.f;
+        }
+      } else {
+        kv[c] = d0 < D ? Store<KV>::load1(kb, row + d0) : 0.f;
+        vv[c] = d0 < D ? Store<KV>::load1(vb, row + d0) : 0.f;
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < GC; ++g) {
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) part = fmaf(qv[g][e], kv[e], part);
+#pragma unroll
+      for (int off = LPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off);
+      const float s = part * a.scale_log2;
+      const float mn = fmaxf(m[g], s);
+      const float alpha = fast_exp2(m[g] - mn);  // 0 on the first slot (m = -inf)
+      const float p = fast_exp2(s - mn);
+      l[g] = l[g] * alpha + p;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(p, vv[e], acc[g][e] * alpha);
+      m[g] = mn;
+    }
+  }
+
+  // Merge the row groups of each wave (partials over disjoint slot sets).
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1) {
+#pragma unroll
+    for (int g = 0; g < GC; ++g) {
+      const float mo = __shfl_xor(m[g], off);
+      const float lo = __shfl_xor(l[g], off);
+      const float mn = fmaxf(m[g], mo);
+      const float a1 = m[g] == kNegInf ? 0.f : fast_exp2(m[g] - mn);
+      const float a2 = mo == kNegInf ? 0.f : fast_exp2(mo - mn);
+      l[g] = l[g] * a1 + lo * a2;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float ao = __shfl_xor(acc[g][e], off);
+        acc[g][e] = acc[g][e] * a1 + ao * a2;
+      }
+      m[g] = mn;
+    }
+  }
+  // Merge the 4 waves through LDS; row group 0 of each wave holds its wave's totals.
+  if (lane < LPR) {
+#pragma unroll
+    for (int g = 0; g < GC; ++g) {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const int d = (c * LPR + rl) * VEC + e;
+          if (d < D) sm_o[wave][g][d] = acc[g][c * VEC + e];
+        }
+      if (rl == 0) {
+        sm_m[wave][g] = m[g];
+        sm_l[wave][g] = l[g];
+      }
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < gc * D; idx += 256) {
+    const int g = idx / D;
+    const int d = idx - g * D;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][g]);
+    float O = 0.f, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = sm_m[w][g];
+      const float sc = mw == kNegInf ? 0.f : fast_exp2(mw - M);
+      O += sm_o[w][g][d] * sc;
+      L += sm_l[w][g] * sc;
+    }
+    const int hq = h * a.G + g0 + g;
+    if (a.nsplit == 1) {
+      Store<QO>::store1(a.out, ((int64_t)b * a.Hq + hq) * D + d, L > 0.f ? O / L : 0.f);
+    } else {
+      const int64_t pi = ((int64_t)b * a.Hq + hq) * a.nsplit + split;
+      a.part_o[pi * D + d] = O;
+      if (d == 0) {
+        a.part_m[pi] = M;
+        a.part_l[pi] = L;
+      }
+    }
+  }
+}
+
+template <int KV, int QO, int VEC, int NCH, int LPR>
+static hipError_t launch_generic_t(const AttnArgs& a, const Plan& p, hipStream_t s) {
+  AttnArgs arg = a;
+  void* params[] = {&arg};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attend_generic_kernel<KV, QO, VEC, NCH, LPR>),
+                         dim3(p.grid), dim3(256), params, 0, s);
+}
+
+// vec_path: every cache row starts 16-byte aligned and D is a multiple of the
+// 16-byte vector (8 bf16 or 4 f32), so rows are read with 16-byte loads.
+template <int KV, int QO>
+static hipError_t dispatch_generic(const AttnArgs& a, const Plan& p, int vec_path, hipStream_t s) {
+  const int D = a.D;
+  if (vec_path) {
+    if constexpr (KV == GQA_BF16) {
+      if (D <= 32) return launch_generic_t<KV, QO, 8, 1, 4>(a, p, s);
+      if (D <= 128) return launch_generic_t<KV, QO, 8, 1, 16>(a, p, s);
+      return launch_generic_t<KV, QO, 8, 1, 32>(a, p, s);
+    } else {
+      if (D <= 16) return launch_generic_t<KV, QO, 4, 1, 4>(a, p, s);
+      if (D <= 64) return launch_generic_t<KV, QO, 4, 1, 16>(a, p, s);
+      return launch_generic_t<KV, QO, 4, 1, 64>(a, p, s);
+    }
+  }
+  if (D <= 4) return launch_generic_t<KV, QO, 1, 1, 4>(a, p, s);
+  if (D <= 16) return launch_generic_t<KV, QO, 1, 1, 16>(a, p, s);
+  if (D <= 64) return launch_generic_t<KV, QO, 1, 1, 64>(a, p, s);
+  return launch_generic_t<KV, QO, 1, 4, 64>(a, p, s);
+}
+
+hipError_t launch_attend_generic(const AttnArgs& a, const Plan& p, int vec_path, hipStream_t s) {
+  if (a.kv_dtype == GQA_F32 && a.qo_dtype == GQA_F32) return dispatch_generic<GQA_F32, GQA_F32>(a, p, vec_path, s);
+  if (a.kv_dtype == GQA_F32) return dispatch_generic<GQA_F32, GQA_BF16>(a, p, vec_path, s);
+  if (a.qo_dtype == GQA_F32) return dispatch_generic<GQA_BF16, GQA_F32>(a, p, vec_path, s);
+  return dispatch_generic<GQA_BF16, GQA_BF16>(a, p, vec_path, s);
+}
+
+// ---------------------------------------------------------------------------
+// Combine: one workgroup per (b, query head) merges the active splits.
+// ---------------------------------------------------------------------------
+template <int QO>
+__global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
+  const int bh = blockIdx.x;  // b * Hq + hq
+  const int b = bh / a.Hq;
+  int n = a.lengths[b] + a.len_offset;
+  n = n < 0 ? 0 : (n > a.S ? a.S : n);
+  int nact = n == 0 ? 0 : (n + a.split_tokens - 1) / a.split_tokens;
+  nact = min(nact, a.nsplit);
+  const int64_t pbase = (int64_t)bh * a.nsplit;
+  float M = kNegInf;
+  for (int i = 0; i < nact; ++i) M = fmaxf(M, a.part_m[pbase + i]);
+  for (int d = threadIdx.x; d < a.D; d += blockDim.x) {
+    float O = 0.f, L = 0.f;
+    for (int i = 0; i < nact; ++i) {
+      const float w = fast_exp2(a.part_m[pbase + i] - M);
+      L = fmaf(w, a.part_l[pbase + i], L);
+      O = fmaf(w, a.part_o[(pbase + i) * a.D + d], O);
+    }
+    Store<QO>::store1(a.out, (int64_t)bh * a.D + d, (nact > 0 && L > 0.f) ? O / L : 0.f);
+  }
+}
+
+hipError_t launch_combine(const AttnArgs& a, const Plan& p, hipStream_t s) {
+  (void)p;
+  const int threads = ((a.D + 63) / 64) * 64;
+  const unsigned blocks = (unsigned)(a.B * a.Hq);
+  AttnArgs arg = a;
+  void* params[] = {&arg};
+  const void* fn = a.qo_dtype == GQA_F32 ? reinterpret_cast<const void*>(&combine_kernel<GQA_F32>)
+                                         : reinterpret_cast<const void*>(&combine_kernel<GQA_BF16>);
+  return hipLaunchKernel(fn, dim3(blocks), dim3(threads), params, 0, s);
+}
+
+}  // namespace gqa

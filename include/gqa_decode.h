@@ -1,0 +1,172 @@
+/*
+ * gqa_decode.h -- C ABI of the MI355X (gfx950) grouped-query attention decode step.
+ *
+ * One decode step of one attention layer for a batch of sequences:
+ *   1. append: each sequence's new key/value (one per kv-head) is written in
+ *      place at slot lengths[b] of a fixed-capacity cache;
+ *   2. attend: every query head h reads cache head floor(h / G), G = Hq / Hkv,
+ *      and returns softmax(q . K_j / sqrt(D)) weighted sums of V_j over the
+ *      valid slots only.
+ *
+ * Sources of the semantics (web pages, cited by title and section):
+ *   - TensorTonic, "KV cache decode step" problem page (CS336 L10): problem
+ *     statement -- query (B,Hq,D), new key/value (B,Hkv,D), caches
+ *     (B,Hkv,S,D); contiguous groups (query head hG+g of kv-head h); the new
+ *     key/value take position S; the softmax runs over every cached position
+ *     plus the new token; dtype is preserved.
+ *   - TensorTonic, "Grouped-Query Decode Step" (JAX) problem page: problem
+ *     statement and formulas -- caches (B,S,Hkv,D), query head h reads cache
+ *     head floor(h/G), only slots j < lengths[b] are valid (the new token
+ *     already among them), s_j = q.K_j/sqrt(D), softmax, o = sum w_j V_j;
+ *     requirements -- stale slots get zero weight, bfloat16 caches are
+ *     widened to float32 and scores/softmax/sums run in float32; constraints
+ *     -- lengths is int32 (B,), each in [1,S].
+ *   - CLIKA runtime, "groupQueryAttention" API page: the decode perf path
+ *     appends the new K/V in place into the bound cache; a read-only attend is
+ *     a separate call; malformed arguments are refused with INVALID_ARGUMENT
+ *     after validating the whole input before any read.
+ *   - Huawei CANN, "aclnnMlaPrologV3WeightNz" operator page: two-phase call
+ *     convention (a size/validation phase, then execution), status-code
+ *     returns, empty batch allowed with caches left untouched.
+ *
+ * Conventions shared by every entry point
+ *   - All tensors are caller-owned, dense, row-major buffers in device memory
+ *     of the current HIP device.  The library allocates nothing, keeps no
+ *     pointer after returning and never writes `lengths`.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued on it and the call returns without synchronising:
+ *     GQA_OK means "validated and enqueued"; a fault inside a kernel surfaces
+ *     at the caller's next synchronisation.
+ *   - Every condition the host can check is checked before anything is
+ *     enqueued; on any error nothing has been enqueued or written.
+ *   - `lengths` lives on the device and is never read by the host, so every
+ *     call can be captured in a HIP graph.  Values outside the documented
+ *     range do not fault: append skips the write, attend clamps the count to
+ *     [0, capacity], and a sequence with no valid slot yields zeros; such
+ *     outputs are outside the numerical contract.
+ *   - Storage types: GQA_F32 = IEEE binary32, GQA_BF16 = bfloat16 (upper half of
+ *     a binary32).  Scores, softmax and sums are float32 whatever the storage;
+ *     a bf16 output is rounded to nearest-even from the float32 result.
+ *   - Calls are deterministic: the same inputs give the same bits (no
+ *     floating-point atomics; reductions have a fixed order).
+ */
+#ifndef GQA_DECODE_H
+#define GQA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GQA_OK = 0,
+  GQA_ERR_INVALID_ARGUMENT = 1,    /* malformed descriptor, null/misaligned/overlapping pointer */
+  GQA_ERR_UNSUPPORTED = 2,         /* well-formed but not implemented (head_dim > 256)          */
+  GQA_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes below gqa_decode_workspace_size()         */
+  GQA_ERR_HIP = 4,                 /* a HIP launch failed                                       */
+  GQA_ERR_INTERNAL = 5             /* unexpected library error (no C++ exception crosses)       */
+} gqa_status_t;
+
+enum { GQA_F32 = 0, GQA_BF16 = 1 };
+enum {
+  GQA_LAYOUT_BHSD = 0,  /* caches (B, Hkv, S, D): KV cache decode step page            */
+  GQA_LAYOUT_BSHD = 1   /* caches (B, S, Hkv, D): JAX Grouped-Query Decode Step page   */
+};
+
+typedef struct {
+  int32_t batch;        /* B >= 0.  B == 0: the call validates the descriptor, returns GQA_OK
+                           and enqueues nothing (pointers may then be NULL).               */
+  int32_t num_q_heads;  /* Hq >= 1, a multiple of num_kv_heads                              */
+  int32_t num_kv_heads; /* Hkv >= 1                                                         */
+  int32_t head_dim;     /* D in [1, 256]; D > 256 is GQA_ERR_UNSUPPORTED                    */
+  int32_t capacity;     /* S >= 1 slots per (sequence, kv-head) in both caches              */
+  int32_t layout;       /* GQA_LAYOUT_BHSD or GQA_LAYOUT_BSHD, shared by both caches         */
+  int32_t kv_dtype;     /* storage of k_cache, v_cache, k_new, v_new: GQA_F32 or GQA_BF16    */
+  int32_t qo_dtype;     /* storage of q and out: GQA_F32 or GQA_BF16                         */
+  int32_t num_splits;   /* 0 = library's choice; n > 0 cuts the token axis into n splits
+                           (results agree within rounding for every n)                      */
+} gqa_decode_desc_t;
+
+/* How a call with this descriptor runs (introspection for tests and tuning).
+ * A pure function of the descriptor: never of `lengths` or of pointers. */
+typedef struct {
+  int32_t kernel;        /* GQA_KERNEL_* of the attention pass                              */
+  int32_t num_splits;    /* splits of the token axis                                        */
+  int32_t split_tokens;  /* slots per split (the last split may be shorter)                 */
+  int32_t grid;          /* workgroups of the attention pass                                */
+  int32_t block;         /* threads per workgroup of the attention pass                     */
+  int32_t combine;       /* 1 if a split-combine pass follows                               */
+  size_t workspace_bytes;
+} gqa_decode_plan_t;
+
+enum {
+  GQA_KERNEL_GENERIC = 0,  /* vector ALU, any D <= 256, f32 or bf16 storage                  */
+  GQA_KERNEL_MFMA_QK = 1,  /* bf16, D = 128, G <= 16: scores on MFMA, V sum on vector ALU    */
+  GQA_KERNEL_MFMA_ALL = 2  /* bf16, D = 128, G > 16: scores and V sum on MFMA                */
+};
+
+/* Phase one (CANN operator page, two-phase call convention): validate the
+ * descriptor and report the workspace the attend/step calls need, in bytes
+ * (0 when the token axis is not split).  Returns GQA_ERR_INVALID_ARGUMENT or
+ * GQA_ERR_UNSUPPORTED for a bad descriptor; *bytes is then untouched. */
+gqa_status_t gqa_decode_workspace_size(const gqa_decode_desc_t* desc, size_t* bytes);
+
+/* The execution plan for `desc` (see gqa_decode_plan_t). */
+gqa_status_t gqa_decode_get_plan(const gqa_decode_desc_t* desc, gqa_decode_plan_t* plan);
+
+/* In-place append (KV cache decode step page, problem statement: the new key
+ * and value occupy the position after the cached ones; CLIKA
+ * groupQueryAttention: in-place append into the bound cache).
+ *   k_cache, v_cache : (B,Hkv,S,D) or (B,S,Hkv,D) per desc->layout, kv_dtype, written
+ *   k_new, v_new     : (B, Hkv, D), kv_dtype, read
+ *   lengths          : int32 (B,), device; lengths[b] = tokens held before the call.
+ *                      Slot lengths[b] of every kv-head of sequence b receives a raw
+ *                      copy of the new key/value bits; no other byte changes.
+ *                      Contract: 0 <= lengths[b] < S (otherwise that sequence is skipped).
+ * Pointers must be non-null and aligned to the element size; k_cache/v_cache
+ * must not overlap each other or k_new/v_new. */
+gqa_status_t gqa_decode_append(const gqa_decode_desc_t* desc, void* k_cache, void* v_cache,
+                               const void* k_new, const void* v_new, const int32_t* lengths,
+                               void* stream);
+
+/* Read-only attend (JAX Grouped-Query Decode Step page, problem statement and
+ * formulas; CLIKA groupQueryAttention: attention over the cache without
+ * present outputs).
+ *   q        : (B, Hq, D), qo_dtype, read
+ *   k_cache, v_cache : per desc->layout, kv_dtype, read only
+ *   lengths  : int32 (B,), device; lengths[b] = valid slots (the new token already
+ *              stored among them).  Contract: 1 <= lengths[b] <= S.
+ *   out      : (B, Hq, D), qo_dtype, written; out[b,h] = sum_{j<lengths[b]} w_j V_j of
+ *              cache head h / (Hq/Hkv); must not overlap any other argument.
+ *   workspace: device scratch of at least gqa_decode_workspace_size() bytes, 256-byte
+ *              aligned (may be NULL when that size is 0).  Its contents on entry do not
+ *              matter and are overwritten.
+ * Pointers must be non-null and aligned to the element size. */
+gqa_status_t gqa_decode_attend(const gqa_decode_desc_t* desc, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* lengths, void* out,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Fused decode step = append, then attend over lengths[b] + 1 slots (KV cache
+ * decode step page: the softmax covers every cached position plus the new
+ * token).  Arguments as in gqa_decode_append and gqa_decode_attend;
+ * lengths[b] is the pre-append count (contract: 0 <= lengths[b] < S).  The
+ * caller advances lengths itself afterwards (for example lengths += 1 on the
+ * same stream). */
+gqa_status_t gqa_decode_step(const gqa_decode_desc_t* desc, const void* q, void* k_cache,
+                             void* v_cache, const void* k_new, const void* v_new,
+                             const int32_t* lengths, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Static, NUL-terminated name of a status code. */
+const char* gqa_decode_status_string(gqa_status_t status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t gqa_decode_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_DECODE_H */

@@ -1,0 +1,232 @@
+"""C-ABI checks that need no GPU.
+
+The library must load and export every function include/gqa_decode.h
+declares; every malformed call must return its status before any HIP call.
+Only calls that are invalid (or have batch 0) are made here: pointers are
+fake host integers that the library never dereferences on these paths.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import torch
+
+import gqa_decode_attention_amd as g
+from gqa_decode_attention_amd import _lib
+
+# The calls below pass fake pointers that must never reach a real device: a
+# test bug that made one of them valid would launch a kernel on them.
+pytestmark = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                                reason="fake-pointer ABI tests run only where no GPU is visible")
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "gqa_decode.h")
+OK, INVALID, UNSUPPORTED, WS_SMALL = 0, 1, 2, 3
+
+FAKE = 1 << 40          # 256-byte aligned fake device address: never dereferenced on error paths
+GAP = 1 << 34           # spacing that keeps fake buffers disjoint
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:gqa_status_t|const char\*|int32_t)\s+(gqa_decode_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    L = g.lib()
+    names = header_functions()
+    assert len(names) >= 7
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_lib.EXPORTS)
+
+
+def test_status_strings_and_version():
+    L = g.lib()
+    for code, name in _lib.STATUS_NAMES.items():
+        assert L.gqa_decode_status_string(code).decode() == name
+    assert L.gqa_decode_status_string(99).decode() == "GQA_ERR_UNKNOWN"
+    assert L.gqa_decode_version() >= 100
+
+
+def desc(**kw):
+    base = dict(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, capacity=4096, layout="BHSD",
+                kv_dtype=g.BF16, qo_dtype=g.BF16, num_splits=0)
+    base.update(kw)
+    return g.make_desc(**base)
+
+
+BAD_DESCS = [
+    (dict(batch=-1), INVALID),
+    (dict(num_q_heads=0), INVALID),
+    (dict(num_kv_heads=0), INVALID),
+    (dict(num_q_heads=6, num_kv_heads=4), INVALID),     # Hq not a multiple of Hkv
+    (dict(head_dim=0), INVALID),
+    (dict(capacity=0), INVALID),
+    (dict(kv_dtype=7), INVALID),
+    (dict(qo_dtype=-1), INVALID),
+    (dict(num_splits=-2), INVALID),
+    (dict(head_dim=257), UNSUPPORTED),
+    (dict(batch=1 << 30, capacity=1 << 30), UNSUPPORTED),   # byte count past 2^62
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD_DESCS)
+def test_bad_descriptor_rejected_everywhere(kw, status):
+    L = g.lib()
+    d = desc(**kw)
+    n = ctypes.c_size_t(12345)
+    assert L.gqa_decode_workspace_size(ctypes.byref(d), ctypes.byref(n)) == status
+    assert n.value == 12345                                   # untouched on error
+    p = _lib.PlanT()
+    assert L.gqa_decode_get_plan(ctypes.byref(d), ctypes.byref(p)) == status
+    ptrs = [FAKE + i * GAP for i in range(8)]
+    assert L.gqa_decode_attend(ctypes.byref(d), ptrs[0], ptrs[1], ptrs[2], ptrs[3], ptrs[4], ptrs[5], 1 << 30,
+                               None) == status
+    assert L.gqa_decode_step(ctypes.byref(d), ptrs[0], ptrs[1], ptrs[2], ptrs[6], ptrs[7], ptrs[3], ptrs[4],
+                             ptrs[5], 1 << 30, None) == status
+    assert L.gqa_decode_append(ctypes.byref(d), ptrs[1], ptrs[2], ptrs[6], ptrs[7], ptrs[3], None) == status
+
+
+def test_null_desc_and_null_outputs():
+    L = g.lib()
+    assert L.gqa_decode_workspace_size(None, ctypes.byref(ctypes.c_size_t())) == INVALID
+    d = desc()
+    assert L.gqa_decode_workspace_size(ctypes.byref(d), None) == INVALID
+    assert L.gqa_decode_get_plan(ctypes.byref(d), None) == INVALID
+
+
+def test_empty_batch_is_a_noop():
+    """Batch 0 validates the descriptor and returns OK without touching pointers (all NULL)."""
+    L = g.lib()
+    d = desc(batch=0)
+    assert L.gqa_decode_attend(ctypes.byref(d), None, None, None, None, None, None, 0, None) == OK
+    assert L.gqa_decode_step(ctypes.byref(d), None, None, None, None, None, None, None, None, 0, None) == OK
+    assert L.gqa_decode_append(ctypes.byref(d), None, None, None, None, None, None) == OK
+    n = ctypes.c_size_t(1)
+    assert L.gqa_decode_workspace_size(ctypes.byref(d), ctypes.byref(n)) == OK and n.value == 0
+
+
+def _attend_ptrs():
+    return dict(q=FAKE, kc=FAKE + GAP, vc=FAKE + 2 * GAP, lens=FAKE + 3 * GAP, out=FAKE + 4 * GAP,
+                ws=FAKE + 5 * GAP, kn=FAKE + 6 * GAP, vn=FAKE + 7 * GAP)
+
+
+def _attend(d, p, wsb):
+    return g.lib().gqa_decode_attend(ctypes.byref(d), p["q"], p["kc"], p["vc"], p["lens"], p["out"], p["ws"], wsb,
+                                     None)
+
+
+def _step(d, p, wsb):
+    return g.lib().gqa_decode_step(ctypes.byref(d), p["q"], p["kc"], p["vc"], p["kn"], p["vn"], p["lens"], p["out"],
+                                   p["ws"], wsb, None)
+
+
+@pytest.mark.parametrize("call", [_attend, _step])
+@pytest.mark.parametrize("field", ["q", "kc", "vc", "lens", "out"])
+def test_null_pointer_rejected(call, field):
+    d = desc()
+    p = _attend_ptrs()
+    p[field] = None
+    assert call(d, p, 1 << 30) == INVALID
+
+
+def test_step_null_new_kv_rejected():
+    d = desc()
+    for f in ("kn", "vn"):
+        p = _attend_ptrs()
+        p[f] = None
+        assert _step(d, p, 1 << 30) == INVALID
+
+
+@pytest.mark.parametrize("call", [_attend, _step])
+def test_workspace_too_small(call):
+    d = desc()
+    need = g.workspace_size(d)
+    assert need > 0
+    assert call(d, _attend_ptrs(), need - 1) == WS_SMALL
+    p = _attend_ptrs()
+    p["ws"] = None
+    assert call(d, p, need) == INVALID
+    p = _attend_ptrs()
+    p["ws"] += 16                                             # not 256-byte aligned
+    assert call(d, p, need) == INVALID
+
+
+@pytest.mark.parametrize("call", [_attend, _step])
+@pytest.mark.parametrize("field,shift", [("q", 1), ("out", 1), ("kc", 1), ("vc", 1), ("lens", 2)])
+def test_misaligned_pointer_rejected(call, field, shift):
+    d = desc(kv_dtype=g.F32, qo_dtype=g.F32, head_dim=4)
+    p = _attend_ptrs()
+    p[field] += shift
+    assert call(d, p, 1 << 30) == INVALID
+
+
+@pytest.mark.parametrize("call", [_attend, _step])
+@pytest.mark.parametrize("other", ["q", "kc", "vc", "lens", "ws"])
+def test_output_overlapping_an_input_rejected(call, other):
+    d = desc()
+    p = _attend_ptrs()
+    p["out"] = p[other]
+    assert call(d, p, 1 << 30) == INVALID
+    p = _attend_ptrs()
+    p["out"] = p[other] - 256          # out's span reaches into the other buffer
+    assert call(d, p, 1 << 30) == INVALID
+
+
+def test_step_and_append_reject_aliased_caches():
+    d = desc()
+    p = _attend_ptrs()
+    p["vc"] = p["kc"] + 512
+    assert _step(d, p, 1 << 30) == INVALID
+    assert g.lib().gqa_decode_append(ctypes.byref(d), p["kc"], p["vc"], p["kn"], p["vn"], p["lens"], None) == INVALID
+    p = _attend_ptrs()
+    p["kn"] = p["vc"] + 1024
+    assert _step(d, p, 1 << 30) == INVALID
+    assert g.lib().gqa_decode_append(ctypes.byref(d), p["kc"], p["vc"], p["kn"], p["vn"], p["lens"], None) == INVALID
+
+
+def test_append_null_and_misaligned():
+    L = g.lib()
+    d = desc()
+    p = _attend_ptrs()
+    for f in ("kc", "vc", "kn", "vn", "lens"):
+        q = dict(p)
+        q[f] = None
+        assert L.gqa_decode_append(ctypes.byref(d), q["kc"], q["vc"], q["kn"], q["vn"], q["lens"], None) == INVALID
+        q = dict(p)
+        q[f] += 1
+        assert L.gqa_decode_append(ctypes.byref(d), q["kc"], q["vc"], q["kn"], q["vn"], q["lens"], None) == INVALID
+
+
+def test_plan_is_a_function_of_the_descriptor_only():
+    """Same descriptor -> same plan and workspace; the plan has no lengths input at all."""
+    for kw in (dict(), dict(layout="BSHD"), dict(batch=64, num_q_heads=64, num_kv_heads=8, capacity=8192),
+               dict(batch=4, num_q_heads=32, num_kv_heads=8, capacity=131073),
+               dict(batch=128, num_q_heads=64, num_kv_heads=1, capacity=2048),
+               dict(batch=2, num_q_heads=4, num_kv_heads=2, head_dim=4, capacity=8, kv_dtype=g.F32, qo_dtype=g.F32)):
+        d = desc(**kw)
+        p1, p2 = g.get_plan(d), g.get_plan(d)
+        assert p1 == p2
+        assert p1["workspace_bytes"] == g.workspace_size(d)
+        assert p1["num_splits"] * p1["split_tokens"] >= d.capacity
+        assert (p1["num_splits"] - 1) * p1["split_tokens"] < d.capacity     # no empty split
+        assert p1["combine"] == (p1["num_splits"] > 1)
+        assert (p1["workspace_bytes"] == 0) == (p1["num_splits"] == 1)
+
+
+@pytest.mark.parametrize("ns", [1, 2, 3, 7, 64, 10_000])
+def test_forced_split_count(ns):
+    d = desc(num_splits=ns, capacity=4097)
+    p = g.get_plan(d)
+    assert 1 <= p["num_splits"] <= min(ns, 4097)
+    assert p["num_splits"] * p["split_tokens"] >= 4097
+    if ns == 1:
+        assert p["workspace_bytes"] == 0 and not p["combine"]
+
+
+def test_workspace_bytes_cover_partials():
+    d = desc(batch=32, num_q_heads=32, num_kv_heads=8, capacity=4097)
+    p = g.get_plan(d)
+    assert p["workspace_bytes"] >= 32 * 32 * p["num_splits"] * (128 + 2) * 4

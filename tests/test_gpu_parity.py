@@ -1,0 +1,357 @@
+"""GPU parity: the HIP library against the float64 oracle, element by element.
+
+Tolerances (abs + rel, elementwise): fp32 outputs |gpu - ref| <= 2e-5 + 2e-5 |ref|;
+bf16 outputs <= 1e-2 + 1e-2 |ref|.  The append is compared byte for byte.
+Inputs come from the seeded generators in workloads.py; the oracle gets the
+same stored bits through workloads.to_numpy_storage.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+TOL = {"f32": 2e-5, "bf16": 1e-2}
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def g():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gqa_decode_attention_amd as lib
+    lib.lib()           # raises if the HIP library is not built
+    return lib
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def np_of(t):
+    return W.to_numpy_storage(t)
+
+
+def assert_close(out_gpu, ref, qo_dtype, what=""):
+    got = out_gpu.detach().float().cpu().double().numpy()
+    tol = TOL[qo_dtype]
+    err = np.abs(got - ref)
+    bound = tol + tol * np.abs(ref)
+    bad = ~(err <= bound)
+    assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} outside tolerance; worst excess "
+                           f"{np.max(err - bound):.3g} at {np.unravel_index(np.argmax(err - bound), err.shape)}")
+
+
+def run_step(g, inp, w, num_splits=0):
+    return g.step(inp["q"], inp["k_cache"], inp["v_cache"], inp["k_new"], inp["v_new"], inp["lengths"],
+                  layout=w.layout, num_splits=num_splits)
+
+
+def oracle_step(inp, w):
+    return oracle.step(np_of(inp["q"]), w.qo_dtype, np_of(inp["k_cache"]), np_of(inp["v_cache"]),
+                       np_of(inp["k_new"]), np_of(inp["v_new"]), w.kv_dtype, inp["lengths"].cpu().numpy(),
+                       w.layout, w.Hq, w.Hkv)
+
+
+def check_step_full(g, w, lengths=None, num_splits=0):
+    """Step on the GPU vs the oracle: output within tolerance, caches byte-exact."""
+    inp = W.make_inputs(w, DEV, lengths=lengths)
+    ref_out, ref_k, ref_v = oracle_step(inp, w)         # oracle sees the caches before the append
+    say(f"step {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} S={w.capacity} {w.layout} "
+        f"kv={w.kv_dtype} qo={w.qo_dtype} splits={num_splits} plan={g.get_plan(g.desc_for(inp['q'], inp['k_cache'], w.layout, num_splits))}")
+    out = run_step(g, inp, w, num_splits)
+    torch.cuda.synchronize()
+    assert_close(out, ref_out, w.qo_dtype, w.name)
+    assert np_of(inp["k_cache"]).tobytes() == ref_k.tobytes()
+    assert np_of(inp["v_cache"]).tobytes() == ref_v.tobytes()
+    return inp, out
+
+
+# ---------------------------------------------------------------------------
+# The pages' worked examples, run through the library.
+# ---------------------------------------------------------------------------
+def test_kv_cache_decode_step_page_examples(g):
+    cases = json.load(open(os.path.join(GOLDEN, "kv_cache_decode_step_examples.json")))["cases"]
+    for c in cases:
+        say("page example (KV cache decode step):", c["name"])
+        q = torch.tensor(c["query"], dtype=torch.float32)
+        kc = torch.tensor(c["key_cache"], dtype=torch.float32)
+        vc = torch.tensor(c["value_cache"], dtype=torch.float32)
+        B, Hkv, S, D = kc.shape
+        kcap = torch.full((B, Hkv, S + 1, D), 777.0)
+        vcap = torch.full((B, Hkv, S + 1, D), -777.0)
+        kcap[:, :, :S] = kc
+        vcap[:, :, :S] = vc
+        kn = torch.tensor(c["new_key"], dtype=torch.float32)
+        vn = torch.tensor(c["new_value"], dtype=torch.float32)
+        L = torch.full((B,), S, dtype=torch.int32)
+        ref, rk, rv = oracle.step(q.numpy(), "f32", kcap.numpy(), vcap.numpy(), kn.numpy(), vn.numpy(), "f32",
+                                  L.numpy(), "BHSD", c["num_query_heads"], c["num_kv_heads"])
+        qd, kd, vd, knd, vnd, Ld = (t.to(DEV) for t in (q, kcap, vcap, kn, vn, L))
+        out = g.step(qd, kd, vd, knd, vnd, Ld, layout="BHSD")
+        torch.cuda.synchronize()
+        assert_close(out, ref, "f32", c["name"])
+        printed = np.array(c["output"]).astype(np.float64)
+        assert np.max(np.abs(out.cpu().double().numpy() - printed)) < 1e-6
+        assert kd.cpu().numpy().tobytes() == rk.tobytes() and vd.cpu().numpy().tobytes() == rv.tobytes()
+
+
+def test_gqa_jax_page_examples(g):
+    cases = json.load(open(os.path.join(GOLDEN, "gqa_decode_step_jax_examples.json")))["cases"]
+    for c in cases:
+        say("page example (JAX Grouped-Query Decode Step):", c["name"])
+        q = torch.tensor(c["query"], dtype=torch.float32)
+        kc = torch.tensor(c["key_cache"], dtype=torch.float32)
+        vc = torch.tensor(c["value_cache"], dtype=torch.float32)
+        L = torch.tensor(c["lengths"], dtype=torch.int32)
+        ref = oracle.attend(q.numpy(), "f32", kc.numpy(), vc.numpy(), "f32", L.numpy(), "BSHD",
+                            c["num_query_heads"], c["num_kv_heads"])
+        out = g.attend(q.to(DEV), kc.to(DEV), vc.to(DEV), L.to(DEV), layout="BSHD")
+        torch.cuda.synchronize()
+        assert_close(out, ref, "f32", c["name"])
+        printed = np.array(c["output"]).astype(np.float64)
+        dec = np.vectorize(lambda s: len(s.split(".")[1]) if "." in s else 0)(np.array(c["output"]))
+        assert np.all(np.abs(out.cpu().double().numpy() - printed) <= 0.5 * 10.0 ** (-dec) + 1e-6)
+
+
+def test_page_example_with_bf16_caches_and_f32_query(g):
+    """JAX page requirement: bf16 caches widened to f32, f32 query and output."""
+    c = json.load(open(os.path.join(GOLDEN, "gqa_decode_step_jax_examples.json")))["cases"][1]
+    q = torch.tensor(c["query"], dtype=torch.float32)
+    kc = torch.tensor(c["key_cache"], dtype=torch.float32).to(torch.bfloat16)   # small integers: exact
+    vc = torch.tensor(c["value_cache"], dtype=torch.float32).to(torch.bfloat16)
+    L = torch.tensor(c["lengths"], dtype=torch.int32)
+    ref = oracle.attend(q.numpy(), "f32", np_of(kc), np_of(vc), "bf16", L.numpy(), "BSHD", 4, 2)
+    out = g.attend(q.to(DEV), kc.to(DEV), vc.to(DEV), L.to(DEV), layout="BSHD")
+    torch.cuda.synchronize()
+    assert out.dtype == torch.float32
+    assert_close(out, ref, "f32", "bf16 caches")
+
+
+# ---------------------------------------------------------------------------
+# The tiny workload, whole.
+# ---------------------------------------------------------------------------
+def test_tiny_workload_step(g):
+    check_step_full(g, W.WORKLOADS["tiny"])
+
+
+# ---------------------------------------------------------------------------
+# Shapes that span several tiles and splits with ragged tails, every head
+# width class, group sizes from 1 to 64, both layouts and storage types.
+# ---------------------------------------------------------------------------
+SHAPES = [
+    # B, Hq, Hkv, D, S, layout, kv, qo, num_splits
+    (2, 4, 2, 1, 37, "BHSD", "f32", "f32", 0),
+    (2, 6, 3, 2, 50, "BSHD", "f32", "f32", 3),
+    (3, 4, 4, 3, 41, "BHSD", "bf16", "bf16", 2),
+    (2, 8, 2, 4, 300, "BSHD", "f32", "f32", 0),
+    (2, 8, 2, 8, 333, "BHSD", "bf16", "f32", 4),
+    (1, 12, 1, 16, 777, "BHSD", "f32", "bf16", 0),
+    (2, 16, 2, 24, 513, "BSHD", "bf16", "bf16", 5),
+    (2, 8, 8, 64, 1000, "BHSD", "f32", "f32", 0),
+    (3, 16, 2, 100, 650, "BSHD", "f32", "f32", 2),
+    (3, 32, 8, 128, 1500, "BHSD", "bf16", "bf16", 0),
+    (2, 24, 2, 128, 1030, "BSHD", "bf16", "bf16", 3),
+    (2, 16, 4, 128, 700, "BHSD", "f32", "f32", 0),
+    (2, 16, 1, 128, 900, "BHSD", "bf16", "bf16", 0),
+    (2, 64, 1, 128, 600, "BHSD", "bf16", "bf16", 0),
+    (2, 128, 2, 128, 300, "BSHD", "bf16", "bf16", 2),
+    (2, 8, 2, 256, 400, "BHSD", "bf16", "bf16", 0),
+    (2, 4, 1, 256, 259, "BSHD", "f32", "f32", 2),
+    (2, 8, 2, 136, 200, "BHSD", "bf16", "bf16", 0),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"B{s[0]}Hq{s[1]}Hkv{s[2]}D{s[3]}S{s[4]}{s[5]}{s[6]}{s[7]}n{s[8]}"
+                                               for s in SHAPES])
+def test_step_shapes(g, shape):
+    B, Hq, Hkv, D, S, layout, kv, qo, ns = shape
+    w = W.custom(B, Hq, Hkv, D, S, layout, kv, qo, seed=B * 1000 + D, stale="pm:1000")
+    gen = torch.Generator().manual_seed(S)
+    L = torch.randint(0, S, (B,), generator=gen, dtype=torch.int32)
+    L[0] = S - 1                       # a full cache
+    if B > 2:
+        L[1] = 0                       # only the new token
+    check_step_full(g, w, lengths=L, num_splits=ns)
+
+
+@pytest.mark.parametrize("shape", SHAPES[::3], ids=[f"B{s[0]}Hq{s[1]}D{s[3]}S{s[4]}{s[5]}{s[6]}" for s in SHAPES[::3]])
+def test_attend_shapes(g, shape):
+    B, Hq, Hkv, D, S, layout, kv, qo, ns = shape
+    w = W.custom(B, Hq, Hkv, D, S, layout, kv, qo, seed=7 + D, stale="pm:1000")
+    gen = torch.Generator().manual_seed(S + 1)
+    n = torch.randint(1, S + 1, (B,), generator=gen, dtype=torch.int32)
+    n[0] = S
+    inp = W.make_inputs(w, DEV, lengths=n)
+    say(f"attend {shape}")
+    ref = oracle.attend(np_of(inp["q"]), qo, np_of(inp["k_cache"]), np_of(inp["v_cache"]), kv, n.numpy(), layout,
+                        Hq, Hkv)
+    out = g.attend(inp["q"], inp["k_cache"], inp["v_cache"], inp["lengths"], layout=layout, num_splits=ns)
+    torch.cuda.synchronize()
+    assert_close(out, ref, qo, "attend")
+
+
+@pytest.mark.parametrize("ns", [1, 2, 3, 7, 0])
+def test_split_count_does_not_change_the_result(g, ns):
+    w = W.custom(3, 16, 4, 128, 2100, "BHSD", "bf16", "bf16", seed=31, stale="pm:10000")
+    L = torch.tensor([2099, 1, 1234], dtype=torch.int32)
+    check_step_full(g, w, lengths=L, num_splits=ns)
+
+
+# ---------------------------------------------------------------------------
+# Properties the method fixes.
+# ---------------------------------------------------------------------------
+def test_stale_slots_never_read(g):
+    """Refilling every slot past the attended range with NaN/Inf leaves the output bitwise equal."""
+    w = W.custom(4, 32, 8, 128, 1200, "BSHD", "bf16", "bf16", seed=41, stale="pm:10000")
+    L = torch.tensor([5, 1199, 640, 0], dtype=torch.int32)
+    inp = W.make_inputs(w, DEV, lengths=L)
+    keep = {k: v.clone() for k, v in inp.items()}
+    say("stale NaN refill")
+    out1 = run_step(g, inp, w)
+    slot = torch.arange(w.capacity, device=DEV)
+    stale = slot[None, :] > L.to(DEV)[:, None]            # beyond the appended slot
+    stale = stale[:, :, None, None]                        # (B, S, 1, 1) for BSHD
+    for name, fill in (("k_cache", float("nan")), ("v_cache", float("inf"))):
+        keep[name] = torch.where(stale, torch.tensor(fill, dtype=torch.bfloat16, device=DEV), keep[name])
+    out2 = run_step(g, keep, w)
+    torch.cuda.synchronize()
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    assert torch.isfinite(out1.float()).all()
+
+
+def test_step_from_empty_cache_returns_new_value(g):
+    for kv, qo in (("f32", "f32"), ("bf16", "bf16")):
+        w = W.custom(3, 16, 4, 128, 64, "BHSD", kv, qo, seed=5, stale="const:1000")
+        inp = W.make_inputs(w, DEV, lengths=torch.zeros(3, dtype=torch.int32))
+        out = run_step(g, inp, w)
+        torch.cuda.synchronize()
+        expect = inp["v_new"].repeat_interleave(4, dim=1).to(out.dtype)
+        assert torch.equal(out, expect)
+
+
+def test_deterministic(g):
+    w = W.custom(8, 32, 8, 128, 4097, "BHSD", "bf16", "bf16", seed=2)
+    L = torch.full((8,), 4096, dtype=torch.int32)
+    a = W.make_inputs(w, DEV, lengths=L)
+    b = {k: v.clone() for k, v in a.items()}
+    o1 = run_step(g, a, w)
+    o2 = run_step(g, b, w)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_out_of_contract_lengths_are_memory_safe(g):
+    """Append skips lengths outside [0, S); attend clamps the count to [0, S]."""
+    w = W.custom(4, 8, 2, 64, 32, "BHSD", "f32", "f32", seed=9)
+    L = torch.tensor([-1, 32, 40, 3], dtype=torch.int32)
+    inp = W.make_inputs(w, DEV, lengths=torch.tensor([0, 0, 0, 3], dtype=torch.int32))
+    before_k = inp["k_cache"].clone()
+    g.append(inp["k_cache"], inp["v_cache"], inp["k_new"], inp["v_new"], L.to(DEV), layout="BHSD")
+    torch.cuda.synchronize()
+    diff = (inp["k_cache"] != before_k).any(dim=-1)        # (B, Hkv, S)
+    assert not diff[:3].any()                               # skipped sequences untouched
+    assert diff[3, :, 3].all() and diff[3].sum() == 2
+    ref = g.attend(inp["q"], inp["k_cache"], inp["v_cache"], torch.tensor([5, 32, 32, 3], dtype=torch.int32,
+                                                                            device=DEV))
+    out = g.attend(inp["q"], inp["k_cache"], inp["v_cache"], torch.tensor([0, 99, 33, -7], dtype=torch.int32,
+                                                                            device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(out[0], torch.zeros_like(out[0])) and torch.equal(out[3], torch.zeros_like(out[3]))
+    assert torch.equal(out[1], ref[1]) and torch.equal(out[2], ref[2])   # counts past S clamp to S = 32
+
+
+def test_empty_batch(g):
+    q = torch.empty(0, 8, 128, dtype=torch.bfloat16, device=DEV)
+    kc = torch.empty(0, 2, 16, 128, dtype=torch.bfloat16, device=DEV)
+    L = torch.empty(0, dtype=torch.int32, device=DEV)
+    out = g.attend(q, kc, kc.clone(), L)
+    assert out.shape == (0, 8, 128)
+
+
+def test_graph_capture_replays(g):
+    """The step has no host sync and no memset: it can be captured and replayed."""
+    w = W.custom(4, 32, 8, 128, 2048, "BHSD", "bf16", "bf16", seed=77)
+    L = torch.tensor([2047, 100, 1500, 7], dtype=torch.int32)
+    inp = W.make_inputs(w, DEV, lengths=L)
+    desc = g.desc_for(inp["q"], inp["k_cache"], "BHSD")
+    ws = torch.empty(max(g.workspace_size(desc), 1), dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(inp["q"])
+    eager = run_step(g, {k: v.clone() for k, v in inp.items()}, w)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run_step(g, inp, w)                                 # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        g.step(inp["q"], inp["k_cache"], inp["v_cache"], inp["k_new"], inp["v_new"], inp["lengths"],
+               out=out, workspace=ws)
+    for r in range(4):
+        out.zero_()
+        inp["q"].mul_(1.0)                                  # eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {r}"
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads in the launch configuration the benchmark times:
+# sampled (b, query head) outputs against the oracle computed one by one,
+# and the append checked on every byte of the caches.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["llama3_8b_layer", "ragged_batch", "long_context", "large_group"])
+def test_full_size_workload(g, name):
+    w = W.WORKLOADS[name]
+    inp = W.make_inputs(w, DEV)
+    L = inp["lengths"].cpu().numpy()
+    desc = g.desc_for(inp["q"], inp["k_cache"], w.layout)
+    say(f"full size {name}: plan {g.get_plan(desc)}")
+    k_before, v_before = inp["k_cache"].clone(), inp["v_cache"].clone()
+    out = run_step(g, inp, w)
+    torch.cuda.synchronize()
+    # append: slot L[b] of every kv-head holds the new bits; nothing else changed
+    bidx = torch.arange(w.B, device=DEV)
+    Ld = inp["lengths"].long()
+    for before, after, new in ((k_before, inp["k_cache"], inp["k_new"]), (v_before, inp["v_cache"], inp["v_new"])):
+        if w.layout == "BHSD":
+            assert torch.equal(after[bidx, :, Ld].view(torch.int16), new.view(torch.int16))
+            after[bidx, :, Ld] = before[bidx, :, Ld]
+        else:
+            assert torch.equal(after[bidx, Ld].view(torch.int16), new.view(torch.int16))
+            after[bidx, Ld] = before[bidx, Ld]
+        assert torch.equal(after.view(torch.int16), before.view(torch.int16))
+    del k_before, v_before
+    # put the new bits back for the oracle's reads
+    if w.layout == "BHSD":
+        inp["k_cache"][bidx, :, Ld] = inp["k_new"]
+        inp["v_cache"][bidx, :, Ld] = inp["v_new"]
+    else:
+        inp["k_cache"][bidx, Ld] = inp["k_new"]
+        inp["v_cache"][bidx, Ld] = inp["v_new"]
+    rng = np.random.default_rng(w.seed)
+    G = w.Hq // w.Hkv
+    samples = {(0, 0), (w.B - 1, w.Hq - 1)} | {(int(rng.integers(w.B)), int(rng.integers(w.Hq))) for _ in range(10)}
+    q_np = np_of(inp["q"])
+    got = out.float().cpu().double().numpy()
+    for b, hq in sorted(samples):
+        h = hq // G
+        n = int(L[b]) + 1
+        if w.layout == "BHSD":
+            Kt, Vt = inp["k_cache"][b, h, :n], inp["v_cache"][b, h, :n]
+        else:
+            Kt, Vt = inp["k_cache"][b, :n, h], inp["v_cache"][b, :n, h]
+        K = oracle.decode(np_of(Kt), w.kv_dtype)
+        V = oracle.decode(np_of(Vt), w.kv_dtype)
+        ref = oracle.attend_one(oracle.decode(q_np[b, hq], w.qo_dtype), K, V)
+        tol = TOL[w.qo_dtype]
+        assert np.all(np.abs(got[b, hq] - ref) <= tol + tol * np.abs(ref)), (b, hq, np.abs(got[b, hq] - ref).max())
+    assert torch.isfinite(out.float()).all()

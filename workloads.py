@@ -138,3 +138,11 @@ def algorithmic_bytes(w: Workload, lengths) -> int:
     n = np.asarray(lengths, dtype=np.int64) + 1
     kv_read = int(n.sum()) * w.Hkv * w.D * 2 * e_kv
     return kv_read + 2 * w.B * w.Hq * w.D * e_qo + 2 * w.B * w.Hkv * w.D * e_kv
+
+
+def custom(B, Hq, Hkv, D, capacity, layout="BHSD", kv_dtype="bf16", qo_dtype="bf16", seed=0, stale="none",
+           key_scale=1.0) -> Workload:
+    """A workload of any shape (lengths are passed to ``make_inputs``)."""
+    return Workload(f"custom{seed}", seed, B=B, Hq=Hq, Hkv=Hkv, D=D, capacity=capacity, layout=layout,
+                    kv_dtype=kv_dtype, qo_dtype=qo_dtype, len_lo=0, len_hi=max(capacity - 1, 0),
+                    key_scale=key_scale, stale=stale)
