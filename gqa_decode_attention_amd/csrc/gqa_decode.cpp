@@ -60,7 +60,7 @@ int32_t choose_kernel(const gqa_decode_desc_t* d) {
   const int32_t G = d->num_q_heads / d->num_kv_heads;
   const bool bf16 = d->kv_dtype == GQA_BF16 && d->qo_dtype == GQA_BF16;
   if (bf16 && d->head_dim == 128 && G <= 16 && kHaveMfmaQk) return GQA_KERNEL_MFMA_QK;
-  if (bf16 && d->head_dim == 128 && G > 16 && kHaveMfmaAll) return GQA_KERNEL_MFMA_ALL;
+  if (bf16 && d->head_dim == 128 && G > 16 && G <= 64 && kHaveMfmaAll) return GQA_KERNEL_MFMA_ALL;
   return GQA_KERNEL_GENERIC;
 }
 

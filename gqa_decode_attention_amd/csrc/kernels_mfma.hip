@@ -1,13 +1,515 @@
-// Matrix-core (MFMA) kernels of the GQA decode step for gfx950.
+// Matrix-core (MFMA) attention kernels of the GQA decode step for gfx950,
+// bf16 storage, head width 128.
+//
+// What is computed is the JAX "Grouped-Query Decode Step" page's definition
+// (query head h reads cache head floor(h/G); s_j = q.K_j/sqrt(D) over the
+// valid slots; softmax; o = sum_j w_j V_j) with the step of the "KV cache
+// decode step" page (the new token's key/value are attended and appended at
+// slot lengths[b]).  The softmax is evaluated online over 16-slot tiles
+// (running maximum m, denominator l, unnormalised output o, rescaled by
+// 2^(m_old - m_new) when the maximum grows); splits of the token axis leave
+// (m, l, o) partials that the combine kernel merges.
+//
+// Kernel MFMA_QK (G <= 16).  One workgroup = 4 waves = one (sequence,
+// kv-head, split); each wave walks its own run of 16-slot tiles.  Per tile:
+//   scores  S(16 slots x 16 heads) = K_tile(16 x 128) . Q^T(128 x 16) as four
+//           v_mfma_f32_16x16x32_bf16.  Lane l = 16*r + c loads 16-byte pieces of
+//           cache row t0 + c straight into the A operand (bytes 16r + 64kk of
+//           the row for MFMA kk, so one instruction covers 16 rows x 64
+//           contiguous bytes); the B operand holds query head c at the same
+//           head-width positions (zero for c >= G).  Lane l then holds the
+//           scores of slots t0 + 4r .. t0 + 4r + 3 for head c.
+//   softmax the tile maximum per head is a max over the lane's 4 slots and
+//           the 4 rows of lanes (two cross-row exchanges); exp2 with log2(e)
+//           folded into the scale.
+//   V sum   on the vector ALU in float32: lane l loads slots t0 + 4r + i,
+//           elements 8c .. 8c + 7 (each load instruction covers 4 full rows),
+//           and takes the weight of (slot, head g) from lane 16r + g with a DPP
+//           row broadcast.
+// Scores are exact products of bf16 values summed in float32; weights and sums
+// stay float32 (bf16 only for the stored output).
+//
+// Fused step: the new token (slot lengths[b]) is not read from the cache; the
+// workgroup whose split holds it runs one extra tile whose only valid row comes
+// from k_new/v_new, and writes those bits into the cache slot.  No other
+// workgroup reads that slot, so the write cannot race a read.
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
 namespace gqa {
 
-const bool kHaveMfmaQk = false;
-const bool kHaveMfmaAll = false;
+const bool kHaveMfmaQk = true;
+const bool kHaveMfmaAll = true;
 
-hipError_t launch_attend_mfma_qk(const AttnArgs&, const Plan&, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_attend_mfma_all(const AttnArgs&, const Plan&, hipStream_t) { return hipErrorNotSupported; }
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kNegInfM = -__builtin_inff();
+constexpr int kD = 128;
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// Value of lane (16 * row + G) of `x`, in every lane of the same 16-lane row.
+template <int G>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + G, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+
+__device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Online-softmax state of one wave: lane (r, c) keeps m (running max, log2
+// units) and l (its own slots' share of the denominator) for head c, and the
+// unnormalised output of head g at elements 8c .. 8c + 7 summed over its
+// row's slots.
+template <int GP>
+struct WaveState {
+  float m, l;
+  float acc[GP][8];
+};
+
+// One 16-slot tile.  kf: this lane's A-operand pieces; vf[i]: slot t0 + 4r + i,
+// elements 8c..8c+7; valid: number of valid slots in the tile (from t0).
+template <int GP>
+__device__ __forceinline__ void tile_update(WaveState<GP>& st, const u32x4 (&qf)[4], const u32x4 (&kf)[4],
+                                            const u32x4 (&vf)[4], int valid, int r, float scale_log2) {
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) s = mfma_16x16x32(kf[kk], qf[kk], s);
+  float sv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sv[i] = (4 * r + i < valid) ? s[i] * scale_log2 : kNegInfM;
+  float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(st.m, mx);
+  const float alpha = fast_exp2(st.m - m_new);  // 0 on the first tile
+  float p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sv[i] - m_new);
+  st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+  st.m = m_new;
+  if (__any(alpha != 1.0f)) {  // the running maximum moved for some head
+    static_for<0, GP>([&](auto gi) {
+      constexpr int g = decltype(gi)::value;
+      const float ag = row_bcast<g>(alpha);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) st.acc[g][e] *= ag;
+    });
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float v[8];
+    widen16<1>(vf[i], v);
+    static_for<0, GP>([&](auto gi) {
+      constexpr int g = decltype(gi)::value;
+      const float pg = row_bcast<g>(p[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) st.acc[g][e] = fmaf(pg, v[e], st.acc[g][e]);
+    });
+  }
+}
+
+template <int GP>
+__global__ __launch_bounds__(256) void attend_mfma_qk_kernel(AttnArgs a) {
+  __shared__ float sm_o[4][GP][kD];
+  __shared__ float sm_m[4][GP];
+  __shared__ float sm_l[4][GP];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r = lane >> 4;
+  const int c = lane & 15;
+
+  int x = blockIdx.x;
+  const int split = x % a.nsplit;
+  x /= a.nsplit;
+  const int h = x % a.Hkv;
+  const int b = x / a.Hkv;
+  const int G = a.G;
+
+  const int L = a.lengths[b];
+  int n = L + a.len_offset;
+  n = n < 0 ? 0 : (n > a.S ? a.S : n);
+  const int t_begin = split * a.split_tokens;
+  const int t_end = min(t_begin + a.split_tokens, n);
+  if (a.nsplit > 1 && t_begin >= n) return;  // inactive split: the combine pass skips it
+
+  // Fused step: slot L holds the new token; it is taken from k_new/v_new.
+  const bool own_new = a.k_new != nullptr && L >= t_begin && L < t_end;
+  const int t_cache_end = own_new ? L : t_end;
+
+  // This wave's run of slots: a multiple of 16 per wave.
+  const int per_wave = ((a.split_tokens + 63) / 64) * 16;
+  const int w0 = t_begin + wave * per_wave;
+  const int w1 = min(w0 + per_wave, t_cache_end);
+
+  const int64_t qrow = ((int64_t)b * a.Hq + (int64_t)h * G + c) * kD;
+  u32x4 qf[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    qf[kk] = (c < G) ? load16(reinterpret_cast<const uint16_t*>(a.q) + qrow + 32 * kk + 8 * r) : u32x4{0, 0, 0, 0};
+  }
+
+  WaveState<GP> st;
+  st.m = kNegInfM;
+  st.l = 0.f;
+#pragma unroll
+  for (int g = 0; g < GP; ++g)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st.acc[g][e] = 0.f;
+
+  const int64_t base = (int64_t)b * a.sb + (int64_t)h * a.sh;
+  const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.k_cache) + base;
+  const uint16_t* vb = reinterpret_cast<const uint16_t*>(a.v_cache) + base;
+  const int64_t rs = a.st;  // elements between consecutive slots
+
+  // Rows past the wave's last valid slot are clamped to that slot: every load
+  // is unconditional (so the next tile's loads stay in flight during this
+  // tile's math), nothing at or beyond the valid length is ever read, and the
+  // clamped rows get score -inf, i.e. weight exactly 0, on finite values.
+  u32x4 kf[4], vf[4];
+  auto load_tile = [&](int t0, u32x4 (&k)[4], u32x4 (&v)[4]) {
+    const int rk = min(t0 + c, w1 - 1);
+    const uint16_t* p = kb + (int64_t)rk * rs + 8 * r;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) k[kk] = load_nt16(p + 32 * kk);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rv = min(t0 + 4 * r + i, w1 - 1);
+      v[i] = load_nt16(vb + (int64_t)rv * rs + 8 * c);
+    }
+  };
+
+  if (w0 < w1) {
+    load_tile(w0, kf, vf);
+    for (int t0 = w0; t0 < w1; t0 += 16) {
+      u32x4 kn[4], vn[4];
+      load_tile(t0 + 16, kn, vn);  // prefetch; past w1 it re-reads row w1 - 1
+      tile_update<GP>(st, qf, kf, vf, w1 - t0, r, a.scale_log2);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        kf[kk] = kn[kk];
+        vf[kk] = vn[kk];
+      }
+    }
+  }
+
+  if (own_new && wave == 0) {
+    const int64_t nrow = ((int64_t)b * a.Hkv + h) * kD;
+    const uint16_t* knp = reinterpret_cast<const uint16_t*>(a.k_new) + nrow;
+    const uint16_t* vnp = reinterpret_cast<const uint16_t*>(a.v_new) + nrow;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) kf[kk] = (c == 0) ? load16(knp + 32 * kk + 8 * r) : u32x4{0, 0, 0, 0};
+    vf[0] = (r == 0) ? load16(vnp + 8 * c) : u32x4{0, 0, 0, 0};
+    vf[1] = vf[2] = vf[3] = u32x4{0, 0, 0, 0};
+    tile_update<GP>(st, qf, kf, vf, 1, r, a.scale_log2);
+    uint16_t* kw = reinterpret_cast<uint16_t*>(a.k_cache_w) + base + (int64_t)L * rs;
+    uint16_t* vw = reinterpret_cast<uint16_t*>(a.v_cache_w) + base + (int64_t)L * rs;
+    if (c == 0) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) store16(kw + 32 * kk + 8 * r, kf[kk]);
+    }
+    if (r == 0) store16(vw + 8 * c, vf[0]);
+  }
+
+  // Merge the 4 rows of lanes of each wave (disjoint slots, same running max).
+  st.l += __shfl_xor(st.l, 16);
+  st.l += __shfl_xor(st.l, 32);
+#pragma unroll
+  for (int g = 0; g < GP; ++g)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      st.acc[g][e] += __shfl_xor(st.acc[g][e], 16);
+      st.acc[g][e] += __shfl_xor(st.acc[g][e], 32);
+    }
+  if (r == 0) {
+#pragma unroll
+    for (int g = 0; g < GP; ++g)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sm_o[wave][g][8 * c + e] = st.acc[g][e];
+    if (c < GP) {
+      sm_m[wave][c] = st.m;
+      sm_l[wave][c] = st.l;
+    }
+  }
+  __syncthreads();
+
+  // Merge the 4 waves; write the output or this split's partial.
+  for (int idx = threadIdx.x; idx < G * kD; idx += 256) {
+    const int g = idx / kD;
+    const int d = idx - g * kD;
+    float M = kNegInfM;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][g]);
+    float O = 0.f, Lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = sm_m[w][g];
+      const float sc = mw == kNegInfM ? 0.f : fast_exp2(mw - M);
+      O += sm_o[w][g][d] * sc;
+      Lsum += sm_l[w][g] * sc;
+    }
+    const int hq = h * G + g;
+    if (a.nsplit == 1) {
+      reinterpret_cast<uint16_t*>(a.out)[((int64_t)b * a.Hq + hq) * kD + d] =
+          f32_to_bf16_rne(Lsum > 0.f ? O / Lsum : 0.f);
+    } else {
+      const int64_t pi = ((int64_t)b * a.Hq + hq) * a.nsplit + split;
+      a.part_o[pi * kD + d] = O;
+      if (d == 0) {
+        a.part_m[pi] = M;
+        a.part_l[pi] = Lsum;
+      }
+    }
+  }
+}
+
+template <int GP>
+static hipError_t launch_qk_t(const AttnArgs& a, const Plan& p, hipStream_t s) {
+  AttnArgs arg = a;
+  void* params[] = {&arg};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attend_mfma_qk_kernel<GP>), dim3(p.grid), dim3(256), params,
+                         0, s);
+}
+
+hipError_t launch_attend_mfma_qk(const AttnArgs& a, const Plan& p, hipStream_t s) {
+  if (a.D != kD || a.G > 16) return hipErrorInvalidValue;
+  if (a.G <= 1) return launch_qk_t<1>(a, p, s);
+  if (a.G <= 2) return launch_qk_t<2>(a, p, s);
+  if (a.G <= 4) return launch_qk_t<4>(a, p, s);
+  if (a.G <= 8) return launch_qk_t<8>(a, p, s);
+  return launch_qk_t<16>(a, p, s);
+}
+
+// ---------------------------------------------------------------------------
+// Kernel MFMA_ALL (16 < G <= 64): scores and the V sum both on MFMA.
+//
+// One workgroup = 4 waves = one (sequence, kv-head, split).  The workgroup
+// stages 32-slot K and V tiles in LDS (double-buffered, rows padded to 288
+// bytes to spread LDS banks); wave w owns query heads 16w .. 16w + 15 and
+// reads every tile from LDS.  Per tile and wave:
+//   scores  two 16-slot halves, S^T(16 slots x 16 heads) = K(16 x 128) . Q^T,
+//           four v_mfma_f32_16x16x32_bf16 each (A operand: 16-byte LDS reads of
+//           K rows; B operand: the wave's query heads).  Lane (r, c) holds slots
+//           4r .. 4r+3 of each half for head c.
+//   softmax as in MFMA_QK, over the 32 slots.
+//   V sum   O(16 heads x 128) += P(16 x 32 slots) . V(32 x 128) as eight MFMAs
+//           (one per 16-column block).  The A operand is the weights lane (r, c)
+//           already holds (head c; slots 4r..4r+3 of the first half then of the
+//           second half, rounded to bf16); the B operand -- V transposed, 8 slots
+//           of one column per lane -- comes from two ds_read_b64_tr_b16 per
+//           block: within each 16-lane group, lane rho names the 4 elements at
+//           slot 4r + rho/4, columns 16nb + 4(rho mod 4) .. +3, and lane c
+//           receives column 16nb + c of the 4 slots.
+// The weights enter the V-sum MFMA rounded to bf16 (their sum l stays float32);
+// the accumulation is float32.
+// ---------------------------------------------------------------------------
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int kTileT = 32;    // slots per LDS tile
+constexpr int kPitch = 144;   // LDS row pitch in bf16 elements (288 bytes)
+
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)((__attribute__((address_space(3))) char*)(const_cast<uint16_t*>(p))));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+}
+
+__global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sk[2][kTileT * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t sv[2][kTileT * kPitch];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r = lane >> 4;
+  const int c = lane & 15;
+
+  int x = blockIdx.x;
+  const int split = x % a.nsplit;
+  x /= a.nsplit;
+  const int h = x % a.Hkv;
+  const int b = x / a.Hkv;
+  const int G = a.G;
+
+  const int L = a.lengths[b];
+  int n = L + a.len_offset;
+  n = n < 0 ? 0 : (n > a.S ? a.S : n);
+  const int t_begin = split * a.split_tokens;
+  const int t_end = min(t_begin + a.split_tokens, n);
+  if (a.nsplit > 1 && t_begin >= n) return;  // inactive split: the combine pass skips it
+  const bool own_new = a.k_new != nullptr && L >= t_begin && L < t_end;
+
+  const int hw = wave * 16;  // first head of this wave
+  const int64_t qrow = ((int64_t)b * a.Hq + (int64_t)h * G + hw + c) * kD;
+  u32x4 qf[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    qf[kk] = (hw + c < G) ? load16(reinterpret_cast<const uint16_t*>(a.q) + qrow + 32 * kk + 8 * r)
+                          : u32x4{0, 0, 0, 0};
+
+  float m = kNegInfM, l = 0.f;
+  f32x4 O[8];
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) O[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int64_t base = (int64_t)b * a.sb + (int64_t)h * a.sh;
+  const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.k_cache) + base;
+  const uint16_t* vb = reinterpret_cast<const uint16_t*>(a.v_cache) + base;
+  const int64_t rs = a.st;
+  const int64_t nrow = ((int64_t)b * a.Hkv + h) * kD;
+
+  // Cooperative tile load: thread t moves 16 bytes (piece t & 15) of rows
+  // t >> 4 and 16 + (t >> 4).  Rows past the split's last valid slot are
+  // clamped to it; the new token's row (fused step) comes from k_new/v_new.
+  const int prow = tid >> 4;
+  const int piece = tid & 15;
+  u32x4 kr[2], vr[2];
+  auto gload = [&](int t0) {
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2) {
+      const int rc = min(t0 + prow + 16 * q2, t_end - 1);
+      if (own_new && rc == L) {
+        kr[q2] = load16(reinterpret_cast<const uint16_t*>(a.k_new) + nrow + 8 * piece);
+        vr[q2] = load16(reinterpret_cast<const uint16_t*>(a.v_new) + nrow + 8 * piece);
+      } else {
+        kr[q2] = load_nt16(kb + (int64_t)rc * rs + 8 * piece);
+        vr[q2] = load_nt16(vb + (int64_t)rc * rs + 8 * piece);
+      }
+    }
+  };
+  auto swrite = [&](int t0, int buf) {
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2) {
+      const int row = prow + 16 * q2;
+      *reinterpret_cast<u32x4*>(&sk[buf][row * kPitch + 8 * piece]) = kr[q2];
+      *reinterpret_cast<u32x4*>(&sv[buf][row * kPitch + 8 * piece]) = vr[q2];
+      if (own_new && t0 + row == L) {  // the appended slot: write the new bits to the cache
+        store16(reinterpret_cast<uint16_t*>(a.k_cache_w) + base + (int64_t)L * rs + 8 * piece, kr[q2]);
+        store16(reinterpret_cast<uint16_t*>(a.v_cache_w) + base + (int64_t)L * rs + 8 * piece, vr[q2]);
+      }
+    }
+  };
+
+  if (t_begin < t_end) {
+    gload(t_begin);
+    swrite(t_begin, 0);
+    __syncthreads();
+    int buf = 0;
+    for (int t0 = t_begin; t0 < t_end; t0 += kTileT) {
+      const bool more = t0 + kTileT < t_end;
+      if (more) gload(t0 + kTileT);
+      const uint16_t* K = sk[buf];
+      const uint16_t* V = sv[buf];
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(&K[c * kPitch + 32 * kk + 8 * r]);
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(&K[(16 + c) * kPitch + 32 * kk + 8 * r]);
+        s0 = mfma_16x16x32(a0, qf[kk], s0);
+        s1 = mfma_16x16x32(a1, qf[kk], s1);
+      }
+      const int valid = t_end - t0;
+      float sc[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sc[i] = (4 * r + i < valid) ? s0[i] * a.scale_log2 : kNegInfM;
+        sc[4 + i] = (16 + 4 * r + i < valid) ? s1[i] * a.scale_log2 : kNegInfM;
+      }
+      float mx = sc[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - m_new);
+      float p[8], ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        p[i] = fast_exp2(sc[i] - m_new);
+        ps += p[i];
+      }
+      l = l * alpha + ps;
+      m = m_new;
+      if (__any(alpha != 1.0f)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float ai = __shfl(alpha, 4 * r + i);  // alpha of head 4r + i
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb) O[nb][i] *= ai;
+        }
+      }
+      const u32x4 pa = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                        pack_bf16x2(p[6], p[7])};
+      const int trow = 4 * r + (c >> 2);
+      const int tcol = 4 * (c & 3);
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const s16x4 lo = lds_read_tr16(&V[trow * kPitch + 16 * nb + tcol]);
+        const s16x4 hi = lds_read_tr16(&V[(16 + trow) * kPitch + 16 * nb + tcol]);
+        const u32x4 vt = {(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
+                          (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
+                          (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
+                          (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
+        O[nb] = mfma_16x16x32(pa, vt, O[nb]);
+      }
+      if (more) swrite(t0 + kTileT, buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
+    }
+  }
+
+  // Denominator and max per head: lane (r, c) holds head c; the output rows of
+  // lane (r, c) are heads 4r + i.
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hl = 4 * r + i;  // head within the wave
+    const float li = __shfl(l, hl);
+    const float mi = __shfl(m, hl);
+    if (hw + hl >= G) continue;
+    const int hq = h * G + hw + hl;
+    if (a.nsplit == 1) {
+      const float inv = li > 0.f ? 1.f / li : 0.f;
+      uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)b * a.Hq + hq) * kD;
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) o[16 * nb + c] = f32_to_bf16_rne(O[nb][i] * inv);
+    } else {
+      const int64_t pi = ((int64_t)b * a.Hq + hq) * a.nsplit + split;
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) a.part_o[pi * kD + 16 * nb + c] = O[nb][i];
+      if (c == 0) {
+        a.part_m[pi] = mi;
+        a.part_l[pi] = li;
+      }
+    }
+  }
+}
+
+hipError_t launch_attend_mfma_all(const AttnArgs& a, const Plan& p, hipStream_t s) {
+  if (a.D != kD || a.G > 64) return hipErrorInvalidValue;
+  AttnArgs arg = a;
+  void* params[] = {&arg};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attend_mfma_all_kernel), dim3(p.grid), dim3(256), params, 0,
+                         s);
+}
 
 }  // namespace gqa

@@ -167,6 +167,10 @@ SHAPES = [
     (2, 8, 2, 256, 400, "BHSD", "bf16", "bf16", 0),
     (2, 4, 1, 256, 259, "BSHD", "f32", "f32", 2),
     (2, 8, 2, 136, 200, "BHSD", "bf16", "bf16", 0),
+    (2, 48, 2, 128, 700, "BHSD", "bf16", "bf16", 0),     # G = 24: a partly used head block
+    (3, 40, 1, 128, 333, "BSHD", "bf16", "bf16", 3),     # G = 40
+    (2, 32, 1, 128, 1000, "BSHD", "bf16", "bf16", 0),    # G = 32
+    (2, 80, 1, 128, 200, "BHSD", "bf16", "bf16", 0),     # G = 80: beyond the matrix-core kernels
 ]
 
 
@@ -199,9 +203,10 @@ def test_attend_shapes(g, shape):
     assert_close(out, ref, qo, "attend")
 
 
+@pytest.mark.parametrize("G", [4, 64])
 @pytest.mark.parametrize("ns", [1, 2, 3, 7, 0])
-def test_split_count_does_not_change_the_result(g, ns):
-    w = W.custom(3, 16, 4, 128, 2100, "BHSD", "bf16", "bf16", seed=31, stale="pm:10000")
+def test_split_count_does_not_change_the_result(g, ns, G):
+    w = W.custom(3, 4 * G, 4, 128, 2100, "BHSD", "bf16", "bf16", seed=31, stale="pm:10000")
     L = torch.tensor([2099, 1, 1234], dtype=torch.int32)
     check_step_full(g, w, lengths=L, num_splits=ns)
 
