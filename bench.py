@@ -54,9 +54,10 @@ def traffic_from_profiles(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, inp, budget_s=15.0):
-    """The float64 oracle on this host's cores, on a bounded sample: whole
-    sequences of the same inputs, as many as fit in about budget_s seconds."""
+def cpu_baseline(w, inp, budget_s=12.0):
+    """The float64 oracle on this host's cores over a bounded sample of the same
+    inputs: whole sequences (all query heads), repeated until about budget_s
+    seconds of CPU work, scaled to GB/s with the same byte formula."""
     import numpy as np
     import oracle
     import workloads as W
@@ -67,33 +68,43 @@ def cpu_baseline(w, inp, budget_s=15.0):
         threads = 1
     L = inp["lengths"].cpu().numpy()
 
-    def run(bs):
-        sl = slice(bs[0], bs[1])
-        q = W.to_numpy_storage(inp["q"][sl])
-        kc = W.to_numpy_storage(inp["k_cache"][sl])
-        vc = W.to_numpy_storage(inp["v_cache"][sl])
-        kn = W.to_numpy_storage(inp["k_new"][sl])
-        vn = W.to_numpy_storage(inp["v_new"][sl])
+    def host(nb):
+        return {k: W.to_numpy_storage(inp[k][:nb]) for k in ("q", "k_cache", "v_cache", "k_new", "v_new")}
+
+    def run(st, nb):
         t0 = time.perf_counter()
-        oracle.step(q, w.qo_dtype, kc, vc, kn, vn, w.kv_dtype, L[sl], w.layout, w.Hq, w.Hkv)
+        oracle.step(st["q"], w.qo_dtype, st["k_cache"], st["v_cache"], st["k_new"], st["v_new"], w.kv_dtype, L[:nb],
+                    w.layout, w.Hq, w.Hkv)
         return time.perf_counter() - t0
 
-    t1 = run((0, 1))
-    nb = int(max(1, min(w.B, budget_s / max(t1, 1e-6))))
-    if w.name == "tiny":
-        reps = max(1, int(budget_s / 10 / max(t1, 1e-6)))
-        t = sum(run((0, w.B)) for _ in range(min(reps, 1000)))
-        nbytes = W.algorithmic_bytes(w, L) * min(reps, 1000)
-        sample = f"{min(reps, 1000)} whole steps"
-    else:
-        t = run((0, nb)) if nb > 1 else t1
-        sub = W.Workload(**{**w.__dict__, "B": nb})
-        nbytes = W.algorithmic_bytes(sub, L[:nb])
-        sample = f"oracle.step over sequences 0..{nb - 1} of {w.B} (all {w.Hq} query heads), same inputs"
+    st1 = host(1)
+    t1 = run(st1, 1)                      # one sequence, to size the sample
+    nb = int(max(1, min(w.B, budget_s / max(t1, 1e-9))))
+    st = host(nb)
+    reps, t = 0, 0.0
+    while t < budget_s and reps < 100000:
+        t += run(st, nb)
+        reps += 1
+    sub = W.Workload(**{**w.__dict__, "B": nb})
+    nbytes = W.algorithmic_bytes(sub, L[:nb]) * reps
     gbs = nbytes / t / 1e9
+    sample = (f"oracle.step over sequences 0..{nb - 1} of {w.B} (all {w.Hq} query heads) of the same inputs, "
+              f"{reps} repetition(s), {t:.1f} s")
     return {"value": round(gbs, 6), "unit": "GB/s", "cores": threads, "kind": "oracle", "sample": sample,
-            "seconds": round(t, 3), "steps_per_sec_equiv": round(gbs * 1e9 / W.algorithmic_bytes(w, L), 6),
+            "steps_per_sec_equiv": round(gbs * 1e9 / W.algorithmic_bytes(w, L), 6),
             "host_cpus": os.cpu_count(), "affinity": len(os.sched_getaffinity(0))}
+
+
+def calibration_copy(mib: int, reps: int = 5):
+    """A plain device-to-device copy of known size, for scaling the FETCH_SIZE /
+    WRITE_SIZE counters of a profile run: each launch reads and writes mib MiB."""
+    import torch
+    src = torch.ones(mib << 18, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes_per_launch": mib << 20, "launches": reps}), flush=True)
 
 
 def main():
@@ -104,6 +115,8 @@ def main():
     ap.add_argument("--workload", default="llama3_8b_layer")
     ap.add_argument("--num-splits", type=int, default=0, help="0 = the library's plan")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="only run a plain copy of this many MiB (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -117,6 +130,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.calibration_copy_mib > 0:
+        calibration_copy(args.calibration_copy_mib)
+        return
     g.lib()
     w = W.WORKLOADS[args.workload]
     dev = "cuda"
@@ -124,7 +140,9 @@ def main():
     L = inp["lengths"].cpu().numpy()
     nbytes = W.algorithmic_bytes(w, L)
     kv_bytes = 2 * inp["k_cache"].numel() * inp["k_cache"].element_size()
-    R = max(1, math.ceil(3 * MALL_BYTES / kv_bytes))
+    # Rotate over R cache copies so one rotation touches over 3x the Infinity
+    # Cache; a workload too small to matter (16 copies would still fit) uses one.
+    R = min(16, math.ceil(3 * MALL_BYTES / kv_bytes)) if 16 * kv_bytes >= MALL_BYTES else 1
     caches = [(inp["k_cache"], inp["v_cache"])] + [(inp["k_cache"].clone(), inp["v_cache"].clone())
                                                     for _ in range(R - 1)]
     desc = g.desc_for(inp["q"], inp["k_cache"], w.layout, args.num_splits)

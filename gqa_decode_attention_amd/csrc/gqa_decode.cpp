@@ -80,14 +80,16 @@ gqa_status_t make_plan(const gqa_decode_desc_t* d, Plan* p) {
     const int64_t ns = std::min<int64_t>(d->num_splits, S);
     split_tokens = (S + ns - 1) / ns;
   } else {
-    // Enough workgroups to fill 256 CUs several times over, but never splits
-    // so short that the partials (D + 2 floats per head) cost a visible share
-    // of the K/V bytes.
-    const int64_t want = std::max<int64_t>(1, (2048 + units - 1) / units);
-    split_tokens = (S + want - 1) / want;
-    split_tokens = ((split_tokens + 63) / 64) * 64;
-    split_tokens = std::max<int64_t>(split_tokens, 256);
+    // About three workgroups per CU (768 on 256 CUs), the resident count of the
+    // vector/MFMA_QK kernels; for large groups each split's partial (G rows of
+    // D + 2 floats) is as big as G/2 K/V rows, so those get half as many.
+    // Never splits shorter than 256 slots, and equal splits.
+    const int64_t target = p->kernel == GQA_KERNEL_MFMA_ALL ? 384 : 768;
+    int64_t ns = std::max<int64_t>(1, (target + units / 2) / units);
+    ns = std::min<int64_t>(ns, std::max<int64_t>(1, S / 256));
+    split_tokens = (S + ns - 1) / ns;
   }
+  split_tokens = std::max<int64_t>(split_tokens, (S + kMaxSplits - 1) / kMaxSplits);
   if (split_tokens >= S) split_tokens = S;
   const int64_t nsplit = (S + split_tokens - 1) / split_tokens;
   p->split_tokens = (int32_t)split_tokens;

@@ -49,7 +49,8 @@ struct Plan {
 extern const bool kHaveMfmaQk;
 extern const bool kHaveMfmaAll;
 
-constexpr int kNumCUs = 256;          // MI355X: 8 XCDs x 32 CUs
+constexpr int kNumCUs = 256;
+constexpr int kMaxSplits = 64;        // one lane per split in the combine pass          // MI355X: 8 XCDs x 32 CUs
 constexpr int kGenericHeadChunk = 8;  // query heads per workgroup in the generic kernel
 constexpr int kBlock = 256;
 

@@ -103,7 +103,10 @@ __global__ __launch_bounds__(256) void attend_generic_kernel(AttnArgs a) {
   n = n < 0 ? 0 : (n > a.S ? a.S : n);
   const int t_begin = split * a.split_tokens;
   const int t_end = min(t_begin + a.split_tokens, n);
-  if (a.nsplit > 1 && t_begin >= n) return;  // inactive split: the combine pass skips it
+  // Splits holding valid slots.  A lone active split (or split 0 when n = 0)
+  // writes the output itself and the combine pass leaves that sequence alone.
+  const int nact = n == 0 ? 0 : min(a.nsplit, (n + a.split_tokens - 1) / a.split_tokens);
+  if (split >= max(nact, 1)) return;
 
   const int64_t qrow0 = ((int64_t)b * a.Hq + (int64_t)h * a.G + g0) * D;
   float qv[GC][EPL];
@@ -219,7 +222,7 @@ __global__ __launch_bounds__(256) void attend_generic_kernel(AttnArgs a) {
       L += sm_l[w][g] * sc;
     }
     const int hq = h * a.G + g0 + g;
-    if (a.nsplit == 1) {
+    if (nact <= 1) {
       Store<QO>::store1(a.out, ((int64_t)b * a.Hq + hq) * D + d, L > 0.f ? O / L : 0.f);
     } else {
       const int64_t pi = ((int64_t)b * a.Hq + hq) * a.nsplit + split;
@@ -270,39 +273,66 @@ hipError_t launch_attend_generic(const AttnArgs& a, const Plan& p, int vec_path,
 }
 
 // ---------------------------------------------------------------------------
-// Combine: one workgroup per (b, query head) merges the active splits.
+// Combine: one wave per (b, query head), four per workgroup.  Lane i holds
+// split i's maximum and denominator (at most 64 splits), so the merged maximum
+// M, the weights 2^(m_i - M) and the merged denominator are wave reductions;
+// each lane then sums up to four output columns over the active splits with
+// independent loads.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
 template <int QO>
 __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
-  const int bh = blockIdx.x;  // b * Hq + hq
-  const int b = bh / a.Hq;
+  const int lane = threadIdx.x & 63;
+  const int64_t bh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // b * Hq + hq
+  if (bh >= (int64_t)a.B * a.Hq) return;  // whole waves only; no workgroup barrier follows
+  const int b = (int)(bh / a.Hq);
   int n = a.lengths[b] + a.len_offset;
   n = n < 0 ? 0 : (n > a.S ? a.S : n);
-  int nact = n == 0 ? 0 : (n + a.split_tokens - 1) / a.split_tokens;
-  nact = min(nact, a.nsplit);
-  const int64_t pbase = (int64_t)bh * a.nsplit;
-  float M = kNegInf;
-  for (int i = 0; i < nact; ++i) M = fmaxf(M, a.part_m[pbase + i]);
-  for (int d = threadIdx.x; d < a.D; d += blockDim.x) {
-    float O = 0.f, L = 0.f;
-    for (int i = 0; i < nact; ++i) {
-      const float w = fast_exp2(a.part_m[pbase + i] - M);
-      L = fmaf(w, a.part_l[pbase + i], L);
-      O = fmaf(w, a.part_o[(pbase + i) * a.D + d], O);
+  const int nact = n == 0 ? 0 : min(a.nsplit, (n + a.split_tokens - 1) / a.split_tokens);
+  if (nact <= 1) return;  // the attention pass wrote this sequence's output itself
+  const int64_t pbase = bh * a.nsplit;
+  const float mi = lane < nact ? a.part_m[pbase + lane] : kNegInf;
+  const float li = lane < nact ? a.part_l[pbase + lane] : 0.f;
+  const float M = wave_max(mi);
+  const float wi = lane < nact ? fast_exp2(mi - M) : 0.f;
+  const float L = wave_sum(wi * li);
+  const int D = a.D;
+  float O[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int i = 0; i < nact; ++i) {
+    const float w = __shfl(wi, i);
+    const float* po = a.part_o + (pbase + i) * D;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int d = lane + 64 * k;
+      if (d < D) O[k] = fmaf(w, po[d], O[k]);
     }
-    Store<QO>::store1(a.out, (int64_t)bh * a.D + d, (nact > 0 && L > 0.f) ? O / L : 0.f);
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int d = lane + 64 * k;
+    if (d < D) Store<QO>::store1(a.out, bh * D + d, L > 0.f ? O[k] / L : 0.f);
   }
 }
 
 hipError_t launch_combine(const AttnArgs& a, const Plan& p, hipStream_t s) {
   (void)p;
-  const int threads = ((a.D + 63) / 64) * 64;
-  const unsigned blocks = (unsigned)(a.B * a.Hq);
+  const unsigned blocks = (unsigned)(((int64_t)a.B * a.Hq + 3) / 4);
   AttnArgs arg = a;
   void* params[] = {&arg};
   const void* fn = a.qo_dtype == GQA_F32 ? reinterpret_cast<const void*>(&combine_kernel<GQA_F32>)
                                          : reinterpret_cast<const void*>(&combine_kernel<GQA_BF16>);
-  return hipLaunchKernel(fn, dim3(blocks), dim3(threads), params, 0, s);
+  return hipLaunchKernel(fn, dim3(blocks), dim3(256), params, 0, s);
 }
 
 }  // namespace gqa

@@ -145,7 +145,10 @@ __global__ __launch_bounds__(256) void attend_mfma_qk_kernel(AttnArgs a) {
   n = n < 0 ? 0 : (n > a.S ? a.S : n);
   const int t_begin = split * a.split_tokens;
   const int t_end = min(t_begin + a.split_tokens, n);
-  if (a.nsplit > 1 && t_begin >= n) return;  // inactive split: the combine pass skips it
+  // Splits holding valid slots; split 0 always runs (it writes the output,
+  // zeros when n = 0, if it is the only active split).
+  const int nact = n == 0 ? 0 : min(a.nsplit, (n + a.split_tokens - 1) / a.split_tokens);
+  if (split >= max(nact, 1)) return;
 
   // Fused step: slot L holds the new token; it is taken from k_new/v_new.
   const bool own_new = a.k_new != nullptr && L >= t_begin && L < t_end;
@@ -247,7 +250,7 @@ __global__ __launch_bounds__(256) void attend_mfma_qk_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  // Merge the 4 waves; write the output or this split's partial.
+  // Merge the 4 waves; write the output, or this split's partial.
   for (int idx = threadIdx.x; idx < G * kD; idx += 256) {
     const int g = idx / kD;
     const int d = idx - g * kD;
@@ -263,7 +266,7 @@ __global__ __launch_bounds__(256) void attend_mfma_qk_kernel(AttnArgs a) {
       Lsum += sm_l[w][g] * sc;
     }
     const int hq = h * G + g;
-    if (a.nsplit == 1) {
+    if (nact <= 1) {
       reinterpret_cast<uint16_t*>(a.out)[((int64_t)b * a.Hq + hq) * kD + d] =
           f32_to_bf16_rne(Lsum > 0.f ? O / Lsum : 0.f);
     } else {
@@ -354,7 +357,8 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
   n = n < 0 ? 0 : (n > a.S ? a.S : n);
   const int t_begin = split * a.split_tokens;
   const int t_end = min(t_begin + a.split_tokens, n);
-  if (a.nsplit > 1 && t_begin >= n) return;  // inactive split: the combine pass skips it
+  const int nact = n == 0 ? 0 : min(a.nsplit, (n + a.split_tokens - 1) / a.split_tokens);
+  if (split >= max(nact, 1)) return;
   const bool own_new = a.k_new != nullptr && L >= t_begin && L < t_end;
 
   const int hw = wave * 16;  // first head of this wave
@@ -487,7 +491,7 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
     const float mi = __shfl(m, hl);
     if (hw + hl >= G) continue;
     const int hq = h * G + hw + hl;
-    if (a.nsplit == 1) {
+    if (nact <= 1) {
       const float inv = li > 0.f ? 1.f / li : 0.f;
       uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)b * a.Hq + hq) * kD;
 #pragma unroll

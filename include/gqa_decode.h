@@ -85,8 +85,9 @@ typedef struct {
   int32_t layout;       /* GQA_LAYOUT_BHSD or GQA_LAYOUT_BSHD, shared by both caches         */
   int32_t kv_dtype;     /* storage of k_cache, v_cache, k_new, v_new: GQA_F32 or GQA_BF16    */
   int32_t qo_dtype;     /* storage of q and out: GQA_F32 or GQA_BF16                         */
-  int32_t num_splits;   /* 0 = library's choice; n > 0 cuts the token axis into n splits
-                           (results agree within rounding for every n)                      */
+  int32_t num_splits;   /* 0 = library's choice; n > 0 asks for n splits of the token axis
+                           (the plan uses at most 64, and fewer when n would leave a split
+                           empty; results agree within rounding for every n)                */
 } gqa_decode_desc_t;
 
 /* How a call with this descriptor runs (introspection for tests and tuning).
@@ -97,14 +98,14 @@ typedef struct {
   int32_t split_tokens;  /* slots per split (the last split may be shorter)                 */
   int32_t grid;          /* workgroups of the attention pass                                */
   int32_t block;         /* threads per workgroup of the attention pass                     */
-  int32_t combine;       /* 1 if a split-combine pass follows                               */
+  int32_t combine;       /* 1 if a split-combine pass follows the attention pass            */
   size_t workspace_bytes;
 } gqa_decode_plan_t;
 
 enum {
   GQA_KERNEL_GENERIC = 0,  /* vector ALU, any D <= 256, f32 or bf16 storage                  */
   GQA_KERNEL_MFMA_QK = 1,  /* bf16, D = 128, G <= 16: scores on MFMA, V sum on vector ALU    */
-  GQA_KERNEL_MFMA_ALL = 2  /* bf16, D = 128, G > 16: scores and V sum on MFMA                */
+  GQA_KERNEL_MFMA_ALL = 2  /* bf16, D = 128, 16 < G <= 64: scores and V sum on MFMA           */
 };
 
 /* Phase one (CANN operator page, two-phase call convention): validate the
@@ -141,9 +142,13 @@ gqa_status_t gqa_decode_append(const gqa_decode_desc_t* desc, void* k_cache, voi
  *   out      : (B, Hq, D), qo_dtype, written; out[b,h] = sum_{j<lengths[b]} w_j V_j of
  *              cache head h / (Hq/Hkv); must not overlap any other argument.
  *   workspace: device scratch of at least gqa_decode_workspace_size() bytes, 256-byte
- *              aligned (may be NULL when that size is 0).  Its contents on entry do not
- *              matter and are overwritten.
- * Pointers must be non-null and aligned to the element size. */
+ *              aligned (may be NULL when that size is 0).  It holds the split partials;
+ *              its contents on entry do not matter, it needs no clearing and it may be
+ *              reused by later calls with any descriptor.  Calls that run concurrently
+ *              must not share one workspace.
+ * Pointers must be non-null and aligned to the element size; when the plan's
+ * kernel is a matrix-core one (bf16 storage, head_dim 128, G <= 64), q, out and
+ * the caches must be 16-byte aligned (GQA_ERR_INVALID_ARGUMENT otherwise). */
 gqa_status_t gqa_decode_attend(const gqa_decode_desc_t* desc, const void* q, const void* k_cache,
                                const void* v_cache, const int32_t* lengths, void* out,
                                void* workspace, size_t workspace_bytes, void* stream);
@@ -153,7 +158,8 @@ gqa_status_t gqa_decode_attend(const gqa_decode_desc_t* desc, const void* q, con
  * token).  Arguments as in gqa_decode_append and gqa_decode_attend;
  * lengths[b] is the pre-append count (contract: 0 <= lengths[b] < S).  The
  * caller advances lengths itself afterwards (for example lengths += 1 on the
- * same stream). */
+ * same stream).  On the matrix-core kernels k_new and v_new must be 16-byte
+ * aligned as well. */
 gqa_status_t gqa_decode_step(const gqa_decode_desc_t* desc, const void* q, void* k_cache,
                              void* v_cache, const void* k_new, const void* v_new,
                              const int32_t* lengths, void* out, void* workspace,

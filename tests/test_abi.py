@@ -213,6 +213,7 @@ def test_plan_is_a_function_of_the_descriptor_only():
         assert p1["num_splits"] * p1["split_tokens"] >= d.capacity
         assert (p1["num_splits"] - 1) * p1["split_tokens"] < d.capacity     # no empty split
         assert p1["combine"] == (p1["num_splits"] > 1)
+        assert p1["num_splits"] <= 64
         assert (p1["workspace_bytes"] == 0) == (p1["num_splits"] == 1)
 
 

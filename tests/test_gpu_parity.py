@@ -274,6 +274,29 @@ def test_out_of_contract_lengths_are_memory_safe(g):
     assert torch.equal(out[1], ref[1]) and torch.equal(out[2], ref[2])   # counts past S clamp to S = 32
 
 
+def test_workspace_contents_do_not_matter(g):
+    """A workspace full of garbage, reused across descriptors and calls, gives the clean result."""
+    cases = [W.custom(4, 32, 8, 128, 3000, "BHSD", "bf16", "bf16", seed=51),
+             W.custom(2, 128, 2, 128, 2500, "BSHD", "bf16", "bf16", seed=52),
+             W.custom(3, 16, 2, 64, 900, "BHSD", "f32", "f32", seed=53)]
+    ws = torch.randint(0, 256, (64 << 20,), dtype=torch.uint8, device=DEV)
+    for w in cases:
+        L = torch.tensor([w.capacity - 1, 5, w.capacity // 2, 0][:w.B], dtype=torch.int32)
+        a = W.make_inputs(w, DEV, lengths=L)
+        b = {k: v.clone() for k, v in a.items()}
+        desc = g.desc_for(a["q"], a["k_cache"], w.layout)
+        assert g.workspace_size(desc) <= ws.numel()
+        say(f"workspace reuse {w.name}: plan {g.get_plan(desc)}")
+        clean = g.step(a["q"], a["k_cache"], a["v_cache"], a["k_new"], a["v_new"], a["lengths"], layout=w.layout,
+                       workspace=torch.zeros_like(ws))
+        for rep in range(3):
+            got = g.step(b["q"], b["k_cache"], b["v_cache"], b["k_new"], b["v_new"], b["lengths"], layout=w.layout,
+                         workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(got.view(torch.int16) if got.dtype == torch.bfloat16 else got,
+                               clean.view(torch.int16) if clean.dtype == torch.bfloat16 else clean), (w.name, rep)
+
+
 def test_empty_batch(g):
     q = torch.empty(0, 8, 128, dtype=torch.bfloat16, device=DEV)
     kc = torch.empty(0, 2, 16, 128, dtype=torch.bfloat16, device=DEV)
