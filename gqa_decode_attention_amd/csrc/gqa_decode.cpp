@@ -73,18 +73,23 @@ gqa_status_t make_plan(const gqa_decode_desc_t* d, Plan* p) {
   const int64_t G = Hq / Hkv;
   p->kernel = choose_kernel(d);
   p->head_chunks = p->kernel == GQA_KERNEL_GENERIC ? (int32_t)((G + kGenericHeadChunk - 1) / kGenericHeadChunk) : 1;
-  p->block = kBlock;
+  // Four waves per workgroup for every kernel.  (For MFMA_QK, measured on
+  // MI355X: one 4-wave workgroup per CU streams faster than 8- or 12-wave
+  // workgroups or more, shorter splits -- fewer concurrent streams suit HBM.)
+  p->block = 256;
   const int64_t units = std::max<int64_t>(1, B * Hkv * p->head_chunks);
   int64_t split_tokens;
   if (d->num_splits > 0) {
     const int64_t ns = std::min<int64_t>(d->num_splits, S);
     split_tokens = (S + ns - 1) / ns;
   } else {
-    // About three workgroups per CU (768 on 256 CUs), the resident count of the
-    // vector/MFMA_QK kernels; for large groups each split's partial (G rows of
-    // D + 2 floats) is as big as G/2 K/V rows, so those get half as many.
-    // Never splits shorter than 256 slots, and equal splits.
-    const int64_t target = p->kernel == GQA_KERNEL_MFMA_ALL ? 384 : 768;
+    // Workgroups wanted: about one per CU for MFMA_QK (each wave streams its
+    // own run of slots with a tile in flight), three per CU for the generic
+    // kernel, 1.5 per CU for large groups, whose split partials (G rows of
+    // D + 2 floats) are as big as G/2 K/V rows.  Splits are equal and at
+    // least 256 slots long.
+    const int64_t target = p->kernel == GQA_KERNEL_MFMA_QK ? kNumCUs
+                           : p->kernel == GQA_KERNEL_MFMA_ALL ? 384 : 768;
     int64_t ns = std::max<int64_t>(1, (target + units / 2) / units);
     ns = std::min<int64_t>(ns, std::max<int64_t>(1, S / 256));
     split_tokens = (S + ns - 1) / ns;

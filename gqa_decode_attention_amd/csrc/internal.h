@@ -52,7 +52,6 @@ extern const bool kHaveMfmaAll;
 constexpr int kNumCUs = 256;
 constexpr int kMaxSplits = 64;        // one lane per split in the combine pass          // MI355X: 8 XCDs x 32 CUs
 constexpr int kGenericHeadChunk = 8;  // query heads per workgroup in the generic kernel
-constexpr int kBlock = 256;
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_append(const AttnArgs& a, void* k_cache, void* v_cache, hipStream_t s);

@@ -10,8 +10,9 @@
 // 2^(m_old - m_new) when the maximum grows); splits of the token axis leave
 // (m, l, o) partials that the combine kernel merges.
 //
-// Kernel MFMA_QK (G <= 16).  One workgroup = 4 waves = one (sequence,
-// kv-head, split); each wave walks its own run of 16-slot tiles.  Per tile:
+// Kernel MFMA_QK (G <= 16).  One workgroup = NW waves (4) = one (sequence,
+// kv-head, split); the split's valid 16-slot tiles are dealt out evenly and
+// each wave walks its own run of them.  Per tile:
 //   scores  S(16 slots x 16 heads) = K_tile(16 x 128) . Q^T(128 x 16) as four
 //           v_mfma_f32_16x16x32_bf16.  Lane l = 16*r + c loads 16-byte pieces of
 //           cache row t0 + c straight into the A operand (bytes 16r + 64kk of
@@ -122,11 +123,11 @@ __device__ __forceinline__ void tile_update(WaveState<GP>& st, const u32x4 (&qf)
   }
 }
 
-template <int GP>
-__global__ __launch_bounds__(256) void attend_mfma_qk_kernel(AttnArgs a) {
-  __shared__ float sm_o[4][GP][kD];
-  __shared__ float sm_m[4][GP];
-  __shared__ float sm_l[4][GP];
+template <int GP, int NW>
+__global__ __launch_bounds__(64 * NW) void attend_mfma_qk_kernel(AttnArgs a) {
+  __shared__ float sm_o[NW][GP][kD];
+  __shared__ float sm_m[NW][GP];
+  __shared__ float sm_l[NW][GP];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -154,10 +155,16 @@ __global__ __launch_bounds__(256) void attend_mfma_qk_kernel(AttnArgs a) {
   const bool own_new = a.k_new != nullptr && L >= t_begin && L < t_end;
   const int t_cache_end = own_new ? L : t_end;
 
-  // This wave's run of slots: a multiple of 16 per wave.
-  const int per_wave = ((a.split_tokens + 63) / 64) * 16;
-  const int w0 = t_begin + wave * per_wave;
-  const int w1 = min(w0 + per_wave, t_cache_end);
+  // This wave's run of cache slots: the split's valid 16-slot tiles dealt out
+  // evenly (counts differ by at most one tile), so short sequences use every
+  // wave too.  The run boundaries depend on lengths, the grid does not.
+  // Wave w takes tiles [ceil(w T / NW), ceil((w + 1) T / NW)): the first waves
+  // take the extra tiles and the last wave never has more than any other.
+  const int ntile = (t_cache_end - t_begin + 15) >> 4;
+  const int w0 = t_begin + 16 * ((wave * ntile + NW - 1) / NW);
+  const int w1 = min(t_begin + 16 * (((wave + 1) * ntile + NW - 1) / NW), t_cache_end);
+  // The new token goes to the last wave.
+  const bool new_here = own_new && wave == NW - 1;
 
   const int64_t qrow = ((int64_t)b * a.Hq + (int64_t)h * G + c) * kD;
   u32x4 qf[4];
@@ -184,6 +191,25 @@ __global__ __launch_bounds__(256) void attend_mfma_qk_kernel(AttnArgs a) {
   // tile's math), nothing at or beyond the valid length is ever read, and the
   // clamped rows get score -inf, i.e. weight exactly 0, on finite values.
   u32x4 kf[4], vf[4];
+  // The new token first (its loads overlap the first cache tiles'): a tile
+  // whose only valid row is k_new/v_new, whose bits are also stored to slot L.
+  if (new_here) {
+    const int64_t nrow = ((int64_t)b * a.Hkv + h) * kD;
+    const uint16_t* knp = reinterpret_cast<const uint16_t*>(a.k_new) + nrow;
+    const uint16_t* vnp = reinterpret_cast<const uint16_t*>(a.v_new) + nrow;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) kf[kk] = (c == 0) ? load16(knp + 32 * kk + 8 * r) : u32x4{0, 0, 0, 0};
+    vf[0] = (r == 0) ? load16(vnp + 8 * c) : u32x4{0, 0, 0, 0};
+    vf[1] = vf[2] = vf[3] = u32x4{0, 0, 0, 0};
+    tile_update<GP>(st, qf, kf, vf, 1, r, a.scale_log2);
+    uint16_t* kw = reinterpret_cast<uint16_t*>(a.k_cache_w) + base + (int64_t)L * rs;
+    uint16_t* vw = reinterpret_cast<uint16_t*>(a.v_cache_w) + base + (int64_t)L * rs;
+    if (c == 0) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) store16(kw + 32 * kk + 8 * r, kf[kk]);
+    }
+    if (r == 0) store16(vw + 8 * c, vf[0]);
+  }
   auto load_tile = [&](int t0, u32x4 (&k)[4], u32x4 (&v)[4]) {
     const int rk = min(t0 + c, w1 - 1);
     const uint16_t* p = kb + (int64_t)rk * rs + 8 * r;
@@ -210,23 +236,6 @@ __global__ __launch_bounds__(256) void attend_mfma_qk_kernel(AttnArgs a) {
     }
   }
 
-  if (own_new && wave == 0) {
-    const int64_t nrow = ((int64_t)b * a.Hkv + h) * kD;
-    const uint16_t* knp = reinterpret_cast<const uint16_t*>(a.k_new) + nrow;
-    const uint16_t* vnp = reinterpret_cast<const uint16_t*>(a.v_new) + nrow;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) kf[kk] = (c == 0) ? load16(knp + 32 * kk + 8 * r) : u32x4{0, 0, 0, 0};
-    vf[0] = (r == 0) ? load16(vnp + 8 * c) : u32x4{0, 0, 0, 0};
-    vf[1] = vf[2] = vf[3] = u32x4{0, 0, 0, 0};
-    tile_update<GP>(st, qf, kf, vf, 1, r, a.scale_log2);
-    uint16_t* kw = reinterpret_cast<uint16_t*>(a.k_cache_w) + base + (int64_t)L * rs;
-    uint16_t* vw = reinterpret_cast<uint16_t*>(a.v_cache_w) + base + (int64_t)L * rs;
-    if (c == 0) {
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) store16(kw + 32 * kk + 8 * r, kf[kk]);
-    }
-    if (r == 0) store16(vw + 8 * c, vf[0]);
-  }
 
   // Merge the 4 rows of lanes of each wave (disjoint slots, same running max).
   st.l += __shfl_xor(st.l, 16);
@@ -250,16 +259,16 @@ __global__ __launch_bounds__(256) void attend_mfma_qk_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  // Merge the 4 waves; write the output, or this split's partial.
-  for (int idx = threadIdx.x; idx < G * kD; idx += 256) {
+  // Merge the NW waves; write the output, or this split's partial.
+  for (int idx = threadIdx.x; idx < G * kD; idx += 64 * NW) {
     const int g = idx / kD;
     const int d = idx - g * kD;
     float M = kNegInfM;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][g]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][g]);
     float O = 0.f, Lsum = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float mw = sm_m[w][g];
       const float sc = mw == kNegInfM ? 0.f : fast_exp2(mw - M);
       O += sm_o[w][g][d] * sc;
@@ -282,10 +291,12 @@ __global__ __launch_bounds__(256) void attend_mfma_qk_kernel(AttnArgs a) {
 
 template <int GP>
 static hipError_t launch_qk_t(const AttnArgs& a, const Plan& p, hipStream_t s) {
+  constexpr int NW = 4;
+  if (p.block != 64 * NW) return hipErrorInvalidValue;
   AttnArgs arg = a;
   void* params[] = {&arg};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&attend_mfma_qk_kernel<GP>), dim3(p.grid), dim3(256), params,
-                         0, s);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attend_mfma_qk_kernel<GP, NW>), dim3(p.grid), dim3(p.block),
+                         params, 0, s);
 }
 
 hipError_t launch_attend_mfma_qk(const AttnArgs& a, const Plan& p, hipStream_t s) {

@@ -227,7 +227,20 @@ def test_forced_split_count(ns):
         assert p["workspace_bytes"] == 0 and not p["combine"]
 
 
-def test_workspace_bytes_cover_partials():
-    d = desc(batch=32, num_q_heads=32, num_kv_heads=8, capacity=4097)
+@pytest.mark.parametrize("ns", [0, 2, 5])
+def test_workspace_bytes_cover_partials(ns):
+    d = desc(batch=32, num_q_heads=32, num_kv_heads=8, capacity=4097, num_splits=ns)
     p = g.get_plan(d)
-    assert p["workspace_bytes"] >= 32 * 32 * p["num_splits"] * (128 + 2) * 4
+    if p["num_splits"] == 1:
+        assert p["workspace_bytes"] == 0
+    else:
+        assert p["workspace_bytes"] >= 32 * 32 * p["num_splits"] * (128 + 2) * 4
+
+
+def test_block_shapes():
+    """Every kernel runs 4-wave workgroups; MFMA_QK aims at about one workgroup per CU."""
+    for kw in (dict(num_q_heads=8, num_kv_heads=2), dict(num_q_heads=32, num_kv_heads=2),
+               dict(num_q_heads=64, num_kv_heads=1), dict(kv_dtype=g.F32, qo_dtype=g.F32)):
+        assert g.get_plan(desc(**kw))["block"] == 256
+    p = g.get_plan(desc(batch=32, num_q_heads=32, num_kv_heads=8, capacity=4097))
+    assert p["kernel"] == "mfma_qk" and p["grid"] == 256 and p["num_splits"] == 1
