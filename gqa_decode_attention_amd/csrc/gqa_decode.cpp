@@ -84,12 +84,11 @@ gqa_status_t make_plan(const gqa_decode_desc_t* d, Plan* p) {
     split_tokens = (S + ns - 1) / ns;
   } else {
     // Workgroups wanted: about one per CU for MFMA_QK (each wave streams its
-    // own run of slots with a tile in flight), three per CU for the generic
-    // kernel, 1.5 per CU for large groups, whose split partials (G rows of
-    // D + 2 floats) are as big as G/2 K/V rows.  Splits are equal and at
-    // least 256 slots long.
-    const int64_t target = p->kernel == GQA_KERNEL_MFMA_QK ? kNumCUs
-                           : p->kernel == GQA_KERNEL_MFMA_ALL ? 384 : 768;
+    // own run of slots with a tile in flight), two per CU for MFMA_ALL (its
+    // waves share LDS tiles; more splits would cost partials of G rows of
+    // D + 2 floats each), three per CU for the generic kernel.  Splits are
+    // equal and at least 256 slots long.
+    const int64_t target = p->kernel == GQA_KERNEL_MFMA_QK ? kNumCUs : p->kernel == GQA_KERNEL_MFMA_ALL ? 512 : 768;
     int64_t ns = std::max<int64_t>(1, (target + units / 2) / units);
     ns = std::min<int64_t>(ns, std::max<int64_t>(1, S / 256));
     split_tokens = (S + ns - 1) / ns;

@@ -396,96 +396,116 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
   // clamped to it; the new token's row (fused step) comes from k_new/v_new.
   const int prow = tid >> 4;
   const int piece = tid & 15;
-  u32x4 kr[2], vr[2];
-  auto gload = [&](int t0) {
+  // Two register sets (tile t0 + 32 waiting for its LDS buffer, tile t0 + 64
+  // loading) keep two tiles in flight per workgroup.  The new token's row is
+  // selected per row, not per lane group, so the loads stay unconditional.
+  struct Regs {
+    u32x4 k[2], v[2];
+  };
+  const uint16_t* knew = a.k_new != nullptr ? reinterpret_cast<const uint16_t*>(a.k_new) + nrow : nullptr;
+  const uint16_t* vnew = a.v_new != nullptr ? reinterpret_cast<const uint16_t*>(a.v_new) + nrow : nullptr;
+  auto gload = [&](int t0, Regs& R) {
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2) {
       const int rc = min(t0 + prow + 16 * q2, t_end - 1);
-      if (own_new && rc == L) {
-        kr[q2] = load16(reinterpret_cast<const uint16_t*>(a.k_new) + nrow + 8 * piece);
-        vr[q2] = load16(reinterpret_cast<const uint16_t*>(a.v_new) + nrow + 8 * piece);
-      } else {
-        kr[q2] = load_nt16(kb + (int64_t)rc * rs + 8 * piece);
-        vr[q2] = load_nt16(vb + (int64_t)rc * rs + 8 * piece);
-      }
+      const bool is_new = own_new && rc == L;
+      const uint16_t* ks = is_new ? knew + 8 * piece : kb + (int64_t)rc * rs + 8 * piece;
+      const uint16_t* vs = is_new ? vnew + 8 * piece : vb + (int64_t)rc * rs + 8 * piece;
+      R.k[q2] = load_nt16(ks);
+      R.v[q2] = load_nt16(vs);
     }
   };
-  auto swrite = [&](int t0, int buf) {
+  auto swrite = [&](int t0, int buf, const Regs& R) {
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2) {
       const int row = prow + 16 * q2;
-      *reinterpret_cast<u32x4*>(&sk[buf][row * kPitch + 8 * piece]) = kr[q2];
-      *reinterpret_cast<u32x4*>(&sv[buf][row * kPitch + 8 * piece]) = vr[q2];
+      *reinterpret_cast<u32x4*>(&sk[buf][row * kPitch + 8 * piece]) = R.k[q2];
+      *reinterpret_cast<u32x4*>(&sv[buf][row * kPitch + 8 * piece]) = R.v[q2];
       if (own_new && t0 + row == L) {  // the appended slot: write the new bits to the cache
-        store16(reinterpret_cast<uint16_t*>(a.k_cache_w) + base + (int64_t)L * rs + 8 * piece, kr[q2]);
-        store16(reinterpret_cast<uint16_t*>(a.v_cache_w) + base + (int64_t)L * rs + 8 * piece, vr[q2]);
+        store16(reinterpret_cast<uint16_t*>(a.k_cache_w) + base + (int64_t)L * rs + 8 * piece, R.k[q2]);
+        store16(reinterpret_cast<uint16_t*>(a.v_cache_w) + base + (int64_t)L * rs + 8 * piece, R.v[q2]);
       }
     }
   };
 
-  if (t_begin < t_end) {
-    gload(t_begin);
-    swrite(t_begin, 0);
-    __syncthreads();
-    int buf = 0;
-    for (int t0 = t_begin; t0 < t_end; t0 += kTileT) {
-      const bool more = t0 + kTileT < t_end;
-      if (more) gload(t0 + kTileT);
-      const uint16_t* K = sk[buf];
-      const uint16_t* V = sv[buf];
-      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  // One tile: compute on LDS buffer `buf`, then move the next tile (register
+  // set Rn) into the other buffer; Rl receives the tile after that.
+  auto compute_tile = [&](int t0, int buf) {
+    const uint16_t* K = sk[buf];
+    const uint16_t* V = sv[buf];
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(&K[c * kPitch + 32 * kk + 8 * r]);
-        const u32x4 a1 = *reinterpret_cast<const u32x4*>(&K[(16 + c) * kPitch + 32 * kk + 8 * r]);
-        s0 = mfma_16x16x32(a0, qf[kk], s0);
-        s1 = mfma_16x16x32(a1, qf[kk], s1);
-      }
-      const int valid = t_end - t0;
-      float sc[8];
+    for (int kk = 0; kk < 4; ++kk) {
+      const u32x4 a0 = *reinterpret_cast<const u32x4*>(&K[c * kPitch + 32 * kk + 8 * r]);
+      const u32x4 a1 = *reinterpret_cast<const u32x4*>(&K[(16 + c) * kPitch + 32 * kk + 8 * r]);
+      s0 = mfma_16x16x32(a0, qf[kk], s0);
+      s1 = mfma_16x16x32(a1, qf[kk], s1);
+    }
+    const int valid = t_end - t0;
+    float sc[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sc[i] = (4 * r + i < valid) ? s0[i] * a.scale_log2 : kNegInfM;
+      sc[4 + i] = (16 + 4 * r + i < valid) ? s1[i] * a.scale_log2 : kNegInfM;
+    }
+    float mx = sc[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m, mx);
+    const float alpha = fast_exp2(m - m_new);
+    float p[8], ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[i] = fast_exp2(sc[i] - m_new);
+      ps += p[i];
+    }
+    l = l * alpha + ps;
+    m = m_new;
+    if (__any(alpha != 1.0f)) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sc[i] = (4 * r + i < valid) ? s0[i] * a.scale_log2 : kNegInfM;
-        sc[4 + i] = (16 + 4 * r + i < valid) ? s1[i] * a.scale_log2 : kNegInfM;
+        const float ai = __shfl(alpha, 4 * r + i);  // alpha of head 4r + i
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) O[nb][i] *= ai;
       }
-      float mx = sc[0];
+    }
+    const u32x4 pa = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                      pack_bf16x2(p[6], p[7])};
+    const int trow = 4 * r + (c >> 2);
+    const int tcol = 4 * (c & 3);
 #pragma unroll
-      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m, mx);
-      const float alpha = fast_exp2(m - m_new);
-      float p[8], ps = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        p[i] = fast_exp2(sc[i] - m_new);
-        ps += p[i];
-      }
-      l = l * alpha + ps;
-      m = m_new;
-      if (__any(alpha != 1.0f)) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float ai = __shfl(alpha, 4 * r + i);  // alpha of head 4r + i
-#pragma unroll
-          for (int nb = 0; nb < 8; ++nb) O[nb][i] *= ai;
-        }
-      }
-      const u32x4 pa = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                        pack_bf16x2(p[6], p[7])};
-      const int trow = 4 * r + (c >> 2);
-      const int tcol = 4 * (c & 3);
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        const s16x4 lo = lds_read_tr16(&V[trow * kPitch + 16 * nb + tcol]);
-        const s16x4 hi = lds_read_tr16(&V[(16 + trow) * kPitch + 16 * nb + tcol]);
-        const u32x4 vt = {(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
-                          (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
-                          (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
-                          (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
-        O[nb] = mfma_16x16x32(pa, vt, O[nb]);
-      }
-      if (more) swrite(t0 + kTileT, buf ^ 1);
+    for (int nb = 0; nb < 8; ++nb) {
+      const s16x4 lo = lds_read_tr16(&V[trow * kPitch + 16 * nb + tcol]);
+      const s16x4 hi = lds_read_tr16(&V[(16 + trow) * kPitch + 16 * nb + tcol]);
+      const u32x4 vt = {(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
+                        (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
+                        (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
+                        (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
+      O[nb] = mfma_16x16x32(pa, vt, O[nb]);
+    }
+  };
+  if (t_begin < t_end) {
+    Regs R0, R1;
+    gload(t_begin, R0);
+    swrite(t_begin, 0, R0);
+    if (t_begin + kTileT < t_end) gload(t_begin + kTileT, R1);
+    __syncthreads();
+    int buf = 0;
+    for (int t0 = t_begin; t0 < t_end; t0 += 2 * kTileT) {
+      // tile t0 (in LDS), t0 + T in R1, load t0 + 2T into R0
+      if (t0 + 2 * kTileT < t_end) gload(t0 + 2 * kTileT, R0);
+      compute_tile(t0, buf);
+      if (t0 + kTileT < t_end) swrite(t0 + kTileT, buf ^ 1, R1);
+      __syncthreads();
+      buf ^= 1;
+      const int t1 = t0 + kTileT;
+      if (t1 >= t_end) break;
+      // tile t1 (in LDS), t1 + T in R0, load t1 + 2T into R1
+      if (t1 + 2 * kTileT < t_end) gload(t1 + 2 * kTileT, R1);
+      compute_tile(t1, buf);
+      if (t1 + kTileT < t_end) swrite(t1 + kTileT, buf ^ 1, R0);
       __syncthreads();
       buf ^= 1;
     }
