@@ -24,8 +24,12 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # Packed fp32 instructions are turned off for the device code; the host pass
 # warns that it does not know the feature, which is harmless.
+# Matrix-core results are kept in ordinary VGPRs (not accumulation registers):
+# the online softmax rescales the V-sum accumulators on the vector ALU, which
+# with accumulation registers costs a copy out and back in on every tile.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
-          "-packed-fp32-ops", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-function"]
+          "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form=1", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall",
+          "-Wno-unused-function"]
 
 
 def _run(cmd):

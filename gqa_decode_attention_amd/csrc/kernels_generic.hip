@@ -325,13 +325,80 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
   }
 }
 
+// Combine for head width 128 with a 16-byte aligned output.  One wave per
+// (b, query head); lane (half, q) = (lane / 32, lane % 32) accumulates output
+// elements 4q .. 4q + 3 over splits half, half + 2, ...  Every load is issued
+// before any result is needed (the sequence length, the split maxima and
+// denominators, the first eight partial rows), so the pass costs about one
+// memory round trip; partial rows of inactive splits are never used.
+template <int QO>
+__global__ __launch_bounds__(256) void combine128_kernel(AttnArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t bh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // b * Hq + hq
+  if (bh >= (int64_t)a.B * a.Hq) return;  // whole waves only; no workgroup barrier follows
+  const int b = (int)(bh / a.Hq);
+  const int64_t pbase = bh * a.nsplit;
+  const int q = lane & 31;
+  const int half = lane >> 5;
+  const int len = a.lengths[b];
+  const float mraw = lane < a.nsplit ? a.part_m[pbase + lane] : kNegInf;
+  const float lraw = lane < a.nsplit ? a.part_l[pbase + lane] : 0.f;
+  const f32x4* po = reinterpret_cast<const f32x4*>(a.part_o + pbase * 128) + q;  // split i: po[32 i]
+  f32x4 o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = half + 2 * j;
+    o[j] = i < a.nsplit ? po[32 * i] : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  int n = len + a.len_offset;
+  n = n < 0 ? 0 : (n > a.S ? a.S : n);
+  const int nact = n == 0 ? 0 : min(a.nsplit, (n + a.split_tokens - 1) / a.split_tokens);
+  if (nact <= 1) return;  // the attention pass wrote this sequence's output itself
+  const float M = wave_max(lane < nact ? mraw : kNegInf);
+  const float w = lane < nact ? fast_exp2(mraw - M) : 0.f;
+  const float L = wave_sum(w * lraw);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = half + 2 * j;
+    const float wi = __shfl(w, i);
+    if (i < nact) acc += wi * o[j];
+  }
+  for (int i0 = 8; i0 < nact; i0 += 2) {  // more than eight splits
+    const int i = i0 + half;
+    const float wi = __shfl(w, min(i, 63));
+    if (i < nact) acc += wi * po[32 * i];
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], 32);
+  if (half == 0) {
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    if (QO == GQA_F32) {
+      reinterpret_cast<f32x4*>(a.out)[bh * 32 + q] = acc * inv;
+    } else {
+      const uint32_t lo = (uint32_t)f32_to_bf16_rne(acc[0] * inv) | ((uint32_t)f32_to_bf16_rne(acc[1] * inv) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16_rne(acc[2] * inv) | ((uint32_t)f32_to_bf16_rne(acc[3] * inv) << 16);
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      reinterpret_cast<u32x2*>(a.out)[bh * 32 + q] = u32x2{lo, hi};
+    }
+  }
+}
+
 hipError_t launch_combine(const AttnArgs& a, const Plan& p, hipStream_t s) {
   (void)p;
   const unsigned blocks = (unsigned)(((int64_t)a.B * a.Hq + 3) / 4);
   AttnArgs arg = a;
   void* params[] = {&arg};
-  const void* fn = a.qo_dtype == GQA_F32 ? reinterpret_cast<const void*>(&combine_kernel<GQA_F32>)
-                                         : reinterpret_cast<const void*>(&combine_kernel<GQA_BF16>);
+  const bool fast = a.D == 128 && (reinterpret_cast<uintptr_t>(a.out) & 15) == 0 &&
+                    (reinterpret_cast<uintptr_t>(a.part_o) & 15) == 0;
+  const void* fn;
+  if (fast) {
+    fn = a.qo_dtype == GQA_F32 ? reinterpret_cast<const void*>(&combine128_kernel<GQA_F32>)
+                               : reinterpret_cast<const void*>(&combine128_kernel<GQA_BF16>);
+  } else {
+    fn = a.qo_dtype == GQA_F32 ? reinterpret_cast<const void*>(&combine_kernel<GQA_F32>)
+                               : reinterpret_cast<const void*>(&combine_kernel<GQA_BF16>);
+  }
   return hipLaunchKernel(fn, dim3(blocks), dim3(256), params, 0, s);
 }
 

@@ -49,6 +49,12 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr float kNegInfM = -__builtin_inff();
 constexpr int kD = 128;
 
+// Lazy rescaling: a tile whose maximum exceeds the running reference m by at
+// most this much (log2 units) keeps m, so its weights reach at most 2^8; only a
+// larger jump moves m and rescales o and l.  o / l is the same softmax either
+// way, and partials carry their own reference m into the combine.
+constexpr float kRescaleSlack = 8.f;
+
 template <int I, int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
   if constexpr (I < N) {
@@ -89,20 +95,22 @@ __device__ __forceinline__ void tile_update(WaveState<GP>& st, const u32x4 (&qf)
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) s = mfma_16x16x32(kf[kk], qf[kk], s);
-  float sv[4];
+  // Raw scores; the scale log2(e)/sqrt(D) > 0 is folded into the exponent.
+  float sv[4] = {s[0], s[1], s[2], s[3]};
+  if (valid < 16) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) sv[i] = (4 * r + i < valid) ? s[i] * scale_log2 : kNegInfM;
+    for (int i = 0; i < 4; ++i)
+      if (4 * r + i >= valid) sv[i] = kNegInfM;
+  }
   float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(st.m, mx);
-  const float alpha = fast_exp2(st.m - m_new);  // 0 on the first tile
-  float p[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sv[i] - m_new);
-  st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-  st.m = m_new;
-  if (__any(alpha != 1.0f)) {  // the running maximum moved for some head
+  const float mc = mx * scale_log2;
+  if (__any(mc > st.m + kRescaleSlack)) {  // some head's maximum jumped: move the reference
+    const float m_new = fmaxf(st.m, mc);
+    const float alpha = fast_exp2(st.m - m_new);  // 0 on the first tile
+    st.l *= alpha;
+    st.m = m_new;
     static_for<0, GP>([&](auto gi) {
       constexpr int g = decltype(gi)::value;
       const float ag = row_bcast<g>(alpha);
@@ -110,6 +118,11 @@ __device__ __forceinline__ void tile_update(WaveState<GP>& st, const u32x4 (&qf)
       for (int e = 0; e < 8; ++e) st.acc[g][e] *= ag;
     });
   }
+  const float nm = -st.m;
+  float p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(sv[i], scale_log2, nm));
+  st.l += (p[0] + p[1]) + (p[2] + p[3]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float v[8];
@@ -186,56 +199,63 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qk_kernel(AttnArgs a) {
   const uint16_t* vb = reinterpret_cast<const uint16_t*>(a.v_cache) + base;
   const int64_t rs = a.st;  // elements between consecutive slots
 
-  // Rows past the wave's last valid slot are clamped to that slot: every load
-  // is unconditional (so the next tile's loads stay in flight during this
-  // tile's math), nothing at or beyond the valid length is ever read, and the
-  // clamped rows get score -inf, i.e. weight exactly 0, on finite values.
-  u32x4 kf[4], vf[4];
-  // The new token first (its loads overlap the first cache tiles'): a tile
-  // whose only valid row is k_new/v_new, whose bits are also stored to slot L.
-  if (new_here) {
-    const int64_t nrow = ((int64_t)b * a.Hkv + h) * kD;
-    const uint16_t* knp = reinterpret_cast<const uint16_t*>(a.k_new) + nrow;
-    const uint16_t* vnp = reinterpret_cast<const uint16_t*>(a.v_new) + nrow;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) kf[kk] = (c == 0) ? load16(knp + 32 * kk + 8 * r) : u32x4{0, 0, 0, 0};
-    vf[0] = (r == 0) ? load16(vnp + 8 * c) : u32x4{0, 0, 0, 0};
-    vf[1] = vf[2] = vf[3] = u32x4{0, 0, 0, 0};
-    tile_update<GP>(st, qf, kf, vf, 1, r, a.scale_log2);
-    uint16_t* kw = reinterpret_cast<uint16_t*>(a.k_cache_w) + base + (int64_t)L * rs;
-    uint16_t* vw = reinterpret_cast<uint16_t*>(a.v_cache_w) + base + (int64_t)L * rs;
-    if (c == 0) {
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) store16(kw + 32 * kk + 8 * r, kf[kk]);
-    }
-    if (r == 0) store16(vw + 8 * c, vf[0]);
-  }
+  // Rows past the wave's last valid slot are clamped to that slot (and to slot
+  // 0 for a wave without tiles): every load is unconditional and in bounds,
+  // nothing at or beyond the valid length is ever read, and the clamped rows
+  // get score -inf, i.e. weight exactly 0, on finite values.
   auto load_tile = [&](int t0, u32x4 (&k)[4], u32x4 (&v)[4]) {
-    const int rk = min(t0 + c, w1 - 1);
+    const int rk = max(min(t0 + c, w1 - 1), 0);
     const uint16_t* p = kb + (int64_t)rk * rs + 8 * r;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) k[kk] = load_nt16(p + 32 * kk);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int rv = min(t0 + 4 * r + i, w1 - 1);
+      const int rv = max(min(t0 + 4 * r + i, w1 - 1), 0);
       v[i] = load_nt16(vb + (int64_t)rv * rs + 8 * c);
     }
   };
 
-  if (w0 < w1) {
-    load_tile(w0, kf, vf);
-    for (int t0 = w0; t0 < w1; t0 += 16) {
-      u32x4 kn[4], vn[4];
-      load_tile(t0 + 16, kn, vn);  // prefetch; past w1 it re-reads row w1 - 1
-      tile_update<GP>(st, qf, kf, vf, w1 - t0, r, a.scale_log2);
+  // The new token is a tile whose only valid row is k_new/v_new; its loads are
+  // issued before the first cache tile's, and its bits are copied to slot L
+  // after the loop (no store is in flight while the tiles stream).
+  u32x4 knw[4], vnw;
+  if (new_here) {
+    const int64_t nrow = ((int64_t)b * a.Hkv + h) * kD;
+    const uint16_t* knp = reinterpret_cast<const uint16_t*>(a.k_new) + nrow;
+    const uint16_t* vnp = reinterpret_cast<const uint16_t*>(a.v_new) + nrow;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        kf[kk] = kn[kk];
-        vf[kk] = vn[kk];
-      }
-    }
+    for (int kk = 0; kk < 4; ++kk) knw[kk] = (c == 0) ? load16(knp + 32 * kk + 8 * r) : u32x4{0, 0, 0, 0};
+    vnw = (r == 0) ? load16(vnp + 8 * c) : u32x4{0, 0, 0, 0};
   }
-
+  // Two register sets alternate, so the next tile's loads are in flight during
+  // this tile's math and no register copy waits for them.
+  u32x4 ka[4], va[4], kc[4], vc[4];
+  load_tile(w0, ka, va);
+  if (new_here) {
+    const u32x4 vf[4] = {vnw, u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}};
+    tile_update<GP>(st, qf, knw, vf, 1, r, a.scale_log2);
+  }
+  if (w0 < w1) {
+    const int nt = (w1 - w0 + 15) >> 4;
+    int t0 = w0;
+    for (int it = 0; it < nt / 2; ++it) {
+      load_tile(t0 + 16, kc, vc);
+      tile_update<GP>(st, qf, ka, va, w1 - t0, r, a.scale_log2);
+      load_tile(t0 + 32, ka, va);  // past w1 it re-reads row w1 - 1
+      tile_update<GP>(st, qf, kc, vc, w1 - t0 - 16, r, a.scale_log2);
+      t0 += 32;
+    }
+    if (nt & 1) tile_update<GP>(st, qf, ka, va, w1 - t0, r, a.scale_log2);
+  }
+  if (new_here) {
+    uint16_t* kw = reinterpret_cast<uint16_t*>(a.k_cache_w) + base + (int64_t)L * rs;
+    uint16_t* vw = reinterpret_cast<uint16_t*>(a.v_cache_w) + base + (int64_t)L * rs;
+    if (c == 0) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) store16(kw + 32 * kk + 8 * r, knw[kk]);
+    }
+    if (r == 0) store16(vw + 8 * c, vnw);
+  }
 
   // Merge the 4 rows of lanes of each wave (disjoint slots, same running max).
   st.l += __shfl_xor(st.l, 16);
@@ -342,9 +362,14 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
       (lds_s16x4*)((__attribute__((address_space(3))) char*)(const_cast<uint16_t*>(p))));
 }
 
+// Two floats to a bf16 pair (low half = lo) with gfx950's v_cvt_pk_bf16_f32,
+// round to nearest even.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
+
 
 __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sk[2][kTileT * kPitch];
@@ -392,39 +417,42 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
   const int64_t nrow = ((int64_t)b * a.Hkv + h) * kD;
 
   // Cooperative tile load: thread t moves 16 bytes (piece t & 15) of rows
-  // t >> 4 and 16 + (t >> 4).  Rows past the split's last valid slot are
-  // clamped to it; the new token's row (fused step) comes from k_new/v_new.
+  // t >> 4 and 16 + (t >> 4) of a 32-slot tile.  Rows past the split's last
+  // valid slot are clamped to it, so every load reads a valid slot and no load
+  // carries a condition (the count of loads in flight is then the same on every
+  // path, and each LDS write waits only for its own tile).
+  // Fused step: the appended slot L is the owning split's last valid slot.  The
+  // cache still holds stale bits there, so when the tile holding L is written
+  // to LDS its rows >= L take the new key/value from registers (rows past L are
+  // masked and only need finite values); the new bits are copied to the cache
+  // slot after the loop (no store is in flight while the tiles stream).
   const int prow = tid >> 4;
   const int piece = tid & 15;
-  // Two register sets (tile t0 + 32 waiting for its LDS buffer, tile t0 + 64
-  // loading) keep two tiles in flight per workgroup.  The new token's row is
-  // selected per row, not per lane group, so the loads stay unconditional.
   struct Regs {
     u32x4 k[2], v[2];
   };
-  const uint16_t* knew = a.k_new != nullptr ? reinterpret_cast<const uint16_t*>(a.k_new) + nrow : nullptr;
-  const uint16_t* vnew = a.v_new != nullptr ? reinterpret_cast<const uint16_t*>(a.v_new) + nrow : nullptr;
+  u32x4 kn = {0u, 0u, 0u, 0u}, vn = {0u, 0u, 0u, 0u};
+  if (own_new) {
+    kn = load16(reinterpret_cast<const uint16_t*>(a.k_new) + nrow + 8 * piece);
+    vn = load16(reinterpret_cast<const uint16_t*>(a.v_new) + nrow + 8 * piece);
+  }
   auto gload = [&](int t0, Regs& R) {
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2) {
       const int rc = min(t0 + prow + 16 * q2, t_end - 1);
-      const bool is_new = own_new && rc == L;
-      const uint16_t* ks = is_new ? knew + 8 * piece : kb + (int64_t)rc * rs + 8 * piece;
-      const uint16_t* vs = is_new ? vnew + 8 * piece : vb + (int64_t)rc * rs + 8 * piece;
-      R.k[q2] = load_nt16(ks);
-      R.v[q2] = load_nt16(vs);
+      const int64_t off = (int64_t)rc * rs + 8 * piece;
+      R.k[q2] = load_nt16(kb + off);
+      R.v[q2] = load_nt16(vb + off);
     }
   };
   auto swrite = [&](int t0, int buf, const Regs& R) {
+    const bool holds_new = own_new && t0 + kTileT > L;  // uniform
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2) {
       const int row = prow + 16 * q2;
-      *reinterpret_cast<u32x4*>(&sk[buf][row * kPitch + 8 * piece]) = R.k[q2];
-      *reinterpret_cast<u32x4*>(&sv[buf][row * kPitch + 8 * piece]) = R.v[q2];
-      if (own_new && t0 + row == L) {  // the appended slot: write the new bits to the cache
-        store16(reinterpret_cast<uint16_t*>(a.k_cache_w) + base + (int64_t)L * rs + 8 * piece, R.k[q2]);
-        store16(reinterpret_cast<uint16_t*>(a.v_cache_w) + base + (int64_t)L * rs + 8 * piece, R.v[q2]);
-      }
+      const bool nw = holds_new && t0 + row >= L;
+      *reinterpret_cast<u32x4*>(&sk[buf][row * kPitch + 8 * piece]) = nw ? kn : R.k[q2];
+      *reinterpret_cast<u32x4*>(&sv[buf][row * kPitch + 8 * piece]) = nw ? vn : R.v[q2];
     }
   };
 
@@ -441,29 +469,26 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
       s0 = mfma_16x16x32(a0, qf[kk], s0);
       s1 = mfma_16x16x32(a1, qf[kk], s1);
     }
-    const int valid = t_end - t0;
-    float sc[8];
+    // Raw scores; the scale log2(e)/sqrt(D) is positive, so the maximum is
+    // taken on raw scores and the scale is folded into the exponent's fma.
+    float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+    if (t0 + kTileT > t_end) {  // the split's last, partial tile
+      const int valid = t_end - t0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sc[i] = (4 * r + i < valid) ? s0[i] * a.scale_log2 : kNegInfM;
-      sc[4 + i] = (16 + 4 * r + i < valid) ? s1[i] * a.scale_log2 : kNegInfM;
+      for (int i = 0; i < 4; ++i) {
+        if (4 * r + i >= valid) sc[i] = kNegInfM;
+        if (16 + 4 * r + i >= valid) sc[4 + i] = kNegInfM;
+      }
     }
-    float mx = sc[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
+    float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float alpha = fast_exp2(m - m_new);
-    float p[8], ps = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      p[i] = fast_exp2(sc[i] - m_new);
-      ps += p[i];
-    }
-    l = l * alpha + ps;
-    m = m_new;
-    if (__any(alpha != 1.0f)) {
+    const float mc = mx * a.scale_log2;
+    if (__any(mc > m + kRescaleSlack)) {  // some head's maximum jumped: move the reference
+      const float m_new = fmaxf(m, mc);
+      const float alpha = fast_exp2(m - m_new);  // 0 on the first tile
+      l *= alpha;
+      m = m_new;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float ai = __shfl(alpha, 4 * r + i);  // alpha of head 4r + i
@@ -471,6 +496,14 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
         for (int nb = 0; nb < 8; ++nb) O[nb][i] *= ai;
       }
     }
+    const float nm = -m;
+    float p[8], ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[i] = fast_exp2(fmaf(sc[i], a.scale_log2, nm));
+      ps += p[i];
+    }
+    l += ps;
     const u32x4 pa = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                       pack_bf16x2(p[6], p[7])};
     const int trow = 4 * r + (c >> 2);
@@ -486,29 +519,39 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
       O[nb] = mfma_16x16x32(pa, vt, O[nb]);
     }
   };
+  // Two register sets keep two tiles in flight: at the top of each iteration
+  // tile t0 sits in LDS buffer `buf` and R1 is loading tile t0 + T.  Loads of
+  // tiles past the end clamp to the last valid row (cache hits, never used), so
+  // every path issues the same loads, the loop has one exit, and each LDS write
+  // waits only for its own tile's loads.
   if (t_begin < t_end) {
+    const int ntile = (t_end - t_begin + kTileT - 1) / kTileT;
     Regs R0, R1;
     gload(t_begin, R0);
+    gload(t_begin + kTileT, R1);
     swrite(t_begin, 0, R0);
-    if (t_begin + kTileT < t_end) gload(t_begin + kTileT, R1);
     __syncthreads();
     int buf = 0;
-    for (int t0 = t_begin; t0 < t_end; t0 += 2 * kTileT) {
-      // tile t0 (in LDS), t0 + T in R1, load t0 + 2T into R0
-      if (t0 + 2 * kTileT < t_end) gload(t0 + 2 * kTileT, R0);
+    int t0 = t_begin;
+    for (int it = 0; it < ntile / 2; ++it) {
+      gload(t0 + 2 * kTileT, R0);
       compute_tile(t0, buf);
-      if (t0 + kTileT < t_end) swrite(t0 + kTileT, buf ^ 1, R1);
+      swrite(t0 + kTileT, buf ^ 1, R1);
       __syncthreads();
       buf ^= 1;
-      const int t1 = t0 + kTileT;
-      if (t1 >= t_end) break;
-      // tile t1 (in LDS), t1 + T in R0, load t1 + 2T into R1
-      if (t1 + 2 * kTileT < t_end) gload(t1 + 2 * kTileT, R1);
-      compute_tile(t1, buf);
-      if (t1 + kTileT < t_end) swrite(t1 + kTileT, buf ^ 1, R0);
+      gload(t0 + 3 * kTileT, R1);
+      compute_tile(t0 + kTileT, buf);
+      swrite(t0 + 2 * kTileT, buf ^ 1, R0);
       __syncthreads();
       buf ^= 1;
+      t0 += 2 * kTileT;
     }
+    if (ntile & 1) compute_tile(t0, buf);
+  }
+
+  if (own_new && prow == 0) {  // the appended slot
+    store16(reinterpret_cast<uint16_t*>(a.k_cache_w) + base + (int64_t)L * rs + 8 * piece, kn);
+    store16(reinterpret_cast<uint16_t*>(a.v_cache_w) + base + (int64_t)L * rs + 8 * piece, vn);
   }
 
   // Denominator and max per head: lane (r, c) holds head c; the output rows of

@@ -171,6 +171,9 @@ SHAPES = [
     (3, 40, 1, 128, 333, "BSHD", "bf16", "bf16", 3),     # G = 40
     (2, 32, 1, 128, 1000, "BSHD", "bf16", "bf16", 0),    # G = 32
     (2, 80, 1, 128, 200, "BHSD", "bf16", "bf16", 0),     # G = 80: beyond the matrix-core kernels
+    (2, 32, 8, 128, 2000, "BHSD", "bf16", "bf16", 24),   # many splits: the combine's second loop
+    (2, 16, 2, 128, 1500, "BSHD", "f32", "f32", 64),     # 64 splits, float32 combine
+    (2, 64, 1, 128, 3000, "BHSD", "bf16", "bf16", 13),   # G = 64, an odd split count above 8
 ]
 
 
@@ -204,7 +207,7 @@ def test_attend_shapes(g, shape):
 
 
 @pytest.mark.parametrize("G", [4, 64])
-@pytest.mark.parametrize("ns", [1, 2, 3, 7, 0])
+@pytest.mark.parametrize("ns", [1, 2, 3, 7, 20, 0])
 def test_split_count_does_not_change_the_result(g, ns, G):
     w = W.custom(3, 4 * G, 4, 128, 2100, "BHSD", "bf16", "bf16", seed=31, stale="pm:10000")
     L = torch.tensor([2099, 1, 1234], dtype=torch.int32)
