@@ -88,19 +88,20 @@ struct WaveState {
 };
 
 // One 16-slot tile.  kf: this lane's A-operand pieces; vf[i]: slot t0 + 4r + i,
-// elements 8c..8c+7; valid: number of valid slots in the tile (from t0).
+// elements 8c..8c+7; rows lo .. valid - 1 of the tile (from t0) are valid, the
+// others are masked.
 template <int GP>
 __device__ __forceinline__ void tile_update(WaveState<GP>& st, const u32x4 (&qf)[4], const u32x4 (&kf)[4],
-                                            const u32x4 (&vf)[4], int valid, int r, float scale_log2) {
+                                            const u32x4 (&vf)[4], int lo, int valid, int r, float scale_log2) {
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) s = mfma_16x16x32(kf[kk], qf[kk], s);
   // Raw scores; the scale log2(e)/sqrt(D) > 0 is folded into the exponent.
   float sv[4] = {s[0], s[1], s[2], s[3]};
-  if (valid < 16) {
+  if (lo > 0 || valid < 16) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (4 * r + i >= valid) sv[i] = kNegInfM;
+      if (4 * r + i < lo || 4 * r + i >= valid) sv[i] = kNegInfM;
   }
   float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
   mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -168,14 +169,27 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qk_kernel(AttnArgs a) {
   const bool own_new = a.k_new != nullptr && L >= t_begin && L < t_end;
   const int t_cache_end = own_new ? L : t_end;
 
-  // This wave's run of cache slots: the split's valid 16-slot tiles dealt out
+  const int64_t base = (int64_t)b * a.sb + (int64_t)h * a.sh;
+  const int64_t rs = a.st;  // elements between consecutive slots
+
+  // Tile grid.  When a kv-head's slots are contiguous 256-byte rows, the
+  // 16-slot tiles start at 4 KB-aligned cache addresses (measured faster than
+  // tiles that straddle 4 KB boundaries); the grid then begins up to 15 slots
+  // before t_begin and those leading rows are masked.
+  int tv = t_begin;
+  if (rs == kD) {
+    const uint64_t row = (reinterpret_cast<uintptr_t>(a.k_cache) >> 8) + (uint64_t)((base >> 7) + t_begin);
+    tv = t_begin - (int)(row & 15);
+  }
+  // This wave's run of cache slots: the split's 16-slot tiles dealt out
   // evenly (counts differ by at most one tile), so short sequences use every
   // wave too.  The run boundaries depend on lengths, the grid does not.
   // Wave w takes tiles [ceil(w T / NW), ceil((w + 1) T / NW)): the first waves
   // take the extra tiles and the last wave never has more than any other.
-  const int ntile = (t_cache_end - t_begin + 15) >> 4;
-  const int w0 = t_begin + 16 * ((wave * ntile + NW - 1) / NW);
-  const int w1 = min(t_begin + 16 * (((wave + 1) * ntile + NW - 1) / NW), t_cache_end);
+  // Only wave 0's first tile can hold leading rows; it always holds a valid one.
+  const int ntile = t_cache_end > t_begin ? (t_cache_end - tv + 15) >> 4 : 0;
+  const int w0 = tv + 16 * ((wave * ntile + NW - 1) / NW);
+  const int w1 = min(tv + 16 * (((wave + 1) * ntile + NW - 1) / NW), t_cache_end);
   // The new token goes to the last wave.
   const bool new_here = own_new && wave == NW - 1;
 
@@ -194,23 +208,21 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qk_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) st.acc[g][e] = 0.f;
 
-  const int64_t base = (int64_t)b * a.sb + (int64_t)h * a.sh;
   const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.k_cache) + base;
   const uint16_t* vb = reinterpret_cast<const uint16_t*>(a.v_cache) + base;
-  const int64_t rs = a.st;  // elements between consecutive slots
 
-  // Rows past the wave's last valid slot are clamped to that slot (and to slot
-  // 0 for a wave without tiles): every load is unconditional and in bounds,
-  // nothing at or beyond the valid length is ever read, and the clamped rows
-  // get score -inf, i.e. weight exactly 0, on finite values.
+  // Rows past the wave's last valid slot are clamped to that slot, rows before
+  // t_begin to t_begin: every load is unconditional and in bounds, nothing at
+  // or beyond the valid length is ever read, and the clamped rows get score
+  // -inf, i.e. weight exactly 0, on finite values.
   auto load_tile = [&](int t0, u32x4 (&k)[4], u32x4 (&v)[4]) {
-    const int rk = max(min(t0 + c, w1 - 1), 0);
+    const int rk = max(min(t0 + c, w1 - 1), t_begin);
     const uint16_t* p = kb + (int64_t)rk * rs + 8 * r;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) k[kk] = load_nt16(p + 32 * kk);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int rv = max(min(t0 + 4 * r + i, w1 - 1), 0);
+      const int rv = max(min(t0 + 4 * r + i, w1 - 1), t_begin);
       v[i] = load_nt16(vb + (int64_t)rv * rs + 8 * c);
     }
   };
@@ -233,19 +245,19 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qk_kernel(AttnArgs a) {
   load_tile(w0, ka, va);
   if (new_here) {
     const u32x4 vf[4] = {vnw, u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}};
-    tile_update<GP>(st, qf, knw, vf, 1, r, a.scale_log2);
+    tile_update<GP>(st, qf, knw, vf, 0, 1, r, a.scale_log2);
   }
   if (w0 < w1) {
     const int nt = (w1 - w0 + 15) >> 4;
     int t0 = w0;
     for (int it = 0; it < nt / 2; ++it) {
       load_tile(t0 + 16, kc, vc);
-      tile_update<GP>(st, qf, ka, va, w1 - t0, r, a.scale_log2);
+      tile_update<GP>(st, qf, ka, va, t_begin - t0, w1 - t0, r, a.scale_log2);
       load_tile(t0 + 32, ka, va);  // past w1 it re-reads row w1 - 1
-      tile_update<GP>(st, qf, kc, vc, w1 - t0 - 16, r, a.scale_log2);
+      tile_update<GP>(st, qf, kc, vc, t_begin - t0 - 16, w1 - t0 - 16, r, a.scale_log2);
       t0 += 32;
     }
-    if (nt & 1) tile_update<GP>(st, qf, ka, va, w1 - t0, r, a.scale_log2);
+    if (nt & 1) tile_update<GP>(st, qf, ka, va, t_begin - t0, w1 - t0, r, a.scale_log2);
   }
   if (new_here) {
     uint16_t* kw = reinterpret_cast<uint16_t*>(a.k_cache_w) + base + (int64_t)L * rs;
