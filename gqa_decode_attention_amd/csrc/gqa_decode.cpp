@@ -51,6 +51,8 @@ gqa_status_t check_desc(const gqa_decode_desc_t* d) {
       !mul_ok(t, 4, &t))
     return GQA_ERR_UNSUPPORTED;
   if (!mul_ok(d->batch, d->num_q_heads, &t) || t > INT32_MAX) return GQA_ERR_UNSUPPORTED;
+  // The byte stride between consecutive slots must fit 32 bits.
+  if (!mul_ok(d->num_kv_heads, d->head_dim, &t) || t * 4 > (int64_t)UINT32_MAX) return GQA_ERR_UNSUPPORTED;
   return GQA_OK;
 }
 

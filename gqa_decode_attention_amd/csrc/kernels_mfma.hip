@@ -214,16 +214,21 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qk_kernel(AttnArgs a) {
   // Rows past the wave's last valid slot are clamped to that slot, rows before
   // t_begin to t_begin: every load is unconditional and in bounds, nothing at
   // or beyond the valid length is ever read, and the clamped rows get score
-  // -inf, i.e. weight exactly 0, on finite values.
+  // -inf, i.e. weight exactly 0, on finite values.  A row address is one
+  // 32 x 32 -> 64-bit multiply-add (the byte stride between slots fits 32 bits
+  // and clamped rows are never negative).
+  const uint32_t rsb = (uint32_t)rs * 2u;
+  const char* kl = reinterpret_cast<const char*>(kb) + 16 * r;
+  const char* vl = reinterpret_cast<const char*>(vb) + 16 * c;
   auto load_tile = [&](int t0, u32x4 (&k)[4], u32x4 (&v)[4]) {
-    const int rk = max(min(t0 + c, w1 - 1), t_begin);
-    const uint16_t* p = kb + (int64_t)rk * rs + 8 * r;
+    const uint32_t rk = (uint32_t)max(min(t0 + c, w1 - 1), t_begin);
+    const char* p = kl + (uint64_t)rk * rsb;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) k[kk] = load_nt16(p + 32 * kk);
+    for (int kk = 0; kk < 4; ++kk) k[kk] = load_nt16(p + 64 * kk);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int rv = max(min(t0 + 4 * r + i, w1 - 1), t_begin);
-      v[i] = load_nt16(vb + (int64_t)rv * rs + 8 * c);
+      const uint32_t rv = (uint32_t)max(min(t0 + 4 * r + i, w1 - 1), t_begin);
+      v[i] = load_nt16(vl + (uint64_t)rv * rsb);
     }
   };
 

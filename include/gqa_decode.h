@@ -63,7 +63,8 @@ extern "C" {
 typedef enum {
   GQA_OK = 0,
   GQA_ERR_INVALID_ARGUMENT = 1,    /* malformed descriptor, null/misaligned/overlapping pointer */
-  GQA_ERR_UNSUPPORTED = 2,         /* well-formed but not implemented (head_dim > 256)          */
+  GQA_ERR_UNSUPPORTED = 2,         /* well-formed but not implemented (head_dim > 256, sizes
+                                      beyond the limits in gqa_decode_desc_t)                    */
   GQA_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes below gqa_decode_workspace_size()         */
   GQA_ERR_HIP = 4,                 /* a HIP launch failed                                       */
   GQA_ERR_INTERNAL = 5             /* unexpected library error (no C++ exception crosses)       */
@@ -79,7 +80,8 @@ typedef struct {
   int32_t batch;        /* B >= 0.  B == 0: the call validates the descriptor, returns GQA_OK
                            and enqueues nothing (pointers may then be NULL).               */
   int32_t num_q_heads;  /* Hq >= 1, a multiple of num_kv_heads                              */
-  int32_t num_kv_heads; /* Hkv >= 1                                                         */
+  int32_t num_kv_heads; /* Hkv >= 1; Hkv * head_dim * 4 <= 2^32 - 1 (GQA_ERR_UNSUPPORTED
+                           otherwise), as are caches beyond 2^63 bytes and B * Hq > 2^31 - 1 */
   int32_t head_dim;     /* D in [1, 256]; D > 256 is GQA_ERR_UNSUPPORTED                    */
   int32_t capacity;     /* S >= 1 slots per (sequence, kv-head) in both caches              */
   int32_t layout;       /* GQA_LAYOUT_BHSD or GQA_LAYOUT_BSHD, shared by both caches         */

@@ -69,6 +69,8 @@ BAD_DESCS = [
     (dict(num_splits=-2), INVALID),
     (dict(head_dim=257), UNSUPPORTED),
     (dict(batch=1 << 30, capacity=1 << 30), UNSUPPORTED),   # byte count past 2^62
+    (dict(batch=1, num_q_heads=1 << 23, num_kv_heads=1 << 23, head_dim=128, capacity=1),
+     UNSUPPORTED),                                          # slot stride past 2^32 bytes
 ]
 
 
