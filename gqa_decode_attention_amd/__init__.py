@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     GqaError,
     append,
     attend,
+    check_lengths,
     desc_for,
     get_plan,
     lib,

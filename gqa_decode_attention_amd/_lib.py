@@ -65,6 +65,7 @@ EXPORTS = (
     "gqa_decode_append",
     "gqa_decode_attend",
     "gqa_decode_step",
+    "gqa_decode_check_lengths",
     "gqa_decode_status_string",
     "gqa_decode_version",
 )
@@ -87,8 +88,9 @@ def lib() -> ctypes.CDLL:
     L.gqa_decode_append.argtypes = [DP, P, P, P, P, I32P, P]
     L.gqa_decode_attend.argtypes = [DP, P, P, P, I32P, P, P, S, P]
     L.gqa_decode_step.argtypes = [DP, P, P, P, P, P, I32P, P, P, S, P]
+    L.gqa_decode_check_lengths.argtypes = [DP, I32P, ctypes.c_int32, P, ctypes.POINTER(ctypes.c_int32)]
     for name in ("gqa_decode_workspace_size", "gqa_decode_get_plan", "gqa_decode_append", "gqa_decode_attend",
-                 "gqa_decode_step"):
+                 "gqa_decode_step", "gqa_decode_check_lengths"):
         getattr(L, name).restype = ctypes.c_int
     L.gqa_decode_status_string.argtypes = [ctypes.c_int]
     L.gqa_decode_status_string.restype = ctypes.c_char_p
@@ -206,3 +208,18 @@ def step(q, k_cache, v_cache, k_new, v_new, lengths, *, layout="BHSD", out=None,
                                 k_new.data_ptr(), v_new.data_ptr(), lengths.data_ptr(), out.data_ptr(), wptr, wbytes,
                                 _stream(dev)), "gqa_decode_step")
     return out
+
+
+def check_lengths(lengths, capacity, *, mode="step"):
+    """Number of lengths[b] outside the contract of `mode` ("step"/"append": 0 <= L < capacity,
+    "attend": 1 <= L <= capacity). Synchronous debugging aid."""
+    if mode not in ("step", "append", "attend"):
+        raise ValueError(f"mode {mode!r}: 'step', 'append' or 'attend'")
+    if lengths.dtype != torch.int32 or lengths.dim() != 1 or not lengths.is_contiguous() or not lengths.is_cuda:
+        raise ValueError("lengths must be a contiguous 1-D int32 CUDA tensor")
+    B = lengths.numel()
+    desc = make_desc(B, 1, 1, 1, capacity)
+    n = ctypes.c_int32(-1)
+    check(lib().gqa_decode_check_lengths(ctypes.byref(desc), lengths.data_ptr(), 1 if mode == "attend" else 0,
+                                         _stream(lengths.device), ctypes.byref(n)), "gqa_decode_check_lengths")
+    return int(n.value)

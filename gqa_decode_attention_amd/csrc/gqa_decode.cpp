@@ -354,6 +354,27 @@ gqa_status_t gqa_decode_step(const gqa_decode_desc_t* desc, const void* q, void*
   }
 }
 
+gqa_status_t gqa_decode_check_lengths(const gqa_decode_desc_t* desc, const int32_t* lengths, int32_t mode,
+                                      void* stream, int32_t* bad_count) {
+  try {
+    gqa_status_t st = check_desc(desc);
+    if (st != GQA_OK) return st;
+    if ((mode != 0 && mode != 1) || bad_count == nullptr) return GQA_ERR_INVALID_ARGUMENT;
+    if (desc->batch == 0) {
+      *bad_count = 0;
+      return GQA_OK;
+    }
+    if (lengths == nullptr || (reinterpret_cast<uintptr_t>(lengths) & 3) != 0) return GQA_ERR_INVALID_ARGUMENT;
+    const int32_t lo = mode == 0 ? 0 : 1;
+    const int32_t hi = mode == 0 ? desc->capacity - 1 : desc->capacity;
+    if (run_check_lengths(lengths, desc->batch, lo, hi, (hipStream_t)stream, bad_count) != hipSuccess)
+      return GQA_ERR_HIP;
+    return GQA_OK;
+  } catch (...) {
+    return GQA_ERR_INTERNAL;
+  }
+}
+
 const char* gqa_decode_status_string(gqa_status_t s) {
   switch (s) {
     case GQA_OK: return "GQA_OK";

@@ -59,5 +59,8 @@ hipError_t launch_attend_generic(const AttnArgs& a, const Plan& p, int vec_path,
 hipError_t launch_attend_mfma_qk(const AttnArgs& a, const Plan& p, hipStream_t s);
 hipError_t launch_attend_mfma_all(const AttnArgs& a, const Plan& p, hipStream_t s);
 hipError_t launch_combine(const AttnArgs& a, const Plan& p, hipStream_t s);
+// Count lengths[b] outside [lo, hi] (synchronous; *bad receives the count).
+hipError_t run_check_lengths(const int32_t* lengths, int32_t B, int32_t lo, int32_t hi, hipStream_t s,
+                             int32_t* bad);
 
 }  // namespace gqa

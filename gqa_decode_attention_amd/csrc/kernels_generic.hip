@@ -15,6 +15,8 @@
 // token ranges merge exactly: M = max m_i, l = sum l_i exp(m_i - M), o = sum
 // o_i exp(m_i - M); the output is o / l.  Exponentials are base 2 with log2(e)
 // folded into the score scale.
+#include <mutex>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -400,6 +402,50 @@ hipError_t launch_combine(const AttnArgs& a, const Plan& p, hipStream_t s) {
                                : reinterpret_cast<const void*>(&combine_kernel<GQA_BF16>);
   }
   return hipLaunchKernel(fn, dim3(blocks), dim3(256), params, 0, s);
+}
+
+// ---------------------------------------------------------------------------
+// Length check (debugging aid): one workgroup counts the entries outside
+// [lo, hi] and stores the count in a device variable the host copies back.
+// ---------------------------------------------------------------------------
+__device__ int32_t g_bad_lengths;
+
+__global__ __launch_bounds__(1024) void check_lengths_kernel(const int32_t* lengths, int32_t B, int32_t lo,
+                                                             int32_t hi) {
+  __shared__ int32_t part[16];
+  int32_t cnt = 0;
+  for (int32_t i = threadIdx.x; i < B; i += blockDim.x) {
+    const int32_t v = lengths[i];
+    cnt += (v < lo || v > hi) ? 1 : 0;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = cnt;
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    int32_t t = threadIdx.x < (blockDim.x >> 6) ? part[threadIdx.x] : 0;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off);
+    if (threadIdx.x == 0) g_bad_lengths = t;
+  }
+}
+
+hipError_t run_check_lengths(const int32_t* lengths, int32_t B, int32_t lo, int32_t hi, hipStream_t s,
+                             int32_t* bad) {
+  static std::mutex mu;  // one device variable per GPU: serialise the calls
+  std::lock_guard<std::mutex> lock(mu);
+  const int32_t* lp = lengths;
+  void* params[] = {&lp, &B, &lo, &hi};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&check_lengths_kernel), dim3(1), dim3(1024), params,
+                                 0, s);
+  if (e != hipSuccess) return e;
+  int32_t host = 0;
+  e = hipMemcpyFromSymbolAsync(&host, HIP_SYMBOL(g_bad_lengths), sizeof(host), 0, hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return e;
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return e;
+  *bad = host;
+  return hipSuccess;
 }
 
 }  // namespace gqa

@@ -167,6 +167,21 @@ gqa_status_t gqa_decode_step(const gqa_decode_desc_t* desc, const void* q, void*
                              const int32_t* lengths, void* out, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* Debugging aid, not on the hot path: counts the entries of the device array
+ * `lengths` (B = desc->batch entries) that lie outside the contract of a call
+ * (JAX Grouped-Query Decode Step page, constraints: lengths in [1, S] for the
+ * read-only attend; KV cache decode step page: the new token goes to slot
+ * lengths[b], so 0 <= lengths[b] < S for append and step).
+ *   mode      : 0 = append/step contract, 1 = attend contract
+ *   bad_count : host pointer, receives the count
+ * Synchronous: enqueues one small kernel on `stream`, copies the count back and
+ * waits for the stream.  Calls are serialised inside the library (the count
+ * lives in one device variable per GPU).  B == 0 gives 0 without a GPU call.
+ * Errors: GQA_ERR_INVALID_ARGUMENT for a bad descriptor or mode, or a null
+ * `bad_count` (or null `lengths` with B > 0); GQA_ERR_HIP if a HIP call fails. */
+gqa_status_t gqa_decode_check_lengths(const gqa_decode_desc_t* desc, const int32_t* lengths, int32_t mode,
+                                      void* stream, int32_t* bad_count);
+
 /* Static, NUL-terminated name of a status code. */
 const char* gqa_decode_status_string(gqa_status_t status);
 

@@ -110,6 +110,22 @@ def test_empty_batch_is_a_noop():
     assert L.gqa_decode_workspace_size(ctypes.byref(d), ctypes.byref(n)) == OK and n.value == 0
 
 
+def test_check_lengths_argument_errors():
+    """Every refusal happens before any HIP call (no GPU is touched here)."""
+    L = g.lib()
+    d = desc()
+    n = ctypes.c_int32(-7)
+    assert L.gqa_decode_check_lengths(ctypes.byref(d), FAKE, 2, None, ctypes.byref(n)) == INVALID   # bad mode
+    assert L.gqa_decode_check_lengths(ctypes.byref(d), FAKE, 0, None, None) == INVALID              # no result
+    assert L.gqa_decode_check_lengths(ctypes.byref(d), None, 0, None, ctypes.byref(n)) == INVALID   # no lengths
+    assert L.gqa_decode_check_lengths(ctypes.byref(d), FAKE + 2, 1, None, ctypes.byref(n)) == INVALID  # misaligned
+    assert L.gqa_decode_check_lengths(None, FAKE, 0, None, ctypes.byref(n)) == INVALID
+    assert n.value == -7
+    d0 = desc(batch=0)
+    assert L.gqa_decode_check_lengths(ctypes.byref(d0), None, 1, None, ctypes.byref(n)) == OK
+    assert n.value == 0
+
+
 def _attend_ptrs():
     return dict(q=FAKE, kc=FAKE + GAP, vc=FAKE + 2 * GAP, lens=FAKE + 3 * GAP, out=FAKE + 4 * GAP,
                 ws=FAKE + 5 * GAP, kn=FAKE + 6 * GAP, vn=FAKE + 7 * GAP)

@@ -308,6 +308,24 @@ def test_empty_batch(g):
     assert out.shape == (0, 8, 128)
 
 
+def test_check_lengths_counts_out_of_contract_entries(g):
+    S = 100
+    vals = torch.tensor([-1, 0, 1, 5, S - 1, S, S + 1, 2 ** 31 - 1, -(2 ** 31)], dtype=torch.int32)
+    lens = vals.to(DEV)
+    want_step = int(((vals < 0) | (vals >= S)).sum())
+    want_attend = int(((vals < 1) | (vals > S)).sum())
+    assert g.check_lengths(lens, S, mode="step") == want_step == 5
+    assert g.check_lengths(lens, S, mode="attend") == want_attend == 5
+    big = torch.randint(-50, 3 * S, (5000,), generator=torch.Generator().manual_seed(11), dtype=torch.int32)
+    assert g.check_lengths(big.to(DEV), S, mode="attend") == int(((big < 1) | (big > S)).sum())
+    assert g.check_lengths(big.to(DEV), S, mode="append") == int(((big < 0) | (big >= S)).sum())
+    # every workload's lengths are inside the contract
+    for name in ("tiny", "ragged_batch", "large_group"):
+        w = W.WORKLOADS[name]
+        Lw = W.draw_lengths(w).to(DEV)
+        assert g.check_lengths(Lw, w.capacity, mode="step") == 0
+
+
 def test_graph_capture_replays(g):
     """The step has no host sync and no memset: it can be captured and replayed."""
     w = W.custom(4, 32, 8, 128, 2048, "BHSD", "bf16", "bf16", seed=77)
