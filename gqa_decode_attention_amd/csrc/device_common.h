@@ -72,6 +72,25 @@ template <> __device__ __forceinline__ void widen16<1>(u32x4 w, float* out) {
   out[4] = bf16_lo(w.z); out[5] = bf16_hi(w.z); out[6] = bf16_lo(w.w); out[7] = bf16_hi(w.w);
 }
 
+// Reductions over the four 16-lane rows of a wave (lanes c, c + 16, c + 32,
+// c + 48), result in every lane, with gfx950's cross-row swaps
+// (v_permlane16_swap, v_permlane32_swap): vector-ALU only, no LDS round trip.
+// With both operands x, permlane16_swap returns rows (0,0,2,2) and (1,1,3,3),
+// permlane32_swap returns halves (lo,lo) and (hi,hi); the sums associate as
+// (r0 + r1) + (r2 + r3).  All 64 lanes must be active.
+__device__ __forceinline__ float rows_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float rows_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Fast base-2 exponential (v_exp_f32).  exp2(-inf) = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

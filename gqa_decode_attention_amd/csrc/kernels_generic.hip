@@ -358,7 +358,7 @@ __global__ __launch_bounds__(256) void combine128_kernel(AttnArgs a) {
   if (nact <= 1) return;  // the attention pass wrote this sequence's output itself
   const float M = wave_max(lane < nact ? mraw : kNegInf);
   const float w = lane < nact ? fast_exp2(mraw - M) : 0.f;
-  const float L = wave_sum(w * lraw);
+  const float L = wave_sum(lane < nact ? w * lraw : 0.f);  // stale l of inactive splits may be NaN or Inf
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {

@@ -104,8 +104,7 @@ __device__ __forceinline__ void tile_update(WaveState<GP>& st, const u32x4 (&qf)
       if (4 * r + i < lo || 4 * r + i >= valid) sv[i] = kNegInfM;
   }
   float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = rows_max(mx);
   const float mc = mx * scale_log2;
   if (__any(mc > st.m + kRescaleSlack)) {  // some head's maximum jumped: move the reference
     const float m_new = fmaxf(st.m, mc);
@@ -275,14 +274,12 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qk_kernel(AttnArgs a) {
   }
 
   // Merge the 4 rows of lanes of each wave (disjoint slots, same running max).
-  st.l += __shfl_xor(st.l, 16);
-  st.l += __shfl_xor(st.l, 32);
+  st.l = rows_sum(st.l);
 #pragma unroll
   for (int g = 0; g < GP; ++g)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      st.acc[g][e] += __shfl_xor(st.acc[g][e], 16);
-      st.acc[g][e] += __shfl_xor(st.acc[g][e], 32);
+      st.acc[g][e] = rows_sum(st.acc[g][e]);
     }
   if (r == 0) {
 #pragma unroll
@@ -498,8 +495,7 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
       }
     }
     float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = rows_max(mx);
     const float mc = mx * a.scale_log2;
     if (__any(mc > m + kRescaleSlack)) {  // some head's maximum jumped: move the reference
       const float m_new = fmaxf(m, mc);
@@ -573,8 +569,7 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
 
   // Denominator and max per head: lane (r, c) holds head c; the output rows of
   // lane (r, c) are heads 4r + i.
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  l = rows_sum(l);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int hl = 4 * r + i;  // head within the wave

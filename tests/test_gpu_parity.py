@@ -282,7 +282,9 @@ def test_workspace_contents_do_not_matter(g):
     cases = [W.custom(4, 32, 8, 128, 3000, "BHSD", "bf16", "bf16", seed=51),
              W.custom(2, 128, 2, 128, 2500, "BSHD", "bf16", "bf16", seed=52),
              W.custom(3, 16, 2, 64, 900, "BHSD", "f32", "f32", seed=53)]
-    ws = torch.randint(0, 256, (64 << 20,), dtype=torch.uint8, device=DEV)
+    ws = torch.randint(0, 256, (64 << 20,), generator=torch.Generator().manual_seed(5), dtype=torch.uint8).to(DEV)
+    ws[: 16 << 20].fill_(0xFF)                                   # NaN floats
+    ws[16 << 20: 32 << 20].view(torch.float32).fill_(float("inf"))
     for w in cases:
         L = torch.tensor([w.capacity - 1, 5, w.capacity // 2, 0][:w.B], dtype=torch.int32)
         a = W.make_inputs(w, DEV, lengths=L)
