@@ -167,6 +167,61 @@ gqa_status_t gqa_decode_step(const gqa_decode_desc_t* desc, const void* q, void*
                              const int32_t* lengths, void* out, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Mapped caches (CLIKA runtime, "groupQueryAttention" API page: the slot_ids
+ * and paged block-table parameters).  The same decode step on caches that are
+ * not indexed by batch row:
+ *
+ *   GQA_MAP_SLOTS  continuous cache of num_rows rows; batch row b appends to and
+ *                  attends from cache row map[b].  Caches (num_rows, Hkv, S, D)
+ *                  for GQA_LAYOUT_BHSD or (num_rows, S, Hkv, D) for BSHD, with
+ *                  S = desc->capacity.  map: int32 [B], every entry in
+ *                  [0, num_rows) and no two equal.
+ *   GQA_MAP_PAGED  block pool of num_blocks blocks of block_size slots; token j
+ *                  of batch row b lives in block map[b * max_blocks + j /
+ *                  block_size] at slot j % block_size.  Pools (num_blocks, Hkv,
+ *                  block_size, D) for BHSD or (num_blocks, block_size, Hkv, D)
+ *                  for BSHD; desc->capacity must equal max_blocks * block_size.
+ *                  map: int32 [B, max_blocks], every entry -1 (unused tail
+ *                  pad) or in [0, num_blocks), and no block named twice within
+ *                  one row.  Blocks holding slots below a row's length must not
+ *                  be -1 (the device lengths are not checked, as above).
+ *
+ * The table is passed twice with the same entries: `map` in device memory for
+ * the kernels and `map_host` in host memory, which is validated whole before
+ * anything is enqueued (an out-of-range or repeated entry refuses
+ * GQA_ERR_INVALID_ARGUMENT).  The device copy is trusted to match; entries it
+ * holds out of range are clamped (reads) or skip the write (append), so a
+ * mismatch cannot fault.  Rows of a paged table may share blocks for reading;
+ * a step or append into a block shared by two rows races.
+ * Matrix-core kernels serve paged caches whose block_size is a multiple of 16;
+ * other block sizes run on the generic kernel.
+ * ------------------------------------------------------------------------- */
+enum { GQA_MAP_SLOTS = 1, GQA_MAP_PAGED = 2 };
+typedef struct {
+  int32_t kind;              /* GQA_MAP_SLOTS or GQA_MAP_PAGED                              */
+  int32_t num_rows;          /* SLOTS: cache rows; PAGED: pool blocks.  >= 1               */
+  int32_t block_size;        /* PAGED: slots per block, >= 1 (ignored for SLOTS)            */
+  int32_t max_blocks;        /* PAGED: table columns, >= 1 (ignored for SLOTS)              */
+  const int32_t* map;        /* device table (4-byte aligned)                               */
+  const int32_t* map_host;   /* host copy of the same entries                               */
+} gqa_cache_map_t;
+
+/* As gqa_decode_append / _attend / _step, with caches addressed through `map`.
+ * The descriptor's batch, heads, head_dim, capacity, layout and dtypes keep
+ * their meaning (capacity = slots per sequence); the workspace size and plan
+ * are those of the descriptor.  B == 0 validates and enqueues nothing. */
+gqa_status_t gqa_decode_append_mapped(const gqa_decode_desc_t* desc, const gqa_cache_map_t* map, void* k_cache,
+                                      void* v_cache, const void* k_new, const void* v_new,
+                                      const int32_t* lengths, void* stream);
+gqa_status_t gqa_decode_attend_mapped(const gqa_decode_desc_t* desc, const gqa_cache_map_t* map, const void* q,
+                                      const void* k_cache, const void* v_cache, const int32_t* lengths, void* out,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+gqa_status_t gqa_decode_step_mapped(const gqa_decode_desc_t* desc, const gqa_cache_map_t* map, const void* q,
+                                    void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                                    const int32_t* lengths, void* out, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
 /* Debugging aid, not on the hot path: counts the entries of the device array
  * `lengths` (B = desc->batch entries) that lie outside the contract of a call
  * (JAX Grouped-Query Decode Step page, constraints: lengths in [1, S] for the

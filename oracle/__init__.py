@@ -14,3 +14,12 @@ from .oracle import (  # noqa: F401
     softmax_weights,
     step,
 )
+from .mapped import (  # noqa: F401
+    append_mapped,
+    attend_mapped,
+    mapped_rows,
+    slot_location,
+    step_mapped,
+    validate_slots,
+    validate_table,
+)
