@@ -13,13 +13,17 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     Desc,
     GqaError,
+    MapT,
     append,
+    append_mapped,
     attend,
+    attend_mapped,
     check_lengths,
     desc_for,
     get_plan,
     lib,
     make_desc,
     step,
+    step_mapped,
     workspace_size,
 )

@@ -59,12 +59,30 @@ class PlanT(ctypes.Structure):
     ]
 
 
+MAP_KINDS = {"slots": 1, "paged": 2}
+
+
+class MapT(ctypes.Structure):
+    """gqa_cache_map_t."""
+    _fields_ = [
+        ("kind", ctypes.c_int32),
+        ("num_rows", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("max_blocks", ctypes.c_int32),
+        ("map", ctypes.c_void_p),
+        ("map_host", ctypes.c_void_p),
+    ]
+
+
 EXPORTS = (
     "gqa_decode_workspace_size",
     "gqa_decode_get_plan",
     "gqa_decode_append",
     "gqa_decode_attend",
     "gqa_decode_step",
+    "gqa_decode_append_mapped",
+    "gqa_decode_attend_mapped",
+    "gqa_decode_step_mapped",
     "gqa_decode_check_lengths",
     "gqa_decode_status_string",
     "gqa_decode_version",
@@ -89,8 +107,13 @@ def lib() -> ctypes.CDLL:
     L.gqa_decode_attend.argtypes = [DP, P, P, P, I32P, P, P, S, P]
     L.gqa_decode_step.argtypes = [DP, P, P, P, P, P, I32P, P, P, S, P]
     L.gqa_decode_check_lengths.argtypes = [DP, I32P, ctypes.c_int32, P, ctypes.POINTER(ctypes.c_int32)]
+    MP = ctypes.POINTER(MapT)
+    L.gqa_decode_append_mapped.argtypes = [DP, MP, P, P, P, P, I32P, P]
+    L.gqa_decode_attend_mapped.argtypes = [DP, MP, P, P, P, I32P, P, P, S, P]
+    L.gqa_decode_step_mapped.argtypes = [DP, MP, P, P, P, P, P, I32P, P, P, S, P]
     for name in ("gqa_decode_workspace_size", "gqa_decode_get_plan", "gqa_decode_append", "gqa_decode_attend",
-                 "gqa_decode_step", "gqa_decode_check_lengths"):
+                 "gqa_decode_step", "gqa_decode_check_lengths", "gqa_decode_append_mapped",
+                 "gqa_decode_attend_mapped", "gqa_decode_step_mapped"):
         getattr(L, name).restype = ctypes.c_int
     L.gqa_decode_status_string.argtypes = [ctypes.c_int]
     L.gqa_decode_status_string.restype = ctypes.c_char_p
@@ -223,3 +246,82 @@ def check_lengths(lengths, capacity, *, mode="step"):
     check(lib().gqa_decode_check_lengths(ctypes.byref(desc), lengths.data_ptr(), 1 if mode == "attend" else 0,
                                          _stream(lengths.device), ctypes.byref(n)), "gqa_decode_check_lengths")
     return int(n.value)
+
+
+def _mapped_desc(q_like_B, Hq, D, kv_dtype, qo_dtype, k_cache, kind, layout, table, num_splits, Hkv=None):
+    """Descriptor and gqa_cache_map_t for a mapped call (kept alive by the caller)."""
+    if kind not in MAP_KINDS:
+        raise ValueError(f"kind must be one of {list(MAP_KINDS)}")
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {list(LAYOUTS)}")
+    if k_cache.dim() != 4:
+        raise ValueError("caches are 4-D")
+    rows = k_cache.shape[0]
+    if layout == "BHSD":
+        _, Hc, inner, Dc = k_cache.shape
+    else:
+        _, inner, Hc, Dc = k_cache.shape
+    if Dc != D or (Hkv is not None and Hkv != Hc):
+        raise ValueError("cache disagrees on head_dim or kv-heads")
+    if table.dtype != torch.int32:
+        raise ValueError("the map is int32")
+    host = table.detach().to("cpu").contiguous()
+    dev_t = table.to(k_cache.device).contiguous()
+    if kind == "slots":
+        if host.dim() != 1 or host.shape[0] != q_like_B:
+            raise ValueError("slot map is (B,)")
+        S, bs, mb = inner, 0, 0
+    else:
+        if host.dim() != 2 or host.shape[0] != q_like_B:
+            raise ValueError("block table is (B, max_blocks)")
+        bs, mb = inner, host.shape[1]
+        S = bs * mb
+    desc = make_desc(q_like_B, Hq, Hc, D, S, layout, kv_dtype, qo_dtype, num_splits)
+    m = MapT(MAP_KINDS[kind], rows, bs, mb, dev_t.data_ptr(), host.data_ptr())
+    return desc, m, (host, dev_t)
+
+
+def append_mapped(k_cache, v_cache, k_new, v_new, lengths, table, *, kind, layout="BHSD"):
+    """In-place append at slot lengths[b] of a slot-indexed cache or a block pool."""
+    dev = _dev([k_cache, v_cache, k_new, v_new], lengths)
+    B, Hkv, D = k_new.shape
+    code = _dtype_code(k_cache.dtype)
+    desc, m, keep = _mapped_desc(B, Hkv, D, code, code, k_cache, kind, layout, table, 0, Hkv)
+    check(lib().gqa_decode_append_mapped(ctypes.byref(desc), ctypes.byref(m), k_cache.data_ptr(), v_cache.data_ptr(),
+                                         k_new.data_ptr(), v_new.data_ptr(), lengths.data_ptr(), _stream(dev)),
+          "gqa_decode_append_mapped")
+    del keep
+
+
+def attend_mapped(q, k_cache, v_cache, lengths, table, *, kind, layout="BHSD", out=None, workspace=None,
+                  num_splits=0):
+    """Read-only attention over a slot-indexed cache or a block pool. Returns out (B, Hq, D)."""
+    dev = _dev([q, k_cache, v_cache], lengths)
+    B, Hq, D = q.shape
+    desc, m, keep = _mapped_desc(B, Hq, D, _dtype_code(k_cache.dtype), _dtype_code(q.dtype), k_cache, kind, layout,
+                                 table, num_splits)
+    if out is None:
+        out = torch.empty_like(q)
+    workspace, wptr, wbytes = _workspace(desc, dev, workspace)
+    check(lib().gqa_decode_attend_mapped(ctypes.byref(desc), ctypes.byref(m), q.data_ptr(), k_cache.data_ptr(),
+                                         v_cache.data_ptr(), lengths.data_ptr(), out.data_ptr(), wptr, wbytes,
+                                         _stream(dev)), "gqa_decode_attend_mapped")
+    del keep
+    return out
+
+
+def step_mapped(q, k_cache, v_cache, k_new, v_new, lengths, table, *, kind, layout="BHSD", out=None, workspace=None,
+                num_splits=0):
+    """Fused decode step on a slot-indexed cache or a block pool. Returns out (B, Hq, D)."""
+    dev = _dev([q, k_cache, v_cache, k_new, v_new], lengths)
+    B, Hq, D = q.shape
+    desc, m, keep = _mapped_desc(B, Hq, D, _dtype_code(k_cache.dtype), _dtype_code(q.dtype), k_cache, kind, layout,
+                                 table, num_splits, k_new.shape[1])
+    if out is None:
+        out = torch.empty_like(q)
+    workspace, wptr, wbytes = _workspace(desc, dev, workspace)
+    check(lib().gqa_decode_step_mapped(ctypes.byref(desc), ctypes.byref(m), q.data_ptr(), k_cache.data_ptr(),
+                                       v_cache.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), lengths.data_ptr(),
+                                       out.data_ptr(), wptr, wbytes, _stream(dev)), "gqa_decode_step_mapped")
+    del keep
+    return out

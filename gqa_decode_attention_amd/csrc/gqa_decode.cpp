@@ -13,6 +13,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <vector>
 
 #include "gqa_decode.h"
 #include "internal.h"
@@ -124,6 +125,67 @@ Span span(const void* p, size_t bytes) {
 }
 bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
 
+// Cache map (mapped entry points).  Shape fields first, then -- for B > 0 --
+// the pointers and the whole host table (CLIKA groupQueryAttention page:
+// slot rows in range and distinct; block entries -1 or in range, no block
+// twice within a row).
+gqa_status_t check_map(const gqa_decode_desc_t* d, const gqa_cache_map_t* m, const Plan& p) {
+  if (m == nullptr) return GQA_ERR_INVALID_ARGUMENT;
+  if ((m->kind != GQA_MAP_SLOTS && m->kind != GQA_MAP_PAGED) || m->num_rows < 1) return GQA_ERR_INVALID_ARGUMENT;
+  int64_t t;
+  if (m->kind == GQA_MAP_PAGED) {
+    if (m->block_size < 1 || m->max_blocks < 1) return GQA_ERR_INVALID_ARGUMENT;
+    if (!mul_ok(m->max_blocks, m->block_size, &t) || t != d->capacity) return GQA_ERR_INVALID_ARGUMENT;
+    if (!mul_ok(m->num_rows, d->num_kv_heads, &t) || !mul_ok(t, m->block_size, &t) || !mul_ok(t, d->head_dim, &t) ||
+        !mul_ok(t, 4, &t))
+      return GQA_ERR_UNSUPPORTED;
+    if (!mul_ok(d->batch, m->max_blocks, &t)) return GQA_ERR_UNSUPPORTED;
+    // The matrix-core kernels take one block per 16-slot tile.
+    if (p.kernel != GQA_KERNEL_GENERIC && m->block_size % 16 != 0) return GQA_ERR_UNSUPPORTED;
+  } else {
+    if (!mul_ok(m->num_rows, d->num_kv_heads, &t) || !mul_ok(t, d->capacity, &t) || !mul_ok(t, d->head_dim, &t) ||
+        !mul_ok(t, 4, &t))
+      return GQA_ERR_UNSUPPORTED;
+  }
+  if (d->batch == 0) return GQA_OK;
+  if (m->map == nullptr || m->map_host == nullptr || (reinterpret_cast<uintptr_t>(m->map) & 3) != 0)
+    return GQA_ERR_INVALID_ARGUMENT;
+  const int32_t* h = m->map_host;
+  if (m->kind == GQA_MAP_SLOTS) {
+    std::vector<int32_t> v(h, h + d->batch);
+    for (int32_t x : v)
+      if (x < 0 || x >= m->num_rows) return GQA_ERR_INVALID_ARGUMENT;
+    std::sort(v.begin(), v.end());
+    if (std::adjacent_find(v.begin(), v.end()) != v.end()) return GQA_ERR_INVALID_ARGUMENT;
+  } else {
+    std::vector<int32_t> row;
+    for (int64_t b = 0; b < d->batch; ++b) {
+      row.clear();
+      for (int64_t j = 0; j < m->max_blocks; ++j) {
+        const int32_t x = h[b * m->max_blocks + j];
+        if (x == -1) continue;
+        if (x < 0 || x >= m->num_rows) return GQA_ERR_INVALID_ARGUMENT;
+        row.push_back(x);
+      }
+      std::sort(row.begin(), row.end());
+      if (std::adjacent_find(row.begin(), row.end()) != row.end()) return GQA_ERR_INVALID_ARGUMENT;
+    }
+  }
+  return GQA_OK;
+}
+
+// Elements of one cache tensor (K or V) and bytes of the device table.
+size_t cache_elems(const gqa_decode_desc_t* d, const gqa_cache_map_t* m) {
+  const size_t Hkv = d->num_kv_heads, S = d->capacity, D = d->head_dim;
+  if (m == nullptr) return (size_t)d->batch * Hkv * S * D;
+  if (m->kind == GQA_MAP_SLOTS) return (size_t)m->num_rows * Hkv * S * D;
+  return (size_t)m->num_rows * Hkv * (size_t)m->block_size * D;
+}
+size_t map_bytes(const gqa_decode_desc_t* d, const gqa_cache_map_t* m) {
+  if (m == nullptr) return 0;
+  return (size_t)d->batch * (m->kind == GQA_MAP_SLOTS ? 1 : (size_t)m->max_blocks) * 4;
+}
+
 void fill_args(const gqa_decode_desc_t* d, const Plan& p, AttnArgs* a) {
   std::memset(a, 0, sizeof(*a));
   a->B = d->batch;
@@ -150,10 +212,33 @@ void fill_args(const gqa_decode_desc_t* d, const Plan& p, AttnArgs* a) {
   a->scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d->head_dim));
 }
 
+// Map fields and pool strides of a mapped call (dense calls keep map_kind 0).
+void fill_map(const gqa_decode_desc_t* d, const gqa_cache_map_t* m, AttnArgs* a) {
+  if (m == nullptr) return;
+  a->map = m->map;
+  a->map_kind = m->kind;
+  a->map_rows = m->num_rows;
+  if (m->kind == GQA_MAP_PAGED) {
+    const int64_t bs = m->block_size, D = d->head_dim, Hkv = d->num_kv_heads;
+    a->bs = m->block_size;
+    a->max_blocks = m->max_blocks;
+    a->sblk = Hkv * bs * D;
+    if (d->layout == GQA_LAYOUT_BHSD) {  // pool (blocks, Hkv, bs, D)
+      a->sh = bs * D;
+      a->st = D;
+    } else {                             // pool (blocks, bs, Hkv, D)
+      a->sh = D;
+      a->st = Hkv * D;
+    }
+    a->sb = 0;
+  }
+}
+
 // Pointer checks shared by attend and step.  `k_new`/`v_new` are null for attend.
-gqa_status_t check_attend_ptrs(const gqa_decode_desc_t* d, const Plan& p, const void* q, const void* kc,
-                               const void* vc, const void* kn, const void* vn, const int32_t* lengths,
-                               const void* out, const void* ws, size_t ws_bytes, bool step) {
+gqa_status_t check_attend_ptrs(const gqa_decode_desc_t* d, const gqa_cache_map_t* m, const Plan& p, const void* q,
+                               const void* kc, const void* vc, const void* kn, const void* vn,
+                               const int32_t* lengths, const void* out, const void* ws, size_t ws_bytes,
+                               bool step) {
   const size_t ekv = elem_bytes(d->kv_dtype), eqo = elem_bytes(d->qo_dtype);
   if (!q || !kc || !vc || !lengths || !out) return GQA_ERR_INVALID_ARGUMENT;
   if (step && (!kn || !vn)) return GQA_ERR_INVALID_ARGUMENT;
@@ -172,10 +257,15 @@ gqa_status_t check_attend_ptrs(const gqa_decode_desc_t* d, const Plan& p, const 
   const size_t B = d->batch, Hq = d->num_q_heads, Hkv = d->num_kv_heads, S = d->capacity, D = d->head_dim;
   const Span s_out = span(out, B * Hq * D * eqo);
   const Span s_q = span(q, B * Hq * D * eqo);
-  const Span s_kc = span(kc, B * Hkv * S * D * ekv);
-  const Span s_vc = span(vc, B * Hkv * S * D * ekv);
+  (void)S;
+  const Span s_kc = span(kc, cache_elems(d, m) * ekv);
+  const Span s_vc = span(vc, cache_elems(d, m) * ekv);
   const Span s_len = span(lengths, B * 4);
   const Span s_ws = span(ws, p.workspace_bytes);
+  const Span s_map = span(m ? m->map : nullptr, map_bytes(d, m));
+  if (m != nullptr && (overlap(s_out, s_map) || (p.workspace_bytes > 0 && overlap(s_ws, s_map)) ||
+                       (step && (overlap(s_kc, s_map) || overlap(s_vc, s_map)))))
+    return GQA_ERR_INVALID_ARGUMENT;
   if (overlap(s_out, s_q) || overlap(s_out, s_kc) || overlap(s_out, s_vc) || overlap(s_out, s_len) ||
       (p.workspace_bytes > 0 && (overlap(s_out, s_ws) || overlap(s_ws, s_q) || overlap(s_ws, s_kc) ||
                                  overlap(s_ws, s_vc) || overlap(s_ws, s_len))))
@@ -246,34 +336,99 @@ gqa_status_t gqa_decode_get_plan(const gqa_decode_desc_t* desc, gqa_decode_plan_
   }
 }
 
+}  // extern "C"
+
+namespace {
+
+gqa_status_t do_append(const gqa_decode_desc_t* desc, const gqa_cache_map_t* map, void* k_cache, void* v_cache,
+                       const void* k_new, const void* v_new, const int32_t* lengths, void* stream) {
+  gqa_status_t st = check_desc(desc);
+  if (st != GQA_OK) return st;
+  Plan p;
+  std::memset(&p, 0, sizeof(p));
+  p.kernel = GQA_KERNEL_GENERIC;  // the append kernel takes any block size
+  p.nsplit = 1;
+  if (map != nullptr && (st = check_map(desc, map, p)) != GQA_OK) return st;
+  if (desc->batch == 0) return GQA_OK;
+  if (!k_cache || !v_cache || !k_new || !v_new || !lengths) return GQA_ERR_INVALID_ARGUMENT;
+  const size_t e = elem_bytes(desc->kv_dtype);
+  if (!aligned(k_cache, e) || !aligned(v_cache, e) || !aligned(k_new, e) || !aligned(v_new, e) ||
+      !aligned(lengths, 4))
+    return GQA_ERR_INVALID_ARGUMENT;
+  const size_t B = desc->batch, Hkv = desc->num_kv_heads, D = desc->head_dim;
+  const Span s_kc = span(k_cache, cache_elems(desc, map) * e), s_vc = span(v_cache, cache_elems(desc, map) * e);
+  const Span s_kn = span(k_new, B * Hkv * D * e), s_vn = span(v_new, B * Hkv * D * e);
+  const Span s_len = span(lengths, B * 4);
+  const Span s_map = span(map ? map->map : nullptr, map_bytes(desc, map));
+  if (overlap(s_kc, s_vc) || overlap(s_kn, s_kc) || overlap(s_kn, s_vc) || overlap(s_vn, s_kc) ||
+      overlap(s_vn, s_vc) || overlap(s_len, s_kc) || overlap(s_len, s_vc) || overlap(s_map, s_kc) ||
+      overlap(s_map, s_vc))
+    return GQA_ERR_INVALID_ARGUMENT;
+  AttnArgs a;
+  fill_args(desc, p, &a);
+  fill_map(desc, map, &a);
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.lengths = lengths;
+  if (launch_append(a, k_cache, v_cache, (hipStream_t)stream) != hipSuccess) return GQA_ERR_HIP;
+  return GQA_OK;
+}
+
+// Attend (step == false) or fused step (step == true), dense or mapped.
+gqa_status_t do_attend(const gqa_decode_desc_t* desc, const gqa_cache_map_t* map, const void* q, void* k_cache,
+                       void* v_cache, const void* k_new, const void* v_new, const int32_t* lengths, void* out,
+                       void* workspace, size_t workspace_bytes, void* stream, bool step) {
+  Plan p;
+  gqa_status_t st = make_plan(desc, &p);
+  if (st != GQA_OK) return st;
+  if (map != nullptr && (st = check_map(desc, map, p)) != GQA_OK) return st;
+  if (desc->batch == 0) return GQA_OK;
+  st = check_attend_ptrs(desc, map, p, q, k_cache, v_cache, step ? k_new : nullptr, step ? v_new : nullptr,
+                         lengths, out, workspace, workspace_bytes, step);
+  if (st != GQA_OK) return st;
+  AttnArgs a;
+  fill_args(desc, p, &a);
+  fill_map(desc, map, &a);
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.lengths = lengths;
+  a.out = out;
+  a.len_offset = step ? 1 : 0;
+  if (p.workspace_bytes > 0) {
+    char* w = static_cast<char*>(workspace);
+    a.part_o = reinterpret_cast<float*>(w);
+    a.part_m = reinterpret_cast<float*>(w + p.off_m);
+    a.part_l = reinterpret_cast<float*>(w + p.off_l);
+  }
+  if (step) {
+    a.k_new = k_new;
+    a.v_new = v_new;
+    if (p.kernel == GQA_KERNEL_GENERIC) {
+      // Generic path: the append kernel, then attention over lengths[b] + 1
+      // slots, ordered by the stream.
+      if (launch_append(a, k_cache, v_cache, (hipStream_t)stream) != hipSuccess) return GQA_ERR_HIP;
+      a.k_new = nullptr;
+      a.v_new = nullptr;
+    } else {
+      // Matrix-core paths fuse the append: the workgroup whose split holds
+      // slot lengths[b] takes the new K/V from k_new/v_new and writes it to
+      // the cache; no other workgroup reads that slot.
+      a.k_cache_w = k_cache;
+      a.v_cache_w = v_cache;
+    }
+  }
+  return run_attend(desc, p, a, (hipStream_t)stream);
+}
+
+}  // namespace
+
+extern "C" {
+
 gqa_status_t gqa_decode_append(const gqa_decode_desc_t* desc, void* k_cache, void* v_cache, const void* k_new,
                                const void* v_new, const int32_t* lengths, void* stream) {
   try {
-    gqa_status_t st = check_desc(desc);
-    if (st != GQA_OK) return st;
-    if (desc->batch == 0) return GQA_OK;
-    if (!k_cache || !v_cache || !k_new || !v_new || !lengths) return GQA_ERR_INVALID_ARGUMENT;
-    const size_t e = elem_bytes(desc->kv_dtype);
-    if (!aligned(k_cache, e) || !aligned(v_cache, e) || !aligned(k_new, e) || !aligned(v_new, e) ||
-        !aligned(lengths, 4))
-      return GQA_ERR_INVALID_ARGUMENT;
-    const size_t B = desc->batch, Hkv = desc->num_kv_heads, S = desc->capacity, D = desc->head_dim;
-    const Span s_kc = span(k_cache, B * Hkv * S * D * e), s_vc = span(v_cache, B * Hkv * S * D * e);
-    const Span s_kn = span(k_new, B * Hkv * D * e), s_vn = span(v_new, B * Hkv * D * e);
-    const Span s_len = span(lengths, B * 4);
-    if (overlap(s_kc, s_vc) || overlap(s_kn, s_kc) || overlap(s_kn, s_vc) || overlap(s_vn, s_kc) ||
-        overlap(s_vn, s_vc) || overlap(s_len, s_kc) || overlap(s_len, s_vc))
-      return GQA_ERR_INVALID_ARGUMENT;
-    Plan p;
-    std::memset(&p, 0, sizeof(p));
-    p.nsplit = 1;
-    AttnArgs a;
-    fill_args(desc, p, &a);
-    a.k_new = k_new;
-    a.v_new = v_new;
-    a.lengths = lengths;
-    if (launch_append(a, k_cache, v_cache, (hipStream_t)stream) != hipSuccess) return GQA_ERR_HIP;
-    return GQA_OK;
+    return do_append(desc, nullptr, k_cache, v_cache, k_new, v_new, lengths, stream);
   } catch (...) {
     return GQA_ERR_INTERNAL;
   }
@@ -283,28 +438,8 @@ gqa_status_t gqa_decode_attend(const gqa_decode_desc_t* desc, const void* q, con
                                const void* v_cache, const int32_t* lengths, void* out, void* workspace,
                                size_t workspace_bytes, void* stream) {
   try {
-    Plan p;
-    gqa_status_t st = make_plan(desc, &p);
-    if (st != GQA_OK) return st;
-    if (desc->batch == 0) return GQA_OK;
-    st = check_attend_ptrs(desc, p, q, k_cache, v_cache, nullptr, nullptr, lengths, out, workspace, workspace_bytes,
-                           false);
-    if (st != GQA_OK) return st;
-    AttnArgs a;
-    fill_args(desc, p, &a);
-    a.q = q;
-    a.k_cache = k_cache;
-    a.v_cache = v_cache;
-    a.lengths = lengths;
-    a.out = out;
-    a.len_offset = 0;
-    if (p.workspace_bytes > 0) {
-      char* w = static_cast<char*>(workspace);
-      a.part_o = reinterpret_cast<float*>(w);
-      a.part_m = reinterpret_cast<float*>(w + p.off_m);
-      a.part_l = reinterpret_cast<float*>(w + p.off_l);
-    }
-    return run_attend(desc, p, a, (hipStream_t)stream);
+    return do_attend(desc, nullptr, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache), nullptr, nullptr,
+                     lengths, out, workspace, workspace_bytes, stream, false);
   } catch (...) {
     return GQA_ERR_INTERNAL;
   }
@@ -314,41 +449,44 @@ gqa_status_t gqa_decode_step(const gqa_decode_desc_t* desc, const void* q, void*
                              const void* k_new, const void* v_new, const int32_t* lengths, void* out,
                              void* workspace, size_t workspace_bytes, void* stream) {
   try {
-    Plan p;
-    gqa_status_t st = make_plan(desc, &p);
-    if (st != GQA_OK) return st;
-    if (desc->batch == 0) return GQA_OK;
-    st = check_attend_ptrs(desc, p, q, k_cache, v_cache, k_new, v_new, lengths, out, workspace, workspace_bytes,
-                           true);
-    if (st != GQA_OK) return st;
-    AttnArgs a;
-    fill_args(desc, p, &a);
-    a.q = q;
-    a.k_cache = k_cache;
-    a.v_cache = v_cache;
-    a.k_new = k_new;
-    a.v_new = v_new;
-    a.lengths = lengths;
-    a.out = out;
-    a.len_offset = 1;
-    if (p.workspace_bytes > 0) {
-      char* w = static_cast<char*>(workspace);
-      a.part_o = reinterpret_cast<float*>(w);
-      a.part_m = reinterpret_cast<float*>(w + p.off_m);
-      a.part_l = reinterpret_cast<float*>(w + p.off_l);
-    }
-    if (p.kernel == GQA_KERNEL_GENERIC) {
-      // Generic path: the append kernel, then attention over lengths[b] + 1
-      // slots, ordered by the stream.
-      if (launch_append(a, k_cache, v_cache, (hipStream_t)stream) != hipSuccess) return GQA_ERR_HIP;
-    } else {
-      // Matrix-core paths fuse the append: the workgroup whose split holds
-      // slot lengths[b] takes the new K/V from k_new/v_new and writes it to
-      // the cache; no other workgroup reads that slot.
-      a.k_cache_w = k_cache;
-      a.v_cache_w = v_cache;
-    }
-    return run_attend(desc, p, a, (hipStream_t)stream);
+    return do_attend(desc, nullptr, q, k_cache, v_cache, k_new, v_new, lengths, out, workspace, workspace_bytes,
+                     stream, true);
+  } catch (...) {
+    return GQA_ERR_INTERNAL;
+  }
+}
+
+gqa_status_t gqa_decode_append_mapped(const gqa_decode_desc_t* desc, const gqa_cache_map_t* map, void* k_cache,
+                                      void* v_cache, const void* k_new, const void* v_new,
+                                      const int32_t* lengths, void* stream) {
+  try {
+    if (map == nullptr) return GQA_ERR_INVALID_ARGUMENT;
+    return do_append(desc, map, k_cache, v_cache, k_new, v_new, lengths, stream);
+  } catch (...) {
+    return GQA_ERR_INTERNAL;
+  }
+}
+
+gqa_status_t gqa_decode_attend_mapped(const gqa_decode_desc_t* desc, const gqa_cache_map_t* map, const void* q,
+                                      const void* k_cache, const void* v_cache, const int32_t* lengths, void* out,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    if (map == nullptr) return GQA_ERR_INVALID_ARGUMENT;
+    return do_attend(desc, map, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache), nullptr, nullptr,
+                     lengths, out, workspace, workspace_bytes, stream, false);
+  } catch (...) {
+    return GQA_ERR_INTERNAL;
+  }
+}
+
+gqa_status_t gqa_decode_step_mapped(const gqa_decode_desc_t* desc, const gqa_cache_map_t* map, const void* q,
+                                    void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                                    const int32_t* lengths, void* out, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  try {
+    if (map == nullptr) return GQA_ERR_INVALID_ARGUMENT;
+    return do_attend(desc, map, q, k_cache, v_cache, k_new, v_new, lengths, out, workspace, workspace_bytes, stream,
+                     true);
   } catch (...) {
     return GQA_ERR_INTERNAL;
   }

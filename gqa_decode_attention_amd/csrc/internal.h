@@ -24,7 +24,12 @@ struct AttnArgs {
   float* part_m;         // [B][Hq][nsplit] running max (log2 units)
   float* part_l;         // [B][Hq][nsplit] softmax denominators
   int32_t B, Hq, Hkv, D, S, G;
-  int64_t sb, sh, st;    // cache element strides of sequence, kv-head, slot
+  int64_t sb, sh, st;    // cache element strides of cache row, kv-head, slot (paged: within a block)
+  // Cache map (mapped entry points): map_kind 0 = dense (row b), GQA_MAP_SLOTS
+  // (row map[b]), GQA_MAP_PAGED (slot t in block map[b * max_blocks + t / bs]).
+  const int32_t* map;
+  int32_t map_kind, map_rows, bs, max_blocks;
+  int64_t sblk;          // paged: elements between pool blocks
   int32_t nsplit, split_tokens;
   int32_t head_chunks;   // generic kernel: query-head chunks per kv-head
   int32_t len_offset;    // slots attended = lengths[b] + len_offset (1 for a step, 0 for attend)

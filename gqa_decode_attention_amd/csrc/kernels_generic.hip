@@ -17,6 +17,7 @@
 // folded into the score scale.
 #include <mutex>
 
+#include "cache_map.h"
 #include "device_common.h"
 #include "internal.h"
 
@@ -28,34 +29,27 @@ constexpr float kNegInf = -__builtin_inff();
 // Append: one thread per element of the new K/V; raw copy of the stored bits.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256) void append_kernel(T* __restrict__ kc, T* __restrict__ vc,
-                                                     const T* __restrict__ kn, const T* __restrict__ vn,
-                                                     const int32_t* __restrict__ lengths, int32_t B,
-                                                     int32_t Hkv, int32_t D, int32_t S, int64_t sb, int64_t sh,
-                                                     int64_t st) {
+__global__ __launch_bounds__(256) void append_kernel(AttnArgs a, T* __restrict__ kc, T* __restrict__ vc) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = (int64_t)B * Hkv * D;
+  const int64_t total = (int64_t)a.B * a.Hkv * a.D;
   if (i >= total) return;
-  const int32_t d = (int32_t)(i % D);
-  const int64_t bh = i / D;
-  const int32_t h = (int32_t)(bh % Hkv);
-  const int32_t b = (int32_t)(bh / Hkv);
-  const int32_t pos = lengths[b];
-  if (pos < 0 || pos >= S) return;  // out of contract: nothing written
-  const int64_t off = b * sb + h * sh + (int64_t)pos * st + d;
-  kc[off] = kn[i];
-  vc[off] = vn[i];
+  const int32_t d = (int32_t)(i % a.D);
+  const int64_t bh = i / a.D;
+  const int32_t h = (int32_t)(bh % a.Hkv);
+  const int32_t b = (int32_t)(bh / a.Hkv);
+  const int32_t pos = a.lengths[b];
+  if (pos < 0 || pos >= a.S) return;  // out of contract: nothing written
+  const int64_t off = slot_offset_checked(a, b, h, pos);
+  if (off < 0) return;                // the map names no valid row/block
+  kc[off + d] = reinterpret_cast<const T*>(a.k_new)[i];
+  vc[off + d] = reinterpret_cast<const T*>(a.v_new)[i];
 }
 
 hipError_t launch_append(const AttnArgs& a, void* k_cache, void* v_cache, hipStream_t s) {
   const int64_t total = (int64_t)a.B * a.Hkv * a.D;
   const unsigned blocks = (unsigned)((total + 255) / 256);
-  const void* kn = a.k_new;
-  const void* vn = a.v_new;
-  const int32_t* lens = a.lengths;
-  int32_t B = a.B, Hkv = a.Hkv, D = a.D, S = a.S;
-  int64_t sb = a.sb, sh = a.sh, st = a.st;
-  void* params[] = {&k_cache, &v_cache, &kn, &vn, &lens, &B, &Hkv, &D, &S, &sb, &sh, &st};
+  AttnArgs arg = a;
+  void* params[] = {&arg, &k_cache, &v_cache};
   const void* fn = a.kv_dtype == GQA_F32 ? reinterpret_cast<const void*>(&append_kernel<uint32_t>)
                                          : reinterpret_cast<const void*>(&append_kernel<uint16_t>);
   return hipLaunchKernel(fn, dim3(blocks), dim3(256), params, 0, s);
@@ -131,12 +125,11 @@ __global__ __launch_bounds__(256) void attend_generic_kernel(AttnArgs a) {
     for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
   }
 
-  const int64_t base = (int64_t)b * a.sb + (int64_t)h * a.sh;
-  const char* kb = reinterpret_cast<const char*>(a.k_cache) + base * KB;
-  const char* vb = reinterpret_cast<const char*>(a.v_cache) + base * KB;
+  const char* kb = reinterpret_cast<const char*>(a.k_cache);
+  const char* vb = reinterpret_cast<const char*>(a.v_cache);
 
   for (int t = t_begin + rg; t < t_end; t += NRG) {
-    const int64_t row = (int64_t)t * a.st;
+    const int64_t row = slot_offset(a, b, h, t);
     float kv[EPL], vv[EPL];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {

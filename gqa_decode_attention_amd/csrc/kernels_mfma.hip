@@ -36,6 +36,7 @@
 // workgroup reads that slot, so the write cannot race a read.
 #include <type_traits>
 
+#include "cache_map.h"
 #include "device_common.h"
 #include "internal.h"
 
@@ -136,7 +137,7 @@ __device__ __forceinline__ void tile_update(WaveState<GP>& st, const u32x4 (&qf)
   }
 }
 
-template <int GP, int NW>
+template <int GP, int NW, bool PAGED>
 __global__ __launch_bounds__(64 * NW) void attend_mfma_qk_kernel(AttnArgs a) {
   __shared__ float sm_o[NW][GP][kD];
   __shared__ float sm_m[NW][GP];
@@ -168,15 +169,19 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qk_kernel(AttnArgs a) {
   const bool own_new = a.k_new != nullptr && L >= t_begin && L < t_end;
   const int t_cache_end = own_new ? L : t_end;
 
-  const int64_t base = (int64_t)b * a.sb + (int64_t)h * a.sh;
-  const int64_t rs = a.st;  // elements between consecutive slots
+  const int64_t base = PAGED ? 0 : row_head_offset(a, b, h);  // dense or slot-indexed row
+  const int64_t rs = a.st;  // elements between consecutive slots (paged: within a block)
 
   // Tile grid.  When a kv-head's slots are contiguous 256-byte rows, the
   // 16-slot tiles start at 4 KB-aligned cache addresses (measured faster than
   // tiles that straddle 4 KB boundaries); the grid then begins up to 15 slots
-  // before t_begin and those leading rows are masked.
+  // before t_begin and those leading rows are masked.  A paged cache (block
+  // size a multiple of 16) starts tiles at multiples of 16 slots, so a tile
+  // never crosses a block.
   int tv = t_begin;
-  if (rs == kD) {
+  if (PAGED) {
+    tv = t_begin & ~15;
+  } else if (rs == kD) {
     const uint64_t row = (reinterpret_cast<uintptr_t>(a.k_cache) >> 8) + (uint64_t)((base >> 7) + t_begin);
     tv = t_begin - (int)(row & 15);
   }
@@ -219,15 +224,33 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qk_kernel(AttnArgs a) {
   const uint32_t rsb = (uint32_t)rs * 2u;
   const char* kl = reinterpret_cast<const char*>(kb) + 16 * r;
   const char* vl = reinterpret_cast<const char*>(vb) + 16 * c;
-  auto load_tile = [&](int t0, u32x4 (&k)[4], u32x4 (&v)[4]) {
-    const uint32_t rk = (uint32_t)max(min(t0 + c, w1 - 1), t_begin);
-    const char* p = kl + (uint64_t)rk * rsb;
+  // Paged: a tile's rows lie in the block of its 16-slot origin tc (clamped
+  // into the wave's run, so prefetches past the end stay in a mapped block);
+  // `blk` is that block's table entry, loaded a tile pair ahead.
+  const int last16 = max((w1 - 1) & ~15, tv);
+  auto tile_origin = [&](int t0) { return max(min(t0, last16), tv); };
+  auto entry = [&](int t0) -> int32_t {
+    if (!PAGED) return 0;
+    return __builtin_amdgcn_readfirstlane(a.map[(int64_t)b * a.max_blocks + tile_origin(t0) / a.bs]);
+  };
+  auto load_tile = [&](int t0, u32x4 (&k)[4], u32x4 (&v)[4], int32_t blk) {
+    const char* kt = kl;
+    const char* vt = vl;
+    int tc = 0;
+    if (PAGED) {
+      tc = tile_origin(t0);
+      const int64_t off = (block_head_offset(a, blk, h) + (int64_t)(tc % a.bs) * rs) * 2;
+      kt = reinterpret_cast<const char*>(a.k_cache) + off + 16 * r;
+      vt = reinterpret_cast<const char*>(a.v_cache) + off + 16 * c;
+    }
+    const uint32_t rk = (uint32_t)(max(min(t0 + c, w1 - 1), t_begin) - tc);
+    const char* p = kt + (uint64_t)rk * rsb;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) k[kk] = load_nt16(p + 64 * kk);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t rv = (uint32_t)max(min(t0 + 4 * r + i, w1 - 1), t_begin);
-      v[i] = load_nt16(vl + (uint64_t)rv * rsb);
+      const uint32_t rv = (uint32_t)(max(min(t0 + 4 * r + i, w1 - 1), t_begin) - tc);
+      v[i] = load_nt16(vt + (uint64_t)rv * rsb);
     }
   };
 
@@ -246,7 +269,8 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qk_kernel(AttnArgs a) {
   // Two register sets alternate, so the next tile's loads are in flight during
   // this tile's math and no register copy waits for them.
   u32x4 ka[4], va[4], kc[4], vc[4];
-  load_tile(w0, ka, va);
+  int32_t eC = entry(w0 + 16), eA = entry(w0 + 32);  // table entries of the first tile pair's successors
+  load_tile(w0, ka, va, entry(w0));
   if (new_here) {
     const u32x4 vf[4] = {vnw, u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}};
     tile_update<GP>(st, qf, knw, vf, 0, 1, r, a.scale_log2);
@@ -255,22 +279,26 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qk_kernel(AttnArgs a) {
     const int nt = (w1 - w0 + 15) >> 4;
     int t0 = w0;
     for (int it = 0; it < nt / 2; ++it) {
-      load_tile(t0 + 16, kc, vc);
+      const int32_t nC = entry(t0 + 48), nA = entry(t0 + 64);
+      load_tile(t0 + 16, kc, vc, eC);
       tile_update<GP>(st, qf, ka, va, t_begin - t0, w1 - t0, r, a.scale_log2);
-      load_tile(t0 + 32, ka, va);  // past w1 it re-reads row w1 - 1
+      load_tile(t0 + 32, ka, va, eA);  // past w1 it re-reads row w1 - 1
       tile_update<GP>(st, qf, kc, vc, t_begin - t0 - 16, w1 - t0 - 16, r, a.scale_log2);
+      eC = nC;
+      eA = nA;
       t0 += 32;
     }
     if (nt & 1) tile_update<GP>(st, qf, ka, va, t_begin - t0, w1 - t0, r, a.scale_log2);
   }
   if (new_here) {
-    uint16_t* kw = reinterpret_cast<uint16_t*>(a.k_cache_w) + base + (int64_t)L * rs;
-    uint16_t* vw = reinterpret_cast<uint16_t*>(a.v_cache_w) + base + (int64_t)L * rs;
-    if (c == 0) {
+    const int64_t off = slot_offset_checked(a, b, h, L);  // -1: the map names no valid row/block
+    uint16_t* kw = reinterpret_cast<uint16_t*>(a.k_cache_w) + off;
+    uint16_t* vw = reinterpret_cast<uint16_t*>(a.v_cache_w) + off;
+    if (off >= 0 && c == 0) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) store16(kw + 32 * kk + 8 * r, knw[kk]);
     }
-    if (r == 0) store16(vw + 8 * c, vnw);
+    if (off >= 0 && r == 0) store16(vw + 8 * c, vnw);
   }
 
   // Merge the 4 rows of lanes of each wave (disjoint slots, same running max).
@@ -329,8 +357,9 @@ static hipError_t launch_qk_t(const AttnArgs& a, const Plan& p, hipStream_t s) {
   if (p.block != 64 * NW) return hipErrorInvalidValue;
   AttnArgs arg = a;
   void* params[] = {&arg};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&attend_mfma_qk_kernel<GP, NW>), dim3(p.grid), dim3(p.block),
-                         params, 0, s);
+  const void* fn = a.map_kind == GQA_MAP_PAGED ? reinterpret_cast<const void*>(&attend_mfma_qk_kernel<GP, NW, true>)
+                                               : reinterpret_cast<const void*>(&attend_mfma_qk_kernel<GP, NW, false>);
+  return hipLaunchKernel(fn, dim3(p.grid), dim3(p.block), params, 0, s);
 }
 
 hipError_t launch_attend_mfma_qk(const AttnArgs& a, const Plan& p, hipStream_t s) {
@@ -385,6 +414,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 
+template <bool PAGED>
 __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sk[2][kTileT * kPitch];
   __shared__ __attribute__((aligned(16))) uint16_t sv[2][kTileT * kPitch];
@@ -424,11 +454,16 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) O[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int64_t base = (int64_t)b * a.sb + (int64_t)h * a.sh;
+  const int64_t base = PAGED ? 0 : row_head_offset(a, b, h);  // dense or slot-indexed row
   const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.k_cache) + base;
   const uint16_t* vb = reinterpret_cast<const uint16_t*>(a.v_cache) + base;
   const int64_t rs = a.st;
   const int64_t nrow = ((int64_t)b * a.Hkv + h) * kD;
+  // Tile grid origin: the split start, or for a paged cache (block size a
+  // multiple of 16) the multiple of 16 at or below it, so each 16-row half of a
+  // tile lies in one block; rows before t_begin are clamped and masked.
+  const int tv = PAGED ? (t_begin & ~15) : t_begin;
+  const int last16 = max((t_end - 1) & ~15, tv);
 
   // Cooperative tile load: thread t moves 16 bytes (piece t & 15) of rows
   // t >> 4 and 16 + (t >> 4) of a 32-slot tile.  Rows past the split's last
@@ -450,11 +485,33 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
     kn = load16(reinterpret_cast<const uint16_t*>(a.k_new) + nrow + 8 * piece);
     vn = load16(reinterpret_cast<const uint16_t*>(a.v_new) + nrow + 8 * piece);
   }
-  auto gload = [&](int t0, Regs& R) {
+  // Paged: the table entries of a tile's two 16-row halves, loaded a tile pair
+  // before the tile itself (clamped into the split, like the rows).
+  struct Ent {
+    int32_t e[2];
+  };
+  auto entries = [&](int t0) -> Ent {
+    Ent en = {{0, 0}};
+    if (PAGED) {
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        const int hc = max(min(t0 + 16 * q2, last16), tv);
+        en.e[q2] = __builtin_amdgcn_readfirstlane(a.map[(int64_t)b * a.max_blocks + hc / a.bs]);
+      }
+    }
+    return en;
+  };
+  auto gload = [&](int t0, Regs& R, const Ent& en) {
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2) {
-      const int rc = min(t0 + prow + 16 * q2, t_end - 1);
-      const int64_t off = (int64_t)rc * rs + 8 * piece;
+      const int rc = max(min(t0 + prow + 16 * q2, t_end - 1), t_begin);
+      int64_t off;
+      if (PAGED) {
+        const int hc = max(min(t0 + 16 * q2, last16), tv);
+        off = block_head_offset(a, en.e[q2], h) + (int64_t)(hc % a.bs + (rc - hc)) * rs + 8 * piece;
+      } else {
+        off = (int64_t)rc * rs + 8 * piece;
+      }
       R.k[q2] = load_nt16(kb + off);
       R.v[q2] = load_nt16(vb + off);
     }
@@ -486,12 +543,13 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
     // Raw scores; the scale log2(e)/sqrt(D) is positive, so the maximum is
     // taken on raw scores and the scale is folded into the exponent's fma.
     float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-    if (t0 + kTileT > t_end) {  // the split's last, partial tile
+    if (t0 + kTileT > t_end || t0 < t_begin) {  // the split's first (paged) or last, partial tile
       const int valid = t_end - t0;
+      const int lo = t_begin - t0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (4 * r + i >= valid) sc[i] = kNegInfM;
-        if (16 + 4 * r + i >= valid) sc[4 + i] = kNegInfM;
+        if (4 * r + i >= valid || 4 * r + i < lo) sc[i] = kNegInfM;
+        if (16 + 4 * r + i >= valid || 16 + 4 * r + i < lo) sc[4 + i] = kNegInfM;
       }
     }
     float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
@@ -538,33 +596,40 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
   // every path issues the same loads, the loop has one exit, and each LDS write
   // waits only for its own tile's loads.
   if (t_begin < t_end) {
-    const int ntile = (t_end - t_begin + kTileT - 1) / kTileT;
+    const int ntile = (t_end - tv + kTileT - 1) / kTileT;
     Regs R0, R1;
-    gload(t_begin, R0);
-    gload(t_begin + kTileT, R1);
-    swrite(t_begin, 0, R0);
+    gload(tv, R0, entries(tv));
+    gload(tv + kTileT, R1, entries(tv + kTileT));
+    Ent e2 = entries(tv + 2 * kTileT), e3 = entries(tv + 3 * kTileT);
+    swrite(tv, 0, R0);
     __syncthreads();
     int buf = 0;
-    int t0 = t_begin;
+    int t0 = tv;
     for (int it = 0; it < ntile / 2; ++it) {
-      gload(t0 + 2 * kTileT, R0);
+      const Ent n2 = entries(t0 + 4 * kTileT), n3 = entries(t0 + 5 * kTileT);
+      gload(t0 + 2 * kTileT, R0, e2);
       compute_tile(t0, buf);
       swrite(t0 + kTileT, buf ^ 1, R1);
       __syncthreads();
       buf ^= 1;
-      gload(t0 + 3 * kTileT, R1);
+      gload(t0 + 3 * kTileT, R1, e3);
       compute_tile(t0 + kTileT, buf);
       swrite(t0 + 2 * kTileT, buf ^ 1, R0);
       __syncthreads();
       buf ^= 1;
+      e2 = n2;
+      e3 = n3;
       t0 += 2 * kTileT;
     }
     if (ntile & 1) compute_tile(t0, buf);
   }
 
-  if (own_new && prow == 0) {  // the appended slot
-    store16(reinterpret_cast<uint16_t*>(a.k_cache_w) + base + (int64_t)L * rs + 8 * piece, kn);
-    store16(reinterpret_cast<uint16_t*>(a.v_cache_w) + base + (int64_t)L * rs + 8 * piece, vn);
+  if (own_new && prow == 0) {  // the appended slot (skipped if the map names no valid row/block)
+    const int64_t off = slot_offset_checked(a, b, h, L);
+    if (off >= 0) {
+      store16(reinterpret_cast<uint16_t*>(a.k_cache_w) + off + 8 * piece, kn);
+      store16(reinterpret_cast<uint16_t*>(a.v_cache_w) + off + 8 * piece, vn);
+    }
   }
 
   // Denominator and max per head: lane (r, c) holds head c; the output rows of
@@ -598,8 +663,9 @@ hipError_t launch_attend_mfma_all(const AttnArgs& a, const Plan& p, hipStream_t 
   if (a.D != kD || a.G > 64) return hipErrorInvalidValue;
   AttnArgs arg = a;
   void* params[] = {&arg};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&attend_mfma_all_kernel), dim3(p.grid), dim3(256), params, 0,
-                         s);
+  const void* fn = a.map_kind == GQA_MAP_PAGED ? reinterpret_cast<const void*>(&attend_mfma_all_kernel<true>)
+                                               : reinterpret_cast<const void*>(&attend_mfma_all_kernel<false>);
+  return hipLaunchKernel(fn, dim3(p.grid), dim3(256), params, 0, s);
 }
 
 }  // namespace gqa

@@ -262,3 +262,118 @@ def test_block_shapes():
         assert g.get_plan(desc(**kw))["block"] == 256
     p = g.get_plan(desc(batch=32, num_q_heads=32, num_kv_heads=8, capacity=4097))
     assert p["kernel"] == "mfma_qk" and p["grid"] == 256 and p["num_splits"] == 1
+
+
+# ---------------------------------------------------------------------------
+# Mapped caches: every refusal of the CLIKA groupQueryAttention page's rules
+# (slot rows in range and distinct; block entries -1 or in range, no block
+# twice within one row) and of the map's shape fields happens on the host,
+# before any HIP call.
+# ---------------------------------------------------------------------------
+import numpy as np  # noqa: E402
+
+
+def _map(kind, num_rows, table, block_size=0, max_blocks=0, dev=FAKE + 8 * GAP):
+    host = np.ascontiguousarray(np.asarray(table, dtype=np.int32))
+    m = _lib.MapT(_lib.MAP_KINDS[kind], num_rows, block_size, max_blocks, dev, host.ctypes.data)
+    return m, host
+
+
+def _mapped_calls(d, m):
+    L = g.lib()
+    p = _attend_ptrs()
+    return [
+        L.gqa_decode_attend_mapped(ctypes.byref(d), ctypes.byref(m), p["q"], p["kc"], p["vc"], p["lens"], p["out"],
+                                   p["ws"], 1 << 30, None),
+        L.gqa_decode_step_mapped(ctypes.byref(d), ctypes.byref(m), p["q"], p["kc"], p["vc"], p["kn"], p["vn"],
+                                 p["lens"], p["out"], p["ws"], 1 << 30, None),
+        L.gqa_decode_append_mapped(ctypes.byref(d), ctypes.byref(m), p["kc"], p["vc"], p["kn"], p["vn"], p["lens"],
+                                   None),
+    ]
+
+
+BAD_SLOTS = [
+    ([0, 4], 4),      # out of range
+    ([-1, 0], 4),     # negative
+    ([2, 2], 4),      # two rows share a cache row
+]
+
+
+@pytest.mark.parametrize("table,rows", BAD_SLOTS)
+def test_bad_slot_map_refused(table, rows):
+    m, keep = _map("slots", rows, table)
+    assert _mapped_calls(desc(), m) == [INVALID] * 3
+
+
+BAD_TABLES = [
+    [[0, 1, 2, 3], [4, 5, 6, 99]],    # entry past num_blocks
+    [[0, 1, 2, 3], [4, 5, -2, -1]],   # negative other than the -1 pad
+    [[0, 1, 0, -1], [4, 5, 6, 7]],    # block named twice within one row
+    [[0, -1, 3, 3], [4, 5, 6, 7]],    # repeat after a pad
+]
+
+
+@pytest.mark.parametrize("table", BAD_TABLES)
+def test_bad_block_table_refused(table):
+    m, keep = _map("paged", 16, table, block_size=1024, max_blocks=4)
+    assert _mapped_calls(desc(), m) == [INVALID] * 3
+
+
+@pytest.mark.parametrize("field,value", [("kind", 0), ("kind", 3), ("num_rows", 0), ("block_size", 0),
+                                         ("max_blocks", 0), ("block_size", 512)])   # 512 * 4 != capacity 4096
+def test_bad_map_shape_refused(field, value):
+    m, keep = _map("paged", 16, [[0, 1, 2, 3], [4, 5, 6, 7]], block_size=1024, max_blocks=4)
+    setattr(m, field, value)
+    assert _mapped_calls(desc(), m) == [INVALID] * 3
+
+
+def test_missing_or_misaligned_map_refused():
+    L = g.lib()
+    d = desc()
+    for dev, host_ok in ((0, True), (FAKE + 8 * GAP + 2, True), (FAKE + 8 * GAP, False)):
+        m, keep = _map("slots", 4, [1, 2], dev=dev)
+        if not host_ok:
+            m.map_host = None
+        assert _mapped_calls(d, m) == [INVALID] * 3
+    p = _attend_ptrs()
+    assert L.gqa_decode_attend_mapped(ctypes.byref(d), None, p["q"], p["kc"], p["vc"], p["lens"], p["out"], p["ws"],
+                                      1 << 30, None) == INVALID
+
+
+def test_matrix_core_paged_needs_block_multiple_of_16():
+    """bf16, D = 128, G = 4 is a matrix-core descriptor: a block size of 8 is
+    refused by attend and step (the append, which takes any block size, is not
+    called: this table is valid and it would launch)."""
+    L = g.lib()
+    m, keep = _map("paged", 1024, [list(range(0, 512)), list(range(512, 1024))], block_size=8, max_blocks=512)
+    d = desc()
+    p = _attend_ptrs()
+    assert L.gqa_decode_attend_mapped(ctypes.byref(d), ctypes.byref(m), p["q"], p["kc"], p["vc"], p["lens"], p["out"],
+                                      p["ws"], 1 << 30, None) == UNSUPPORTED
+    assert L.gqa_decode_step_mapped(ctypes.byref(d), ctypes.byref(m), p["q"], p["kc"], p["vc"], p["kn"], p["vn"],
+                                    p["lens"], p["out"], p["ws"], 1 << 30, None) == UNSUPPORTED
+
+
+def test_map_overlapping_output_or_caches_refused():
+    L = g.lib()
+    p = _attend_ptrs()
+    d = desc()
+    m, keep = _map("slots", 4, [1, 2], dev=p["out"])
+    assert L.gqa_decode_attend_mapped(ctypes.byref(d), ctypes.byref(m), p["q"], p["kc"], p["vc"], p["lens"], p["out"],
+                                      p["ws"], 1 << 30, None) == INVALID
+    m, keep = _map("slots", 4, [1, 2], dev=p["kc"])       # the step and the append write the caches
+    assert L.gqa_decode_step_mapped(ctypes.byref(d), ctypes.byref(m), p["q"], p["kc"], p["vc"], p["kn"], p["vn"],
+                                    p["lens"], p["out"], p["ws"], 1 << 30, None) == INVALID
+    assert L.gqa_decode_append_mapped(ctypes.byref(d), ctypes.byref(m), p["kc"], p["vc"], p["kn"], p["vn"], p["lens"],
+                                      None) == INVALID
+
+
+def test_mapped_empty_batch_is_a_noop():
+    L = g.lib()
+    d = desc(batch=0)
+    m = _lib.MapT(_lib.MAP_KINDS["paged"], 4, 1024, 4, None, None)
+    assert L.gqa_decode_attend_mapped(ctypes.byref(d), ctypes.byref(m), None, None, None, None, None, None, 0,
+                                      None) == OK
+    assert L.gqa_decode_step_mapped(ctypes.byref(d), ctypes.byref(m), None, None, None, None, None, None, None, None,
+                                    0, None) == OK
+    assert L.gqa_decode_append_mapped(ctypes.byref(d), ctypes.byref(m), None, None, None, None, None, None) == OK

@@ -120,6 +120,65 @@ def make_inputs(w: Workload, device="cpu", lengths: torch.Tensor | None = None) 
                 lengths=L.to(device))
 
 
+def make_mapped(inp: dict, w: Workload, kind: str, *, block_size: int = 16, num_rows: int | None = None,
+                spare_blocks: int = 7, seed: int = 0) -> dict:
+    """The same logical caches stored through a map (data movement only).
+
+    ``kind == "slots"``: a continuous cache of ``num_rows`` rows (default 2B+1);
+    batch row b lives at row ``map[b]`` of a seeded permutation.  ``"paged"``:
+    a pool of ``B * ceil(S / block_size) + spare_blocks`` blocks; the table maps
+    each sequence's blocks to a seeded permutation of the pool.  Cache rows or
+    blocks that no sequence maps, and the slots past the capacity in the last
+    block, hold NaN bit patterns.  Returns a dict like ``inp`` with
+    k_cache/v_cache replaced, plus ``map`` (int32, same device) and, for a
+    paged cache, ``block_size`` and the mapped capacity (a multiple of it).
+    """
+    gen = torch.Generator().manual_seed(1000 + w.seed * 17 + seed)
+    dev = inp["k_cache"].device
+    B, Hkv, D, S = w.B, w.Hkv, w.D, w.capacity
+    kc, vc = inp["k_cache"], inp["v_cache"]
+    nan_bits = 0x7FC1 if kc.dtype == torch.bfloat16 else 0x7FC00001
+    itype = torch.int16 if kc.dtype == torch.bfloat16 else torch.int32
+
+    def garbage(shape):
+        return torch.full(shape, nan_bits, dtype=itype, device=dev).view(kc.dtype)
+
+    out = dict(inp)
+    if kind == "slots":
+        R = num_rows if num_rows is not None else 2 * B + 1
+        slot_ids = torch.randperm(R, generator=gen)[:B].to(torch.int32)
+        for name, c in (("k_cache", kc), ("v_cache", vc)):
+            m = garbage((R,) + tuple(c.shape[1:]))
+            m[slot_ids.to(dev).long()] = c
+            out[name] = m
+        out["map"] = slot_ids.to(dev)
+        out["capacity"] = S
+        return out
+    if kind != "paged":
+        raise ValueError(kind)
+    bs = block_size
+    nb = -(-S // bs)
+    total = B * nb + spare_blocks
+    table = torch.randperm(total, generator=gen)[: B * nb].to(torch.int32).view(B, nb)
+    idx = table.to(dev).long().flatten()
+    pad = nb * bs - S
+    for name, c in (("k_cache", kc), ("v_cache", vc)):
+        if w.layout == "BHSD":                                   # (B, Hkv, S, D) -> blocks (B*nb, Hkv, bs, D)
+            full = torch.cat([c, garbage((B, Hkv, pad, D))], dim=2) if pad else c
+            blocks = full.view(B, Hkv, nb, bs, D).permute(0, 2, 1, 3, 4).reshape(B * nb, Hkv, bs, D)
+            pool = garbage((total, Hkv, bs, D))
+        else:                                                    # (B, S, Hkv, D) -> blocks (B*nb, bs, Hkv, D)
+            full = torch.cat([c, garbage((B, pad, Hkv, D))], dim=1) if pad else c
+            blocks = full.view(B, nb, bs, Hkv, D).reshape(B * nb, bs, Hkv, D)
+            pool = garbage((total, bs, Hkv, D))
+        pool[idx] = blocks
+        out[name] = pool
+    out["map"] = table.to(dev)
+    out["block_size"] = bs
+    out["capacity"] = nb * bs
+    return out
+
+
 def to_numpy_storage(t: torch.Tensor) -> np.ndarray:
     """A tensor's stored bits as the oracle takes them: float32, or uint16 bf16 patterns."""
     t = t.detach().cpu().contiguous()
