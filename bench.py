@@ -115,6 +115,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama3_8b_layer")
     ap.add_argument("--num-splits", type=int, default=0, help="0 = the library's plan")
+    ap.add_argument("--cache", default="dense",
+                    help="dense (default), slots (slot-indexed rows), pagedN (pool of N-slot blocks in a "
+                         "seeded random order) or pagedNseq (blocks in pool order)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="only run a plain copy of this many MiB (counter calibration) and exit")
@@ -140,21 +143,41 @@ def main():
     inp = W.make_inputs(w, dev)
     L = inp["lengths"].cpu().numpy()
     nbytes = W.algorithmic_bytes(w, L)
+    desc = g.desc_for(inp["q"], inp["k_cache"], w.layout, args.num_splits)
+    plan = g.get_plan(desc)
+    kind, table = None, None
+    inp_dense = inp
+    if args.cache != "dense":
+        # The same logical caches stored through a map (slot-indexed rows or a
+        # block pool); the bytes the step must move are the same.
+        if args.cache == "slots":
+            kind, m = "slots", W.make_mapped(inp, w, "slots")
+        elif args.cache.startswith("paged"):
+            seq = args.cache.endswith("seq")          # pagedNseq: blocks in pool order
+            bs = int(args.cache[5:-3] if seq else args.cache[5:])
+            kind, m = "paged", W.make_mapped(inp, w, "paged", block_size=bs, shuffle=not seq)
+        else:
+            raise SystemExit(f"--cache {args.cache}: dense, slots or pagedN")
+        inp = {**inp, "k_cache": m["k_cache"], "v_cache": m["v_cache"]}
+        table = m["map"]
+        table_host = table.cpu()      # the host copy the library validates, made once
     kv_bytes = 2 * inp["k_cache"].numel() * inp["k_cache"].element_size()
     # Rotate over R cache copies so one rotation touches over 3x the Infinity
     # Cache; a workload too small to matter (16 copies would still fit) uses one.
     R = min(16, math.ceil(3 * MALL_BYTES / kv_bytes)) if 16 * kv_bytes >= MALL_BYTES else 1
     caches = [(inp["k_cache"], inp["v_cache"])] + [(inp["k_cache"].clone(), inp["v_cache"].clone())
                                                     for _ in range(R - 1)]
-    desc = g.desc_for(inp["q"], inp["k_cache"], w.layout, args.num_splits)
-    plan = g.get_plan(desc)
     ws = torch.empty(max(plan["workspace_bytes"], 1), dtype=torch.uint8, device=dev)
     out = torch.empty_like(inp["q"])
 
     def step(i):
         kc, vc = caches[i % R]
-        g.step(inp["q"], kc, vc, inp["k_new"], inp["v_new"], inp["lengths"], layout=w.layout, out=out,
-               workspace=ws, num_splits=args.num_splits)
+        if kind is None:
+            g.step(inp["q"], kc, vc, inp["k_new"], inp["v_new"], inp["lengths"], layout=w.layout, out=out,
+                   workspace=ws, num_splits=args.num_splits)
+        else:
+            g.step_mapped(inp["q"], kc, vc, inp["k_new"], inp["v_new"], inp["lengths"], table, kind=kind,
+                          layout=w.layout, out=out, workspace=ws, num_splits=args.num_splits, table_host=table_host)
 
     for i in range(args.warmup):
         step(i)
@@ -172,7 +195,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, inp)
+        cpu = cpu_baseline(w, inp_dense)   # the dense oracle on the same logical caches
 
     kv = "bf16" if w.kv_dtype == "bf16" else "f32"
     line = {
@@ -191,12 +214,13 @@ def main():
         "data": "synthetic",
         "steps_per_sec": round(1000.0 / ms, 2),
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
-        "config": {"workload": w.name, "batch": w.B, "num_q_heads": w.Hq, "num_kv_heads": w.Hkv, "head_dim": w.D,
+        "config": {"workload": w.name, "cache": args.cache, "batch": w.B, "num_q_heads": w.Hq, "num_kv_heads": w.Hkv, "head_dim": w.D,
                    "capacity": w.capacity, "layout": w.layout, "kv_dtype": w.kv_dtype, "qo_dtype": w.qo_dtype,
                    "tokens_attended": int((L + 1).sum()), "algorithmic_bytes_per_step": nbytes,
                    "cache_rotation": R, "plan": plan},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(w.name),
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profiles(w.name) if args.cache == "dense" else None,
                      "per": "one gqa_decode_step call (attention kernel + split combine), HIP events over the "
                             "timed region"},
         "cpu_baseline": cpu,

@@ -248,8 +248,14 @@ def check_lengths(lengths, capacity, *, mode="step"):
     return int(n.value)
 
 
-def _mapped_desc(q_like_B, Hq, D, kv_dtype, qo_dtype, k_cache, kind, layout, table, num_splits, Hkv=None):
-    """Descriptor and gqa_cache_map_t for a mapped call (kept alive by the caller)."""
+def _mapped_desc(q_like_B, Hq, D, kv_dtype, qo_dtype, k_cache, kind, layout, table, num_splits, Hkv=None,
+                 table_host=None):
+    """Descriptor and gqa_cache_map_t for a mapped call (kept alive by the caller).
+
+    ``table`` is the device table the kernels read; ``table_host`` the same
+    entries in host memory, which the library validates.  Without
+    ``table_host`` the binding copies ``table`` to the host, which waits for the
+    stream: pass the host copy in a decode loop."""
     if kind not in MAP_KINDS:
         raise ValueError(f"kind must be one of {list(MAP_KINDS)}")
     if layout not in LAYOUTS:
@@ -265,8 +271,15 @@ def _mapped_desc(q_like_B, Hq, D, kv_dtype, qo_dtype, k_cache, kind, layout, tab
         raise ValueError("cache disagrees on head_dim or kv-heads")
     if table.dtype != torch.int32:
         raise ValueError("the map is int32")
-    host = table.detach().to("cpu").contiguous()
-    dev_t = table.to(k_cache.device).contiguous()
+    if table_host is None:
+        host = table.detach().to("cpu").contiguous()
+    else:
+        host = torch.as_tensor(table_host, dtype=torch.int32).contiguous()
+        if host.device.type != "cpu" or host.shape != table.shape:
+            raise ValueError("table_host must be a host copy of table")
+    if table.device != k_cache.device or not table.is_contiguous():
+        raise ValueError("table must be contiguous on the caches' device")
+    dev_t = table
     if kind == "slots":
         if host.dim() != 1 or host.shape[0] != q_like_B:
             raise ValueError("slot map is (B,)")
@@ -281,12 +294,12 @@ def _mapped_desc(q_like_B, Hq, D, kv_dtype, qo_dtype, k_cache, kind, layout, tab
     return desc, m, (host, dev_t)
 
 
-def append_mapped(k_cache, v_cache, k_new, v_new, lengths, table, *, kind, layout="BHSD"):
+def append_mapped(k_cache, v_cache, k_new, v_new, lengths, table, *, kind, layout="BHSD", table_host=None):
     """In-place append at slot lengths[b] of a slot-indexed cache or a block pool."""
     dev = _dev([k_cache, v_cache, k_new, v_new], lengths)
     B, Hkv, D = k_new.shape
     code = _dtype_code(k_cache.dtype)
-    desc, m, keep = _mapped_desc(B, Hkv, D, code, code, k_cache, kind, layout, table, 0, Hkv)
+    desc, m, keep = _mapped_desc(B, Hkv, D, code, code, k_cache, kind, layout, table, 0, Hkv, table_host)
     check(lib().gqa_decode_append_mapped(ctypes.byref(desc), ctypes.byref(m), k_cache.data_ptr(), v_cache.data_ptr(),
                                          k_new.data_ptr(), v_new.data_ptr(), lengths.data_ptr(), _stream(dev)),
           "gqa_decode_append_mapped")
@@ -294,12 +307,12 @@ def append_mapped(k_cache, v_cache, k_new, v_new, lengths, table, *, kind, layou
 
 
 def attend_mapped(q, k_cache, v_cache, lengths, table, *, kind, layout="BHSD", out=None, workspace=None,
-                  num_splits=0):
+                  num_splits=0, table_host=None):
     """Read-only attention over a slot-indexed cache or a block pool. Returns out (B, Hq, D)."""
     dev = _dev([q, k_cache, v_cache], lengths)
     B, Hq, D = q.shape
     desc, m, keep = _mapped_desc(B, Hq, D, _dtype_code(k_cache.dtype), _dtype_code(q.dtype), k_cache, kind, layout,
-                                 table, num_splits)
+                                 table, num_splits, None, table_host)
     if out is None:
         out = torch.empty_like(q)
     workspace, wptr, wbytes = _workspace(desc, dev, workspace)
@@ -311,12 +324,12 @@ def attend_mapped(q, k_cache, v_cache, lengths, table, *, kind, layout="BHSD", o
 
 
 def step_mapped(q, k_cache, v_cache, k_new, v_new, lengths, table, *, kind, layout="BHSD", out=None, workspace=None,
-                num_splits=0):
+                num_splits=0, table_host=None):
     """Fused decode step on a slot-indexed cache or a block pool. Returns out (B, Hq, D)."""
     dev = _dev([q, k_cache, v_cache, k_new, v_new], lengths)
     B, Hq, D = q.shape
     desc, m, keep = _mapped_desc(B, Hq, D, _dtype_code(k_cache.dtype), _dtype_code(q.dtype), k_cache, kind, layout,
-                                 table, num_splits, k_new.shape[1])
+                                 table, num_splits, k_new.shape[1], table_host)
     if out is None:
         out = torch.empty_like(q)
     workspace, wptr, wbytes = _workspace(desc, dev, workspace)

@@ -150,25 +150,37 @@ gqa_status_t check_map(const gqa_decode_desc_t* d, const gqa_cache_map_t* m, con
   if (d->batch == 0) return GQA_OK;
   if (m->map == nullptr || m->map_host == nullptr || (reinterpret_cast<uintptr_t>(m->map) & 3) != 0)
     return GQA_ERR_INVALID_ARGUMENT;
+  // One pass over the table: a per-thread stamp array (one word per cache row
+  // or pool block, grown on demand and reused across calls) marks the entries
+  // seen in the current group -- the whole slot map, or one table row -- so a
+  // repeat is found in O(1) without sorting.
+  thread_local std::vector<uint32_t> stamp;
+  thread_local uint32_t epoch = 0;
+  if (stamp.size() < (size_t)m->num_rows) stamp.assign((size_t)m->num_rows, 0u);
+  auto next_epoch = [&]() {
+    if (++epoch == 0) {  // wrapped: forget every old mark
+      std::fill(stamp.begin(), stamp.end(), 0u);
+      epoch = 1;
+    }
+  };
   const int32_t* h = m->map_host;
   if (m->kind == GQA_MAP_SLOTS) {
-    std::vector<int32_t> v(h, h + d->batch);
-    for (int32_t x : v)
-      if (x < 0 || x >= m->num_rows) return GQA_ERR_INVALID_ARGUMENT;
-    std::sort(v.begin(), v.end());
-    if (std::adjacent_find(v.begin(), v.end()) != v.end()) return GQA_ERR_INVALID_ARGUMENT;
-  } else {
-    std::vector<int32_t> row;
+    next_epoch();
     for (int64_t b = 0; b < d->batch; ++b) {
-      row.clear();
+      const int32_t x = h[b];
+      if (x < 0 || x >= m->num_rows || stamp[x] == epoch) return GQA_ERR_INVALID_ARGUMENT;
+      stamp[x] = epoch;
+    }
+  } else {
+    for (int64_t b = 0; b < d->batch; ++b) {
+      next_epoch();
+      const int32_t* row = h + b * (int64_t)m->max_blocks;
       for (int64_t j = 0; j < m->max_blocks; ++j) {
-        const int32_t x = h[b * m->max_blocks + j];
+        const int32_t x = row[j];
         if (x == -1) continue;
-        if (x < 0 || x >= m->num_rows) return GQA_ERR_INVALID_ARGUMENT;
-        row.push_back(x);
+        if (x < 0 || x >= m->num_rows || stamp[x] == epoch) return GQA_ERR_INVALID_ARGUMENT;
+        stamp[x] = epoch;
       }
-      std::sort(row.begin(), row.end());
-      if (std::adjacent_find(row.begin(), row.end()) != row.end()) return GQA_ERR_INVALID_ARGUMENT;
     }
   }
   return GQA_OK;

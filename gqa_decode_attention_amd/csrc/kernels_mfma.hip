@@ -226,12 +226,13 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qk_kernel(AttnArgs a) {
   const char* vl = reinterpret_cast<const char*>(vb) + 16 * c;
   // Paged: a tile's rows lie in the block of its 16-slot origin tc (clamped
   // into the wave's run, so prefetches past the end stay in a mapped block);
-  // `blk` is that block's table entry, loaded a tile pair ahead.
+  // `blk` is that block's table entry, loaded a tile pair ahead and kept in a
+  // vector register until its tile is loaded (its wait is then far behind it).
   const int last16 = max((w1 - 1) & ~15, tv);
   auto tile_origin = [&](int t0) { return max(min(t0, last16), tv); };
   auto entry = [&](int t0) -> int32_t {
     if (!PAGED) return 0;
-    return __builtin_amdgcn_readfirstlane(a.map[(int64_t)b * a.max_blocks + tile_origin(t0) / a.bs]);
+    return a.map[(int64_t)b * a.max_blocks + tile_origin(t0) / a.bs];
   };
   auto load_tile = [&](int t0, u32x4 (&k)[4], u32x4 (&v)[4], int32_t blk) {
     const char* kt = kl;
@@ -496,7 +497,7 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2) {
         const int hc = max(min(t0 + 16 * q2, last16), tv);
-        en.e[q2] = __builtin_amdgcn_readfirstlane(a.map[(int64_t)b * a.max_blocks + hc / a.bs]);
+        en.e[q2] = a.map[(int64_t)b * a.max_blocks + hc / a.bs];
       }
     }
     return en;

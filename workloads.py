@@ -121,13 +121,14 @@ def make_inputs(w: Workload, device="cpu", lengths: torch.Tensor | None = None) 
 
 
 def make_mapped(inp: dict, w: Workload, kind: str, *, block_size: int = 16, num_rows: int | None = None,
-                spare_blocks: int = 7, seed: int = 0) -> dict:
+                spare_blocks: int = 7, seed: int = 0, shuffle: bool = True) -> dict:
     """The same logical caches stored through a map (data movement only).
 
     ``kind == "slots"``: a continuous cache of ``num_rows`` rows (default 2B+1);
     batch row b lives at row ``map[b]`` of a seeded permutation.  ``"paged"``:
     a pool of ``B * ceil(S / block_size) + spare_blocks`` blocks; the table maps
-    each sequence's blocks to a seeded permutation of the pool.  Cache rows or
+    each sequence's blocks to a seeded permutation of the pool (``shuffle=False``:
+    to consecutive blocks in order).  Cache rows or
     blocks that no sequence maps, and the slots past the capacity in the last
     block, hold NaN bit patterns.  Returns a dict like ``inp`` with
     k_cache/v_cache replaced, plus ``map`` (int32, same device) and, for a
@@ -159,7 +160,8 @@ def make_mapped(inp: dict, w: Workload, kind: str, *, block_size: int = 16, num_
     bs = block_size
     nb = -(-S // bs)
     total = B * nb + spare_blocks
-    table = torch.randperm(total, generator=gen)[: B * nb].to(torch.int32).view(B, nb)
+    order = torch.randperm(total, generator=gen) if shuffle else torch.arange(total)
+    table = order[: B * nb].to(torch.int32).view(B, nb)
     idx = table.to(dev).long().flatten()
     pad = nb * bs - S
     for name, c in (("k_cache", kc), ("v_cache", vc)):
