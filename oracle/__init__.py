@@ -23,3 +23,10 @@ from .mapped import (  # noqa: F401
     validate_slots,
     validate_table,
 )
+from .quant import (  # noqa: F401
+    append_q8,
+    attend_q8,
+    dequantize,
+    quantize_row,
+    step_q8,
+)
