@@ -68,14 +68,20 @@ def cpu_baseline(w, inp, budget_s=12.0):
     except Exception:  # pragma: no cover
         threads = 1
     L = inp["lengths"].cpu().numpy()
+    q8 = w.kv_dtype == "i8"
+    names = ("q", "k_cache", "v_cache", "k_new", "v_new") + (("k_scale", "v_scale") if q8 else ())
 
     def host(nb):
-        return {k: W.to_numpy_storage(inp[k][:nb]) for k in ("q", "k_cache", "v_cache", "k_new", "v_new")}
+        return {k: W.to_numpy_storage(inp[k][:nb]) for k in names}
 
     def run(st, nb):
         t0 = time.perf_counter()
-        oracle.step(st["q"], w.qo_dtype, st["k_cache"], st["v_cache"], st["k_new"], st["v_new"], w.kv_dtype, L[:nb],
-                    w.layout, w.Hq, w.Hkv)
+        if q8:
+            oracle.step_q8(st["q"], w.qo_dtype, st["k_cache"], st["v_cache"], st["k_scale"], st["v_scale"],
+                           st["k_new"], st["v_new"], L[:nb], w.layout, w.Hq, w.Hkv)
+        else:
+            oracle.step(st["q"], w.qo_dtype, st["k_cache"], st["v_cache"], st["k_new"], st["v_new"], w.kv_dtype,
+                        L[:nb], w.layout, w.Hq, w.Hkv)
         return time.perf_counter() - t0
 
     st1 = host(1)
@@ -89,7 +95,7 @@ def cpu_baseline(w, inp, budget_s=12.0):
     sub = W.Workload(**{**w.__dict__, "B": nb})
     nbytes = W.algorithmic_bytes(sub, L[:nb]) * reps
     gbs = nbytes / t / 1e9
-    sample = (f"oracle.step over sequences 0..{nb - 1} of {w.B} (all {w.Hq} query heads) of the same inputs, "
+    sample = (f"oracle.{'step_q8' if q8 else 'step'} over sequences 0..{nb - 1} of {w.B} (all {w.Hq} query heads) of the same inputs, "
               f"{reps} repetition(s), {t:.1f} s")
     return {"value": round(gbs, 6), "unit": "GB/s", "cores": threads, "kind": "oracle", "sample": sample,
             "steps_per_sec_equiv": round(gbs * 1e9 / W.algorithmic_bytes(w, L), 6),
@@ -118,6 +124,9 @@ def main():
     ap.add_argument("--cache", default="dense",
                     help="dense (default), slots (slot-indexed rows), pagedN (pool of N-slot blocks in a "
                          "seeded random order) or pagedNseq (blocks in pool order)")
+    ap.add_argument("--kv", default="native", choices=["native", "int8"],
+                    help="native: the workload's cache dtype; int8: int8 codes with per-row float32 scales "
+                         "(the step quantizes the new rows)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="only run a plain copy of this many MiB (counter calibration) and exit")
@@ -140,7 +149,14 @@ def main():
     g.lib()
     w = W.WORKLOADS[args.workload]
     dev = "cuda"
-    inp = W.make_inputs(w, dev)
+    q8 = args.kv == "int8"
+    if q8:
+        if args.cache != "dense":
+            raise SystemExit("--kv int8 takes dense caches")
+        w = W.Workload(**{**w.__dict__, "kv_dtype": "i8"})
+        inp = W.make_q8(w, dev)
+    else:
+        inp = W.make_inputs(w, dev)
     L = inp["lengths"].cpu().numpy()
     nbytes = W.algorithmic_bytes(w, L)
     desc = g.desc_for(inp["q"], inp["k_cache"], w.layout, args.num_splits)
@@ -162,17 +178,23 @@ def main():
         table = m["map"]
         table_host = table.cpu()      # the host copy the library validates, made once
     kv_bytes = 2 * inp["k_cache"].numel() * inp["k_cache"].element_size()
+    if q8:
+        kv_bytes += 2 * inp["k_scale"].numel() * 4
     # Rotate over R cache copies so one rotation touches over 3x the Infinity
     # Cache; a workload too small to matter (16 copies would still fit) uses one.
     R = min(16, math.ceil(3 * MALL_BYTES / kv_bytes)) if 16 * kv_bytes >= MALL_BYTES else 1
-    caches = [(inp["k_cache"], inp["v_cache"])] + [(inp["k_cache"].clone(), inp["v_cache"].clone())
-                                                    for _ in range(R - 1)]
+    names = ("k_cache", "v_cache") + (("k_scale", "v_scale") if q8 else ())
+    caches = [tuple(inp[n] for n in names)] + [tuple(inp[n].clone() for n in names) for _ in range(R - 1)]
     ws = torch.empty(max(plan["workspace_bytes"], 1), dtype=torch.uint8, device=dev)
     out = torch.empty_like(inp["q"])
 
     def step(i):
-        kc, vc = caches[i % R]
-        if kind is None:
+        kc, vc = caches[i % R][:2]
+        if q8:
+            ks, vs = caches[i % R][2:]
+            g.step_q8(inp["q"], kc, vc, ks, vs, inp["k_new"], inp["v_new"], inp["lengths"], layout=w.layout, out=out,
+                      workspace=ws, num_splits=args.num_splits)
+        elif kind is None:
             g.step(inp["q"], kc, vc, inp["k_new"], inp["v_new"], inp["lengths"], layout=w.layout, out=out,
                    workspace=ws, num_splits=args.num_splits)
         else:
@@ -197,7 +219,7 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, inp_dense)   # the dense oracle on the same logical caches
 
-    kv = "bf16" if w.kv_dtype == "bf16" else "f32"
+    kv = {"bf16": "bf16", "f32": "f32", "i8": "i8+f32 row scales"}[w.kv_dtype]
     line = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -220,7 +242,7 @@ def main():
                    "cache_rotation": R, "plan": plan},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_from_profiles(w.name) if args.cache == "dense" else None,
+                     "traffic": traffic_from_profiles(w.name) if args.cache == "dense" and not q8 else None,
                      "per": "one gqa_decode_step call (attention kernel + split combine), HIP events over the "
                             "timed region"},
         "cpu_baseline": cpu,

@@ -3,21 +3,27 @@
 Python face of the HIP library ``libgqa_decode.so`` (C ABI in
 ``include/gqa_decode.h``): ``append`` writes each sequence's new key/value at
 slot ``lengths[b]`` of a fixed-capacity cache, ``attend`` runs length-masked
-GQA attention over the cache, and ``step`` does both in one call.  torch is
+GQA attention over the cache, and ``step`` does both in one call; the
+``_mapped`` calls take slot-indexed or paged caches and the ``_q8`` calls int8
+caches with per-row scales.  torch is
 used for device memory and streams only.
 """
 from ._lib import (  # noqa: F401
     BF16,
     EXPORTS,
     F32,
+    I8,
     LIB_PATH,
     Desc,
     GqaError,
     MapT,
+    ScalesT,
     append,
+    append_q8,
     append_mapped,
     attend,
     attend_mapped,
+    attend_q8,
     check_lengths,
     desc_for,
     get_plan,
@@ -25,5 +31,6 @@ from ._lib import (  # noqa: F401
     make_desc,
     step,
     step_mapped,
+    step_q8,
     workspace_size,
 )

@@ -22,7 +22,7 @@ STATUS_NAMES = {
     4: "GQA_ERR_HIP",
     5: "GQA_ERR_INTERNAL",
 }
-F32, BF16 = 0, 1
+F32, BF16, I8 = 0, 1, 2
 LAYOUTS = {"BHSD": 0, "BSHD": 1}
 KERNEL_NAMES = {0: "generic", 1: "mfma_qk", 2: "mfma_all"}
 
@@ -74,6 +74,11 @@ class MapT(ctypes.Structure):
     ]
 
 
+class ScalesT(ctypes.Structure):
+    """gqa_kv_scales_t."""
+    _fields_ = [("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
+
+
 EXPORTS = (
     "gqa_decode_workspace_size",
     "gqa_decode_get_plan",
@@ -83,6 +88,9 @@ EXPORTS = (
     "gqa_decode_append_mapped",
     "gqa_decode_attend_mapped",
     "gqa_decode_step_mapped",
+    "gqa_decode_append_q8",
+    "gqa_decode_attend_q8",
+    "gqa_decode_step_q8",
     "gqa_decode_check_lengths",
     "gqa_decode_status_string",
     "gqa_decode_version",
@@ -111,9 +119,14 @@ def lib() -> ctypes.CDLL:
     L.gqa_decode_append_mapped.argtypes = [DP, MP, P, P, P, P, I32P, P]
     L.gqa_decode_attend_mapped.argtypes = [DP, MP, P, P, P, I32P, P, P, S, P]
     L.gqa_decode_step_mapped.argtypes = [DP, MP, P, P, P, P, P, I32P, P, P, S, P]
+    SP = ctypes.POINTER(ScalesT)
+    L.gqa_decode_append_q8.argtypes = [DP, SP, P, P, P, P, I32P, P]
+    L.gqa_decode_attend_q8.argtypes = [DP, SP, P, P, P, I32P, P, P, S, P]
+    L.gqa_decode_step_q8.argtypes = [DP, SP, P, P, P, P, P, I32P, P, P, S, P]
     for name in ("gqa_decode_workspace_size", "gqa_decode_get_plan", "gqa_decode_append", "gqa_decode_attend",
                  "gqa_decode_step", "gqa_decode_check_lengths", "gqa_decode_append_mapped",
-                 "gqa_decode_attend_mapped", "gqa_decode_step_mapped"):
+                 "gqa_decode_attend_mapped", "gqa_decode_step_mapped", "gqa_decode_append_q8",
+                 "gqa_decode_attend_q8", "gqa_decode_step_q8"):
         getattr(L, name).restype = ctypes.c_int
     L.gqa_decode_status_string.argtypes = [ctypes.c_int]
     L.gqa_decode_status_string.restype = ctypes.c_char_p
@@ -128,7 +141,9 @@ def _dtype_code(t: torch.dtype) -> int:
         return F32
     if t == torch.bfloat16:
         return BF16
-    raise ValueError(f"unsupported dtype {t}; float32 or bfloat16")
+    if t == torch.int8:
+        return I8
+    raise ValueError(f"unsupported dtype {t}; float32, bfloat16 or int8 (caches only)")
 
 
 def make_desc(batch, num_q_heads, num_kv_heads, head_dim, capacity, layout="BHSD", kv_dtype=BF16, qo_dtype=BF16,
@@ -337,4 +352,57 @@ def step_mapped(q, k_cache, v_cache, k_new, v_new, lengths, table, *, kind, layo
                                        v_cache.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), lengths.data_ptr(),
                                        out.data_ptr(), wptr, wbytes, _stream(dev)), "gqa_decode_step_mapped")
     del keep
+    return out
+
+
+def _scales(k_cache, k_scale, v_scale, layout):
+    """gqa_kv_scales_t for int8 caches; scales are float32 of the cache's shape without D."""
+    if k_cache.dtype != torch.int8:
+        raise ValueError("the _q8 calls take int8 caches")
+    for t in (k_scale, v_scale):
+        if t.dtype != torch.float32 or tuple(t.shape) != tuple(k_cache.shape[:3]):
+            raise ValueError(f"scales are float32 of shape {tuple(k_cache.shape[:3])} for {layout} caches")
+    return ScalesT(k_scale.data_ptr(), v_scale.data_ptr())
+
+
+def append_q8(k_cache, v_cache, k_scale, v_scale, k_new, v_new, lengths, *, layout="BHSD"):
+    """Quantize k_new/v_new (B, Hkv, D; float32 or bfloat16) row by row and store
+    codes and scales at slot lengths[b] of the int8 caches."""
+    dev = _dev([k_cache, v_cache, k_scale, v_scale, k_new, v_new], lengths)
+    B, Hkv, D = k_new.shape
+    S = k_cache.shape[2] if layout == "BHSD" else k_cache.shape[1]
+    desc = make_desc(B, Hkv, Hkv, D, S, layout, I8, _dtype_code(k_new.dtype))
+    sc = _scales(k_cache, k_scale, v_scale, layout)
+    check(lib().gqa_decode_append_q8(ctypes.byref(desc), ctypes.byref(sc), k_cache.data_ptr(), v_cache.data_ptr(),
+                                     k_new.data_ptr(), v_new.data_ptr(), lengths.data_ptr(), _stream(dev)),
+          "gqa_decode_append_q8")
+
+
+def attend_q8(q, k_cache, v_cache, k_scale, v_scale, lengths, *, layout="BHSD", out=None, workspace=None,
+              num_splits=0):
+    """Attention over int8 caches read as code * scale; lengths[b] = valid slots."""
+    dev = _dev([q, k_cache, v_cache, k_scale, v_scale], lengths)
+    desc = desc_for(q, k_cache, layout, num_splits)
+    sc = _scales(k_cache, k_scale, v_scale, layout)
+    if out is None:
+        out = torch.empty_like(q)
+    workspace, wptr, wbytes = _workspace(desc, dev, workspace)
+    check(lib().gqa_decode_attend_q8(ctypes.byref(desc), ctypes.byref(sc), q.data_ptr(), k_cache.data_ptr(),
+                                     v_cache.data_ptr(), lengths.data_ptr(), out.data_ptr(), wptr, wbytes,
+                                     _stream(dev)), "gqa_decode_attend_q8")
+    return out
+
+
+def step_q8(q, k_cache, v_cache, k_scale, v_scale, k_new, v_new, lengths, *, layout="BHSD", out=None,
+            workspace=None, num_splits=0):
+    """Quantizing append at lengths[b], then attention over lengths[b] + 1 slots."""
+    dev = _dev([q, k_cache, v_cache, k_scale, v_scale, k_new, v_new], lengths)
+    desc = desc_for(q, k_cache, layout, num_splits)
+    sc = _scales(k_cache, k_scale, v_scale, layout)
+    if out is None:
+        out = torch.empty_like(q)
+    workspace, wptr, wbytes = _workspace(desc, dev, workspace)
+    check(lib().gqa_decode_step_q8(ctypes.byref(desc), ctypes.byref(sc), q.data_ptr(), k_cache.data_ptr(),
+                                   v_cache.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), lengths.data_ptr(),
+                                   out.data_ptr(), wptr, wbytes, _stream(dev)), "gqa_decode_step_q8")
     return out

@@ -61,7 +61,17 @@ template <> struct Store<1> {  // bfloat16
   }
 };
 
-// Widen one 16-byte vector of storage into floats (8 bf16 or 4 f32).
+template <> struct Store<2> {  // int8 codes (read only; the value is code * row scale)
+  static constexpr int kBytes = 1;
+  __device__ static __forceinline__ float load1(const void* base, int64_t i) {
+    return (float)__builtin_nontemporal_load(reinterpret_cast<const int8_t*>(base) + i);
+  }
+  __device__ static __forceinline__ float load1_cached(const void* base, int64_t i) {
+    return (float)reinterpret_cast<const int8_t*>(base)[i];
+  }
+};
+
+// Widen one 16-byte vector of storage into floats (8 bf16, 4 f32 or 16 int8).
 template <int DT> __device__ __forceinline__ void widen16(u32x4 w, float* out);
 template <> __device__ __forceinline__ void widen16<0>(u32x4 w, float* out) {
   out[0] = __uint_as_float(w.x); out[1] = __uint_as_float(w.y);
@@ -70,6 +80,13 @@ template <> __device__ __forceinline__ void widen16<0>(u32x4 w, float* out) {
 template <> __device__ __forceinline__ void widen16<1>(u32x4 w, float* out) {
   out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x); out[2] = bf16_lo(w.y); out[3] = bf16_hi(w.y);
   out[4] = bf16_lo(w.z); out[5] = bf16_hi(w.z); out[6] = bf16_lo(w.w); out[7] = bf16_hi(w.w);
+}
+template <> __device__ __forceinline__ void widen16<2>(u32x4 w, float* out) {
+  const uint32_t v[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[4 * i + j] = (float)(int32_t)((int32_t)(v[i] << (24 - 8 * j)) >> 24);
 }
 
 // Reductions over the four 16-lane rows of a wave (lanes c, c + 16, c + 32,

@@ -13,6 +13,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <initializer_list>
 #include <vector>
 
 #include "gqa_decode.h"
@@ -26,7 +27,7 @@ constexpr int32_t kVersion = 100;  // 0.1.0
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-int elem_bytes(int32_t dt) { return dt == GQA_F32 ? 4 : 2; }
+int elem_bytes(int32_t dt) { return dt == GQA_F32 ? 4 : dt == GQA_BF16 ? 2 : 1; }
 
 // Checked product of non-negative factors; false on overflow past 2^62.
 bool mul_ok(int64_t a, int64_t b, int64_t* r) {
@@ -42,7 +43,8 @@ gqa_status_t check_desc(const gqa_decode_desc_t* d) {
     return GQA_ERR_INVALID_ARGUMENT;
   if (d->num_q_heads % d->num_kv_heads != 0) return GQA_ERR_INVALID_ARGUMENT;
   if (d->layout != GQA_LAYOUT_BHSD && d->layout != GQA_LAYOUT_BSHD) return GQA_ERR_INVALID_ARGUMENT;
-  if ((d->kv_dtype != GQA_F32 && d->kv_dtype != GQA_BF16) || (d->qo_dtype != GQA_F32 && d->qo_dtype != GQA_BF16))
+  if ((d->kv_dtype != GQA_F32 && d->kv_dtype != GQA_BF16 && d->kv_dtype != GQA_I8) ||
+      (d->qo_dtype != GQA_F32 && d->qo_dtype != GQA_BF16))
     return GQA_ERR_INVALID_ARGUMENT;
   if (d->num_splits < 0) return GQA_ERR_INVALID_ARGUMENT;
   if (d->head_dim > 256) return GQA_ERR_UNSUPPORTED;
@@ -62,6 +64,10 @@ gqa_status_t check_desc(const gqa_decode_desc_t* d) {
 int32_t choose_kernel(const gqa_decode_desc_t* d) {
   const int32_t G = d->num_q_heads / d->num_kv_heads;
   const bool bf16 = d->kv_dtype == GQA_BF16 && d->qo_dtype == GQA_BF16;
+  if (d->kv_dtype == GQA_I8) {
+    return (d->qo_dtype == GQA_BF16 && d->head_dim == 128 && G <= 16 && kHaveMfmaQkI8) ? GQA_KERNEL_MFMA_QK
+                                                                                       : GQA_KERNEL_GENERIC;
+  }
   if (bf16 && d->head_dim == 128 && G <= 16 && kHaveMfmaQk) return GQA_KERNEL_MFMA_QK;
   if (bf16 && d->head_dim == 128 && G > 16 && G <= 64 && kHaveMfmaAll) return GQA_KERNEL_MFMA_ALL;
   return GQA_KERNEL_GENERIC;
@@ -252,11 +258,12 @@ gqa_status_t check_attend_ptrs(const gqa_decode_desc_t* d, const gqa_cache_map_t
                                const int32_t* lengths, const void* out, const void* ws, size_t ws_bytes,
                                bool step) {
   const size_t ekv = elem_bytes(d->kv_dtype), eqo = elem_bytes(d->qo_dtype);
+  const size_t enew = d->kv_dtype == GQA_I8 ? eqo : ekv;  // int8 caches take new K/V as activations
   if (!q || !kc || !vc || !lengths || !out) return GQA_ERR_INVALID_ARGUMENT;
   if (step && (!kn || !vn)) return GQA_ERR_INVALID_ARGUMENT;
   if (!aligned(q, eqo) || !aligned(out, eqo) || !aligned(kc, ekv) || !aligned(vc, ekv) || !aligned(lengths, 4))
     return GQA_ERR_INVALID_ARGUMENT;
-  if (step && (!aligned(kn, ekv) || !aligned(vn, ekv))) return GQA_ERR_INVALID_ARGUMENT;
+  if (step && (!aligned(kn, enew) || !aligned(vn, enew))) return GQA_ERR_INVALID_ARGUMENT;
   if (p.kernel != GQA_KERNEL_GENERIC) {
     // The matrix-core kernels read q, caches and new K/V with 16-byte loads.
     if (!aligned(q, 16) || !aligned(kc, 16) || !aligned(vc, 16) || !aligned(out, 16)) return GQA_ERR_INVALID_ARGUMENT;
@@ -283,7 +290,7 @@ gqa_status_t check_attend_ptrs(const gqa_decode_desc_t* d, const gqa_cache_map_t
                                  overlap(s_ws, s_vc) || overlap(s_ws, s_len))))
     return GQA_ERR_INVALID_ARGUMENT;
   if (step) {
-    const Span s_kn = span(kn, B * Hkv * D * ekv), s_vn = span(vn, B * Hkv * D * ekv);
+    const Span s_kn = span(kn, B * Hkv * D * enew), s_vn = span(vn, B * Hkv * D * enew);
     if (overlap(s_kc, s_vc) || overlap(s_kn, s_kc) || overlap(s_kn, s_vc) || overlap(s_vn, s_kc) ||
         overlap(s_vn, s_vc) || overlap(s_out, s_kn) || overlap(s_out, s_vn) || overlap(s_len, s_kc) ||
         overlap(s_len, s_vc) ||
@@ -352,10 +359,33 @@ gqa_status_t gqa_decode_get_plan(const gqa_decode_desc_t* desc, gqa_decode_plan_
 
 namespace {
 
-gqa_status_t do_append(const gqa_decode_desc_t* desc, const gqa_cache_map_t* map, void* k_cache, void* v_cache,
-                       const void* k_new, const void* v_new, const int32_t* lengths, void* stream) {
+// Int8 caches need their row scales and nothing else does; scales are 4-byte
+// aligned float32 arrays of B * Hkv * S entries that overlap no other buffer
+// (`others`: the call's other spans).
+gqa_status_t check_scales(const gqa_decode_desc_t* d, const gqa_kv_scales_t* sc, const gqa_cache_map_t* map) {
+  if ((d->kv_dtype == GQA_I8) != (sc != nullptr)) return GQA_ERR_INVALID_ARGUMENT;
+  if (sc != nullptr && map != nullptr) return GQA_ERR_UNSUPPORTED;  // int8 mapped caches: not built
+  return GQA_OK;
+}
+gqa_status_t check_scale_ptrs(const gqa_decode_desc_t* d, const gqa_kv_scales_t* sc,
+                              std::initializer_list<Span> others) {
+  if (sc == nullptr) return GQA_OK;
+  if (!sc->k_scale || !sc->v_scale || !aligned(sc->k_scale, 4) || !aligned(sc->v_scale, 4))
+    return GQA_ERR_INVALID_ARGUMENT;
+  const size_t n = (size_t)d->batch * d->num_kv_heads * d->capacity * 4;
+  const Span ks = span(sc->k_scale, n), vs = span(sc->v_scale, n);
+  if (overlap(ks, vs)) return GQA_ERR_INVALID_ARGUMENT;
+  for (const Span& o : others)
+    if (overlap(ks, o) || overlap(vs, o)) return GQA_ERR_INVALID_ARGUMENT;
+  return GQA_OK;
+}
+
+gqa_status_t do_append(const gqa_decode_desc_t* desc, const gqa_cache_map_t* map, const gqa_kv_scales_t* sc,
+                       void* k_cache, void* v_cache, const void* k_new, const void* v_new, const int32_t* lengths,
+                       void* stream) {
   gqa_status_t st = check_desc(desc);
   if (st != GQA_OK) return st;
+  if ((st = check_scales(desc, sc, map)) != GQA_OK) return st;
   Plan p;
   std::memset(&p, 0, sizeof(p));
   p.kernel = GQA_KERNEL_GENERIC;  // the append kernel takes any block size
@@ -364,43 +394,67 @@ gqa_status_t do_append(const gqa_decode_desc_t* desc, const gqa_cache_map_t* map
   if (desc->batch == 0) return GQA_OK;
   if (!k_cache || !v_cache || !k_new || !v_new || !lengths) return GQA_ERR_INVALID_ARGUMENT;
   const size_t e = elem_bytes(desc->kv_dtype);
-  if (!aligned(k_cache, e) || !aligned(v_cache, e) || !aligned(k_new, e) || !aligned(v_new, e) ||
+  const size_t en = sc ? elem_bytes(desc->qo_dtype) : e;  // int8 caches take new K/V as activations
+  if (!aligned(k_cache, e) || !aligned(v_cache, e) || !aligned(k_new, en) || !aligned(v_new, en) ||
       !aligned(lengths, 4))
     return GQA_ERR_INVALID_ARGUMENT;
   const size_t B = desc->batch, Hkv = desc->num_kv_heads, D = desc->head_dim;
   const Span s_kc = span(k_cache, cache_elems(desc, map) * e), s_vc = span(v_cache, cache_elems(desc, map) * e);
-  const Span s_kn = span(k_new, B * Hkv * D * e), s_vn = span(v_new, B * Hkv * D * e);
+  const Span s_kn = span(k_new, B * Hkv * D * en), s_vn = span(v_new, B * Hkv * D * en);
   const Span s_len = span(lengths, B * 4);
   const Span s_map = span(map ? map->map : nullptr, map_bytes(desc, map));
   if (overlap(s_kc, s_vc) || overlap(s_kn, s_kc) || overlap(s_kn, s_vc) || overlap(s_vn, s_kc) ||
       overlap(s_vn, s_vc) || overlap(s_len, s_kc) || overlap(s_len, s_vc) || overlap(s_map, s_kc) ||
       overlap(s_map, s_vc))
     return GQA_ERR_INVALID_ARGUMENT;
+  if ((st = check_scale_ptrs(desc, sc, {s_kc, s_vc, s_kn, s_vn, s_len})) != GQA_OK) return st;
   AttnArgs a;
   fill_args(desc, p, &a);
   fill_map(desc, map, &a);
   a.k_new = k_new;
   a.v_new = v_new;
   a.lengths = lengths;
+  if (sc != nullptr) {
+    a.k_scale_w = sc->k_scale;
+    a.v_scale_w = sc->v_scale;
+    if (launch_append_q8(a, k_cache, v_cache, (hipStream_t)stream) != hipSuccess) return GQA_ERR_HIP;
+    return GQA_OK;
+  }
   if (launch_append(a, k_cache, v_cache, (hipStream_t)stream) != hipSuccess) return GQA_ERR_HIP;
   return GQA_OK;
 }
 
 // Attend (step == false) or fused step (step == true), dense or mapped.
-gqa_status_t do_attend(const gqa_decode_desc_t* desc, const gqa_cache_map_t* map, const void* q, void* k_cache,
-                       void* v_cache, const void* k_new, const void* v_new, const int32_t* lengths, void* out,
-                       void* workspace, size_t workspace_bytes, void* stream, bool step) {
+gqa_status_t do_attend(const gqa_decode_desc_t* desc, const gqa_cache_map_t* map, const gqa_kv_scales_t* sc,
+                       const void* q, void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                       const int32_t* lengths, void* out, void* workspace, size_t workspace_bytes, void* stream,
+                       bool step) {
   Plan p;
   gqa_status_t st = make_plan(desc, &p);
   if (st != GQA_OK) return st;
+  if ((st = check_scales(desc, sc, map)) != GQA_OK) return st;
   if (map != nullptr && (st = check_map(desc, map, p)) != GQA_OK) return st;
   if (desc->batch == 0) return GQA_OK;
   st = check_attend_ptrs(desc, map, p, q, k_cache, v_cache, step ? k_new : nullptr, step ? v_new : nullptr,
                          lengths, out, workspace, workspace_bytes, step);
   if (st != GQA_OK) return st;
+  if (sc != nullptr) {
+    const size_t B = desc->batch, Hq = desc->num_q_heads, Hkv = desc->num_kv_heads, D = desc->head_dim;
+    const size_t eqo = elem_bytes(desc->qo_dtype), ce = cache_elems(desc, map);
+    st = check_scale_ptrs(desc, sc,
+                          {span(q, B * Hq * D * eqo), span(out, B * Hq * D * eqo), span(k_cache, ce),
+                           span(v_cache, ce), span(lengths, B * 4), span(workspace, p.workspace_bytes),
+                           span(step ? k_new : nullptr, step ? B * Hkv * D * eqo : 0),
+                           span(step ? v_new : nullptr, step ? B * Hkv * D * eqo : 0)});
+    if (st != GQA_OK) return st;
+  }
   AttnArgs a;
   fill_args(desc, p, &a);
   fill_map(desc, map, &a);
+  if (sc != nullptr) {
+    a.k_scale = sc->k_scale;
+    a.v_scale = sc->v_scale;
+  }
   a.q = q;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
@@ -416,7 +470,15 @@ gqa_status_t do_attend(const gqa_decode_desc_t* desc, const gqa_cache_map_t* map
   if (step) {
     a.k_new = k_new;
     a.v_new = v_new;
-    if (p.kernel == GQA_KERNEL_GENERIC) {
+    if (sc != nullptr) {
+      // Int8 caches: the quantizing append, then attention over lengths[b] + 1
+      // slots (the new token is attended in its stored, quantized form).
+      a.k_scale_w = sc->k_scale;
+      a.v_scale_w = sc->v_scale;
+      if (launch_append_q8(a, k_cache, v_cache, (hipStream_t)stream) != hipSuccess) return GQA_ERR_HIP;
+      a.k_new = nullptr;
+      a.v_new = nullptr;
+    } else if (p.kernel == GQA_KERNEL_GENERIC) {
       // Generic path: the append kernel, then attention over lengths[b] + 1
       // slots, ordered by the stream.
       if (launch_append(a, k_cache, v_cache, (hipStream_t)stream) != hipSuccess) return GQA_ERR_HIP;
@@ -440,7 +502,7 @@ extern "C" {
 gqa_status_t gqa_decode_append(const gqa_decode_desc_t* desc, void* k_cache, void* v_cache, const void* k_new,
                                const void* v_new, const int32_t* lengths, void* stream) {
   try {
-    return do_append(desc, nullptr, k_cache, v_cache, k_new, v_new, lengths, stream);
+    return do_append(desc, nullptr, nullptr, k_cache, v_cache, k_new, v_new, lengths, stream);
   } catch (...) {
     return GQA_ERR_INTERNAL;
   }
@@ -450,8 +512,8 @@ gqa_status_t gqa_decode_attend(const gqa_decode_desc_t* desc, const void* q, con
                                const void* v_cache, const int32_t* lengths, void* out, void* workspace,
                                size_t workspace_bytes, void* stream) {
   try {
-    return do_attend(desc, nullptr, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache), nullptr, nullptr,
-                     lengths, out, workspace, workspace_bytes, stream, false);
+    return do_attend(desc, nullptr, nullptr, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache), nullptr,
+                     nullptr, lengths, out, workspace, workspace_bytes, stream, false);
   } catch (...) {
     return GQA_ERR_INTERNAL;
   }
@@ -461,8 +523,8 @@ gqa_status_t gqa_decode_step(const gqa_decode_desc_t* desc, const void* q, void*
                              const void* k_new, const void* v_new, const int32_t* lengths, void* out,
                              void* workspace, size_t workspace_bytes, void* stream) {
   try {
-    return do_attend(desc, nullptr, q, k_cache, v_cache, k_new, v_new, lengths, out, workspace, workspace_bytes,
-                     stream, true);
+    return do_attend(desc, nullptr, nullptr, q, k_cache, v_cache, k_new, v_new, lengths, out, workspace,
+                     workspace_bytes, stream, true);
   } catch (...) {
     return GQA_ERR_INTERNAL;
   }
@@ -473,7 +535,7 @@ gqa_status_t gqa_decode_append_mapped(const gqa_decode_desc_t* desc, const gqa_c
                                       const int32_t* lengths, void* stream) {
   try {
     if (map == nullptr) return GQA_ERR_INVALID_ARGUMENT;
-    return do_append(desc, map, k_cache, v_cache, k_new, v_new, lengths, stream);
+    return do_append(desc, map, nullptr, k_cache, v_cache, k_new, v_new, lengths, stream);
   } catch (...) {
     return GQA_ERR_INTERNAL;
   }
@@ -484,8 +546,8 @@ gqa_status_t gqa_decode_attend_mapped(const gqa_decode_desc_t* desc, const gqa_c
                                       void* workspace, size_t workspace_bytes, void* stream) {
   try {
     if (map == nullptr) return GQA_ERR_INVALID_ARGUMENT;
-    return do_attend(desc, map, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache), nullptr, nullptr,
-                     lengths, out, workspace, workspace_bytes, stream, false);
+    return do_attend(desc, map, nullptr, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache), nullptr,
+                     nullptr, lengths, out, workspace, workspace_bytes, stream, false);
   } catch (...) {
     return GQA_ERR_INTERNAL;
   }
@@ -497,8 +559,44 @@ gqa_status_t gqa_decode_step_mapped(const gqa_decode_desc_t* desc, const gqa_cac
                                     void* stream) {
   try {
     if (map == nullptr) return GQA_ERR_INVALID_ARGUMENT;
-    return do_attend(desc, map, q, k_cache, v_cache, k_new, v_new, lengths, out, workspace, workspace_bytes, stream,
-                     true);
+    return do_attend(desc, map, nullptr, q, k_cache, v_cache, k_new, v_new, lengths, out, workspace,
+                     workspace_bytes, stream, true);
+  } catch (...) {
+    return GQA_ERR_INTERNAL;
+  }
+}
+
+gqa_status_t gqa_decode_append_q8(const gqa_decode_desc_t* desc, const gqa_kv_scales_t* scales, void* k_cache,
+                                  void* v_cache, const void* k_new, const void* v_new, const int32_t* lengths,
+                                  void* stream) {
+  try {
+    if (scales == nullptr) return GQA_ERR_INVALID_ARGUMENT;
+    return do_append(desc, nullptr, scales, k_cache, v_cache, k_new, v_new, lengths, stream);
+  } catch (...) {
+    return GQA_ERR_INTERNAL;
+  }
+}
+
+gqa_status_t gqa_decode_attend_q8(const gqa_decode_desc_t* desc, const gqa_kv_scales_t* scales, const void* q,
+                                  const void* k_cache, const void* v_cache, const int32_t* lengths, void* out,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    if (scales == nullptr) return GQA_ERR_INVALID_ARGUMENT;
+    return do_attend(desc, nullptr, scales, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache), nullptr,
+                     nullptr, lengths, out, workspace, workspace_bytes, stream, false);
+  } catch (...) {
+    return GQA_ERR_INTERNAL;
+  }
+}
+
+gqa_status_t gqa_decode_step_q8(const gqa_decode_desc_t* desc, const gqa_kv_scales_t* scales, const void* q,
+                                void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                                const int32_t* lengths, void* out, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  try {
+    if (scales == nullptr) return GQA_ERR_INVALID_ARGUMENT;
+    return do_attend(desc, nullptr, scales, q, k_cache, v_cache, k_new, v_new, lengths, out, workspace,
+                     workspace_bytes, stream, true);
   } catch (...) {
     return GQA_ERR_INTERNAL;
   }

@@ -30,6 +30,12 @@ struct AttnArgs {
   const int32_t* map;
   int32_t map_kind, map_rows, bs, max_blocks;
   int64_t sblk;          // paged: elements between pool blocks
+  // Int8 caches: float32 row scales, indexed by a row's element offset / D
+  // (read by attention; the quantizing append writes the appended rows).
+  const float* k_scale;
+  const float* v_scale;
+  float* k_scale_w;
+  float* v_scale_w;
   int32_t nsplit, split_tokens;
   int32_t head_chunks;   // generic kernel: query-head chunks per kv-head
   int32_t len_offset;    // slots attended = lengths[b] + len_offset (1 for a step, 0 for attend)
@@ -53,6 +59,7 @@ struct Plan {
 // generic kernel for the others).
 extern const bool kHaveMfmaQk;
 extern const bool kHaveMfmaAll;
+extern const bool kHaveMfmaQkI8;  // int8 caches on the G <= 16 matrix-core kernel
 
 constexpr int kNumCUs = 256;
 constexpr int kMaxSplits = 64;        // one lane per split in the combine pass          // MI355X: 8 XCDs x 32 CUs
@@ -60,6 +67,8 @@ constexpr int kGenericHeadChunk = 8;  // query heads per workgroup in the generi
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_append(const AttnArgs& a, void* k_cache, void* v_cache, hipStream_t s);
+// Quantizing append into int8 caches (new K/V in a.qo_dtype).
+hipError_t launch_append_q8(const AttnArgs& a, void* k_cache, void* v_cache, hipStream_t s);
 hipError_t launch_attend_generic(const AttnArgs& a, const Plan& p, int vec_path, hipStream_t s);
 hipError_t launch_attend_mfma_qk(const AttnArgs& a, const Plan& p, hipStream_t s);
 hipError_t launch_attend_mfma_all(const AttnArgs& a, const Plan& p, hipStream_t s);

@@ -56,6 +56,67 @@ hipError_t launch_append(const AttnArgs& a, void* k_cache, void* v_cache, hipStr
 }
 
 // ---------------------------------------------------------------------------
+// Quantizing append into int8 caches (CANN "aclnnMlaPrologV3WeightNz" page,
+// dynamic-quantization formula): one wave per (b, kv-head); each new K and V
+// row (D <= 256 elements, in the query/output storage type) gets
+// scale = max|x| / 127 and codes round-half-even(x / scale), with correctly
+// rounded float32 divisions; a zero row stores scale 0 and codes 0.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max64(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+
+template <int NEW>
+__global__ __launch_bounds__(256) void append_q8_kernel(AttnArgs a, int8_t* __restrict__ kc, int8_t* __restrict__ vc) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // b * Hkv + h
+  const int lane = threadIdx.x & 63;
+  if (row >= (int64_t)a.B * a.Hkv) return;  // whole waves; no barrier follows
+  const int b = (int)(row / a.Hkv);
+  const int h = (int)(row % a.Hkv);
+  const int pos = a.lengths[b];
+  if (pos < 0 || pos >= a.S) return;        // out of contract: nothing written
+  const int64_t off = slot_offset_checked(a, b, h, pos);
+  if (off < 0) return;
+  const int D = a.D;
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    const void* src = which ? a.v_new : a.k_new;
+    int8_t* dst = which ? vc : kc;
+    float* sdst = which ? a.v_scale_w : a.k_scale_w;
+    float x[4];
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = lane + 64 * i;
+      x[i] = d < D ? Store<NEW>::load1_cached(src, row * D + d) : 0.f;
+      amax = fmaxf(amax, fabsf(x[i]));
+    }
+    amax = wave_max64(amax);
+    const float scale = amax / 127.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = lane + 64 * i;
+      if (d < D) {
+        const float c = amax > 0.f ? fminf(fmaxf(rintf(x[i] / scale), -127.f), 127.f) : 0.f;
+        dst[off + d] = (int8_t)(int32_t)c;
+      }
+    }
+    if (lane == 0) sdst[off / D] = scale;
+  }
+}
+
+hipError_t launch_append_q8(const AttnArgs& a, void* k_cache, void* v_cache, hipStream_t s) {
+  const unsigned blocks = (unsigned)(((int64_t)a.B * a.Hkv + 3) / 4);
+  AttnArgs arg = a;
+  void* params[] = {&arg, &k_cache, &v_cache};
+  const void* fn = a.qo_dtype == GQA_F32 ? reinterpret_cast<const void*>(&append_q8_kernel<GQA_F32>)
+                                         : reinterpret_cast<const void*>(&append_q8_kernel<GQA_BF16>);
+  return hipLaunchKernel(fn, dim3(blocks), dim3(256), params, 0, s);
+}
+
+// ---------------------------------------------------------------------------
 // Generic split attention.
 //
 // Grid: blockIdx.x = ((b * Hkv + h) * head_chunks + c) * nsplit + split; the
@@ -131,6 +192,11 @@ __global__ __launch_bounds__(256) void attend_generic_kernel(AttnArgs a) {
   for (int t = t_begin + rg; t < t_end; t += NRG) {
     const int64_t row = slot_offset(a, b, h, t);
     float kv[EPL], vv[EPL];
+    float ks = 1.f, vs = 1.f;  // int8 caches: the row scales
+    if constexpr (KV == GQA_I8) {
+      ks = a.k_scale[row / D];
+      vs = a.v_scale[row / D];
+    }
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int d0 = (c * LPR + rl) * VEC;
@@ -154,13 +220,14 @@ __global__ __launch_bounds__(256) void attend_generic_kernel(AttnArgs a) {
       for (int e = 0; e < EPL; ++e) part = fmaf(qv[g][e], kv[e], part);
 #pragma unroll
       for (int off = LPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off);
-      const float s = part * a.scale_log2;
+      const float s = part * (KV == GQA_I8 ? ks * a.scale_log2 : a.scale_log2);
       const float mn = fmaxf(m[g], s);
       const float alpha = fast_exp2(m[g] - mn);  // 0 on the first slot (m = -inf)
       const float p = fast_exp2(s - mn);
       l[g] = l[g] * alpha + p;
+      const float pv = KV == GQA_I8 ? p * vs : p;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(p, vv[e], acc[g][e] * alpha);
+      for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(pv, vv[e], acc[g][e] * alpha);
       m[g] = mn;
     }
   }
@@ -244,7 +311,11 @@ template <int KV, int QO>
 static hipError_t dispatch_generic(const AttnArgs& a, const Plan& p, int vec_path, hipStream_t s) {
   const int D = a.D;
   if (vec_path) {
-    if constexpr (KV == GQA_BF16) {
+    if constexpr (KV == GQA_I8) {
+      if (D <= 64) return launch_generic_t<KV, QO, 16, 1, 4>(a, p, s);
+      if (D <= 128) return launch_generic_t<KV, QO, 16, 1, 8>(a, p, s);
+      return launch_generic_t<KV, QO, 16, 1, 16>(a, p, s);
+    } else if constexpr (KV == GQA_BF16) {
       if (D <= 32) return launch_generic_t<KV, QO, 8, 1, 4>(a, p, s);
       if (D <= 128) return launch_generic_t<KV, QO, 8, 1, 16>(a, p, s);
       return launch_generic_t<KV, QO, 8, 1, 32>(a, p, s);
@@ -261,6 +332,9 @@ static hipError_t dispatch_generic(const AttnArgs& a, const Plan& p, int vec_pat
 }
 
 hipError_t launch_attend_generic(const AttnArgs& a, const Plan& p, int vec_path, hipStream_t s) {
+  if (a.kv_dtype == GQA_I8)
+    return a.qo_dtype == GQA_F32 ? dispatch_generic<GQA_I8, GQA_F32>(a, p, vec_path, s)
+                                 : dispatch_generic<GQA_I8, GQA_BF16>(a, p, vec_path, s);
   if (a.kv_dtype == GQA_F32 && a.qo_dtype == GQA_F32) return dispatch_generic<GQA_F32, GQA_F32>(a, p, vec_path, s);
   if (a.kv_dtype == GQA_F32) return dispatch_generic<GQA_F32, GQA_BF16>(a, p, vec_path, s);
   if (a.qo_dtype == GQA_F32) return dispatch_generic<GQA_BF16, GQA_F32>(a, p, vec_path, s);

@@ -44,6 +44,7 @@ namespace gqa {
 
 const bool kHaveMfmaQk = true;
 const bool kHaveMfmaAll = true;
+const bool kHaveMfmaQkI8 = false;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 

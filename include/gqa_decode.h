@@ -70,7 +70,7 @@ typedef enum {
   GQA_ERR_INTERNAL = 5             /* unexpected library error (no C++ exception crosses)       */
 } gqa_status_t;
 
-enum { GQA_F32 = 0, GQA_BF16 = 1 };
+enum { GQA_F32 = 0, GQA_BF16 = 1, GQA_I8 = 2 /* int8 codes with per-row scales: the _q8 calls only */ };
 enum {
   GQA_LAYOUT_BHSD = 0,  /* caches (B, Hkv, S, D): KV cache decode step page            */
   GQA_LAYOUT_BSHD = 1   /* caches (B, S, Hkv, D): JAX Grouped-Query Decode Step page   */
@@ -85,7 +85,8 @@ typedef struct {
   int32_t head_dim;     /* D in [1, 256]; D > 256 is GQA_ERR_UNSUPPORTED                    */
   int32_t capacity;     /* S >= 1 slots per (sequence, kv-head) in both caches              */
   int32_t layout;       /* GQA_LAYOUT_BHSD or GQA_LAYOUT_BSHD, shared by both caches         */
-  int32_t kv_dtype;     /* storage of k_cache, v_cache, k_new, v_new: GQA_F32 or GQA_BF16    */
+  int32_t kv_dtype;     /* storage of k_cache, v_cache, k_new, v_new: GQA_F32 or GQA_BF16
+                           (GQA_I8 for the _q8 calls, whose k_new/v_new are in qo_dtype)    */
   int32_t qo_dtype;     /* storage of q and out: GQA_F32 or GQA_BF16                         */
   int32_t num_splits;   /* 0 = library's choice; n > 0 asks for n splits of the token axis
                            (the plan uses at most 64, and fewer when n would leave a split
@@ -106,7 +107,8 @@ typedef struct {
 
 enum {
   GQA_KERNEL_GENERIC = 0,  /* vector ALU, any D <= 256, f32 or bf16 storage                  */
-  GQA_KERNEL_MFMA_QK = 1,  /* bf16, D = 128, G <= 16: scores on MFMA, V sum on vector ALU    */
+  GQA_KERNEL_MFMA_QK = 1,  /* bf16 (or int8 caches, bf16 q/out), D = 128, G <= 16: scores on
+                              MFMA, V sum on vector ALU                                       */
   GQA_KERNEL_MFMA_ALL = 2  /* bf16, D = 128, 16 < G <= 64: scores and V sum on MFMA           */
 };
 
@@ -221,6 +223,41 @@ gqa_status_t gqa_decode_step_mapped(const gqa_decode_desc_t* desc, const gqa_cac
                                     void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                                     const int32_t* lengths, void* out, void* workspace, size_t workspace_bytes,
                                     void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Int8 caches with per-row scales (Huawei CANN "aclnnMlaPrologV3WeightNz"
+ * operator page, dynamic-quantization formula: a row's dequantization scale is
+ * its largest absolute value divided by 127 and its code the row divided by
+ * that scale, rounded).  desc->kv_dtype = GQA_I8: the caches hold int8 codes in
+ * the descriptor's layout, and every (sequence, kv-head, slot) row has a float32
+ * scale; a cached value reads as code * scale.
+ *   k_scale, v_scale : float32 (B, Hkv, S) for GQA_LAYOUT_BHSD, (B, S, Hkv) for
+ *                      BSHD; read by attend, the appended rows written by
+ *                      append and step.
+ *   k_new, v_new     : (B, Hkv, D) in desc->qo_dtype (the model's activations);
+ *                      each row is quantized on the device: float32 widening,
+ *                      scale = max|x| / 127 and code = round-half-even(x / scale)
+ *                      with correctly rounded float32 divisions (a zero row has
+ *                      scale 0 and codes 0).
+ * Other arguments, contracts and errors as in the unquantized calls; the
+ * unquantized calls refuse GQA_I8 (GQA_ERR_INVALID_ARGUMENT).  Scale arrays must
+ * be 4-byte aligned and overlap no other argument.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  float* k_scale;
+  float* v_scale;
+} gqa_kv_scales_t;
+
+gqa_status_t gqa_decode_append_q8(const gqa_decode_desc_t* desc, const gqa_kv_scales_t* scales, void* k_cache,
+                                  void* v_cache, const void* k_new, const void* v_new, const int32_t* lengths,
+                                  void* stream);
+gqa_status_t gqa_decode_attend_q8(const gqa_decode_desc_t* desc, const gqa_kv_scales_t* scales, const void* q,
+                                  const void* k_cache, const void* v_cache, const int32_t* lengths, void* out,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+gqa_status_t gqa_decode_step_q8(const gqa_decode_desc_t* desc, const gqa_kv_scales_t* scales, const void* q,
+                                void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                                const int32_t* lengths, void* out, void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 /* Debugging aid, not on the hot path: counts the entries of the device array
  * `lengths` (B = desc->batch entries) that lie outside the contract of a call

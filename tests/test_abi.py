@@ -377,3 +377,82 @@ def test_mapped_empty_batch_is_a_noop():
     assert L.gqa_decode_step_mapped(ctypes.byref(d), ctypes.byref(m), None, None, None, None, None, None, None, None,
                                     0, None) == OK
     assert L.gqa_decode_append_mapped(ctypes.byref(d), ctypes.byref(m), None, None, None, None, None, None) == OK
+
+
+# ---------------------------------------------------------------------------
+# Int8 caches (CANN dynamic-quantization rule): the _q8 calls need an int8
+# descriptor and both scale arrays; every other call refuses int8 caches.
+# ---------------------------------------------------------------------------
+def _q8_calls(d, sc, p=None):
+    L = g.lib()
+    p = p or _attend_ptrs()
+    scp = ctypes.byref(sc) if sc is not None else None
+    return [
+        L.gqa_decode_attend_q8(ctypes.byref(d), scp, p["q"], p["kc"], p["vc"], p["lens"], p["out"], p["ws"], 1 << 30,
+                               None),
+        L.gqa_decode_step_q8(ctypes.byref(d), scp, p["q"], p["kc"], p["vc"], p["kn"], p["vn"], p["lens"], p["out"],
+                             p["ws"], 1 << 30, None),
+        L.gqa_decode_append_q8(ctypes.byref(d), scp, p["kc"], p["vc"], p["kn"], p["vn"], p["lens"], None),
+    ]
+
+
+def _scales(k=FAKE + 9 * GAP, v=FAKE + 10 * GAP):
+    return _lib.ScalesT(k, v)
+
+
+def test_unquantized_calls_refuse_int8_caches():
+    L = g.lib()
+    d = desc(kv_dtype=g.I8)
+    p = _attend_ptrs()
+    assert _attend(d, p, 1 << 30) == INVALID
+    assert _step(d, p, 1 << 30) == INVALID
+    assert L.gqa_decode_append(ctypes.byref(d), p["kc"], p["vc"], p["kn"], p["vn"], p["lens"], None) == INVALID
+    m, keep = _map("slots", 4, [1, 2])
+    assert _mapped_calls(d, m) == [INVALID] * 3
+
+
+def test_q8_calls_refuse_other_cache_dtypes_and_missing_scales():
+    for kv in (g.BF16, g.F32):
+        assert _q8_calls(desc(kv_dtype=kv), _scales()) == [INVALID] * 3
+    d = desc(kv_dtype=g.I8)
+    assert _q8_calls(d, None) == [INVALID] * 3
+    assert _q8_calls(d, _scales(k=0)) == [INVALID] * 3
+    assert _q8_calls(d, _scales(v=0)) == [INVALID] * 3
+    assert _q8_calls(d, _scales(k=FAKE + 9 * GAP + 2)) == [INVALID] * 3     # not 4-byte aligned
+    assert _q8_calls(desc(kv_dtype=g.I8, qo_dtype=g.I8), _scales()) == [INVALID] * 3   # q/out are activations
+
+
+def test_q8_scales_overlapping_anything_refused():
+    d = desc(kv_dtype=g.I8)
+    p = _attend_ptrs()
+    n = 2 * 2 * 4096 * 4                                   # B * Hkv * S float32 scales
+    assert _q8_calls(d, _scales(k=FAKE + 9 * GAP, v=FAKE + 9 * GAP + n - 4)) == [INVALID] * 3
+    for other in ("kc", "vc", "lens"):
+        assert _q8_calls(d, _scales(k=p[other]), p) == [INVALID] * 3, other
+    for other in ("kn", "vn"):                             # attend does not take these
+        assert _q8_calls(d, _scales(k=p[other]), p)[1:] == [INVALID] * 2, other
+    for other in ("q", "out", "ws"):                       # append does not take these
+        assert _q8_calls(d, _scales(v=p[other]), p)[:2] == [INVALID] * 2, other
+
+
+def test_q8_new_rows_aligned_for_their_activation_dtype():
+    """k_new/v_new of the _q8 calls are in qo_dtype: 2-byte alignment for
+    bf16, 4-byte for float32; int8 caches need none."""
+    for qo, shift, want in ((g.BF16, 1, INVALID), (g.F32, 2, INVALID)):
+        d = desc(kv_dtype=g.I8, qo_dtype=qo)
+        p = _attend_ptrs()
+        p["kn"] += shift
+        assert _q8_calls(d, _scales(), p)[1:] == [want] * 2
+
+
+def test_q8_empty_batch_is_a_noop_and_plans_int8():
+    L = g.lib()
+    d = desc(batch=0, kv_dtype=g.I8)
+    sc = _scales()
+    assert L.gqa_decode_attend_q8(ctypes.byref(d), ctypes.byref(sc), None, None, None, None, None, None, 0,
+                                  None) == OK
+    assert L.gqa_decode_step_q8(ctypes.byref(d), ctypes.byref(sc), None, None, None, None, None, None, None, None,
+                                0, None) == OK
+    assert L.gqa_decode_append_q8(ctypes.byref(d), ctypes.byref(sc), None, None, None, None, None, None) == OK
+    p = g.get_plan(desc(kv_dtype=g.I8))
+    assert p["block"] == 256 and p["workspace_bytes"] == g.workspace_size(desc(kv_dtype=g.I8))

@@ -1,0 +1,162 @@
+"""GPU parity for int8 caches with per-row scales (Huawei CANN
+"aclnnMlaPrologV3WeightNz" page, dynamic-quantization formula).
+
+The library's _q8 step/attend/append against the float64 int8 oracle on the
+same stored bits: codes and scales of the appended rows byte-exact (the
+quantization is an integer decision taken in float32 on both sides), outputs
+within the dense tolerances (fp32 2e-5, bf16 1e-2, abs + rel).  Scales of the
+slots past lengths[b] are NaN, so any read outside the valid slots shows up.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 2e-5, "bf16": 1e-2}
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def g():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gqa_decode_attention_amd as lib
+    lib.lib()
+    return lib
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def np_of(t):
+    return W.to_numpy_storage(t)
+
+
+def assert_close(out_gpu, ref, qo_dtype, what=""):
+    got = out_gpu.detach().float().cpu().double().numpy()
+    tol = TOL[qo_dtype]
+    err = np.abs(got - ref)
+    bound = tol + tol * np.abs(ref)
+    bad = ~(err <= bound)
+    assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} outside tolerance; worst excess "
+                           f"{np.max(err - bound):.3g} at {np.unravel_index(np.argmax(err - bound), err.shape)}")
+
+
+def assert_same_bytes(got, want, what):
+    g_ = np_of(got)
+    if g_.tobytes() != want.tobytes():
+        bad = np.argwhere(g_.view(np.uint8).reshape(g_.shape + (-1,)) != want.view(np.uint8).reshape(g_.shape + (-1,)))
+        raise AssertionError(f"{what}: {len(bad)} bytes differ, first at {bad[:3].tolist()}")
+
+
+CASES = [
+    # B, Hq, Hkv, D, S, layout, qo, num_splits
+    (3, 32, 8, 128, 1500, "BHSD", "bf16", 0),      # Llama-like group of 4
+    (2, 16, 2, 128, 700, "BSHD", "bf16", 3),       # G=8, forced splits
+    (2, 64, 1, 128, 900, "BHSD", "bf16", 0),       # G=64
+    (3, 8, 2, 64, 300, "BHSD", "f32", 0),          # float32 activations
+    (2, 6, 3, 24, 200, "BSHD", "f32", 2),          # D not a multiple of 16: element loads
+    (2, 4, 1, 256, 100, "BHSD", "bf16", 0),        # largest head
+    (4, 8, 8, 80, 64, "BSHD", "bf16", 0),          # G=1
+    (2, 8, 2, 7, 50, "BHSD", "f32", 0),            # odd head_dim
+]
+
+
+def _ids(c):
+    return f"B{c[0]}Hq{c[1]}Hkv{c[2]}D{c[3]}S{c[4]}{c[5]}{c[6]}n{c[7]}"
+
+
+def _inputs(case, seed_extra=0):
+    B, Hq, Hkv, D, S, layout, qo, ns = case
+    w = W.custom(B, Hq, Hkv, D, S, layout, "i8", qo, seed=B * 100 + D + seed_extra, stale="pm:1")
+    L = torch.randint(0, S, (B,), generator=torch.Generator().manual_seed(S + 7), dtype=torch.int32)
+    L[0] = S - 1                          # a full sequence
+    if B > 2:
+        L[1] = 0                          # only the new token
+    return w, L, W.make_q8(w, DEV, lengths=L)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[_ids(c) for c in CASES])
+def test_q8_step_and_attend(g, case):
+    B, Hq, Hkv, D, S, layout, qo, ns = case
+    w, L, inp = _inputs(case)
+    say(f"q8 step {_ids(case)}")
+    ref, rk, rv, rks, rvs = oracle.step_q8(np_of(inp["q"]), qo, np_of(inp["k_cache"]), np_of(inp["v_cache"]),
+                                           np_of(inp["k_scale"]), np_of(inp["v_scale"]), np_of(inp["k_new"]),
+                                           np_of(inp["v_new"]), L.numpy(), layout, Hq, Hkv)
+    out = g.step_q8(inp["q"], inp["k_cache"], inp["v_cache"], inp["k_scale"], inp["v_scale"], inp["k_new"],
+                    inp["v_new"], inp["lengths"], layout=layout, num_splits=ns)
+    torch.cuda.synchronize()
+    assert_close(out, ref, qo, "step")
+    assert_same_bytes(inp["k_cache"], rk, "k codes")
+    assert_same_bytes(inp["v_cache"], rv, "v codes")
+    assert_same_bytes(inp["k_scale"], rks, "k scales")
+    assert_same_bytes(inp["v_scale"], rvs, "v scales")
+    n = (inp["lengths"] + 1).contiguous()
+    out2 = g.attend_q8(inp["q"], inp["k_cache"], inp["v_cache"], inp["k_scale"], inp["v_scale"], n, layout=layout,
+                       num_splits=ns)
+    torch.cuda.synchronize()
+    assert_close(out2, ref, qo, "attend")
+
+
+@pytest.mark.parametrize("qo", ["f32", "bf16"])
+def test_q8_append_alone_with_ties_and_zero_rows(g, qo):
+    """Rows built so that x / scale lands exactly on .5 (scale = 1 when the
+    row's largest magnitude is 127), a zero row (scale 0, codes 0), and a row
+    whose largest entry is negative; the other rows are random."""
+    w = W.custom(3, 4, 2, 16, 20, "BHSD", "i8", qo, seed=41, stale="pm:1")
+    L = torch.tensor([0, 7, 19], dtype=torch.int32)
+    inp = W.make_q8(w, DEV, lengths=L)
+    tie = torch.tensor([127, 0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 3.5, 126.5, -126.5, 0, 4.5, 5.5, -3.5, 1, 2],
+                       dtype=torch.float32)
+    inp["k_new"][0, 0] = tie.to(inp["k_new"].dtype).to(DEV)
+    inp["v_new"][0, 1] = 0
+    inp["k_new"][1, 0] = (-tie).to(inp["k_new"].dtype).to(DEV)
+    rk, rv, rks, rvs = oracle.append_q8(np_of(inp["k_cache"]), np_of(inp["v_cache"]), np_of(inp["k_scale"]),
+                                        np_of(inp["v_scale"]), np_of(inp["k_new"]), np_of(inp["v_new"]), qo,
+                                        L.numpy(), "BHSD")
+    assert rks[0, 0, 0] == 1.0 and list(rk[0, 0, 0, :4]) == [127, 0, 2, 2]      # the oracle rounds half to even
+    g.append_q8(inp["k_cache"], inp["v_cache"], inp["k_scale"], inp["v_scale"], inp["k_new"], inp["v_new"],
+                inp["lengths"], layout="BHSD")
+    torch.cuda.synchronize()
+    assert_same_bytes(inp["k_cache"], rk, "k codes")
+    assert_same_bytes(inp["v_cache"], rv, "v codes")
+    assert_same_bytes(inp["k_scale"], rks, "k scales")
+    assert_same_bytes(inp["v_scale"], rvs, "v scales")
+
+
+def test_q8_full_size_llama_layer(g):
+    """The Llama-like layer (B=32, Hq=32, Hkv=8, D=128, 4096 cached + 1 new) on
+    int8 caches in the benchmark's launch configuration: sampled outputs
+    against the oracle one head at a time, appended codes and scales exact."""
+    base = W.WORKLOADS["llama3_8b_layer"]
+    w = W.custom(base.B, base.Hq, base.Hkv, base.D, base.capacity, base.layout, "i8", "bf16", seed=base.seed)
+    L = W.draw_lengths(base)
+    inp = W.make_q8(w, DEV, lengths=L)
+    out = g.step_q8(inp["q"], inp["k_cache"], inp["v_cache"], inp["k_scale"], inp["v_scale"], inp["k_new"],
+                    inp["v_new"], inp["lengths"], layout=w.layout)
+    torch.cuda.synchronize()
+    q = oracle.decode(np_of(inp["q"]), "bf16")
+    knew, vnew = np_of(inp["k_new"]), np_of(inp["v_new"])
+    got = out.float().cpu().double().numpy()
+    rng = np.random.default_rng(5)
+    G = w.Hq // w.Hkv
+    for _ in range(6):
+        b, hq = int(rng.integers(w.B)), int(rng.integers(w.Hq))
+        h, n = hq // G, int(L[b]) + 1
+        kc = inp["k_cache"][b, h, :n].cpu().numpy()
+        vc = inp["v_cache"][b, h, :n].cpu().numpy()
+        ks = inp["k_scale"][b, h, :n].cpu().numpy()
+        vs = inp["v_scale"][b, h, :n].cpu().numpy()
+        ck, sk = oracle.quantize_row(oracle.decode(knew[b, h], "bf16").astype(np.float32))
+        cv, sv = oracle.quantize_row(oracle.decode(vnew[b, h], "bf16").astype(np.float32))
+        assert np.array_equal(kc[-1], ck) and ks[-1] == sk
+        assert np.array_equal(vc[-1], cv) and vs[-1] == sv
+        ref = oracle.attend_one(q[b, hq], oracle.dequantize(kc, ks), oracle.dequantize(vc, vs))
+        err = np.abs(got[b, hq] - ref)
+        assert np.all(err <= 1e-2 + 1e-2 * np.abs(ref)), (b, hq, err.max())

@@ -37,7 +37,7 @@ class Workload:
     D: int
     capacity: int
     layout: str            # "BHSD" = (B, Hkv, S, D); "BSHD" = (B, S, Hkv, D)
-    kv_dtype: str          # "f32" | "bf16"
+    kv_dtype: str          # "f32" | "bf16" | "i8" (int8 codes + per-row scales: make_q8)
     qo_dtype: str          # "f32" | "bf16"
     len_lo: int            # pre-append length range, inclusive
     len_hi: int
@@ -181,22 +181,68 @@ def make_mapped(inp: dict, w: Workload, kind: str, *, block_size: int = 16, num_
     return out
 
 
+def make_q8(w: Workload, device="cpu", lengths: torch.Tensor | None = None) -> dict:
+    """Seeded inputs for int8 caches with per-row float32 scales.
+
+    The caches hold int8 codes drawn uniformly from [-127, 127] and the scales
+    are drawn uniformly from [0.5, 1.5] * 3 * key_scale / 127 (keys) or
+    [0.5, 1.5] * 3 / 127 (values), so cached values span about +-3 like the
+    normal draws of ``make_inputs``.  q and the new key/value rows are normal
+    draws stored as ``w.qo_dtype`` (the step quantizes the new rows itself).
+    With ``w.stale != "none"`` the scales of slots >= lengths[b] are NaN, so a
+    read past the valid slots shows up in the output.  Draw order (one
+    generator seeded with ``w.seed + 5000``): q, K codes, V codes, K scales,
+    V scales, new K, new V.  Returns q, k_cache, v_cache, k_scale, v_scale,
+    k_new, v_new, lengths.
+    """
+    g = torch.Generator(device=device).manual_seed(w.seed + 5000)
+    L = draw_lengths(w) if lengths is None else lengths.to(torch.int32).cpu()
+    qot = TORCH_DTYPE[w.qo_dtype]
+    shape = cache_shape(w)
+    sshape = shape[:3]
+
+    def randn(shp, scale=1.0):
+        x = torch.randn(shp, generator=g, device=device, dtype=torch.float32)
+        return x.mul_(scale) if scale != 1.0 else x
+
+    q = randn((w.B, w.Hq, w.D)).to(qot)
+    k_cache = torch.randint(-127, 128, shape, generator=g, device=device, dtype=torch.int8)
+    v_cache = torch.randint(-127, 128, shape, generator=g, device=device, dtype=torch.int8)
+    k_scale = (torch.rand(sshape, generator=g, device=device) + 0.5).mul_(3.0 * w.key_scale / 127)
+    v_scale = (torch.rand(sshape, generator=g, device=device) + 0.5).mul_(3.0 / 127)
+    k_new = randn((w.B, w.Hkv, w.D), w.key_scale).to(qot)
+    v_new = randn((w.B, w.Hkv, w.D)).to(qot)
+    if w.stale != "none":
+        slot = torch.arange(w.capacity, device=device)
+        stale = slot[None, :] >= L.to(device)[:, None].to(torch.int64)          # (B, S)
+        stale = stale[:, None, :] if w.layout == "BHSD" else stale[:, :, None]
+        for sc in (k_scale, v_scale):
+            sc.masked_fill_(stale.expand(sshape), float("nan"))
+    return dict(q=q, k_cache=k_cache, v_cache=v_cache, k_scale=k_scale, v_scale=v_scale, k_new=k_new, v_new=v_new,
+                lengths=L.to(device))
+
+
 def to_numpy_storage(t: torch.Tensor) -> np.ndarray:
-    """A tensor's stored bits as the oracle takes them: float32, or uint16 bf16 patterns."""
+    """A tensor's stored bits as the oracle takes them: float32, int8, or uint16 bf16 patterns."""
     t = t.detach().cpu().contiguous()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
-    if t.dtype == torch.float32:
+    if t.dtype in (torch.float32, torch.int8):
         return t.numpy()
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
 def algorithmic_bytes(w: Workload, lengths) -> int:
     """Bytes one step must move at minimum: valid K+V read (the new token
-    included), Q read, new K/V write, output write."""
-    e_kv = 4 if w.kv_dtype == "f32" else 2
+    included), Q read, new K/V write, output write.  Int8 caches ("i8") move a
+    float32 scale with every row and take the new rows in the q/out dtype."""
     e_qo = 4 if w.qo_dtype == "f32" else 2
     n = np.asarray(lengths, dtype=np.int64) + 1
+    if w.kv_dtype == "i8":
+        row = w.D + 4
+        kv_read = int(n.sum()) * w.Hkv * row * 2
+        return kv_read + 2 * w.B * w.Hq * w.D * e_qo + 2 * w.B * w.Hkv * (w.D * e_qo + row)
+    e_kv = 4 if w.kv_dtype == "f32" else 2
     kv_read = int(n.sum()) * w.Hkv * w.D * 2 * e_kv
     return kv_read + 2 * w.B * w.Hq * w.D * e_qo + 2 * w.B * w.Hkv * w.D * e_kv
 
