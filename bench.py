@@ -30,6 +30,7 @@ MALL_BYTES = 256 << 20
 METRIC = "achieved HBM GB/s (% of MI355X peak) + decode steps/sec per config"
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["gqa_decode_attention_amd/csrc/kernels_mfma.hip", "gqa_decode_attention_amd/csrc/kernels_generic.hip",
+                  "gqa_decode_attention_amd/csrc/kernels_mfma_qkv.hip",
                   "gqa_decode_attention_amd/csrc/device_common.h", "gqa_decode_attention_amd/csrc/gqa_decode.cpp",
                   "gqa_decode_attention_amd/csrc/internal.h", "gqa_decode_attention_amd/build.py"]
 

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libgqa_decode.so")
 
-SOURCES = ["gqa_decode.cpp", "kernels_generic.hip", "kernels_mfma.hip"]
+SOURCES = ["gqa_decode.cpp", "kernels_generic.hip", "kernels_mfma.hip", "kernels_mfma_qkv.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

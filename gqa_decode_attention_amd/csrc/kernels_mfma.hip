@@ -1,5 +1,6 @@
-// Matrix-core (MFMA) attention kernels of the GQA decode step for gfx950,
-// bf16 storage, head width 128.
+// Matrix-core (MFMA) attention kernel of the GQA decode step for gfx950 for
+// large groups (16 < G <= 64), bf16 storage, head width 128.  (Groups of up to
+// 16 query heads run the kernel in kernels_mfma_qkv.hip.)
 //
 // What is computed is the JAX "Grouped-Query Decode Step" page's definition
 // (query head h reads cache head floor(h/G); s_j = q.K_j/sqrt(D) over the
@@ -10,30 +11,10 @@
 // 2^(m_old - m_new) when the maximum grows); splits of the token axis leave
 // (m, l, o) partials that the combine kernel merges.
 //
-// Kernel MFMA_QK (G <= 16).  One workgroup = NW waves (4) = one (sequence,
-// kv-head, split); the split's valid 16-slot tiles are dealt out evenly and
-// each wave walks its own run of them.  Per tile:
-//   scores  S(16 slots x 16 heads) = K_tile(16 x 128) . Q^T(128 x 16) as four
-//           v_mfma_f32_16x16x32_bf16.  Lane l = 16*r + c loads 16-byte pieces of
-//           cache row t0 + c straight into the A operand (bytes 16r + 64kk of
-//           the row for MFMA kk, so one instruction covers 16 rows x 64
-//           contiguous bytes); the B operand holds query head c at the same
-//           head-width positions (zero for c >= G).  Lane l then holds the
-//           scores of slots t0 + 4r .. t0 + 4r + 3 for head c.
-//   softmax the tile maximum per head is a max over the lane's 4 slots and
-//           the 4 rows of lanes (two cross-row exchanges); exp2 with log2(e)
-//           folded into the scale.
-//   V sum   on the vector ALU in float32: lane l loads slots t0 + 4r + i,
-//           elements 8c .. 8c + 7 (each load instruction covers 4 full rows),
-//           and takes the weight of (slot, head g) from lane 16r + g with a DPP
-//           row broadcast.
-// Scores are exact products of bf16 values summed in float32; weights and sums
-// stay float32 (bf16 only for the stored output).
-//
 // Fused step: the new token (slot lengths[b]) is not read from the cache; the
-// workgroup whose split holds it runs one extra tile whose only valid row comes
-// from k_new/v_new, and writes those bits into the cache slot.  No other
-// workgroup reads that slot, so the write cannot race a read.
+// workgroup whose split holds it substitutes k_new/v_new for that row, and
+// writes those bits into the cache slot.  No other workgroup reads that slot,
+// so the write cannot race a read.
 #include <type_traits>
 
 #include "cache_map.h"
@@ -42,9 +23,7 @@
 
 namespace gqa {
 
-const bool kHaveMfmaQk = true;
 const bool kHaveMfmaAll = true;
-const bool kHaveMfmaQkI8 = false;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -57,20 +36,6 @@ constexpr int kD = 128;
 // way, and partials carry their own reference m into the combine.
 constexpr float kRescaleSlack = 8.f;
 
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<I + 1, N>(f);
-  }
-}
-
-// Value of lane (16 * row + G) of `x`, in every lane of the same 16-lane row.
-template <int G>
-__device__ __forceinline__ float row_bcast(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + G, 0xf, 0xf, false));
-}
-
 __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
                                                  0, 0);
@@ -78,300 +43,6 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
 
 __device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
-
-// Online-softmax state of one wave: lane (r, c) keeps m (running max, log2
-// units) and l (its own slots' share of the denominator) for head c, and the
-// unnormalised output of head g at elements 8c .. 8c + 7 summed over its
-// row's slots.
-template <int GP>
-struct WaveState {
-  float m, l;
-  float acc[GP][8];
-};
-
-// One 16-slot tile.  kf: this lane's A-operand pieces; vf[i]: slot t0 + 4r + i,
-// elements 8c..8c+7; rows lo .. valid - 1 of the tile (from t0) are valid, the
-// others are masked.
-template <int GP>
-__device__ __forceinline__ void tile_update(WaveState<GP>& st, const u32x4 (&qf)[4], const u32x4 (&kf)[4],
-                                            const u32x4 (&vf)[4], int lo, int valid, int r, float scale_log2) {
-  f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) s = mfma_16x16x32(kf[kk], qf[kk], s);
-  // Raw scores; the scale log2(e)/sqrt(D) > 0 is folded into the exponent.
-  float sv[4] = {s[0], s[1], s[2], s[3]};
-  if (lo > 0 || valid < 16) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (4 * r + i < lo || 4 * r + i >= valid) sv[i] = kNegInfM;
-  }
-  float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-  mx = rows_max(mx);
-  const float mc = mx * scale_log2;
-  if (__any(mc > st.m + kRescaleSlack)) {  // some head's maximum jumped: move the reference
-    const float m_new = fmaxf(st.m, mc);
-    const float alpha = fast_exp2(st.m - m_new);  // 0 on the first tile
-    st.l *= alpha;
-    st.m = m_new;
-    static_for<0, GP>([&](auto gi) {
-      constexpr int g = decltype(gi)::value;
-      const float ag = row_bcast<g>(alpha);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) st.acc[g][e] *= ag;
-    });
-  }
-  const float nm = -st.m;
-  float p[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(sv[i], scale_log2, nm));
-  st.l += (p[0] + p[1]) + (p[2] + p[3]);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float v[8];
-    widen16<1>(vf[i], v);
-    static_for<0, GP>([&](auto gi) {
-      constexpr int g = decltype(gi)::value;
-      const float pg = row_bcast<g>(p[i]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) st.acc[g][e] = fmaf(pg, v[e], st.acc[g][e]);
-    });
-  }
-}
-
-template <int GP, int NW, bool PAGED>
-__global__ __launch_bounds__(64 * NW) void attend_mfma_qk_kernel(AttnArgs a) {
-  __shared__ float sm_o[NW][GP][kD];
-  __shared__ float sm_m[NW][GP];
-  __shared__ float sm_l[NW][GP];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int r = lane >> 4;
-  const int c = lane & 15;
-
-  int x = blockIdx.x;
-  const int split = x % a.nsplit;
-  x /= a.nsplit;
-  const int h = x % a.Hkv;
-  const int b = x / a.Hkv;
-  const int G = a.G;
-
-  const int L = a.lengths[b];
-  int n = L + a.len_offset;
-  n = n < 0 ? 0 : (n > a.S ? a.S : n);
-  const int t_begin = split * a.split_tokens;
-  const int t_end = min(t_begin + a.split_tokens, n);
-  // Splits holding valid slots; split 0 always runs (it writes the output,
-  // zeros when n = 0, if it is the only active split).
-  const int nact = n == 0 ? 0 : min(a.nsplit, (n + a.split_tokens - 1) / a.split_tokens);
-  if (split >= max(nact, 1)) return;
-
-  // Fused step: slot L holds the new token; it is taken from k_new/v_new.
-  const bool own_new = a.k_new != nullptr && L >= t_begin && L < t_end;
-  const int t_cache_end = own_new ? L : t_end;
-
-  const int64_t base = PAGED ? 0 : row_head_offset(a, b, h);  // dense or slot-indexed row
-  const int64_t rs = a.st;  // elements between consecutive slots (paged: within a block)
-
-  // Tile grid.  When a kv-head's slots are contiguous 256-byte rows, the
-  // 16-slot tiles start at 4 KB-aligned cache addresses (measured faster than
-  // tiles that straddle 4 KB boundaries); the grid then begins up to 15 slots
-  // before t_begin and those leading rows are masked.  A paged cache (block
-  // size a multiple of 16) starts tiles at multiples of 16 slots, so a tile
-  // never crosses a block.
-  int tv = t_begin;
-  if (PAGED) {
-    tv = t_begin & ~15;
-  } else if (rs == kD) {
-    const uint64_t row = (reinterpret_cast<uintptr_t>(a.k_cache) >> 8) + (uint64_t)((base >> 7) + t_begin);
-    tv = t_begin - (int)(row & 15);
-  }
-  // This wave's run of cache slots: the split's 16-slot tiles dealt out
-  // evenly (counts differ by at most one tile), so short sequences use every
-  // wave too.  The run boundaries depend on lengths, the grid does not.
-  // Wave w takes tiles [ceil(w T / NW), ceil((w + 1) T / NW)): the first waves
-  // take the extra tiles and the last wave never has more than any other.
-  // Only wave 0's first tile can hold leading rows; it always holds a valid one.
-  const int ntile = t_cache_end > t_begin ? (t_cache_end - tv + 15) >> 4 : 0;
-  const int w0 = tv + 16 * ((wave * ntile + NW - 1) / NW);
-  const int w1 = min(tv + 16 * (((wave + 1) * ntile + NW - 1) / NW), t_cache_end);
-  // The new token goes to the last wave.
-  const bool new_here = own_new && wave == NW - 1;
-
-  const int64_t qrow = ((int64_t)b * a.Hq + (int64_t)h * G + c) * kD;
-  u32x4 qf[4];
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    qf[kk] = (c < G) ? load16(reinterpret_cast<const uint16_t*>(a.q) + qrow + 32 * kk + 8 * r) : u32x4{0, 0, 0, 0};
-  }
-
-  WaveState<GP> st;
-  st.m = kNegInfM;
-  st.l = 0.f;
-#pragma unroll
-  for (int g = 0; g < GP; ++g)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) st.acc[g][e] = 0.f;
-
-  const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.k_cache) + base;
-  const uint16_t* vb = reinterpret_cast<const uint16_t*>(a.v_cache) + base;
-
-  // Rows past the wave's last valid slot are clamped to that slot, rows before
-  // t_begin to t_begin: every load is unconditional and in bounds, nothing at
-  // or beyond the valid length is ever read, and the clamped rows get score
-  // -inf, i.e. weight exactly 0, on finite values.  A row address is one
-  // 32 x 32 -> 64-bit multiply-add (the byte stride between slots fits 32 bits
-  // and clamped rows are never negative).
-  const uint32_t rsb = (uint32_t)rs * 2u;
-  const char* kl = reinterpret_cast<const char*>(kb) + 16 * r;
-  const char* vl = reinterpret_cast<const char*>(vb) + 16 * c;
-  // Paged: a tile's rows lie in the block of its 16-slot origin tc (clamped
-  // into the wave's run, so prefetches past the end stay in a mapped block);
-  // `blk` is that block's table entry, loaded a tile pair ahead and kept in a
-  // vector register until its tile is loaded (its wait is then far behind it).
-  const int last16 = max((w1 - 1) & ~15, tv);
-  auto tile_origin = [&](int t0) { return max(min(t0, last16), tv); };
-  auto entry = [&](int t0) -> int32_t {
-    if (!PAGED) return 0;
-    return a.map[(int64_t)b * a.max_blocks + tile_origin(t0) / a.bs];
-  };
-  auto load_tile = [&](int t0, u32x4 (&k)[4], u32x4 (&v)[4], int32_t blk) {
-    const char* kt = kl;
-    const char* vt = vl;
-    int tc = 0;
-    if (PAGED) {
-      tc = tile_origin(t0);
-      const int64_t off = (block_head_offset(a, blk, h) + (int64_t)(tc % a.bs) * rs) * 2;
-      kt = reinterpret_cast<const char*>(a.k_cache) + off + 16 * r;
-      vt = reinterpret_cast<const char*>(a.v_cache) + off + 16 * c;
-    }
-    const uint32_t rk = (uint32_t)(max(min(t0 + c, w1 - 1), t_begin) - tc);
-    const char* p = kt + (uint64_t)rk * rsb;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) k[kk] = load_nt16(p + 64 * kk);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t rv = (uint32_t)(max(min(t0 + 4 * r + i, w1 - 1), t_begin) - tc);
-      v[i] = load_nt16(vt + (uint64_t)rv * rsb);
-    }
-  };
-
-  // The new token is a tile whose only valid row is k_new/v_new; its loads are
-  // issued before the first cache tile's, and its bits are copied to slot L
-  // after the loop (no store is in flight while the tiles stream).
-  u32x4 knw[4], vnw;
-  if (new_here) {
-    const int64_t nrow = ((int64_t)b * a.Hkv + h) * kD;
-    const uint16_t* knp = reinterpret_cast<const uint16_t*>(a.k_new) + nrow;
-    const uint16_t* vnp = reinterpret_cast<const uint16_t*>(a.v_new) + nrow;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) knw[kk] = (c == 0) ? load16(knp + 32 * kk + 8 * r) : u32x4{0, 0, 0, 0};
-    vnw = (r == 0) ? load16(vnp + 8 * c) : u32x4{0, 0, 0, 0};
-  }
-  // Two register sets alternate, so the next tile's loads are in flight during
-  // this tile's math and no register copy waits for them.
-  u32x4 ka[4], va[4], kc[4], vc[4];
-  int32_t eC = entry(w0 + 16), eA = entry(w0 + 32);  // table entries of the first tile pair's successors
-  load_tile(w0, ka, va, entry(w0));
-  if (new_here) {
-    const u32x4 vf[4] = {vnw, u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}};
-    tile_update<GP>(st, qf, knw, vf, 0, 1, r, a.scale_log2);
-  }
-  if (w0 < w1) {
-    const int nt = (w1 - w0 + 15) >> 4;
-    int t0 = w0;
-    for (int it = 0; it < nt / 2; ++it) {
-      const int32_t nC = entry(t0 + 48), nA = entry(t0 + 64);
-      load_tile(t0 + 16, kc, vc, eC);
-      tile_update<GP>(st, qf, ka, va, t_begin - t0, w1 - t0, r, a.scale_log2);
-      load_tile(t0 + 32, ka, va, eA);  // past w1 it re-reads row w1 - 1
-      tile_update<GP>(st, qf, kc, vc, t_begin - t0 - 16, w1 - t0 - 16, r, a.scale_log2);
-      eC = nC;
-      eA = nA;
-      t0 += 32;
-    }
-    if (nt & 1) tile_update<GP>(st, qf, ka, va, t_begin - t0, w1 - t0, r, a.scale_log2);
-  }
-  if (new_here) {
-    const int64_t off = slot_offset_checked(a, b, h, L);  // -1: the map names no valid row/block
-    uint16_t* kw = reinterpret_cast<uint16_t*>(a.k_cache_w) + off;
-    uint16_t* vw = reinterpret_cast<uint16_t*>(a.v_cache_w) + off;
-    if (off >= 0 && c == 0) {
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) store16(kw + 32 * kk + 8 * r, knw[kk]);
-    }
-    if (off >= 0 && r == 0) store16(vw + 8 * c, vnw);
-  }
-
-  // Merge the 4 rows of lanes of each wave (disjoint slots, same running max).
-  st.l = rows_sum(st.l);
-#pragma unroll
-  for (int g = 0; g < GP; ++g)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      st.acc[g][e] = rows_sum(st.acc[g][e]);
-    }
-  if (r == 0) {
-#pragma unroll
-    for (int g = 0; g < GP; ++g)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sm_o[wave][g][8 * c + e] = st.acc[g][e];
-    if (c < GP) {
-      sm_m[wave][c] = st.m;
-      sm_l[wave][c] = st.l;
-    }
-  }
-  __syncthreads();
-
-  // Merge the NW waves; write the output, or this split's partial.
-  for (int idx = threadIdx.x; idx < G * kD; idx += 64 * NW) {
-    const int g = idx / kD;
-    const int d = idx - g * kD;
-    float M = kNegInfM;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][g]);
-    float O = 0.f, Lsum = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float mw = sm_m[w][g];
-      const float sc = mw == kNegInfM ? 0.f : fast_exp2(mw - M);
-      O += sm_o[w][g][d] * sc;
-      Lsum += sm_l[w][g] * sc;
-    }
-    const int hq = h * G + g;
-    if (nact <= 1) {
-      reinterpret_cast<uint16_t*>(a.out)[((int64_t)b * a.Hq + hq) * kD + d] =
-          f32_to_bf16_rne(Lsum > 0.f ? O / Lsum : 0.f);
-    } else {
-      const int64_t pi = ((int64_t)b * a.Hq + hq) * a.nsplit + split;
-      a.part_o[pi * kD + d] = O;
-      if (d == 0) {
-        a.part_m[pi] = M;
-        a.part_l[pi] = Lsum;
-      }
-    }
-  }
-}
-
-template <int GP>
-static hipError_t launch_qk_t(const AttnArgs& a, const Plan& p, hipStream_t s) {
-  constexpr int NW = 4;
-  if (p.block != 64 * NW) return hipErrorInvalidValue;
-  AttnArgs arg = a;
-  void* params[] = {&arg};
-  const void* fn = a.map_kind == GQA_MAP_PAGED ? reinterpret_cast<const void*>(&attend_mfma_qk_kernel<GP, NW, true>)
-                                               : reinterpret_cast<const void*>(&attend_mfma_qk_kernel<GP, NW, false>);
-  return hipLaunchKernel(fn, dim3(p.grid), dim3(p.block), params, 0, s);
-}
-
-hipError_t launch_attend_mfma_qk(const AttnArgs& a, const Plan& p, hipStream_t s) {
-  if (a.D != kD || a.G > 16) return hipErrorInvalidValue;
-  if (a.G <= 1) return launch_qk_t<1>(a, p, s);
-  if (a.G <= 2) return launch_qk_t<2>(a, p, s);
-  if (a.G <= 4) return launch_qk_t<4>(a, p, s);
-  if (a.G <= 8) return launch_qk_t<8>(a, p, s);
-  return launch_qk_t<16>(a, p, s);
-}
 
 // ---------------------------------------------------------------------------
 // Kernel MFMA_ALL (16 < G <= 64): scores and the V sum both on MFMA.

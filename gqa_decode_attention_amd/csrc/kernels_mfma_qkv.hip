@@ -1,0 +1,445 @@
+// Matrix-core attention kernel of the GQA decode step for small groups
+// (G <= 16), head width 128, bf16 q/out: scores and the V sum on MFMA.
+//
+// Serves int8 caches with per-row float32 scales (Huawei CANN
+// "aclnnMlaPrologV3WeightNz" page, dynamic-quantization formula: a cached
+// value reads as code * row scale), and bf16 caches.  What is computed is the
+// JAX "Grouped-Query Decode Step" page's definition over the dequantized rows,
+// with the online softmax over 16-slot tiles of the other matrix-core kernels.
+//
+// One workgroup = NW waves = one (sequence, kv-head, split); each wave walks
+// its own run of 16-slot tiles.  Lane l = 16 r + c.  Per tile:
+//   scores  S(16 slots x 16 heads) = K(16 x 128) . Q^T as four
+//           v_mfma_f32_16x16x32_bf16: lane (r, c) supplies A-operand pieces of
+//           cache row t0 + c.  bf16 caches: bytes 16r + 64kk of the row for
+//           MFMA kk.  int8: two 16-byte loads (bytes 16r + 64j, j = 0, 1) give
+//           32 codes, widened exactly to bf16 (|code| <= 127); MFMA 2j + h
+//           takes codes 64j + 16r + 8h .. +7, and the query operand holds the
+//           same head-width positions (the dot product does not care how the
+//           positions are dealt, only that both operands agree).  Lane (r, c)
+//           then holds the scores of slots 4r .. 4r + 3 for head c; int8 rows
+//           multiply them by their key scales.
+//   softmax per head c, as in the other kernels (lazy rescale, exp2 with the
+//           scale folded in).
+//   V sum   O^T(128 x 16 heads) += V^T(128 x 16 slots) . P'(16 slots x 16
+//           heads) as eight v_mfma_f32_16x16x16_bf16, e = 0..7.  Lane (r, c)
+//           loads slots 4r + i (i = 0..3) at elements 8c .. 8c + 7; the A
+//           operand of MFMA e is element 8c + e of its four slots (so MFMA e
+//           covers head-width positions e, 8 + e, ..., 120 + e), and the B
+//           operand is the lane's own four weights of head c, times the value
+//           scales of int8 rows, rounded to bf16.  Lane (r, c) receives head c
+//           at positions 8(4r + i) + e: complete sums, no cross-lane reduction.
+// Scores are exact products (bf16 or small integers) summed in float32; the
+// weights enter the V sum rounded to bf16 (their sum l stays float32).
+//
+// Fused step (bf16 caches): the new token (slot lengths[b]) is not read from
+// the cache; the last wave of the workgroup whose split holds it runs one extra
+// tile whose only valid row comes from k_new / v_new, and writes those bits
+// into the cache slot after its loop.  No other workgroup reads that slot, so
+// the write cannot race a read.  Int8 caches get the new row from the
+// quantizing append kernel, launched first on the same stream.
+//
+// Paged bf16 caches (CLIKA runtime "groupQueryAttention" API page, block
+// table): with a block size that is a multiple of 16, every 16-slot tile lies
+// in one block, whose table entry each wave loads a tile pair ahead.
+#include <type_traits>
+
+#include "cache_map.h"
+#include "device_common.h"
+#include "internal.h"
+
+namespace gqa {
+
+namespace qkv {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kNegInfQ = -__builtin_inff();
+constexpr int kDq = 128;
+constexpr float kSlackQ = 8.f;  // lazy rescale threshold, log2 units
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void unroll(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    unroll<I + 1, N>(f);
+  }
+}
+
+__device__ __forceinline__ f32x4 mfma_k32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_k16(u32x2_t a, u32x2_t b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a), __builtin_bit_cast(s16x4_t, b), c,
+                                                   0, 0, 0);
+}
+
+// Two floats to a bf16 pair (low half = lo), round to nearest even.
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
+// Signed byte B of w as a float (one SDWA conversion).
+template <int B>
+__device__ __forceinline__ float sbyte(uint32_t w) {
+  return (float)(int32_t)((int32_t)(w << (24 - 8 * B)) >> 24);
+}
+
+// Value of lane I of this lane's group of four (DPP quad permutation).
+template <int I>
+__device__ __forceinline__ float quad_bcast(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), I * 0x55, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ u32x2_t load_nt8(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+}
+
+// One tile's loads.  bf16: k[kk] = A pieces of MFMA kk, v[i] = 16 bytes of slot
+// 4r + i.  int8: k[0..1] = 32 codes, v8[i] = 8 codes of slot 4r + i, ks / vs =
+// the scales of slot 4r + (c & 3).
+template <int KV>
+struct Tile;
+template <>
+struct Tile<GQA_BF16> {
+  u32x4 k[4];
+  u32x4 v[4];
+};
+template <>
+struct Tile<GQA_I8> {
+  u32x4 k[2];
+  u32x2_t v[4];
+  float ks, vs;
+};
+
+struct State {
+  float m, l;
+  f32x4 acc[8];
+};
+
+template <int KV>
+__device__ __forceinline__ void tile_math(State& st, const u32x4 (&qf)[4], const Tile<KV>& t, int lo, int valid,
+                                          int r, float scale_log2) {
+  // Scores.
+  u32x4 kf[4];
+  if constexpr (KV == GQA_BF16) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) kf[kk] = t.k[kk];
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t w0 = t.k[j][2 * h], w1 = t.k[j][2 * h + 1];
+        kf[2 * j + h] = u32x4{pk_bf16(sbyte<0>(w0), sbyte<1>(w0)), pk_bf16(sbyte<2>(w0), sbyte<3>(w0)),
+                              pk_bf16(sbyte<0>(w1), sbyte<1>(w1)), pk_bf16(sbyte<2>(w1), sbyte<3>(w1))};
+      }
+  }
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) s = mfma_k32(kf[kk], qf[kk], s);
+  float sv[4] = {s[0], s[1], s[2], s[3]};
+  if constexpr (KV == GQA_I8) {
+    sv[0] *= quad_bcast<0>(t.ks);
+    sv[1] *= quad_bcast<1>(t.ks);
+    sv[2] *= quad_bcast<2>(t.ks);
+    sv[3] *= quad_bcast<3>(t.ks);
+  }
+  if (lo > 0 || valid < 16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * r + i < lo || 4 * r + i >= valid) sv[i] = kNegInfQ;
+  }
+  // Softmax (per head c = this lane's column).
+  float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+  mx = rows_max(mx);
+  const float mc = mx * scale_log2;
+  if (__any(mc > st.m + kSlackQ)) {
+    const float m_new = fmaxf(st.m, mc);
+    const float alpha = fast_exp2(st.m - m_new);  // 0 on the first tile
+    st.l *= alpha;
+    st.m = m_new;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st.acc[e] *= alpha;
+  }
+  const float nm = -st.m;
+  float p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(sv[i], scale_log2, nm));
+  st.l += (p[0] + p[1]) + (p[2] + p[3]);
+  if constexpr (KV == GQA_I8) {
+    p[0] *= quad_bcast<0>(t.vs);
+    p[1] *= quad_bcast<1>(t.vs);
+    p[2] *= quad_bcast<2>(t.vs);
+    p[3] *= quad_bcast<3>(t.vs);
+  }
+  const u32x2_t pb = {pk_bf16(p[0], p[1]), pk_bf16(p[2], p[3])};
+  // V sum: A operand of MFMA e = element 8c + e of slots 4r .. 4r + 3.
+  unroll<0, 8>([&](auto ei) {
+    constexpr int e = decltype(ei)::value;
+    u32x2_t va;
+    if constexpr (KV == GQA_BF16) {
+      constexpr uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      va = u32x2_t{__builtin_amdgcn_perm(t.v[1][e >> 1], t.v[0][e >> 1], sel),
+                   __builtin_amdgcn_perm(t.v[3][e >> 1], t.v[2][e >> 1], sel)};
+    } else {
+      constexpr int wd = e >> 2, by = e & 3;
+      va = u32x2_t{pk_bf16(sbyte<by>(t.v[0][wd]), sbyte<by>(t.v[1][wd])),
+                   pk_bf16(sbyte<by>(t.v[2][wd]), sbyte<by>(t.v[3][wd]))};
+    }
+    st.acc[e] = mfma_k16(va, pb, st.acc[e]);
+  });
+}
+
+template <int KV, int NW, bool PAGED>
+__global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
+  static_assert(!(PAGED && KV == GQA_I8), "int8 caches are dense");
+  __shared__ float sm_o[NW][16][kDq];
+  __shared__ float sm_m[NW][16];
+  __shared__ float sm_l[NW][16];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r = lane >> 4;
+  const int c = lane & 15;
+
+  int x = blockIdx.x;
+  const int split = x % a.nsplit;
+  x /= a.nsplit;
+  const int h = x % a.Hkv;
+  const int b = x / a.Hkv;
+  const int G = a.G;
+
+  const int L = a.lengths[b];
+  int n = L + a.len_offset;
+  n = n < 0 ? 0 : (n > a.S ? a.S : n);
+  const int t_begin = split * a.split_tokens;
+  const int t_end = min(t_begin + a.split_tokens, n);
+  const int nact = n == 0 ? 0 : min(a.nsplit, (n + a.split_tokens - 1) / a.split_tokens);
+  if (split >= max(nact, 1)) return;
+
+  // Fused step (bf16 caches only): slot L is taken from k_new / v_new.
+  const bool own_new = KV == GQA_BF16 && a.k_new != nullptr && L >= t_begin && L < t_end;
+  const int t_cache_end = own_new ? L : t_end;
+
+  constexpr int EB = KV == GQA_BF16 ? 2 : 1;  // bytes per cached element
+  const int64_t base = PAGED ? 0 : row_head_offset(a, b, h);  // dense or slot-indexed row
+  const int64_t rs = a.st;  // elements between consecutive slots (paged: within a block)
+
+  // Tile grid.  When a kv-head's rows are contiguous, tiles start at 16-row
+  // aligned cache addresses (4 KB for bf16, measured faster than tiles that
+  // straddle 4 KB boundaries); a paged cache (block size a multiple of 16)
+  // starts them at multiples of 16 slots, so a tile never crosses a block.
+  // The leading rows before t_begin are masked.
+  int tv = t_begin;
+  if (PAGED) {
+    tv = t_begin & ~15;
+  } else if (rs == kDq) {
+    const uint64_t row = (reinterpret_cast<uintptr_t>(a.k_cache) / (kDq * EB)) + (uint64_t)(base / kDq + t_begin);
+    tv = t_begin - (int)(row & 15);
+  }
+  // This wave's run: the split's tiles dealt out evenly (wave w takes tiles
+  // [ceil(w T / NW), ceil((w + 1) T / NW))), so short sequences use every wave
+  // too; only wave 0's first tile can hold leading rows, and it always holds a
+  // valid one.  The new token goes to the last wave.
+  const int ntile = t_cache_end > t_begin ? (t_cache_end - tv + 15) >> 4 : 0;
+  const int w0 = tv + 16 * ((wave * ntile + NW - 1) / NW);
+  const int w1 = min(tv + 16 * (((wave + 1) * ntile + NW - 1) / NW), t_cache_end);
+  const bool new_here = own_new && wave == NW - 1;
+
+  // Query operand: positions matching the K operand's.
+  const int64_t qrow = ((int64_t)b * a.Hq + (int64_t)h * G + c) * kDq;
+  const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + qrow;
+  u32x4 qf[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int d0 = KV == GQA_BF16 ? 32 * kk + 8 * r : 64 * (kk >> 1) + 16 * r + 8 * (kk & 1);
+    qf[kk] = (c < G) ? *reinterpret_cast<const u32x4*>(qp + d0) : u32x4{0, 0, 0, 0};
+  }
+
+  State st;
+  st.m = kNegInfQ;
+  st.l = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) st.acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Rows are clamped into [t_begin, w1 - 1]: every load is in bounds and reads
+  // a valid slot; clamped rows are masked to weight 0.
+  const uint32_t rsb = (uint32_t)rs * EB;
+  const char* kl = reinterpret_cast<const char*>(a.k_cache) + base * EB + 16 * r;
+  const char* vl = reinterpret_cast<const char*>(a.v_cache) + base * EB + (KV == GQA_BF16 ? 16 : 8) * c;
+  const int64_t sbase = base / kDq;     // scale index of slot 0 (dense rows are multiples of D)
+  const int64_t sst = rs / kDq;         // scale entries between slots
+  // Paged: a tile's rows lie in the block of its 16-slot origin (clamped into
+  // the wave's run, so prefetches past the end stay in a mapped block); `blk`
+  // is that block's table entry, loaded a tile pair ahead.
+  const int last16 = max((w1 - 1) & ~15, tv);
+  auto tile_origin = [&](int t0) { return max(min(t0, last16), tv); };
+  auto entry = [&](int t0) -> int32_t {
+    if (!PAGED) return 0;
+    return a.map[(int64_t)b * a.max_blocks + tile_origin(t0) / a.bs];
+  };
+  auto load_tile = [&](int t0, Tile<KV>& t, int32_t blk) {
+    const char* kt = kl;
+    const char* vt = vl;
+    int tc = 0;
+    if (PAGED) {
+      tc = tile_origin(t0);
+      const int64_t off = (block_head_offset(a, blk, h) + (int64_t)(tc % a.bs) * rs) * EB;
+      kt = reinterpret_cast<const char*>(a.k_cache) + off + 16 * r;
+      vt = reinterpret_cast<const char*>(a.v_cache) + off + 16 * c;
+    }
+    const uint32_t rk = (uint32_t)(max(min(t0 + c, w1 - 1), t_begin) - tc);
+    const char* p = kt + (uint64_t)rk * rsb;
+    if constexpr (KV == GQA_BF16) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) t.k[kk] = load_nt16(p + 64 * kk);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) t.k[j] = load_nt16(p + 64 * j);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t rv = (uint32_t)(max(min(t0 + 4 * r + i, w1 - 1), t_begin) - tc);
+      if constexpr (KV == GQA_BF16)
+        t.v[i] = load_nt16(vt + (uint64_t)rv * rsb);
+      else
+        t.v[i] = load_nt8(vt + (uint64_t)rv * rsb);
+    }
+    if constexpr (KV == GQA_I8) {
+      const int64_t rsc = sbase + (int64_t)max(min(t0 + 4 * r + (c & 3), w1 - 1), t_begin) * sst;
+      t.ks = __uint_as_float(load_nt4(a.k_scale + rsc));
+      t.vs = __uint_as_float(load_nt4(a.v_scale + rsc));
+    }
+  };
+
+  // Fused step, bf16: the new token is a tile whose only valid row is
+  // k_new / v_new (row 0: lanes c = 0 for K, slot 0 = lanes of row r = 0, i = 0
+  // for V); its bits are copied to slot L after the loop.
+  Tile<KV> tn;
+  if constexpr (KV == GQA_BF16) {
+    if (new_here) {
+      const int64_t nrow = ((int64_t)b * a.Hkv + h) * kDq;
+      const uint16_t* knp = reinterpret_cast<const uint16_t*>(a.k_new) + nrow;
+      const uint16_t* vnp = reinterpret_cast<const uint16_t*>(a.v_new) + nrow;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        tn.k[kk] = (c == 0) ? *reinterpret_cast<const u32x4*>(knp + 32 * kk + 8 * r) : u32x4{0, 0, 0, 0};
+      tn.v[0] = (r == 0) ? *reinterpret_cast<const u32x4*>(vnp + 8 * c) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int i = 1; i < 4; ++i) tn.v[i] = u32x4{0, 0, 0, 0};
+    }
+  }
+
+  // Two tile register sets alternate, so the next tile's loads are in flight
+  // during this tile's math.
+  Tile<KV> ta, tb;
+  int32_t eB = entry(w0 + 16), eA = entry(w0 + 32);  // table entries of the first pair's successors
+  load_tile(w0, ta, entry(w0));
+  if constexpr (KV == GQA_BF16) {
+    if (new_here) tile_math<KV>(st, qf, tn, 0, 1, r, a.scale_log2);
+  }
+  if (w0 < w1) {
+    const int nt = (w1 - w0 + 15) >> 4;
+    int t0 = w0;
+    for (int it = 0; it < nt / 2; ++it) {
+      const int32_t nB = entry(t0 + 48), nA = entry(t0 + 64);
+      load_tile(t0 + 16, tb, eB);
+      tile_math<KV>(st, qf, ta, t_begin - t0, w1 - t0, r, a.scale_log2);
+      load_tile(t0 + 32, ta, eA);  // past w1 it re-reads row w1 - 1
+      tile_math<KV>(st, qf, tb, t_begin - t0 - 16, w1 - t0 - 16, r, a.scale_log2);
+      eB = nB;
+      eA = nA;
+      t0 += 32;
+    }
+    if (nt & 1) tile_math<KV>(st, qf, ta, t_begin - t0, w1 - t0, r, a.scale_log2);
+  }
+  if constexpr (KV == GQA_BF16) {
+    if (new_here) {
+      const int64_t off = slot_offset_checked(a, b, h, L);
+      uint16_t* kw = reinterpret_cast<uint16_t*>(a.k_cache_w) + off;
+      uint16_t* vw = reinterpret_cast<uint16_t*>(a.v_cache_w) + off;
+      if (off >= 0 && c == 0) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) *reinterpret_cast<u32x4*>(kw + 32 * kk + 8 * r) = tn.k[kk];
+      }
+      if (off >= 0 && r == 0) *reinterpret_cast<u32x4*>(vw + 8 * c) = tn.v[0];
+    }
+  }
+
+  // Each lane holds complete sums of head c at positions 8(4r + i) + e.
+  st.l = rows_sum(st.l);
+  if (c < G) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm_o[wave][c][8 * (4 * r + i) + e] = st.acc[e][i];
+    if (r == 0) {
+      sm_m[wave][c] = st.m;
+      sm_l[wave][c] = st.l;
+    }
+  }
+  __syncthreads();
+
+  for (int idx = threadIdx.x; idx < G * kDq; idx += 64 * NW) {
+    const int g = idx / kDq;
+    const int d = idx - g * kDq;
+    float M = kNegInfQ;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][g]);
+    float O = 0.f, Lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float mw = sm_m[w][g];
+      const float sc = mw == kNegInfQ ? 0.f : fast_exp2(mw - M);
+      O += sm_o[w][g][d] * sc;
+      Lsum += sm_l[w][g] * sc;
+    }
+    const int hq = h * G + g;
+    if (nact <= 1) {
+      reinterpret_cast<uint16_t*>(a.out)[((int64_t)b * a.Hq + hq) * kDq + d] =
+          f32_to_bf16_rne(Lsum > 0.f ? O / Lsum : 0.f);
+    } else {
+      const int64_t pi = ((int64_t)b * a.Hq + hq) * a.nsplit + split;
+      a.part_o[pi * kDq + d] = O;
+      if (d == 0) {
+        a.part_m[pi] = M;
+        a.part_l[pi] = Lsum;
+      }
+    }
+  }
+}
+
+}  // namespace qkv
+
+using qkv::attend_mfma_qkv_kernel;
+
+const bool kHaveMfmaQk = true;
+const bool kHaveMfmaQkI8 = true;
+
+// bf16 caches (dense, slot-indexed or paged) or int8 caches (dense, new token
+// appended beforehand).
+hipError_t launch_attend_mfma_qk(const AttnArgs& a, const Plan& p, hipStream_t s) {
+  constexpr int NW = 4;
+  if (a.D != qkv::kDq || a.G > 16 || p.block != 64 * NW) return hipErrorInvalidValue;
+  const void* fn;
+  if (a.kv_dtype == GQA_I8) {
+    if (a.map_kind != 0 || a.k_new != nullptr || a.k_scale == nullptr || a.v_scale == nullptr)
+      return hipErrorInvalidValue;
+    fn = reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_I8, NW, false>);
+  } else if (a.map_kind == GQA_MAP_PAGED) {
+    fn = reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_BF16, NW, true>);
+  } else {
+    fn = reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_BF16, NW, false>);
+  }
+  AttnArgs arg = a;
+  void* params[] = {&arg};
+  return hipLaunchKernel(fn, dim3(p.grid), dim3(p.block), params, 0, s);
+}
+
+}  // namespace gqa
