@@ -30,3 +30,10 @@ from .quant import (  # noqa: F401
     quantize_row,
     step_q8,
 )
+from .rope import (  # noqa: F401
+    encode,
+    rms_norm,
+    rope_rotate,
+    rotate_new,
+    step_rope,
+)
