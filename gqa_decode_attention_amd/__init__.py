@@ -5,7 +5,8 @@ Python face of the HIP library ``libgqa_decode.so`` (C ABI in
 slot ``lengths[b]`` of a fixed-capacity cache, ``attend`` runs length-masked
 GQA attention over the cache, and ``step`` does both in one call; the
 ``_mapped`` calls take slot-indexed or paged caches and the ``_q8`` calls int8
-caches with per-row scales.  torch is
+caches with per-row scales; the ``_ex`` calls take any combination of a cache
+map, int8 scales and rotary encoding (``Rope``).  torch is
 used for device memory and streams only.
 """
 from ._lib import (  # noqa: F401
@@ -17,11 +18,16 @@ from ._lib import (  # noqa: F401
     Desc,
     GqaError,
     MapT,
+    OptsT,
+    Rope,
+    RopeT,
     ScalesT,
     append,
+    append_ex,
     append_q8,
     append_mapped,
     attend,
+    attend_ex,
     attend_mapped,
     attend_q8,
     check_lengths,
@@ -30,7 +36,9 @@ from ._lib import (  # noqa: F401
     lib,
     make_desc,
     step,
+    step_ex,
     step_mapped,
     step_q8,
     workspace_size,
+    workspace_size_ex,
 )

@@ -79,6 +79,32 @@ class ScalesT(ctypes.Structure):
     _fields_ = [("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
 
 
+ROPE_MODES = {"half": 0, "interleaved": 1}
+
+
+class RopeT(ctypes.Structure):
+    """gqa_rope_t."""
+    _fields_ = [
+        ("cos", ctypes.c_void_p),
+        ("sin", ctypes.c_void_p),
+        ("max_pos", ctypes.c_int32),
+        ("mode", ctypes.c_int32),
+        ("positions", ctypes.c_void_p),
+        ("q_norm_gain", ctypes.c_void_p),
+        ("k_norm_gain", ctypes.c_void_p),
+        ("norm_eps", ctypes.c_float),
+    ]
+
+
+class OptsT(ctypes.Structure):
+    """gqa_decode_opts_t."""
+    _fields_ = [
+        ("map", ctypes.POINTER(MapT)),
+        ("scales", ctypes.POINTER(ScalesT)),
+        ("rope", ctypes.POINTER(RopeT)),
+    ]
+
+
 EXPORTS = (
     "gqa_decode_workspace_size",
     "gqa_decode_get_plan",
@@ -91,6 +117,10 @@ EXPORTS = (
     "gqa_decode_append_q8",
     "gqa_decode_attend_q8",
     "gqa_decode_step_q8",
+    "gqa_decode_workspace_size_ex",
+    "gqa_decode_append_ex",
+    "gqa_decode_attend_ex",
+    "gqa_decode_step_ex",
     "gqa_decode_check_lengths",
     "gqa_decode_status_string",
     "gqa_decode_version",
@@ -123,10 +153,16 @@ def lib() -> ctypes.CDLL:
     L.gqa_decode_append_q8.argtypes = [DP, SP, P, P, P, P, I32P, P]
     L.gqa_decode_attend_q8.argtypes = [DP, SP, P, P, P, I32P, P, P, S, P]
     L.gqa_decode_step_q8.argtypes = [DP, SP, P, P, P, P, P, I32P, P, P, S, P]
+    OP = ctypes.POINTER(OptsT)
+    L.gqa_decode_workspace_size_ex.argtypes = [DP, OP, ctypes.POINTER(ctypes.c_size_t)]
+    L.gqa_decode_append_ex.argtypes = [DP, OP, P, P, P, P, I32P, P]
+    L.gqa_decode_attend_ex.argtypes = [DP, OP, P, P, P, I32P, P, P, S, P]
+    L.gqa_decode_step_ex.argtypes = [DP, OP, P, P, P, P, P, I32P, P, P, S, P]
     for name in ("gqa_decode_workspace_size", "gqa_decode_get_plan", "gqa_decode_append", "gqa_decode_attend",
                  "gqa_decode_step", "gqa_decode_check_lengths", "gqa_decode_append_mapped",
                  "gqa_decode_attend_mapped", "gqa_decode_step_mapped", "gqa_decode_append_q8",
-                 "gqa_decode_attend_q8", "gqa_decode_step_q8"):
+                 "gqa_decode_attend_q8", "gqa_decode_step_q8", "gqa_decode_workspace_size_ex",
+                 "gqa_decode_append_ex", "gqa_decode_attend_ex", "gqa_decode_step_ex"):
         getattr(L, name).restype = ctypes.c_int
     L.gqa_decode_status_string.argtypes = [ctypes.c_int]
     L.gqa_decode_status_string.restype = ctypes.c_char_p
@@ -405,4 +441,136 @@ def step_q8(q, k_cache, v_cache, k_scale, v_scale, k_new, v_new, lengths, *, lay
     check(lib().gqa_decode_step_q8(ctypes.byref(desc), ctypes.byref(sc), q.data_ptr(), k_cache.data_ptr(),
                                    v_cache.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), lengths.data_ptr(),
                                    out.data_ptr(), wptr, wbytes, _stream(dev)), "gqa_decode_step_q8")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Calls with options: any combination of a cache map, int8 scales and rotary
+# encoding (gqa_decode_opts_t).
+# ---------------------------------------------------------------------------
+class Rope:
+    """Rotary encoding of q and the new key (gqa_rope_t).
+
+    cos, sin: float32 (max_pos, D/2) device tensors; mode "half" or
+    "interleaved"; positions: int32 (B,) device tensor or None (the new slot
+    lengths[b]); q_gain / k_gain: float32 (D,) device tensors or None, with eps
+    (>= 0) exactly when a gain is given."""
+
+    def __init__(self, cos, sin, mode="half", positions=None, q_gain=None, k_gain=None, eps=None):
+        if mode not in ROPE_MODES:
+            raise ValueError(f"mode must be one of {list(ROPE_MODES)}")
+        for t in (cos, sin, q_gain, k_gain):
+            if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda):
+                raise ValueError("rope tables and gains are contiguous float32 device tensors")
+        if positions is not None and (positions.dtype != torch.int32 or not positions.is_contiguous()):
+            raise ValueError("positions is a contiguous int32 tensor")
+        if cos.dim() != 2 or cos.shape != sin.shape:
+            raise ValueError("cos / sin are (max_pos, D/2)")
+        self.cos, self.sin, self.mode, self.positions = cos, sin, mode, positions
+        self.q_gain, self.k_gain, self.eps = q_gain, k_gain, eps
+
+    def struct(self) -> RopeT:
+        ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+        return RopeT(self.cos.data_ptr(), self.sin.data_ptr(), self.cos.shape[0], ROPE_MODES[self.mode],
+                     ptr(self.positions), ptr(self.q_gain), ptr(self.k_gain),
+                     -1.0 if self.eps is None else float(self.eps))
+
+
+def _opts(desc_args, *, table=None, kind=None, table_host=None, k_scale=None, v_scale=None, k_cache=None,
+          layout="BHSD", rope=None):
+    """(desc, opts, keep-alive) for an _ex call; desc_args = (B, Hq, D, kv_code, qo_code, num_splits, Hkv)."""
+    B, Hq, D, kv_code, qo_code, ns, Hkv = desc_args
+    keep = []
+    o = OptsT()
+    if table is not None:
+        desc, m, k = _mapped_desc(B, Hq, D, kv_code, qo_code, k_cache, kind, layout, table, ns, Hkv, table_host)
+        keep += [m, k]
+        o.map = ctypes.pointer(m)
+    else:
+        if layout == "BHSD":
+            Bc, Hc, S, Dc = k_cache.shape
+        else:
+            Bc, S, Hc, Dc = k_cache.shape
+        if Bc != B or Dc != D or (Hkv is not None and Hc != Hkv):
+            raise ValueError("cache shape disagrees with q / new rows")
+        desc = make_desc(B, Hq, Hc, D, S, layout, kv_code, qo_code, ns)
+    if k_scale is not None:
+        sc = _scales(k_cache, k_scale, v_scale, layout)
+        keep.append(sc)
+        o.scales = ctypes.pointer(sc)
+    if rope is not None:
+        r = rope.struct()
+        keep.append(r)
+        o.rope = ctypes.pointer(r)
+    return desc, o, keep
+
+
+def workspace_size_ex(desc: Desc, opts: OptsT) -> int:
+    n = ctypes.c_size_t(0)
+    check(lib().gqa_decode_workspace_size_ex(ctypes.byref(desc), ctypes.byref(opts), ctypes.byref(n)),
+          "gqa_decode_workspace_size_ex")
+    return n.value
+
+
+def _workspace_ex(desc, opts, dev, workspace):
+    need = workspace_size_ex(desc, opts)
+    if need == 0:
+        return workspace, None, 0
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    return workspace, workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def append_ex(k_cache, v_cache, k_new, v_new, lengths, *, layout="BHSD", table=None, kind=None, table_host=None,
+              k_scale=None, v_scale=None, rope=None, qo_dtype=None):
+    """In-place append with options (map, int8 scales, rotary encoding of the key).
+    For int8 caches the new rows are activations (float32 or bfloat16)."""
+    tens = [k_cache, v_cache, k_new, v_new] + ([k_scale, v_scale] if k_scale is not None else [])
+    dev = _dev(tens, lengths)
+    B, Hkv, D = k_new.shape
+    kv = _dtype_code(k_cache.dtype)
+    qo = _dtype_code(k_new.dtype) if kv == I8 else (kv if qo_dtype is None else _dtype_code(qo_dtype))
+    desc, o, keep = _opts((B, Hkv, D, kv, qo, 0, Hkv), table=table, kind=kind, table_host=table_host,
+                          k_scale=k_scale, v_scale=v_scale, k_cache=k_cache, layout=layout, rope=rope)
+    check(lib().gqa_decode_append_ex(ctypes.byref(desc), ctypes.byref(o), k_cache.data_ptr(), v_cache.data_ptr(),
+                                     k_new.data_ptr(), v_new.data_ptr(), lengths.data_ptr(), _stream(dev)),
+          "gqa_decode_append_ex")
+    del keep
+
+
+def attend_ex(q, k_cache, v_cache, lengths, *, layout="BHSD", table=None, kind=None, table_host=None, k_scale=None,
+              v_scale=None, out=None, workspace=None, num_splits=0):
+    """Read-only attention with options (map, int8 scales)."""
+    tens = [q, k_cache, v_cache] + ([k_scale, v_scale] if k_scale is not None else [])
+    dev = _dev(tens, lengths)
+    B, Hq, D = q.shape
+    desc, o, keep = _opts((B, Hq, D, _dtype_code(k_cache.dtype), _dtype_code(q.dtype), num_splits, None),
+                          table=table, kind=kind, table_host=table_host, k_scale=k_scale, v_scale=v_scale,
+                          k_cache=k_cache, layout=layout)
+    if out is None:
+        out = torch.empty_like(q)
+    workspace, wptr, wbytes = _workspace_ex(desc, o, dev, workspace)
+    check(lib().gqa_decode_attend_ex(ctypes.byref(desc), ctypes.byref(o), q.data_ptr(), k_cache.data_ptr(),
+                                     v_cache.data_ptr(), lengths.data_ptr(), out.data_ptr(), wptr, wbytes,
+                                     _stream(dev)), "gqa_decode_attend_ex")
+    del keep
+    return out
+
+
+def step_ex(q, k_cache, v_cache, k_new, v_new, lengths, *, layout="BHSD", table=None, kind=None, table_host=None,
+            k_scale=None, v_scale=None, rope=None, out=None, workspace=None, num_splits=0):
+    """Decode step with options (map, int8 scales, rotary encoding). Returns out."""
+    tens = [q, k_cache, v_cache, k_new, v_new] + ([k_scale, v_scale] if k_scale is not None else [])
+    dev = _dev(tens, lengths)
+    B, Hq, D = q.shape
+    desc, o, keep = _opts((B, Hq, D, _dtype_code(k_cache.dtype), _dtype_code(q.dtype), num_splits, None),
+                          table=table, kind=kind, table_host=table_host, k_scale=k_scale, v_scale=v_scale,
+                          k_cache=k_cache, layout=layout, rope=rope)
+    if out is None:
+        out = torch.empty_like(q)
+    workspace, wptr, wbytes = _workspace_ex(desc, o, dev, workspace)
+    check(lib().gqa_decode_step_ex(ctypes.byref(desc), ctypes.byref(o), q.data_ptr(), k_cache.data_ptr(),
+                                   v_cache.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), lengths.data_ptr(),
+                                   out.data_ptr(), wptr, wbytes, _stream(dev)), "gqa_decode_step_ex")
+    del keep
     return out

@@ -380,12 +380,63 @@ gqa_status_t check_scale_ptrs(const gqa_decode_desc_t* d, const gqa_kv_scales_t*
   return GQA_OK;
 }
 
-gqa_status_t do_append(const gqa_decode_desc_t* desc, const gqa_cache_map_t* map, const gqa_kv_scales_t* sc,
-                       void* k_cache, void* v_cache, const void* k_new, const void* v_new, const int32_t* lengths,
-                       void* stream) {
+// Rotary encoding: the descriptor-level rules (before the batch-0 early
+// return), then the pointers (tables, positions, gains: read-only inputs that
+// must not overlap anything the call writes, `written`).
+gqa_status_t check_rope(const gqa_decode_desc_t* d, const gqa_rope_t* r) {
+  if (r == nullptr) return GQA_OK;
+  if (d->head_dim % 2 != 0 || r->max_pos < 1) return GQA_ERR_INVALID_ARGUMENT;
+  if (r->mode != GQA_ROPE_HALF && r->mode != GQA_ROPE_INTERLEAVED) return GQA_ERR_INVALID_ARGUMENT;
+  const bool gains = r->q_norm_gain != nullptr || r->k_norm_gain != nullptr;
+  const bool eps = r->norm_eps >= 0.f && std::isfinite(r->norm_eps);
+  if (gains != eps) return GQA_ERR_INVALID_ARGUMENT;
+  if (gains && d->kv_dtype == GQA_I8) return GQA_ERR_UNSUPPORTED;
+  int64_t t;
+  if (!mul_ok(r->max_pos, d->head_dim, &t) || !mul_ok(t, 2, &t)) return GQA_ERR_UNSUPPORTED;
+  return GQA_OK;
+}
+gqa_status_t check_rope_ptrs(const gqa_decode_desc_t* d, const gqa_rope_t* r, std::initializer_list<Span> written) {
+  if (r == nullptr) return GQA_OK;
+  if (!r->cos || !r->sin || !aligned(r->cos, 4) || !aligned(r->sin, 4)) return GQA_ERR_INVALID_ARGUMENT;
+  if (!aligned(r->positions, 4) || !aligned(r->q_norm_gain, 4) || !aligned(r->k_norm_gain, 4))
+    return GQA_ERR_INVALID_ARGUMENT;
+  const size_t tb = (size_t)r->max_pos * (d->head_dim / 2) * 4, gb = (size_t)d->head_dim * 4;
+  const Span in[] = {span(r->cos, tb), span(r->sin, tb), span(r->positions, r->positions ? d->batch * 4 : 0),
+                     span(r->q_norm_gain, r->q_norm_gain ? gb : 0), span(r->k_norm_gain, r->k_norm_gain ? gb : 0)};
+  for (const Span& w : written)
+    for (const Span& x : in)
+      if (overlap(w, x)) return GQA_ERR_INVALID_ARGUMENT;
+  return GQA_OK;
+}
+void fill_rope(const gqa_rope_t* r, AttnArgs* a) {
+  a->rope_cos = r->cos;
+  a->rope_sin = r->sin;
+  a->rope_pos = r->positions;
+  a->q_gain = r->q_norm_gain;
+  a->k_gain = r->k_norm_gain;
+  a->rope_max_pos = r->max_pos;
+  a->rope_mode = r->mode;
+  a->norm_eps = r->norm_eps;
+}
+
+const gqa_decode_opts_t kNoOpts = {nullptr, nullptr, nullptr};
+
+// Bytes of the rotated q a rotary step keeps after the plan's workspace.
+size_t rope_q_offset(const Plan& p) { return align256(p.workspace_bytes); }
+size_t workspace_total(const gqa_decode_desc_t* d, const Plan& p, const gqa_decode_opts_t* o) {
+  if (o->rope == nullptr) return p.workspace_bytes;
+  return rope_q_offset(p) + (size_t)d->batch * d->num_q_heads * d->head_dim * elem_bytes(d->qo_dtype);
+}
+
+gqa_status_t do_append(const gqa_decode_desc_t* desc, const gqa_decode_opts_t* opts, void* k_cache, void* v_cache,
+                       const void* k_new, const void* v_new, const int32_t* lengths, void* stream) {
   gqa_status_t st = check_desc(desc);
   if (st != GQA_OK) return st;
+  const gqa_decode_opts_t* o = opts ? opts : &kNoOpts;
+  const gqa_cache_map_t* map = o->map;
+  const gqa_kv_scales_t* sc = o->scales;
   if ((st = check_scales(desc, sc, map)) != GQA_OK) return st;
+  if ((st = check_rope(desc, o->rope)) != GQA_OK) return st;
   Plan p;
   std::memset(&p, 0, sizeof(p));
   p.kernel = GQA_KERNEL_GENERIC;  // the append kernel takes any block size
@@ -408,6 +459,11 @@ gqa_status_t do_append(const gqa_decode_desc_t* desc, const gqa_cache_map_t* map
       overlap(s_map, s_vc))
     return GQA_ERR_INVALID_ARGUMENT;
   if ((st = check_scale_ptrs(desc, sc, {s_kc, s_vc, s_kn, s_vn, s_len})) != GQA_OK) return st;
+  const size_t sb = sc ? B * Hkv * desc->capacity * 4 : 0;
+  if ((st = check_rope_ptrs(desc, o->rope,
+                            {s_kc, s_vc, span(sc ? sc->k_scale : nullptr, sb), span(sc ? sc->v_scale : nullptr, sb)})) !=
+      GQA_OK)
+    return st;
   AttnArgs a;
   fill_args(desc, p, &a);
   fill_map(desc, map, &a);
@@ -417,35 +473,56 @@ gqa_status_t do_append(const gqa_decode_desc_t* desc, const gqa_cache_map_t* map
   if (sc != nullptr) {
     a.k_scale_w = sc->k_scale;
     a.v_scale_w = sc->v_scale;
-    if (launch_append_q8(a, k_cache, v_cache, (hipStream_t)stream) != hipSuccess) return GQA_ERR_HIP;
-    return GQA_OK;
   }
-  if (launch_append(a, k_cache, v_cache, (hipStream_t)stream) != hipSuccess) return GQA_ERR_HIP;
-  return GQA_OK;
+  hipError_t e2;
+  if (o->rope != nullptr) {
+    fill_rope(o->rope, &a);
+    e2 = launch_rope_append(a, k_cache, v_cache, (hipStream_t)stream);
+  } else if (sc != nullptr) {
+    e2 = launch_append_q8(a, k_cache, v_cache, (hipStream_t)stream);
+  } else {
+    e2 = launch_append(a, k_cache, v_cache, (hipStream_t)stream);
+  }
+  return e2 == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 
-// Attend (step == false) or fused step (step == true), dense or mapped.
-gqa_status_t do_attend(const gqa_decode_desc_t* desc, const gqa_cache_map_t* map, const gqa_kv_scales_t* sc,
-                       const void* q, void* k_cache, void* v_cache, const void* k_new, const void* v_new,
-                       const int32_t* lengths, void* out, void* workspace, size_t workspace_bytes, void* stream,
-                       bool step) {
+// Attend (step == false) or fused step (step == true), with options.
+gqa_status_t do_attend(const gqa_decode_desc_t* desc, const gqa_decode_opts_t* opts, const void* q, void* k_cache,
+                       void* v_cache, const void* k_new, const void* v_new, const int32_t* lengths, void* out,
+                       void* workspace, size_t workspace_bytes, void* stream, bool step) {
   Plan p;
   gqa_status_t st = make_plan(desc, &p);
   if (st != GQA_OK) return st;
+  const gqa_decode_opts_t* o = opts ? opts : &kNoOpts;
+  const gqa_cache_map_t* map = o->map;
+  const gqa_kv_scales_t* sc = o->scales;
+  const gqa_rope_t* rope = o->rope;
   if ((st = check_scales(desc, sc, map)) != GQA_OK) return st;
+  if (rope != nullptr && !step) return GQA_ERR_INVALID_ARGUMENT;  // rotation belongs to the append
+  if ((st = check_rope(desc, rope)) != GQA_OK) return st;
   if (map != nullptr && (st = check_map(desc, map, p)) != GQA_OK) return st;
   if (desc->batch == 0) return GQA_OK;
-  st = check_attend_ptrs(desc, map, p, q, k_cache, v_cache, step ? k_new : nullptr, step ? v_new : nullptr,
+  Plan pw = p;  // the plan with the whole workspace the call needs (rotated q after the partials)
+  pw.workspace_bytes = workspace_total(desc, p, o);
+  st = check_attend_ptrs(desc, map, pw, q, k_cache, v_cache, step ? k_new : nullptr, step ? v_new : nullptr,
                          lengths, out, workspace, workspace_bytes, step);
   if (st != GQA_OK) return st;
+  const size_t B = desc->batch, Hq = desc->num_q_heads, Hkv = desc->num_kv_heads, D = desc->head_dim;
+  const size_t eqo = elem_bytes(desc->qo_dtype), ce = cache_elems(desc, map) * elem_bytes(desc->kv_dtype);
   if (sc != nullptr) {
-    const size_t B = desc->batch, Hq = desc->num_q_heads, Hkv = desc->num_kv_heads, D = desc->head_dim;
-    const size_t eqo = elem_bytes(desc->qo_dtype), ce = cache_elems(desc, map);
     st = check_scale_ptrs(desc, sc,
                           {span(q, B * Hq * D * eqo), span(out, B * Hq * D * eqo), span(k_cache, ce),
-                           span(v_cache, ce), span(lengths, B * 4), span(workspace, p.workspace_bytes),
+                           span(v_cache, ce), span(lengths, B * 4), span(workspace, pw.workspace_bytes),
                            span(step ? k_new : nullptr, step ? B * Hkv * D * eqo : 0),
                            span(step ? v_new : nullptr, step ? B * Hkv * D * eqo : 0)});
+    if (st != GQA_OK) return st;
+  }
+  if (rope != nullptr) {
+    const size_t sb = sc ? B * Hkv * desc->capacity * 4 : 0;
+    st = check_rope_ptrs(desc, rope,
+                         {span(out, B * Hq * D * eqo), span(k_cache, ce), span(v_cache, ce),
+                          span(workspace, pw.workspace_bytes), span(sc ? sc->k_scale : nullptr, sb),
+                          span(sc ? sc->v_scale : nullptr, sb)});
     if (st != GQA_OK) return st;
   }
   AttnArgs a;
@@ -470,7 +547,21 @@ gqa_status_t do_attend(const gqa_decode_desc_t* desc, const gqa_cache_map_t* map
   if (step) {
     a.k_new = k_new;
     a.v_new = v_new;
-    if (sc != nullptr) {
+    if (rope != nullptr) {
+      // Rotary step: the rope append kernel writes the rotated key (quantized
+      // for int8 caches) and the value at slot lengths[b] and the rotated q
+      // into the workspace; attention over lengths[b] + 1 slots then reads it.
+      if (sc != nullptr) {
+        a.k_scale_w = sc->k_scale;
+        a.v_scale_w = sc->v_scale;
+      }
+      fill_rope(rope, &a);
+      a.q_rot = static_cast<char*>(workspace) + rope_q_offset(p);
+      if (launch_rope_append(a, k_cache, v_cache, (hipStream_t)stream) != hipSuccess) return GQA_ERR_HIP;
+      a.q = a.q_rot;
+      a.k_new = nullptr;
+      a.v_new = nullptr;
+    } else if (sc != nullptr) {
       // Int8 caches: the quantizing append, then attention over lengths[b] + 1
       // slots (the new token is attended in its stored, quantized form).
       a.k_scale_w = sc->k_scale;
@@ -502,7 +593,7 @@ extern "C" {
 gqa_status_t gqa_decode_append(const gqa_decode_desc_t* desc, void* k_cache, void* v_cache, const void* k_new,
                                const void* v_new, const int32_t* lengths, void* stream) {
   try {
-    return do_append(desc, nullptr, nullptr, k_cache, v_cache, k_new, v_new, lengths, stream);
+    return do_append(desc, nullptr, k_cache, v_cache, k_new, v_new, lengths, stream);
   } catch (...) {
     return GQA_ERR_INTERNAL;
   }
@@ -512,8 +603,8 @@ gqa_status_t gqa_decode_attend(const gqa_decode_desc_t* desc, const void* q, con
                                const void* v_cache, const int32_t* lengths, void* out, void* workspace,
                                size_t workspace_bytes, void* stream) {
   try {
-    return do_attend(desc, nullptr, nullptr, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache), nullptr,
-                     nullptr, lengths, out, workspace, workspace_bytes, stream, false);
+    return do_attend(desc, nullptr, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache), nullptr, nullptr,
+                     lengths, out, workspace, workspace_bytes, stream, false);
   } catch (...) {
     return GQA_ERR_INTERNAL;
   }
@@ -523,8 +614,8 @@ gqa_status_t gqa_decode_step(const gqa_decode_desc_t* desc, const void* q, void*
                              const void* k_new, const void* v_new, const int32_t* lengths, void* out,
                              void* workspace, size_t workspace_bytes, void* stream) {
   try {
-    return do_attend(desc, nullptr, nullptr, q, k_cache, v_cache, k_new, v_new, lengths, out, workspace,
-                     workspace_bytes, stream, true);
+    return do_attend(desc, nullptr, q, k_cache, v_cache, k_new, v_new, lengths, out, workspace, workspace_bytes,
+                     stream, true);
   } catch (...) {
     return GQA_ERR_INTERNAL;
   }
@@ -535,7 +626,8 @@ gqa_status_t gqa_decode_append_mapped(const gqa_decode_desc_t* desc, const gqa_c
                                       const int32_t* lengths, void* stream) {
   try {
     if (map == nullptr) return GQA_ERR_INVALID_ARGUMENT;
-    return do_append(desc, map, nullptr, k_cache, v_cache, k_new, v_new, lengths, stream);
+    const gqa_decode_opts_t o = {map, nullptr, nullptr};
+    return do_append(desc, &o, k_cache, v_cache, k_new, v_new, lengths, stream);
   } catch (...) {
     return GQA_ERR_INTERNAL;
   }
@@ -546,8 +638,9 @@ gqa_status_t gqa_decode_attend_mapped(const gqa_decode_desc_t* desc, const gqa_c
                                       void* workspace, size_t workspace_bytes, void* stream) {
   try {
     if (map == nullptr) return GQA_ERR_INVALID_ARGUMENT;
-    return do_attend(desc, map, nullptr, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache), nullptr,
-                     nullptr, lengths, out, workspace, workspace_bytes, stream, false);
+    const gqa_decode_opts_t o = {map, nullptr, nullptr};
+    return do_attend(desc, &o, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache), nullptr, nullptr, lengths,
+                     out, workspace, workspace_bytes, stream, false);
   } catch (...) {
     return GQA_ERR_INTERNAL;
   }
@@ -559,8 +652,9 @@ gqa_status_t gqa_decode_step_mapped(const gqa_decode_desc_t* desc, const gqa_cac
                                     void* stream) {
   try {
     if (map == nullptr) return GQA_ERR_INVALID_ARGUMENT;
-    return do_attend(desc, map, nullptr, q, k_cache, v_cache, k_new, v_new, lengths, out, workspace,
-                     workspace_bytes, stream, true);
+    const gqa_decode_opts_t o = {map, nullptr, nullptr};
+    return do_attend(desc, &o, q, k_cache, v_cache, k_new, v_new, lengths, out, workspace, workspace_bytes, stream,
+                     true);
   } catch (...) {
     return GQA_ERR_INTERNAL;
   }
@@ -571,7 +665,8 @@ gqa_status_t gqa_decode_append_q8(const gqa_decode_desc_t* desc, const gqa_kv_sc
                                   void* stream) {
   try {
     if (scales == nullptr) return GQA_ERR_INVALID_ARGUMENT;
-    return do_append(desc, nullptr, scales, k_cache, v_cache, k_new, v_new, lengths, stream);
+    const gqa_decode_opts_t o = {nullptr, scales, nullptr};
+    return do_append(desc, &o, k_cache, v_cache, k_new, v_new, lengths, stream);
   } catch (...) {
     return GQA_ERR_INTERNAL;
   }
@@ -582,8 +677,9 @@ gqa_status_t gqa_decode_attend_q8(const gqa_decode_desc_t* desc, const gqa_kv_sc
                                   void* workspace, size_t workspace_bytes, void* stream) {
   try {
     if (scales == nullptr) return GQA_ERR_INVALID_ARGUMENT;
-    return do_attend(desc, nullptr, scales, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache), nullptr,
-                     nullptr, lengths, out, workspace, workspace_bytes, stream, false);
+    const gqa_decode_opts_t o = {nullptr, scales, nullptr};
+    return do_attend(desc, &o, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache), nullptr, nullptr, lengths,
+                     out, workspace, workspace_bytes, stream, false);
   } catch (...) {
     return GQA_ERR_INTERNAL;
   }
@@ -595,8 +691,58 @@ gqa_status_t gqa_decode_step_q8(const gqa_decode_desc_t* desc, const gqa_kv_scal
                                 void* stream) {
   try {
     if (scales == nullptr) return GQA_ERR_INVALID_ARGUMENT;
-    return do_attend(desc, nullptr, scales, q, k_cache, v_cache, k_new, v_new, lengths, out, workspace,
-                     workspace_bytes, stream, true);
+    const gqa_decode_opts_t o = {nullptr, scales, nullptr};
+    return do_attend(desc, &o, q, k_cache, v_cache, k_new, v_new, lengths, out, workspace, workspace_bytes, stream,
+                     true);
+  } catch (...) {
+    return GQA_ERR_INTERNAL;
+  }
+}
+
+gqa_status_t gqa_decode_workspace_size_ex(const gqa_decode_desc_t* desc, const gqa_decode_opts_t* opts,
+                                          size_t* bytes) {
+  try {
+    if (bytes == nullptr) return GQA_ERR_INVALID_ARGUMENT;
+    Plan p;
+    gqa_status_t st = make_plan(desc, &p);
+    if (st != GQA_OK) return st;
+    const gqa_decode_opts_t* o = opts ? opts : &kNoOpts;
+    if ((st = check_rope(desc, o->rope)) != GQA_OK) return st;
+    *bytes = workspace_total(desc, p, o);
+    return GQA_OK;
+  } catch (...) {
+    return GQA_ERR_INTERNAL;
+  }
+}
+
+gqa_status_t gqa_decode_append_ex(const gqa_decode_desc_t* desc, const gqa_decode_opts_t* opts, void* k_cache,
+                                  void* v_cache, const void* k_new, const void* v_new, const int32_t* lengths,
+                                  void* stream) {
+  try {
+    return do_append(desc, opts, k_cache, v_cache, k_new, v_new, lengths, stream);
+  } catch (...) {
+    return GQA_ERR_INTERNAL;
+  }
+}
+
+gqa_status_t gqa_decode_attend_ex(const gqa_decode_desc_t* desc, const gqa_decode_opts_t* opts, const void* q,
+                                  const void* k_cache, const void* v_cache, const int32_t* lengths, void* out,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    return do_attend(desc, opts, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache), nullptr, nullptr,
+                     lengths, out, workspace, workspace_bytes, stream, false);
+  } catch (...) {
+    return GQA_ERR_INTERNAL;
+  }
+}
+
+gqa_status_t gqa_decode_step_ex(const gqa_decode_desc_t* desc, const gqa_decode_opts_t* opts, const void* q,
+                                void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                                const int32_t* lengths, void* out, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  try {
+    return do_attend(desc, opts, q, k_cache, v_cache, k_new, v_new, lengths, out, workspace, workspace_bytes,
+                     stream, true);
   } catch (...) {
     return GQA_ERR_INTERNAL;
   }

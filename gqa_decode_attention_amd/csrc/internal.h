@@ -36,6 +36,17 @@ struct AttnArgs {
   const float* v_scale;
   float* k_scale_w;
   float* v_scale_w;
+  // Rotary encoding (the rope append kernel): float32 (max_pos, D/2) tables,
+  // the new token's position per sequence (null: lengths[b]), optional norm
+  // gains, and the rotated q it writes (qo_dtype, (B, Hq, D)).
+  const float* rope_cos;
+  const float* rope_sin;
+  const int32_t* rope_pos;
+  const float* q_gain;
+  const float* k_gain;
+  void* q_rot;
+  int32_t rope_max_pos, rope_mode;
+  float norm_eps;
   int32_t nsplit, split_tokens;
   int32_t head_chunks;   // generic kernel: query-head chunks per kv-head
   int32_t len_offset;    // slots attended = lengths[b] + len_offset (1 for a step, 0 for attend)
@@ -61,12 +72,16 @@ extern const bool kHaveMfmaQk;
 extern const bool kHaveMfmaAll;
 extern const bool kHaveMfmaQkI8;  // int8 caches on the G <= 16 matrix-core kernel
 
-constexpr int kNumCUs = 256;
-constexpr int kMaxSplits = 64;        // one lane per split in the combine pass          // MI355X: 8 XCDs x 32 CUs
+constexpr int kNumCUs = 256;          // MI355X: 8 XCDs x 32 CUs
+constexpr int kMaxSplits = 64;        // one lane per split in the combine pass
 constexpr int kGenericHeadChunk = 8;  // query heads per workgroup in the generic kernel
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_append(const AttnArgs& a, void* k_cache, void* v_cache, hipStream_t s);
+// Rotary append: rotates (and normalizes) the new key, writes it and the value
+// at slot lengths[b] (int8 caches: quantized), and, when a.q_rot is set, the
+// rotated (and normalized) q into a.q_rot.
+hipError_t launch_rope_append(const AttnArgs& a, void* k_cache, void* v_cache, hipStream_t s);
 // Quantizing append into int8 caches (new K/V in a.qo_dtype).
 hipError_t launch_append_q8(const AttnArgs& a, void* k_cache, void* v_cache, hipStream_t s);
 hipError_t launch_attend_generic(const AttnArgs& a, const Plan& p, int vec_path, hipStream_t s);

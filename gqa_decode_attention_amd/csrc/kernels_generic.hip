@@ -62,10 +62,25 @@ hipError_t launch_append(const AttnArgs& a, void* k_cache, void* v_cache, hipStr
 // scale = max|x| / 127 and codes round-half-even(x / scale), with correctly
 // rounded float32 divisions; a zero row stores scale 0 and codes 0.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float wave_max64(float x) {
+
+// One row held as elements d = lane + 64 i (i < 4, d < D) of a wave, quantized
+// into int8 codes at dst[off + d] and its scale at sdst[off / D].
+__device__ __forceinline__ void store_q8_row(const float (&x)[4], int lane, int D, int8_t* dst, float* sdst,
+                                             int64_t off) {
+  float amax = 0.f;
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-  return x;
+  for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(x[i]));  // lanes past D hold 0
+  amax = wave_max(amax);
+  const float scale = amax / 127.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int d = lane + 64 * i;
+    if (d < D) {
+      const float c = amax > 0.f ? fminf(fmaxf(rintf(x[i] / scale), -127.f), 127.f) : 0.f;
+      dst[off + d] = (int8_t)(int32_t)c;
+    }
+  }
+  if (lane == 0) sdst[off / D] = scale;
 }
 
 template <int NEW>
@@ -83,27 +98,13 @@ __global__ __launch_bounds__(256) void append_q8_kernel(AttnArgs a, int8_t* __re
 #pragma unroll
   for (int which = 0; which < 2; ++which) {
     const void* src = which ? a.v_new : a.k_new;
-    int8_t* dst = which ? vc : kc;
-    float* sdst = which ? a.v_scale_w : a.k_scale_w;
     float x[4];
-    float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int d = lane + 64 * i;
       x[i] = d < D ? Store<NEW>::load1_cached(src, row * D + d) : 0.f;
-      amax = fmaxf(amax, fabsf(x[i]));
     }
-    amax = wave_max64(amax);
-    const float scale = amax / 127.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d = lane + 64 * i;
-      if (d < D) {
-        const float c = amax > 0.f ? fminf(fmaxf(rintf(x[i] / scale), -127.f), 127.f) : 0.f;
-        dst[off + d] = (int8_t)(int32_t)c;
-      }
-    }
-    if (lane == 0) sdst[off / D] = scale;
+    store_q8_row(x, lane, D, which ? vc : kc, which ? a.v_scale_w : a.k_scale_w, off);
   }
 }
 
@@ -114,6 +115,143 @@ hipError_t launch_append_q8(const AttnArgs& a, void* k_cache, void* v_cache, hip
   const void* fn = a.qo_dtype == GQA_F32 ? reinterpret_cast<const void*>(&append_q8_kernel<GQA_F32>)
                                          : reinterpret_cast<const void*>(&append_q8_kernel<GQA_BF16>);
   return hipLaunchKernel(fn, dim3(blocks), dim3(256), params, 0, s);
+}
+
+// ---------------------------------------------------------------------------
+// Rotary append (CLIKA "groupQueryAttention" page: q and the new k rotated with
+// the rope planes, optional post-rotation RMS norm with gains, the rotated key
+// appended in place).  One workgroup per (b, kv-head); its 4 waves take rows
+// k, v, then the G query heads (rotated q is written only when a.q_rot is
+// set).  A row is held as elements d = lane + 64 i; the partner of a rotation
+// pair comes from another lane by a cross-lane read.  Products and sums are
+// rounded separately (no contraction), so the rotation is reproducible.  The
+// value row is a raw copy (int8 caches: quantized like the key).
+// ---------------------------------------------------------------------------
+// One element of a rotated pair: x1 c - x2 s for the first, x2 c + x1 s for the
+// second (x = this element, xp = its partner), each product and the sum
+// rounded separately: contraction into a fused multiply-add is off here.
+__device__ __forceinline__ float rope_pair(bool first, float x, float xp, float c, float s) {
+#pragma clang fp contract(off)
+  const float a = x * c;
+  const float b = xp * s;
+  return first ? a - b : a + b;
+}
+
+template <int KV, int QO>
+__global__ __launch_bounds__(256) void rope_append_kernel(AttnArgs a, void* __restrict__ kc, void* __restrict__ vc) {
+  constexpr int NEW = KV == GQA_I8 ? QO : KV;  // storage of k_new / v_new
+  const int bh = blockIdx.x;                   // b * Hkv + h
+  const int b = bh / a.Hkv;
+  const int h = bh - b * a.Hkv;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int D = a.D;
+  const int half = D >> 1;
+  const int L = a.lengths[b];
+  int p = a.rope_pos != nullptr ? a.rope_pos[b] : L;
+  p = min(max(p, 0), a.rope_max_pos - 1);      // memory-safe for out-of-contract positions
+  const float* cs = a.rope_cos + (int64_t)p * half;
+  const float* sn = a.rope_sin + (int64_t)p * half;
+  const int64_t off = (L >= 0 && L < a.S) ? slot_offset_checked(a, b, h, L) : -1;
+  const int nrows = 2 + (a.q_rot != nullptr ? a.G : 0);
+  for (int row = wave; row < nrows; row += 4) {  // uniform within a wave
+    const bool isv = row == 1;
+    const bool isq = row >= 2;
+    if (!isq && off < 0) continue;             // the map names no valid slot: nothing appended
+    const int64_t base = isq ? ((int64_t)b * a.Hq + (int64_t)h * a.G + (row - 2)) * D : (int64_t)bh * D;
+    if (isv && KV != GQA_I8) {
+      for (int d = lane; d < D; d += 64) {
+        if constexpr (KV == GQA_BF16)
+          reinterpret_cast<uint16_t*>(vc)[off + d] = reinterpret_cast<const uint16_t*>(a.v_new)[base + d];
+        else
+          reinterpret_cast<uint32_t*>(vc)[off + d] = reinterpret_cast<const uint32_t*>(a.v_new)[base + d];
+      }
+      continue;
+    }
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = lane + 64 * i;
+      x[i] = d >= D ? 0.f
+             : isq  ? Store<QO>::load1_cached(a.q, base + d)
+                    : Store<NEW>::load1_cached(isv ? a.v_new : a.k_new, base + d);
+    }
+    if (!isv) {
+      float y[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = lane + 64 * i;
+        bool first;
+        int dp, j;
+        if (a.rope_mode == GQA_ROPE_HALF) {
+          first = d < half;
+          dp = first ? d + half : d - half;
+          j = first ? d : d - half;
+        } else {
+          first = (d & 1) == 0;
+          dp = d ^ 1;
+          j = d >> 1;
+        }
+        float xp = 0.f;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const float t = __shfl(x[ii], dp & 63);
+          if ((dp >> 6) == ii) xp = t;
+        }
+        const bool in = d < D;
+        const float c = in ? cs[j] : 0.f;
+        const float sv = in ? sn[j] : 0.f;
+        y[i] = rope_pair(first, x[i], xp, c, sv);
+      }
+      const float* gain = isq ? a.q_gain : a.k_gain;
+      if (gain != nullptr) {
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ss += y[i] * y[i];  // lanes past D hold 0
+        ss = wave_sum(ss);
+        const float r = 1.0f / sqrtf(ss / (float)D + a.norm_eps);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d = lane + 64 * i;
+          y[i] = d < D ? (y[i] * r) * gain[d] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = y[i];
+    }
+    if (isq) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = lane + 64 * i;
+        if (d < D) Store<QO>::store1(a.q_rot, base + d, x[i]);
+      }
+    } else if constexpr (KV == GQA_I8) {
+      store_q8_row(x, lane, D, reinterpret_cast<int8_t*>(isv ? vc : kc), isv ? a.v_scale_w : a.k_scale_w, off);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = lane + 64 * i;
+        if (d < D) Store<KV>::store1(kc, off + d, x[i]);
+      }
+    }
+  }
+}
+
+hipError_t launch_rope_append(const AttnArgs& a, void* k_cache, void* v_cache, hipStream_t s) {
+  AttnArgs arg = a;
+  void* params[] = {&arg, &k_cache, &v_cache};
+  const void* fn;
+  const bool f32 = a.qo_dtype == GQA_F32;
+  if (a.kv_dtype == GQA_I8)
+    fn = f32 ? reinterpret_cast<const void*>(&rope_append_kernel<GQA_I8, GQA_F32>)
+             : reinterpret_cast<const void*>(&rope_append_kernel<GQA_I8, GQA_BF16>);
+  else if (a.kv_dtype == GQA_BF16)
+    fn = f32 ? reinterpret_cast<const void*>(&rope_append_kernel<GQA_BF16, GQA_F32>)
+             : reinterpret_cast<const void*>(&rope_append_kernel<GQA_BF16, GQA_BF16>);
+  else
+    fn = f32 ? reinterpret_cast<const void*>(&rope_append_kernel<GQA_F32, GQA_F32>)
+             : reinterpret_cast<const void*>(&rope_append_kernel<GQA_F32, GQA_BF16>);
+  return hipLaunchKernel(fn, dim3((unsigned)((int64_t)a.B * a.Hkv)), dim3(256), params, 0, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -348,16 +486,6 @@ hipError_t launch_attend_generic(const AttnArgs& a, const Plan& p, int vec_path,
 // each lane then sums up to four output columns over the active splits with
 // independent loads.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-  return x;
-}
 
 template <int QO>
 __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {

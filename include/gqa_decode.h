@@ -107,8 +107,8 @@ typedef struct {
 
 enum {
   GQA_KERNEL_GENERIC = 0,  /* vector ALU, any D <= 256, f32 or bf16 storage                  */
-  GQA_KERNEL_MFMA_QK = 1,  /* bf16 (or int8 caches, bf16 q/out), D = 128, G <= 16: scores on
-                              MFMA, V sum on vector ALU                                       */
+  GQA_KERNEL_MFMA_QK = 1,  /* bf16 (or int8 caches, bf16 q/out), D = 128, G <= 16: scores and
+                              V sum on MFMA, 16 query heads per 16-slot tile                   */
   GQA_KERNEL_MFMA_ALL = 2  /* bf16, D = 128, 16 < G <= 64: scores and V sum on MFMA           */
 };
 
@@ -255,6 +255,76 @@ gqa_status_t gqa_decode_attend_q8(const gqa_decode_desc_t* desc, const gqa_kv_sc
                                   const void* k_cache, const void* v_cache, const int32_t* lengths, void* out,
                                   void* workspace, size_t workspace_bytes, void* stream);
 gqa_status_t gqa_decode_step_q8(const gqa_decode_desc_t* desc, const gqa_kv_scales_t* scales, const void* q,
+                                void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                                const int32_t* lengths, void* out, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Rotary position encoding fused into the append (CLIKA runtime,
+ * "groupQueryAttention" API page, operator summary: q and the new k are rotated
+ * with the rope planes and the post-rotation key is appended in place; optional
+ * per-head RMS norm gains applied after the rotation, before the append; the
+ * Huawei CANN "aclnnMlaPrologV3WeightNz" page rotates its query and key the
+ * same way and gives the RmsNorm formula, epsilon inside the square root).
+ *   cos, sin     : float32 (max_pos, D/2) tables in device memory; row p holds the
+ *                  angles of position p, column i the i-th rotation pair.
+ *   mode         : GQA_ROPE_HALF pairs elements (i, i + D/2); GQA_ROPE_INTERLEAVED
+ *                  pairs (2i, 2i + 1).  A pair (x1, x2) at position p becomes
+ *                  (x1 c - x2 s, x2 c + x1 s), c = cos[p][i], s = sin[p][i], in float32
+ *                  with each product and sum rounded separately (no fused
+ *                  multiply-add), so a stored key is a reproducible rounding.
+ *   positions    : int32 (B,) device, the new token's position per sequence, or NULL:
+ *                  position lengths[b] (its cache slot).  Contract: 0 <= p < max_pos
+ *                  (out-of-range positions are clamped into the table, memory-safe,
+ *                  outside the numerical contract).
+ *   q_norm_gain, k_norm_gain : float32 (D,) device, or NULL.  A gain normalizes the
+ *                  rotated vector of every head: x / sqrt(mean(x^2) + norm_eps) * gain.
+ *   norm_eps     : >= 0 when a gain is given; < 0 when neither is (a gain without
+ *                  an epsilon, or an epsilon without a gain, is GQA_ERR_INVALID_ARGUMENT).
+ * The step rotates q (every query head, at its sequence's position) and the new
+ * key, appends the rotated key and the unchanged value at slot lengths[b], and
+ * attends with the rotated q; the append alone rotates the key only.  The
+ * rotated q is kept in the workspace (gqa_decode_workspace_size_ex), rounded to
+ * qo_dtype.  D must be even.  Int8 caches take the rotation (the rotated key is
+ * then quantized) but not the norm gains (GQA_ERR_UNSUPPORTED).
+ * ------------------------------------------------------------------------- */
+enum { GQA_ROPE_HALF = 0, GQA_ROPE_INTERLEAVED = 1 };
+
+typedef struct {
+  const float* cos;
+  const float* sin;
+  int32_t max_pos;
+  int32_t mode;
+  const int32_t* positions;
+  const float* q_norm_gain;
+  const float* k_norm_gain;
+  float norm_eps;
+} gqa_rope_t;
+
+/* Options of the _ex calls; every member may be NULL (the plain behaviour).
+ *   map    : mapped caches, as in the _mapped calls
+ *   scales : int8 caches (desc->kv_dtype = GQA_I8), as in the _q8 calls; not
+ *            combined with map (GQA_ERR_UNSUPPORTED)
+ *   rope   : rotary encoding (append and step only) */
+typedef struct {
+  const gqa_cache_map_t* map;
+  const gqa_kv_scales_t* scales;
+  const gqa_rope_t* rope;
+} gqa_decode_opts_t;
+
+/* Workspace of an attend/step call with these options (the plain size plus the
+ * rotated q when opts->rope is set).  opts may be NULL. */
+gqa_status_t gqa_decode_workspace_size_ex(const gqa_decode_desc_t* desc, const gqa_decode_opts_t* opts,
+                                          size_t* bytes);
+/* The append, attend and step calls with options; arguments, contracts and
+ * errors as in the plain calls and the sections above.  opts may be NULL. */
+gqa_status_t gqa_decode_append_ex(const gqa_decode_desc_t* desc, const gqa_decode_opts_t* opts, void* k_cache,
+                                  void* v_cache, const void* k_new, const void* v_new, const int32_t* lengths,
+                                  void* stream);
+gqa_status_t gqa_decode_attend_ex(const gqa_decode_desc_t* desc, const gqa_decode_opts_t* opts, const void* q,
+                                  const void* k_cache, const void* v_cache, const int32_t* lengths, void* out,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+gqa_status_t gqa_decode_step_ex(const gqa_decode_desc_t* desc, const gqa_decode_opts_t* opts, const void* q,
                                 void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                                 const int32_t* lengths, void* out, void* workspace, size_t workspace_bytes,
                                 void* stream);

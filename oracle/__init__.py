@@ -35,5 +35,6 @@ from .rope import (  # noqa: F401
     rms_norm,
     rope_rotate,
     rotate_new,
+    step_q8_rope,
     step_rope,
 )

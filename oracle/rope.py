@@ -39,8 +39,9 @@ import numpy as np
 
 from .mapped import append_mapped, mapped_rows
 from .oracle import append, attend_one, decode, kv_rows
+from .quant import step_q8
 
-__all__ = ["rope_rotate", "rms_norm", "encode", "rotate_new", "step_rope"]
+__all__ = ["rope_rotate", "rms_norm", "encode", "rotate_new", "step_rope", "step_q8_rope"]
 
 MODES = ("half", "interleaved")
 
@@ -167,3 +168,27 @@ def step_rope(q, q_dtype: str, k_cache, v_cache, k_new, v_new, kv_dtype: str, le
             for hq in range(h * G, (h + 1) * G):
                 out[b, hq] = attend_one(qr[b, hq], K, V)
     return out, kc, vc
+
+
+def step_q8_rope(q, q_dtype: str, k_cache, v_cache, k_scale, v_scale, k_new, v_new, lengths, layout: str,
+                 num_q_heads: int, num_kv_heads: int, cos, sin, mode: str, positions=None):
+    """Int8 caches (``oracle.quant``): the new key is rotated in float32 as above
+    and then quantized by the per-row rule; q is rotated the same way and used
+    unrounded.  Returns (out, k_cache, v_cache, k_scale, v_scale) after the step."""
+    B, Hq, D = q.shape
+    cos, sin = _check_tables(cos, sin, D)
+    lengths = np.asarray(lengths)
+    pos = lengths if positions is None else np.asarray(positions)
+    if pos.shape != (B,) or np.any(pos < 0) or np.any(pos >= cos.shape[0]):
+        raise ValueError("positions index the tables")
+    q32 = decode(q, q_dtype).astype(np.float32)
+    k32 = decode(k_new, q_dtype).astype(np.float32)
+    qr = np.empty_like(q32)
+    kr = np.empty_like(k32)
+    for b in range(B):
+        p = int(pos[b])
+        qr[b] = rope_rotate(q32[b], cos[p], sin[p], mode)
+        kr[b] = rope_rotate(k32[b], cos[p], sin[p], mode)
+    vn = decode(v_new, q_dtype).astype(np.float32)            # exact
+    return step_q8(qr, "f32", k_cache, v_cache, k_scale, v_scale, kr, vn, lengths, layout, num_q_heads,
+                   num_kv_heads)

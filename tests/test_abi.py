@@ -456,3 +456,97 @@ def test_q8_empty_batch_is_a_noop_and_plans_int8():
     assert L.gqa_decode_append_q8(ctypes.byref(d), ctypes.byref(sc), None, None, None, None, None, None) == OK
     p = g.get_plan(desc(kv_dtype=g.I8))
     assert p["block"] == 256 and p["workspace_bytes"] == g.workspace_size(desc(kv_dtype=g.I8))
+
+
+# ---------------------------------------------------------------------------
+# Options (_ex calls) and rotary encoding: refusals before any launch.
+# ---------------------------------------------------------------------------
+def _rope(**kw):
+    base = dict(cos=FAKE + 11 * GAP, sin=FAKE + 12 * GAP, max_pos=4096, mode=0, positions=None, q_norm_gain=None,
+                k_norm_gain=None, norm_eps=-1.0)
+    base.update(kw)
+    return _lib.RopeT(base["cos"], base["sin"], base["max_pos"], base["mode"], base["positions"],
+                      base["q_norm_gain"], base["k_norm_gain"], base["norm_eps"])
+
+
+def _ex_calls(d, o, p=None):
+    L = g.lib()
+    p = p or _attend_ptrs()
+    op = ctypes.byref(o) if o is not None else None
+    return [
+        L.gqa_decode_step_ex(ctypes.byref(d), op, p["q"], p["kc"], p["vc"], p["kn"], p["vn"], p["lens"], p["out"],
+                             p["ws"], 1 << 30, None),
+        L.gqa_decode_append_ex(ctypes.byref(d), op, p["kc"], p["vc"], p["kn"], p["vn"], p["lens"], None),
+    ]
+
+
+BAD_ROPES = [
+    (dict(mode=2), INVALID),
+    (dict(max_pos=0), INVALID),
+    (dict(cos=0), INVALID),
+    (dict(sin=FAKE + 12 * GAP + 2), INVALID),                        # misaligned table
+    (dict(positions=FAKE + 13 * GAP + 1), INVALID),
+    (dict(q_norm_gain=FAKE + 13 * GAP), INVALID),                    # a gain without an epsilon
+    (dict(norm_eps=1e-6), INVALID),                                  # an epsilon without a gain
+    (dict(k_norm_gain=FAKE + 13 * GAP, norm_eps=float("nan")), INVALID),
+    (dict(cos=FAKE + GAP), INVALID),                                 # table inside the K cache (written)
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD_ROPES)
+def test_bad_rope_refused(kw, status):
+    r = _rope(**kw)
+    o = _lib.OptsT(None, None, ctypes.pointer(r))
+    assert _ex_calls(desc(), o) == [status, status]
+
+
+def test_rope_needs_even_head_dim_and_no_norm_on_int8():
+    r = _rope()
+    o = _lib.OptsT(None, None, ctypes.pointer(r))
+    assert _ex_calls(desc(head_dim=7, kv_dtype=g.F32, qo_dtype=g.F32), o) == [INVALID, INVALID]
+    sc = _scales()
+    r = _rope(k_norm_gain=FAKE + 13 * GAP, norm_eps=1e-6)
+    o = _lib.OptsT(None, ctypes.pointer(sc), ctypes.pointer(r))
+    assert _ex_calls(desc(kv_dtype=g.I8), o) == [UNSUPPORTED, UNSUPPORTED]
+
+
+def test_attend_refuses_rope_and_ex_matches_plain_refusals():
+    L = g.lib()
+    r = _rope()
+    o = _lib.OptsT(None, None, ctypes.pointer(r))
+    p = _attend_ptrs()
+    d = desc()
+    assert L.gqa_decode_attend_ex(ctypes.byref(d), ctypes.byref(o), p["q"], p["kc"], p["vc"], p["lens"], p["out"],
+                                  p["ws"], 1 << 30, None) == INVALID
+    # NULL options = the plain calls: int8 without scales, bad descriptors
+    assert _ex_calls(desc(kv_dtype=g.I8), None) == [INVALID, INVALID]
+    assert _ex_calls(desc(num_q_heads=6, num_kv_heads=4), None) == [INVALID, INVALID]
+
+
+def test_workspace_size_ex_adds_the_rotated_q():
+    L = g.lib()
+    for kw in (dict(), dict(batch=32, num_q_heads=32, num_kv_heads=8, capacity=131073),
+               dict(kv_dtype=g.F32, qo_dtype=g.F32, head_dim=64)):
+        d = desc(**kw)
+        plain = g.workspace_size(d)
+        n = ctypes.c_size_t(0)
+        assert L.gqa_decode_workspace_size_ex(ctypes.byref(d), None, ctypes.byref(n)) == OK and n.value == plain
+        r = _rope()
+        o = _lib.OptsT(None, None, ctypes.pointer(r))
+        assert L.gqa_decode_workspace_size_ex(ctypes.byref(d), ctypes.byref(o), ctypes.byref(n)) == OK
+        eqo = 4 if d.qo_dtype == g.F32 else 2
+        assert n.value == -(-plain // 256) * 256 + d.batch * d.num_q_heads * d.head_dim * eqo
+        # a workspace one byte short of that is refused
+        p = _attend_ptrs()
+        assert L.gqa_decode_step_ex(ctypes.byref(d), ctypes.byref(o), p["q"], p["kc"], p["vc"], p["kn"], p["vn"],
+                                    p["lens"], p["out"], p["ws"], n.value - 1, None) == WS_SMALL
+
+
+def test_ex_empty_batch_is_a_noop():
+    L = g.lib()
+    d = desc(batch=0)
+    r = _rope()
+    o = _lib.OptsT(None, None, ctypes.pointer(r))
+    assert L.gqa_decode_step_ex(ctypes.byref(d), ctypes.byref(o), None, None, None, None, None, None, None, None, 0,
+                                None) == OK
+    assert L.gqa_decode_append_ex(ctypes.byref(d), ctypes.byref(o), None, None, None, None, None, None) == OK

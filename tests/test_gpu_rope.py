@@ -1,0 +1,183 @@
+"""GPU parity for the decode step with rotary encoding fused into the append
+(CLIKA runtime "groupQueryAttention" API page: q and the new key rotated with
+the rope planes, optional post-rotation RMS norm gains, the rotated key
+appended in place).
+
+The library's step_ex / append_ex with a Rope against the oracle on the same
+stored bits: outputs within the dense tolerances (fp32 2e-5, bf16 1e-2, abs +
+rel); the appended key byte-exact when no norm is applied (the rotation is
+specified operation by operation in float32, then rounded once), within one
+unit in the last place of the storage type with a norm (its mean square is a
+float32 reduction on the GPU, float64 in the oracle); values and every other
+cache byte exact; int8 caches: codes and scales exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 2e-5, "bf16": 1e-2}
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def g():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gqa_decode_attention_amd as lib
+    lib.lib()
+    return lib
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def np_of(t):
+    return W.to_numpy_storage(t)
+
+
+def assert_close(out_gpu, ref, qo_dtype, what=""):
+    got = out_gpu.detach().float().cpu().double().numpy()
+    tol = TOL[qo_dtype]
+    err = np.abs(got - ref)
+    bound = tol + tol * np.abs(ref)
+    bad = ~(err <= bound)
+    assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} outside tolerance; worst excess "
+                           f"{np.max(err - bound):.3g} at {np.unravel_index(np.argmax(err - bound), err.shape)}")
+
+
+def appended_rows(cache, layout, L, kind=None, table=None, bs=None):
+    """The rows at slot L[b] of every (b, kv-head), shape (B, Hkv, D)."""
+    B = len(L)
+    Hkv = cache.shape[1] if layout == "BHSD" else cache.shape[2]
+    rows = []
+    for b in range(B):
+        rows.append([cache[oracle.slot_location(kind, layout, table, b, h, int(L[b]), bs)] if kind
+                     else cache[oracle.kv_index(layout, b, h, int(L[b]))] for h in range(Hkv)])
+    return np.array(rows)
+
+
+def assert_key_rows(got_cache, want_cache, layout, L, kv, exact, kind=None, table=None, bs=None):
+    gk = appended_rows(got_cache, layout, L, kind, table, bs)
+    wk = appended_rows(want_cache, layout, L, kind, table, bs)
+    if exact:
+        assert gk.tobytes() == wk.tobytes(), "appended key differs"
+    else:
+        a, b = oracle.decode(gk, kv), oracle.decode(wk, kv)
+        ulp = 2.0 ** -7 if kv == "bf16" else 2.0 ** -20
+        assert np.all(np.abs(a - b) <= ulp * np.abs(b) + 1e-30), np.max(np.abs(a - b) / (np.abs(b) + 1e-30))
+    # every other byte of the cache is the oracle's (the appended rows replaced by the oracle's own)
+    g2 = got_cache.copy()
+    for b_, l_ in enumerate(L):
+        for h in range(gk.shape[1]):
+            idx = (oracle.slot_location(kind, layout, table, b_, h, int(l_), bs) if kind
+                   else oracle.kv_index(layout, b_, h, int(l_)))
+            g2[idx] = want_cache[idx]
+    assert g2.tobytes() == want_cache.tobytes(), "bytes outside the appended rows changed"
+
+
+CASES = [
+    # B, Hq, Hkv, D, S, layout, kv, qo, mode, positions, norm, kind
+    (3, 32, 8, 128, 700, "BHSD", "bf16", "bf16", "half", False, False, None),          # G=4 matrix-core
+    (2, 16, 2, 128, 500, "BSHD", "bf16", "bf16", "interleaved", True, False, None),    # G=8, given positions
+    (2, 64, 1, 128, 300, "BHSD", "bf16", "bf16", "half", False, True, None),           # G=64, norm gains
+    (3, 8, 2, 64, 200, "BHSD", "f32", "f32", "interleaved", False, False, None),       # generic f32
+    (2, 6, 3, 24, 90, "BSHD", "f32", "bf16", "half", True, True, None),                # odd G, D=24, norm
+    (2, 8, 2, 80, 100, "BHSD", "bf16", "f32", "half", False, False, None),             # D=80: cross-lane pairs
+    (2, 4, 1, 256, 64, "BHSD", "bf16", "bf16", "interleaved", False, False, None),     # D=256
+    (3, 32, 8, 128, 512, "BHSD", "bf16", "bf16", "half", False, False, "paged"),      # paged pool
+    (2, 16, 4, 128, 300, "BSHD", "bf16", "bf16", "interleaved", True, True, "slots"),  # slot rows, norm
+]
+
+
+def _ids(c):
+    return (f"B{c[0]}Hq{c[1]}Hkv{c[2]}D{c[3]}S{c[4]}{c[5]}{c[6]}{c[7]}-{c[8]}"
+            f"{'-pos' if c[9] else ''}{'-norm' if c[10] else ''}{'-' + c[11] if c[11] else ''}")
+
+
+@pytest.mark.parametrize("case", CASES, ids=[_ids(c) for c in CASES])
+def test_rope_step(g, case):
+    B, Hq, Hkv, D, S, layout, kv, qo, mode, given_pos, norm, kind = case
+    say(f"rope step {_ids(case)}")
+    w = W.custom(B, Hq, Hkv, D, S, layout, kv, qo, seed=B * 7 + D + Hq, stale="pm:1000")
+    L = torch.randint(0, S, (B,), generator=torch.Generator().manual_seed(S + 3), dtype=torch.int32)
+    L[0] = S - 1
+    if B > 2:
+        L[1] = 0
+    inp = W.make_inputs(w, DEV, lengths=L)
+    max_pos = S + 50
+    cos, sin = W.rope_tables(max_pos, D, DEV)
+    pos = None
+    if given_pos:
+        pos = torch.randint(0, max_pos, (B,), generator=torch.Generator().manual_seed(11), dtype=torch.int32)
+    gq = gk = eps = None
+    if norm:
+        gen = torch.Generator().manual_seed(5)
+        gq = (torch.rand(D, generator=gen) + 0.5).to(DEV)
+        gk = (torch.rand(D, generator=gen) + 0.5).to(DEV)
+        eps = 1e-5
+    rope = g.Rope(cos, sin, mode, positions=pos.to(DEV) if pos is not None else None, q_gain=gq, k_gain=gk, eps=eps)
+    kc, vc = inp["k_cache"], inp["v_cache"]
+    table = bs = None
+    if kind is not None:
+        m = W.make_mapped(inp, w, kind, block_size=16)
+        kc, vc, table = m["k_cache"], m["v_cache"], m["map"]
+        bs = m.get("block_size")
+    tab_np = table.cpu().numpy() if table is not None else None
+    ref, rk, rv = oracle.step_rope(np_of(inp["q"]), qo, np_of(kc), np_of(vc), np_of(inp["k_new"]),
+                                   np_of(inp["v_new"]), kv, L.numpy(), layout, Hq, Hkv, cos.cpu().numpy(),
+                                   sin.cpu().numpy(), mode, positions=None if pos is None else pos.numpy(),
+                                   q_gain=None if gq is None else gq.cpu().numpy(),
+                                   k_gain=None if gk is None else gk.cpu().numpy(), eps=eps, kind=kind,
+                                   mapping=tab_np, bs=bs)
+    out = g.step_ex(inp["q"], kc, vc, inp["k_new"], inp["v_new"], inp["lengths"], layout=layout, table=table,
+                    kind=kind, table_host=None if table is None else table.cpu(), rope=rope)
+    torch.cuda.synchronize()
+    assert_close(out, ref, qo, "step")
+    assert_key_rows(np_of(kc), rk, layout, L.numpy(), kv, exact=not norm, kind=kind, table=tab_np, bs=bs)
+    assert np_of(vc).tobytes() == rv.tobytes()
+
+
+@pytest.mark.parametrize("mode", ["half", "interleaved"])
+def test_rope_append_alone(g, mode):
+    w = W.custom(3, 8, 2, 64, 40, "BSHD", "bf16", "bf16", seed=31)
+    L = torch.tensor([0, 17, 39], dtype=torch.int32)
+    inp = W.make_inputs(w, DEV, lengths=L)
+    cos, sin = W.rope_tables(64, 64, DEV)
+    _, rk, rv = oracle.step_rope(np_of(inp["q"]), "bf16", np_of(inp["k_cache"]), np_of(inp["v_cache"]),
+                                 np_of(inp["k_new"]), np_of(inp["v_new"]), "bf16", L.numpy(), "BSHD", 8, 2,
+                                 cos.cpu().numpy(), sin.cpu().numpy(), mode)
+    g.append_ex(inp["k_cache"], inp["v_cache"], inp["k_new"], inp["v_new"], inp["lengths"], layout="BSHD",
+                rope=g.Rope(cos, sin, mode))
+    torch.cuda.synchronize()
+    assert np_of(inp["k_cache"]).tobytes() == rk.tobytes()
+    assert np_of(inp["v_cache"]).tobytes() == rv.tobytes()
+
+
+@pytest.mark.parametrize("case", [(3, 32, 8, 128, 600, "BHSD", "bf16", "half"),
+                                  (2, 16, 2, 128, 300, "BSHD", "bf16", "interleaved"),
+                                  (2, 8, 2, 64, 100, "BHSD", "f32", "half")],
+                         ids=["G4-bf16-half", "G8-BSHD-interleaved", "generic-f32"])
+def test_rope_step_int8(g, case):
+    B, Hq, Hkv, D, S, layout, qo, mode = case
+    say(f"rope int8 {case}")
+    w = W.custom(B, Hq, Hkv, D, S, layout, "i8", qo, seed=B * 13 + D, stale="pm:1")
+    L = torch.randint(0, S, (B,), generator=torch.Generator().manual_seed(S), dtype=torch.int32)
+    L[0] = S - 1
+    inp = W.make_q8(w, DEV, lengths=L)
+    cos, sin = W.rope_tables(S, D, DEV)
+    ref, rk, rv, rks, rvs = oracle.step_q8_rope(np_of(inp["q"]), qo, np_of(inp["k_cache"]), np_of(inp["v_cache"]),
+                                                np_of(inp["k_scale"]), np_of(inp["v_scale"]), np_of(inp["k_new"]),
+                                                np_of(inp["v_new"]), L.numpy(), layout, Hq, Hkv, cos.cpu().numpy(),
+                                                sin.cpu().numpy(), mode)
+    out = g.step_ex(inp["q"], inp["k_cache"], inp["v_cache"], inp["k_new"], inp["v_new"], inp["lengths"],
+                    layout=layout, k_scale=inp["k_scale"], v_scale=inp["v_scale"], rope=g.Rope(cos, sin, mode))
+    torch.cuda.synchronize()
+    assert_close(out, ref, qo, "step")
+    for name, want in (("k_cache", rk), ("v_cache", rv), ("k_scale", rks), ("v_scale", rvs)):
+        assert np_of(inp[name]).tobytes() == want.tobytes(), name

@@ -219,3 +219,47 @@ def test_rejections():
         rope.rope_rotate(np.zeros(5, np.float32), c[0][:2], s[0][:2], "half")
     with pytest.raises(ValueError):
         rope.rope_rotate(np.zeros(6, np.float32), c[0], s[0], "spiral")
+
+
+# ---------------------------------------------------------------------------
+# Int8 caches: rotation, then the per-row quantization rule.
+# ---------------------------------------------------------------------------
+def _q8_inputs(rng, B, Hq, Hkv, D, S):
+    q = (rng.standard_normal((B, Hq, D)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    kc = rng.integers(-127, 128, (B, Hkv, S, D)).astype(np.int8)
+    vc = rng.integers(-127, 128, (B, Hkv, S, D)).astype(np.int8)
+    ks = rng.uniform(0.01, 0.03, (B, Hkv, S)).astype(np.float32)
+    vs = rng.uniform(0.01, 0.03, (B, Hkv, S)).astype(np.float32)
+    kn = (rng.standard_normal((B, Hkv, D)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    vn = (rng.standard_normal((B, Hkv, D)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    return q, kc, vc, ks, vs, kn, vn
+
+
+def test_q8_identity_row_reduces_to_q8_step():
+    rng = np.random.default_rng(9)
+    B, Hq, Hkv, D, S = 2, 4, 2, 16, 7
+    q, kc, vc, ks, vs, kn, vn = _q8_inputs(rng, B, Hq, Hkv, D, S)
+    L = np.array([0, 6], np.int32)
+    c, s = np.ones((3, D // 2), np.float32), np.zeros((3, D // 2), np.float32)
+    got = rope.step_q8_rope(q, "bf16", kc, vc, ks, vs, kn, vn, L, "BHSD", Hq, Hkv, c, s, "half",
+                            positions=np.array([2, 1], np.int32))
+    ref = oracle.step_q8(q, "bf16", kc, vc, ks, vs, kn, vn, L, "BHSD", Hq, Hkv)
+    for a, b in zip(got, ref):
+        assert np.array_equal(a, b)
+
+
+def test_q8_quarter_turn_permutes_codes_with_signs():
+    """A quarter turn maps (x1, x2) to (-x2, x1) exactly; the row maximum is
+    unchanged and rounding half to even is odd-symmetric, so the stored codes
+    are the unrotated codes moved and negated, with the same scale."""
+    rng = np.random.default_rng(10)
+    B, Hq, Hkv, D, S = 1, 2, 1, 8, 3
+    q, kc, vc, ks, vs, kn, vn = _q8_inputs(rng, B, Hq, Hkv, D, S)
+    L = np.array([1], np.int32)
+    c, s = np.zeros((1, D // 2), np.float32), np.ones((1, D // 2), np.float32)
+    _, rk, _, rks, _ = rope.step_q8_rope(q, "bf16", kc, vc, ks, vs, kn, vn, L, "BHSD", Hq, Hkv, c, s, "half",
+                                         positions=np.zeros(1, np.int32))
+    codes, scale = oracle.quantize_row(oracle.decode(kn[0, 0], "bf16").astype(np.float32))
+    h = D // 2
+    assert rks[0, 0, 1] == scale
+    assert rk[0, 0, 1].tolist() == (-codes[h:]).tolist() + codes[:h].tolist()

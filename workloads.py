@@ -253,3 +253,12 @@ def custom(B, Hq, Hkv, D, capacity, layout="BHSD", kv_dtype="bf16", qo_dtype="bf
     return Workload(f"custom{seed}", seed, B=B, Hq=Hq, Hkv=Hkv, D=D, capacity=capacity, layout=layout,
                     kv_dtype=kv_dtype, qo_dtype=qo_dtype, len_lo=0, len_hi=max(capacity - 1, 0),
                     key_scale=key_scale, stale=stale)
+
+
+def rope_tables(max_pos: int, D: int, device="cpu", base: float = 10000.0):
+    """Rotary planes as a caller would pass them: float32 cos / sin tables of
+    shape (max_pos, D/2) for the angles p * base^(-2i/D) (an input of the
+    rotary step, computed in float64 and rounded once)."""
+    i = torch.arange(D // 2, dtype=torch.float64)
+    ang = torch.arange(max_pos, dtype=torch.float64)[:, None] * base ** (-2.0 * i / D)[None, :]
+    return ang.cos().to(torch.float32).to(device), ang.sin().to(torch.float32).to(device)
