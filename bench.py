@@ -56,7 +56,7 @@ def traffic_from_profiles(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, inp, budget_s=12.0):
+def cpu_baseline(w, inp, budget_s=12.0, rope=None):
     """The float64 oracle on this host's cores over a bounded sample of the same
     inputs: whole sequences (all query heads), repeated until about budget_s
     seconds of CPU work, scaled to GB/s with the same byte formula."""
@@ -77,7 +77,13 @@ def cpu_baseline(w, inp, budget_s=12.0):
 
     def run(st, nb):
         t0 = time.perf_counter()
-        if q8:
+        if rope is not None and q8:
+            oracle.step_q8_rope(st["q"], w.qo_dtype, st["k_cache"], st["v_cache"], st["k_scale"], st["v_scale"],
+                                st["k_new"], st["v_new"], L[:nb], w.layout, w.Hq, w.Hkv, *rope)
+        elif rope is not None:
+            oracle.step_rope(st["q"], w.qo_dtype, st["k_cache"], st["v_cache"], st["k_new"], st["v_new"], w.kv_dtype,
+                             L[:nb], w.layout, w.Hq, w.Hkv, *rope)
+        elif q8:
             oracle.step_q8(st["q"], w.qo_dtype, st["k_cache"], st["v_cache"], st["k_scale"], st["v_scale"],
                            st["k_new"], st["v_new"], L[:nb], w.layout, w.Hq, w.Hkv)
         else:
@@ -96,7 +102,8 @@ def cpu_baseline(w, inp, budget_s=12.0):
     sub = W.Workload(**{**w.__dict__, "B": nb})
     nbytes = W.algorithmic_bytes(sub, L[:nb]) * reps
     gbs = nbytes / t / 1e9
-    sample = (f"oracle.{'step_q8' if q8 else 'step'} over sequences 0..{nb - 1} of {w.B} (all {w.Hq} query heads) of the same inputs, "
+    fn = ("step_q8" if q8 else "step") if rope is None else ("step_q8_rope" if q8 else "step_rope")
+    sample = (f"oracle.{fn} over sequences 0..{nb - 1} of {w.B} (all {w.Hq} query heads) of the same inputs, "
               f"{reps} repetition(s), {t:.1f} s")
     return {"value": round(gbs, 6), "unit": "GB/s", "cores": threads, "kind": "oracle", "sample": sample,
             "steps_per_sec_equiv": round(gbs * 1e9 / W.algorithmic_bytes(w, L), 6),
@@ -128,6 +135,8 @@ def main():
     ap.add_argument("--kv", default="native", choices=["native", "int8"],
                     help="native: the workload's cache dtype; int8: int8 codes with per-row float32 scales "
                          "(the step quantizes the new rows)")
+    ap.add_argument("--rope", default="none", choices=["none", "half", "interleaved"],
+                    help="rotate q and the new key with rotary planes in the append (positions = lengths)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="only run a plain copy of this many MiB (counter calibration) and exit")
@@ -186,12 +195,25 @@ def main():
     R = min(16, math.ceil(3 * MALL_BYTES / kv_bytes)) if 16 * kv_bytes >= MALL_BYTES else 1
     names = ("k_cache", "v_cache") + (("k_scale", "v_scale") if q8 else ())
     caches = [tuple(inp[n] for n in names)] + [tuple(inp[n].clone() for n in names) for _ in range(R - 1)]
-    ws = torch.empty(max(plan["workspace_bytes"], 1), dtype=torch.uint8, device=dev)
+    rope = None
+    wsb = plan["workspace_bytes"]
+    if args.rope != "none":
+        import ctypes
+        cos, sin = W.rope_tables(w.capacity, w.D, dev)
+        rope = g.Rope(cos, sin, args.rope)
+        rs = rope.struct()
+        wsb = g.workspace_size_ex(desc, g.OptsT(None, None, ctypes.pointer(rs)))
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
     out = torch.empty_like(inp["q"])
 
     def step(i):
         kc, vc = caches[i % R][:2]
-        if q8:
+        if rope is not None:
+            ks, vs = caches[i % R][2:] if q8 else (None, None)
+            g.step_ex(inp["q"], kc, vc, inp["k_new"], inp["v_new"], inp["lengths"], layout=w.layout, table=table,
+                      kind=kind, table_host=table_host if kind else None, k_scale=ks, v_scale=vs, rope=rope, out=out,
+                      workspace=ws, num_splits=args.num_splits)
+        elif q8:
             ks, vs = caches[i % R][2:]
             g.step_q8(inp["q"], kc, vc, ks, vs, inp["k_new"], inp["v_new"], inp["lengths"], layout=w.layout, out=out,
                       workspace=ws, num_splits=args.num_splits)
@@ -218,7 +240,8 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, inp_dense)   # the dense oracle on the same logical caches
+        rope_np = None if rope is None else (rope.cos.cpu().numpy(), rope.sin.cpu().numpy(), args.rope)
+        cpu = cpu_baseline(w, inp_dense, rope=rope_np)   # the dense oracle on the same logical caches
 
     kv = {"bf16": "bf16", "f32": "f32", "i8": "i8+f32 row scales"}[w.kv_dtype]
     line = {
@@ -237,13 +260,14 @@ def main():
         "data": "synthetic",
         "steps_per_sec": round(1000.0 / ms, 2),
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
-        "config": {"workload": w.name, "cache": args.cache, "batch": w.B, "num_q_heads": w.Hq, "num_kv_heads": w.Hkv, "head_dim": w.D,
+        "config": {"workload": w.name, "cache": args.cache, "rope": args.rope, "batch": w.B, "num_q_heads": w.Hq, "num_kv_heads": w.Hkv, "head_dim": w.D,
                    "capacity": w.capacity, "layout": w.layout, "kv_dtype": w.kv_dtype, "qo_dtype": w.qo_dtype,
                    "tokens_attended": int((L + 1).sum()), "algorithmic_bytes_per_step": nbytes,
                    "cache_rotation": R, "plan": plan},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_from_profiles(w.name) if args.cache == "dense" and not q8 else None,
+                     "traffic": traffic_from_profiles(w.name)
+                     if args.cache == "dense" and not q8 and rope is None else None,
                      "per": "one gqa_decode_step call (attention kernel + split combine), HIP events over the "
                             "timed region"},
         "cpu_baseline": cpu,

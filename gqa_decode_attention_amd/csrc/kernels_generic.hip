@@ -83,11 +83,14 @@ __device__ __forceinline__ void store_q8_row(const float (&x)[4], int lane, int 
   if (lane == 0) sdst[off / D] = scale;
 }
 
+// One wave per (b, kv-head, K or V) row, four per workgroup.
 template <int NEW>
 __global__ __launch_bounds__(256) void append_q8_kernel(AttnArgs a, int8_t* __restrict__ kc, int8_t* __restrict__ vc) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // b * Hkv + h
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // 2 (b * Hkv + h) + which
   const int lane = threadIdx.x & 63;
-  if (row >= (int64_t)a.B * a.Hkv) return;  // whole waves; no barrier follows
+  if (item >= 2 * (int64_t)a.B * a.Hkv) return;  // whole waves; no barrier follows
+  const int64_t row = item >> 1;
+  const int which = (int)(item & 1);
   const int b = (int)(row / a.Hkv);
   const int h = (int)(row % a.Hkv);
   const int pos = a.lengths[b];
@@ -95,21 +98,18 @@ __global__ __launch_bounds__(256) void append_q8_kernel(AttnArgs a, int8_t* __re
   const int64_t off = slot_offset_checked(a, b, h, pos);
   if (off < 0) return;
   const int D = a.D;
+  const void* src = which ? a.v_new : a.k_new;
+  float x[4];
 #pragma unroll
-  for (int which = 0; which < 2; ++which) {
-    const void* src = which ? a.v_new : a.k_new;
-    float x[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d = lane + 64 * i;
-      x[i] = d < D ? Store<NEW>::load1_cached(src, row * D + d) : 0.f;
-    }
-    store_q8_row(x, lane, D, which ? vc : kc, which ? a.v_scale_w : a.k_scale_w, off);
+  for (int i = 0; i < 4; ++i) {
+    const int d = lane + 64 * i;
+    x[i] = d < D ? Store<NEW>::load1_cached(src, row * D + d) : 0.f;
   }
+  store_q8_row(x, lane, D, which ? vc : kc, which ? a.v_scale_w : a.k_scale_w, off);
 }
 
 hipError_t launch_append_q8(const AttnArgs& a, void* k_cache, void* v_cache, hipStream_t s) {
-  const unsigned blocks = (unsigned)(((int64_t)a.B * a.Hkv + 3) / 4);
+  const unsigned blocks = (unsigned)((2 * (int64_t)a.B * a.Hkv + 3) / 4);
   AttnArgs arg = a;
   void* params[] = {&arg, &k_cache, &v_cache};
   const void* fn = a.qo_dtype == GQA_F32 ? reinterpret_cast<const void*>(&append_q8_kernel<GQA_F32>)
@@ -120,12 +120,13 @@ hipError_t launch_append_q8(const AttnArgs& a, void* k_cache, void* v_cache, hip
 // ---------------------------------------------------------------------------
 // Rotary append (CLIKA "groupQueryAttention" page: q and the new k rotated with
 // the rope planes, optional post-rotation RMS norm with gains, the rotated key
-// appended in place).  One workgroup per (b, kv-head); its 4 waves take rows
-// k, v, then the G query heads (rotated q is written only when a.q_rot is
-// set).  A row is held as elements d = lane + 64 i; the partner of a rotation
+// appended in place).  The rows of (b, kv-head) are k, v, then its G query
+// heads (rotated q is written only when a.q_rot is set).  A row is held as elements d = lane + 64 i; the partner of a rotation
 // pair comes from another lane by a cross-lane read.  Products and sums are
 // rounded separately (no contraction), so the rotation is reproducible.  The
-// value row is a raw copy (int8 caches: quantized like the key).
+// value row is a raw copy (int8 caches: quantized like the key).  One wave per
+// row, four per workgroup, so every row's load-reduce-store chain runs in
+// parallel.
 // ---------------------------------------------------------------------------
 // One element of a rotated pair: x1 c - x2 s for the first, x2 c + x1 s for the
 // second (x = this element, xp = its partner), each product and the sum
@@ -140,10 +141,13 @@ __device__ __forceinline__ float rope_pair(bool first, float x, float xp, float 
 template <int KV, int QO>
 __global__ __launch_bounds__(256) void rope_append_kernel(AttnArgs a, void* __restrict__ kc, void* __restrict__ vc) {
   constexpr int NEW = KV == GQA_I8 ? QO : KV;  // storage of k_new / v_new
-  const int bh = blockIdx.x;                   // b * Hkv + h
+  const int nrows = 2 + (a.q_rot != nullptr ? a.G : 0);  // k, v, then the query heads
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= (int64_t)a.B * a.Hkv * nrows) return;     // whole waves; no barrier follows
+  const int bh = (int)(item / nrows);                    // b * Hkv + h
+  const int row = (int)(item - (int64_t)bh * nrows);
   const int b = bh / a.Hkv;
   const int h = bh - b * a.Hkv;
-  const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int D = a.D;
   const int half = D >> 1;
@@ -153,11 +157,10 @@ __global__ __launch_bounds__(256) void rope_append_kernel(AttnArgs a, void* __re
   const float* cs = a.rope_cos + (int64_t)p * half;
   const float* sn = a.rope_sin + (int64_t)p * half;
   const int64_t off = (L >= 0 && L < a.S) ? slot_offset_checked(a, b, h, L) : -1;
-  const int nrows = 2 + (a.q_rot != nullptr ? a.G : 0);
-  for (int row = wave; row < nrows; row += 4) {  // uniform within a wave
+  {
     const bool isv = row == 1;
     const bool isq = row >= 2;
-    if (!isq && off < 0) continue;             // the map names no valid slot: nothing appended
+    if (!isq && off < 0) return;               // the map names no valid slot: nothing appended
     const int64_t base = isq ? ((int64_t)b * a.Hq + (int64_t)h * a.G + (row - 2)) * D : (int64_t)bh * D;
     if (isv && KV != GQA_I8) {
       for (int d = lane; d < D; d += 64) {
@@ -166,7 +169,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(AttnArgs a, void* __re
         else
           reinterpret_cast<uint32_t*>(vc)[off + d] = reinterpret_cast<const uint32_t*>(a.v_new)[base + d];
       }
-      continue;
+      return;
     }
     float x[4];
 #pragma unroll
@@ -251,7 +254,8 @@ hipError_t launch_rope_append(const AttnArgs& a, void* k_cache, void* v_cache, h
   else
     fn = f32 ? reinterpret_cast<const void*>(&rope_append_kernel<GQA_F32, GQA_F32>)
              : reinterpret_cast<const void*>(&rope_append_kernel<GQA_F32, GQA_BF16>);
-  return hipLaunchKernel(fn, dim3((unsigned)((int64_t)a.B * a.Hkv)), dim3(256), params, 0, s);
+  const int64_t items = (int64_t)a.B * a.Hkv * (2 + (a.q_rot != nullptr ? a.G : 0));
+  return hipLaunchKernel(fn, dim3((unsigned)((items + 3) / 4)), dim3(256), params, 0, s);
 }
 
 // ---------------------------------------------------------------------------
