@@ -38,3 +38,9 @@ from .rope import (  # noqa: F401
     step_q8_rope,
     step_rope,
 )
+from .variants import (  # noqa: F401
+    attend_variant_one,
+    attend_variants,
+    attended_slots,
+    step_variants,
+)
