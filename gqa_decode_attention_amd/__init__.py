@@ -6,7 +6,8 @@ slot ``lengths[b]`` of a fixed-capacity cache, ``attend`` runs length-masked
 GQA attention over the cache, and ``step`` does both in one call; the
 ``_mapped`` calls take slot-indexed or paged caches and the ``_q8`` calls int8
 caches with per-row scales; the ``_ex`` calls take any combination of a cache
-map, int8 scales and rotary encoding (``Rope``).  torch is
+map, int8 scales, rotary encoding (``Rope``) and softmax variants
+(``Softmax``).  torch is
 used for device memory and streams only.
 """
 from ._lib import (  # noqa: F401
@@ -21,6 +22,8 @@ from ._lib import (  # noqa: F401
     OptsT,
     Rope,
     RopeT,
+    Softmax,
+    SoftmaxT,
     ScalesT,
     append,
     append_ex,

@@ -96,12 +96,25 @@ class RopeT(ctypes.Structure):
     ]
 
 
+class SoftmaxT(ctypes.Structure):
+    """gqa_softmax_t."""
+    _fields_ = [
+        ("sink", ctypes.c_void_p),
+        ("smooth", ctypes.c_int32),
+        ("softcap", ctypes.c_float),
+        ("window", ctypes.c_int32),
+        ("kept_prefix", ctypes.c_int32),
+        ("kept_prefix_per_seq", ctypes.c_void_p),
+    ]
+
+
 class OptsT(ctypes.Structure):
     """gqa_decode_opts_t."""
     _fields_ = [
         ("map", ctypes.POINTER(MapT)),
         ("scales", ctypes.POINTER(ScalesT)),
         ("rope", ctypes.POINTER(RopeT)),
+        ("softmax", ctypes.POINTER(SoftmaxT)),
     ]
 
 
@@ -476,8 +489,29 @@ class Rope:
                      -1.0 if self.eps is None else float(self.eps))
 
 
+class Softmax:
+    """Softmax variants (gqa_softmax_t): sink = float32 (Hq,) device logits or
+    None; smooth = a zero logit for every head; softcap > 0 caps the scaled
+    scores; window > 0 keeps the last `window` slots plus the kept prefix
+    (kept_prefix for every sequence, or kept_prefix_per_seq: int32 (B,) device)."""
+
+    def __init__(self, sink=None, smooth=False, softcap=0.0, window=0, kept_prefix=0, kept_prefix_per_seq=None):
+        if sink is not None and (sink.dtype != torch.float32 or not sink.is_contiguous() or not sink.is_cuda):
+            raise ValueError("sink is a contiguous float32 device tensor")
+        if kept_prefix_per_seq is not None and (kept_prefix_per_seq.dtype != torch.int32
+                                                or not kept_prefix_per_seq.is_contiguous()):
+            raise ValueError("kept_prefix_per_seq is a contiguous int32 tensor")
+        self.sink, self.smooth, self.softcap = sink, bool(smooth), float(softcap)
+        self.window, self.kept_prefix, self.kept_prefix_per_seq = int(window), int(kept_prefix), kept_prefix_per_seq
+
+    def struct(self) -> SoftmaxT:
+        ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+        return SoftmaxT(ptr(self.sink), int(self.smooth), self.softcap, self.window, self.kept_prefix,
+                        ptr(self.kept_prefix_per_seq))
+
+
 def _opts(desc_args, *, table=None, kind=None, table_host=None, k_scale=None, v_scale=None, k_cache=None,
-          layout="BHSD", rope=None):
+          layout="BHSD", rope=None, softmax=None):
     """(desc, opts, keep-alive) for an _ex call; desc_args = (B, Hq, D, kv_code, qo_code, num_splits, Hkv)."""
     B, Hq, D, kv_code, qo_code, ns, Hkv = desc_args
     keep = []
@@ -502,6 +536,10 @@ def _opts(desc_args, *, table=None, kind=None, table_host=None, k_scale=None, v_
         r = rope.struct()
         keep.append(r)
         o.rope = ctypes.pointer(r)
+    if softmax is not None:
+        v = softmax.struct()
+        keep.append(v)
+        o.softmax = ctypes.pointer(v)
     return desc, o, keep
 
 
@@ -539,14 +577,14 @@ def append_ex(k_cache, v_cache, k_new, v_new, lengths, *, layout="BHSD", table=N
 
 
 def attend_ex(q, k_cache, v_cache, lengths, *, layout="BHSD", table=None, kind=None, table_host=None, k_scale=None,
-              v_scale=None, out=None, workspace=None, num_splits=0):
-    """Read-only attention with options (map, int8 scales)."""
+              v_scale=None, softmax=None, out=None, workspace=None, num_splits=0):
+    """Read-only attention with options (map, int8 scales, softmax variants)."""
     tens = [q, k_cache, v_cache] + ([k_scale, v_scale] if k_scale is not None else [])
     dev = _dev(tens, lengths)
     B, Hq, D = q.shape
     desc, o, keep = _opts((B, Hq, D, _dtype_code(k_cache.dtype), _dtype_code(q.dtype), num_splits, None),
                           table=table, kind=kind, table_host=table_host, k_scale=k_scale, v_scale=v_scale,
-                          k_cache=k_cache, layout=layout)
+                          k_cache=k_cache, layout=layout, softmax=softmax)
     if out is None:
         out = torch.empty_like(q)
     workspace, wptr, wbytes = _workspace_ex(desc, o, dev, workspace)
@@ -558,14 +596,14 @@ def attend_ex(q, k_cache, v_cache, lengths, *, layout="BHSD", table=None, kind=N
 
 
 def step_ex(q, k_cache, v_cache, k_new, v_new, lengths, *, layout="BHSD", table=None, kind=None, table_host=None,
-            k_scale=None, v_scale=None, rope=None, out=None, workspace=None, num_splits=0):
-    """Decode step with options (map, int8 scales, rotary encoding). Returns out."""
+            k_scale=None, v_scale=None, rope=None, softmax=None, out=None, workspace=None, num_splits=0):
+    """Decode step with options (map, int8 scales, rotary encoding, softmax variants). Returns out."""
     tens = [q, k_cache, v_cache, k_new, v_new] + ([k_scale, v_scale] if k_scale is not None else [])
     dev = _dev(tens, lengths)
     B, Hq, D = q.shape
     desc, o, keep = _opts((B, Hq, D, _dtype_code(k_cache.dtype), _dtype_code(q.dtype), num_splits, None),
                           table=table, kind=kind, table_host=table_host, k_scale=k_scale, v_scale=v_scale,
-                          k_cache=k_cache, layout=layout, rope=rope)
+                          k_cache=k_cache, layout=layout, rope=rope, softmax=softmax)
     if out is None:
         out = torch.empty_like(q)
     workspace, wptr, wbytes = _workspace_ex(desc, o, dev, workspace)

@@ -419,7 +419,43 @@ void fill_rope(const gqa_rope_t* r, AttnArgs* a) {
   a->norm_eps = r->norm_eps;
 }
 
-const gqa_decode_opts_t kNoOpts = {nullptr, nullptr, nullptr};
+// Softmax variants: the values (before the batch-0 early return), then the
+// device arrays, which must not overlap anything the call writes.
+gqa_status_t check_softmax(const gqa_decode_desc_t* d, const gqa_softmax_t* v) {
+  (void)d;
+  if (v == nullptr) return GQA_OK;
+  if (v->smooth != 0 && v->smooth != 1) return GQA_ERR_INVALID_ARGUMENT;
+  if (v->smooth && v->sink != nullptr) return GQA_ERR_INVALID_ARGUMENT;
+  if (!(v->softcap >= 0.f) || !std::isfinite(v->softcap)) return GQA_ERR_INVALID_ARGUMENT;
+  if (v->window < 0 || v->kept_prefix < 0) return GQA_ERR_INVALID_ARGUMENT;
+  if (v->window == 0 && (v->kept_prefix != 0 || v->kept_prefix_per_seq != nullptr)) return GQA_ERR_INVALID_ARGUMENT;
+  return GQA_OK;
+}
+gqa_status_t check_softmax_ptrs(const gqa_decode_desc_t* d, const gqa_softmax_t* v,
+                                std::initializer_list<Span> written) {
+  if (v == nullptr) return GQA_OK;
+  if (!aligned(v->sink, 4) || !aligned(v->kept_prefix_per_seq, 4)) return GQA_ERR_INVALID_ARGUMENT;
+  const Span in[] = {span(v->sink, v->sink ? (size_t)d->num_q_heads * 4 : 0),
+                     span(v->kept_prefix_per_seq, v->kept_prefix_per_seq ? (size_t)d->batch * 4 : 0)};
+  for (const Span& w : written)
+    for (const Span& x : in)
+      if (overlap(w, x)) return GQA_ERR_INVALID_ARGUMENT;
+  return GQA_OK;
+}
+void fill_softmax(const gqa_decode_desc_t* d, const gqa_softmax_t* v, AttnArgs* a) {
+  if (v == nullptr) return;
+  a->sink = v->sink;
+  a->smooth = v->smooth;
+  if (v->softcap > 0.f) {
+    a->cap_T = (float)((double)v->softcap * std::sqrt((double)d->head_dim));
+    a->cap_invT = (float)(1.0 / ((double)v->softcap * std::sqrt((double)d->head_dim)));
+  }
+  a->window = v->window;
+  a->prefix = v->kept_prefix;
+  a->prefix_seq = v->kept_prefix_per_seq;
+}
+
+const gqa_decode_opts_t kNoOpts = {nullptr, nullptr, nullptr, nullptr};
 
 // Bytes of the rotated q a rotary step keeps after the plan's workspace.
 size_t rope_q_offset(const Plan& p) { return align256(p.workspace_bytes); }
@@ -437,6 +473,7 @@ gqa_status_t do_append(const gqa_decode_desc_t* desc, const gqa_decode_opts_t* o
   const gqa_kv_scales_t* sc = o->scales;
   if ((st = check_scales(desc, sc, map)) != GQA_OK) return st;
   if ((st = check_rope(desc, o->rope)) != GQA_OK) return st;
+  if (o->softmax != nullptr) return GQA_ERR_INVALID_ARGUMENT;  // the append computes no softmax
   Plan p;
   std::memset(&p, 0, sizeof(p));
   p.kernel = GQA_KERNEL_GENERIC;  // the append kernel takes any block size
@@ -500,6 +537,7 @@ gqa_status_t do_attend(const gqa_decode_desc_t* desc, const gqa_decode_opts_t* o
   if ((st = check_scales(desc, sc, map)) != GQA_OK) return st;
   if (rope != nullptr && !step) return GQA_ERR_INVALID_ARGUMENT;  // rotation belongs to the append
   if ((st = check_rope(desc, rope)) != GQA_OK) return st;
+  if ((st = check_softmax(desc, o->softmax)) != GQA_OK) return st;
   if (map != nullptr && (st = check_map(desc, map, p)) != GQA_OK) return st;
   if (desc->batch == 0) return GQA_OK;
   Plan pw = p;  // the plan with the whole workspace the call needs (rotated q after the partials)
@@ -525,9 +563,20 @@ gqa_status_t do_attend(const gqa_decode_desc_t* desc, const gqa_decode_opts_t* o
                           span(sc ? sc->v_scale : nullptr, sb)});
     if (st != GQA_OK) return st;
   }
+  if (o->softmax != nullptr) {
+    const size_t sb = sc ? B * Hkv * desc->capacity * 4 : 0;
+    st = check_softmax_ptrs(desc, o->softmax,
+                            {span(out, B * Hq * D * eqo), span(workspace, pw.workspace_bytes),
+                             span(step ? k_cache : nullptr, step ? ce : 0),
+                             span(step ? v_cache : nullptr, step ? ce : 0),
+                             span(step && sc ? sc->k_scale : nullptr, step ? sb : 0),
+                             span(step && sc ? sc->v_scale : nullptr, step ? sb : 0)});
+    if (st != GQA_OK) return st;
+  }
   AttnArgs a;
   fill_args(desc, p, &a);
   fill_map(desc, map, &a);
+  fill_softmax(desc, o->softmax, &a);
   if (sc != nullptr) {
     a.k_scale = sc->k_scale;
     a.v_scale = sc->v_scale;
@@ -626,7 +675,7 @@ gqa_status_t gqa_decode_append_mapped(const gqa_decode_desc_t* desc, const gqa_c
                                       const int32_t* lengths, void* stream) {
   try {
     if (map == nullptr) return GQA_ERR_INVALID_ARGUMENT;
-    const gqa_decode_opts_t o = {map, nullptr, nullptr};
+    const gqa_decode_opts_t o = {map, nullptr, nullptr, nullptr};
     return do_append(desc, &o, k_cache, v_cache, k_new, v_new, lengths, stream);
   } catch (...) {
     return GQA_ERR_INTERNAL;
@@ -638,7 +687,7 @@ gqa_status_t gqa_decode_attend_mapped(const gqa_decode_desc_t* desc, const gqa_c
                                       void* workspace, size_t workspace_bytes, void* stream) {
   try {
     if (map == nullptr) return GQA_ERR_INVALID_ARGUMENT;
-    const gqa_decode_opts_t o = {map, nullptr, nullptr};
+    const gqa_decode_opts_t o = {map, nullptr, nullptr, nullptr};
     return do_attend(desc, &o, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache), nullptr, nullptr, lengths,
                      out, workspace, workspace_bytes, stream, false);
   } catch (...) {
@@ -652,7 +701,7 @@ gqa_status_t gqa_decode_step_mapped(const gqa_decode_desc_t* desc, const gqa_cac
                                     void* stream) {
   try {
     if (map == nullptr) return GQA_ERR_INVALID_ARGUMENT;
-    const gqa_decode_opts_t o = {map, nullptr, nullptr};
+    const gqa_decode_opts_t o = {map, nullptr, nullptr, nullptr};
     return do_attend(desc, &o, q, k_cache, v_cache, k_new, v_new, lengths, out, workspace, workspace_bytes, stream,
                      true);
   } catch (...) {
@@ -665,7 +714,7 @@ gqa_status_t gqa_decode_append_q8(const gqa_decode_desc_t* desc, const gqa_kv_sc
                                   void* stream) {
   try {
     if (scales == nullptr) return GQA_ERR_INVALID_ARGUMENT;
-    const gqa_decode_opts_t o = {nullptr, scales, nullptr};
+    const gqa_decode_opts_t o = {nullptr, scales, nullptr, nullptr};
     return do_append(desc, &o, k_cache, v_cache, k_new, v_new, lengths, stream);
   } catch (...) {
     return GQA_ERR_INTERNAL;
@@ -677,7 +726,7 @@ gqa_status_t gqa_decode_attend_q8(const gqa_decode_desc_t* desc, const gqa_kv_sc
                                   void* workspace, size_t workspace_bytes, void* stream) {
   try {
     if (scales == nullptr) return GQA_ERR_INVALID_ARGUMENT;
-    const gqa_decode_opts_t o = {nullptr, scales, nullptr};
+    const gqa_decode_opts_t o = {nullptr, scales, nullptr, nullptr};
     return do_attend(desc, &o, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache), nullptr, nullptr, lengths,
                      out, workspace, workspace_bytes, stream, false);
   } catch (...) {
@@ -691,7 +740,7 @@ gqa_status_t gqa_decode_step_q8(const gqa_decode_desc_t* desc, const gqa_kv_scal
                                 void* stream) {
   try {
     if (scales == nullptr) return GQA_ERR_INVALID_ARGUMENT;
-    const gqa_decode_opts_t o = {nullptr, scales, nullptr};
+    const gqa_decode_opts_t o = {nullptr, scales, nullptr, nullptr};
     return do_attend(desc, &o, q, k_cache, v_cache, k_new, v_new, lengths, out, workspace, workspace_bytes, stream,
                      true);
   } catch (...) {

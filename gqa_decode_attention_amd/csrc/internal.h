@@ -47,6 +47,15 @@ struct AttnArgs {
   void* q_rot;
   int32_t rope_max_pos, rope_mode;
   float norm_eps;
+  // Softmax variants (attention passes and the combine): per-query-head sink
+  // logits (natural units) or smooth softmax (a zero logit), softcap as
+  // T = cap * sqrt(D) on raw scores (0: none), sliding window (0: none) with a
+  // kept prefix (one value, or one per sequence when prefix_seq is set).
+  const float* sink;
+  int32_t smooth;
+  float cap_T, cap_invT;
+  int32_t window, prefix;
+  const int32_t* prefix_seq;
   int32_t nsplit, split_tokens;
   int32_t head_chunks;   // generic kernel: query-head chunks per kv-head
   int32_t len_offset;    // slots attended = lengths[b] + len_offset (1 for a step, 0 for attend)

@@ -18,6 +18,7 @@
 #include <mutex>
 
 #include "cache_map.h"
+#include "variants.h"
 #include "device_common.h"
 #include "internal.h"
 
@@ -300,11 +301,14 @@ __global__ __launch_bounds__(256) void attend_generic_kernel(AttnArgs a) {
 
   int n = a.lengths[b] + a.len_offset;
   n = n < 0 ? 0 : (n > a.S ? a.S : n);
+  // Slots are walked in the sliding window's virtual order (the identity
+  // without a window).
+  const SeqView view = seq_view(a, b, n);
   const int t_begin = split * a.split_tokens;
-  const int t_end = min(t_begin + a.split_tokens, n);
+  const int t_end = min(t_begin + a.split_tokens, view.nv);
   // Splits holding valid slots.  A lone active split (or split 0 when n = 0)
   // writes the output itself and the combine pass leaves that sequence alone.
-  const int nact = n == 0 ? 0 : min(a.nsplit, (n + a.split_tokens - 1) / a.split_tokens);
+  const int nact = view.nv == 0 ? 0 : min(a.nsplit, (view.nv + a.split_tokens - 1) / a.split_tokens);
   if (split >= max(nact, 1)) return;
 
   const int64_t qrow0 = ((int64_t)b * a.Hq + (int64_t)h * a.G + g0) * D;
@@ -332,7 +336,9 @@ __global__ __launch_bounds__(256) void attend_generic_kernel(AttnArgs a) {
   const char* vb = reinterpret_cast<const char*>(a.v_cache);
 
   for (int t = t_begin + rg; t < t_end; t += NRG) {
-    const int64_t row = slot_offset(a, b, h, t);
+    const int tp = phys_slot(view, t);
+    if (unattended(view, tp)) continue;  // uniform within the row group
+    const int64_t row = slot_offset(a, b, h, tp);
     float kv[EPL], vv[EPL];
     float ks = 1.f, vs = 1.f;  // int8 caches: the row scales
     if constexpr (KV == GQA_I8) {
@@ -362,7 +368,11 @@ __global__ __launch_bounds__(256) void attend_generic_kernel(AttnArgs a) {
       for (int e = 0; e < EPL; ++e) part = fmaf(qv[g][e], kv[e], part);
 #pragma unroll
       for (int off = LPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off);
-      const float s = part * (KV == GQA_I8 ? ks * a.scale_log2 : a.scale_log2);
+      float s;
+      if (a.cap_T > 0.f)
+        s = cap_score(KV == GQA_I8 ? part * ks : part, a.cap_T, a.cap_invT) * a.scale_log2;
+      else
+        s = part * (KV == GQA_I8 ? ks * a.scale_log2 : a.scale_log2);
       const float mn = fmaxf(m[g], s);
       const float alpha = fast_exp2(m[g] - mn);  // 0 on the first slot (m = -inf)
       const float p = fast_exp2(s - mn);
@@ -427,7 +437,8 @@ __global__ __launch_bounds__(256) void attend_generic_kernel(AttnArgs a) {
     }
     const int hq = h * a.G + g0 + g;
     if (nact <= 1) {
-      Store<QO>::store1(a.out, ((int64_t)b * a.Hq + hq) * D + d, L > 0.f ? O / L : 0.f);
+      Store<QO>::store1(a.out, ((int64_t)b * a.Hq + hq) * D + d,
+                        a.sink != nullptr || a.smooth ? O * finish_scale(a, hq, M, L) : (L > 0.f ? O / L : 0.f));
     } else {
       const int64_t pi = ((int64_t)b * a.Hq + hq) * a.nsplit + split;
       a.part_o[pi * D + d] = O;
@@ -499,6 +510,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
   const int b = (int)(bh / a.Hq);
   int n = a.lengths[b] + a.len_offset;
   n = n < 0 ? 0 : (n > a.S ? a.S : n);
+  if (a.window > 0) n = seq_view(a, b, n).nv;  // the splits cover the window's virtual slots
   const int nact = n == 0 ? 0 : min(a.nsplit, (n + a.split_tokens - 1) / a.split_tokens);
   if (nact <= 1) return;  // the attention pass wrote this sequence's output itself
   const int64_t pbase = bh * a.nsplit;
@@ -519,10 +531,12 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
       if (d < D) O[k] = fmaf(w, po[d], O[k]);
     }
   }
+  const bool sink = a.sink != nullptr || a.smooth;
+  const float fs = sink ? finish_scale(a, (int)(bh - (int64_t)b * a.Hq), M, L) : 0.f;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int d = lane + 64 * k;
-    if (d < D) Store<QO>::store1(a.out, bh * D + d, L > 0.f ? O[k] / L : 0.f);
+    if (d < D) Store<QO>::store1(a.out, bh * D + d, sink ? O[k] * fs : (L > 0.f ? O[k] / L : 0.f));
   }
 }
 
@@ -553,6 +567,7 @@ __global__ __launch_bounds__(256) void combine128_kernel(AttnArgs a) {
   }
   int n = len + a.len_offset;
   n = n < 0 ? 0 : (n > a.S ? a.S : n);
+  if (a.window > 0) n = seq_view(a, b, n).nv;  // the splits cover the window's virtual slots
   const int nact = n == 0 ? 0 : min(a.nsplit, (n + a.split_tokens - 1) / a.split_tokens);
   if (nact <= 1) return;  // the attention pass wrote this sequence's output itself
   const float M = wave_max(lane < nact ? mraw : kNegInf);
@@ -573,7 +588,8 @@ __global__ __launch_bounds__(256) void combine128_kernel(AttnArgs a) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], 32);
   if (half == 0) {
-    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const float inv = a.sink != nullptr || a.smooth ? finish_scale(a, (int)(bh - (int64_t)b * a.Hq), M, L)
+                                                    : (L > 0.f ? 1.f / L : 0.f);
     if (QO == GQA_F32) {
       reinterpret_cast<f32x4*>(a.out)[bh * 32 + q] = acc * inv;
     } else {

@@ -20,6 +20,7 @@
 #include "cache_map.h"
 #include "device_common.h"
 #include "internal.h"
+#include "variants.h"
 
 namespace gqa {
 
@@ -87,7 +88,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 
-template <bool PAGED>
+template <bool PAGED, bool VAR>
 __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sk[2][kTileT * kPitch];
   __shared__ __attribute__((aligned(16))) uint16_t sv[2][kTileT * kPitch];
@@ -105,12 +106,19 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
   const int b = x / a.Hkv;
   const int G = a.G;
 
-  const int L = a.lengths[b];
-  int n = L + a.len_offset;
+  const int L0 = a.lengths[b];
+  int n = L0 + a.len_offset;
   n = n < 0 ? 0 : (n > a.S ? a.S : n);
+  // Slots are walked in the sliding window's virtual order (the identity
+  // without a window); the new token is the last virtual slot, L.
+  SeqView view{n, n, 0, 0, 0};
+  if constexpr (VAR) view = seq_view(a, b, n);
+  auto phys = [&](int t) { return VAR ? phys_slot(view, t) : t; };
+  const int nv = view.nv;
+  const int L = L0 - view.gap;
   const int t_begin = split * a.split_tokens;
-  const int t_end = min(t_begin + a.split_tokens, n);
-  const int nact = n == 0 ? 0 : min(a.nsplit, (n + a.split_tokens - 1) / a.split_tokens);
+  const int t_end = min(t_begin + a.split_tokens, nv);
+  const int nact = nv == 0 ? 0 : min(a.nsplit, (nv + a.split_tokens - 1) / a.split_tokens);
   if (split >= max(nact, 1)) return;
   const bool own_new = a.k_new != nullptr && L >= t_begin && L < t_end;
 
@@ -169,7 +177,7 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2) {
         const int hc = max(min(t0 + 16 * q2, last16), tv);
-        en.e[q2] = a.map[(int64_t)b * a.max_blocks + hc / a.bs];
+        en.e[q2] = a.map[(int64_t)b * a.max_blocks + phys(hc) / a.bs];
       }
     }
     return en;
@@ -179,11 +187,11 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
     for (int q2 = 0; q2 < 2; ++q2) {
       const int rc = max(min(t0 + prow + 16 * q2, t_end - 1), t_begin);
       int64_t off;
-      if (PAGED) {
+      if (PAGED) {  // a 16-row half lies in one block and moves with its (16-aligned) origin
         const int hc = max(min(t0 + 16 * q2, last16), tv);
-        off = block_head_offset(a, en.e[q2], h) + (int64_t)(hc % a.bs + (rc - hc)) * rs + 8 * piece;
+        off = block_head_offset(a, en.e[q2], h) + (int64_t)(phys(hc) % a.bs + (rc - hc)) * rs + 8 * piece;
       } else {
-        off = (int64_t)rc * rs + 8 * piece;
+        off = (int64_t)phys(rc) * rs + 8 * piece;
       }
       R.k[q2] = load_nt16(kb + off);
       R.v[q2] = load_nt16(vb + off);
@@ -216,6 +224,19 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
     // Raw scores; the scale log2(e)/sqrt(D) is positive, so the maximum is
     // taken on raw scores and the scale is folded into the exponent's fma.
     float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+    if constexpr (VAR) {
+      if (a.cap_T > 0.f) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sc[i] = cap_score(sc[i], a.cap_T, a.cap_invT);
+      }
+      if (a.window > 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (unattended(view, phys(t0 + 4 * r + i))) sc[i] = kNegInfM;
+          if (unattended(view, phys(t0 + 16 + 4 * r + i))) sc[4 + i] = kNegInfM;
+        }
+      }
+    }
     if (t0 + kTileT > t_end || t0 < t_begin) {  // the split's first (paged) or last, partial tile
       const int valid = t_end - t0;
       const int lo = t_begin - t0;
@@ -240,7 +261,9 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
         for (int nb = 0; nb < 8; ++nb) O[nb][i] *= ai;
       }
     }
-    const float nm = -m;
+    // With the sliding window a wave can meet tiles with no attended row before
+    // its first attended one (m still -inf): their weights are 0, not NaN.
+    const float nm = VAR && m == kNegInfM ? 0.f : -m;
     float p[8], ps = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -298,7 +321,7 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
   }
 
   if (own_new && prow == 0) {  // the appended slot (skipped if the map names no valid row/block)
-    const int64_t off = slot_offset_checked(a, b, h, L);
+    const int64_t off = slot_offset_checked(a, b, h, L0);
     if (off >= 0) {
       store16(reinterpret_cast<uint16_t*>(a.k_cache_w) + off + 8 * piece, kn);
       store16(reinterpret_cast<uint16_t*>(a.v_cache_w) + off + 8 * piece, vn);
@@ -316,7 +339,7 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
     if (hw + hl >= G) continue;
     const int hq = h * G + hw + hl;
     if (nact <= 1) {
-      const float inv = li > 0.f ? 1.f / li : 0.f;
+      const float inv = VAR || a.sink != nullptr || a.smooth ? finish_scale(a, hq, mi, li) : (li > 0.f ? 1.f / li : 0.f);
       uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)b * a.Hq + hq) * kD;
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) o[16 * nb + c] = f32_to_bf16_rne(O[nb][i] * inv);
@@ -336,8 +359,12 @@ hipError_t launch_attend_mfma_all(const AttnArgs& a, const Plan& p, hipStream_t 
   if (a.D != kD || a.G > 64) return hipErrorInvalidValue;
   AttnArgs arg = a;
   void* params[] = {&arg};
-  const void* fn = a.map_kind == GQA_MAP_PAGED ? reinterpret_cast<const void*>(&attend_mfma_all_kernel<true>)
-                                               : reinterpret_cast<const void*>(&attend_mfma_all_kernel<false>);
+  const bool var = a.window > 0 || a.cap_T > 0.f;  // in-loop variants (the sink is applied at the end)
+  const bool paged = a.map_kind == GQA_MAP_PAGED;
+  const void* fn = paged ? (var ? reinterpret_cast<const void*>(&attend_mfma_all_kernel<true, true>)
+                                : reinterpret_cast<const void*>(&attend_mfma_all_kernel<true, false>))
+                         : (var ? reinterpret_cast<const void*>(&attend_mfma_all_kernel<false, true>)
+                                : reinterpret_cast<const void*>(&attend_mfma_all_kernel<false, false>));
   return hipLaunchKernel(fn, dim3(p.grid), dim3(256), params, 0, s);
 }
 

@@ -47,6 +47,7 @@
 #include "cache_map.h"
 #include "device_common.h"
 #include "internal.h"
+#include "variants.h"
 
 namespace gqa {
 
@@ -122,9 +123,17 @@ struct State {
   f32x4 acc[8];
 };
 
-template <int KV>
+// Softmax variants inside a tile (VAR): soft-capped scores, and the rows of
+// the tile (from virtual slot t0) that the sliding window leaves unattended.
+struct TileVar {
+  const AttnArgs* a;
+  const SeqView* sv;
+  int t0;
+};
+
+template <int KV, bool VAR>
 __device__ __forceinline__ void tile_math(State& st, const u32x4 (&qf)[4], const Tile<KV>& t, int lo, int valid,
-                                          int r, float scale_log2) {
+                                          int r, float scale_log2, TileVar tvar = TileVar{nullptr, nullptr, 0}) {
   // Scores.
   u32x4 kf[4];
   if constexpr (KV == GQA_BF16) {
@@ -150,6 +159,18 @@ __device__ __forceinline__ void tile_math(State& st, const u32x4 (&qf)[4], const
     sv[2] *= quad_bcast<2>(t.ks);
     sv[3] *= quad_bcast<3>(t.ks);
   }
+  if constexpr (VAR) {
+    const AttnArgs& a = *tvar.a;
+    if (a.cap_T > 0.f) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[i] = cap_score(sv[i], a.cap_T, a.cap_invT);
+    }
+    if (a.window > 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (unattended(*tvar.sv, phys_slot(*tvar.sv, tvar.t0 + 4 * r + i))) sv[i] = kNegInfQ;
+    }
+  }
   if (lo > 0 || valid < 16) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -167,7 +188,9 @@ __device__ __forceinline__ void tile_math(State& st, const u32x4 (&qf)[4], const
 #pragma unroll
     for (int e = 0; e < 8; ++e) st.acc[e] *= alpha;
   }
-  const float nm = -st.m;
+  // With the sliding window a wave can meet tiles with no attended row before
+  // its first attended one (m still -inf): their weights are 0, not NaN.
+  const float nm = VAR && st.m == kNegInfQ ? 0.f : -st.m;
   float p[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(sv[i], scale_log2, nm));
@@ -196,7 +219,7 @@ __device__ __forceinline__ void tile_math(State& st, const u32x4 (&qf)[4], const
   });
 }
 
-template <int KV, int NW, bool PAGED>
+template <int KV, int NW, bool PAGED, bool VAR>
 __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
   static_assert(!(PAGED && KV == GQA_I8), "int8 caches are dense");
   __shared__ float sm_o[NW][16][kDq];
@@ -218,14 +241,20 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
   const int L = a.lengths[b];
   int n = L + a.len_offset;
   n = n < 0 ? 0 : (n > a.S ? a.S : n);
+  // Slots are walked in the sliding window's virtual order (the identity
+  // without a window); `nv` virtual slots, the new token is the last.
+  SeqView view{n, n, 0, 0, 0};
+  if constexpr (VAR) view = seq_view(a, b, n);
+  const int nv = view.nv;
+  const int Lv = L - view.gap;
   const int t_begin = split * a.split_tokens;
-  const int t_end = min(t_begin + a.split_tokens, n);
-  const int nact = n == 0 ? 0 : min(a.nsplit, (n + a.split_tokens - 1) / a.split_tokens);
+  const int t_end = min(t_begin + a.split_tokens, nv);
+  const int nact = nv == 0 ? 0 : min(a.nsplit, (nv + a.split_tokens - 1) / a.split_tokens);
   if (split >= max(nact, 1)) return;
 
   // Fused step (bf16 caches only): slot L is taken from k_new / v_new.
-  const bool own_new = KV == GQA_BF16 && a.k_new != nullptr && L >= t_begin && L < t_end;
-  const int t_cache_end = own_new ? L : t_end;
+  const bool own_new = KV == GQA_BF16 && a.k_new != nullptr && Lv >= t_begin && Lv < t_end;
+  const int t_cache_end = own_new ? Lv : t_end;
 
   constexpr int EB = KV == GQA_BF16 ? 2 : 1;  // bytes per cached element
   const int64_t base = PAGED ? 0 : row_head_offset(a, b, h);  // dense or slot-indexed row
@@ -239,7 +268,7 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
   int tv = t_begin;
   if (PAGED) {
     tv = t_begin & ~15;
-  } else if (rs == kDq) {
+  } else if (rs == kDq && !VAR) {
     const uint64_t row = (reinterpret_cast<uintptr_t>(a.k_cache) / (kDq * EB)) + (uint64_t)(base / kDq + t_begin);
     tv = t_begin - (int)(row & 15);
   }
@@ -282,19 +311,29 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
   auto tile_origin = [&](int t0) { return max(min(t0, last16), tv); };
   auto entry = [&](int t0) -> int32_t {
     if (!PAGED) return 0;
-    return a.map[(int64_t)b * a.max_blocks + tile_origin(t0) / a.bs];
+    return a.map[(int64_t)b * a.max_blocks + (VAR ? phys_slot(view, tile_origin(t0)) : tile_origin(t0)) / a.bs];
   };
+  // Virtual slot -> physical slot.  Paged tiles start on multiples of 16 and
+  // the window's split point and gap are multiples of 16, so a whole paged
+  // tile moves by the same amount (its block is that of its physical origin).
+  auto phys = [&](int t) { return VAR ? phys_slot(view, t) : t; };
   auto load_tile = [&](int t0, Tile<KV>& t, int32_t blk) {
     const char* kt = kl;
     const char* vt = vl;
-    int tc = 0;
+    int tc = 0;       // virtual origin of the tile's block (paged)
+    int shift = 0;    // physical - virtual for the whole tile (paged)
     if (PAGED) {
       tc = tile_origin(t0);
-      const int64_t off = (block_head_offset(a, blk, h) + (int64_t)(tc % a.bs) * rs) * EB;
+      shift = phys(tc) - tc;
+      const int64_t off = (block_head_offset(a, blk, h) + (int64_t)((tc + shift) % a.bs) * rs) * EB;
       kt = reinterpret_cast<const char*>(a.k_cache) + off + 16 * r;
       vt = reinterpret_cast<const char*>(a.v_cache) + off + 16 * c;
     }
-    const uint32_t rk = (uint32_t)(max(min(t0 + c, w1 - 1), t_begin) - tc);
+    auto row = [&](int tvirt) -> uint32_t {  // row offset from the tile's block (paged) or slot 0
+      const int cl = max(min(tvirt, w1 - 1), t_begin);
+      return (uint32_t)(PAGED ? cl - tc : phys(cl));
+    };
+    const uint32_t rk = row(t0 + c);
     const char* p = kt + (uint64_t)rk * rsb;
     if constexpr (KV == GQA_BF16) {
 #pragma unroll
@@ -305,14 +344,14 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t rv = (uint32_t)(max(min(t0 + 4 * r + i, w1 - 1), t_begin) - tc);
+      const uint32_t rv = row(t0 + 4 * r + i);
       if constexpr (KV == GQA_BF16)
         t.v[i] = load_nt16(vt + (uint64_t)rv * rsb);
       else
         t.v[i] = load_nt8(vt + (uint64_t)rv * rsb);
     }
     if constexpr (KV == GQA_I8) {
-      const int64_t rsc = sbase + (int64_t)max(min(t0 + 4 * r + (c & 3), w1 - 1), t_begin) * sst;
+      const int64_t rsc = sbase + (int64_t)row(t0 + 4 * r + (c & 3)) * sst;
       t.ks = __uint_as_float(load_nt4(a.k_scale + rsc));
       t.vs = __uint_as_float(load_nt4(a.v_scale + rsc));
     }
@@ -342,7 +381,7 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
   int32_t eB = entry(w0 + 16), eA = entry(w0 + 32);  // table entries of the first pair's successors
   load_tile(w0, ta, entry(w0));
   if constexpr (KV == GQA_BF16) {
-    if (new_here) tile_math<KV>(st, qf, tn, 0, 1, r, a.scale_log2);
+    if (new_here) tile_math<KV, VAR>(st, qf, tn, 0, 1, r, a.scale_log2, TileVar{&a, &view, Lv});
   }
   if (w0 < w1) {
     const int nt = (w1 - w0 + 15) >> 4;
@@ -350,14 +389,15 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
     for (int it = 0; it < nt / 2; ++it) {
       const int32_t nB = entry(t0 + 48), nA = entry(t0 + 64);
       load_tile(t0 + 16, tb, eB);
-      tile_math<KV>(st, qf, ta, t_begin - t0, w1 - t0, r, a.scale_log2);
+      tile_math<KV, VAR>(st, qf, ta, t_begin - t0, w1 - t0, r, a.scale_log2, TileVar{&a, &view, t0});
       load_tile(t0 + 32, ta, eA);  // past w1 it re-reads row w1 - 1
-      tile_math<KV>(st, qf, tb, t_begin - t0 - 16, w1 - t0 - 16, r, a.scale_log2);
+      tile_math<KV, VAR>(st, qf, tb, t_begin - t0 - 16, w1 - t0 - 16, r, a.scale_log2,
+                         TileVar{&a, &view, t0 + 16});
       eB = nB;
       eA = nA;
       t0 += 32;
     }
-    if (nt & 1) tile_math<KV>(st, qf, ta, t_begin - t0, w1 - t0, r, a.scale_log2);
+    if (nt & 1) tile_math<KV, VAR>(st, qf, ta, t_begin - t0, w1 - t0, r, a.scale_log2, TileVar{&a, &view, t0});
   }
   if constexpr (KV == GQA_BF16) {
     if (new_here) {
@@ -403,7 +443,8 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
     const int hq = h * G + g;
     if (nact <= 1) {
       reinterpret_cast<uint16_t*>(a.out)[((int64_t)b * a.Hq + hq) * kDq + d] =
-          f32_to_bf16_rne(Lsum > 0.f ? O / Lsum : 0.f);
+          f32_to_bf16_rne(VAR || a.sink != nullptr || a.smooth ? finish_row(a, hq, M, O, Lsum)
+                                                              : (Lsum > 0.f ? O / Lsum : 0.f));
     } else {
       const int64_t pi = ((int64_t)b * a.Hq + hq) * a.nsplit + split;
       a.part_o[pi * kDq + d] = O;
@@ -427,15 +468,19 @@ const bool kHaveMfmaQkI8 = true;
 hipError_t launch_attend_mfma_qk(const AttnArgs& a, const Plan& p, hipStream_t s) {
   constexpr int NW = 4;
   if (a.D != qkv::kDq || a.G > 16 || p.block != 64 * NW) return hipErrorInvalidValue;
+  const bool var = a.window > 0 || a.cap_T > 0.f;  // in-loop variants (the sink is applied at the end)
   const void* fn;
   if (a.kv_dtype == GQA_I8) {
     if (a.map_kind != 0 || a.k_new != nullptr || a.k_scale == nullptr || a.v_scale == nullptr)
       return hipErrorInvalidValue;
-    fn = reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_I8, NW, false>);
+    fn = var ? reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_I8, NW, false, true>)
+             : reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_I8, NW, false, false>);
   } else if (a.map_kind == GQA_MAP_PAGED) {
-    fn = reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_BF16, NW, true>);
+    fn = var ? reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_BF16, NW, true, true>)
+             : reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_BF16, NW, true, false>);
   } else {
-    fn = reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_BF16, NW, false>);
+    fn = var ? reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_BF16, NW, false, true>)
+             : reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_BF16, NW, false, false>);
   }
   AttnArgs arg = a;
   void* params[] = {&arg};

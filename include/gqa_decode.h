@@ -301,15 +301,48 @@ typedef struct {
   float norm_eps;
 } gqa_rope_t;
 
+/* ---------------------------------------------------------------------------
+ * Softmax variants (CLIKA runtime, "groupQueryAttention" API page, parameter
+ * list and operator summary: head_sink, smooth_softmax, softcap,
+ * sliding_window, kept_prefix).  For sequence b with n attended-valid slots
+ * (lengths[b] + 1 for a step, lengths[b] for attend) the query is the newest
+ * token, slot n - 1:
+ *   window       : W > 0 keeps the slots j >= n - W (the last W, the new token's
+ *                  own included) plus the kept prefix j < P; 0 keeps every slot.
+ *   kept_prefix  : P >= 0 (negative: GQA_ERR_INVALID_ARGUMENT), used with a window
+ *                  only (a prefix without a window is GQA_ERR_INVALID_ARGUMENT);
+ *   kept_prefix_per_seq : int32 (B,) device, one P per sequence, or NULL (kept_prefix
+ *                  for all); negative device values count as 0.
+ *   softcap      : c > 0 maps each scaled score s = q.k / sqrt(D) to c tanh(s / c)
+ *                  before the softmax; 0 leaves it.
+ *   sink         : float32 (Hq,) device, a per-query-head logit added to the
+ *                  softmax denominator only: w_j = e^(s_j) / (sum_i e^(s_i) + e^(sink));
+ *                  NULL: none.
+ *   smooth       : 1 adds a zero logit for every head (a sink of 0); not combined
+ *                  with `sink` (GQA_ERR_INVALID_ARGUMENT).
+ * With no attended slot the output is zeros.  Sink and prefix arrays must be
+ * 4-byte aligned and overlap nothing the call writes.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  const float* sink;
+  int32_t smooth;
+  float softcap;
+  int32_t window;
+  int32_t kept_prefix;
+  const int32_t* kept_prefix_per_seq;
+} gqa_softmax_t;
+
 /* Options of the _ex calls; every member may be NULL (the plain behaviour).
- *   map    : mapped caches, as in the _mapped calls
- *   scales : int8 caches (desc->kv_dtype = GQA_I8), as in the _q8 calls; not
- *            combined with map (GQA_ERR_UNSUPPORTED)
- *   rope   : rotary encoding (append and step only) */
+ *   map     : mapped caches, as in the _mapped calls
+ *   scales  : int8 caches (desc->kv_dtype = GQA_I8), as in the _q8 calls; not
+ *             combined with map (GQA_ERR_UNSUPPORTED)
+ *   rope    : rotary encoding (append and step only)
+ *   softmax : softmax variants (attend and step) */
 typedef struct {
   const gqa_cache_map_t* map;
   const gqa_kv_scales_t* scales;
   const gqa_rope_t* rope;
+  const gqa_softmax_t* softmax;
 } gqa_decode_opts_t;
 
 /* Workspace of an attend/step call with these options (the plain size plus the

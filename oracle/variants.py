@@ -34,6 +34,7 @@ import numpy as np
 
 from .mapped import append_mapped, mapped_rows
 from .oracle import append, decode, kv_rows
+from .quant import append_q8, dequantize
 
 __all__ = ["attended_slots", "attend_variant_one", "attend_variants", "step_variants"]
 
@@ -74,12 +75,18 @@ def _sink_of(sink, smooth, hq):
     return None if sink is None else float(sink[hq])
 
 
+def _scale_rows(scale, layout, b, h, n):
+    return scale[b, h, :n] if layout == "BHSD" else scale[b, :n, h]
+
+
 def attend_variants(q, q_dtype: str, k_cache, v_cache, kv_dtype: str, lengths, layout: str, num_q_heads: int,
                     num_kv_heads: int, sink=None, smooth: bool = False, softcap: float = 0.0, window: int = 0,
-                    prefix=0, kind: str | None = None, mapping=None, bs=None) -> np.ndarray:
+                    prefix=0, kind: str | None = None, mapping=None, bs=None, scales=None) -> np.ndarray:
     """Length-masked GQA attention with the variants, float64 (B, Hq, D).
     ``prefix`` is one value or one per sequence; ``kind``/``mapping``/``bs``
-    select a mapped cache as in ``oracle.mapped``."""
+    select a mapped cache as in ``oracle.mapped``; ``kv_dtype`` "i8" takes
+    int8 caches read as code * row scale with ``scales = (k_scale, v_scale)``
+    (``oracle.quant`` storage)."""
     B, Hq, D = q.shape
     Hkv = num_kv_heads
     if Hq != num_q_heads or Hq % Hkv:
@@ -99,16 +106,29 @@ def attend_variants(q, q_dtype: str, k_cache, v_cache, kv_dtype: str, lengths, l
             else:
                 Kr = mapped_rows(k_cache, kind, layout, mapping, b, h, n, bs)
                 Vr = mapped_rows(v_cache, kind, layout, mapping, b, h, n, bs)
-            K, V = decode(Kr, kv_dtype)[idx], decode(Vr, kv_dtype)[idx]
+            if kv_dtype == "i8":
+                K = dequantize(Kr, _scale_rows(scales[0], layout, b, h, n))[idx]
+                V = dequantize(Vr, _scale_rows(scales[1], layout, b, h, n))[idx]
+            else:
+                K, V = decode(Kr, kv_dtype)[idx], decode(Vr, kv_dtype)[idx]
             for hq in range(h * G, (h + 1) * G):
                 out[b, hq] = attend_variant_one(qf[b, hq], K, V, _sink_of(sink, smooth, hq), softcap)
     return out
 
 
 def step_variants(q, q_dtype: str, k_cache, v_cache, k_new, v_new, kv_dtype: str, lengths, layout: str,
-                  num_q_heads: int, num_kv_heads: int, kind: str | None = None, mapping=None, bs=None, **variants):
+                  num_q_heads: int, num_kv_heads: int, kind: str | None = None, mapping=None, bs=None, scales=None,
+                  **variants):
     """Append at ``lengths[b]``, then attend with the variants over
-    ``lengths[b] + 1`` slots.  Returns (out, k_cache_after, v_cache_after)."""
+    ``lengths[b] + 1`` slots.  Returns (out, k_cache_after, v_cache_after);
+    int8 caches ("i8", new rows in ``q_dtype``, ``scales = (k_scale, v_scale)``)
+    return (out, k_cache, v_cache, k_scale, v_scale)."""
+    if kv_dtype == "i8":
+        kc, vc, ks, vs = append_q8(k_cache, v_cache, scales[0], scales[1], k_new, v_new, q_dtype, lengths, layout)
+        n = np.asarray(lengths).astype(np.int64) + 1
+        out = attend_variants(q, q_dtype, kc, vc, "i8", n, layout, num_q_heads, num_kv_heads, scales=(ks, vs),
+                              **variants)
+        return out, kc, vc, ks, vs
     if kind is None:
         kc, vc = append(k_cache, v_cache, k_new, v_new, lengths, layout)
     else:

@@ -496,24 +496,24 @@ BAD_ROPES = [
 @pytest.mark.parametrize("kw,status", BAD_ROPES)
 def test_bad_rope_refused(kw, status):
     r = _rope(**kw)
-    o = _lib.OptsT(None, None, ctypes.pointer(r))
+    o = _lib.OptsT(None, None, ctypes.pointer(r), None)
     assert _ex_calls(desc(), o) == [status, status]
 
 
 def test_rope_needs_even_head_dim_and_no_norm_on_int8():
     r = _rope()
-    o = _lib.OptsT(None, None, ctypes.pointer(r))
+    o = _lib.OptsT(None, None, ctypes.pointer(r), None)
     assert _ex_calls(desc(head_dim=7, kv_dtype=g.F32, qo_dtype=g.F32), o) == [INVALID, INVALID]
     sc = _scales()
     r = _rope(k_norm_gain=FAKE + 13 * GAP, norm_eps=1e-6)
-    o = _lib.OptsT(None, ctypes.pointer(sc), ctypes.pointer(r))
+    o = _lib.OptsT(None, ctypes.pointer(sc), ctypes.pointer(r), None)
     assert _ex_calls(desc(kv_dtype=g.I8), o) == [UNSUPPORTED, UNSUPPORTED]
 
 
 def test_attend_refuses_rope_and_ex_matches_plain_refusals():
     L = g.lib()
     r = _rope()
-    o = _lib.OptsT(None, None, ctypes.pointer(r))
+    o = _lib.OptsT(None, None, ctypes.pointer(r), None)
     p = _attend_ptrs()
     d = desc()
     assert L.gqa_decode_attend_ex(ctypes.byref(d), ctypes.byref(o), p["q"], p["kc"], p["vc"], p["lens"], p["out"],
@@ -532,7 +532,7 @@ def test_workspace_size_ex_adds_the_rotated_q():
         n = ctypes.c_size_t(0)
         assert L.gqa_decode_workspace_size_ex(ctypes.byref(d), None, ctypes.byref(n)) == OK and n.value == plain
         r = _rope()
-        o = _lib.OptsT(None, None, ctypes.pointer(r))
+        o = _lib.OptsT(None, None, ctypes.pointer(r), None)
         assert L.gqa_decode_workspace_size_ex(ctypes.byref(d), ctypes.byref(o), ctypes.byref(n)) == OK
         eqo = 4 if d.qo_dtype == g.F32 else 2
         assert n.value == -(-plain // 256) * 256 + d.batch * d.num_q_heads * d.head_dim * eqo
@@ -546,7 +546,78 @@ def test_ex_empty_batch_is_a_noop():
     L = g.lib()
     d = desc(batch=0)
     r = _rope()
-    o = _lib.OptsT(None, None, ctypes.pointer(r))
+    o = _lib.OptsT(None, None, ctypes.pointer(r), None)
     assert L.gqa_decode_step_ex(ctypes.byref(d), ctypes.byref(o), None, None, None, None, None, None, None, None, 0,
                                 None) == OK
     assert L.gqa_decode_append_ex(ctypes.byref(d), ctypes.byref(o), None, None, None, None, None, None) == OK
+
+
+# ---------------------------------------------------------------------------
+# Softmax variants: refusals before any launch.
+# ---------------------------------------------------------------------------
+def _smx(**kw):
+    base = dict(sink=None, smooth=0, softcap=0.0, window=0, kept_prefix=0, kept_prefix_per_seq=None)
+    base.update(kw)
+    return _lib.SoftmaxT(base["sink"], base["smooth"], base["softcap"], base["window"], base["kept_prefix"],
+                         base["kept_prefix_per_seq"])
+
+
+def _attend_step_ex(d, o, p=None):
+    L = g.lib()
+    p = p or _attend_ptrs()
+    return [
+        L.gqa_decode_attend_ex(ctypes.byref(d), ctypes.byref(o), p["q"], p["kc"], p["vc"], p["lens"], p["out"],
+                               p["ws"], 1 << 30, None),
+        L.gqa_decode_step_ex(ctypes.byref(d), ctypes.byref(o), p["q"], p["kc"], p["vc"], p["kn"], p["vn"], p["lens"],
+                             p["out"], p["ws"], 1 << 30, None),
+    ]
+
+
+BAD_SOFTMAX = [
+    dict(smooth=2),
+    dict(smooth=1, sink=FAKE + 14 * GAP),            # a sink and smooth softmax together
+    dict(softcap=-1.0),
+    dict(softcap=float("nan")),
+    dict(softcap=float("inf")),
+    dict(window=-3),
+    dict(window=8, kept_prefix=-1),
+    dict(kept_prefix=4),                              # a prefix without a window
+    dict(kept_prefix_per_seq=FAKE + 15 * GAP),
+    dict(sink=FAKE + 14 * GAP + 2),                   # misaligned
+    dict(window=8, kept_prefix_per_seq=FAKE + 15 * GAP + 1),
+    dict(sink=FAKE + 4 * GAP),                        # the sink inside the output
+    dict(window=4, kept_prefix_per_seq=FAKE + 5 * GAP),  # the prefixes inside the workspace
+]
+
+
+@pytest.mark.parametrize("kw", BAD_SOFTMAX, ids=[str(k) for k in BAD_SOFTMAX])
+def test_bad_softmax_refused(kw):
+    v = _smx(**kw)
+    o = _lib.OptsT(None, None, None, ctypes.pointer(v))
+    assert _attend_step_ex(desc(), o) == [INVALID, INVALID]
+
+
+def test_softmax_arrays_may_share_read_only_inputs_but_not_written_caches():
+    """A sink stored inside the K cache is refused by the step, which writes
+    the cache (attend, which only reads it, would accept it)."""
+    L = g.lib()
+    v = _smx(sink=FAKE + GAP)
+    o = _lib.OptsT(None, None, None, ctypes.pointer(v))
+    p = _attend_ptrs()
+    d = desc()
+    assert L.gqa_decode_step_ex(ctypes.byref(d), ctypes.byref(o), p["q"], p["kc"], p["vc"], p["kn"], p["vn"],
+                                p["lens"], p["out"], p["ws"], 1 << 30, None) == INVALID
+
+
+def test_append_refuses_softmax_options_and_empty_batch_is_a_noop():
+    L = g.lib()
+    v = _smx(window=4)
+    o = _lib.OptsT(None, None, None, ctypes.pointer(v))
+    p = _attend_ptrs()
+    assert L.gqa_decode_append_ex(ctypes.byref(desc()), ctypes.byref(o), p["kc"], p["vc"], p["kn"], p["vn"],
+                                  p["lens"], None) == INVALID
+    d0 = desc(batch=0)
+    assert L.gqa_decode_attend_ex(ctypes.byref(d0), ctypes.byref(o), None, None, None, None, None, None, 0,
+                                  None) == OK
+    assert L.gqa_decode_step_ex(ctypes.byref(d0), ctypes.byref(o), None, None, None, None, None, None, None, None, 0,
+                                None) == OK

@@ -132,3 +132,24 @@ def test_step_appends_then_windows_over_the_new_token():
         assert np.array_equal(out[b], np.repeat(vn[b].astype(np.float64), Hq, axis=0))
     ref, ek, ev = oracle.step(q, "f32", kc, vc, kn, vn, "f32", L, "BHSD", Hq, Hkv)
     assert rk.tobytes() == ek.tobytes() and rv.tobytes() == ev.tobytes()
+
+
+def test_int8_variants_reduce_to_the_int8_oracle():
+    rng = np.random.default_rng(6)
+    B, Hq, Hkv, D, S = 2, 4, 2, 8, 9
+    q = (rng.standard_normal((B, Hq, D)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    kc = rng.integers(-127, 128, (B, Hkv, S, D)).astype(np.int8)
+    vc = rng.integers(-127, 128, (B, Hkv, S, D)).astype(np.int8)
+    ks = rng.uniform(0.01, 0.03, (B, Hkv, S)).astype(np.float32)
+    vs = rng.uniform(0.01, 0.03, (B, Hkv, S)).astype(np.float32)
+    kn = (rng.standard_normal((B, Hkv, D)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    vn = (rng.standard_normal((B, Hkv, D)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    L = np.array([3, 8], np.int32)
+    got = V.step_variants(q, "bf16", kc, vc, kn, vn, "i8", L, "BHSD", Hq, Hkv, scales=(ks, vs), window=S)
+    ref = oracle.step_q8(q, "bf16", kc, vc, ks, vs, kn, vn, L, "BHSD", Hq, Hkv)
+    for a, b in zip(got, ref):
+        assert np.allclose(a, b, rtol=1e-13, atol=1e-15) if a.dtype == np.float64 else np.array_equal(a, b)
+    w1 = V.step_variants(q, "bf16", kc, vc, kn, vn, "i8", L, "BHSD", Hq, Hkv, scales=(ks, vs), window=1)[0]
+    for b in range(B):
+        row = oracle.dequantize(ref[2][b, :, L[b]], ref[4][b, :, L[b]])       # the appended value rows
+        assert np.allclose(w1[b], np.repeat(row, Hq // Hkv, axis=0), rtol=1e-13)
