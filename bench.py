@@ -56,7 +56,7 @@ def traffic_from_profiles(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, inp, budget_s=12.0, rope=None):
+def cpu_baseline(w, inp, budget_s=12.0, rope=None, variants=None, window=0, prefix=0):
     """The float64 oracle on this host's cores over a bounded sample of the same
     inputs: whole sequences (all query heads), repeated until about budget_s
     seconds of CPU work, scaled to GB/s with the same byte formula."""
@@ -77,7 +77,11 @@ def cpu_baseline(w, inp, budget_s=12.0, rope=None):
 
     def run(st, nb):
         t0 = time.perf_counter()
-        if rope is not None and q8:
+        if variants is not None and rope is None:
+            oracle.step_variants(st["q"], w.qo_dtype, st["k_cache"], st["v_cache"], st["k_new"], st["v_new"],
+                                 w.kv_dtype, L[:nb], w.layout, w.Hq, w.Hkv,
+                                 scales=(st["k_scale"], st["v_scale"]) if q8 else None, **variants)
+        elif rope is not None and q8:
             oracle.step_q8_rope(st["q"], w.qo_dtype, st["k_cache"], st["v_cache"], st["k_scale"], st["v_scale"],
                                 st["k_new"], st["v_new"], L[:nb], w.layout, w.Hq, w.Hkv, *rope)
         elif rope is not None:
@@ -100,13 +104,15 @@ def cpu_baseline(w, inp, budget_s=12.0, rope=None):
         t += run(st, nb)
         reps += 1
     sub = W.Workload(**{**w.__dict__, "B": nb})
-    nbytes = W.algorithmic_bytes(sub, L[:nb]) * reps
+    nbytes = W.algorithmic_bytes(sub, L[:nb], window, prefix) * reps
     gbs = nbytes / t / 1e9
     fn = ("step_q8" if q8 else "step") if rope is None else ("step_q8_rope" if q8 else "step_rope")
+    if variants is not None and rope is None:
+        fn = "step_variants"
     sample = (f"oracle.{fn} over sequences 0..{nb - 1} of {w.B} (all {w.Hq} query heads) of the same inputs, "
               f"{reps} repetition(s), {t:.1f} s")
     return {"value": round(gbs, 6), "unit": "GB/s", "cores": threads, "kind": "oracle", "sample": sample,
-            "steps_per_sec_equiv": round(gbs * 1e9 / W.algorithmic_bytes(w, L), 6),
+            "steps_per_sec_equiv": round(gbs * 1e9 / W.algorithmic_bytes(w, L, window, prefix), 6),
             "host_cpus": os.cpu_count(), "affinity": len(os.sched_getaffinity(0))}
 
 
@@ -137,6 +143,10 @@ def main():
                          "(the step quantizes the new rows)")
     ap.add_argument("--rope", default="none", choices=["none", "half", "interleaved"],
                     help="rotate q and the new key with rotary planes in the append (positions = lengths)")
+    ap.add_argument("--window", type=int, default=0, help="sliding window of the softmax (0: none)")
+    ap.add_argument("--kept-prefix", type=int, default=0, help="slots kept beside the window")
+    ap.add_argument("--softcap", type=float, default=0.0, help="cap of the scaled scores (0: none)")
+    ap.add_argument("--sink", action="store_true", help="a per-query-head sink logit")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="only run a plain copy of this many MiB (counter calibration) and exit")
@@ -168,7 +178,17 @@ def main():
     else:
         inp = W.make_inputs(w, dev)
     L = inp["lengths"].cpu().numpy()
-    nbytes = W.algorithmic_bytes(w, L)
+    nbytes = W.algorithmic_bytes(w, L, args.window, args.kept_prefix)
+    n_att = L.astype("int64") + 1
+    if args.window > 0:
+        wv = n_att.clip(max=args.window)
+        n_att = wv + (n_att - wv).clip(max=args.kept_prefix)
+    smx, smx_np = None, None
+    if args.window or args.softcap or args.sink:
+        sink = torch.randn(w.Hq, generator=torch.Generator().manual_seed(1)).to(dev) if args.sink else None
+        smx = g.Softmax(sink=sink, softcap=args.softcap, window=args.window, kept_prefix=args.kept_prefix)
+        smx_np = dict(sink=None if sink is None else sink.cpu().numpy(), softcap=args.softcap, window=args.window,
+                      prefix=args.kept_prefix)
     desc = g.desc_for(inp["q"], inp["k_cache"], w.layout, args.num_splits)
     plan = g.get_plan(desc)
     kind, table = None, None
@@ -198,21 +218,24 @@ def main():
     rope = None
     wsb = plan["workspace_bytes"]
     if args.rope != "none":
-        import ctypes
         cos, sin = W.rope_tables(w.capacity, w.D, dev)
         rope = g.Rope(cos, sin, args.rope)
-        rs = rope.struct()
-        wsb = g.workspace_size_ex(desc, g.OptsT(None, None, ctypes.pointer(rs)))
+    if rope is not None or smx is not None:
+        import ctypes
+        rs = rope.struct() if rope is not None else None
+        ss = smx.struct() if smx is not None else None
+        wsb = g.workspace_size_ex(desc, g.OptsT(None, None, ctypes.pointer(rs) if rs is not None else None,
+                                                ctypes.pointer(ss) if ss is not None else None))
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
     out = torch.empty_like(inp["q"])
 
     def step(i):
         kc, vc = caches[i % R][:2]
-        if rope is not None:
+        if rope is not None or smx is not None:
             ks, vs = caches[i % R][2:] if q8 else (None, None)
             g.step_ex(inp["q"], kc, vc, inp["k_new"], inp["v_new"], inp["lengths"], layout=w.layout, table=table,
-                      kind=kind, table_host=table_host if kind else None, k_scale=ks, v_scale=vs, rope=rope, out=out,
-                      workspace=ws, num_splits=args.num_splits)
+                      kind=kind, table_host=table_host if kind else None, k_scale=ks, v_scale=vs, rope=rope,
+                      softmax=smx, out=out, workspace=ws, num_splits=args.num_splits)
         elif q8:
             ks, vs = caches[i % R][2:]
             g.step_q8(inp["q"], kc, vc, ks, vs, inp["k_new"], inp["v_new"], inp["lengths"], layout=w.layout, out=out,
@@ -241,7 +264,8 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         rope_np = None if rope is None else (rope.cos.cpu().numpy(), rope.sin.cpu().numpy(), args.rope)
-        cpu = cpu_baseline(w, inp_dense, rope=rope_np)   # the dense oracle on the same logical caches
+        cpu = cpu_baseline(w, inp_dense, rope=rope_np, variants=smx_np, window=args.window,
+                           prefix=args.kept_prefix)   # the dense oracle on the same logical caches
 
     kv = {"bf16": "bf16", "f32": "f32", "i8": "i8+f32 row scales"}[w.kv_dtype]
     line = {
@@ -260,14 +284,15 @@ def main():
         "data": "synthetic",
         "steps_per_sec": round(1000.0 / ms, 2),
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
-        "config": {"workload": w.name, "cache": args.cache, "rope": args.rope, "batch": w.B, "num_q_heads": w.Hq, "num_kv_heads": w.Hkv, "head_dim": w.D,
+        "config": {"workload": w.name, "cache": args.cache, "rope": args.rope, "window": args.window,
+                   "kept_prefix": args.kept_prefix, "softcap": args.softcap, "sink": args.sink, "batch": w.B, "num_q_heads": w.Hq, "num_kv_heads": w.Hkv, "head_dim": w.D,
                    "capacity": w.capacity, "layout": w.layout, "kv_dtype": w.kv_dtype, "qo_dtype": w.qo_dtype,
-                   "tokens_attended": int((L + 1).sum()), "algorithmic_bytes_per_step": nbytes,
+                   "tokens_attended": int(n_att.sum()), "algorithmic_bytes_per_step": nbytes,
                    "cache_rotation": R, "plan": plan},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profiles(w.name)
-                     if args.cache == "dense" and not q8 and rope is None else None,
+                     if args.cache == "dense" and not q8 and rope is None and smx is None else None,
                      "per": "one gqa_decode_step call (attention kernel + split combine), HIP events over the "
                             "timed region"},
         "cpu_baseline": cpu,

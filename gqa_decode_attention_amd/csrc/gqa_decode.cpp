@@ -74,11 +74,14 @@ int32_t choose_kernel(const gqa_decode_desc_t* d) {
 }
 
 // Plan: a pure function of the descriptor.
-gqa_status_t make_plan(const gqa_decode_desc_t* d, Plan* p) {
+// `span` > 0 bounds the slots any sequence walks (a sliding window with a
+// host-known prefix); the splits then cover [0, span) instead of the capacity.
+gqa_status_t make_plan(const gqa_decode_desc_t* d, Plan* p, int64_t span = 0) {
   gqa_status_t st = check_desc(d);
   if (st != GQA_OK) return st;
   std::memset(p, 0, sizeof(*p));
-  const int64_t B = d->batch, Hq = d->num_q_heads, Hkv = d->num_kv_heads, S = d->capacity, D = d->head_dim;
+  const int64_t B = d->batch, Hq = d->num_q_heads, Hkv = d->num_kv_heads, D = d->head_dim;
+  const int64_t S = span > 0 ? std::min<int64_t>(span, d->capacity) : d->capacity;
   const int64_t G = Hq / Hkv;
   p->kernel = choose_kernel(d);
   p->head_chunks = p->kernel == GQA_KERNEL_GENERIC ? (int32_t)((G + kGenericHeadChunk - 1) / kGenericHeadChunk) : 1;
@@ -442,6 +445,13 @@ gqa_status_t check_softmax_ptrs(const gqa_decode_desc_t* d, const gqa_softmax_t*
       if (overlap(w, x)) return GQA_ERR_INVALID_ARGUMENT;
   return GQA_OK;
 }
+// Slots a sequence walks at most: with a window W and a kept prefix P known on
+// the host, the virtual range is below W + P + 32 (0: no bound).
+int64_t walk_span(const gqa_softmax_t* v) {
+  if (v == nullptr || v->window <= 0 || v->kept_prefix < 0 || v->kept_prefix_per_seq != nullptr) return 0;
+  return (int64_t)v->window + v->kept_prefix + 32;
+}
+
 void fill_softmax(const gqa_decode_desc_t* d, const gqa_softmax_t* v, AttnArgs* a) {
   if (v == nullptr) return;
   a->sink = v->sink;
@@ -527,10 +537,10 @@ gqa_status_t do_append(const gqa_decode_desc_t* desc, const gqa_decode_opts_t* o
 gqa_status_t do_attend(const gqa_decode_desc_t* desc, const gqa_decode_opts_t* opts, const void* q, void* k_cache,
                        void* v_cache, const void* k_new, const void* v_new, const int32_t* lengths, void* out,
                        void* workspace, size_t workspace_bytes, void* stream, bool step) {
-  Plan p;
-  gqa_status_t st = make_plan(desc, &p);
-  if (st != GQA_OK) return st;
   const gqa_decode_opts_t* o = opts ? opts : &kNoOpts;
+  Plan p;
+  gqa_status_t st = make_plan(desc, &p, walk_span(o->softmax));
+  if (st != GQA_OK) return st;
   const gqa_cache_map_t* map = o->map;
   const gqa_kv_scales_t* sc = o->scales;
   const gqa_rope_t* rope = o->rope;
@@ -752,11 +762,12 @@ gqa_status_t gqa_decode_workspace_size_ex(const gqa_decode_desc_t* desc, const g
                                           size_t* bytes) {
   try {
     if (bytes == nullptr) return GQA_ERR_INVALID_ARGUMENT;
-    Plan p;
-    gqa_status_t st = make_plan(desc, &p);
-    if (st != GQA_OK) return st;
     const gqa_decode_opts_t* o = opts ? opts : &kNoOpts;
+    Plan p;
+    gqa_status_t st = make_plan(desc, &p, walk_span(o->softmax));
+    if (st != GQA_OK) return st;
     if ((st = check_rope(desc, o->rope)) != GQA_OK) return st;
+    if ((st = check_softmax(desc, o->softmax)) != GQA_OK) return st;
     *bytes = workspace_total(desc, p, o);
     return GQA_OK;
   } catch (...) {

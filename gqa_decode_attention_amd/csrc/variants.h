@@ -39,10 +39,11 @@ __device__ __forceinline__ bool unattended(const SeqView& v, int tp) { return tp
 
 // Soft-capping of a raw score s = q.k: with T = cap * sqrt(D) (so that the
 // scaled score s / sqrt(D) becomes cap * tanh(s / (sqrt(D) cap))), returns
-// T tanh(s / T); tanh(x) = 1 - 2 / (e^(2x) + 1), exact limits +-1.
+// T tanh(s / T); tanh(x) = 1 - 2 / (e^(2x) + 1) with the hardware exponential
+// and reciprocal (about 1 ulp each), exact limits +-1.
 __device__ __forceinline__ float cap_score(float s, float T, float invT) {
   const float e = fast_exp2(s * invT * 2.8853900817779268f);  // e^(2x), 2 log2(e)
-  return T * (1.f - 2.f / (e + 1.f));
+  return T * (1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f));
 }
 
 // The sink logit of query head hq in log2 units, or -inf when there is none.

@@ -621,3 +621,26 @@ def test_append_refuses_softmax_options_and_empty_batch_is_a_noop():
                                   None) == OK
     assert L.gqa_decode_step_ex(ctypes.byref(d0), ctypes.byref(o), None, None, None, None, None, None, None, None, 0,
                                 None) == OK
+
+
+def test_window_plans_splits_over_its_span():
+    """With a host-known window and prefix the splits cover W + P + 32 slots,
+    not the capacity: the workspace follows that plan."""
+    L = g.lib()
+    d = desc(batch=4, num_q_heads=32, num_kv_heads=8, capacity=131073)
+    plain = g.workspace_size(d)
+    n = ctypes.c_size_t(0)
+    for W_, P_ in ((4096, 4), (64, 0), (200000, 0)):
+        v = _smx(window=W_, kept_prefix=P_)
+        o = _lib.OptsT(None, None, None, ctypes.pointer(v))
+        assert L.gqa_decode_workspace_size_ex(ctypes.byref(d), ctypes.byref(o), ctypes.byref(n)) == OK
+        if W_ == 64:
+            assert n.value == 0                    # one split
+        elif W_ == 4096:
+            assert 0 < n.value
+        else:
+            assert n.value == plain                # the window spans the capacity
+    v = _smx(window=64, kept_prefix_per_seq=FAKE + 15 * GAP)  # prefixes on the device: no bound
+    o = _lib.OptsT(None, None, None, ctypes.pointer(v))
+    assert L.gqa_decode_workspace_size_ex(ctypes.byref(d), ctypes.byref(o), ctypes.byref(n)) == OK
+    assert n.value == plain

@@ -232,12 +232,16 @@ def to_numpy_storage(t: torch.Tensor) -> np.ndarray:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def algorithmic_bytes(w: Workload, lengths) -> int:
+def algorithmic_bytes(w: Workload, lengths, window: int = 0, prefix: int = 0) -> int:
     """Bytes one step must move at minimum: valid K+V read (the new token
     included), Q read, new K/V write, output write.  Int8 caches ("i8") move a
-    float32 scale with every row and take the new rows in the q/out dtype."""
+    float32 scale with every row and take the new rows in the q/out dtype.  A
+    sliding window (with a kept prefix) reads only the slots it attends."""
     e_qo = 4 if w.qo_dtype == "f32" else 2
     n = np.asarray(lengths, dtype=np.int64) + 1
+    if window > 0:
+        wv = np.minimum(n, window)
+        n = wv + np.minimum(prefix, n - wv)
     if w.kv_dtype == "i8":
         row = w.D + 4
         kv_read = int(n.sum()) * w.Hkv * row * 2
