@@ -32,7 +32,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["gqa_decode_attention_amd/csrc/kernels_mfma.hip", "gqa_decode_attention_amd/csrc/kernels_generic.hip",
                   "gqa_decode_attention_amd/csrc/kernels_mfma_qkv.hip",
                   "gqa_decode_attention_amd/csrc/device_common.h", "gqa_decode_attention_amd/csrc/gqa_decode.cpp",
-                  "gqa_decode_attention_amd/csrc/internal.h", "gqa_decode_attention_amd/build.py"]
+                  "gqa_decode_attention_amd/csrc/internal.h", "gqa_decode_attention_amd/csrc/cache_map.h",
+                  "gqa_decode_attention_amd/csrc/variants.h", "gqa_decode_attention_amd/build.py"]
 
 
 def kernel_source_hash() -> str:
