@@ -32,12 +32,12 @@
 // Scores are exact products (bf16 or small integers) summed in float32; the
 // weights enter the V sum rounded to bf16 (their sum l stays float32).
 //
-// Fused step (bf16 caches): the new token (slot lengths[b]) is not read from
-// the cache; the last wave of the workgroup whose split holds it runs one extra
-// tile whose only valid row comes from k_new / v_new, and writes those bits
-// into the cache slot after its loop.  No other workgroup reads that slot, so
-// the write cannot race a read.  Int8 caches get the new row from the
-// quantizing append kernel, launched first on the same stream.
+// Fused step: the new token (slot lengths[b]) is not read from the cache; the
+// last wave of the workgroup whose split holds it runs one extra tile whose
+// only valid row comes from k_new / v_new (int8 caches: quantized in the
+// kernel by the per-row rule), and writes that row (and its scales) into the
+// cache slot after its loop.  No other workgroup reads that slot, so the write
+// cannot race a read.
 //
 // Paged bf16 caches (CLIKA runtime "groupQueryAttention" API page, block
 // table): with a block size that is a multiple of 16, every 16-slot tile lies
@@ -252,8 +252,8 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
   const int nact = nv == 0 ? 0 : min(a.nsplit, (nv + a.split_tokens - 1) / a.split_tokens);
   if (split >= max(nact, 1)) return;
 
-  // Fused step (bf16 caches only): slot L is taken from k_new / v_new.
-  const bool own_new = KV == GQA_BF16 && a.k_new != nullptr && Lv >= t_begin && Lv < t_end;
+  // Fused step: slot L is taken from k_new / v_new (int8 caches: quantized here).
+  const bool own_new = a.k_new != nullptr && Lv >= t_begin && Lv < t_end;
   const int t_cache_end = own_new ? Lv : t_end;
 
   constexpr int EB = KV == GQA_BF16 ? 2 : 1;  // bytes per cached element
@@ -373,6 +373,64 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 1; i < 4; ++i) tn.v[i] = u32x4{0, 0, 0, 0};
     }
+  } else {
+    // Int8 caches: the new rows (bf16 activations) are quantized here by the
+    // per-row rule (float32 row maximum, scale = max / 127 and codes =
+    // round-half-even(x / scale) with correctly rounded divisions, clamped to
+    // +-127; a zero row has scale 0 and codes 0) straight into the tile's
+    // layout: lanes (r, 0) hold key codes 64j + 16r .. +15, lanes (0, c) value
+    // codes 8c .. 8c + 7.
+    if (new_here) {
+      const int64_t nrow = ((int64_t)b * a.Hkv + h) * kDq;
+      const uint16_t* knp = reinterpret_cast<const uint16_t*>(a.k_new) + nrow;
+      const uint16_t* vnp = reinterpret_cast<const uint16_t*>(a.v_new) + nrow;
+      float kx[32], vx[8];
+      float kmax = 0.f, vmax = 0.f;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {  // 8 elements each: positions 64(q4 >> 1) + 16r + 8(q4 & 1)
+        const u32x4 w = (c == 0) ? *reinterpret_cast<const u32x4*>(knp + 64 * (q4 >> 1) + 16 * r + 8 * (q4 & 1))
+                                 : u32x4{0, 0, 0, 0};
+        widen16<GQA_BF16>(w, &kx[8 * q4]);
+      }
+      {
+        const u32x4 w = (r == 0) ? *reinterpret_cast<const u32x4*>(vnp + 8 * c) : u32x4{0, 0, 0, 0};
+        widen16<GQA_BF16>(w, vx);
+      }
+#pragma unroll
+      for (int e = 0; e < 32; ++e) kmax = fmaxf(kmax, fabsf(kx[e]));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vmax = fmaxf(vmax, fabsf(vx[e]));
+      kmax = rows_max(kmax);                                  // column 0 holds the key row's maximum
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off));  // row 0: value's
+      kmax = __shfl(kmax, 0);
+      vmax = __shfl(vmax, 0);
+      const float ksc = kmax / 127.0f, vsc = vmax / 127.0f;
+      auto code = [](float x, float amax, float sc) -> uint32_t {
+        const float q = amax > 0.f ? fminf(fmaxf(rintf(x / sc), -127.f), 127.f) : 0.f;
+        return (uint32_t)(int32_t)q & 0xffu;
+      };
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {
+          uint32_t w = 0;
+#pragma unroll
+          for (int by = 0; by < 4; ++by) w |= code(kx[16 * j + 4 * wd + by], kmax, ksc) << (8 * by);
+          tn.k[j][wd] = c == 0 ? w : 0u;
+        }
+#pragma unroll
+      for (int wd = 0; wd < 2; ++wd) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int by = 0; by < 4; ++by) w |= code(vx[4 * wd + by], vmax, vsc) << (8 * by);
+        tn.v[0][wd] = r == 0 ? w : 0u;
+      }
+#pragma unroll
+      for (int i = 1; i < 4; ++i) tn.v[i] = u32x2_t{0u, 0u};
+      tn.ks = ksc;
+      tn.vs = vsc;
+    }
   }
 
   // Two tile register sets alternate, so the next tile's loads are in flight
@@ -380,9 +438,7 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
   Tile<KV> ta, tb;
   int32_t eB = entry(w0 + 16), eA = entry(w0 + 32);  // table entries of the first pair's successors
   load_tile(w0, ta, entry(w0));
-  if constexpr (KV == GQA_BF16) {
-    if (new_here) tile_math<KV, VAR>(st, qf, tn, 0, 1, r, a.scale_log2, TileVar{&a, &view, Lv});
-  }
+  if (new_here) tile_math<KV, VAR>(st, qf, tn, 0, 1, r, a.scale_log2, TileVar{&a, &view, Lv});
   if (w0 < w1) {
     const int nt = (w1 - w0 + 15) >> 4;
     int t0 = w0;
@@ -409,6 +465,21 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
         for (int kk = 0; kk < 4; ++kk) *reinterpret_cast<u32x4*>(kw + 32 * kk + 8 * r) = tn.k[kk];
       }
       if (off >= 0 && r == 0) *reinterpret_cast<u32x4*>(vw + 8 * c) = tn.v[0];
+    }
+  } else {
+    if (new_here) {
+      const int64_t off = slot_offset_checked(a, b, h, L);
+      int8_t* kw = reinterpret_cast<int8_t*>(a.k_cache_w) + off;
+      int8_t* vw = reinterpret_cast<int8_t*>(a.v_cache_w) + off;
+      if (off >= 0 && c == 0) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4*>(kw + 64 * j + 16 * r) = tn.k[j];
+      }
+      if (off >= 0 && r == 0) *reinterpret_cast<u32x2_t*>(vw + 8 * c) = tn.v[0];
+      if (off >= 0 && lane == 0) {
+        a.k_scale_w[off / kDq] = tn.ks;
+        a.v_scale_w[off / kDq] = tn.vs;
+      }
     }
   }
 
@@ -471,7 +542,8 @@ hipError_t launch_attend_mfma_qk(const AttnArgs& a, const Plan& p, hipStream_t s
   const bool var = a.window > 0 || a.cap_T > 0.f;  // in-loop variants (the sink is applied at the end)
   const void* fn;
   if (a.kv_dtype == GQA_I8) {
-    if (a.map_kind != 0 || a.k_new != nullptr || a.k_scale == nullptr || a.v_scale == nullptr)
+    if (a.map_kind != 0 || a.k_scale == nullptr || a.v_scale == nullptr || a.qo_dtype != GQA_BF16 ||
+        (a.k_new != nullptr && (a.k_cache_w == nullptr || a.k_scale_w == nullptr || a.v_scale_w == nullptr)))
       return hipErrorInvalidValue;
     fn = var ? reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_I8, NW, false, true>)
              : reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_I8, NW, false, false>);
