@@ -65,7 +65,8 @@ int32_t choose_kernel(const gqa_decode_desc_t* d) {
   const int32_t G = d->num_q_heads / d->num_kv_heads;
   const bool bf16 = d->kv_dtype == GQA_BF16 && d->qo_dtype == GQA_BF16;
   if (d->kv_dtype == GQA_I8) {
-    return (d->qo_dtype == GQA_BF16 && d->head_dim == 128 && G <= 16 && kHaveMfmaQkI8) ? GQA_KERNEL_MFMA_QK
+    // Groups of up to 64 query heads: 16-head chunks of the G <= 16 kernel.
+    return (d->qo_dtype == GQA_BF16 && d->head_dim == 128 && G <= 64 && kHaveMfmaQkI8) ? GQA_KERNEL_MFMA_QK
                                                                                        : GQA_KERNEL_GENERIC;
   }
   if (bf16 && d->head_dim == 128 && G <= 16 && kHaveMfmaQk) return GQA_KERNEL_MFMA_QK;
@@ -84,7 +85,11 @@ gqa_status_t make_plan(const gqa_decode_desc_t* d, Plan* p, int64_t span = 0) {
   const int64_t S = span > 0 ? std::min<int64_t>(span, d->capacity) : d->capacity;
   const int64_t G = Hq / Hkv;
   p->kernel = choose_kernel(d);
-  p->head_chunks = p->kernel == GQA_KERNEL_GENERIC ? (int32_t)((G + kGenericHeadChunk - 1) / kGenericHeadChunk) : 1;
+  // Query-head chunks per kv-head: 8 heads per workgroup in the generic
+  // kernel, 16 (one MFMA tile) in MFMA_QK, all G in MFMA_ALL.
+  p->head_chunks = p->kernel == GQA_KERNEL_GENERIC ? (int32_t)((G + kGenericHeadChunk - 1) / kGenericHeadChunk)
+                   : p->kernel == GQA_KERNEL_MFMA_QK ? (int32_t)((G + 15) / 16)
+                                                     : 1;
   // Four waves per workgroup for every kernel.  (For MFMA_QK, measured on
   // MI355X: one 4-wave workgroup per CU streams faster than 8- or 12-wave
   // workgroups or more, shorter splits -- fewer concurrent streams suit HBM.)

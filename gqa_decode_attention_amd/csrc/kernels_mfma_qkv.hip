@@ -231,12 +231,28 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
   const int r = lane >> 4;
   const int c = lane & 15;
 
+  // Workgroup -> (split, query-head chunk, b, kv-head).  Groups of more than
+  // 16 query heads are served 16 at a time by head chunks that all read the
+  // same K/V rows; the chunks of one (b, kv-head) are numbered 8 apart, so
+  // the round-robin dispatch puts them on the same XCD at about the same time
+  // and only the first of them reads the rows from HBM (the others from L2).
   int x = blockIdx.x;
   const int split = x % a.nsplit;
   x /= a.nsplit;
-  const int h = x % a.Hkv;
-  const int b = x / a.Hkv;
-  const int G = a.G;
+  int hc = 0, bh = x;
+  if (a.head_chunks > 1) {
+    const int HC = a.head_chunks;
+    const int units = a.B * a.Hkv;
+    const int grp = x / (8 * HC);
+    const int gsz = min(8, units - grp * 8);  // the last group may hold fewer (b, kv-head) units
+    const int rem = x - grp * 8 * HC;
+    hc = rem / gsz;
+    bh = grp * 8 + rem % gsz;
+  }
+  const int h = bh % a.Hkv;
+  const int b = bh / a.Hkv;
+  const int hq0 = h * a.G + 16 * hc;       // first query head of this workgroup
+  const int G = min(16, a.G - 16 * hc);   // query heads in this workgroup
 
   const int L = a.lengths[b];
   int n = L + a.len_offset;
@@ -282,7 +298,7 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
   const bool new_here = own_new && wave == NW - 1;
 
   // Query operand: positions matching the K operand's.
-  const int64_t qrow = ((int64_t)b * a.Hq + (int64_t)h * G + c) * kDq;
+  const int64_t qrow = ((int64_t)b * a.Hq + hq0 + c) * kDq;
   const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + qrow;
   u32x4 qf[4];
 #pragma unroll
@@ -456,7 +472,7 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
     if (nt & 1) tile_math<KV, VAR>(st, qf, ta, t_begin - t0, w1 - t0, r, a.scale_log2, TileVar{&a, &view, t0});
   }
   if constexpr (KV == GQA_BF16) {
-    if (new_here) {
+    if (new_here && hc == 0) {  // one head chunk writes the appended row
       const int64_t off = slot_offset_checked(a, b, h, L);
       uint16_t* kw = reinterpret_cast<uint16_t*>(a.k_cache_w) + off;
       uint16_t* vw = reinterpret_cast<uint16_t*>(a.v_cache_w) + off;
@@ -467,7 +483,7 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
       if (off >= 0 && r == 0) *reinterpret_cast<u32x4*>(vw + 8 * c) = tn.v[0];
     }
   } else {
-    if (new_here) {
+    if (new_here && hc == 0) {
       const int64_t off = slot_offset_checked(a, b, h, L);
       int8_t* kw = reinterpret_cast<int8_t*>(a.k_cache_w) + off;
       int8_t* vw = reinterpret_cast<int8_t*>(a.v_cache_w) + off;
@@ -511,7 +527,7 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
       O += sm_o[w][g][d] * sc;
       Lsum += sm_l[w][g] * sc;
     }
-    const int hq = h * G + g;
+    const int hq = hq0 + g;
     if (nact <= 1) {
       reinterpret_cast<uint16_t*>(a.out)[((int64_t)b * a.Hq + hq) * kDq + d] =
           f32_to_bf16_rne(VAR || a.sink != nullptr || a.smooth ? finish_row(a, hq, M, O, Lsum)
@@ -538,7 +554,7 @@ const bool kHaveMfmaQkI8 = true;
 // appended beforehand).
 hipError_t launch_attend_mfma_qk(const AttnArgs& a, const Plan& p, hipStream_t s) {
   constexpr int NW = 4;
-  if (a.D != qkv::kDq || a.G > 16 || p.block != 64 * NW) return hipErrorInvalidValue;
+  if (a.D != qkv::kDq || a.G > 16 * a.head_chunks || p.block != 64 * NW) return hipErrorInvalidValue;
   const bool var = a.window > 0 || a.cap_T > 0.f;  // in-loop variants (the sink is applied at the end)
   const void* fn;
   if (a.kv_dtype == GQA_I8) {

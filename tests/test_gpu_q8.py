@@ -64,6 +64,8 @@ CASES = [
     (2, 4, 1, 256, 100, "BHSD", "bf16", 0),        # largest head
     (4, 8, 8, 80, 64, "BSHD", "bf16", 0),          # G=1
     (2, 8, 2, 7, 50, "BHSD", "f32", 0),            # odd head_dim
+    (3, 48, 2, 128, 600, "BSHD", "bf16", 2),       # G=24: two 16-head chunks (16 + 8)
+    (2, 64, 1, 128, 700, "BHSD", "bf16", 3),       # G=64: four chunks, forced splits
 ]
 
 
@@ -157,6 +159,35 @@ def test_q8_full_size_llama_layer(g):
         cv, sv = oracle.quantize_row(oracle.decode(vnew[b, h], "bf16").astype(np.float32))
         assert np.array_equal(kc[-1], ck) and ks[-1] == sk
         assert np.array_equal(vc[-1], cv) and vs[-1] == sv
+        ref = oracle.attend_one(q[b, hq], oracle.dequantize(kc, ks), oracle.dequantize(vc, vs))
+        err = np.abs(got[b, hq] - ref)
+        assert np.all(err <= 1e-2 + 1e-2 * np.abs(ref)), (b, hq, err.max())
+
+
+def test_q8_full_size_large_group(g):
+    """The large-group shape (B=128, Hq=64, Hkv=1, D=128, capacity 2048,
+    attended counts U[1024, 2048]) on int8 caches in the benchmark's launch
+    configuration: sampled heads against the oracle, appended rows exact."""
+    base = W.WORKLOADS["large_group"]
+    w = W.custom(base.B, base.Hq, base.Hkv, base.D, base.capacity, base.layout, "i8", "bf16", seed=base.seed)
+    L = W.draw_lengths(base)
+    inp = W.make_q8(w, DEV, lengths=L)
+    out = g.step_q8(inp["q"], inp["k_cache"], inp["v_cache"], inp["k_scale"], inp["v_scale"], inp["k_new"],
+                    inp["v_new"], inp["lengths"], layout=w.layout)
+    torch.cuda.synchronize()
+    q = oracle.decode(np_of(inp["q"]), "bf16")
+    knew = np_of(inp["k_new"])
+    got = out.float().cpu().double().numpy()
+    rng = np.random.default_rng(6)
+    for _ in range(8):
+        b, hq = int(rng.integers(w.B)), int(rng.integers(w.Hq))
+        n = int(L[b]) + 1
+        kc = inp["k_cache"][b, 0, :n].cpu().numpy()
+        vc = inp["v_cache"][b, 0, :n].cpu().numpy()
+        ks = inp["k_scale"][b, 0, :n].cpu().numpy()
+        vs = inp["v_scale"][b, 0, :n].cpu().numpy()
+        ck, sk = oracle.quantize_row(oracle.decode(knew[b, 0], "bf16").astype(np.float32))
+        assert np.array_equal(kc[-1], ck) and ks[-1] == sk
         ref = oracle.attend_one(q[b, hq], oracle.dequantize(kc, ks), oracle.dequantize(vc, vs))
         err = np.abs(got[b, hq] - ref)
         assert np.all(err <= 1e-2 + 1e-2 * np.abs(ref)), (b, hq, err.max())
