@@ -405,7 +405,7 @@ gqa_status_t check_rope(const gqa_decode_desc_t* d, const gqa_rope_t* r) {
 }
 gqa_status_t check_rope_ptrs(const gqa_decode_desc_t* d, const gqa_rope_t* r, std::initializer_list<Span> written) {
   if (r == nullptr) return GQA_OK;
-  if (!r->cos || !r->sin || !aligned(r->cos, 4) || !aligned(r->sin, 4)) return GQA_ERR_INVALID_ARGUMENT;
+  if (!r->cos || !r->sin || !aligned(r->cos, 16) || !aligned(r->sin, 16)) return GQA_ERR_INVALID_ARGUMENT;
   if (!aligned(r->positions, 4) || !aligned(r->q_norm_gain, 4) || !aligned(r->k_norm_gain, 4))
     return GQA_ERR_INVALID_ARGUMENT;
   const size_t tb = (size_t)r->max_pos * (d->head_dim / 2) * 4, gb = (size_t)d->head_dim * 4;
@@ -475,7 +475,8 @@ const gqa_decode_opts_t kNoOpts = {nullptr, nullptr, nullptr, nullptr};
 // Bytes of the rotated q a rotary step keeps after the plan's workspace.
 size_t rope_q_offset(const Plan& p) { return align256(p.workspace_bytes); }
 size_t workspace_total(const gqa_decode_desc_t* d, const Plan& p, const gqa_decode_opts_t* o) {
-  if (o->rope == nullptr) return p.workspace_bytes;
+  // MFMA_ALL rotates q itself; the other kernels read a rotated copy.
+  if (o->rope == nullptr || p.kernel == GQA_KERNEL_MFMA_ALL) return p.workspace_bytes;
   return rope_q_offset(p) + (size_t)d->batch * d->num_q_heads * d->head_dim * elem_bytes(d->qo_dtype);
 }
 
@@ -611,10 +612,24 @@ gqa_status_t do_attend(const gqa_decode_desc_t* desc, const gqa_decode_opts_t* o
   if (step) {
     a.k_new = k_new;
     a.v_new = v_new;
-    if (rope != nullptr) {
-      // Rotary step: the rope append kernel writes the rotated key (quantized
-      // for int8 caches) and the value at slot lengths[b] and the rotated q
-      // into the workspace; attention over lengths[b] + 1 slots then reads it.
+    if (rope != nullptr && p.kernel == GQA_KERNEL_MFMA_ALL) {
+      // Rotary step on MFMA_ALL: every workgroup rotates its q (all G heads of
+      // its kv-head), the workgroup whose split holds slot lengths[b] rotates
+      // the new key, attends it and stores it.  (On the G <= 16 kernel the
+      // same fusion measured slower than the separate rotary append: its
+      // single workgroup per CU pays the prologue's dependent loads in full.)
+      fill_rope(rope, &a);
+      if (sc != nullptr) {
+        a.k_scale_w = sc->k_scale;
+        a.v_scale_w = sc->v_scale;
+      }
+      a.k_cache_w = k_cache;
+      a.v_cache_w = v_cache;
+    } else if (rope != nullptr) {
+      // Rotary step, other kernels: the rope append kernel writes the rotated key
+      // (quantized for int8 caches) and the value at slot lengths[b] and the
+      // rotated q into the workspace; attention over lengths[b] + 1 slots then
+      // reads it.
       if (sc != nullptr) {
         a.k_scale_w = sc->k_scale;
         a.v_scale_w = sc->v_scale;
@@ -625,6 +640,7 @@ gqa_status_t do_attend(const gqa_decode_desc_t* desc, const gqa_decode_opts_t* o
       a.q = a.q_rot;
       a.k_new = nullptr;
       a.v_new = nullptr;
+      a.rope_cos = nullptr;  // the attention pass reads the rotated q and key as they are
     } else if (sc != nullptr && p.kernel == GQA_KERNEL_GENERIC) {
       // Int8 caches, generic path: the quantizing append, then attention over
       // lengths[b] + 1 slots (the new token is attended in its stored,

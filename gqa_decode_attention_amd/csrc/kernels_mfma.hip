@@ -20,6 +20,7 @@
 #include "cache_map.h"
 #include "device_common.h"
 #include "internal.h"
+#include "rope_dev.h"
 #include "variants.h"
 
 namespace gqa {
@@ -129,6 +130,22 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
   for (int kk = 0; kk < 4; ++kk)
     qf[kk] = (hw + c < G) ? load16(reinterpret_cast<const uint16_t*>(a.q) + qrow + 32 * kk + 8 * r)
                           : u32x4{0, 0, 0, 0};
+  // Rotary step: q (positions 32kk + 8r of head c) and the new key are rotated
+  // (and normalized) here, at the new token's position.
+  const bool rope = a.rope_cos != nullptr;
+  const int rp = rope ? rope_row(a, b, L0) : 0;
+  if (rope) {
+    float x[4][8];
+    const int pos[4] = {8 * r, 32 + 8 * r, 64 + 8 * r, 96 + 8 * r};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) widen16<GQA_BF16>(qf[kk], x[kk]);
+    rope_chunks(a, rp, pos, x, a.q_gain);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      qf[kk] = hw + c < G ? u32x4{pack_bf16x2(x[kk][0], x[kk][1]), pack_bf16x2(x[kk][2], x[kk][3]),
+                                  pack_bf16x2(x[kk][4], x[kk][5]), pack_bf16x2(x[kk][6], x[kk][7])}
+                          : u32x4{0, 0, 0, 0};
+  }
 
   float m = kNegInfM, l = 0.f;
   f32x4 O[8];
@@ -165,6 +182,35 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
   if (own_new) {
     kn = load16(reinterpret_cast<const uint16_t*>(a.k_new) + nrow + 8 * piece);
     vn = load16(reinterpret_cast<const uint16_t*>(a.v_new) + nrow + 8 * piece);
+    if (rope) {
+      // Each 16-lane group holds the whole key (piece = 8 elements); the half
+      // pairing's partner piece is loaded as well, the norm reduces over the group.
+      const u32x4 kp = load16(reinterpret_cast<const uint16_t*>(a.k_new) + nrow + 8 * (piece ^ 8));
+      float x[8], xp[8], y[8];
+      widen16<GQA_BF16>(kn, x);
+      widen16<GQA_BF16>(kp, xp);
+      const float* cs = a.rope_cos + (int64_t)rp * 64;
+      const float* sn = a.rope_sin + (int64_t)rp * 64;
+      const bool half = a.rope_mode == GQA_ROPE_HALF;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = 8 * piece + e;
+        const bool first = half ? d < 64 : (e & 1) == 0;
+        const int j = half ? (d & 63) : (d >> 1);
+        y[e] = rope_rot(first, x[e], half ? xp[e] : x[e ^ 1], cs[j], sn[j]);
+      }
+      if (a.k_gain != nullptr) {
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += y[e] * y[e];
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) ss += __shfl_xor(ss, off);
+        const float rn = 1.0f / sqrtf(ss / 128.f + a.norm_eps);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = (y[e] * rn) * a.k_gain[8 * piece + e];
+      }
+      kn = u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])};
+    }
   }
   // Paged: the table entries of a tile's two 16-row halves, loaded a tile pair
   // before the tile itself (clamped into the split, like the rows).

@@ -266,8 +266,8 @@ gqa_status_t gqa_decode_step_q8(const gqa_decode_desc_t* desc, const gqa_kv_scal
  * per-head RMS norm gains applied after the rotation, before the append; the
  * Huawei CANN "aclnnMlaPrologV3WeightNz" page rotates its query and key the
  * same way and gives the RmsNorm formula, epsilon inside the square root).
- *   cos, sin     : float32 (max_pos, D/2) tables in device memory; row p holds the
- *                  angles of position p, column i the i-th rotation pair.
+ *   cos, sin     : float32 (max_pos, D/2) tables in device memory, 16-byte aligned;
+ *                  row p holds the angles of position p, column i the i-th rotation pair.
  *   mode         : GQA_ROPE_HALF pairs elements (i, i + D/2); GQA_ROPE_INTERLEAVED
  *                  pairs (2i, 2i + 1).  A pair (x1, x2) at position p becomes
  *                  (x1 c - x2 s, x2 c + x1 s), c = cos[p][i], s = sin[p][i], in float32
