@@ -125,6 +125,16 @@ gqa_status_t make_plan(const gqa_decode_desc_t* d, Plan* p, int64_t span = 0) {
     p->off_l = p->off_m + align256(nparts * sizeof(float));
     p->workspace_bytes = p->off_l + align256(nparts * sizeof(float));
   }
+  // More MFMA_QK workgroups than CUs: the work per workgroup follows the
+  // sequence lengths, so the workgroups are dealt out longest first (a small
+  // kernel ranks the lengths on the device) and run one per CU, and the
+  // dispatcher's in-order hand-out of the rest is a longest-processing-time
+  // schedule.  Not for huge batches (the ranking is quadratic in B).
+  if (p->kernel == GQA_KERNEL_MFMA_QK && grid > kNumCUs && B > 1 && B <= kMaxOrderedBatch) {
+    p->order = 1;
+    p->off_order = p->workspace_bytes;
+    p->workspace_bytes += align256((size_t)B * sizeof(int32_t));
+  }
   return GQA_OK;
 }
 
@@ -308,8 +318,13 @@ gqa_status_t check_attend_ptrs(const gqa_decode_desc_t* d, const gqa_cache_map_t
   return GQA_OK;
 }
 
-gqa_status_t run_attend(const gqa_decode_desc_t* d, const Plan& p, AttnArgs& a, hipStream_t s) {
+gqa_status_t run_attend(const gqa_decode_desc_t* d, const Plan& p, AttnArgs& a, hipStream_t s, void* workspace) {
   hipError_t e;
+  if (p.order) {
+    int32_t* order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + p.off_order);
+    if (launch_order(a, order, s) != hipSuccess) return GQA_ERR_HIP;
+    a.order = order;
+  }
   switch (p.kernel) {
     case GQA_KERNEL_MFMA_QK: e = launch_attend_mfma_qk(a, p, s); break;
     case GQA_KERNEL_MFMA_ALL: e = launch_attend_mfma_all(a, p, s); break;
@@ -357,6 +372,7 @@ gqa_status_t gqa_decode_get_plan(const gqa_decode_desc_t* desc, gqa_decode_plan_
     plan->block = p.block;
     plan->combine = p.combine;
     plan->workspace_bytes = p.workspace_bytes;
+    plan->length_order = p.order;
     return GQA_OK;
   } catch (...) {
     return GQA_ERR_INTERNAL;
@@ -603,7 +619,7 @@ gqa_status_t do_attend(const gqa_decode_desc_t* desc, const gqa_decode_opts_t* o
   a.lengths = lengths;
   a.out = out;
   a.len_offset = step ? 1 : 0;
-  if (p.workspace_bytes > 0) {
+  if (p.nsplit > 1) {
     char* w = static_cast<char*>(workspace);
     a.part_o = reinterpret_cast<float*>(w);
     a.part_m = reinterpret_cast<float*>(w + p.off_m);
@@ -672,7 +688,7 @@ gqa_status_t do_attend(const gqa_decode_desc_t* desc, const gqa_decode_opts_t* o
       a.v_cache_w = v_cache;
     }
   }
-  return run_attend(desc, p, a, (hipStream_t)stream);
+  return run_attend(desc, p, a, (hipStream_t)stream, workspace);
 }
 
 }  // namespace

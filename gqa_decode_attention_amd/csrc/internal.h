@@ -56,6 +56,9 @@ struct AttnArgs {
   float cap_T, cap_invT;
   int32_t window, prefix;
   const int32_t* prefix_seq;
+  // Longest-first order of the sequences (order[k] = the sequence with the
+  // k-th largest attended count), or null for batch order.
+  const int32_t* order;
   int32_t nsplit, split_tokens;
   int32_t head_chunks;   // generic kernel: query-head chunks per kv-head
   int32_t len_offset;    // slots attended = lengths[b] + len_offset (1 for a step, 0 for attend)
@@ -73,6 +76,8 @@ struct Plan {
   int32_t combine;
   size_t workspace_bytes;
   size_t off_m, off_l;   // byte offsets of part_m / part_l inside the workspace
+  int32_t order;         // 1: sequences are dealt out longest first (see AttnArgs::order)
+  size_t off_order;      // byte offset of that order inside the workspace
 };
 
 // Which matrix-core kernels this build provides (the planner falls back to the
@@ -84,9 +89,12 @@ extern const bool kHaveMfmaQkI8;  // int8 caches on the G <= 16 matrix-core kern
 constexpr int kNumCUs = 256;          // MI355X: 8 XCDs x 32 CUs
 constexpr int kMaxSplits = 64;        // one lane per split in the combine pass
 constexpr int kGenericHeadChunk = 8;  // query heads per workgroup in the generic kernel
+constexpr int kMaxOrderedBatch = 4096;  // largest batch ranked by length on the device
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_append(const AttnArgs& a, void* k_cache, void* v_cache, hipStream_t s);
+// Sequences by attended count, longest first (ties by index), into `order`.
+hipError_t launch_order(const AttnArgs& a, int32_t* order, hipStream_t s);
 // Rotary append: rotates (and normalizes) the new key, writes it and the value
 // at slot lengths[b] (int8 caches: quantized), and, when a.q_rot is set, the
 // rotated (and normalized) q into a.q_rot.

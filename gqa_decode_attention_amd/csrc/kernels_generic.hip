@@ -119,6 +119,37 @@ hipError_t launch_append_q8(const AttnArgs& a, void* k_cache, void* v_cache, hip
 }
 
 // ---------------------------------------------------------------------------
+// Longest-first order of the sequences: thread b ranks its attended count
+// (sliding-window view when set) against every other sequence's (ties by
+// index) and writes its index at that rank.  Quadratic in B, used for
+// B <= kMaxOrderedBatch.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int attended_span(const AttnArgs& a, int b) {
+  int n = a.lengths[b] + a.len_offset;
+  n = n < 0 ? 0 : (n > a.S ? a.S : n);
+  return a.window > 0 ? seq_view(a, b, n).nv : n;
+}
+
+__global__ __launch_bounds__(256) void order_kernel(AttnArgs a, int32_t* __restrict__ order) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= a.B) return;
+  const int nb = attended_span(a, b);
+  int rank = 0;
+  for (int j = 0; j < a.B; ++j) {
+    const int nj = attended_span(a, j);
+    rank += (nj > nb || (nj == nb && j < b)) ? 1 : 0;
+  }
+  order[rank] = b;
+}
+
+hipError_t launch_order(const AttnArgs& a, int32_t* order, hipStream_t s) {
+  AttnArgs arg = a;
+  void* params[] = {&arg, &order};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&order_kernel), dim3((unsigned)((a.B + 255) / 256)), dim3(256),
+                         params, 0, s);
+}
+
+// ---------------------------------------------------------------------------
 // Rotary append (CLIKA "groupQueryAttention" page: q and the new k rotated with
 // the rope planes, optional post-rotation RMS norm with gains, the rotated key
 // appended in place).  The rows of (b, kv-head) are k, v, then its G query

@@ -250,7 +250,7 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
     bh = grp * 8 + rem % gsz;
   }
   const int h = bh % a.Hkv;
-  const int b = bh / a.Hkv;
+  const int b = a.order != nullptr ? a.order[bh / a.Hkv] : bh / a.Hkv;  // longest sequences first
   const int hq0 = h * a.G + 16 * hc;       // first query head of this workgroup
   const int G = min(16, a.G - 16 * hc);   // query heads in this workgroup
 
@@ -547,6 +547,10 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
 
 using qkv::attend_mfma_qkv_kernel;
 
+// Dynamic LDS that, with the kernel's 33 KB static arrays, exceeds half of a
+// CU's 160 KB.
+constexpr unsigned kOneWorkgroupLds = 48u * 1024u;
+
 const bool kHaveMfmaQk = true;
 const bool kHaveMfmaQkI8 = true;
 
@@ -572,7 +576,11 @@ hipError_t launch_attend_mfma_qk(const AttnArgs& a, const Plan& p, hipStream_t s
   }
   AttnArgs arg = a;
   void* params[] = {&arg};
-  return hipLaunchKernel(fn, dim3(p.grid), dim3(p.block), params, 0, s);
+  // Dealt out longest first: an unused dynamic LDS reservation keeps one
+  // workgroup per CU (two would exceed the CU's 160 KB), so the rest wait in
+  // dispatch order and take the next CU that frees up.
+  const unsigned lds = a.order != nullptr ? kOneWorkgroupLds : 0u;
+  return hipLaunchKernel(fn, dim3(p.grid), dim3(p.block), params, lds, s);
 }
 
 }  // namespace gqa

@@ -103,6 +103,8 @@ typedef struct {
   int32_t block;         /* threads per workgroup of the attention pass                     */
   int32_t combine;       /* 1 if a split-combine pass follows the attention pass            */
   size_t workspace_bytes;
+  int32_t length_order;  /* 1 if the workgroups are dealt out longest sequence first (a small
+                            ranking pass runs before the attention pass)                    */
 } gqa_decode_plan_t;
 
 enum {

@@ -232,7 +232,10 @@ def test_plan_is_a_function_of_the_descriptor_only():
         assert (p1["num_splits"] - 1) * p1["split_tokens"] < d.capacity     # no empty split
         assert p1["combine"] == (p1["num_splits"] > 1)
         assert p1["num_splits"] <= 64
-        assert (p1["workspace_bytes"] == 0) == (p1["num_splits"] == 1)
+        # the workspace holds split partials, and the length order when sequences are ranked
+        assert (p1["workspace_bytes"] == 0) == (p1["num_splits"] == 1 and not p1["length_order"])
+        if p1["length_order"]:
+            assert p1["kernel"] == "mfma_qk" and p1["grid"] > 256
 
 
 @pytest.mark.parametrize("ns", [1, 2, 3, 7, 64, 10_000])

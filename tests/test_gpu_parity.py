@@ -406,3 +406,57 @@ def test_full_size_workload(g, name):
         tol = TOL[w.qo_dtype]
         assert np.all(np.abs(got[b, hq] - ref) <= tol + tol * np.abs(ref)), (b, hq, np.abs(got[b, hq] - ref).max())
     assert torch.isfinite(out.float()).all()
+
+
+@pytest.mark.parametrize("kind", ["dense", "paged", "int8", "window"])
+def test_longest_first_order_matches_oracle(g, kind):
+    """More matrix-core workgroups than CUs: the plan ranks the sequences by
+    length on the device and deals them out longest first.  Shuffled ragged
+    lengths (including 0 and the full capacity) on dense, paged and int8
+    caches and with a sliding window must match the oracle."""
+    B, Hq, Hkv, D, S = 40, 32, 8, 128, 300
+    kv = "i8" if kind == "int8" else "bf16"
+    w = W.custom(B, Hq, Hkv, D, S, "BHSD", kv, "bf16", seed=91, stale="pm:1")
+    L = torch.randint(0, S, (B,), generator=torch.Generator().manual_seed(92), dtype=torch.int32)
+    L[5], L[17], L[30] = 0, S - 1, S - 1
+    desc = g.make_desc(B, Hq, Hkv, D, S, "BHSD", g.I8 if kind == "int8" else g.BF16, g.BF16)
+    assert g.get_plan(desc)["length_order"]
+    say(f"ordered {kind}")
+    if kind == "int8":
+        inp = W.make_q8(w, DEV, lengths=L)
+        ref, rk, rv, rks, rvs = oracle.step_q8(np_of(inp["q"]), "bf16", np_of(inp["k_cache"]), np_of(inp["v_cache"]),
+                                               np_of(inp["k_scale"]), np_of(inp["v_scale"]), np_of(inp["k_new"]),
+                                               np_of(inp["v_new"]), L.numpy(), "BHSD", Hq, Hkv)
+        out = g.step_q8(inp["q"], inp["k_cache"], inp["v_cache"], inp["k_scale"], inp["v_scale"], inp["k_new"],
+                        inp["v_new"], inp["lengths"], layout="BHSD")
+        torch.cuda.synchronize()
+        assert_close(out, ref, "bf16", "int8 step")
+        assert np_of(inp["k_cache"]).tobytes() == rk.tobytes() and np_of(inp["k_scale"]).tobytes() == rks.tobytes()
+        return
+    inp = W.make_inputs(w, DEV, lengths=L)
+    if kind == "paged":
+        m = W.make_mapped(inp, w, "paged", block_size=16)
+        ref, rk, rv = oracle.step_mapped("paged", np_of(inp["q"]), "bf16", np_of(m["k_cache"]), np_of(m["v_cache"]),
+                                         np_of(inp["k_new"]), np_of(inp["v_new"]), "bf16", L.numpy(), "BHSD", Hq,
+                                         Hkv, m["map"].cpu().numpy(), 16)
+        out = g.step_mapped(inp["q"], m["k_cache"], m["v_cache"], inp["k_new"], inp["v_new"], inp["lengths"],
+                            m["map"], kind="paged", layout="BHSD")
+        torch.cuda.synchronize()
+        assert_close(out, ref, "bf16", "paged step")
+        assert np_of(m["k_cache"]).tobytes() == rk.tobytes()
+        return
+    if kind == "window":
+        sm = g.Softmax(window=50, kept_prefix=7)
+        ref, rk, rv = oracle.step_variants(np_of(inp["q"]), "bf16", np_of(inp["k_cache"]), np_of(inp["v_cache"]),
+                                           np_of(inp["k_new"]), np_of(inp["v_new"]), "bf16", L.numpy(), "BHSD", Hq,
+                                           Hkv, window=50, prefix=7)
+        out = g.step_ex(inp["q"], inp["k_cache"], inp["v_cache"], inp["k_new"], inp["v_new"], inp["lengths"],
+                        layout="BHSD", softmax=sm)
+    else:
+        ref, rk, rv = oracle.step(np_of(inp["q"]), "bf16", np_of(inp["k_cache"]), np_of(inp["v_cache"]),
+                                  np_of(inp["k_new"]), np_of(inp["v_new"]), "bf16", L.numpy(), "BHSD", Hq, Hkv)
+        out = g.step(inp["q"], inp["k_cache"], inp["v_cache"], inp["k_new"], inp["v_new"], inp["lengths"],
+                     layout="BHSD")
+    torch.cuda.synchronize()
+    assert_close(out, ref, "bf16", f"{kind} step")
+    assert np_of(inp["k_cache"]).tobytes() == rk.tobytes() and np_of(inp["v_cache"]).tobytes() == rv.tobytes()
