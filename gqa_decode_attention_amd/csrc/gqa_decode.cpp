@@ -126,14 +126,16 @@ gqa_status_t make_plan(const gqa_decode_desc_t* d, Plan* p, int64_t span = 0) {
     p->workspace_bytes = p->off_l + align256(nparts * sizeof(float));
   }
   // More MFMA_QK workgroups than CUs: the work per workgroup follows the
-  // sequence lengths, so the workgroups are dealt out longest first (a small
-  // kernel ranks the lengths on the device) and run one per CU, and the
-  // dispatcher's in-order hand-out of the rest is a longest-processing-time
-  // schedule.  Not for huge batches (the ranking is quadratic in B).
-  if (p->kernel == GQA_KERNEL_MFMA_QK && grid > kNumCUs && B > 1 && B <= kMaxOrderedBatch) {
+  // sequence lengths, so the work items (sequence, split) are dealt out
+  // longest first (a small kernel ranks them on the device) and run one
+  // workgroup per CU, and the dispatcher's in-order hand-out of the rest is a
+  // longest-processing-time schedule.  Not for huge batches (the ranking is
+  // quadratic in the item count).
+  if (p->kernel == GQA_KERNEL_MFMA_QK && p->head_chunks == 1 && grid > kNumCUs && B * nsplit > 1 &&
+      B * nsplit <= kMaxOrderedBatch) {
     p->order = 1;
     p->off_order = p->workspace_bytes;
-    p->workspace_bytes += align256((size_t)B * sizeof(int32_t));
+    p->workspace_bytes += align256((size_t)(B * nsplit) * sizeof(int32_t));
   }
   return GQA_OK;
 }

@@ -56,8 +56,8 @@ struct AttnArgs {
   float cap_T, cap_invT;
   int32_t window, prefix;
   const int32_t* prefix_seq;
-  // Longest-first order of the sequences (order[k] = the sequence with the
-  // k-th largest attended count), or null for batch order.
+  // Longest-first order of the work items (order[k] = b * nsplit + split of
+  // the item with the k-th largest slot count), or null for grid order.
   const int32_t* order;
   int32_t nsplit, split_tokens;
   int32_t head_chunks;   // generic kernel: query-head chunks per kv-head
@@ -89,11 +89,11 @@ extern const bool kHaveMfmaQkI8;  // int8 caches on the G <= 16 matrix-core kern
 constexpr int kNumCUs = 256;          // MI355X: 8 XCDs x 32 CUs
 constexpr int kMaxSplits = 64;        // one lane per split in the combine pass
 constexpr int kGenericHeadChunk = 8;  // query heads per workgroup in the generic kernel
-constexpr int kMaxOrderedBatch = 4096;  // largest batch ranked by length on the device
+constexpr int kMaxOrderedBatch = 4096;  // most (sequence, split) items ranked by length on the device
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_append(const AttnArgs& a, void* k_cache, void* v_cache, hipStream_t s);
-// Sequences by attended count, longest first (ties by index), into `order`.
+// Work items (sequence, split) by slot count, longest first (ties by index), into `order`.
 hipError_t launch_order(const AttnArgs& a, int32_t* order, hipStream_t s);
 // Rotary append: rotates (and normalizes) the new key, writes it and the value
 // at slot lengths[b] (int8 caches: quantized), and, when a.q_rot is set, the

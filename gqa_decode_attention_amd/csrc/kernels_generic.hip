@@ -119,34 +119,40 @@ hipError_t launch_append_q8(const AttnArgs& a, void* k_cache, void* v_cache, hip
 }
 
 // ---------------------------------------------------------------------------
-// Longest-first order of the sequences: thread b ranks its attended count
-// (sliding-window view when set) against every other sequence's (ties by
-// index) and writes its index at that rank.  Quadratic in B, used for
-// B <= kMaxOrderedBatch.
+// Longest-first order of the work items (sequence, split): thread i ranks its
+// item's slot count (the split's share of the sequence's attended count, in
+// the sliding window's view when set) against every other item's (ties by
+// index) and writes its index at that rank.  Quadratic in the item count,
+// used for at most kMaxOrderedBatch items.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int attended_span(const AttnArgs& a, int b) {
+__device__ __forceinline__ int item_work(const AttnArgs& a, int item) {
+  const int b = item / a.nsplit;
+  const int split = item - b * a.nsplit;
   int n = a.lengths[b] + a.len_offset;
   n = n < 0 ? 0 : (n > a.S ? a.S : n);
-  return a.window > 0 ? seq_view(a, b, n).nv : n;
+  if (a.window > 0) n = seq_view(a, b, n).nv;
+  return max(0, min(n - split * a.split_tokens, a.split_tokens));
 }
 
 __global__ __launch_bounds__(256) void order_kernel(AttnArgs a, int32_t* __restrict__ order) {
-  const int b = blockIdx.x * 256 + threadIdx.x;
-  if (b >= a.B) return;
-  const int nb = attended_span(a, b);
+  const int items = a.B * a.nsplit;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= items) return;
+  const int wi = item_work(a, i);
   int rank = 0;
-  for (int j = 0; j < a.B; ++j) {
-    const int nj = attended_span(a, j);
-    rank += (nj > nb || (nj == nb && j < b)) ? 1 : 0;
+  for (int j = 0; j < items; ++j) {
+    const int wj = item_work(a, j);
+    rank += (wj > wi || (wj == wi && j < i)) ? 1 : 0;
   }
-  order[rank] = b;
+  order[rank] = i;
 }
 
 hipError_t launch_order(const AttnArgs& a, int32_t* order, hipStream_t s) {
   AttnArgs arg = a;
   void* params[] = {&arg, &order};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&order_kernel), dim3((unsigned)((a.B + 255) / 256)), dim3(256),
-                         params, 0, s);
+  const int items = a.B * a.nsplit;
+  return hipLaunchKernel(reinterpret_cast<const void*>(&order_kernel), dim3((unsigned)((items + 255) / 256)),
+                         dim3(256), params, 0, s);
 }
 
 // ---------------------------------------------------------------------------

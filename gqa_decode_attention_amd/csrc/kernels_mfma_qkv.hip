@@ -237,8 +237,14 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
   // the round-robin dispatch puts them on the same XCD at about the same time
   // and only the first of them reads the rows from HBM (the others from L2).
   int x = blockIdx.x;
-  const int split = x % a.nsplit;
+  int split = x % a.nsplit;
   x /= a.nsplit;
+  if (a.order != nullptr) {  // longest items first: x = (item rank) * Hkv + h, item = b * nsplit + split
+    const int item = a.order[blockIdx.x / a.Hkv];
+    const int bq = item / a.nsplit;
+    split = item - bq * a.nsplit;
+    x = bq * a.Hkv + (int)(blockIdx.x % a.Hkv);
+  }
   int hc = 0, bh = x;
   if (a.head_chunks > 1) {
     const int HC = a.head_chunks;
@@ -250,7 +256,7 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
     bh = grp * 8 + rem % gsz;
   }
   const int h = bh % a.Hkv;
-  const int b = a.order != nullptr ? a.order[bh / a.Hkv] : bh / a.Hkv;  // longest sequences first
+  const int b = bh / a.Hkv;
   const int hq0 = h * a.G + 16 * hc;       // first query head of this workgroup
   const int G = min(16, a.G - 16 * hc);   // query heads in this workgroup
 
