@@ -56,7 +56,7 @@ class PlanT(ctypes.Structure):
         ("block", ctypes.c_int32),
         ("combine", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
-        ("length_order", ctypes.c_int32),
+        ("balanced", ctypes.c_int32),
     ]
 
 
@@ -233,7 +233,7 @@ def get_plan(desc: Desc) -> dict:
     check(lib().gqa_decode_get_plan(ctypes.byref(desc), ctypes.byref(p)), "gqa_decode_get_plan")
     return dict(kernel=KERNEL_NAMES.get(p.kernel, p.kernel), num_splits=p.num_splits, split_tokens=p.split_tokens,
                 grid=p.grid, block=p.block, combine=bool(p.combine), workspace_bytes=p.workspace_bytes,
-                length_order=bool(p.length_order))
+                balanced=bool(p.balanced))
 
 
 def _dev(tensors, lengths):

@@ -125,17 +125,26 @@ gqa_status_t make_plan(const gqa_decode_desc_t* d, Plan* p, int64_t span = 0) {
     p->off_l = p->off_m + align256(nparts * sizeof(float));
     p->workspace_bytes = p->off_l + align256(nparts * sizeof(float));
   }
-  // More MFMA_QK workgroups than CUs: the work per workgroup follows the
-  // sequence lengths, so the work items (sequence, split) are dealt out
-  // longest first (a small kernel ranks them on the device) and run one
-  // workgroup per CU, and the dispatcher's in-order hand-out of the rest is a
-  // longest-processing-time schedule.  Not for huge batches (the ranking is
-  // quadratic in the item count).
-  if (p->kernel == GQA_KERNEL_MFMA_QK && p->head_chunks == 1 && grid > kNumCUs && B * nsplit > 1 &&
-      B * nsplit <= kMaxOrderedBatch) {
-    p->order = 1;
-    p->off_order = p->workspace_bytes;
-    p->workspace_bytes += align256((size_t)(B * nsplit) * sizeof(int32_t));
+  // More MFMA_QK work items (sequence, kv-head) than CUs and no forced split
+  // count: balanced mode.  The work per item follows the sequence lengths, so
+  // instead of one workgroup per item, one workgroup per CU takes an equal
+  // contiguous range of the batch's 16-slot tiles (cut on the device from the
+  // lengths), and the items cut between workgroups are merged by the balanced
+  // combine pass.  Its partials: two rows of G heads per workgroup.  Not for
+  // huge batches (each workgroup scans the lengths of the whole batch).
+  int64_t tiles_max;
+  if (p->kernel == GQA_KERNEL_MFMA_QK && p->head_chunks == 1 && d->num_splits == 0 && B * Hkv > kNumCUs &&
+      B <= kMaxBalancedBatch && mul_ok(B * Hkv, S / 16 + 1, &tiles_max) && tiles_max < INT32_MAX) {
+    const size_t rows = (size_t)kNumCUs * 2 * G;
+    p->balanced = 1;
+    p->nsplit = 1;
+    p->split_tokens = (int32_t)S;
+    p->grid = kNumCUs;
+    p->combine = 1;
+    p->off_m = align256(rows * D * sizeof(float));
+    p->off_l = p->off_m + align256(rows * sizeof(float));
+    p->off_pre = p->off_l + align256(rows * sizeof(float));
+    p->workspace_bytes = p->off_pre + align256((size_t)(B + 1) * sizeof(int32_t));
   }
   return GQA_OK;
 }
@@ -322,10 +331,13 @@ gqa_status_t check_attend_ptrs(const gqa_decode_desc_t* d, const gqa_cache_map_t
 
 gqa_status_t run_attend(const gqa_decode_desc_t* d, const Plan& p, AttnArgs& a, hipStream_t s, void* workspace) {
   hipError_t e;
-  if (p.order) {
-    int32_t* order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + p.off_order);
-    if (launch_order(a, order, s) != hipSuccess) return GQA_ERR_HIP;
-    a.order = order;
+  if (p.balanced) {
+    char* w = static_cast<char*>(workspace);
+    a.part_o = reinterpret_cast<float*>(w);
+    a.part_m = reinterpret_cast<float*>(w + p.off_m);
+    a.part_l = reinterpret_cast<float*>(w + p.off_l);
+    a.bal_pre = reinterpret_cast<int32_t*>(w + p.off_pre);
+    a.bal_units = p.grid;
   }
   switch (p.kernel) {
     case GQA_KERNEL_MFMA_QK: e = launch_attend_mfma_qk(a, p, s); break;
@@ -374,7 +386,7 @@ gqa_status_t gqa_decode_get_plan(const gqa_decode_desc_t* desc, gqa_decode_plan_
     plan->block = p.block;
     plan->combine = p.combine;
     plan->workspace_bytes = p.workspace_bytes;
-    plan->length_order = p.order;
+    plan->balanced = p.balanced;
     return GQA_OK;
   } catch (...) {
     return GQA_ERR_INTERNAL;

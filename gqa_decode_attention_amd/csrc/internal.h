@@ -23,6 +23,7 @@ struct AttnArgs {
   float* part_o;         // split partials: [B][Hq][nsplit][D] unnormalised sums
   float* part_m;         // [B][Hq][nsplit] running max (log2 units)
   float* part_l;         // [B][Hq][nsplit] softmax denominators
+                         // (balanced mode: rows [grid][2][G] instead of [B][Hq][nsplit])
   int32_t B, Hq, Hkv, D, S, G;
   int64_t sb, sh, st;    // cache element strides of cache row, kv-head, slot (paged: within a block)
   // Cache map (mapped entry points): map_kind 0 = dense (row b), GQA_MAP_SLOTS
@@ -56,9 +57,10 @@ struct AttnArgs {
   float cap_T, cap_invT;
   int32_t window, prefix;
   const int32_t* prefix_seq;
-  // Longest-first order of the work items (order[k] = b * nsplit + split of
-  // the item with the k-th largest slot count), or null for grid order.
-  const int32_t* order;
+  // Balanced mode (MFMA_QK): tile offsets of the sequences (B + 1 entries,
+  // written by the attention pass for the combine pass), or null in split mode.
+  int32_t* bal_pre;
+  int32_t bal_units;     // balanced mode: workgroups of the attention pass
   int32_t nsplit, split_tokens;
   int32_t head_chunks;   // generic kernel: query-head chunks per kv-head
   int32_t len_offset;    // slots attended = lengths[b] + len_offset (1 for a step, 0 for attend)
@@ -76,8 +78,8 @@ struct Plan {
   int32_t combine;
   size_t workspace_bytes;
   size_t off_m, off_l;   // byte offsets of part_m / part_l inside the workspace
-  int32_t order;         // 1: sequences are dealt out longest first (see AttnArgs::order)
-  size_t off_order;      // byte offset of that order inside the workspace
+  int32_t balanced;      // 1: equal tile ranges per workgroup (see AttnArgs::bal_pre)
+  size_t off_pre;        // byte offset of the tile offsets inside the workspace
 };
 
 // Which matrix-core kernels this build provides (the planner falls back to the
@@ -89,12 +91,10 @@ extern const bool kHaveMfmaQkI8;  // int8 caches on the G <= 16 matrix-core kern
 constexpr int kNumCUs = 256;          // MI355X: 8 XCDs x 32 CUs
 constexpr int kMaxSplits = 64;        // one lane per split in the combine pass
 constexpr int kGenericHeadChunk = 8;  // query heads per workgroup in the generic kernel
-constexpr int kMaxOrderedBatch = 4096;  // most (sequence, split) items ranked by length on the device
+constexpr int kMaxBalancedBatch = 4096;  // most sequences in the balanced mode (16 per thread of its scan)
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_append(const AttnArgs& a, void* k_cache, void* v_cache, hipStream_t s);
-// Work items (sequence, split) by slot count, longest first (ties by index), into `order`.
-hipError_t launch_order(const AttnArgs& a, int32_t* order, hipStream_t s);
 // Rotary append: rotates (and normalizes) the new key, writes it and the value
 // at slot lengths[b] (int8 caches: quantized), and, when a.q_rot is set, the
 // rotated (and normalized) q into a.q_rot.

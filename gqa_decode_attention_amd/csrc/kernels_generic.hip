@@ -119,43 +119,6 @@ hipError_t launch_append_q8(const AttnArgs& a, void* k_cache, void* v_cache, hip
 }
 
 // ---------------------------------------------------------------------------
-// Longest-first order of the work items (sequence, split): thread i ranks its
-// item's slot count (the split's share of the sequence's attended count, in
-// the sliding window's view when set) against every other item's (ties by
-// index) and writes its index at that rank.  Quadratic in the item count,
-// used for at most kMaxOrderedBatch items.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ int item_work(const AttnArgs& a, int item) {
-  const int b = item / a.nsplit;
-  const int split = item - b * a.nsplit;
-  int n = a.lengths[b] + a.len_offset;
-  n = n < 0 ? 0 : (n > a.S ? a.S : n);
-  if (a.window > 0) n = seq_view(a, b, n).nv;
-  return max(0, min(n - split * a.split_tokens, a.split_tokens));
-}
-
-__global__ __launch_bounds__(256) void order_kernel(AttnArgs a, int32_t* __restrict__ order) {
-  const int items = a.B * a.nsplit;
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= items) return;
-  const int wi = item_work(a, i);
-  int rank = 0;
-  for (int j = 0; j < items; ++j) {
-    const int wj = item_work(a, j);
-    rank += (wj > wi || (wj == wi && j < i)) ? 1 : 0;
-  }
-  order[rank] = i;
-}
-
-hipError_t launch_order(const AttnArgs& a, int32_t* order, hipStream_t s) {
-  AttnArgs arg = a;
-  void* params[] = {&arg, &order};
-  const int items = a.B * a.nsplit;
-  return hipLaunchKernel(reinterpret_cast<const void*>(&order_kernel), dim3((unsigned)((items + 255) / 256)),
-                         dim3(256), params, 0, s);
-}
-
-// ---------------------------------------------------------------------------
 // Rotary append (CLIKA "groupQueryAttention" page: q and the new k rotated with
 // the rope planes, optional post-rotation RMS norm with gains, the rotated key
 // appended in place).  The rows of (b, kv-head) are k, v, then its G query
@@ -638,6 +601,70 @@ __global__ __launch_bounds__(256) void combine128_kernel(AttnArgs a) {
   }
 }
 
+// Balanced-mode combine (head width 128): one wave per (b, hq) row.  Item
+// (b, h) covers tiles [s, e) of the batch's tile sequence (offsets written by
+// the attention pass); workgroup k of `a.bal_units` held tiles
+// [k per, (k + 1) per).  An item inside one workgroup's range was written by
+// the attention pass; a cut one left a partial in every workgroup it touched:
+// row 2k + 1 of the first workgroup when the item starts inside its range,
+// row 2k + 0 otherwise.  The partials merge by the same log-sum-exp rule as
+// the split combine, any number of them (64 per round).
+template <int QO>
+__global__ __launch_bounds__(256) void combine_balanced_kernel(AttnArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t bh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // b * Hq + hq
+  if (bh >= (int64_t)a.B * a.Hq) return;  // whole waves only; no workgroup barrier follows
+  const int b = (int)(bh / a.Hq);
+  const int hq = (int)(bh - (int64_t)b * a.Hq);
+  const int h = hq / a.G;
+  const int g = hq - h * a.G;
+  const int* pre = a.bal_pre;
+  const int T = pre[a.B];
+  const int W = a.bal_units;  // workgroups of the attention pass
+  const int per = (T + W - 1) / W;
+  const int cb = (pre[b + 1] - pre[b]) / a.Hkv;
+  const int s0 = pre[b] + h * cb;
+  const int k0 = s0 / per, k1 = (s0 + cb - 1) / per;
+  if (k0 == k1) return;  // whole in one workgroup: written by the attention pass
+  const int np = k1 - k0 + 1;
+  auto row = [&](int i) -> int64_t {  // partial row of the i-th piece
+    const int k = k0 + i;
+    return (2 * (int64_t)k + ((i == 0 && s0 != k * per) ? 1 : 0)) * a.G + g;
+  };
+  float M = kNegInf;
+  for (int i0 = 0; i0 < np; i0 += 64) {
+    const int i = i0 + lane;
+    M = fmaxf(M, wave_max(i < np ? a.part_m[row(i)] : kNegInf));
+  }
+  const int q = lane & 31;
+  const int half = lane >> 5;
+  float L = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int i0 = 0; i0 < np; i0 += 64) {
+    const int i = i0 + lane;
+    const float w = i < np ? fast_exp2(a.part_m[row(i)] - M) : 0.f;
+    L += wave_sum(i < np ? w * a.part_l[row(i)] : 0.f);
+    const int nr = min(64, np - i0);
+    for (int j = half; j < nr; j += 2) {
+      const float wj = __shfl(w, j);
+      acc += wj * reinterpret_cast<const f32x4*>(a.part_o + row(i0 + j) * 128)[q];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], 32);
+  if (half == 0) {
+    const float inv = a.sink != nullptr || a.smooth ? finish_scale(a, hq, M, L) : (L > 0.f ? 1.f / L : 0.f);
+    if (QO == GQA_F32) {
+      reinterpret_cast<f32x4*>(a.out)[bh * 32 + q] = acc * inv;
+    } else {
+      const uint32_t lo = (uint32_t)f32_to_bf16_rne(acc[0] * inv) | ((uint32_t)f32_to_bf16_rne(acc[1] * inv) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16_rne(acc[2] * inv) | ((uint32_t)f32_to_bf16_rne(acc[3] * inv) << 16);
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      reinterpret_cast<u32x2*>(a.out)[bh * 32 + q] = u32x2{lo, hi};
+    }
+  }
+}
+
 hipError_t launch_combine(const AttnArgs& a, const Plan& p, hipStream_t s) {
   (void)p;
   const unsigned blocks = (unsigned)(((int64_t)a.B * a.Hq + 3) / 4);
@@ -646,7 +673,11 @@ hipError_t launch_combine(const AttnArgs& a, const Plan& p, hipStream_t s) {
   const bool fast = a.D == 128 && (reinterpret_cast<uintptr_t>(a.out) & 15) == 0 &&
                     (reinterpret_cast<uintptr_t>(a.part_o) & 15) == 0;
   const void* fn;
-  if (fast) {
+  if (a.bal_pre != nullptr) {
+    if (a.D != 128 || !fast) return hipErrorInvalidValue;
+    fn = a.qo_dtype == GQA_F32 ? reinterpret_cast<const void*>(&combine_balanced_kernel<GQA_F32>)
+                               : reinterpret_cast<const void*>(&combine_balanced_kernel<GQA_BF16>);
+  } else if (fast) {
     fn = a.qo_dtype == GQA_F32 ? reinterpret_cast<const void*>(&combine128_kernel<GQA_F32>)
                                : reinterpret_cast<const void*>(&combine128_kernel<GQA_BF16>);
   } else {

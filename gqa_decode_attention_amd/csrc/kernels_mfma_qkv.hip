@@ -42,6 +42,7 @@
 // Paged bf16 caches (CLIKA runtime "groupQueryAttention" API page, block
 // table): with a block size that is a multiple of 16, every 16-slot tile lies
 // in one block, whose table entry each wave loads a tile pair ahead.
+#include <algorithm>
 #include <type_traits>
 
 #include "cache_map.h"
@@ -219,60 +220,36 @@ __device__ __forceinline__ void tile_math(State& st, const u32x4 (&qf)[4], const
   });
 }
 
-template <int KV, int NW, bool PAGED, bool VAR>
-__global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
-  static_assert(!(PAGED && KV == GQA_I8), "int8 caches are dense");
-  __shared__ float sm_o[NW][16][kDq];
-  __shared__ float sm_m[NW][16];
-  __shared__ float sm_l[NW][16];
+// One piece of work of a workgroup: virtual slots [t_begin, t_end) of
+// (sequence b, kv-head h, query-head chunk hc).  `whole`: the piece is all of
+// the sequence's slots, so its rows are final and go to `out`; otherwise they
+// are partials (m, l, o) at rows pbase + pstride * g of the split workspace
+// (g = head within the chunk).  Every wave of the workgroup calls it with the
+// same arguments (it holds workgroup barriers).
+struct Piece {
+  int b, h, hc;
+  int t_begin, t_end;  // virtual slots
+  int L;               // lengths[b]
+  SeqView view;
+  bool whole;
+  int64_t pbase, pstride;
+};
 
+template <int KV, int NW, bool PAGED, bool VAR>
+__device__ __forceinline__ void attend_piece(const AttnArgs& a, const Piece& pc, float (*sm_o)[16][kDq],
+                                             float (*sm_m)[16], float (*sm_l)[16]) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r = lane >> 4;
   const int c = lane & 15;
-
-  // Workgroup -> (split, query-head chunk, b, kv-head).  Groups of more than
-  // 16 query heads are served 16 at a time by head chunks that all read the
-  // same K/V rows; the chunks of one (b, kv-head) are numbered 8 apart, so
-  // the round-robin dispatch puts them on the same XCD at about the same time
-  // and only the first of them reads the rows from HBM (the others from L2).
-  int x = blockIdx.x;
-  int split = x % a.nsplit;
-  x /= a.nsplit;
-  if (a.order != nullptr) {  // longest items first: x = (item rank) * Hkv + h, item = b * nsplit + split
-    const int item = a.order[blockIdx.x / a.Hkv];
-    const int bq = item / a.nsplit;
-    split = item - bq * a.nsplit;
-    x = bq * a.Hkv + (int)(blockIdx.x % a.Hkv);
-  }
-  int hc = 0, bh = x;
-  if (a.head_chunks > 1) {
-    const int HC = a.head_chunks;
-    const int units = a.B * a.Hkv;
-    const int grp = x / (8 * HC);
-    const int gsz = min(8, units - grp * 8);  // the last group may hold fewer (b, kv-head) units
-    const int rem = x - grp * 8 * HC;
-    hc = rem / gsz;
-    bh = grp * 8 + rem % gsz;
-  }
-  const int h = bh % a.Hkv;
-  const int b = bh / a.Hkv;
+  const int b = pc.b, h = pc.h, hc = pc.hc;
   const int hq0 = h * a.G + 16 * hc;       // first query head of this workgroup
   const int G = min(16, a.G - 16 * hc);   // query heads in this workgroup
-
-  const int L = a.lengths[b];
-  int n = L + a.len_offset;
-  n = n < 0 ? 0 : (n > a.S ? a.S : n);
-  // Slots are walked in the sliding window's virtual order (the identity
-  // without a window); `nv` virtual slots, the new token is the last.
-  SeqView view{n, n, 0, 0, 0};
-  if constexpr (VAR) view = seq_view(a, b, n);
-  const int nv = view.nv;
+  const int L = pc.L;
+  const SeqView& view = pc.view;
   const int Lv = L - view.gap;
-  const int t_begin = split * a.split_tokens;
-  const int t_end = min(t_begin + a.split_tokens, nv);
-  const int nact = nv == 0 ? 0 : min(a.nsplit, (nv + a.split_tokens - 1) / a.split_tokens);
-  if (split >= max(nact, 1)) return;
+  const int t_begin = pc.t_begin;
+  const int t_end = pc.t_end;
 
   // Fused step: slot L is taken from k_new / v_new (int8 caches: quantized here).
   const bool own_new = a.k_new != nullptr && Lv >= t_begin && Lv < t_end;
@@ -534,12 +511,12 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
       Lsum += sm_l[w][g] * sc;
     }
     const int hq = hq0 + g;
-    if (nact <= 1) {
+    if (pc.whole) {
       reinterpret_cast<uint16_t*>(a.out)[((int64_t)b * a.Hq + hq) * kDq + d] =
           f32_to_bf16_rne(VAR || a.sink != nullptr || a.smooth ? finish_row(a, hq, M, O, Lsum)
                                                               : (Lsum > 0.f ? O / Lsum : 0.f));
     } else {
-      const int64_t pi = ((int64_t)b * a.Hq + hq) * a.nsplit + split;
+      const int64_t pi = pc.pbase + pc.pstride * g;
       a.part_o[pi * kDq + d] = O;
       if (d == 0) {
         a.part_m[pi] = M;
@@ -549,12 +526,163 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
   }
 }
 
+
+// Tile counts in the balanced mode: a sequence's virtual slots in 16-slot
+// tiles, at least one (an empty sequence still writes its zero rows).
+__device__ __forceinline__ int seq_tiles(const AttnArgs& a, int b) {
+  int n = a.lengths[b] + a.len_offset;
+  n = n < 0 ? 0 : (n > a.S ? a.S : n);
+  if (a.window > 0) n = seq_view(a, b, n).nv;
+  return max(1, (n + 15) >> 4);
+}
+
+template <int KV, int NW, bool PAGED, bool VAR>
+__global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
+  static_assert(!(PAGED && KV == GQA_I8), "int8 caches are dense");
+  __shared__ float sm_o[NW][16][kDq];
+  __shared__ float sm_m[NW][16];
+  __shared__ float sm_l[NW][16];
+  extern __shared__ int32_t sm_pre[];  // balanced mode: tile offsets of the sequences (B + 1 entries)
+
+  auto piece_of = [&](int b, int h, int hc, int t_begin, int t_end, bool whole, int64_t pbase, int64_t pstride) {
+    Piece pc;
+    pc.b = b;
+    pc.h = h;
+    pc.hc = hc;
+    pc.L = a.lengths[b];
+    int n = pc.L + a.len_offset;
+    n = n < 0 ? 0 : (n > a.S ? a.S : n);
+    // Slots are walked in the sliding window's virtual order (the identity
+    // without a window); the new token is the last virtual slot.
+    pc.view = SeqView{n, n, 0, 0, 0};
+    if constexpr (VAR) pc.view = seq_view(a, b, n);
+    pc.t_begin = t_begin;
+    pc.t_end = min(t_end, pc.view.nv);
+    pc.whole = whole;
+    pc.pbase = pbase;
+    pc.pstride = pstride;
+    return pc;
+  };
+
+  int lo = 0, hi = 0;  // balanced mode: this workgroup's tile range
+  Piece split_piece;   // split mode: the workgroup's piece
+  if (a.bal_pre != nullptr) {
+    // Balanced mode (ragged batches): the batch's work is cut into equal
+    // contiguous ranges of 16-slot tiles, one per workgroup (one workgroup per
+    // CU).  Sequence b holds Hkv items (b, h) of c_b tiles each; item (b, h)
+    // is tiles [P_b + h c_b, P_b + (h + 1) c_b) with P_b = Hkv * sum of c_b'
+    // over b' < b.  A workgroup attends each piece of an item that falls in its
+    // range: a whole item writes its output rows, a cut one leaves partials at
+    // workspace row 2 * blockIdx + (0 for the range's first piece, 1 for its
+    // last), which the balanced combine pass merges.
+    const int B = a.B;
+    const int nt = blockDim.x;
+    const int per_t = (B + nt - 1) / nt;  // consecutive sequences per thread (at most 16)
+    const int b0 = threadIdx.x * per_t;
+    int cnt[16];
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      cnt[i] = (i < per_t && b0 + i < B) ? a.Hkv * seq_tiles(a, b0 + i) : 0;
+      sum += cnt[i];
+    }
+    // Exclusive scan of the per-thread sums: within each wave, then across waves.
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int inc = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(inc, off);
+      if (lane >= off) inc += y;
+    }
+    __shared__ int32_t wsum[NW];
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += wsum[w];
+    int run = base + inc - sum;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i < per_t && b0 + i < B) sm_pre[b0 + i] = run;
+      run += cnt[i];
+    }
+    if (threadIdx.x == nt - 1) sm_pre[B] = base + inc;
+    __syncthreads();
+    if (blockIdx.x == 0) {  // the offsets for the combine pass
+      for (int i = threadIdx.x; i <= B; i += nt) a.bal_pre[i] = sm_pre[i];
+    }
+    const int T = sm_pre[B];
+    const int per = (T + (int)gridDim.x - 1) / (int)gridDim.x;
+    lo = (int)blockIdx.x * per;
+    hi = min(lo + per, T);
+    if (lo >= hi) return;
+  } else {
+    // Split mode: workgroup -> (split, query-head chunk, b, kv-head).  Groups
+    // of more than 16 query heads are served 16 at a time by head chunks that
+    // all read the same K/V rows; the chunks of one (b, kv-head) are numbered 8
+    // apart, so the round-robin dispatch puts them on the same XCD at about the
+    // same time and only the first of them reads the rows from HBM (the others
+    // from L2).
+    int x = blockIdx.x;
+    const int split = x % a.nsplit;
+    x /= a.nsplit;
+    int hc = 0, bh = x;
+    if (a.head_chunks > 1) {
+      const int HC = a.head_chunks;
+      const int units = a.B * a.Hkv;
+      const int grp = x / (8 * HC);
+      const int gsz = min(8, units - grp * 8);  // the last group may hold fewer (b, kv-head) units
+      const int rem = x - grp * 8 * HC;
+      hc = rem / gsz;
+      bh = grp * 8 + rem % gsz;
+    }
+    const int h = bh % a.Hkv;
+    const int b = bh / a.Hkv;
+    const int t_begin = split * a.split_tokens;
+    Piece pc = piece_of(b, h, hc, t_begin, t_begin + a.split_tokens, false, 0, 0);
+    const int nv = pc.view.nv;
+    const int nact = nv == 0 ? 0 : min(a.nsplit, (nv + a.split_tokens - 1) / a.split_tokens);
+    if (split >= max(nact, 1)) return;
+    pc.whole = nact <= 1;
+    pc.pbase = ((int64_t)b * a.Hq + h * a.G + 16 * hc) * a.nsplit + split;
+    pc.pstride = a.nsplit;
+    split_piece = pc;
+  }
+
+  // Split mode: the one piece; balanced mode: the pieces of [lo, hi), in order.
+  for (int t = lo;;) {
+    Piece pc = split_piece;
+    int step = 0;
+    if (a.bal_pre != nullptr) {
+      int l0 = 0, l1 = a.B;  // pre[l0] <= t < pre[l1]
+      while (l1 - l0 > 1) {
+        const int mid = (l0 + l1) >> 1;
+        if (sm_pre[mid] <= t) l0 = mid;
+        else l1 = mid;
+      }
+      const int b = l0;
+      const int cb = (sm_pre[b + 1] - sm_pre[b]) / a.Hkv;
+      const int off = t - sm_pre[b];
+      const int h = off / cb;
+      const int j0 = off - h * cb;
+      const int j1 = min(cb, j0 + (hi - t));
+      const int64_t pbase = (2 * (int64_t)blockIdx.x + (t == lo ? 0 : 1)) * a.G;
+      pc = piece_of(b, h, 0, 16 * j0, 16 * j1, j0 == 0 && j1 == cb, pbase, 1);
+      step = j1 - j0;
+    }
+    attend_piece<KV, NW, PAGED, VAR>(a, pc, sm_o, sm_m, sm_l);
+    t += step;
+    if (t >= hi) break;
+    __syncthreads();  // the next piece reuses the merge buffers
+  }
+}
+
+
 }  // namespace qkv
 
 using qkv::attend_mfma_qkv_kernel;
 
 // Dynamic LDS that, with the kernel's 33 KB static arrays, exceeds half of a
-// CU's 160 KB.
+// CU's 160 KB (one workgroup per CU).
 constexpr unsigned kOneWorkgroupLds = 48u * 1024u;
 
 const bool kHaveMfmaQk = true;
@@ -582,10 +710,14 @@ hipError_t launch_attend_mfma_qk(const AttnArgs& a, const Plan& p, hipStream_t s
   }
   AttnArgs arg = a;
   void* params[] = {&arg};
-  // Dealt out longest first: an unused dynamic LDS reservation keeps one
-  // workgroup per CU (two would exceed the CU's 160 KB), so the rest wait in
-  // dispatch order and take the next CU that frees up.
-  const unsigned lds = a.order != nullptr ? kOneWorkgroupLds : 0u;
+  // Balanced mode: one workgroup per CU (the tile ranges are equal only if all
+  // of them run at once).  The dynamic LDS holds the sequences' tile offsets
+  // and, with the kernel's 33 KB static arrays, exceeds half of a CU's 160 KB.
+  unsigned lds = 0;
+  if (a.bal_pre != nullptr) {
+    if (a.B > kMaxBalancedBatch || a.head_chunks != 1 || p.grid != kNumCUs) return hipErrorInvalidValue;
+    lds = std::max<unsigned>(kOneWorkgroupLds, (unsigned)(a.B + 1) * 4u);
+  }
   return hipLaunchKernel(fn, dim3(p.grid), dim3(p.block), params, lds, s);
 }
 

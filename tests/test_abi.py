@@ -230,12 +230,29 @@ def test_plan_is_a_function_of_the_descriptor_only():
         assert p1["workspace_bytes"] == g.workspace_size(d)
         assert p1["num_splits"] * p1["split_tokens"] >= d.capacity
         assert (p1["num_splits"] - 1) * p1["split_tokens"] < d.capacity     # no empty split
-        assert p1["combine"] == (p1["num_splits"] > 1)
+        assert p1["combine"] == (p1["num_splits"] > 1 or p1["balanced"])
         assert p1["num_splits"] <= 64
-        # the workspace holds split partials, and the length order when sequences are ranked
-        assert (p1["workspace_bytes"] == 0) == (p1["num_splits"] == 1 and not p1["length_order"])
-        if p1["length_order"]:
-            assert p1["kernel"] == "mfma_qk" and p1["grid"] > 256
+        # the workspace holds split partials, or the balanced mode's partials and tile offsets
+        assert (p1["workspace_bytes"] == 0) == (p1["num_splits"] == 1 and not p1["balanced"])
+        if p1["balanced"]:
+            # more (b, kv-head) items than CUs: one workgroup per CU, two partial rows of G heads each
+            assert p1["kernel"] == "mfma_qk" and p1["grid"] == 256 and p1["num_splits"] == 1
+            assert d.batch * d.num_kv_heads > 256
+            G = d.num_q_heads // d.num_kv_heads
+            assert p1["workspace_bytes"] >= 256 * 2 * G * (d.head_dim + 2) * 4 + (d.batch + 1) * 4
+
+
+def test_balanced_mode_only_where_items_outnumber_cus():
+    """The balanced mode replaces one workgroup per (b, kv-head) item only when
+    the items outnumber the CUs, no split count is forced, and the batch fits
+    the kernel's on-device scan (4096 sequences)."""
+    assert not g.get_plan(desc(batch=32, num_q_heads=32, num_kv_heads=8, capacity=4097))["balanced"]   # 256 items
+    assert g.get_plan(desc(batch=33, num_q_heads=32, num_kv_heads=8, capacity=4097))["balanced"]
+    assert g.get_plan(desc(batch=64, num_q_heads=64, num_kv_heads=8, capacity=8192, layout="BSHD"))["balanced"]
+    assert not g.get_plan(desc(batch=64, num_q_heads=64, num_kv_heads=8, capacity=8192, num_splits=1))["balanced"]
+    assert g.get_plan(desc(batch=4096, num_q_heads=8, num_kv_heads=1, capacity=64))["balanced"]
+    assert not g.get_plan(desc(batch=4097, num_q_heads=8, num_kv_heads=1, capacity=64))["balanced"]
+    assert not g.get_plan(desc(batch=300, num_q_heads=8, num_kv_heads=1, kv_dtype=g.F32, qo_dtype=g.F32))["balanced"]
 
 
 @pytest.mark.parametrize("ns", [1, 2, 3, 7, 64, 10_000])

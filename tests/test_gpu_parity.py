@@ -409,19 +409,20 @@ def test_full_size_workload(g, name):
 
 
 @pytest.mark.parametrize("kind", ["dense", "paged", "int8", "window"])
-def test_longest_first_order_matches_oracle(g, kind):
-    """More matrix-core workgroups than CUs: the plan ranks the sequences by
-    length on the device and deals them out longest first.  Shuffled ragged
-    lengths (including 0 and the full capacity) on dense, paged and int8
-    caches and with a sliding window must match the oracle."""
+def test_balanced_mode_matches_oracle(g, kind):
+    """More (b, kv-head) items than CUs: the plan switches to the balanced mode
+    (equal tile ranges per workgroup, cut on the device from the lengths, and a
+    combine of the items cut between workgroups).  Shuffled ragged lengths
+    (including 0 and the full capacity) on dense, paged and int8 caches and
+    with a sliding window must match the oracle."""
     B, Hq, Hkv, D, S = 40, 32, 8, 128, 300
     kv = "i8" if kind == "int8" else "bf16"
     w = W.custom(B, Hq, Hkv, D, S, "BHSD", kv, "bf16", seed=91, stale="pm:1")
     L = torch.randint(0, S, (B,), generator=torch.Generator().manual_seed(92), dtype=torch.int32)
     L[5], L[17], L[30] = 0, S - 1, S - 1
     desc = g.make_desc(B, Hq, Hkv, D, S, "BHSD", g.I8 if kind == "int8" else g.BF16, g.BF16)
-    assert g.get_plan(desc)["length_order"]
-    say(f"ordered {kind}")
+    assert g.get_plan(desc)["balanced"]
+    say(f"balanced {kind}")
     if kind == "int8":
         inp = W.make_q8(w, DEV, lengths=L)
         ref, rk, rv, rks, rvs = oracle.step_q8(np_of(inp["q"]), "bf16", np_of(inp["k_cache"]), np_of(inp["v_cache"]),
@@ -459,4 +460,51 @@ def test_longest_first_order_matches_oracle(g, kind):
                      layout="BHSD")
     torch.cuda.synchronize()
     assert_close(out, ref, "bf16", f"{kind} step")
+    assert np_of(inp["k_cache"]).tobytes() == rk.tobytes() and np_of(inp["v_cache"]).tobytes() == rv.tobytes()
+
+
+@pytest.mark.parametrize("case", ["one_long", "attend_empty", "sink_bshd"])
+def test_balanced_mode_edge_cases(g, case):
+    """Balanced-mode cases: one long sequence among many short ones (its items
+    are cut across more than 64 workgroups, so the combine merges its partials
+    in several rounds), attend with empty sequences (zero rows, never cut),
+    and a per-head sink on a (B, S, Hkv, D) cache."""
+    if case == "one_long":
+        B, Hq, Hkv, S, lay = 300, 16, 1, 20000, "BHSD"
+        L = torch.randint(0, 40, (B,), generator=torch.Generator().manual_seed(93), dtype=torch.int32)
+        L[123] = S - 1
+    elif case == "attend_empty":
+        B, Hq, Hkv, S, lay = 70, 32, 4, 700, "BHSD"
+        L = torch.randint(0, S + 1, (B,), generator=torch.Generator().manual_seed(94), dtype=torch.int32)
+        L[0], L[9], L[69] = 0, 0, S
+    else:
+        B, Hq, Hkv, S, lay = 36, 64, 8, 520, "BSHD"
+        L = torch.randint(0, S, (B,), generator=torch.Generator().manual_seed(95), dtype=torch.int32)
+    qo = "bf16"
+    w = W.custom(B, Hq, Hkv, 128, S, lay, "bf16", qo, seed=96, stale="pm:100")
+    inp = W.make_inputs(w, DEV, lengths=L)
+    desc = g.make_desc(B, Hq, Hkv, 128, S, lay, g.BF16, g.BF16)
+    assert g.get_plan(desc)["balanced"]
+    say(f"balanced {case}: B={B} Hq={Hq} Hkv={Hkv} S={S} {lay}")
+    args = (np_of(inp["q"]), qo, np_of(inp["k_cache"]), np_of(inp["v_cache"]))
+    if case == "attend_empty":
+        ref = oracle.attend(*args, "bf16", L.numpy(), lay, Hq, Hkv)
+        out = g.attend(inp["q"], inp["k_cache"], inp["v_cache"], inp["lengths"], layout=lay)
+        torch.cuda.synchronize()
+        got = out.float().cpu().double().numpy()
+        empty = L.numpy() == 0
+        assert np.all(got[empty] == 0.0)
+        assert_close(out[torch.from_numpy(~empty).to(DEV)], ref[~empty], qo, "balanced attend")
+        return
+    if case == "sink_bshd":
+        sink = torch.randn(Hq, generator=torch.Generator().manual_seed(97)).to(DEV)
+        ref, rk, rv = oracle.step_variants(*args, np_of(inp["k_new"]), np_of(inp["v_new"]), "bf16", L.numpy(), lay,
+                                           Hq, Hkv, sink=sink.cpu().numpy())
+        out = g.step_ex(inp["q"], inp["k_cache"], inp["v_cache"], inp["k_new"], inp["v_new"], inp["lengths"],
+                        layout=lay, softmax=g.Softmax(sink=sink))
+    else:
+        ref, rk, rv = oracle.step(*args, np_of(inp["k_new"]), np_of(inp["v_new"]), "bf16", L.numpy(), lay, Hq, Hkv)
+        out = g.step(inp["q"], inp["k_cache"], inp["v_cache"], inp["k_new"], inp["v_new"], inp["lengths"], layout=lay)
+    torch.cuda.synchronize()
+    assert_close(out, ref, qo, f"balanced {case}")
     assert np_of(inp["k_cache"]).tobytes() == rk.tobytes() and np_of(inp["v_cache"]).tobytes() == rv.tobytes()
