@@ -1,0 +1,104 @@
+// Balanced work split of the matrix-core attention kernels (ragged batches).
+//
+// The batch's work is a sequence of tiles: sequence b holds Hkv items
+// (b, kv-head h) of c_b tiles each (its attended slots -- in the sliding
+// window's virtual order when one is set -- in tiles of 2^shift slots, at
+// least one tile so an empty sequence still writes its zero rows).  Item
+// (b, h) is tiles [P_b + h c_b, P_b + (h + 1) c_b), P_b = Hkv * sum of c_b'
+// over b' < b.  The T tiles are cut into gridDim.x equal contiguous ranges,
+// one per workgroup.  A workgroup attends every piece of an item inside its
+// range: a whole item writes its output rows; an item cut between ranges
+// leaves partial rows (m, l, o of its G heads) at workspace row
+// 2 * blockIdx + (0 for the range's first piece, 1 for its last), and the
+// balanced combine pass merges them.  The offsets P_b (and T) are written to
+// the workspace by workgroup 0 for that pass.
+#pragma once
+
+#include "device_common.h"
+#include "internal.h"
+#include "variants.h"
+
+namespace gqa {
+
+__device__ __forceinline__ int seq_tiles(const AttnArgs& a, int b, int shift) {
+  int n = a.lengths[b] + a.len_offset;
+  n = n < 0 ? 0 : (n > a.S ? a.S : n);
+  if (a.window > 0) n = seq_view(a, b, n).nv;
+  return max(1, (n + (1 << shift) - 1) >> shift);
+}
+
+// Block-wide exclusive scan of the tile counts into pre[0..B] (LDS, B + 1
+// entries); `wsum` holds one int per wave.  Called by every thread of the
+// workgroup (it holds barriers); at most 16 sequences per thread.
+__device__ __forceinline__ void balanced_scan(const AttnArgs& a, int shift, int32_t* pre, int32_t* wsum) {
+  const int B = a.B;
+  const int nt = blockDim.x;
+  const int per_t = (B + nt - 1) / nt;  // consecutive sequences per thread
+  const int b0 = threadIdx.x * per_t;
+  int cnt[16];
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    cnt[i] = (i < per_t && b0 + i < B) ? a.Hkv * seq_tiles(a, b0 + i, shift) : 0;
+    sum += cnt[i];
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = sum;  // inclusive scan within the wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(inc, off);
+    if (lane >= off) inc += y;
+  }
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += wsum[w];
+  int run = base + inc - sum;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (i < per_t && b0 + i < B) pre[b0 + i] = run;
+    run += cnt[i];
+  }
+  if (threadIdx.x == nt - 1) pre[B] = base + inc;
+  __syncthreads();
+  if (blockIdx.x == 0) {  // the offsets for the combine pass
+    for (int i = threadIdx.x; i <= B; i += nt) a.bal_pre[i] = pre[i];
+  }
+}
+
+// The workgroup's tile range [lo, hi) (empty when lo >= hi).
+__device__ __forceinline__ void balanced_range(const int32_t* pre, int B, int* lo, int* hi) {
+  const int T = pre[B];
+  const int per = (T + (int)gridDim.x - 1) / (int)gridDim.x;
+  *lo = (int)blockIdx.x * per;
+  *hi = min(*lo + per, T);
+}
+
+// The piece of the range [lo, hi) that starts at tile t: item (b, h), its
+// tiles [j0, j1), whether that is the whole item, and its partial row base.
+struct BalancedPiece {
+  int b, h, j0, j1;
+  bool whole;
+  int64_t pbase;
+};
+__device__ __forceinline__ BalancedPiece balanced_piece(const AttnArgs& a, const int32_t* pre, int t, int lo,
+                                                        int hi) {
+  int l0 = 0, l1 = a.B;  // pre[l0] <= t < pre[l1]
+  while (l1 - l0 > 1) {
+    const int mid = (l0 + l1) >> 1;
+    if (pre[mid] <= t) l0 = mid;
+    else l1 = mid;
+  }
+  BalancedPiece p;
+  p.b = l0;
+  const int cb = (pre[l0 + 1] - pre[l0]) / a.Hkv;
+  const int off = t - pre[l0];
+  p.h = off / cb;
+  p.j0 = off - p.h * cb;
+  p.j1 = min(cb, p.j0 + (hi - t));
+  p.whole = p.j0 == 0 && p.j1 == cb;
+  p.pbase = (2 * (int64_t)blockIdx.x + (t == lo ? 0 : 1)) * a.G;
+  return p;
+}
+
+}  // namespace gqa

@@ -131,7 +131,9 @@ gqa_status_t make_plan(const gqa_decode_desc_t* d, Plan* p, int64_t span = 0) {
   // contiguous range of the batch's 16-slot tiles (cut on the device from the
   // lengths), and the items cut between workgroups are merged by the balanced
   // combine pass.  Its partials: two rows of G heads per workgroup.  Not for
-  // huge batches (each workgroup scans the lengths of the whole batch).
+  // huge batches (each workgroup scans the lengths of the whole batch).  (On
+  // the large-group kernel the same mode measured slower than its splits: the
+  // scan and the extra pieces cost more than the balance gains there.)
   int64_t tiles_max;
   if (p->kernel == GQA_KERNEL_MFMA_QK && p->head_chunks == 1 && d->num_splits == 0 && B * Hkv > kNumCUs &&
       B <= kMaxBalancedBatch && mul_ok(B * Hkv, S / 16 + 1, &tiles_max) && tiles_max < INT32_MAX) {

@@ -631,23 +631,41 @@ __global__ __launch_bounds__(256) void combine_balanced_kernel(AttnArgs a) {
     const int k = k0 + i;
     return (2 * (int64_t)k + ((i == 0 && s0 != k * per) ? 1 : 0)) * a.G + g;
   };
-  float M = kNegInf;
-  for (int i0 = 0; i0 < np; i0 += 64) {
+  // One round of loads: m and l of the first 64 pieces (one per lane) and o
+  // of the first eight (half-waves take alternate pieces), then the rest.
+  const int q = lane & 31;
+  const int half = lane >> 5;
+  const float mraw = lane < np ? a.part_m[row(lane)] : kNegInf;
+  const float lraw = lane < np ? a.part_l[row(lane)] : 0.f;
+  f32x4 o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = half + 2 * j;
+    o[j] = i < np ? reinterpret_cast<const f32x4*>(a.part_o + row(i) * 128)[q] : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  float M = wave_max(mraw);
+  for (int i0 = 64; i0 < np; i0 += 64) {
     const int i = i0 + lane;
     M = fmaxf(M, wave_max(i < np ? a.part_m[row(i)] : kNegInf));
   }
-  const int q = lane & 31;
-  const int half = lane >> 5;
-  float L = 0.f;
+  float w = lane < np ? fast_exp2(mraw - M) : 0.f;
+  float L = wave_sum(w * lraw);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc += __shfl(w, half + 2 * j) * o[j];
+  // Pieces past the eighth.  Every loop below is uniform over the wave, so all
+  // lanes take part in each cross-lane read of the weights.
   for (int i0 = 0; i0 < np; i0 += 64) {
-    const int i = i0 + lane;
-    const float w = i < np ? fast_exp2(a.part_m[row(i)] - M) : 0.f;
-    L += wave_sum(i < np ? w * a.part_l[row(i)] : 0.f);
+    if (i0 > 0) {
+      const int i = i0 + lane;
+      w = i < np ? fast_exp2(a.part_m[row(i)] - M) : 0.f;
+      L += wave_sum(i < np ? w * a.part_l[row(i)] : 0.f);
+    }
     const int nr = min(64, np - i0);
-    for (int j = half; j < nr; j += 2) {
-      const float wj = __shfl(w, j);
-      acc += wj * reinterpret_cast<const f32x4*>(a.part_o + row(i0 + j) * 128)[q];
+    for (int j0 = i0 == 0 ? 8 : 0; j0 < nr; j0 += 2) {
+      const int j = j0 + half;
+      const float wj = __shfl(w, min(j, 63));
+      if (j < nr) acc += wj * reinterpret_cast<const f32x4*>(a.part_o + row(i0 + j) * 128)[q];
     }
   }
 #pragma unroll

@@ -45,6 +45,7 @@
 #include <algorithm>
 #include <type_traits>
 
+#include "balanced.h"
 #include "cache_map.h"
 #include "device_common.h"
 #include "internal.h"
@@ -527,15 +528,6 @@ __device__ __forceinline__ void attend_piece(const AttnArgs& a, const Piece& pc,
 }
 
 
-// Tile counts in the balanced mode: a sequence's virtual slots in 16-slot
-// tiles, at least one (an empty sequence still writes its zero rows).
-__device__ __forceinline__ int seq_tiles(const AttnArgs& a, int b) {
-  int n = a.lengths[b] + a.len_offset;
-  n = n < 0 ? 0 : (n > a.S ? a.S : n);
-  if (a.window > 0) n = seq_view(a, b, n).nv;
-  return max(1, (n + 15) >> 4);
-}
-
 template <int KV, int NW, bool PAGED, bool VAR>
 __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
   static_assert(!(PAGED && KV == GQA_I8), "int8 caches are dense");
@@ -567,53 +559,10 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
   int lo = 0, hi = 0;  // balanced mode: this workgroup's tile range
   Piece split_piece;   // split mode: the workgroup's piece
   if (a.bal_pre != nullptr) {
-    // Balanced mode (ragged batches): the batch's work is cut into equal
-    // contiguous ranges of 16-slot tiles, one per workgroup (one workgroup per
-    // CU).  Sequence b holds Hkv items (b, h) of c_b tiles each; item (b, h)
-    // is tiles [P_b + h c_b, P_b + (h + 1) c_b) with P_b = Hkv * sum of c_b'
-    // over b' < b.  A workgroup attends each piece of an item that falls in its
-    // range: a whole item writes its output rows, a cut one leaves partials at
-    // workspace row 2 * blockIdx + (0 for the range's first piece, 1 for its
-    // last), which the balanced combine pass merges.
-    const int B = a.B;
-    const int nt = blockDim.x;
-    const int per_t = (B + nt - 1) / nt;  // consecutive sequences per thread (at most 16)
-    const int b0 = threadIdx.x * per_t;
-    int cnt[16];
-    int sum = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      cnt[i] = (i < per_t && b0 + i < B) ? a.Hkv * seq_tiles(a, b0 + i) : 0;
-      sum += cnt[i];
-    }
-    // Exclusive scan of the per-thread sums: within each wave, then across waves.
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int inc = sum;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(inc, off);
-      if (lane >= off) inc += y;
-    }
+    // Balanced mode (ragged batches), 16-slot tiles: see balanced.h.
     __shared__ int32_t wsum[NW];
-    if (lane == 63) wsum[wave] = inc;
-    __syncthreads();
-    int base = 0;
-    for (int w = 0; w < wave; ++w) base += wsum[w];
-    int run = base + inc - sum;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i < per_t && b0 + i < B) sm_pre[b0 + i] = run;
-      run += cnt[i];
-    }
-    if (threadIdx.x == nt - 1) sm_pre[B] = base + inc;
-    __syncthreads();
-    if (blockIdx.x == 0) {  // the offsets for the combine pass
-      for (int i = threadIdx.x; i <= B; i += nt) a.bal_pre[i] = sm_pre[i];
-    }
-    const int T = sm_pre[B];
-    const int per = (T + (int)gridDim.x - 1) / (int)gridDim.x;
-    lo = (int)blockIdx.x * per;
-    hi = min(lo + per, T);
+    balanced_scan(a, 4, sm_pre, wsum);
+    balanced_range(sm_pre, a.B, &lo, &hi);
     if (lo >= hi) return;
   } else {
     // Split mode: workgroup -> (split, query-head chunk, b, kv-head).  Groups
@@ -653,21 +602,9 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
     Piece pc = split_piece;
     int step = 0;
     if (a.bal_pre != nullptr) {
-      int l0 = 0, l1 = a.B;  // pre[l0] <= t < pre[l1]
-      while (l1 - l0 > 1) {
-        const int mid = (l0 + l1) >> 1;
-        if (sm_pre[mid] <= t) l0 = mid;
-        else l1 = mid;
-      }
-      const int b = l0;
-      const int cb = (sm_pre[b + 1] - sm_pre[b]) / a.Hkv;
-      const int off = t - sm_pre[b];
-      const int h = off / cb;
-      const int j0 = off - h * cb;
-      const int j1 = min(cb, j0 + (hi - t));
-      const int64_t pbase = (2 * (int64_t)blockIdx.x + (t == lo ? 0 : 1)) * a.G;
-      pc = piece_of(b, h, 0, 16 * j0, 16 * j1, j0 == 0 && j1 == cb, pbase, 1);
-      step = j1 - j0;
+      const BalancedPiece bp = balanced_piece(a, sm_pre, t, lo, hi);
+      pc = piece_of(bp.b, bp.h, 0, 16 * bp.j0, 16 * bp.j1, bp.whole, bp.pbase, 1);
+      step = bp.j1 - bp.j0;
     }
     attend_piece<KV, NW, PAGED, VAR>(a, pc, sm_o, sm_m, sm_l);
     t += step;

@@ -243,9 +243,12 @@ def test_plan_is_a_function_of_the_descriptor_only():
 
 
 def test_balanced_mode_only_where_items_outnumber_cus():
-    """The balanced mode replaces one workgroup per (b, kv-head) item only when
-    the items outnumber the CUs, no split count is forced, and the batch fits
-    the kernel's on-device scan (4096 sequences)."""
+    """The balanced mode replaces one workgroup per (b, kv-head) item on the
+    G <= 16 kernel only when the items outnumber the CUs, no split count is
+    forced and the batch fits the kernel's on-device scan (4096 sequences);
+    the large-group kernel keeps its splits."""
+    assert not g.get_plan(desc(batch=128, num_q_heads=64, num_kv_heads=1, capacity=2048))["balanced"]
+    assert not g.get_plan(desc(batch=300, num_q_heads=64, num_kv_heads=1, capacity=2048))["balanced"]
     assert not g.get_plan(desc(batch=32, num_q_heads=32, num_kv_heads=8, capacity=4097))["balanced"]   # 256 items
     assert g.get_plan(desc(batch=33, num_q_heads=32, num_kv_heads=8, capacity=4097))["balanced"]
     assert g.get_plan(desc(batch=64, num_q_heads=64, num_kv_heads=8, capacity=8192, layout="BSHD"))["balanced"]

@@ -463,20 +463,33 @@ def test_balanced_mode_matches_oracle(g, kind):
     assert np_of(inp["k_cache"]).tobytes() == rk.tobytes() and np_of(inp["v_cache"]).tobytes() == rv.tobytes()
 
 
-@pytest.mark.parametrize("case", ["one_long", "attend_empty", "sink_bshd"])
+@pytest.mark.parametrize("case", ["one_long", "attend_empty", "sink_bshd", "one_long_bshd", "attend_empty_g4",
+                                  "window"])
 def test_balanced_mode_edge_cases(g, case):
     """Balanced-mode cases: one long sequence among many short ones (its items
     are cut across more than 64 workgroups, so the combine merges its partials
-    in several rounds), attend with empty sequences (zero rows, never cut),
-    and a per-head sink on a (B, S, Hkv, D) cache."""
+    in several rounds, an odd number of them in the last), attend with empty
+    sequences (zero rows, never cut), a per-head sink on a (B, S, Hkv, D)
+    cache, and a sliding window with a kept prefix."""
     if case == "one_long":
         B, Hq, Hkv, S, lay = 300, 16, 1, 20000, "BHSD"
         L = torch.randint(0, 40, (B,), generator=torch.Generator().manual_seed(93), dtype=torch.int32)
         L[123] = S - 1
+    elif case == "one_long_bshd":
+        B, Hq, Hkv, S, lay = 150, 8, 2, 9000, "BSHD"
+        L = torch.randint(0, 40, (B,), generator=torch.Generator().manual_seed(98), dtype=torch.int32)
+        L[7] = S - 1
     elif case == "attend_empty":
         B, Hq, Hkv, S, lay = 70, 32, 4, 700, "BHSD"
         L = torch.randint(0, S + 1, (B,), generator=torch.Generator().manual_seed(94), dtype=torch.int32)
         L[0], L[9], L[69] = 0, 0, S
+    elif case == "attend_empty_g4":
+        B, Hq, Hkv, S, lay = 300, 4, 1, 700, "BSHD"
+        L = torch.randint(0, S + 1, (B,), generator=torch.Generator().manual_seed(99), dtype=torch.int32)
+        L[0], L[9], L[29] = 0, 0, S
+    elif case == "window":
+        B, Hq, Hkv, S, lay = 20, 64, 16, 1500, "BHSD"
+        L = torch.randint(0, S, (B,), generator=torch.Generator().manual_seed(100), dtype=torch.int32)
     else:
         B, Hq, Hkv, S, lay = 36, 64, 8, 520, "BSHD"
         L = torch.randint(0, S, (B,), generator=torch.Generator().manual_seed(95), dtype=torch.int32)
@@ -487,7 +500,7 @@ def test_balanced_mode_edge_cases(g, case):
     assert g.get_plan(desc)["balanced"]
     say(f"balanced {case}: B={B} Hq={Hq} Hkv={Hkv} S={S} {lay}")
     args = (np_of(inp["q"]), qo, np_of(inp["k_cache"]), np_of(inp["v_cache"]))
-    if case == "attend_empty":
+    if case.startswith("attend_empty"):
         ref = oracle.attend(*args, "bf16", L.numpy(), lay, Hq, Hkv)
         out = g.attend(inp["q"], inp["k_cache"], inp["v_cache"], inp["lengths"], layout=lay)
         torch.cuda.synchronize()
@@ -502,6 +515,11 @@ def test_balanced_mode_edge_cases(g, case):
                                            Hq, Hkv, sink=sink.cpu().numpy())
         out = g.step_ex(inp["q"], inp["k_cache"], inp["v_cache"], inp["k_new"], inp["v_new"], inp["lengths"],
                         layout=lay, softmax=g.Softmax(sink=sink))
+    elif case == "window":
+        ref, rk, rv = oracle.step_variants(*args, np_of(inp["k_new"]), np_of(inp["v_new"]), "bf16", L.numpy(), lay,
+                                           Hq, Hkv, window=300, prefix=20)
+        out = g.step_ex(inp["q"], inp["k_cache"], inp["v_cache"], inp["k_new"], inp["v_new"], inp["lengths"],
+                        layout=lay, softmax=g.Softmax(window=300, kept_prefix=20))
     else:
         ref, rk, rv = oracle.step(*args, np_of(inp["k_new"]), np_of(inp["v_new"]), "bf16", L.numpy(), lay, Hq, Hkv)
         out = g.step(inp["q"], inp["k_cache"], inp["v_cache"], inp["k_new"], inp["v_new"], inp["lengths"], layout=lay)
