@@ -29,11 +29,11 @@ HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20
 METRIC = "achieved HBM GB/s (% of MI355X peak) + decode steps/sec per config"
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["gqa_decode_attention_amd/csrc/kernels_mfma.hip", "gqa_decode_attention_amd/csrc/kernels_generic.hip",
-                  "gqa_decode_attention_amd/csrc/kernels_mfma_qkv.hip",
-                  "gqa_decode_attention_amd/csrc/device_common.h", "gqa_decode_attention_amd/csrc/gqa_decode.cpp",
-                  "gqa_decode_attention_amd/csrc/internal.h", "gqa_decode_attention_amd/csrc/cache_map.h",
-                  "gqa_decode_attention_amd/csrc/variants.h", "gqa_decode_attention_amd/build.py"]
+# Every source the library is built from: the recorded traffic counts only
+# while none of them has changed since the counters were taken.
+KERNEL_SOURCES = sorted(
+    [os.path.join("gqa_decode_attention_amd/csrc", f) for f in os.listdir(os.path.join(ROOT, "gqa_decode_attention_amd/csrc"))
+     if f.endswith((".hip", ".cpp", ".h"))]) + ["include/gqa_decode.h", "gqa_decode_attention_amd/build.py"]
 
 
 def kernel_source_hash() -> str:
