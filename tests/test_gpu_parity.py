@@ -328,25 +328,38 @@ def test_check_lengths_counts_out_of_contract_entries(g):
         assert g.check_lengths(Lw, w.capacity, mode="step") == 0
 
 
-def test_graph_capture_replays(g):
-    """The step has no host sync and no memset: it can be captured and replayed."""
-    w = W.custom(4, 32, 8, 128, 2048, "BHSD", "bf16", "bf16", seed=77)
-    L = torch.tensor([2047, 100, 1500, 7], dtype=torch.int32)
+@pytest.mark.parametrize("B", [4, 40])
+def test_graph_capture_replays(g, B):
+    """The step has no host sync and no memset: it can be captured and
+    replayed.  B = 4 splits the token axis (attention + combine); B = 40 has
+    more (b, kv-head) items than CUs, so the balanced mode cuts the batch on
+    the device from the lengths at run time.  Each replay runs on new lengths
+    (written into the captured buffer) and matches an eager call on them."""
+    w = W.custom(B, 32, 8, 128, 2048, "BHSD", "bf16", "bf16", seed=77)
+    gen = torch.Generator().manual_seed(78)
+    L = torch.randint(0, 2048, (B,), generator=gen, dtype=torch.int32)
+    L[0] = 2047
     inp = W.make_inputs(w, DEV, lengths=L)
     desc = g.desc_for(inp["q"], inp["k_cache"], "BHSD")
+    assert g.get_plan(desc)["balanced"] == (B == 40)
     ws = torch.empty(max(g.workspace_size(desc), 1), dtype=torch.uint8, device=DEV)
     out = torch.empty_like(inp["q"])
-    eager = run_step(g, {k: v.clone() for k, v in inp.items()}, w)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        run_step(g, inp, w)                                 # warm-up outside capture
+        run_step(g, {k: v.clone() for k, v in inp.items()}, w)   # warm-up outside capture
     torch.cuda.current_stream().wait_stream(s)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         g.step(inp["q"], inp["k_cache"], inp["v_cache"], inp["k_new"], inp["v_new"], inp["lengths"],
                out=out, workspace=ws)
+    caches = (inp["k_cache"].clone(), inp["v_cache"].clone())
     for r in range(4):
+        Lr = torch.randint(0, 2048, (B,), generator=gen, dtype=torch.int32)
+        inp["lengths"].copy_(Lr.to(DEV))
+        inp["k_cache"].copy_(caches[0])
+        inp["v_cache"].copy_(caches[1])
+        eager = run_step(g, {k: v.clone() for k, v in inp.items()}, w)
         out.zero_()
         inp["q"].mul_(1.0)                                  # eager work between replays
         graph.replay()
