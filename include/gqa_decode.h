@@ -101,7 +101,7 @@ typedef struct {
   int32_t split_tokens;  /* slots per split (the last split may be shorter)                 */
   int32_t grid;          /* workgroups of the attention pass                                */
   int32_t block;         /* threads per workgroup of the attention pass                     */
-  int32_t combine;       /* 1 if a split-combine pass follows the attention pass            */
+  int32_t combine;       /* 1 if a combine pass follows the attention pass                  */
   size_t workspace_bytes;
   int32_t balanced;      /* 1 if each workgroup of the attention pass takes an equal share of
                             the batch's 16-slot tiles, cut on the device from `lengths`
@@ -118,7 +118,7 @@ enum {
 
 /* Phase one (CANN operator page, two-phase call convention): validate the
  * descriptor and report the workspace the attend/step calls need, in bytes
- * (0 when the token axis is not split).  Returns GQA_ERR_INVALID_ARGUMENT or
+ * (0 when the token axis is not split and the plan is not balanced).  Returns GQA_ERR_INVALID_ARGUMENT or
  * GQA_ERR_UNSUPPORTED for a bad descriptor; *bytes is then untouched. */
 gqa_status_t gqa_decode_workspace_size(const gqa_decode_desc_t* desc, size_t* bytes);
 
@@ -150,7 +150,9 @@ gqa_status_t gqa_decode_append(const gqa_decode_desc_t* desc, void* k_cache, voi
  *   out      : (B, Hq, D), qo_dtype, written; out[b,h] = sum_{j<lengths[b]} w_j V_j of
  *              cache head h / (Hq/Hkv); must not overlap any other argument.
  *   workspace: device scratch of at least gqa_decode_workspace_size() bytes, 256-byte
- *              aligned (may be NULL when that size is 0).  It holds the split partials;
+ *              aligned (may be NULL when that size is 0).  It holds the split partials
+ *              (balanced plans: the partials of cut items and the batch's tile
+ *              offsets, written by the attention pass for the combine pass);
  *              its contents on entry do not matter, it needs no clearing and it may be
  *              reused by later calls with any descriptor.  Calls that run concurrently
  *              must not share one workspace.
