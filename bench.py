@@ -228,7 +228,10 @@ def main():
         import ctypes
         rs = rope.struct() if rope is not None else None
         ss = smx.struct() if smx is not None else None
-        wsb = g.workspace_size_ex(desc, g.OptsT(None, None, ctypes.pointer(rs) if rs is not None else None,
+        from gqa_decode_attention_amd import _lib
+        sc = _lib._scales(inp["k_cache"], inp["k_scale"], inp["v_scale"], w.layout) if q8 else None
+        wsb = g.workspace_size_ex(desc, g.OptsT(None, ctypes.pointer(sc) if sc is not None else None,
+                                                ctypes.pointer(rs) if rs is not None else None,
                                                 ctypes.pointer(ss) if ss is not None else None))
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
     out = torch.empty_like(inp["q"])

@@ -65,9 +65,12 @@ int32_t choose_kernel(const gqa_decode_desc_t* d) {
   const int32_t G = d->num_q_heads / d->num_kv_heads;
   const bool bf16 = d->kv_dtype == GQA_BF16 && d->qo_dtype == GQA_BF16;
   if (d->kv_dtype == GQA_I8) {
-    // Groups of up to 64 query heads: 16-head chunks of the G <= 16 kernel.
-    return (d->qo_dtype == GQA_BF16 && d->head_dim == 128 && G <= 64 && kHaveMfmaQkI8) ? GQA_KERNEL_MFMA_QK
-                                                                                       : GQA_KERNEL_GENERIC;
+    // G <= 16 on the G <= 16 kernel (which quantizes a step's new rows itself),
+    // 16 < G <= 64 on the large-group kernel (codes widened into its LDS tiles).
+    if (d->qo_dtype != GQA_BF16 || d->head_dim != 128) return GQA_KERNEL_GENERIC;
+    if (G <= 16 && kHaveMfmaQkI8) return GQA_KERNEL_MFMA_QK;
+    if (G <= 64 && kHaveMfmaAll) return GQA_KERNEL_MFMA_ALL;
+    return GQA_KERNEL_GENERIC;
   }
   if (bf16 && d->head_dim == 128 && G <= 16 && kHaveMfmaQk) return GQA_KERNEL_MFMA_QK;
   if (bf16 && d->head_dim == 128 && G > 16 && G <= 64 && kHaveMfmaAll) return GQA_KERNEL_MFMA_ALL;
@@ -506,9 +509,13 @@ const gqa_decode_opts_t kNoOpts = {nullptr, nullptr, nullptr, nullptr};
 
 // Bytes of the rotated q a rotary step keeps after the plan's workspace.
 size_t rope_q_offset(const Plan& p) { return align256(p.workspace_bytes); }
+// MFMA_ALL rotates q and the new key itself on bf16 caches; the other paths
+// (and int8 caches) read a rotated copy written by the rotary append.
+bool rope_fused(const Plan& p, const gqa_decode_opts_t* o) {
+  return p.kernel == GQA_KERNEL_MFMA_ALL && o->scales == nullptr;
+}
 size_t workspace_total(const gqa_decode_desc_t* d, const Plan& p, const gqa_decode_opts_t* o) {
-  // MFMA_ALL rotates q itself; the other kernels read a rotated copy.
-  if (o->rope == nullptr || p.kernel == GQA_KERNEL_MFMA_ALL) return p.workspace_bytes;
+  if (o->rope == nullptr || rope_fused(p, o)) return p.workspace_bytes;
   return rope_q_offset(p) + (size_t)d->batch * d->num_q_heads * d->head_dim * elem_bytes(d->qo_dtype);
 }
 
@@ -644,7 +651,7 @@ gqa_status_t do_attend(const gqa_decode_desc_t* desc, const gqa_decode_opts_t* o
   if (step) {
     a.k_new = k_new;
     a.v_new = v_new;
-    if (rope != nullptr && p.kernel == GQA_KERNEL_MFMA_ALL) {
+    if (rope != nullptr && rope_fused(p, o)) {
       // Rotary step on MFMA_ALL: every workgroup rotates its q (all G heads of
       // its kv-head), the workgroup whose split holds slot lengths[b] rotates
       // the new key, attends it and stores it.  (On the G <= 16 kernel the
@@ -673,10 +680,10 @@ gqa_status_t do_attend(const gqa_decode_desc_t* desc, const gqa_decode_opts_t* o
       a.k_new = nullptr;
       a.v_new = nullptr;
       a.rope_cos = nullptr;  // the attention pass reads the rotated q and key as they are
-    } else if (sc != nullptr && p.kernel == GQA_KERNEL_GENERIC) {
-      // Int8 caches, generic path: the quantizing append, then attention over
-      // lengths[b] + 1 slots (the new token is attended in its stored,
-      // quantized form).
+    } else if (sc != nullptr && p.kernel != GQA_KERNEL_MFMA_QK) {
+      // Int8 caches, generic and large-group paths: the quantizing append,
+      // then attention over lengths[b] + 1 slots (the new token is attended in
+      // its stored, quantized form).
       a.k_scale_w = sc->k_scale;
       a.v_scale_w = sc->v_scale;
       if (launch_append_q8(a, k_cache, v_cache, (hipStream_t)stream) != hipSuccess) return GQA_ERR_HIP;

@@ -89,10 +89,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 
-template <bool PAGED, bool VAR>
+// Int8 caches (KV = GQA_I8, dense, attend only: a step quantizes its new
+// rows with the append kernel first).  Rows are 128 codes with a float32
+// scale each (Huawei CANN "aclnnMlaPrologV3WeightNz" page, dynamic
+// quantization: a cached value reads as code * row scale).  Thread t loads 16
+// codes (bytes 16 (t & 7) ..) of row t >> 3 of the K and V tiles with the
+// rows' scales; the codes are widened exactly to bf16 (|code| <= 127) as they
+// are written to LDS, so the tile math is that of bf16 caches, with each
+// slot's score times its key scale and its weight times its value scale in
+// the V sum (the denominator sums the unscaled weights).
+template <int KV, bool PAGED, bool VAR>
 __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
+  static_assert(!(PAGED && KV == GQA_I8), "int8 caches are dense");
+  constexpr bool Q8 = KV == GQA_I8;
   __shared__ __attribute__((aligned(16))) uint16_t sk[2][kTileT * kPitch];
   __shared__ __attribute__((aligned(16))) uint16_t sv[2][kTileT * kPitch];
+  __shared__ float sks[2][kTileT], svs[2][kTileT];  // int8: the tile rows' scales
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -155,6 +167,8 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
   const int64_t base = PAGED ? 0 : row_head_offset(a, b, h);  // dense or slot-indexed row
   const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.k_cache) + base;
   const uint16_t* vb = reinterpret_cast<const uint16_t*>(a.v_cache) + base;
+  const int8_t* kb8 = reinterpret_cast<const int8_t*>(a.k_cache) + base;  // int8 caches
+  const int8_t* vb8 = reinterpret_cast<const int8_t*>(a.v_cache) + base;
   const int64_t rs = a.st;
   const int64_t nrow = ((int64_t)b * a.Hkv + h) * kD;
   // Tile grid origin: the split start, or for a paged cache (block size a
@@ -177,6 +191,7 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
   const int piece = tid & 15;
   struct Regs {
     u32x4 k[2], v[2];
+    float ks, vs;  // int8: the scales of row t >> 3 (codes in k[0], v[0])
   };
   u32x4 kn = {0u, 0u, 0u, 0u}, vn = {0u, 0u, 0u, 0u};
   if (own_new) {
@@ -229,6 +244,29 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
     return en;
   };
   auto gload = [&](int t0, Regs& R, const Ent& en) {
+    if constexpr (Q8) {
+      const int rc = max(min(t0 + (tid >> 3), t_end - 1), t_begin);
+      const int64_t off = (int64_t)phys(rc) * rs;
+      R.k[0] = load_nt16(kb8 + off + 16 * (tid & 7));
+      R.v[0] = load_nt16(vb8 + off + 16 * (tid & 7));
+      const int64_t si = (base + off) / kD;  // dense rows: element offsets are multiples of D
+      R.ks = __uint_as_float(load_nt4(a.k_scale + si));
+      R.vs = __uint_as_float(load_nt4(a.v_scale + si));
+      return;
+    }
+    if constexpr (!PAGED) {
+      // Dense or slot-indexed rows (tiles start at t_begin, so only the end
+      // clamps): one 32x32->64-bit multiply-add per row address (slot strides
+      // fit 32 bits: the descriptor check refuses larger ones).
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        const int rc = min(t0 + prow + 16 * q2, t_end - 1);
+        const uint64_t off = (uint64_t)(uint32_t)phys(rc) * (uint32_t)rs + (uint32_t)(8 * piece);
+        R.k[q2] = load_nt16(kb + off);
+        R.v[q2] = load_nt16(vb + off);
+      }
+      return;
+    }
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2) {
       const int rc = max(min(t0 + prow + 16 * q2, t_end - 1), t_begin);
@@ -244,13 +282,42 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
     }
   };
   auto swrite = [&](int t0, int buf, const Regs& R) {
-    const bool holds_new = own_new && t0 + kTileT > L;  // uniform
+    if constexpr (Q8) {
+      const int row = tid >> 3;
+      const int col = 16 * (tid & 7);
+      float x[16];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {  // K then V
+        widen16<GQA_I8>(hh ? R.v[0] : R.k[0], x);
+        const u32x4 lo = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                          pack_bf16x2(x[6], x[7])};
+        const u32x4 hi = {pack_bf16x2(x[8], x[9]), pack_bf16x2(x[10], x[11]), pack_bf16x2(x[12], x[13]),
+                          pack_bf16x2(x[14], x[15])};
+        uint16_t* dst = (hh ? sv[buf] : sk[buf]) + row * kPitch + col;
+        *reinterpret_cast<u32x4*>(dst) = lo;
+        *reinterpret_cast<u32x4*>(dst + 8) = hi;
+      }
+      if ((tid & 7) == 0) {
+        sks[buf][row] = R.ks;
+        svs[buf][row] = R.vs;
+      }
+      return;
+    }
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2) {
       const int row = prow + 16 * q2;
-      const bool nw = holds_new && t0 + row >= L;
-      *reinterpret_cast<u32x4*>(&sk[buf][row * kPitch + 8 * piece]) = nw ? kn : R.k[q2];
-      *reinterpret_cast<u32x4*>(&sv[buf][row * kPitch + 8 * piece]) = nw ? vn : R.v[q2];
+      *reinterpret_cast<u32x4*>(&sk[buf][row * kPitch + 8 * piece]) = R.k[q2];
+      *reinterpret_cast<u32x4*>(&sv[buf][row * kPitch + 8 * piece]) = R.v[q2];
+    }
+    if (own_new && t0 + kTileT > L) {  // uniform: the tile holding the new token; rows >= L take it
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        const int row = prow + 16 * q2;
+        if (t0 + row >= L) {
+          *reinterpret_cast<u32x4*>(&sk[buf][row * kPitch + 8 * piece]) = kn;
+          *reinterpret_cast<u32x4*>(&sv[buf][row * kPitch + 8 * piece]) = vn;
+        }
+      }
     }
   };
 
@@ -270,6 +337,13 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
     // Raw scores; the scale log2(e)/sqrt(D) is positive, so the maximum is
     // taken on raw scores and the scale is folded into the exponent's fma.
     float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+    if constexpr (Q8) {  // code-space scores times the slots' key scales
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sc[i] *= sks[buf][4 * r + i];
+        sc[4 + i] *= sks[buf][16 + 4 * r + i];
+      }
+    }
     if constexpr (VAR) {
       if (a.cap_T > 0.f) {
 #pragma unroll
@@ -317,6 +391,13 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
       ps += p[i];
     }
     l += ps;
+    if constexpr (Q8) {  // the V sum takes the weights times the slots' value scales
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] *= svs[buf][4 * r + i];
+        p[4 + i] *= svs[buf][16 + 4 * r + i];
+      }
+    }
     const u32x4 pa = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                       pack_bf16x2(p[6], p[7])};
     const int trow = 4 * r + (c >> 2);
@@ -407,10 +488,20 @@ hipError_t launch_attend_mfma_all(const AttnArgs& a, const Plan& p, hipStream_t 
   void* params[] = {&arg};
   const bool var = a.window > 0 || a.cap_T > 0.f;  // in-loop variants (the sink is applied at the end)
   const bool paged = a.map_kind == GQA_MAP_PAGED;
-  const void* fn = paged ? (var ? reinterpret_cast<const void*>(&attend_mfma_all_kernel<true, true>)
-                                : reinterpret_cast<const void*>(&attend_mfma_all_kernel<true, false>))
-                         : (var ? reinterpret_cast<const void*>(&attend_mfma_all_kernel<false, true>)
-                                : reinterpret_cast<const void*>(&attend_mfma_all_kernel<false, false>));
+  const void* fn;
+  if (a.kv_dtype == GQA_I8) {
+    // Int8 caches: dense, attend only (a step appends its quantized rows first).
+    if (a.map_kind != 0 || a.k_new != nullptr || a.rope_cos != nullptr || a.k_scale == nullptr ||
+        a.v_scale == nullptr || a.qo_dtype != GQA_BF16)
+      return hipErrorInvalidValue;
+    fn = var ? reinterpret_cast<const void*>(&attend_mfma_all_kernel<GQA_I8, false, true>)
+             : reinterpret_cast<const void*>(&attend_mfma_all_kernel<GQA_I8, false, false>);
+  } else {
+    fn = paged ? (var ? reinterpret_cast<const void*>(&attend_mfma_all_kernel<GQA_BF16, true, true>)
+                      : reinterpret_cast<const void*>(&attend_mfma_all_kernel<GQA_BF16, true, false>))
+               : (var ? reinterpret_cast<const void*>(&attend_mfma_all_kernel<GQA_BF16, false, true>)
+                      : reinterpret_cast<const void*>(&attend_mfma_all_kernel<GQA_BF16, false, false>));
+  }
   return hipLaunchKernel(fn, dim3(p.grid), dim3(256), params, 0, s);
 }
 
