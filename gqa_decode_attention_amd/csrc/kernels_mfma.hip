@@ -357,7 +357,9 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
         }
       }
     }
-    if (t0 + kTileT > t_end || t0 < t_begin) {  // the split's first (paged) or last, partial tile
+    // The split's first (paged) or last, partial tile: a real (uniform) branch,
+    // so whole tiles run no per-row compares.
+    if (__builtin_expect(__builtin_amdgcn_readfirstlane(t0 + kTileT > t_end || t0 < t_begin), 0)) {
       const int valid = t_end - t0;
       const int lo = t_begin - t0;
 #pragma unroll
