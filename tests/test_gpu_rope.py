@@ -161,8 +161,10 @@ def test_rope_append_alone(g, mode):
 
 @pytest.mark.parametrize("case", [(3, 32, 8, 128, 600, "BHSD", "bf16", "half"),
                                   (2, 16, 2, 128, 300, "BSHD", "bf16", "interleaved"),
-                                  (2, 8, 2, 64, 100, "BHSD", "f32", "half")],
-                         ids=["G4-bf16-half", "G8-BSHD-interleaved", "generic-f32"])
+                                  (2, 8, 2, 64, 100, "BHSD", "f32", "half"),
+                                  (2, 64, 1, 128, 400, "BHSD", "bf16", "half"),
+                                  (3, 48, 2, 128, 300, "BSHD", "bf16", "interleaved")],
+                         ids=["G4-bf16-half", "G8-BSHD-interleaved", "generic-f32", "G64-half", "G24-BSHD-interleaved"])
 def test_rope_step_int8(g, case):
     B, Hq, Hkv, D, S, layout, qo, mode = case
     say(f"rope int8 {case}")

@@ -151,10 +151,12 @@ def test_variants_on_mapped_caches(g, case, ns):
 
 @pytest.mark.parametrize("vname", ["winpre", "all", "cap", "sink"])
 @pytest.mark.parametrize("ns", [0, 3])
-def test_variants_on_int8_caches(g, vname, ns):
-    B, Hq, Hkv, D, S, layout = 3, 32, 8, 128, 800, "BHSD"
+@pytest.mark.parametrize("shape", [(3, 32, 8), (2, 64, 1)], ids=["G4", "G64"])
+def test_variants_on_int8_caches(g, vname, ns, shape):
+    B, Hq, Hkv = shape
+    D, S, layout = 128, 800, "BHSD"
     v = dict(VARIANTS)[vname]
-    say(f"variants int8 {vname} splits={ns}")
+    say(f"variants int8 {vname} splits={ns} shape={shape}")
     w = W.custom(B, Hq, Hkv, D, S, layout, "i8", "bf16", seed=77, stale="pm:1")
     L = _lengths(B, S, 5)
     inp = W.make_q8(w, DEV, lengths=L)
