@@ -377,55 +377,37 @@ __device__ __forceinline__ void attend_piece(const AttnArgs& a, const Piece& pc,
     // Int8 caches: the new rows (bf16 activations) are quantized here by the
     // per-row rule (float32 row maximum, scale = max / 127 and codes =
     // round-half-even(x / scale) with correctly rounded divisions, clamped to
-    // +-127; a zero row has scale 0 and codes 0) straight into the tile's
-    // layout: lanes (r, 0) hold key codes 64j + 16r .. +15, lanes (0, c) value
-    // codes 8c .. 8c + 7.
+    // +-127; a zero row has scale 0 and codes 0).  Lane l quantizes elements
+    // 2l and 2l + 1 of each row; the codes are regrouped into the tile's layout
+    // (lanes (r, 0) hold key codes 64j + 16r .. +15, lanes (0, c) value codes
+    // 8c .. 8c + 7) through this wave's merge buffer, which is idle until the
+    // merge at the end of the piece.
     if (new_here) {
       const int64_t nrow = ((int64_t)b * a.Hkv + h) * kDq;
-      const uint16_t* knp = reinterpret_cast<const uint16_t*>(a.k_new) + nrow;
-      const uint16_t* vnp = reinterpret_cast<const uint16_t*>(a.v_new) + nrow;
-      float kx[32], vx[8];
-      float kmax = 0.f, vmax = 0.f;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {  // 8 elements each: positions 64(q4 >> 1) + 16r + 8(q4 & 1)
-        const u32x4 w = (c == 0) ? *reinterpret_cast<const u32x4*>(knp + 64 * (q4 >> 1) + 16 * r + 8 * (q4 & 1))
-                                 : u32x4{0, 0, 0, 0};
-        widen16<GQA_BF16>(w, &kx[8 * q4]);
-      }
-      {
-        const u32x4 w = (r == 0) ? *reinterpret_cast<const u32x4*>(vnp + 8 * c) : u32x4{0, 0, 0, 0};
-        widen16<GQA_BF16>(w, vx);
-      }
-#pragma unroll
-      for (int e = 0; e < 32; ++e) kmax = fmaxf(kmax, fabsf(kx[e]));
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vmax = fmaxf(vmax, fabsf(vx[e]));
-      kmax = rows_max(kmax);                                  // column 0 holds the key row's maximum
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off));  // row 0: value's
-      kmax = __shfl(kmax, 0);
-      vmax = __shfl(vmax, 0);
+      const uint32_t kp = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(a.k_new) + nrow)[lane];
+      const uint32_t vp = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(a.v_new) + nrow)[lane];
+      const float k0 = bf16_lo(kp), k1 = bf16_hi(kp), v0 = bf16_lo(vp), v1 = bf16_hi(vp);
+      const float kmax = wave_max(fmaxf(fabsf(k0), fabsf(k1)));
+      const float vmax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
       const float ksc = kmax / 127.0f, vsc = vmax / 127.0f;
       auto code = [](float x, float amax, float sc) -> uint32_t {
         const float q = amax > 0.f ? fminf(fmaxf(rintf(x / sc), -127.f), 127.f) : 0.f;
         return (uint32_t)(int32_t)q & 0xffu;
       };
+      uint16_t* xb = reinterpret_cast<uint16_t*>(&sm_o[wave][0][0]);  // key codes at bytes 0..127, values 128..255
+      xb[lane] = (uint16_t)(code(k0, kmax, ksc) | (code(k1, kmax, ksc) << 8));
+      xb[64 + lane] = (uint16_t)(code(v0, vmax, vsc) | (code(v1, vmax, vsc) << 8));
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const uint8_t* xr = reinterpret_cast<const uint8_t*>(xb);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int wd = 0; wd < 4; ++wd) {
-          uint32_t w = 0;
-#pragma unroll
-          for (int by = 0; by < 4; ++by) w |= code(kx[16 * j + 4 * wd + by], kmax, ksc) << (8 * by);
-          tn.k[j][wd] = c == 0 ? w : 0u;
-        }
-#pragma unroll
-      for (int wd = 0; wd < 2; ++wd) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int by = 0; by < 4; ++by) w |= code(vx[4 * wd + by], vmax, vsc) << (8 * by);
-        tn.v[0][wd] = r == 0 ? w : 0u;
+      for (int j = 0; j < 2; ++j) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(xr + 64 * j + 16 * r);
+        tn.k[j] = c == 0 ? w : u32x4{0, 0, 0, 0};
       }
+      const u32x2_t wv = *reinterpret_cast<const u32x2_t*>(xr + 128 + 8 * c);
+      tn.v[0] = r == 0 ? wv : u32x2_t{0u, 0u};
 #pragma unroll
       for (int i = 1; i < 4; ++i) tn.v[i] = u32x2_t{0u, 0u};
       tn.ks = ksc;
