@@ -1,17 +1,20 @@
 // Balanced work split of the matrix-core attention kernels (ragged batches).
 //
-// The batch's work is a sequence of tiles: sequence b holds Hkv items
-// (b, kv-head h) of c_b tiles each (its attended slots -- in the sliding
-// window's virtual order when one is set -- in tiles of 2^shift slots, at
-// least one tile so an empty sequence still writes its zero rows).  Item
-// (b, h) is tiles [P_b + h c_b, P_b + (h + 1) c_b), P_b = Hkv * sum of c_b'
-// over b' < b.  The T tiles are cut into gridDim.x equal contiguous ranges,
-// one per workgroup.  A workgroup attends every piece of an item inside its
-// range: a whole item writes its output rows; an item cut between ranges
-// leaves partial rows (m, l, o of its G heads) at workspace row
-// 2 * blockIdx + (0 for the range's first piece, 1 for its last), and the
-// balanced combine pass merges them.  The offsets P_b (and T) are written to
-// the workspace by workgroup 0 for that pass.
+// The batch's work is a sequence of units: sequence b holds Hkv items
+// (b, kv-head h) of u_b = C + c_b units each -- C units standing for the
+// fixed cost of a piece (its start-up and merge), then its c_b tiles (its
+// attended slots -- in the sliding window's virtual order when one is set --
+// in tiles of 2^shift slots, at least one tile so an empty sequence still
+// writes its zero rows).  Item (b, h) is units [P_b + h u_b, P_b + (h + 1)
+// u_b), P_b = Hkv * sum of u_b' over b' < b; its tile j is unit P_b + h u_b +
+// C + j.  The units are cut into gridDim.x equal contiguous ranges, one per
+// workgroup, so a workgroup holding many short items gets fewer tiles.  A
+// workgroup attends every item's tiles inside its range: a whole item writes
+// its output rows; an item cut between ranges leaves partial rows (m, l, o of
+// its G heads) at workspace row 2 * blockIdx + 1 if the piece holds the item's
+// first tile (the range's last piece), else 2 * blockIdx (the range's first
+// piece), and the balanced combine pass merges them.  The offsets P_b (and
+// the total) are written to the workspace by workgroup 0 for that pass.
 #pragma once
 
 #include "device_common.h"
@@ -27,7 +30,7 @@ __device__ __forceinline__ int seq_tiles(const AttnArgs& a, int b, int shift) {
   return max(1, (n + (1 << shift) - 1) >> shift);
 }
 
-// Block-wide exclusive scan of the tile counts into pre[0..B] (LDS, B + 1
+// Block-wide exclusive scan of the unit counts into pre[0..B] (LDS, B + 1
 // entries); `wsum` holds one int per wave.  Called by every thread of the
 // workgroup (it holds barriers); at most 16 sequences per thread.
 __device__ __forceinline__ void balanced_scan(const AttnArgs& a, int shift, int32_t* pre, int32_t* wsum) {
@@ -39,7 +42,7 @@ __device__ __forceinline__ void balanced_scan(const AttnArgs& a, int shift, int3
   int sum = 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    cnt[i] = (i < per_t && b0 + i < B) ? a.Hkv * seq_tiles(a, b0 + i, shift) : 0;
+    cnt[i] = (i < per_t && b0 + i < B) ? a.Hkv * (a.bal_cost + seq_tiles(a, b0 + i, shift)) : 0;
     sum += cnt[i];
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -74,15 +77,17 @@ __device__ __forceinline__ void balanced_range(const int32_t* pre, int B, int* l
   *hi = min(*lo + per, T);
 }
 
-// The piece of the range [lo, hi) that starts at tile t: item (b, h), its
-// tiles [j0, j1), whether that is the whole item, and its partial row base.
+// The piece of the range [lo, hi) at unit t (the range's start or an item's
+// first unit): item (b, h), its tiles [j0, j1) inside the range (none when
+// j0 >= j1: the range holds only cost units of the item), whether that is the
+// whole item, its partial row base, and the unit where the next piece starts.
 struct BalancedPiece {
   int b, h, j0, j1;
   bool whole;
   int64_t pbase;
+  int next;
 };
-__device__ __forceinline__ BalancedPiece balanced_piece(const AttnArgs& a, const int32_t* pre, int t, int lo,
-                                                        int hi) {
+__device__ __forceinline__ BalancedPiece balanced_piece(const AttnArgs& a, const int32_t* pre, int t, int hi) {
   int l0 = 0, l1 = a.B;  // pre[l0] <= t < pre[l1]
   while (l1 - l0 > 1) {
     const int mid = (l0 + l1) >> 1;
@@ -91,13 +96,16 @@ __device__ __forceinline__ BalancedPiece balanced_piece(const AttnArgs& a, const
   }
   BalancedPiece p;
   p.b = l0;
-  const int cb = (pre[l0 + 1] - pre[l0]) / a.Hkv;
-  const int off = t - pre[l0];
-  p.h = off / cb;
-  p.j0 = off - p.h * cb;
-  p.j1 = min(cb, p.j0 + (hi - t));
-  p.whole = p.j0 == 0 && p.j1 == cb;
-  p.pbase = (2 * (int64_t)blockIdx.x + (t == lo ? 0 : 1)) * a.G;
+  const int ub = (pre[l0 + 1] - pre[l0]) / a.Hkv;  // units per item
+  const int cb = ub - a.bal_cost;                  // tiles per item
+  p.h = (t - pre[l0]) / ub;
+  const int s = pre[l0] + p.h * ub + a.bal_cost;   // unit of the item's tile 0
+  p.j0 = max(0, t - s);
+  p.j1 = min(cb, hi - s);
+  const bool first = p.j0 == 0, last = p.j1 == cb;
+  p.whole = first && last;
+  p.pbase = (2 * (int64_t)blockIdx.x + (first && !last ? 1 : 0)) * a.G;
+  p.next = min(s + cb, hi);
   return p;
 }
 

@@ -131,17 +131,28 @@ gqa_status_t make_plan(const gqa_decode_desc_t* d, Plan* p, int64_t span = 0) {
   // More MFMA_QK work items (sequence, kv-head) than CUs and no forced split
   // count: balanced mode.  The work per item follows the sequence lengths, so
   // instead of one workgroup per item, one workgroup per CU takes an equal
-  // contiguous range of the batch's 16-slot tiles (cut on the device from the
-  // lengths), and the items cut between workgroups are merged by the balanced
-  // combine pass.  Its partials: two rows of G heads per workgroup.  Not for
-  // huge batches (each workgroup scans the lengths of the whole batch).  (On
-  // the large-group kernel the same mode measured slower than its splits: the
-  // scan and the extra pieces cost more than the balance gains there.)
-  int64_t tiles_max;
+  // contiguous range of the batch's units (16-slot tiles plus a per-item cost,
+  // cut on the device from the lengths), and the items cut between workgroups
+  // are merged by the balanced combine pass.  Its partials: two rows of G
+  // heads per workgroup.  Not for huge batches (each workgroup scans the
+  // lengths of the whole batch).  (On the large-group kernel the same mode
+  // measured slower than its splits: the scan and the extra pieces cost more
+  // than the balance gains there.)
+  // Each item is charged a piece's fixed cost (start-up and merge: 2.5 us on
+  // bf16 caches, 3.4 us on int8 ones, measured on MI355X) in tiles besides its
+  // own tiles, so the cut gives workgroups holding many short items fewer tiles.
+  // Less where a kv-head's slots are strided (BSHD): there how fast a tile
+  // streams depends on the kv-head, which the charge does not see, and larger
+  // charges measured slower.
+  const bool i8 = d->kv_dtype == GQA_I8;
+  const int32_t cost = d->layout == GQA_LAYOUT_BHSD ? (i8 ? kBalancedCostI8 : kBalancedCostBf16)
+                                                    : (i8 ? kBalancedCostI8Strided : kBalancedCostBf16Strided);
+  int64_t units_max;
   if (p->kernel == GQA_KERNEL_MFMA_QK && p->head_chunks == 1 && d->num_splits == 0 && B * Hkv > kNumCUs &&
-      B <= kMaxBalancedBatch && mul_ok(B * Hkv, S / 16 + 1, &tiles_max) && tiles_max < INT32_MAX) {
+      B <= kMaxBalancedBatch && mul_ok(B * Hkv, S / 16 + 1 + cost, &units_max) && units_max < INT32_MAX) {
     const size_t rows = (size_t)kNumCUs * 2 * G;
     p->balanced = 1;
+    p->bal_cost = cost;
     p->nsplit = 1;
     p->split_tokens = (int32_t)S;
     p->grid = kNumCUs;
@@ -343,6 +354,7 @@ gqa_status_t run_attend(const gqa_decode_desc_t* d, const Plan& p, AttnArgs& a, 
     a.part_l = reinterpret_cast<float*>(w + p.off_l);
     a.bal_pre = reinterpret_cast<int32_t*>(w + p.off_pre);
     a.bal_units = p.grid;
+    a.bal_cost = p.bal_cost;
   }
   switch (p.kernel) {
     case GQA_KERNEL_MFMA_QK: e = launch_attend_mfma_qk(a, p, s); break;

@@ -61,6 +61,7 @@ struct AttnArgs {
   // written by the attention pass for the combine pass), or null in split mode.
   int32_t* bal_pre;
   int32_t bal_units;     // balanced mode: workgroups of the attention pass
+  int32_t bal_cost;      // balanced mode: units charged per item besides its tiles
   int32_t nsplit, split_tokens;
   int32_t head_chunks;   // generic kernel: query-head chunks per kv-head
   int32_t len_offset;    // slots attended = lengths[b] + len_offset (1 for a step, 0 for attend)
@@ -78,7 +79,8 @@ struct Plan {
   int32_t combine;
   size_t workspace_bytes;
   size_t off_m, off_l;   // byte offsets of part_m / part_l inside the workspace
-  int32_t balanced;      // 1: equal tile ranges per workgroup (see AttnArgs::bal_pre)
+  int32_t balanced;      // 1: equal unit ranges per workgroup (see AttnArgs::bal_pre)
+  int32_t bal_cost;      // balanced mode: units charged per item besides its tiles
   size_t off_pre;        // byte offset of the tile offsets inside the workspace
 };
 
@@ -92,6 +94,12 @@ constexpr int kNumCUs = 256;          // MI355X: 8 XCDs x 32 CUs
 constexpr int kMaxSplits = 64;        // one lane per split in the combine pass
 constexpr int kGenericHeadChunk = 8;  // query heads per workgroup in the generic kernel
 constexpr int kMaxBalancedBatch = 4096;  // most sequences in the balanced mode (16 per thread of its scan)
+// Balanced mode: tiles charged per item besides its own (bf16 / int8 caches;
+// contiguous or strided slots of a kv-head), from sweeps on ragged batches.
+constexpr int kBalancedCostBf16 = 12;
+constexpr int kBalancedCostI8 = 28;
+constexpr int kBalancedCostBf16Strided = 4;
+constexpr int kBalancedCostI8Strided = 10;
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_append(const AttnArgs& a, void* k_cache, void* v_cache, hipStream_t s);

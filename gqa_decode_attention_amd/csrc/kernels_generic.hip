@@ -622,14 +622,14 @@ __global__ __launch_bounds__(256) void combine_balanced_kernel(AttnArgs a) {
   const int T = pre[a.B];
   const int W = a.bal_units;  // workgroups of the attention pass
   const int per = (T + W - 1) / W;
-  const int cb = (pre[b + 1] - pre[b]) / a.Hkv;
-  const int s0 = pre[b] + h * cb;
+  const int ub = (pre[b + 1] - pre[b]) / a.Hkv;  // units per item
+  const int cb = ub - a.bal_cost;                // tiles per item
+  const int s0 = pre[b] + h * ub + a.bal_cost;   // unit of the item's tile 0
   const int k0 = s0 / per, k1 = (s0 + cb - 1) / per;
   if (k0 == k1) return;  // whole in one workgroup: written by the attention pass
   const int np = k1 - k0 + 1;
-  auto row = [&](int i) -> int64_t {  // partial row of the i-th piece
-    const int k = k0 + i;
-    return (2 * (int64_t)k + ((i == 0 && s0 != k * per) ? 1 : 0)) * a.G + g;
+  auto row = [&](int i) -> int64_t {  // partial row of the i-th piece (the first holds the item's first tile)
+    return (2 * (int64_t)(k0 + i) + (i == 0 ? 1 : 0)) * a.G + g;
   };
   // One round of loads: m and l of the first 64 pieces (one per lane) and o
   // of the first eight (half-waves take alternate pieces), then the rest.

@@ -579,19 +579,21 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
     split_piece = pc;
   }
 
-  // Split mode: the one piece; balanced mode: the pieces of [lo, hi), in order.
-  for (int t = lo;;) {
-    Piece pc = split_piece;
-    int step = 0;
-    if (a.bal_pre != nullptr) {
-      const BalancedPiece bp = balanced_piece(a, sm_pre, t, lo, hi);
-      pc = piece_of(bp.b, bp.h, 0, 16 * bp.j0, 16 * bp.j1, bp.whole, bp.pbase, 1);
-      step = bp.j1 - bp.j0;
-    }
-    attend_piece<KV, NW, PAGED, VAR>(a, pc, sm_o, sm_m, sm_l);
-    t += step;
-    if (t >= hi) break;
-    __syncthreads();  // the next piece reuses the merge buffers
+  // Split mode: the one piece; balanced mode: the pieces of [lo, hi), in order
+  // (a range that holds only cost units of an item has no piece of it).
+  if (a.bal_pre == nullptr) {
+    attend_piece<KV, NW, PAGED, VAR>(a, split_piece, sm_o, sm_m, sm_l);
+    return;
+  }
+  bool sync = false;
+  for (int t = lo; t < hi;) {
+    const BalancedPiece bp = balanced_piece(a, sm_pre, t, hi);
+    t = bp.next;
+    if (bp.j0 >= bp.j1) continue;
+    if (sync) __syncthreads();  // the next piece reuses the merge buffers
+    sync = true;
+    attend_piece<KV, NW, PAGED, VAR>(a, piece_of(bp.b, bp.h, 0, 16 * bp.j0, 16 * bp.j1, bp.whole, bp.pbase, 1), sm_o,
+                                     sm_m, sm_l);
   }
 }
 

@@ -104,9 +104,10 @@ typedef struct {
   int32_t combine;       /* 1 if a combine pass follows the attention pass                  */
   size_t workspace_bytes;
   int32_t balanced;      /* 1 if each workgroup of the attention pass takes an equal share of
-                            the batch's 16-slot tiles, cut on the device from `lengths`
-                            (ragged batches with more (b, kv-head) items than CUs); the
-                            combine pass then merges the items cut between workgroups      */
+                            the batch's 16-slot tiles (each (b, kv-head) item also charged a
+                            fixed cost in tiles), cut on the device from `lengths` (ragged
+                            batches with more (b, kv-head) items than CUs); the combine pass
+                            then merges the items cut between workgroups                   */
 } gqa_decode_plan_t;
 
 enum {
