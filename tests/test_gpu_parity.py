@@ -479,15 +479,23 @@ def test_balanced_mode_matches_oracle(g, kind):
 @pytest.mark.parametrize("case", ["one_long", "attend_empty", "sink_bshd", "one_long_bshd", "attend_empty_g4",
                                   "window"])
 def test_balanced_mode_edge_cases(g, case):
-    """Balanced-mode cases: one long sequence among many short ones (its items
-    are cut across more than 64 workgroups, so the combine merges its partials
+    """Balanced-mode cases: one long sequence among many short ones (its item
+    is cut across more than 64 workgroups, so the combine merges its partials
     in several rounds, an odd number of them in the last), attend with empty
     sequences (zero rows, never cut), a per-head sink on a (B, S, Hkv, D)
     cache, and a sliding window with a kept prefix."""
     if case == "one_long":
-        B, Hq, Hkv, S, lay = 300, 16, 1, 20000, "BHSD"
+        B, Hq, Hkv, S, lay = 300, 16, 1, 28000, "BHSD"
         L = torch.randint(0, 40, (B,), generator=torch.Generator().manual_seed(93), dtype=torch.int32)
         L[123] = S - 1
+        # The cut as the kernels make it (16-slot tiles, 12 cost units per item for bf16 BHSD caches,
+        # 256 ranges): the long item must span more than 64 ranges, an odd number in the last round.
+        units = 12 + np.maximum(1, -(-(L.numpy().astype(np.int64) + 1) // 16))
+        pre = np.concatenate([[0], np.cumsum(units)])
+        per = -(-int(pre[-1]) // 256)
+        first, last = pre[123] + 12, pre[123 + 1] - 1
+        pieces = int(last // per - first // per + 1)
+        assert pieces > 64 and (pieces - 64) % 2 == 1, pieces
     elif case == "one_long_bshd":
         B, Hq, Hkv, S, lay = 150, 8, 2, 9000, "BSHD"
         L = torch.randint(0, 40, (B,), generator=torch.Generator().manual_seed(98), dtype=torch.int32)
