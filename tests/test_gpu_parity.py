@@ -476,6 +476,56 @@ def test_balanced_mode_matches_oracle(g, kind):
     assert np_of(inp["k_cache"]).tobytes() == rk.tobytes() and np_of(inp["v_cache"]).tobytes() == rv.tobytes()
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_balanced_mode_random_shapes(g, seed):
+    """Balanced mode on seeded random shapes: batch, group size, capacity,
+    layout and cache dtype drawn at random (always more (b, kv-head) items than
+    CUs), and lengths from one of three mixes (all short, heavy-tailed, or
+    uniform with zeros and full sequences), so workgroup ranges start and end
+    inside items' charged cost units, inside their tiles and on their edges."""
+    rng = np.random.default_rng(1000 + seed)
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([1, 2, 4, 8, 16]))
+    B = int(rng.integers(256 // Hkv + 1, 256 // Hkv + 120))
+    S = int(rng.integers(40, 1200))
+    lay = str(rng.choice(["BHSD", "BSHD"]))
+    kv = "i8" if seed % 2 else "bf16"
+    mix = seed % 3
+    if mix == 0:
+        L = rng.integers(0, min(S, 48), B)
+    elif mix == 1:
+        L = np.minimum(S - 1, (rng.pareto(1.2, B) * 20).astype(np.int64))
+    else:
+        L = rng.integers(0, S, B)
+        L[rng.integers(0, B, 3)] = 0
+        L[rng.integers(0, B, 3)] = S - 1
+    L = torch.from_numpy(L.astype(np.int32))
+    Hq = Hkv * G
+    say(f"balanced random seed={seed}: B={B} Hq={Hq} Hkv={Hkv} S={S} {lay} {kv} mix={mix}")
+    desc = g.make_desc(B, Hq, Hkv, 128, S, lay, g.I8 if kv == "i8" else g.BF16, g.BF16)
+    assert g.get_plan(desc)["balanced"]
+    w = W.custom(B, Hq, Hkv, 128, S, lay, kv, "bf16", seed=200 + seed, stale="pm:1")
+    if kv == "i8":
+        inp = W.make_q8(w, DEV, lengths=L)
+        ref, rk, rv, rks, rvs = oracle.step_q8(np_of(inp["q"]), "bf16", np_of(inp["k_cache"]), np_of(inp["v_cache"]),
+                                               np_of(inp["k_scale"]), np_of(inp["v_scale"]), np_of(inp["k_new"]),
+                                               np_of(inp["v_new"]), L.numpy(), lay, Hq, Hkv)
+        out = g.step_q8(inp["q"], inp["k_cache"], inp["v_cache"], inp["k_scale"], inp["v_scale"], inp["k_new"],
+                        inp["v_new"], inp["lengths"], layout=lay)
+        torch.cuda.synchronize()
+        assert_close(out, ref, "bf16", "int8 step")
+        for name, want in (("k_cache", rk), ("v_cache", rv), ("k_scale", rks), ("v_scale", rvs)):
+            assert np_of(inp[name]).tobytes() == want.tobytes(), name
+        return
+    inp = W.make_inputs(w, DEV, lengths=L)
+    ref, rk, rv = oracle_step(inp, w)
+    out = g.step(inp["q"], inp["k_cache"], inp["v_cache"], inp["k_new"], inp["v_new"], inp["lengths"], layout=lay)
+    torch.cuda.synchronize()
+    assert_close(out, ref, "bf16", "step")
+    assert np_of(inp["k_cache"]).tobytes() == rk.tobytes()
+    assert np_of(inp["v_cache"]).tobytes() == rv.tobytes()
+
+
 @pytest.mark.parametrize("case", ["one_long", "attend_empty", "sink_bshd", "one_long_bshd", "attend_empty_g4",
                                   "window"])
 def test_balanced_mode_edge_cases(g, case):
