@@ -692,17 +692,17 @@ gqa_status_t do_attend(const gqa_decode_desc_t* desc, const gqa_decode_opts_t* o
       a.k_new = nullptr;
       a.v_new = nullptr;
       a.rope_cos = nullptr;  // the attention pass reads the rotated q and key as they are
-    } else if (sc != nullptr && p.kernel != GQA_KERNEL_MFMA_QK) {
-      // Int8 caches, generic and large-group paths: the quantizing append,
-      // then attention over lengths[b] + 1 slots (the new token is attended in
-      // its stored, quantized form).
+    } else if (sc != nullptr && p.kernel == GQA_KERNEL_GENERIC) {
+      // Int8 caches, generic path: the quantizing append, then attention over
+      // lengths[b] + 1 slots (the new token is attended in its stored,
+      // quantized form).
       a.k_scale_w = sc->k_scale;
       a.v_scale_w = sc->v_scale;
       if (launch_append_q8(a, k_cache, v_cache, (hipStream_t)stream) != hipSuccess) return GQA_ERR_HIP;
       a.k_new = nullptr;
       a.v_new = nullptr;
     } else if (sc != nullptr) {
-      // Int8 caches, matrix-core path: the workgroup whose split holds slot
+      // Int8 caches, matrix-core paths: the workgroup whose split holds slot
       // lengths[b] quantizes the new rows itself, attends them in their
       // quantized form and stores codes and scales.
       a.k_scale_w = sc->k_scale;

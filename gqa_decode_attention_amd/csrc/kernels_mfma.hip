@@ -89,15 +89,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 
-// Int8 caches (KV = GQA_I8, dense, attend only: a step quantizes its new
-// rows with the append kernel first).  Rows are 128 codes with a float32
+// Int8 caches (KV = GQA_I8, dense).  Rows are 128 codes with a float32
 // scale each (Huawei CANN "aclnnMlaPrologV3WeightNz" page, dynamic
 // quantization: a cached value reads as code * row scale).  Thread t loads 16
 // codes (bytes 16 (t & 7) ..) of row t >> 3 of the K and V tiles with the
 // rows' scales; the codes are widened exactly to bf16 (|code| <= 127) as they
 // are written to LDS, so the tile math is that of bf16 caches, with each
 // slot's score times its key scale and its weight times its value scale in
-// the V sum (the denominator sums the unscaled weights).
+// the V sum (the denominator sums the unscaled weights).  In a step the
+// workgroup whose split holds slot L quantizes the new rows itself (per-row
+// rule: float32 row maximum, scale = max / 127, codes = round-half-even(x /
+// scale) with correctly rounded divisions, clamped to +-127; a zero row has
+// scale 0 and codes 0), attends them in that form and stores codes and scales.
 template <int KV, bool PAGED, bool VAR>
 __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
   static_assert(!(PAGED && KV == GQA_I8), "int8 caches are dense");
@@ -193,8 +196,48 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
     u32x4 k[2], v[2];
     float ks, vs;  // int8: the scales of row t >> 3 (codes in k[0], v[0])
   };
-  u32x4 kn = {0u, 0u, 0u, 0u}, vn = {0u, 0u, 0u, 0u};
-  if (own_new) {
+  u32x4 kn = {0u, 0u, 0u, 0u}, vn = {0u, 0u, 0u, 0u};  // int8: the codes of elements 16 (t & 7) ..
+  float ksn = 0.f, vsn = 0.f;                          // int8: the new rows' scales
+  if (Q8 && own_new) {
+    // Thread t quantizes elements 16 (t & 7) .. + 15 of the new rows; the row
+    // maxima reduce over the 8 threads that hold a row.
+    const uint16_t* knp = reinterpret_cast<const uint16_t*>(a.k_new) + nrow + 16 * (tid & 7);
+    const uint16_t* vnp = reinterpret_cast<const uint16_t*>(a.v_new) + nrow + 16 * (tid & 7);
+    float kx[16], vx[16];
+    widen16<GQA_BF16>(load16(knp), kx);
+    widen16<GQA_BF16>(load16(knp + 8), kx + 8);
+    widen16<GQA_BF16>(load16(vnp), vx);
+    widen16<GQA_BF16>(load16(vnp + 8), vx + 8);
+    float km = 0.f, vm = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      km = fmaxf(km, fabsf(kx[e]));
+      vm = fmaxf(vm, fabsf(vx[e]));
+    }
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) {
+      km = fmaxf(km, __shfl_xor(km, off));
+      vm = fmaxf(vm, __shfl_xor(vm, off));
+    }
+    ksn = km / 127.0f;
+    vsn = vm / 127.0f;
+    auto code = [](float x, float amax, float sc) -> uint32_t {
+      const float q = amax > 0.f ? fminf(fmaxf(rintf(x / sc), -127.f), 127.f) : 0.f;
+      return (uint32_t)(int32_t)q & 0xffu;
+    };
+#pragma unroll
+    for (int wd = 0; wd < 4; ++wd) {
+      uint32_t kw = 0, vw = 0;
+#pragma unroll
+      for (int by = 0; by < 4; ++by) {
+        kw |= code(kx[4 * wd + by], km, ksn) << (8 * by);
+        vw |= code(vx[4 * wd + by], vm, vsn) << (8 * by);
+      }
+      kn[wd] = kw;
+      vn[wd] = vw;
+    }
+  }
+  if (!Q8 && own_new) {
     kn = load16(reinterpret_cast<const uint16_t*>(a.k_new) + nrow + 8 * piece);
     vn = load16(reinterpret_cast<const uint16_t*>(a.v_new) + nrow + 8 * piece);
     if (rope) {
@@ -300,6 +343,25 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
       if ((tid & 7) == 0) {
         sks[buf][row] = R.ks;
         svs[buf][row] = R.vs;
+      }
+      if (own_new && t0 + kTileT > L) {  // uniform: the tile holding the new token; rows >= L take it
+        if (t0 + row >= L) {
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            widen16<GQA_I8>(hh ? vn : kn, x);
+            const u32x4 lo = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                              pack_bf16x2(x[6], x[7])};
+            const u32x4 hi = {pack_bf16x2(x[8], x[9]), pack_bf16x2(x[10], x[11]), pack_bf16x2(x[12], x[13]),
+                              pack_bf16x2(x[14], x[15])};
+            uint16_t* dst = (hh ? sv[buf] : sk[buf]) + row * kPitch + col;
+            *reinterpret_cast<u32x4*>(dst) = lo;
+            *reinterpret_cast<u32x4*>(dst + 8) = hi;
+          }
+          if ((tid & 7) == 0) {
+            sks[buf][row] = ksn;
+            svs[buf][row] = vsn;
+          }
+        }
       }
       return;
     }
@@ -449,11 +511,22 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
     if (ntile & 1) compute_tile(t0, buf);
   }
 
-  if (own_new && prow == 0) {  // the appended slot (skipped if the map names no valid row/block)
+  if (!Q8 && own_new && prow == 0) {  // the appended slot (skipped if the map names no valid row/block)
     const int64_t off = slot_offset_checked(a, b, h, L0);
     if (off >= 0) {
       store16(reinterpret_cast<uint16_t*>(a.k_cache_w) + off + 8 * piece, kn);
       store16(reinterpret_cast<uint16_t*>(a.v_cache_w) + off + 8 * piece, vn);
+    }
+  }
+  if (Q8 && own_new && tid < 8) {  // int8: the appended slot's codes and scales
+    const int64_t off = slot_offset_checked(a, b, h, L0);
+    if (off >= 0) {
+      store16(reinterpret_cast<int8_t*>(a.k_cache_w) + off + 16 * tid, kn);
+      store16(reinterpret_cast<int8_t*>(a.v_cache_w) + off + 16 * tid, vn);
+      if (tid == 0) {
+        a.k_scale_w[off / kD] = ksn;
+        a.v_scale_w[off / kD] = vsn;
+      }
     }
   }
 
@@ -492,9 +565,11 @@ hipError_t launch_attend_mfma_all(const AttnArgs& a, const Plan& p, hipStream_t 
   const bool paged = a.map_kind == GQA_MAP_PAGED;
   const void* fn;
   if (a.kv_dtype == GQA_I8) {
-    // Int8 caches: dense, attend only (a step appends its quantized rows first).
-    if (a.map_kind != 0 || a.k_new != nullptr || a.rope_cos != nullptr || a.k_scale == nullptr ||
-        a.v_scale == nullptr || a.qo_dtype != GQA_BF16)
+    // Int8 caches: dense; a step quantizes its new rows in the kernel (no rotary encoding:
+    // a rotary step appends the rotated, quantized rows first).
+    if (a.map_kind != 0 || a.rope_cos != nullptr || a.k_scale == nullptr || a.v_scale == nullptr ||
+        a.qo_dtype != GQA_BF16 ||
+        (a.k_new != nullptr && (a.k_cache_w == nullptr || a.k_scale_w == nullptr || a.v_scale_w == nullptr)))
       return hipErrorInvalidValue;
     fn = var ? reinterpret_cast<const void*>(&attend_mfma_all_kernel<GQA_I8, false, true>)
              : reinterpret_cast<const void*>(&attend_mfma_all_kernel<GQA_I8, false, false>);

@@ -64,8 +64,8 @@ CASES = [
     (2, 4, 1, 256, 100, "BHSD", "bf16", 0),        # largest head
     (4, 8, 8, 80, 64, "BSHD", "bf16", 0),          # G=1
     (2, 8, 2, 7, 50, "BHSD", "f32", 0),            # odd head_dim
-    (3, 48, 2, 128, 600, "BSHD", "bf16", 2),       # G=24: two 16-head chunks (16 + 8)
-    (2, 64, 1, 128, 700, "BHSD", "bf16", 3),       # G=64: four chunks, forced splits
+    (3, 48, 2, 128, 600, "BSHD", "bf16", 2),       # G=24 on the large-group kernel (one partly used head block)
+    (2, 64, 1, 128, 700, "BHSD", "bf16", 3),       # G=64, forced splits
 ]
 
 
@@ -126,6 +126,40 @@ def test_q8_append_alone_with_ties_and_zero_rows(g, qo):
     g.append_q8(inp["k_cache"], inp["v_cache"], inp["k_scale"], inp["v_scale"], inp["k_new"], inp["v_new"],
                 inp["lengths"], layout="BHSD")
     torch.cuda.synchronize()
+    assert_same_bytes(inp["k_cache"], rk, "k codes")
+    assert_same_bytes(inp["v_cache"], rv, "v codes")
+    assert_same_bytes(inp["k_scale"], rks, "k scales")
+    assert_same_bytes(inp["v_scale"], rvs, "v scales")
+
+
+@pytest.mark.parametrize("Hq", [8, 64], ids=["G4-small-group-kernel", "G32-large-group-kernel"])
+def test_q8_step_quantizes_ties_and_zero_rows_in_kernel(g, Hq):
+    """The matrix-core kernels quantize a step's new rows themselves: rows
+    whose x / scale lands exactly on .5 (largest magnitude 127, so scale 1),
+    their negation, and a zero value row (scale 0, codes 0) must give the
+    oracle's codes and scales bit for bit, and the attention over them its
+    output."""
+    B, Hkv, D, S = 3, 2, 128, 200
+    w = W.custom(B, Hq, Hkv, D, S, "BHSD", "i8", "bf16", seed=43, stale="pm:1")
+    L = torch.tensor([0, 57, S - 1], dtype=torch.int32)
+    inp = W.make_q8(w, DEV, lengths=L)
+    tie = torch.tensor([127, 0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 3.5, 126.5, -126.5, 0, 4.5, 5.5, -3.5, 1, 2],
+                       dtype=torch.float32).repeat(D // 16)
+    inp["k_new"][0, 0] = tie.to(torch.bfloat16).to(DEV)
+    inp["k_new"][1, 1] = (-tie).to(torch.bfloat16).to(DEV)
+    inp["v_new"][2, 0] = 0
+    inp["v_new"][1, 0] = tie.to(torch.bfloat16).to(DEV)
+    desc = g.make_desc(B, Hq, Hkv, D, S, "BHSD", g.I8, g.BF16)
+    assert g.get_plan(desc)["kernel"] == ("mfma_qk" if Hq // Hkv <= 16 else "mfma_all")
+    ref, rk, rv, rks, rvs = oracle.step_q8(np_of(inp["q"]), "bf16", np_of(inp["k_cache"]), np_of(inp["v_cache"]),
+                                           np_of(inp["k_scale"]), np_of(inp["v_scale"]), np_of(inp["k_new"]),
+                                           np_of(inp["v_new"]), L.numpy(), "BHSD", Hq, Hkv)
+    assert rks[0, 0, 0] == 1.0 and list(rk[0, 0, 0, :4]) == [127, 0, 2, 2]      # the oracle rounds half to even
+    assert rvs[2, 0, S - 1] == 0.0
+    out = g.step_q8(inp["q"], inp["k_cache"], inp["v_cache"], inp["k_scale"], inp["v_scale"], inp["k_new"],
+                    inp["v_new"], inp["lengths"], layout="BHSD")
+    torch.cuda.synchronize()
+    assert_close(out, ref, "bf16", "int8 step")
     assert_same_bytes(inp["k_cache"], rk, "k codes")
     assert_same_bytes(inp["v_cache"], rv, "v codes")
     assert_same_bytes(inp["k_scale"], rks, "k scales")
