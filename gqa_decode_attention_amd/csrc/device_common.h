@@ -47,6 +47,9 @@ template <> struct Store<0> {  // float32
   __device__ static __forceinline__ void store1(void* base, int64_t i, float x) {
     reinterpret_cast<float*>(base)[i] = x;
   }
+  __device__ static __forceinline__ void copy1(void* dst, int64_t i, const void* src, int64_t j) {
+    reinterpret_cast<uint32_t*>(dst)[i] = reinterpret_cast<const uint32_t*>(src)[j];
+  }
 };
 template <> struct Store<1> {  // bfloat16
   static constexpr int kBytes = 2;
@@ -58,6 +61,9 @@ template <> struct Store<1> {  // bfloat16
   }
   __device__ static __forceinline__ void store1(void* base, int64_t i, float x) {
     reinterpret_cast<uint16_t*>(base)[i] = f32_to_bf16_rne(x);
+  }
+  __device__ static __forceinline__ void copy1(void* dst, int64_t i, const void* src, int64_t j) {
+    reinterpret_cast<uint16_t*>(dst)[i] = reinterpret_cast<const uint16_t*>(src)[j];
   }
 };
 

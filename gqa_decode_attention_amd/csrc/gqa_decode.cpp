@@ -361,7 +361,8 @@ gqa_status_t run_attend(const gqa_decode_desc_t* d, const Plan& p, AttnArgs& a, 
     case GQA_KERNEL_MFMA_ALL: e = launch_attend_mfma_all(a, p, s); break;
     default: {
       const size_t ekv = elem_bytes(d->kv_dtype);
-      const bool vec = (d->head_dim * ekv) % 16 == 0 && aligned(a.k_cache, 16) && aligned(a.v_cache, 16);
+      const bool vec = (d->head_dim * ekv) % 16 == 0 && aligned(a.k_cache, 16) && aligned(a.v_cache, 16) &&
+                       (a.k_new == nullptr || (aligned(a.k_new, 16) && aligned(a.v_new, 16)));
       e = launch_attend_generic(a, p, vec ? 1 : 0, s);
     }
   }
@@ -709,16 +710,10 @@ gqa_status_t do_attend(const gqa_decode_desc_t* desc, const gqa_decode_opts_t* o
       a.v_scale_w = sc->v_scale;
       a.k_cache_w = k_cache;
       a.v_cache_w = v_cache;
-    } else if (p.kernel == GQA_KERNEL_GENERIC) {
-      // Generic path: the append kernel, then attention over lengths[b] + 1
-      // slots, ordered by the stream.
-      if (launch_append(a, k_cache, v_cache, (hipStream_t)stream) != hipSuccess) return GQA_ERR_HIP;
-      a.k_new = nullptr;
-      a.v_new = nullptr;
     } else {
-      // Matrix-core paths fuse the append: the workgroup whose split holds
-      // slot lengths[b] takes the new K/V from k_new/v_new and writes it to
-      // the cache; no other workgroup reads that slot.
+      // Every kernel fuses the append: the workgroup whose split holds slot
+      // lengths[b] takes the new K/V from k_new/v_new and writes it to the
+      // cache (one head chunk of it); no other workgroup reads that slot.
       a.k_cache_w = k_cache;
       a.v_cache_w = v_cache;
     }

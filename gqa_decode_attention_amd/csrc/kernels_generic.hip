@@ -334,11 +334,22 @@ __global__ __launch_bounds__(256) void attend_generic_kernel(AttnArgs a) {
 
   const char* kb = reinterpret_cast<const char*>(a.k_cache);
   const char* vb = reinterpret_cast<const char*>(a.v_cache);
+  // Fused step (float32 / bf16 caches): the new token, virtual slot Lv, is
+  // read from k_new / v_new instead of the cache, and head chunk 0 of the
+  // split that holds it stores it at slot lengths[b] after the loop.  No other
+  // workgroup reads that slot (the other head chunks take it from k_new too).
+  const int L0 = a.lengths[b];
+  const int Lv = L0 - view.gap;
+  const bool fused_new = KV != GQA_I8 && a.k_new != nullptr;
+  const int64_t nrow = ((int64_t)b * a.Hkv + h) * D;
 
   for (int t = t_begin + rg; t < t_end; t += NRG) {
     const int tp = phys_slot(view, t);
     if (unattended(view, tp)) continue;  // uniform within the row group
-    const int64_t row = slot_offset(a, b, h, tp);
+    const bool is_new = fused_new && t == Lv;
+    const int64_t row = is_new ? nrow : slot_offset(a, b, h, tp);
+    const char* kbr = is_new ? reinterpret_cast<const char*>(a.k_new) : kb;
+    const char* vbr = is_new ? reinterpret_cast<const char*>(a.v_new) : vb;
     float kv[EPL], vv[EPL];
     float ks = 1.f, vs = 1.f;  // int8 caches: the row scales
     if constexpr (KV == GQA_I8) {
@@ -350,15 +361,15 @@ __global__ __launch_bounds__(256) void attend_generic_kernel(AttnArgs a) {
       const int d0 = (c * LPR + rl) * VEC;
       if constexpr (VEC > 1) {
         if (d0 < D) {
-          widen16<KV>(load_nt16(kb + (row + d0) * KB), &kv[c * VEC]);
-          widen16<KV>(load_nt16(vb + (row + d0) * KB), &vv[c * VEC]);
+          widen16<KV>(load_nt16(kbr + (row + d0) * KB), &kv[c * VEC]);
+          widen16<KV>(load_nt16(vbr + (row + d0) * KB), &vv[c * VEC]);
         } else {
 #pragma unroll
           for (int e = 0; e < VEC; ++e) kv[c * VEC + e] = vv[c * VEC + e] = 0.f;
         }
       } else {
-        kv[c] = d0 < D ? Store<KV>::load1(kb, row + d0) : 0.f;
-        vv[c] = d0 < D ? Store<KV>::load1(vb, row + d0) : 0.f;
+        kv[c] = d0 < D ? Store<KV>::load1(kbr, row + d0) : 0.f;
+        vv[c] = d0 < D ? Store<KV>::load1(vbr, row + d0) : 0.f;
       }
     }
 #pragma unroll
@@ -445,6 +456,17 @@ __global__ __launch_bounds__(256) void attend_generic_kernel(AttnArgs a) {
       if (d == 0) {
         a.part_m[pi] = M;
         a.part_l[pi] = L;
+      }
+    }
+  }
+  if constexpr (KV != GQA_I8) {
+    if (fused_new && hc == 0 && Lv >= t_begin && Lv < t_end) {  // the appended slot (raw bits)
+      const int64_t off = slot_offset_checked(a, b, h, L0);
+      if (off >= 0) {
+        for (int d = threadIdx.x; d < D; d += 256) {
+          Store<KV>::copy1(a.k_cache_w, off + d, a.k_new, nrow + d);
+          Store<KV>::copy1(a.v_cache_w, off + d, a.v_new, nrow + d);
+        }
       }
     }
   }
