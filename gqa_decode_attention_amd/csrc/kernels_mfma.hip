@@ -1,6 +1,6 @@
 // Matrix-core (MFMA) attention kernel of the GQA decode step for gfx950 for
-// large groups (16 < G <= 64), bf16 storage, head width 128.  (Groups of up to
-// 16 query heads run the kernel in kernels_mfma_qkv.hip.)
+// large groups (16 < G <= 64), bf16 or int8 storage, head width 128.  (Groups
+// of up to 16 query heads run the kernel in kernels_mfma_qkv.hip.)
 //
 // What is computed is the JAX "Grouped-Query Decode Step" page's definition
 // (query head h reads cache head floor(h/G); s_j = q.K_j/sqrt(D) over the
