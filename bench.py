@@ -195,6 +195,14 @@ def main():
                       prefix=args.kept_prefix)
     desc = g.desc_for(inp["q"], inp["k_cache"], w.layout, args.num_splits)
     plan = g.get_plan(desc)
+    if args.window > 0:
+        # With a window known on the host the library plans its splits over the
+        # slots a sequence can walk (window + kept prefix + 32), not the
+        # capacity: that plan is the one of a descriptor of that capacity.
+        span = min(desc.capacity, args.window + args.kept_prefix + 32)
+        plan = dict(g.get_plan(g.make_desc(desc.batch, desc.num_q_heads, desc.num_kv_heads, desc.head_dim, span,
+                                           w.layout, desc.kv_dtype, desc.qo_dtype, args.num_splits)),
+                    planned_span=span)
     kind, table = None, None
     inp_dense = inp
     if args.cache != "dense":
