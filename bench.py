@@ -130,6 +130,73 @@ def calibration_copy(mib: int, reps: int = 5):
     print(json.dumps({"calibration_copy_bytes_per_launch": mib << 20, "launches": reps}), flush=True)
 
 
+def time_replay(step, steps: int, warmup: int, graph: bool = True) -> float:
+    """Mean milliseconds per step over `steps` steps after `warmup` untimed ones:
+    the timed steps are captured once in a HIP graph and replayed (graph=False:
+    launched one by one), between HIP events on the stream they run on."""
+    import torch
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    g = None
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(g, stream=side):
+            for i in range(steps):
+                step(i)
+        torch.cuda.synchronize()
+        g.replay()  # untimed: the graph's own first launch
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    if g is not None:
+        g.replay()
+    else:
+        for i in range(steps):
+            step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def measure_plain(name: str, steps: int, warmup: int, graph: bool = True) -> dict:
+    """One workload's plain step (dense caches in its own storage type, no
+    options), timed as the headline is: the per-config entry of the JSON line."""
+    import torch
+    import gqa_decode_attention_amd as g
+    import workloads as W
+    w = W.WORKLOADS[name]
+    inp = W.make_inputs(w, "cuda")
+    L = inp["lengths"].cpu().numpy()
+    nbytes = W.algorithmic_bytes(w, L)
+    kv_bytes = 2 * inp["k_cache"].numel() * inp["k_cache"].element_size()
+    R = min(16, math.ceil(3 * MALL_BYTES / kv_bytes)) if 16 * kv_bytes >= MALL_BYTES else 1
+    caches = [(inp["k_cache"], inp["v_cache"])] + [(inp["k_cache"].clone(), inp["v_cache"].clone())
+                                                   for _ in range(R - 1)]
+    desc = g.desc_for(inp["q"], inp["k_cache"], w.layout)
+    plan = g.get_plan(desc)
+    ws = torch.empty(max(plan["workspace_bytes"], 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(inp["q"])
+
+    def step(i):
+        kc, vc = caches[i % R]
+        g.step(inp["q"], kc, vc, inp["k_new"], inp["v_new"], inp["lengths"], layout=w.layout, out=out, workspace=ws)
+
+    ms = time_replay(step, steps, warmup, graph)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    traffic = traffic_from_profiles(name)
+    entry = {"us_per_step": round(ms * 1e3, 3), "steps_per_sec": round(1000.0 / ms, 1), "gbs": round(gbs, 1),
+             "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_step": nbytes, "cache_rotation": R,
+             "plan": plan, "traffic_ratio": None if traffic is None else round(traffic / nbytes, 4)}
+    if name == "tiny":
+        entry["note"] = "launch-latency bound (at most 1.4 KB per step); frac shown, not meaningful"
+    del caches, inp, ws, out
+    torch.cuda.empty_cache()
+    return entry
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -152,6 +219,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch the timed steps one by one instead of replaying them from one HIP graph")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="skip the per_config timings of the five workloads' plain steps")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="only run a plain copy of this many MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -262,37 +331,24 @@ def main():
             g.step_mapped(inp["q"], kc, vc, inp["k_new"], inp["v_new"], inp["lengths"], table, kind=kind,
                           layout=w.layout, out=out, workspace=ws, num_splits=args.num_splits, table_host=table_host)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    graph = None
-    if not args.no_graph:
-        # The K timed steps (cache copies rotating as in the eager loop) are
-        # captured once into a HIP graph and replayed: the library launches only
-        # kernels (no host sync, no memset), so the replay is the same work
-        # without the per-call host marshalling and launch latency.
-        graph = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.graph(graph, stream=side):
-            for i in range(args.steps):
-                step(i)
-        torch.cuda.synchronize()
-        graph.replay()  # untimed: the graph's own first launch
-        torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # The K timed steps (cache copies rotating as in the eager loop) are
+    # captured once into a HIP graph and replayed: the library launches only
+    # kernels (no host sync, no memset), so the replay is the same work without
+    # the per-call host marshalling and launch latency.
     t0 = time.perf_counter()
-    e0.record()
-    if graph is not None:
-        graph.replay()
-    else:
-        for i in range(args.steps):
-            step(i)
-    e1.record()
-    torch.cuda.synchronize()
+    ms = time_replay(step, args.steps, args.warmup, graph=not args.no_graph)
     wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / args.steps
     gbs = nbytes / (ms * 1e-3) / 1e9
+    del caches
+    torch.cuda.empty_cache()
+
+    # Every workload's plain step, timed the same way in the same run.
+    per_config = None
+    if not args.no_per_config:
+        per_config = {}
+        for name in ("tiny", "llama3_8b_layer", "ragged_batch", "long_context", "large_group"):
+            per_config[name] = measure_plain(name, args.steps, args.warmup, graph=not args.no_graph)
+            print(json.dumps({"per_config": name, **per_config[name]}), file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -313,11 +369,14 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
+        "dtype_detail": ("scores, softmax and sums in float32; on the matrix-core kernels each softmax weight "
+                         "enters the V-sum MFMA as a bf16 hi + lo pair (about 16 significant bits) with float32 "
+                         "accumulation"),
         "storage_dtype": kv,
         "data": "synthetic",
         "steps_per_sec": round(1000.0 / ms, 2),
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
-        "config": {"workload": w.name, "launch": "eager" if graph is None else "hip_graph", "cache": args.cache, "rope": args.rope, "window": args.window,
+        "config": {"workload": w.name, "launch": "eager" if args.no_graph else "hip_graph", "cache": args.cache, "rope": args.rope, "window": args.window,
                    "kept_prefix": args.kept_prefix, "softcap": args.softcap, "sink": args.sink, "batch": w.B, "num_q_heads": w.Hq, "num_kv_heads": w.Hkv, "head_dim": w.D,
                    "capacity": w.capacity, "layout": w.layout, "kv_dtype": w.kv_dtype, "qo_dtype": w.qo_dtype,
                    "tokens_attended": int(n_att.sum()), "algorithmic_bytes_per_step": nbytes,
@@ -329,6 +388,7 @@ def main():
                      "per": "one gqa_decode_step call (attention kernel + split combine), HIP events over the "
                             "timed region on the stream the steps run on"},
         "cpu_baseline": cpu,
+        "per_config": per_config,
         "wall_s_timed": round(wall, 4),
     }
     print(json.dumps(line), flush=True)

@@ -36,6 +36,7 @@ from ._lib import (  # noqa: F401
     check_lengths,
     desc_for,
     get_plan,
+    get_plan_ex,
     lib,
     make_desc,
     step,

@@ -132,6 +132,7 @@ EXPORTS = (
     "gqa_decode_attend_q8",
     "gqa_decode_step_q8",
     "gqa_decode_workspace_size_ex",
+    "gqa_decode_get_plan_ex",
     "gqa_decode_append_ex",
     "gqa_decode_attend_ex",
     "gqa_decode_step_ex",
@@ -169,13 +170,14 @@ def lib() -> ctypes.CDLL:
     L.gqa_decode_step_q8.argtypes = [DP, SP, P, P, P, P, P, I32P, P, P, S, P]
     OP = ctypes.POINTER(OptsT)
     L.gqa_decode_workspace_size_ex.argtypes = [DP, OP, ctypes.POINTER(ctypes.c_size_t)]
+    L.gqa_decode_get_plan_ex.argtypes = [DP, OP, ctypes.POINTER(PlanT)]
     L.gqa_decode_append_ex.argtypes = [DP, OP, P, P, P, P, I32P, P]
     L.gqa_decode_attend_ex.argtypes = [DP, OP, P, P, P, I32P, P, P, S, P]
     L.gqa_decode_step_ex.argtypes = [DP, OP, P, P, P, P, P, I32P, P, P, S, P]
     for name in ("gqa_decode_workspace_size", "gqa_decode_get_plan", "gqa_decode_append", "gqa_decode_attend",
                  "gqa_decode_step", "gqa_decode_check_lengths", "gqa_decode_append_mapped",
                  "gqa_decode_attend_mapped", "gqa_decode_step_mapped", "gqa_decode_append_q8",
-                 "gqa_decode_attend_q8", "gqa_decode_step_q8", "gqa_decode_workspace_size_ex",
+                 "gqa_decode_attend_q8", "gqa_decode_step_q8", "gqa_decode_workspace_size_ex", "gqa_decode_get_plan_ex",
                  "gqa_decode_append_ex", "gqa_decode_attend_ex", "gqa_decode_step_ex"):
         getattr(L, name).restype = ctypes.c_int
     L.gqa_decode_status_string.argtypes = [ctypes.c_int]
@@ -231,6 +233,18 @@ def workspace_size(desc: Desc) -> int:
 def get_plan(desc: Desc) -> dict:
     p = PlanT()
     check(lib().gqa_decode_get_plan(ctypes.byref(desc), ctypes.byref(p)), "gqa_decode_get_plan")
+    return _plan_dict(p)
+
+
+def get_plan_ex(desc: Desc, opts) -> dict:
+    """The plan of an attend/step call with options (an OptsT, or None)."""
+    p = PlanT()
+    check(lib().gqa_decode_get_plan_ex(ctypes.byref(desc), None if opts is None else ctypes.byref(opts),
+                                       ctypes.byref(p)), "gqa_decode_get_plan_ex")
+    return _plan_dict(p)
+
+
+def _plan_dict(p: PlanT) -> dict:
     return dict(kernel=KERNEL_NAMES.get(p.kernel, p.kernel), num_splits=p.num_splits, split_tokens=p.split_tokens,
                 grid=p.grid, block=p.block, combine=bool(p.combine), workspace_bytes=p.workspace_bytes,
                 balanced=bool(p.balanced))
@@ -381,7 +395,7 @@ def attend_mapped(q, k_cache, v_cache, lengths, table, *, kind, layout="BHSD", o
                                  table, num_splits, None, table_host)
     if out is None:
         out = torch.empty_like(q)
-    workspace, wptr, wbytes = _workspace(desc, dev, workspace)
+    workspace, wptr, wbytes = _workspace_ex(desc, OptsT(ctypes.pointer(m), None, None, None), dev, workspace)
     check(lib().gqa_decode_attend_mapped(ctypes.byref(desc), ctypes.byref(m), q.data_ptr(), k_cache.data_ptr(),
                                          v_cache.data_ptr(), lengths.data_ptr(), out.data_ptr(), wptr, wbytes,
                                          _stream(dev)), "gqa_decode_attend_mapped")
@@ -398,7 +412,7 @@ def step_mapped(q, k_cache, v_cache, k_new, v_new, lengths, table, *, kind, layo
                                  table, num_splits, k_new.shape[1], table_host)
     if out is None:
         out = torch.empty_like(q)
-    workspace, wptr, wbytes = _workspace(desc, dev, workspace)
+    workspace, wptr, wbytes = _workspace_ex(desc, OptsT(ctypes.pointer(m), None, None, None), dev, workspace)
     check(lib().gqa_decode_step_mapped(ctypes.byref(desc), ctypes.byref(m), q.data_ptr(), k_cache.data_ptr(),
                                        v_cache.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), lengths.data_ptr(),
                                        out.data_ptr(), wptr, wbytes, _stream(dev)), "gqa_decode_step_mapped")

@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libgqa_decode.so")
 
-SOURCES = ["gqa_decode.cpp", "kernels_generic.hip", "kernels_mfma.hip", "kernels_mfma_qkv.hip"]
+# Every C++ and HIP source of csrc/ goes into the one library.
+SOURCES = sorted(f for f in os.listdir(CSRC) if f.endswith((".cpp", ".hip")))
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

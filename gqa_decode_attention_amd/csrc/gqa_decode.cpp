@@ -2,14 +2,15 @@
 //
 // Every condition the host can check is checked before the first HIP call,
 // so an error return means nothing was enqueued (CLIKA groupQueryAttention
-// page: validate the whole input before any read, refuse with
-// INVALID_ARGUMENT; CANN aclnnMlaPrologV3WeightNz page: the first phase
+// page: every argument is checked before any data is read, and a malformed
+// one is refused with INVALID_ARGUMENT; CANN aclnnMlaPrologV3WeightNz page: the first phase
 // verifies parameters and reports the workspace size).  The plan -- kernel,
 // split of the token axis, grid, workspace -- is a pure function of the
 // descriptor: `lengths` stays on the device and is never read here.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -77,17 +78,35 @@ int32_t choose_kernel(const gqa_decode_desc_t* d) {
   return GQA_KERNEL_GENERIC;
 }
 
-// Plan: a pure function of the descriptor.
+// Compute units of the current device, read once per device; without a
+// visible device (host-only planning) the MI355X count.
+int32_t device_cus() {
+  constexpr int kMaxDev = 256;
+  static std::atomic<int32_t> cached[kMaxDev];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return kDefaultCUs;
+  int32_t v = cached[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = kDefaultCUs;
+  cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Plan: a pure function of the descriptor and the device's CU count.
 // `span` > 0 bounds the slots any sequence walks (a sliding window with a
 // host-known prefix); the splits then cover [0, span) instead of the capacity.
-gqa_status_t make_plan(const gqa_decode_desc_t* d, Plan* p, int64_t span = 0) {
+// `generic` forces the vector kernel (paged caches whose blocks the
+// matrix-core kernels cannot tile).
+gqa_status_t make_plan(const gqa_decode_desc_t* d, Plan* p, int64_t span = 0, bool generic = false) {
   gqa_status_t st = check_desc(d);
   if (st != GQA_OK) return st;
   std::memset(p, 0, sizeof(*p));
+  const int64_t cus = device_cus();
   const int64_t B = d->batch, Hq = d->num_q_heads, Hkv = d->num_kv_heads, D = d->head_dim;
   const int64_t S = span > 0 ? std::min<int64_t>(span, d->capacity) : d->capacity;
   const int64_t G = Hq / Hkv;
-  p->kernel = choose_kernel(d);
+  p->kernel = generic ? GQA_KERNEL_GENERIC : choose_kernel(d);
   // Query-head chunks per kv-head: 8 heads per workgroup in the generic
   // kernel, 16 (one MFMA tile) in MFMA_QK, all G in MFMA_ALL.
   p->head_chunks = p->kernel == GQA_KERNEL_GENERIC ? (int32_t)((G + kGenericHeadChunk - 1) / kGenericHeadChunk)
@@ -108,7 +127,7 @@ gqa_status_t make_plan(const gqa_decode_desc_t* d, Plan* p, int64_t span = 0) {
     // waves share LDS tiles; more splits would cost partials of G rows of
     // D + 2 floats each), three per CU for the generic kernel.  Splits are
     // equal and at least 256 slots long.
-    const int64_t target = p->kernel == GQA_KERNEL_MFMA_QK ? kNumCUs : p->kernel == GQA_KERNEL_MFMA_ALL ? 512 : 768;
+    const int64_t target = p->kernel == GQA_KERNEL_MFMA_QK ? cus : p->kernel == GQA_KERNEL_MFMA_ALL ? 2 * cus : 3 * cus;
     int64_t ns = std::max<int64_t>(1, (target + units / 2) / units);
     ns = std::min<int64_t>(ns, std::max<int64_t>(1, S / 256));
     split_tokens = (S + ns - 1) / ns;
@@ -148,14 +167,14 @@ gqa_status_t make_plan(const gqa_decode_desc_t* d, Plan* p, int64_t span = 0) {
   const int32_t cost = d->layout == GQA_LAYOUT_BHSD ? (i8 ? kBalancedCostI8 : kBalancedCostBf16)
                                                     : (i8 ? kBalancedCostI8Strided : kBalancedCostBf16Strided);
   int64_t units_max;
-  if (p->kernel == GQA_KERNEL_MFMA_QK && p->head_chunks == 1 && d->num_splits == 0 && B * Hkv > kNumCUs &&
+  if (p->kernel == GQA_KERNEL_MFMA_QK && p->head_chunks == 1 && d->num_splits == 0 && B * Hkv > cus &&
       B <= kMaxBalancedBatch && mul_ok(B * Hkv, S / 16 + 1 + cost, &units_max) && units_max < INT32_MAX) {
-    const size_t rows = (size_t)kNumCUs * 2 * G;
+    const size_t rows = (size_t)cus * 2 * G;
     p->balanced = 1;
     p->bal_cost = cost;
     p->nsplit = 1;
     p->split_tokens = (int32_t)S;
-    p->grid = kNumCUs;
+    p->grid = (int32_t)cus;
     p->combine = 1;
     p->off_m = align256(rows * D * sizeof(float));
     p->off_l = p->off_m + align256(rows * sizeof(float));
@@ -191,8 +210,9 @@ gqa_status_t check_map(const gqa_decode_desc_t* d, const gqa_cache_map_t* m, con
         !mul_ok(t, 4, &t))
       return GQA_ERR_UNSUPPORTED;
     if (!mul_ok(d->batch, m->max_blocks, &t)) return GQA_ERR_UNSUPPORTED;
-    // The matrix-core kernels take one block per 16-slot tile.
-    if (p.kernel != GQA_KERNEL_GENERIC && m->block_size % 16 != 0) return GQA_ERR_UNSUPPORTED;
+    // The matrix-core kernels take one block per 16-slot tile; other block
+    // sizes are planned on the generic kernel (plan_for).
+    if (p.kernel != GQA_KERNEL_GENERIC && m->block_size % 16 != 0) return GQA_ERR_INTERNAL;
   } else {
     if (!mul_ok(m->num_rows, d->num_kv_heads, &t) || !mul_ok(t, d->capacity, &t) || !mul_ok(t, d->head_dim, &t) ||
         !mul_ok(t, 4, &t))
@@ -520,6 +540,19 @@ void fill_softmax(const gqa_decode_desc_t* d, const gqa_softmax_t* v, AttnArgs* 
 
 const gqa_decode_opts_t kNoOpts = {nullptr, nullptr, nullptr, nullptr};
 
+// The plan of an attend/step call with options: the descriptor's, over the
+// window's span when one is known, and on the generic kernel for paged caches
+// whose block size is not a multiple of the matrix-core kernels' 16-slot tile.
+gqa_status_t plan_for(const gqa_decode_desc_t* d, const gqa_decode_opts_t* o, Plan* p) {
+  gqa_status_t st = make_plan(d, p, walk_span(o->softmax));
+  if (st != GQA_OK) return st;
+  const gqa_cache_map_t* m = o->map;
+  if (m != nullptr && m->kind == GQA_MAP_PAGED && m->block_size > 0 && m->block_size % 16 != 0 &&
+      p->kernel != GQA_KERNEL_GENERIC)
+    st = make_plan(d, p, walk_span(o->softmax), true);
+  return st;
+}
+
 // Bytes of the rotated q a rotary step keeps after the plan's workspace.
 size_t rope_q_offset(const Plan& p) { return align256(p.workspace_bytes); }
 // MFMA_ALL rotates q and the new key itself on bf16 caches; the other paths
@@ -597,7 +630,7 @@ gqa_status_t do_attend(const gqa_decode_desc_t* desc, const gqa_decode_opts_t* o
                        void* workspace, size_t workspace_bytes, void* stream, bool step) {
   const gqa_decode_opts_t* o = opts ? opts : &kNoOpts;
   Plan p;
-  gqa_status_t st = make_plan(desc, &p, walk_span(o->softmax));
+  gqa_status_t st = plan_for(desc, o, &p);
   if (st != GQA_OK) return st;
   const gqa_cache_map_t* map = o->map;
   const gqa_kv_scales_t* sc = o->scales;
@@ -840,11 +873,35 @@ gqa_status_t gqa_decode_workspace_size_ex(const gqa_decode_desc_t* desc, const g
     if (bytes == nullptr) return GQA_ERR_INVALID_ARGUMENT;
     const gqa_decode_opts_t* o = opts ? opts : &kNoOpts;
     Plan p;
-    gqa_status_t st = make_plan(desc, &p, walk_span(o->softmax));
+    gqa_status_t st = plan_for(desc, o, &p);
     if (st != GQA_OK) return st;
     if ((st = check_rope(desc, o->rope)) != GQA_OK) return st;
     if ((st = check_softmax(desc, o->softmax)) != GQA_OK) return st;
     *bytes = workspace_total(desc, p, o);
+    return GQA_OK;
+  } catch (...) {
+    return GQA_ERR_INTERNAL;
+  }
+}
+
+gqa_status_t gqa_decode_get_plan_ex(const gqa_decode_desc_t* desc, const gqa_decode_opts_t* opts,
+                                    gqa_decode_plan_t* plan) {
+  try {
+    if (plan == nullptr) return GQA_ERR_INVALID_ARGUMENT;
+    const gqa_decode_opts_t* o = opts ? opts : &kNoOpts;
+    Plan p;
+    gqa_status_t st = plan_for(desc, o, &p);
+    if (st != GQA_OK) return st;
+    if ((st = check_rope(desc, o->rope)) != GQA_OK) return st;
+    if ((st = check_softmax(desc, o->softmax)) != GQA_OK) return st;
+    plan->kernel = p.kernel;
+    plan->num_splits = p.nsplit;
+    plan->split_tokens = p.split_tokens;
+    plan->grid = p.grid;
+    plan->block = p.block;
+    plan->combine = p.combine;
+    plan->workspace_bytes = workspace_total(desc, p, o);
+    plan->balanced = p.balanced;
     return GQA_OK;
   } catch (...) {
     return GQA_ERR_INTERNAL;

@@ -90,7 +90,7 @@ extern const bool kHaveMfmaQk;
 extern const bool kHaveMfmaAll;
 extern const bool kHaveMfmaQkI8;  // int8 caches on the G <= 16 matrix-core kernel
 
-constexpr int kNumCUs = 256;          // MI355X: 8 XCDs x 32 CUs
+constexpr int kDefaultCUs = 256;      // MI355X: 8 XCDs x 32 CUs (the plan's CU count when no device is visible)
 constexpr int kMaxSplits = 64;        // one lane per split in the combine pass
 constexpr int kGenericHeadChunk = 8;  // query heads per workgroup in the generic kernel
 constexpr int kMaxBalancedBatch = 4096;  // most sequences in the balanced mode (16 per thread of its scan)

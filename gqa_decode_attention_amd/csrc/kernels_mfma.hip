@@ -61,13 +61,15 @@ __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cas
 //   V sum   O(16 heads x 128) += P(16 x 32 slots) . V(32 x 128) as eight MFMAs
 //           (one per 16-column block).  The A operand is the weights lane (r, c)
 //           already holds (head c; slots 4r..4r+3 of the first half then of the
-//           second half, rounded to bf16); the B operand -- V transposed, 8 slots
+//           second half); the B operand -- V transposed, 8 slots
 //           of one column per lane -- comes from two ds_read_b64_tr_b16 per
 //           block: within each 16-lane group, lane rho names the 4 elements at
 //           slot 4r + rho/4, columns 16nb + 4(rho mod 4) .. +3, and lane c
-//           receives column 16nb + c of the 4 slots.
-// The weights enter the V-sum MFMA rounded to bf16 (their sum l stays float32);
-// the accumulation is float32.
+//           receives column 16nb + c of the 4 slots.  Each weight is split
+//           into bf16 hi and lo parts with one MFMA each (sixteen per tile).
+// Scores are exact products summed in float32; the weights reach the V sum
+// with about 16 significant bits (hi + lo) and everything accumulates in
+// float32.
 // ---------------------------------------------------------------------------
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -462,8 +464,15 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
         p[4 + i] *= svs[buf][16 + 4 * r + i];
       }
     }
+    // Each weight enters the V sum as bf16 hi = bf16(p) plus lo = bf16(p - hi)
+    // (about 16 significant bits, so the weighted sum keeps float32 accuracy):
+    // one MFMA per part, accumulating into the same float32 output.
     const u32x4 pa = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                       pack_bf16x2(p[6], p[7])};
+    const u32x4 pl = {pack_bf16x2(p[0] - bf16_lo(pa[0]), p[1] - bf16_hi(pa[0])),
+                      pack_bf16x2(p[2] - bf16_lo(pa[1]), p[3] - bf16_hi(pa[1])),
+                      pack_bf16x2(p[4] - bf16_lo(pa[2]), p[5] - bf16_hi(pa[2])),
+                      pack_bf16x2(p[6] - bf16_lo(pa[3]), p[7] - bf16_hi(pa[3]))};
     const int trow = 4 * r + (c >> 2);
     const int tcol = 4 * (c & 3);
 #pragma unroll
@@ -474,7 +483,7 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
                         (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
                         (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
                         (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
-      O[nb] = mfma_16x16x32(pa, vt, O[nb]);
+      O[nb] = mfma_16x16x32(pl, vt, mfma_16x16x32(pa, vt, O[nb]));
     }
   };
   // Two register sets keep two tiles in flight: at the top of each iteration

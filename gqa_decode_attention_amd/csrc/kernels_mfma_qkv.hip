@@ -22,15 +22,18 @@
 //   softmax per head c, as in the other kernels (lazy rescale, exp2 with the
 //           scale folded in).
 //   V sum   O^T(128 x 16 heads) += V^T(128 x 16 slots) . P'(16 slots x 16
-//           heads) as eight v_mfma_f32_16x16x16_bf16, e = 0..7.  Lane (r, c)
+//           heads) as eight v_mfma_f32_16x16x32_bf16, e = 0..7.  Lane (r, c)
 //           loads slots 4r + i (i = 0..3) at elements 8c .. 8c + 7; the A
-//           operand of MFMA e is element 8c + e of its four slots (so MFMA e
-//           covers head-width positions e, 8 + e, ..., 120 + e), and the B
-//           operand is the lane's own four weights of head c, times the value
-//           scales of int8 rows, rounded to bf16.  Lane (r, c) receives head c
-//           at positions 8(4r + i) + e: complete sums, no cross-lane reduction.
-// Scores are exact products (bf16 or small integers) summed in float32; the
-// weights enter the V sum rounded to bf16 (their sum l stays float32).
+//           operand of MFMA e is element 8c + e of its four slots, twice (so
+//           MFMA e covers head-width positions e, 8 + e, ..., 120 + e), and
+//           the B operand is the lane's own four weights of head c (times the
+//           value scales of int8 rows) split into bf16 hi and lo parts, the
+//           K axis holding each slot once with each part.  Lane (r, c)
+//           receives head c at positions 8(4r + i) + e: complete sums, no
+//           cross-lane reduction.
+// Scores are exact products (bf16 or small integers) summed in float32; each
+// weight reaches the V sum as hi + lo (about 16 significant bits) and the
+// products accumulate in float32, as does the denominator l.
 //
 // Fused step: the new token (slot lengths[b]) is not read from the cache; the
 // last wave of the workgroup whose split holds it runs one extra tile whose
@@ -56,7 +59,6 @@ namespace gqa {
 namespace qkv {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInfQ = -__builtin_inff();
@@ -74,10 +76,6 @@ __device__ __forceinline__ void unroll(F&& f) {
 __device__ __forceinline__ f32x4 mfma_k32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
                                                  0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma_k16(u32x2_t a, u32x2_t b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a), __builtin_bit_cast(s16x4_t, b), c,
-                                                   0, 0, 0);
 }
 
 // Two floats to a bf16 pair (low half = lo), round to nearest even.
@@ -203,8 +201,15 @@ __device__ __forceinline__ void tile_math(State& st, const u32x4 (&qf)[4], const
     p[2] *= quad_bcast<2>(t.vs);
     p[3] *= quad_bcast<3>(t.vs);
   }
-  const u32x2_t pb = {pk_bf16(p[0], p[1]), pk_bf16(p[2], p[3])};
-  // V sum: A operand of MFMA e = element 8c + e of slots 4r .. 4r + 3.
+  // Each weight enters the V sum as a pair of bf16 values hi = bf16(p) and
+  // lo = bf16(p - hi), so it is carried to about 2^-17 of its value (float32
+  // arithmetic within the tolerance of a float32 sum).  The pair is stacked
+  // along the K axis of one 16x16x32 MFMA: k = 8r + i is slot 4r + i times
+  // its hi part, k = 8r + 4 + i the same slot times its lo part.
+  const uint32_t h01 = pk_bf16(p[0], p[1]), h23 = pk_bf16(p[2], p[3]);
+  const u32x4 pb = {h01, h23, pk_bf16(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01)),
+                    pk_bf16(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23))};
+  // V sum: A operand of MFMA e = element 8c + e of slots 4r .. 4r + 3 (twice).
   unroll<0, 8>([&](auto ei) {
     constexpr int e = decltype(ei)::value;
     u32x2_t va;
@@ -217,7 +222,7 @@ __device__ __forceinline__ void tile_math(State& st, const u32x4 (&qf)[4], const
       va = u32x2_t{pk_bf16(sbyte<by>(t.v[0][wd]), sbyte<by>(t.v[1][wd])),
                    pk_bf16(sbyte<by>(t.v[2][wd]), sbyte<by>(t.v[3][wd]))};
     }
-    st.acc[e] = mfma_k16(va, pb, st.acc[e]);
+    st.acc[e] = mfma_k32(u32x4{va[0], va[1], va[0], va[1]}, pb, st.acc[e]);
   });
 }
 
@@ -636,7 +641,8 @@ hipError_t launch_attend_mfma_qk(const AttnArgs& a, const Plan& p, hipStream_t s
   // and, with the kernel's 33 KB static arrays, exceeds half of a CU's 160 KB.
   unsigned lds = 0;
   if (a.bal_pre != nullptr) {
-    if (a.B > kMaxBalancedBatch || a.head_chunks != 1 || p.grid != kNumCUs) return hipErrorInvalidValue;
+    if (a.B > kMaxBalancedBatch || a.head_chunks != 1 || p.grid < 1 || p.grid != a.bal_units)
+      return hipErrorInvalidValue;
     lds = std::max<unsigned>(kOneWorkgroupLds, (unsigned)(a.B + 1) * 4u);
   }
   return hipLaunchKernel(fn, dim3(p.grid), dim3(p.block), params, lds, s);

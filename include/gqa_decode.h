@@ -24,7 +24,7 @@
  *   - CLIKA runtime, "groupQueryAttention" API page: the decode perf path
  *     appends the new K/V in place into the bound cache; a read-only attend is
  *     a separate call; malformed arguments are refused with INVALID_ARGUMENT
- *     after validating the whole input before any read.
+ *     once every argument has been checked, before any data is read.
  *   - Huawei CANN, "aclnnMlaPrologV3WeightNz" operator page: two-phase call
  *     convention (a size/validation phase, then execution), status-code
  *     returns, empty batch allowed with caches left untouched.
@@ -157,6 +157,19 @@ gqa_status_t gqa_decode_append(const gqa_decode_desc_t* desc, void* k_cache, voi
  *              its contents on entry do not matter, it needs no clearing and it may be
  *              reused by later calls with any descriptor.  Calls that run concurrently
  *              must not share one workspace.
+ *              Split plans (num_splits > 1, not balanced) leave, for every (b, hq)
+ *              whose valid slots reach more than one split, the partial of each split
+ *              s holding valid slots ([s * split_tokens, min((s + 1) * split_tokens,
+ *              n)), n = attended slots): with i = (b * Hq + hq) * num_splits + s,
+ *              o = float32 [D] at byte offset 4 * i * D (the unnormalised weighted
+ *              sum), m = float32 at byte offset off_m + 4 * i (the reference maximum
+ *              in log2 units) and l = float32 at off_l + 4 * i (the denominator),
+ *              with off_m = align256(4 * B * Hq * num_splits * D) and off_l = off_m +
+ *              align256(4 * B * Hq * num_splits), align256(x) = x rounded up to a
+ *              multiple of 256.  o / l is the softmax-weighted mean of V over the
+ *              split's slots, in float32 before the output's rounding; the layout
+ *              is exposed so tests can check that arithmetic, not as a data
+ *              interface.
  * Pointers must be non-null and aligned to the element size; when the plan's
  * kernel is a matrix-core one (bf16 storage, head_dim 128, G <= 64), q, out and
  * the caches must be 16-byte aligned (GQA_ERR_INVALID_ARGUMENT otherwise). */
@@ -197,14 +210,17 @@ gqa_status_t gqa_decode_step(const gqa_decode_desc_t* desc, const void* q, void*
  *                  be -1 (the device lengths are not checked, as above).
  *
  * The table is passed twice with the same entries: `map` in device memory for
- * the kernels and `map_host` in host memory, which is validated whole before
- * anything is enqueued (an out-of-range or repeated entry refuses
+ * the kernels and `map_host` in host memory, every entry of which is checked
+ * before anything is enqueued (an out-of-range or repeated entry refuses
  * GQA_ERR_INVALID_ARGUMENT).  The device copy is trusted to match; entries it
  * holds out of range are clamped (reads) or skip the write (append), so a
  * mismatch cannot fault.  Rows of a paged table may share blocks for reading;
  * a step or append into a block shared by two rows races.
- * Matrix-core kernels serve paged caches whose block_size is a multiple of 16;
- * other block sizes run on the generic kernel.
+ * Matrix-core kernels serve paged caches whose block_size is a multiple of 16
+ * (their 16-slot tiles then never straddle a block); calls with another block
+ * size are planned on the generic kernel, whose plan (and workspace) can
+ * differ from the descriptor's: size the workspace of a mapped call with
+ * gqa_decode_workspace_size_ex (or read gqa_decode_get_plan_ex) with the map.
  * ------------------------------------------------------------------------- */
 enum { GQA_MAP_SLOTS = 1, GQA_MAP_PAGED = 2 };
 typedef struct {
@@ -219,7 +235,9 @@ typedef struct {
 /* As gqa_decode_append / _attend / _step, with caches addressed through `map`.
  * The descriptor's batch, heads, head_dim, capacity, layout and dtypes keep
  * their meaning (capacity = slots per sequence); the workspace size and plan
- * are those of the descriptor.  B == 0 validates and enqueues nothing. */
+ * are gqa_decode_workspace_size_ex / gqa_decode_get_plan_ex with the map (the
+ * descriptor's own, unless the block size sends the call to the generic
+ * kernel).  B == 0 validates and enqueues nothing. */
 gqa_status_t gqa_decode_append_mapped(const gqa_decode_desc_t* desc, const gqa_cache_map_t* map, void* k_cache,
                                       void* v_cache, const void* k_new, const void* v_new,
                                       const int32_t* lengths, void* stream);
@@ -356,6 +374,11 @@ typedef struct {
  * rotated q when opts->rope is set).  opts may be NULL. */
 gqa_status_t gqa_decode_workspace_size_ex(const gqa_decode_desc_t* desc, const gqa_decode_opts_t* opts,
                                           size_t* bytes);
+/* The execution plan of an attend/step call with these options (the window's
+ * span, the generic kernel for paged blocks the matrix-core kernels cannot
+ * tile); workspace_bytes as gqa_decode_workspace_size_ex.  opts may be NULL. */
+gqa_status_t gqa_decode_get_plan_ex(const gqa_decode_desc_t* desc, const gqa_decode_opts_t* opts,
+                                    gqa_decode_plan_t* plan);
 /* The append, attend and step calls with options; arguments, contracts and
  * errors as in the plain calls and the sections above.  opts may be NULL. */
 gqa_status_t gqa_decode_append_ex(const gqa_decode_desc_t* desc, const gqa_decode_opts_t* opts, void* k_cache,

@@ -12,8 +12,8 @@ parameter notes on ``slot_ids`` and on the paged block table):
   ``[0, R)`` and no two batch rows share one.
 * Paged cache.  A block table of shape ``(B, max_blocks)`` maps the tokens of
   batch row ``b`` to blocks of a pool: token ``j`` is slot ``j % bs`` of block
-  ``table[b, j // bs]``.  The table is validated whole before any read: every
-  entry is ``-1`` (the pad of the unused tail) or a block index in
+  ``table[b, j // bs]``.  Every entry of the table is checked before the
+  caches are touched: ``-1`` (the pad of the unused tail) or a block index in
   ``[0, num_blocks)``, and no block appears twice in one row.
 
 Everything else is the decode step of ``oracle.oracle`` (append at slot

@@ -27,7 +27,8 @@ What it computes, and where each piece is defined:
 
 * Step (``step``): append, then attend over ``lengths[b] + 1`` slots, i.e.
   over every cached position plus the new token (KV-cache decode step page,
-  "softmax is over all cache positions, including the new token").
+  problem statement: the new token's own position takes part in the
+  softmax).
 
 The attention here is the plain definition written out -- no tiling, no online
 softmax, no split of the token axis.  The maximum score is subtracted before

@@ -21,15 +21,16 @@ from gqa_decode_attention_amd import _lib
 pytestmark = pytest.mark.skipif(torch.cuda.device_count() > 0,
                                 reason="fake-pointer ABI tests run only where no GPU is visible")
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "gqa_decode.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+HEADER = os.path.join(INCLUDE, "gqa_decode.h")
 OK, INVALID, UNSUPPORTED, WS_SMALL = 0, 1, 2, 3
 
 FAKE = 1 << 40          # 256-byte aligned fake device address: never dereferenced on error paths
 GAP = 1 << 34           # spacing that keeps fake buffers disjoint
 
 
-def header_functions():
-    text = open(HEADER).read()
+def header_functions(path=HEADER):
+    text = open(path).read()
     return sorted(set(re.findall(r"^\s*(?:gqa_status_t|const char\*|int32_t)\s+(gqa_decode_\w+)\s*\(", text, re.M)))
 
 
@@ -37,9 +38,11 @@ def test_library_exports_every_declared_function():
     L = g.lib()
     names = header_functions()
     assert len(names) >= 7
-    for n in names:
-        assert hasattr(L, n), n
     assert set(names) == set(_lib.EXPORTS)
+    headers = sorted(f for f in os.listdir(INCLUDE) if f.endswith(".h"))
+    for h in headers:
+        for n in header_functions(os.path.join(INCLUDE, h)):
+            assert hasattr(L, n), (h, n)
 
 
 def test_status_strings_and_version():
@@ -363,18 +366,27 @@ def test_missing_or_misaligned_map_refused():
                                       1 << 30, None) == INVALID
 
 
-def test_matrix_core_paged_needs_block_multiple_of_16():
-    """bf16, D = 128, G = 4 is a matrix-core descriptor: a block size of 8 is
-    refused by attend and step (the append, which takes any block size, is not
-    called: this table is valid and it would launch)."""
-    L = g.lib()
-    m, keep = _map("paged", 1024, [list(range(0, 512)), list(range(512, 1024))], block_size=8, max_blocks=512)
+def test_paged_blocks_not_multiple_of_16_plan_the_generic_kernel():
+    """bf16, D = 128, G = 4 is a matrix-core descriptor: paged caches with a
+    block size that is a multiple of 16 keep the matrix-core plan, any other
+    block size is planned on the generic kernel, and the workspace the call
+    needs is that plan's."""
     d = desc()
-    p = _attend_ptrs()
-    assert L.gqa_decode_attend_mapped(ctypes.byref(d), ctypes.byref(m), p["q"], p["kc"], p["vc"], p["lens"], p["out"],
-                                      p["ws"], 1 << 30, None) == UNSUPPORTED
-    assert L.gqa_decode_step_mapped(ctypes.byref(d), ctypes.byref(m), p["q"], p["kc"], p["vc"], p["kn"], p["vn"],
-                                    p["lens"], p["out"], p["ws"], 1 << 30, None) == UNSUPPORTED
+    assert g.get_plan(d)["kernel"] == "mfma_qk"
+    for bs, kernel in ((16, "mfma_qk"), (48, "mfma_qk"), (8, "generic"), (7, "generic"), (24, "generic")):
+        mb = -(-4096 // bs)
+        dd = desc(capacity=mb * bs)
+        m, keep = _map("paged", 2 * mb, [list(range(0, mb)), list(range(mb, 2 * mb))], block_size=bs, max_blocks=mb)
+        opts = _lib.OptsT(ctypes.pointer(m), None, None, None)
+        plan = g.get_plan_ex(dd, opts)
+        assert plan["kernel"] == kernel, (bs, plan)
+        assert g.workspace_size_ex(dd, opts) == plan["workspace_bytes"]
+        if kernel == "mfma_qk":
+            assert plan == g.get_plan(dd)
+    # int8 caches and large groups fall back the same way
+    for kw in (dict(kv_dtype=g.I8), dict(num_q_heads=64, num_kv_heads=1)):
+        m, keep = _map("paged", 1024, [list(range(0, 512)), list(range(512, 1024))], block_size=8, max_blocks=512)
+        assert g.get_plan_ex(desc(**kw), _lib.OptsT(ctypes.pointer(m), None, None, None))["kernel"] == "generic"
 
 
 def test_map_overlapping_output_or_caches_refused():

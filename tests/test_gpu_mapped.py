@@ -58,6 +58,9 @@ CASES = [
     (3, 8, 2, 64, 300, "BHSD", "f32", "f32", "paged", 7, 0),           # generic kernel, odd block size
     (2, 6, 3, 24, 200, "BSHD", "f32", "bf16", "paged", 1, 2),          # generic, one slot per block
     (2, 8, 2, 128, 333, "BHSD", "bf16", "f32", "paged", 8, 0),         # generic (f32 output), block 8
+    (3, 32, 8, 128, 1500, "BHSD", "bf16", "bf16", "paged", 7, 0),      # matrix-core descriptor, block 7: generic
+    (2, 16, 2, 128, 700, "BSHD", "bf16", "bf16", "paged", 24, 3),      # G=8, block 24: generic
+    (2, 64, 1, 128, 900, "BHSD", "bf16", "bf16", "paged", 24, 0),      # G=64, block 24: generic
     (3, 32, 8, 128, 1500, "BHSD", "bf16", "bf16", "slots", None, 0),
     (2, 64, 1, 128, 900, "BSHD", "bf16", "bf16", "slots", None, 2),
     (3, 8, 2, 64, 300, "BHSD", "f32", "f32", "slots", None, 0),

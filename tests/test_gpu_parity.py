@@ -368,56 +368,14 @@ def test_graph_capture_replays(g, B):
 
 
 # ---------------------------------------------------------------------------
-# Full-size workloads in the launch configuration the benchmark times:
-# sampled (b, query head) outputs against the oracle computed one by one,
-# and the append checked on every byte of the caches.
+# Full-size workloads in the launch configuration the benchmark times: every
+# (b, query head, d) output against the oracle, and every byte of both caches
+# against the oracle's append.
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("name", ["llama3_8b_layer", "ragged_batch", "long_context", "large_group"])
 def test_full_size_workload(g, name):
     w = W.WORKLOADS[name]
-    inp = W.make_inputs(w, DEV)
-    L = inp["lengths"].cpu().numpy()
-    desc = g.desc_for(inp["q"], inp["k_cache"], w.layout)
-    say(f"full size {name}: plan {g.get_plan(desc)}")
-    k_before, v_before = inp["k_cache"].clone(), inp["v_cache"].clone()
-    out = run_step(g, inp, w)
-    torch.cuda.synchronize()
-    # append: slot L[b] of every kv-head holds the new bits; nothing else changed
-    bidx = torch.arange(w.B, device=DEV)
-    Ld = inp["lengths"].long()
-    for before, after, new in ((k_before, inp["k_cache"], inp["k_new"]), (v_before, inp["v_cache"], inp["v_new"])):
-        if w.layout == "BHSD":
-            assert torch.equal(after[bidx, :, Ld].view(torch.int16), new.view(torch.int16))
-            after[bidx, :, Ld] = before[bidx, :, Ld]
-        else:
-            assert torch.equal(after[bidx, Ld].view(torch.int16), new.view(torch.int16))
-            after[bidx, Ld] = before[bidx, Ld]
-        assert torch.equal(after.view(torch.int16), before.view(torch.int16))
-    del k_before, v_before
-    # put the new bits back for the oracle's reads
-    if w.layout == "BHSD":
-        inp["k_cache"][bidx, :, Ld] = inp["k_new"]
-        inp["v_cache"][bidx, :, Ld] = inp["v_new"]
-    else:
-        inp["k_cache"][bidx, Ld] = inp["k_new"]
-        inp["v_cache"][bidx, Ld] = inp["v_new"]
-    rng = np.random.default_rng(w.seed)
-    G = w.Hq // w.Hkv
-    samples = {(0, 0), (w.B - 1, w.Hq - 1)} | {(int(rng.integers(w.B)), int(rng.integers(w.Hq))) for _ in range(10)}
-    q_np = np_of(inp["q"])
-    got = out.float().cpu().double().numpy()
-    for b, hq in sorted(samples):
-        h = hq // G
-        n = int(L[b]) + 1
-        if w.layout == "BHSD":
-            Kt, Vt = inp["k_cache"][b, h, :n], inp["v_cache"][b, h, :n]
-        else:
-            Kt, Vt = inp["k_cache"][b, :n, h], inp["v_cache"][b, :n, h]
-        K = oracle.decode(np_of(Kt), w.kv_dtype)
-        V = oracle.decode(np_of(Vt), w.kv_dtype)
-        ref = oracle.attend_one(oracle.decode(q_np[b, hq], w.qo_dtype), K, V)
-        tol = TOL[w.qo_dtype]
-        assert np.all(np.abs(got[b, hq] - ref) <= tol + tol * np.abs(ref)), (b, hq, np.abs(got[b, hq] - ref).max())
+    inp, out = check_step_full(g, w)
     assert torch.isfinite(out.float()).all()
 
 
