@@ -68,9 +68,11 @@ int32_t choose_kernel(const gqa_decode_desc_t* d) {
   if (d->kv_dtype == GQA_I8) {
     // G <= 16 on the G <= 16 kernel (which quantizes a step's new rows itself),
     // 16 < G <= 64 on the large-group kernel (codes widened into its LDS tiles).
+    // Int8 caches, G <= 64: the G <= 16 kernel (17..64 heads as 32-head chunks
+    // of 8 waves, K/V codes read once per chunk and widened in registers;
+    // measured faster than the large-group kernel's widened LDS tiles).
     if (d->qo_dtype != GQA_BF16 || d->head_dim != 128) return GQA_KERNEL_GENERIC;
-    if (G <= 16 && kHaveMfmaQkI8) return GQA_KERNEL_MFMA_QK;
-    if (G <= 64 && kHaveMfmaAll) return GQA_KERNEL_MFMA_ALL;
+    if (G <= 64 && kHaveMfmaQkI8) return GQA_KERNEL_MFMA_QK;
     return GQA_KERNEL_GENERIC;
   }
   if (bf16 && d->head_dim == 128 && G <= 16 && kHaveMfmaQk) return GQA_KERNEL_MFMA_QK;
@@ -109,13 +111,16 @@ gqa_status_t make_plan(const gqa_decode_desc_t* d, Plan* p, int64_t span = 0, bo
   p->kernel = generic ? GQA_KERNEL_GENERIC : choose_kernel(d);
   // Query-head chunks per kv-head: 8 heads per workgroup in the generic
   // kernel, 16 (one MFMA tile) in MFMA_QK, all G in MFMA_ALL.
+  // MFMA_QK takes 16 heads per workgroup (4 waves) for G <= 16, 32 (8 waves
+  // of two 16-head blocks) above.
+  const int64_t qk_heads = G > 16 ? 32 : 16;
   p->head_chunks = p->kernel == GQA_KERNEL_GENERIC ? (int32_t)((G + kGenericHeadChunk - 1) / kGenericHeadChunk)
-                   : p->kernel == GQA_KERNEL_MFMA_QK ? (int32_t)((G + 15) / 16)
+                   : p->kernel == GQA_KERNEL_MFMA_QK ? (int32_t)((G + qk_heads - 1) / qk_heads)
                                                      : 1;
   // Four waves per workgroup for every kernel.  (For MFMA_QK, measured on
   // MI355X: one 4-wave workgroup per CU streams faster than 8- or 12-wave
   // workgroups or more, shorter splits -- fewer concurrent streams suit HBM.)
-  p->block = 256;
+  p->block = p->kernel == GQA_KERNEL_MFMA_QK && G > 16 ? 512 : 256;
   const int64_t units = std::max<int64_t>(1, B * Hkv * p->head_chunks);
   int64_t split_tokens;
   if (d->num_splits > 0) {
@@ -167,7 +172,7 @@ gqa_status_t make_plan(const gqa_decode_desc_t* d, Plan* p, int64_t span = 0, bo
   const int32_t cost = d->layout == GQA_LAYOUT_BHSD ? (i8 ? kBalancedCostI8 : kBalancedCostBf16)
                                                     : (i8 ? kBalancedCostI8Strided : kBalancedCostBf16Strided);
   int64_t units_max;
-  if (p->kernel == GQA_KERNEL_MFMA_QK && p->head_chunks == 1 && d->num_splits == 0 && B * Hkv > cus &&
+  if (p->kernel == GQA_KERNEL_MFMA_QK && G <= 16 && d->num_splits == 0 && B * Hkv > cus &&
       B <= kMaxBalancedBatch && mul_ok(B * Hkv, S / 16 + 1 + cost, &units_max) && units_max < INT32_MAX) {
     const size_t rows = (size_t)cus * 2 * G;
     p->balanced = 1;

@@ -1,6 +1,6 @@
 // Matrix-core (MFMA) attention kernel of the GQA decode step for gfx950 for
-// large groups (16 < G <= 64), bf16 or int8 storage, head width 128.  (Groups
-// of up to 16 query heads run the kernel in kernels_mfma_qkv.hip.)
+// large groups (16 < G <= 64), bf16 storage, head width 128.  (Groups of up to
+// 16 query heads, and int8 caches, run the kernel in kernels_mfma_qkv.hip.)
 //
 // What is computed is the JAX "Grouped-Query Decode Step" page's definition
 // (query head h reads cache head floor(h/G); s_j = q.K_j/sqrt(D) over the
@@ -91,25 +91,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 
-// Int8 caches (KV = GQA_I8, dense).  Rows are 128 codes with a float32
-// scale each (Huawei CANN "aclnnMlaPrologV3WeightNz" page, dynamic
-// quantization: a cached value reads as code * row scale).  Thread t loads 16
-// codes (bytes 16 (t & 7) ..) of row t >> 3 of the K and V tiles with the
-// rows' scales; the codes are widened exactly to bf16 (|code| <= 127) as they
-// are written to LDS, so the tile math is that of bf16 caches, with each
-// slot's score times its key scale and its weight times its value scale in
-// the V sum (the denominator sums the unscaled weights).  In a step the
-// workgroup whose split holds slot L quantizes the new rows itself (per-row
-// rule: float32 row maximum, scale = max / 127, codes = round-half-even(x /
-// scale) with correctly rounded divisions, clamped to +-127; a zero row has
-// scale 0 and codes 0), attends them in that form and stores codes and scales.
-template <int KV, bool PAGED, bool VAR>
+template <bool PAGED, bool VAR>
 __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
-  static_assert(!(PAGED && KV == GQA_I8), "int8 caches are dense");
-  constexpr bool Q8 = KV == GQA_I8;
   __shared__ __attribute__((aligned(16))) uint16_t sk[2][kTileT * kPitch];
   __shared__ __attribute__((aligned(16))) uint16_t sv[2][kTileT * kPitch];
-  __shared__ float sks[2][kTileT], svs[2][kTileT];  // int8: the tile rows' scales
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -172,8 +157,6 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
   const int64_t base = PAGED ? 0 : row_head_offset(a, b, h);  // dense or slot-indexed row
   const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.k_cache) + base;
   const uint16_t* vb = reinterpret_cast<const uint16_t*>(a.v_cache) + base;
-  const int8_t* kb8 = reinterpret_cast<const int8_t*>(a.k_cache) + base;  // int8 caches
-  const int8_t* vb8 = reinterpret_cast<const int8_t*>(a.v_cache) + base;
   const int64_t rs = a.st;
   const int64_t nrow = ((int64_t)b * a.Hkv + h) * kD;
   // Tile grid origin: the split start, or for a paged cache (block size a
@@ -196,50 +179,9 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
   const int piece = tid & 15;
   struct Regs {
     u32x4 k[2], v[2];
-    float ks, vs;  // int8: the scales of row t >> 3 (codes in k[0], v[0])
   };
-  u32x4 kn = {0u, 0u, 0u, 0u}, vn = {0u, 0u, 0u, 0u};  // int8: the codes of elements 16 (t & 7) ..
-  float ksn = 0.f, vsn = 0.f;                          // int8: the new rows' scales
-  if (Q8 && own_new) {
-    // Thread t quantizes elements 16 (t & 7) .. + 15 of the new rows; the row
-    // maxima reduce over the 8 threads that hold a row.
-    const uint16_t* knp = reinterpret_cast<const uint16_t*>(a.k_new) + nrow + 16 * (tid & 7);
-    const uint16_t* vnp = reinterpret_cast<const uint16_t*>(a.v_new) + nrow + 16 * (tid & 7);
-    float kx[16], vx[16];
-    widen16<GQA_BF16>(load16(knp), kx);
-    widen16<GQA_BF16>(load16(knp + 8), kx + 8);
-    widen16<GQA_BF16>(load16(vnp), vx);
-    widen16<GQA_BF16>(load16(vnp + 8), vx + 8);
-    float km = 0.f, vm = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      km = fmaxf(km, fabsf(kx[e]));
-      vm = fmaxf(vm, fabsf(vx[e]));
-    }
-#pragma unroll
-    for (int off = 1; off < 8; off <<= 1) {
-      km = fmaxf(km, __shfl_xor(km, off));
-      vm = fmaxf(vm, __shfl_xor(vm, off));
-    }
-    ksn = km / 127.0f;
-    vsn = vm / 127.0f;
-    auto code = [](float x, float amax, float sc) -> uint32_t {
-      const float q = amax > 0.f ? fminf(fmaxf(rintf(x / sc), -127.f), 127.f) : 0.f;
-      return (uint32_t)(int32_t)q & 0xffu;
-    };
-#pragma unroll
-    for (int wd = 0; wd < 4; ++wd) {
-      uint32_t kw = 0, vw = 0;
-#pragma unroll
-      for (int by = 0; by < 4; ++by) {
-        kw |= code(kx[4 * wd + by], km, ksn) << (8 * by);
-        vw |= code(vx[4 * wd + by], vm, vsn) << (8 * by);
-      }
-      kn[wd] = kw;
-      vn[wd] = vw;
-    }
-  }
-  if (!Q8 && own_new) {
+  u32x4 kn = {0u, 0u, 0u, 0u}, vn = {0u, 0u, 0u, 0u};  // the new key / value, piece `piece`
+  if (own_new) {
     kn = load16(reinterpret_cast<const uint16_t*>(a.k_new) + nrow + 8 * piece);
     vn = load16(reinterpret_cast<const uint16_t*>(a.v_new) + nrow + 8 * piece);
     if (rope) {
@@ -289,16 +231,6 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
     return en;
   };
   auto gload = [&](int t0, Regs& R, const Ent& en) {
-    if constexpr (Q8) {
-      const int rc = max(min(t0 + (tid >> 3), t_end - 1), t_begin);
-      const int64_t off = (int64_t)phys(rc) * rs;
-      R.k[0] = load_nt16(kb8 + off + 16 * (tid & 7));
-      R.v[0] = load_nt16(vb8 + off + 16 * (tid & 7));
-      const int64_t si = (base + off) / kD;  // dense rows: element offsets are multiples of D
-      R.ks = __uint_as_float(load_nt4(a.k_scale + si));
-      R.vs = __uint_as_float(load_nt4(a.v_scale + si));
-      return;
-    }
     if constexpr (!PAGED) {
       // Dense or slot-indexed rows (tiles start at t_begin, so only the end
       // clamps): one 32x32->64-bit multiply-add per row address (slot strides
@@ -327,46 +259,6 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
     }
   };
   auto swrite = [&](int t0, int buf, const Regs& R) {
-    if constexpr (Q8) {
-      const int row = tid >> 3;
-      const int col = 16 * (tid & 7);
-      float x[16];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {  // K then V
-        widen16<GQA_I8>(hh ? R.v[0] : R.k[0], x);
-        const u32x4 lo = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
-                          pack_bf16x2(x[6], x[7])};
-        const u32x4 hi = {pack_bf16x2(x[8], x[9]), pack_bf16x2(x[10], x[11]), pack_bf16x2(x[12], x[13]),
-                          pack_bf16x2(x[14], x[15])};
-        uint16_t* dst = (hh ? sv[buf] : sk[buf]) + row * kPitch + col;
-        *reinterpret_cast<u32x4*>(dst) = lo;
-        *reinterpret_cast<u32x4*>(dst + 8) = hi;
-      }
-      if ((tid & 7) == 0) {
-        sks[buf][row] = R.ks;
-        svs[buf][row] = R.vs;
-      }
-      if (own_new && t0 + kTileT > L) {  // uniform: the tile holding the new token; rows >= L take it
-        if (t0 + row >= L) {
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            widen16<GQA_I8>(hh ? vn : kn, x);
-            const u32x4 lo = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
-                              pack_bf16x2(x[6], x[7])};
-            const u32x4 hi = {pack_bf16x2(x[8], x[9]), pack_bf16x2(x[10], x[11]), pack_bf16x2(x[12], x[13]),
-                              pack_bf16x2(x[14], x[15])};
-            uint16_t* dst = (hh ? sv[buf] : sk[buf]) + row * kPitch + col;
-            *reinterpret_cast<u32x4*>(dst) = lo;
-            *reinterpret_cast<u32x4*>(dst + 8) = hi;
-          }
-          if ((tid & 7) == 0) {
-            sks[buf][row] = ksn;
-            svs[buf][row] = vsn;
-          }
-        }
-      }
-      return;
-    }
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2) {
       const int row = prow + 16 * q2;
@@ -401,13 +293,6 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
     // Raw scores; the scale log2(e)/sqrt(D) is positive, so the maximum is
     // taken on raw scores and the scale is folded into the exponent's fma.
     float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-    if constexpr (Q8) {  // code-space scores times the slots' key scales
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sc[i] *= sks[buf][4 * r + i];
-        sc[4 + i] *= sks[buf][16 + 4 * r + i];
-      }
-    }
     if constexpr (VAR) {
       if (a.cap_T > 0.f) {
 #pragma unroll
@@ -457,13 +342,6 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
       ps += p[i];
     }
     l += ps;
-    if constexpr (Q8) {  // the V sum takes the weights times the slots' value scales
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] *= svs[buf][4 * r + i];
-        p[4 + i] *= svs[buf][16 + 4 * r + i];
-      }
-    }
     // Each weight enters the V sum as bf16 hi = bf16(p) plus lo = bf16(p - hi)
     // (about 16 significant bits, so the weighted sum keeps float32 accuracy):
     // one MFMA per part, accumulating into the same float32 output.
@@ -520,22 +398,11 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
     if (ntile & 1) compute_tile(t0, buf);
   }
 
-  if (!Q8 && own_new && prow == 0) {  // the appended slot (skipped if the map names no valid row/block)
+  if (own_new && prow == 0) {  // the appended slot (skipped if the map names no valid row/block)
     const int64_t off = slot_offset_checked(a, b, h, L0);
     if (off >= 0) {
       store16(reinterpret_cast<uint16_t*>(a.k_cache_w) + off + 8 * piece, kn);
       store16(reinterpret_cast<uint16_t*>(a.v_cache_w) + off + 8 * piece, vn);
-    }
-  }
-  if (Q8 && own_new && tid < 8) {  // int8: the appended slot's codes and scales
-    const int64_t off = slot_offset_checked(a, b, h, L0);
-    if (off >= 0) {
-      store16(reinterpret_cast<int8_t*>(a.k_cache_w) + off + 16 * tid, kn);
-      store16(reinterpret_cast<int8_t*>(a.v_cache_w) + off + 16 * tid, vn);
-      if (tid == 0) {
-        a.k_scale_w[off / kD] = ksn;
-        a.v_scale_w[off / kD] = vsn;
-      }
     }
   }
 
@@ -572,22 +439,11 @@ hipError_t launch_attend_mfma_all(const AttnArgs& a, const Plan& p, hipStream_t 
   void* params[] = {&arg};
   const bool var = a.window > 0 || a.cap_T > 0.f;  // in-loop variants (the sink is applied at the end)
   const bool paged = a.map_kind == GQA_MAP_PAGED;
-  const void* fn;
-  if (a.kv_dtype == GQA_I8) {
-    // Int8 caches: dense; a step quantizes its new rows in the kernel (no rotary encoding:
-    // a rotary step appends the rotated, quantized rows first).
-    if (a.map_kind != 0 || a.rope_cos != nullptr || a.k_scale == nullptr || a.v_scale == nullptr ||
-        a.qo_dtype != GQA_BF16 ||
-        (a.k_new != nullptr && (a.k_cache_w == nullptr || a.k_scale_w == nullptr || a.v_scale_w == nullptr)))
-      return hipErrorInvalidValue;
-    fn = var ? reinterpret_cast<const void*>(&attend_mfma_all_kernel<GQA_I8, false, true>)
-             : reinterpret_cast<const void*>(&attend_mfma_all_kernel<GQA_I8, false, false>);
-  } else {
-    fn = paged ? (var ? reinterpret_cast<const void*>(&attend_mfma_all_kernel<GQA_BF16, true, true>)
-                      : reinterpret_cast<const void*>(&attend_mfma_all_kernel<GQA_BF16, true, false>))
-               : (var ? reinterpret_cast<const void*>(&attend_mfma_all_kernel<GQA_BF16, false, true>)
-                      : reinterpret_cast<const void*>(&attend_mfma_all_kernel<GQA_BF16, false, false>));
-  }
+  if (a.kv_dtype != GQA_BF16 || a.qo_dtype != GQA_BF16) return hipErrorInvalidValue;
+  const void* fn = paged ? (var ? reinterpret_cast<const void*>(&attend_mfma_all_kernel<true, true>)
+                                : reinterpret_cast<const void*>(&attend_mfma_all_kernel<true, false>))
+                         : (var ? reinterpret_cast<const void*>(&attend_mfma_all_kernel<false, true>)
+                                : reinterpret_cast<const void*>(&attend_mfma_all_kernel<false, false>));
   return hipLaunchKernel(fn, dim3(p.grid), dim3(256), params, 0, s);
 }
 

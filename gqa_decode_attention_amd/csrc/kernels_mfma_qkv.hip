@@ -1,14 +1,17 @@
-// Matrix-core attention kernel of the GQA decode step for small groups
-// (G <= 16), head width 128, bf16 q/out: scores and the V sum on MFMA.
-//
-// Serves int8 caches with per-row float32 scales (Huawei CANN
+// Matrix-core attention kernel of the GQA decode step, head width 128, bf16
+// q/out: scores and the V sum on MFMA with K/V rows loaded straight into the
+// MFMA operands (no LDS staging).  Serves bf16 caches with up to 16 query
+// heads per kv-head, and int8 caches with per-row float32 scales (Huawei CANN
 // "aclnnMlaPrologV3WeightNz" page, dynamic-quantization formula: a cached
-// value reads as code * row scale), and bf16 caches.  What is computed is the
-// JAX "Grouped-Query Decode Step" page's definition over the dequantized rows,
-// with the online softmax over 16-slot tiles of the other matrix-core kernels.
+// value reads as code * row scale) with up to 64.  What is computed is the JAX
+// "Grouped-Query Decode Step" page's definition over the dequantized rows, with
+// the online softmax over 16-slot tiles of the other matrix-core kernels.
 //
-// One workgroup = NW waves = one (sequence, kv-head, split); each wave walks
-// its own run of 16-slot tiles.  Lane l = 16 r + c.  Per tile:
+// One workgroup = NW waves = one (sequence, kv-head, head chunk, split); each
+// wave walks its own run of 16-slot tiles for HB blocks of 16 query heads:
+// HB = 1 (4 waves) up to 16 heads; HB = 2 (8 waves, 32 heads per chunk) for
+// int8 caches with more, where the widened codes of a tile then serve twice
+// as many heads.  Lane l = 16 r + c.  Per tile and head block:
 //   scores  S(16 slots x 16 heads) = K(16 x 128) . Q^T as four
 //           v_mfma_f32_16x16x32_bf16: lane (r, c) supplies A-operand pieces of
 //           cache row t0 + c.  bf16 caches: bytes 16r + 64kk of the row for
@@ -118,9 +121,13 @@ struct Tile<GQA_I8> {
   float ks, vs;
 };
 
+// Online-softmax state of one wave: HB blocks of 16 query heads, each with its
+// running reference maximum m (log2 units), denominator l and the transposed
+// output sums (lane (r, c): head 16 hb + c at positions 8(4r + i) + e).
+template <int HB>
 struct State {
-  float m, l;
-  f32x4 acc[8];
+  float m[HB], l[HB];
+  f32x4 acc[HB][8];
 };
 
 // Softmax variants inside a tile (VAR): soft-capped scores, and the rows of
@@ -131,9 +138,12 @@ struct TileVar {
   int t0;
 };
 
-template <int KV, bool VAR>
-__device__ __forceinline__ void tile_math(State& st, const u32x4 (&qf)[4], const Tile<KV>& t, int lo, int valid,
-                                          int r, float scale_log2, TileVar tvar = TileVar{nullptr, nullptr, 0}) {
+// One 16-slot tile for HB head blocks: the K and V operands are loaded and
+// widened once and serve every block.
+template <int KV, bool VAR, int HB>
+__device__ __forceinline__ void tile_math(State<HB>& st, const u32x4 (&qf)[HB][4], const Tile<KV>& t, int lo,
+                                          int valid, int r, float scale_log2,
+                                          TileVar tvar = TileVar{nullptr, nullptr, 0}) {
   // Scores.
   u32x4 kf[4];
   if constexpr (KV == GQA_BF16) {
@@ -149,67 +159,91 @@ __device__ __forceinline__ void tile_math(State& st, const u32x4 (&qf)[4], const
                               pk_bf16(sbyte<0>(w1), sbyte<1>(w1)), pk_bf16(sbyte<2>(w1), sbyte<3>(w1))};
       }
   }
-  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  float sv[HB][4];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) s = mfma_k32(kf[kk], qf[kk], s);
-  float sv[4] = {s[0], s[1], s[2], s[3]};
-  if constexpr (KV == GQA_I8) {
-    sv[0] *= quad_bcast<0>(t.ks);
-    sv[1] *= quad_bcast<1>(t.ks);
-    sv[2] *= quad_bcast<2>(t.ks);
-    sv[3] *= quad_bcast<3>(t.ks);
+  for (int hb = 0; hb < HB; ++hb) {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) s = mfma_k32(kf[kk], qf[hb][kk], s);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sv[hb][i] = s[i];
   }
+  // Rows of this lane's four slots that take no weight.
+  bool dead[4] = {false, false, false, false};
   if constexpr (VAR) {
     const AttnArgs& a = *tvar.a;
-    if (a.cap_T > 0.f) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sv[i] = cap_score(sv[i], a.cap_T, a.cap_invT);
-    }
     if (a.window > 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (unattended(*tvar.sv, phys_slot(*tvar.sv, tvar.t0 + 4 * r + i))) sv[i] = kNegInfQ;
+      for (int i = 0; i < 4; ++i) dead[i] = unattended(*tvar.sv, phys_slot(*tvar.sv, tvar.t0 + 4 * r + i));
     }
   }
   if (lo > 0 || valid < 16) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (4 * r + i < lo || 4 * r + i >= valid) sv[i] = kNegInfQ;
+    for (int i = 0; i < 4; ++i) dead[i] = dead[i] || 4 * r + i < lo || 4 * r + i >= valid;
   }
-  // Softmax (per head c = this lane's column).
-  float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-  mx = rows_max(mx);
-  const float mc = mx * scale_log2;
-  if (__any(mc > st.m + kSlackQ)) {
-    const float m_new = fmaxf(st.m, mc);
-    const float alpha = fast_exp2(st.m - m_new);  // 0 on the first tile
-    st.l *= alpha;
-    st.m = m_new;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) st.acc[e] *= alpha;
-  }
-  // With the sliding window a wave can meet tiles with no attended row before
-  // its first attended one (m still -inf): their weights are 0, not NaN.
-  const float nm = VAR && st.m == kNegInfQ ? 0.f : -st.m;
-  float p[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(sv[i], scale_log2, nm));
-  st.l += (p[0] + p[1]) + (p[2] + p[3]);
+  float ksc[4], vsc[4];
   if constexpr (KV == GQA_I8) {
-    p[0] *= quad_bcast<0>(t.vs);
-    p[1] *= quad_bcast<1>(t.vs);
-    p[2] *= quad_bcast<2>(t.vs);
-    p[3] *= quad_bcast<3>(t.vs);
+    ksc[0] = quad_bcast<0>(t.ks);
+    ksc[1] = quad_bcast<1>(t.ks);
+    ksc[2] = quad_bcast<2>(t.ks);
+    ksc[3] = quad_bcast<3>(t.ks);
+    vsc[0] = quad_bcast<0>(t.vs);
+    vsc[1] = quad_bcast<1>(t.vs);
+    vsc[2] = quad_bcast<2>(t.vs);
+    vsc[3] = quad_bcast<3>(t.vs);
   }
-  // Each weight enters the V sum as a pair of bf16 values hi = bf16(p) and
-  // lo = bf16(p - hi), so it is carried to about 2^-17 of its value (float32
-  // arithmetic within the tolerance of a float32 sum).  The pair is stacked
-  // along the K axis of one 16x16x32 MFMA: k = 8r + i is slot 4r + i times
-  // its hi part, k = 8r + 4 + i the same slot times its lo part.
-  const uint32_t h01 = pk_bf16(p[0], p[1]), h23 = pk_bf16(p[2], p[3]);
-  const u32x4 pb = {h01, h23, pk_bf16(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01)),
-                    pk_bf16(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23))};
-  // V sum: A operand of MFMA e = element 8c + e of slots 4r .. 4r + 3 (twice).
+  u32x4 pb[HB];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    float* sc = sv[hb];
+    if constexpr (KV == GQA_I8) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[i] *= ksc[i];
+    }
+    if constexpr (VAR) {
+      const AttnArgs& a = *tvar.a;
+      if (a.cap_T > 0.f) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[i] = cap_score(sc[i], a.cap_T, a.cap_invT);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (dead[i]) sc[i] = kNegInfQ;
+    // Softmax (per head 16 hb + c = this lane's column).
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mx = rows_max(mx);
+    const float mc = mx * scale_log2;
+    if (__any(mc > st.m[hb] + kSlackQ)) {
+      const float m_new = fmaxf(st.m[hb], mc);
+      const float alpha = fast_exp2(st.m[hb] - m_new);  // 0 on the first tile
+      st.l[hb] *= alpha;
+      st.m[hb] = m_new;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) st.acc[hb][e] *= alpha;
+    }
+    // With the sliding window a wave can meet tiles with no attended row before
+    // its first attended one (m still -inf): their weights are 0, not NaN.
+    const float nm = VAR && st.m[hb] == kNegInfQ ? 0.f : -st.m[hb];
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(sc[i], scale_log2, nm));
+    st.l[hb] += (p[0] + p[1]) + (p[2] + p[3]);
+    if constexpr (KV == GQA_I8) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] *= vsc[i];
+    }
+    // Each weight enters the V sum as a pair of bf16 values hi = bf16(p) and
+    // lo = bf16(p - hi), so it is carried to about 2^-17 of its value (float32
+    // arithmetic within the tolerance of a float32 sum).  The pair is stacked
+    // along the K axis of one 16x16x32 MFMA: k = 8r + i is slot 4r + i times
+    // its hi part, k = 8r + 4 + i the same slot times its lo part.
+    const uint32_t h01 = pk_bf16(p[0], p[1]), h23 = pk_bf16(p[2], p[3]);
+    pb[hb] = u32x4{h01, h23, pk_bf16(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01)),
+                   pk_bf16(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23))};
+  }
+  // V sum: A operand of MFMA e = element 8c + e of slots 4r .. 4r + 3 (twice),
+  // shared by the head blocks.
   unroll<0, 8>([&](auto ei) {
     constexpr int e = decltype(ei)::value;
     u32x2_t va;
@@ -222,7 +256,8 @@ __device__ __forceinline__ void tile_math(State& st, const u32x4 (&qf)[4], const
       va = u32x2_t{pk_bf16(sbyte<by>(t.v[0][wd]), sbyte<by>(t.v[1][wd])),
                    pk_bf16(sbyte<by>(t.v[2][wd]), sbyte<by>(t.v[3][wd]))};
     }
-    st.acc[e] = mfma_k32(u32x4{va[0], va[1], va[0], va[1]}, pb, st.acc[e]);
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) st.acc[hb][e] = mfma_k32(u32x4{va[0], va[1], va[0], va[1]}, pb[hb], st.acc[hb][e]);
   });
 }
 
@@ -241,16 +276,17 @@ struct Piece {
   int64_t pbase, pstride;
 };
 
-template <int KV, int NW, bool PAGED, bool VAR>
-__device__ __forceinline__ void attend_piece(const AttnArgs& a, const Piece& pc, float (*sm_o)[16][kDq],
-                                             float (*sm_m)[16], float (*sm_l)[16]) {
+template <int KV, int NW, int HB, bool PAGED, bool VAR>
+__device__ __forceinline__ void attend_piece(const AttnArgs& a, const Piece& pc, float (*sm_o)[16 * HB][kDq],
+                                             float (*sm_m)[16 * HB], float (*sm_l)[16 * HB]) {
+  constexpr int GW = 16 * HB;               // query heads per wave (and per workgroup)
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r = lane >> 4;
   const int c = lane & 15;
   const int b = pc.b, h = pc.h, hc = pc.hc;
-  const int hq0 = h * a.G + 16 * hc;       // first query head of this workgroup
-  const int G = min(16, a.G - 16 * hc);   // query heads in this workgroup
+  const int hq0 = h * a.G + GW * hc;       // first query head of this workgroup
+  const int G = min(GW, a.G - GW * hc);   // query heads in this workgroup
   const int L = pc.L;
   const SeqView& view = pc.view;
   const int Lv = L - view.gap;
@@ -289,18 +325,23 @@ __device__ __forceinline__ void attend_piece(const AttnArgs& a, const Piece& pc,
   // Query operand: positions matching the K operand's.
   const int64_t qrow = ((int64_t)b * a.Hq + hq0 + c) * kDq;
   const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + qrow;
-  u32x4 qf[4];
+  u32x4 qf[HB][4];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const int d0 = KV == GQA_BF16 ? 32 * kk + 8 * r : 64 * (kk >> 1) + 16 * r + 8 * (kk & 1);
-    qf[kk] = (c < G) ? *reinterpret_cast<const u32x4*>(qp + d0) : u32x4{0, 0, 0, 0};
-  }
+  for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int d0 = KV == GQA_BF16 ? 32 * kk + 8 * r : 64 * (kk >> 1) + 16 * r + 8 * (kk & 1);
+      qf[hb][kk] = (16 * hb + c < G) ? *reinterpret_cast<const u32x4*>(qp + 16 * hb * kDq + d0) : u32x4{0, 0, 0, 0};
+    }
 
-  State st;
-  st.m = kNegInfQ;
-  st.l = 0.f;
+  State<HB> st;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) st.acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int hb = 0; hb < HB; ++hb) {
+    st.m[hb] = kNegInfQ;
+    st.l[hb] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st.acc[hb][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   // Rows are clamped into [t_begin, w1 - 1]: every load is in bounds and reads
   // a valid slot; clamped rows are masked to weight 0.
@@ -364,8 +405,10 @@ __device__ __forceinline__ void attend_piece(const AttnArgs& a, const Piece& pc,
 
   // Fused step, bf16: the new token is a tile whose only valid row is
   // k_new / v_new (row 0: lanes c = 0 for K, slot 0 = lanes of row r = 0, i = 0
-  // for V); its bits are copied to slot L after the loop.
+  // for V); its bits are copied to slot L after the loop (read again there, so
+  // the tile holds no registers across the loop).
   Tile<KV> tn;
+  float new_ks = 0.f, new_vs = 0.f;  // int8: the new rows' scales
   if constexpr (KV == GQA_BF16) {
     if (new_here) {
       const int64_t nrow = ((int64_t)b * a.Hkv + h) * kDq;
@@ -415,8 +458,8 @@ __device__ __forceinline__ void attend_piece(const AttnArgs& a, const Piece& pc,
       tn.v[0] = r == 0 ? wv : u32x2_t{0u, 0u};
 #pragma unroll
       for (int i = 1; i < 4; ++i) tn.v[i] = u32x2_t{0u, 0u};
-      tn.ks = ksc;
-      tn.vs = vsc;
+      tn.ks = new_ks = ksc;
+      tn.vs = new_vs = vsc;
     }
   }
 
@@ -425,61 +468,76 @@ __device__ __forceinline__ void attend_piece(const AttnArgs& a, const Piece& pc,
   Tile<KV> ta, tb;
   int32_t eB = entry(w0 + 16), eA = entry(w0 + 32);  // table entries of the first pair's successors
   load_tile(w0, ta, entry(w0));
-  if (new_here) tile_math<KV, VAR>(st, qf, tn, 0, 1, r, a.scale_log2, TileVar{&a, &view, Lv});
+  if (new_here) tile_math<KV, VAR, HB>(st, qf, tn, 0, 1, r, a.scale_log2, TileVar{&a, &view, Lv});
   if (w0 < w1) {
     const int nt = (w1 - w0 + 15) >> 4;
     int t0 = w0;
     for (int it = 0; it < nt / 2; ++it) {
       const int32_t nB = entry(t0 + 48), nA = entry(t0 + 64);
       load_tile(t0 + 16, tb, eB);
-      tile_math<KV, VAR>(st, qf, ta, t_begin - t0, w1 - t0, r, a.scale_log2, TileVar{&a, &view, t0});
+      tile_math<KV, VAR, HB>(st, qf, ta, t_begin - t0, w1 - t0, r, a.scale_log2, TileVar{&a, &view, t0});
       load_tile(t0 + 32, ta, eA);  // past w1 it re-reads row w1 - 1
-      tile_math<KV, VAR>(st, qf, tb, t_begin - t0 - 16, w1 - t0 - 16, r, a.scale_log2,
+      tile_math<KV, VAR, HB>(st, qf, tb, t_begin - t0 - 16, w1 - t0 - 16, r, a.scale_log2,
                          TileVar{&a, &view, t0 + 16});
       eB = nB;
       eA = nA;
       t0 += 32;
     }
-    if (nt & 1) tile_math<KV, VAR>(st, qf, ta, t_begin - t0, w1 - t0, r, a.scale_log2, TileVar{&a, &view, t0});
+    if (nt & 1) tile_math<KV, VAR, HB>(st, qf, ta, t_begin - t0, w1 - t0, r, a.scale_log2, TileVar{&a, &view, t0});
   }
   if constexpr (KV == GQA_BF16) {
-    if (new_here && hc == 0) {  // one head chunk writes the appended row
+    if (new_here && hc == 0) {  // one head chunk writes the appended row: a copy of k_new / v_new
       const int64_t off = slot_offset_checked(a, b, h, L);
+      const int64_t nrow = ((int64_t)b * a.Hkv + h) * kDq;
       uint16_t* kw = reinterpret_cast<uint16_t*>(a.k_cache_w) + off;
       uint16_t* vw = reinterpret_cast<uint16_t*>(a.v_cache_w) + off;
       if (off >= 0 && c == 0) {
+        const uint16_t* knp = reinterpret_cast<const uint16_t*>(a.k_new) + nrow;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) *reinterpret_cast<u32x4*>(kw + 32 * kk + 8 * r) = tn.k[kk];
+        for (int kk = 0; kk < 4; ++kk)
+          *reinterpret_cast<u32x4*>(kw + 32 * kk + 8 * r) = *reinterpret_cast<const u32x4*>(knp + 32 * kk + 8 * r);
       }
-      if (off >= 0 && r == 0) *reinterpret_cast<u32x4*>(vw + 8 * c) = tn.v[0];
+      if (off >= 0 && r == 0)
+        *reinterpret_cast<u32x4*>(vw + 8 * c) =
+            *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.v_new) + nrow + 8 * c);
     }
   } else {
-    if (new_here && hc == 0) {
+    if (new_here && hc == 0) {  // the codes still sit in this wave's merge buffer
       const int64_t off = slot_offset_checked(a, b, h, L);
       int8_t* kw = reinterpret_cast<int8_t*>(a.k_cache_w) + off;
       int8_t* vw = reinterpret_cast<int8_t*>(a.v_cache_w) + off;
+      const uint8_t* xr = reinterpret_cast<const uint8_t*>(&sm_o[wave][0][0]);
       if (off >= 0 && c == 0) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4*>(kw + 64 * j + 16 * r) = tn.k[j];
+        for (int j = 0; j < 2; ++j)
+          *reinterpret_cast<u32x4*>(kw + 64 * j + 16 * r) = *reinterpret_cast<const u32x4*>(xr + 64 * j + 16 * r);
       }
-      if (off >= 0 && r == 0) *reinterpret_cast<u32x2_t*>(vw + 8 * c) = tn.v[0];
+      if (off >= 0 && r == 0) *reinterpret_cast<u32x2_t*>(vw + 8 * c) = *reinterpret_cast<const u32x2_t*>(xr + 128 + 8 * c);
       if (off >= 0 && lane == 0) {
-        a.k_scale_w[off / kDq] = tn.ks;
-        a.v_scale_w[off / kDq] = tn.vs;
+        a.k_scale_w[off / kDq] = new_ks;
+        a.v_scale_w[off / kDq] = new_vs;
       }
     }
   }
+  // The merge below overwrites the merge buffers (the int8 new row's codes).
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // Each lane holds complete sums of head c at positions 8(4r + i) + e.
-  st.l = rows_sum(st.l);
-  if (c < G) {
+  // Each lane holds complete sums of head 16 hb + c at positions 8(4r + i) + e.
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
+  for (int hb = 0; hb < HB; ++hb) {
+    const float lsum = rows_sum(st.l[hb]);
+    const int g = 16 * hb + c;
+    if (g < G) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sm_o[wave][c][8 * (4 * r + i) + e] = st.acc[e][i];
-    if (r == 0) {
-      sm_m[wave][c] = st.m;
-      sm_l[wave][c] = st.l;
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm_o[wave][g][8 * (4 * r + i) + e] = st.acc[hb][e][i];
+      if (r == 0) {
+        sm_m[wave][g] = st.m[hb];
+        sm_l[wave][g] = lsum;
+      }
     }
   }
   __syncthreads();
@@ -515,12 +573,12 @@ __device__ __forceinline__ void attend_piece(const AttnArgs& a, const Piece& pc,
 }
 
 
-template <int KV, int NW, bool PAGED, bool VAR>
+template <int KV, int NW, int HB, bool PAGED, bool VAR>
 __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
   static_assert(!(PAGED && KV == GQA_I8), "int8 caches are dense");
-  __shared__ float sm_o[NW][16][kDq];
-  __shared__ float sm_m[NW][16];
-  __shared__ float sm_l[NW][16];
+  __shared__ float sm_o[NW][16 * HB][kDq];
+  __shared__ float sm_m[NW][16 * HB];
+  __shared__ float sm_l[NW][16 * HB];
   extern __shared__ int32_t sm_pre[];  // balanced mode: tile offsets of the sequences (B + 1 entries)
 
   auto piece_of = [&](int b, int h, int hc, int t_begin, int t_end, bool whole, int64_t pbase, int64_t pstride) {
@@ -579,7 +637,7 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
     const int nact = nv == 0 ? 0 : min(a.nsplit, (nv + a.split_tokens - 1) / a.split_tokens);
     if (split >= max(nact, 1)) return;
     pc.whole = nact <= 1;
-    pc.pbase = ((int64_t)b * a.Hq + h * a.G + 16 * hc) * a.nsplit + split;
+    pc.pbase = ((int64_t)b * a.Hq + h * a.G + 16 * HB * hc) * a.nsplit + split;
     pc.pstride = a.nsplit;
     split_piece = pc;
   }
@@ -587,7 +645,7 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
   // Split mode: the one piece; balanced mode: the pieces of [lo, hi), in order
   // (a range that holds only cost units of an item has no piece of it).
   if (a.bal_pre == nullptr) {
-    attend_piece<KV, NW, PAGED, VAR>(a, split_piece, sm_o, sm_m, sm_l);
+    attend_piece<KV, NW, HB, PAGED, VAR>(a, split_piece, sm_o, sm_m, sm_l);
     return;
   }
   bool sync = false;
@@ -597,7 +655,7 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
     if (bp.j0 >= bp.j1) continue;
     if (sync) __syncthreads();  // the next piece reuses the merge buffers
     sync = true;
-    attend_piece<KV, NW, PAGED, VAR>(a, piece_of(bp.b, bp.h, 0, 16 * bp.j0, 16 * bp.j1, bp.whole, bp.pbase, 1), sm_o,
+    attend_piece<KV, NW, HB, PAGED, VAR>(a, piece_of(bp.b, bp.h, 0, 16 * bp.j0, 16 * bp.j1, bp.whole, bp.pbase, 1), sm_o,
                                      sm_m, sm_l);
   }
 }
@@ -607,43 +665,53 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
 
 using qkv::attend_mfma_qkv_kernel;
 
-// Dynamic LDS that, with the kernel's 33 KB static arrays, exceeds half of a
-// CU's 160 KB (one workgroup per CU).
+// Dynamic LDS that, with the 4-wave kernel's 33 KB static arrays, exceeds half
+// of a CU's 160 KB (one workgroup per CU).  The 8-wave kernel's 130 KB of merge
+// buffers already allow only one.
 constexpr unsigned kOneWorkgroupLds = 48u * 1024u;
 
 const bool kHaveMfmaQk = true;
 const bool kHaveMfmaQkI8 = true;
 
-// bf16 caches (dense, slot-indexed or paged) or int8 caches (dense, new token
-// appended beforehand).
+template <int NW, int HB>
+static const void* qk_kernel(const AttnArgs& a, bool var) {
+  if (a.kv_dtype == GQA_I8)
+    return var ? reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_I8, NW, HB, false, true>)
+               : reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_I8, NW, HB, false, false>);
+  if (HB == 1 && a.map_kind == GQA_MAP_PAGED)
+    return var ? reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_BF16, NW, HB, true, true>)
+               : reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_BF16, NW, HB, true, false>);
+  if (HB == 1)
+    return var ? reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_BF16, NW, HB, false, true>)
+               : reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_BF16, NW, HB, false, false>);
+  return nullptr;  // bf16 caches with more than 16 heads run on the large-group kernel
+}
+
+// bf16 caches (dense, slot-indexed or paged) with up to 16 query heads per
+// kv-head: 4 waves of one 16-head block each.  Int8 caches (dense): the same
+// for up to 16 heads; for 17..64 heads, 8 waves of two 16-head blocks each (32
+// query heads per workgroup and head chunk).
 hipError_t launch_attend_mfma_qk(const AttnArgs& a, const Plan& p, hipStream_t s) {
-  constexpr int NW = 4;
-  if (a.D != qkv::kDq || a.G > 16 * a.head_chunks || p.block != 64 * NW) return hipErrorInvalidValue;
+  const int HB = a.G > 16 ? 2 : 1;
+  const int NW = HB == 2 ? 8 : 4;
+  if (a.D != qkv::kDq || a.G > 16 * HB * a.head_chunks || p.block != 64 * NW) return hipErrorInvalidValue;
   const bool var = a.window > 0 || a.cap_T > 0.f;  // in-loop variants (the sink is applied at the end)
-  const void* fn;
-  if (a.kv_dtype == GQA_I8) {
-    if (a.map_kind != 0 || a.k_scale == nullptr || a.v_scale == nullptr || a.qo_dtype != GQA_BF16 ||
-        (a.k_new != nullptr && (a.k_cache_w == nullptr || a.k_scale_w == nullptr || a.v_scale_w == nullptr)))
-      return hipErrorInvalidValue;
-    fn = var ? reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_I8, NW, false, true>)
-             : reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_I8, NW, false, false>);
-  } else if (a.map_kind == GQA_MAP_PAGED) {
-    fn = var ? reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_BF16, NW, true, true>)
-             : reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_BF16, NW, true, false>);
-  } else {
-    fn = var ? reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_BF16, NW, false, true>)
-             : reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_BF16, NW, false, false>);
-  }
+  if (a.kv_dtype == GQA_I8 &&
+      (a.map_kind != 0 || a.k_scale == nullptr || a.v_scale == nullptr || a.qo_dtype != GQA_BF16 ||
+       (a.k_new != nullptr && (a.k_cache_w == nullptr || a.k_scale_w == nullptr || a.v_scale_w == nullptr))))
+    return hipErrorInvalidValue;
+  const void* fn = HB == 2 ? qk_kernel<8, 2>(a, var) : qk_kernel<4, 1>(a, var);
+  if (fn == nullptr) return hipErrorInvalidValue;
   AttnArgs arg = a;
   void* params[] = {&arg};
   // Balanced mode: one workgroup per CU (the tile ranges are equal only if all
-  // of them run at once).  The dynamic LDS holds the sequences' tile offsets
-  // and, with the kernel's 33 KB static arrays, exceeds half of a CU's 160 KB.
+  // of them run at once).  The dynamic LDS holds the sequences' tile offsets.
   unsigned lds = 0;
   if (a.bal_pre != nullptr) {
     if (a.B > kMaxBalancedBatch || a.head_chunks != 1 || p.grid < 1 || p.grid != a.bal_units)
       return hipErrorInvalidValue;
-    lds = std::max<unsigned>(kOneWorkgroupLds, (unsigned)(a.B + 1) * 4u);
+    lds = (unsigned)(a.B + 1) * 4u;
+    if (HB == 1) lds = std::max<unsigned>(kOneWorkgroupLds, lds);
   }
   return hipLaunchKernel(fn, dim3(p.grid), dim3(p.block), params, lds, s);
 }

@@ -282,10 +282,12 @@ def test_workspace_bytes_cover_partials(ns):
 
 
 def test_block_shapes():
-    """Every kernel runs 4-wave workgroups; MFMA_QK aims at about one workgroup per CU."""
+    """Kernels run 4-wave workgroups (8 for int8 caches with G > 16); MFMA_QK aims at about one workgroup per CU."""
     for kw in (dict(num_q_heads=8, num_kv_heads=2), dict(num_q_heads=32, num_kv_heads=2),
                dict(num_q_heads=64, num_kv_heads=1), dict(kv_dtype=g.F32, qo_dtype=g.F32)):
         assert g.get_plan(desc(**kw))["block"] == 256
+    # int8 caches with more than 16 heads per kv-head: 8 waves of two 16-head blocks
+    assert g.get_plan(desc(num_q_heads=64, num_kv_heads=1, kv_dtype=g.I8))["block"] == 512
     p = g.get_plan(desc(batch=32, num_q_heads=32, num_kv_heads=8, capacity=4097))
     assert p["kernel"] == "mfma_qk" and p["grid"] == 256 and p["num_splits"] == 1
 

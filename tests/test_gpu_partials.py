@@ -44,7 +44,8 @@ CASES = {
     "mfma_qk_g16_int8": (2, 32, 2, 1700, "BHSD", "i8", "bf16", 3, 1.0, [1700, 1200], "mfma_qk"),
     "mfma_all_g64": (2, 64, 1, 2100, "BHSD", "bf16", "bf16", 4, 1.0, [2100, 1300], "mfma_all"),
     "mfma_all_g32_keys3": (2, 64, 2, 1600, "BSHD", "bf16", "bf16", 3, 3.0, [1600, 900], "mfma_all"),
-    "mfma_all_g64_int8": (2, 64, 1, 1800, "BHSD", "i8", "bf16", 3, 1.0, [1800, 1100], "mfma_all"),
+    "mfma_qk_g64_int8": (2, 64, 1, 1800, "BHSD", "i8", "bf16", 3, 1.0, [1800, 1100], "mfma_qk"),
+    "mfma_qk_g24_int8_bshd": (2, 48, 2, 1500, "BSHD", "i8", "bf16", 3, 1.0, [1500, 900], "mfma_qk"),
     "generic_bf16_caches_f32_out": (2, 16, 4, 1500, "BHSD", "bf16", "f32", 3, 1.0, [1500, 800], "generic"),
 }
 

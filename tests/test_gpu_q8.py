@@ -132,7 +132,7 @@ def test_q8_append_alone_with_ties_and_zero_rows(g, qo):
     assert_same_bytes(inp["v_scale"], rvs, "v scales")
 
 
-@pytest.mark.parametrize("Hq", [8, 64], ids=["G4-small-group-kernel", "G32-large-group-kernel"])
+@pytest.mark.parametrize("Hq", [8, 64], ids=["G4-one-head-block", "G32-two-head-blocks"])
 def test_q8_step_quantizes_ties_and_zero_rows_in_kernel(g, Hq):
     """The matrix-core kernels quantize a step's new rows themselves: rows
     whose x / scale lands exactly on .5 (largest magnitude 127, so scale 1),
@@ -150,7 +150,8 @@ def test_q8_step_quantizes_ties_and_zero_rows_in_kernel(g, Hq):
     inp["v_new"][2, 0] = 0
     inp["v_new"][1, 0] = tie.to(torch.bfloat16).to(DEV)
     desc = g.make_desc(B, Hq, Hkv, D, S, "BHSD", g.I8, g.BF16)
-    assert g.get_plan(desc)["kernel"] == ("mfma_qk" if Hq // Hkv <= 16 else "mfma_all")
+    assert g.get_plan(desc)["kernel"] == "mfma_qk"
+    assert g.get_plan(desc)["block"] == (256 if Hq // Hkv <= 16 else 512)
     ref, rk, rv, rks, rvs = oracle.step_q8(np_of(inp["q"]), "bf16", np_of(inp["k_cache"]), np_of(inp["v_cache"]),
                                            np_of(inp["k_scale"]), np_of(inp["v_scale"]), np_of(inp["k_new"]),
                                            np_of(inp["v_new"]), L.numpy(), "BHSD", Hq, Hkv)

@@ -8,10 +8,12 @@ every slot past the attended range refilled with NaN (keys) and +Inf (values)
 two outputs must be bitwise equal and finite.  A kernel that loaded a stale
 row and gave it weight 0 would turn the output into NaN (0 * Inf, NaN * 0).
 
-Cases cover the G <= 16 matrix-core kernel (split mode, both layouts, forced
-splits, attend), the large-group matrix-core kernel (G = 24 and 64), the
-generic vector kernel (float32 and bf16 storage, D = 64 and G = 80), the
-balanced mode, and paged / slot-indexed caches on all three kernels.
+Cases cover the small-group matrix-core kernel (split mode, both layouts,
+forced splits, attend; int8 caches with two 16-head blocks per wave), the
+large-group matrix-core kernel (G = 24 and 64), the generic vector kernel
+(float32 and bf16 storage, D = 64 and G = 80), the balanced mode, and paged /
+slot-indexed caches on all three kernels.  Int8 codes cannot hold NaN: there
+the refill puts NaN in the stale slots' scales and -127 in their codes.
 """
 import pytest
 import torch
@@ -49,15 +51,25 @@ CASES = {
     "paged32_mfma_all": (2, 64, 1, 128, 900, "BSHD", "bf16", "bf16", 0, "paged", 32, "mfma_all", False),
     "paged7_generic_f32": (3, 8, 2, 64, 300, "BHSD", "f32", "f32", 0, "paged", 7, "generic", False),
     "slots_mfma_qk": (3, 32, 8, 128, 700, "BSHD", "bf16", "bf16", 0, "slots", 0, "mfma_qk", False),
+    "mfma_qk_g32_two_blocks_int8": (3, 64, 2, 128, 900, "BHSD", "i8", "bf16", 0, None, 0, "mfma_qk", False),
+    "mfma_qk_g64_two_blocks_int8": (2, 64, 1, 128, 1100, "BSHD", "i8", "bf16", 3, None, 0, "mfma_qk", False),
 }
 
 
 def refill(inp, w, n_att):
-    """Copies of the caches with every slot j >= n_att[b] set to NaN (K) / +Inf (V)."""
+    """Copies of the caches with every slot j >= n_att[b] set to NaN (K) / +Inf (V);
+    int8 caches: NaN scales and codes of -127 there."""
     slot = torch.arange(w.capacity, device=DEV)
     stale = slot[None, :] >= n_att.to(DEV).long()[:, None]
-    stale = stale[:, None, :, None] if w.layout == "BHSD" else stale[:, :, None, None]
+    row = stale[:, None, :] if w.layout == "BHSD" else stale[:, :, None]   # the scales' shape
+    stale = row[..., None]                                                 # the caches' shape
     out = dict(inp)
+    if w.kv_dtype == "i8":
+        for name in ("k_cache", "v_cache"):
+            out[name] = torch.where(stale, torch.tensor(-127, dtype=torch.int8, device=DEV), inp[name])
+        for name in ("k_scale", "v_scale"):
+            out[name] = torch.where(row, torch.tensor(float("nan"), device=DEV), inp[name])
+        return out
     for name, fill in (("k_cache", float("nan")), ("v_cache", float("inf"))):
         c = inp[name]
         out[name] = torch.where(stale, torch.tensor(fill, dtype=c.dtype, device=DEV), c)
@@ -74,18 +86,19 @@ def same_bits(a, b):
 @pytest.mark.parametrize("call", ["step", "attend"])
 def test_stale_slots_never_loaded(g, case, call):
     B, Hq, Hkv, D, S, lay, kv, qo, ns, kind, bs, kernel, balanced = CASES[case]
-    w = W.custom(B, Hq, Hkv, D, S, lay, kv, qo, seed=300 + B + Hq, stale="pm:1000")
+    w = W.custom(B, Hq, Hkv, D, S, lay, kv, qo, seed=300 + B + Hq, stale="none" if kv == "i8" else "pm:1000")
     L = torch.randint(0, S, (B,), generator=torch.Generator().manual_seed(S + B), dtype=torch.int32)
     L[0] = S - 1 if call == "step" else S
     L[1] = 0 if call == "step" else 1
     if call == "attend":
         L = L.clamp(min=1)
-    desc = g.make_desc(B, Hq, Hkv, D, S, lay, g.F32 if kv == "f32" else g.BF16, g.F32 if qo == "f32" else g.BF16, ns)
+    code = {"f32": g.F32, "bf16": g.BF16, "i8": g.I8}
+    desc = g.make_desc(B, Hq, Hkv, D, S, lay, code[kv], code[qo], ns)
     plan = g.get_plan(desc)
     print(f"stale refill {case} {call}: plan {plan}", flush=True)
     assert plan["kernel"] == kernel and plan["balanced"] == balanced
     n_att = L + 1 if call == "step" else L
-    base = W.make_inputs(w, DEV, lengths=L)
+    base = W.make_q8(w, DEV, lengths=L) if kv == "i8" else W.make_inputs(w, DEV, lengths=L)
     runs = []
     for inp in (base, refill(base, w, n_att)):
         inp = {k: v.clone() for k, v in inp.items()}
@@ -98,6 +111,12 @@ def test_stale_slots_never_loaded(g, case, call):
             else:
                 out = g.attend_mapped(inp["q"], kc, vc, inp["lengths"], table, kind=kind, layout=lay,
                                       num_splits=ns)
+        elif kv == "i8" and call == "step":
+            out = g.step_q8(inp["q"], inp["k_cache"], inp["v_cache"], inp["k_scale"], inp["v_scale"], inp["k_new"],
+                            inp["v_new"], inp["lengths"], layout=lay, num_splits=ns)
+        elif kv == "i8":
+            out = g.attend_q8(inp["q"], inp["k_cache"], inp["v_cache"], inp["k_scale"], inp["v_scale"],
+                              inp["lengths"], layout=lay, num_splits=ns)
         elif call == "step":
             out = g.step(inp["q"], inp["k_cache"], inp["v_cache"], inp["k_new"], inp["v_new"], inp["lengths"],
                          layout=lay, num_splits=ns)
