@@ -24,7 +24,7 @@ STATUS_NAMES = {
 }
 F32, BF16, I8 = 0, 1, 2
 LAYOUTS = {"BHSD": 0, "BSHD": 1}
-KERNEL_NAMES = {0: "generic", 1: "mfma_qk", 2: "mfma_all"}
+KERNEL_NAMES = {0: "generic", 1: "mfma_qk", 2: "mfma_all", 3: "small"}
 
 
 class GqaError(RuntimeError):

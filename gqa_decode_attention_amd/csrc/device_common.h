@@ -114,6 +114,30 @@ __device__ __forceinline__ float rows_max(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// Reductions over the 16 lanes of each row with DPP lane permutations (quad
+// xor 1, quad xor 2, half-row mirror, row mirror): vector-ALU only, every lane
+// ends with its row's result.  All 64 lanes must be active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f32<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x += dpp_f32<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x += dpp_f32<0x141>(x);  // row_half_mirror: lane i <-> 7 - i
+  return x + dpp_f32<0x140>(x);  // row_mirror: lane i <-> 15 - i
+}
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_f32<0xB1>(x));
+  x = fmaxf(x, dpp_f32<0x4E>(x));
+  x = fmaxf(x, dpp_f32<0x141>(x));
+  return fmaxf(x, dpp_f32<0x140>(x));
+}
+// Whole-wave sum / maximum from the row results and the cross-row swaps; all
+// 64 lanes active.
+__device__ __forceinline__ float wave_sum_dpp(float x) { return rows_sum(row16_sum(x)); }
+__device__ __forceinline__ float wave_max_dpp(float x) { return rows_max(row16_max(x)); }
+
 // Butterfly reductions over the 64 lanes of a wave, result in every lane.
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll

@@ -60,6 +60,8 @@ gqa_status_t check_desc(const gqa_decode_desc_t* d) {
   return GQA_OK;
 }
 
+bool is_matrix_core(int32_t kernel) { return kernel == GQA_KERNEL_MFMA_QK || kernel == GQA_KERNEL_MFMA_ALL; }
+
 // Which attention kernel serves the descriptor (pointer alignment is checked
 // separately: a misaligned call of a fast-path descriptor is refused).
 int32_t choose_kernel(const gqa_decode_desc_t* d) {
@@ -99,8 +101,10 @@ int32_t device_cus() {
 // `span` > 0 bounds the slots any sequence walks (a sliding window with a
 // host-known prefix); the splits then cover [0, span) instead of the capacity.
 // `generic` forces the vector kernel (paged caches whose blocks the
-// matrix-core kernels cannot tile).
-gqa_status_t make_plan(const gqa_decode_desc_t* d, Plan* p, int64_t span = 0, bool generic = false) {
+// matrix-core kernels cannot tile); `small` allows the small-head-width kernel
+// (plain calls: it applies no softmax variant).
+gqa_status_t make_plan(const gqa_decode_desc_t* d, Plan* p, int64_t span = 0, bool generic = false,
+                       bool small = true) {
   gqa_status_t st = check_desc(d);
   if (st != GQA_OK) return st;
   std::memset(p, 0, sizeof(*p));
@@ -109,6 +113,19 @@ gqa_status_t make_plan(const gqa_decode_desc_t* d, Plan* p, int64_t span = 0, bo
   const int64_t S = span > 0 ? std::min<int64_t>(span, d->capacity) : d->capacity;
   const int64_t G = Hq / Hkv;
   p->kernel = generic ? GQA_KERNEL_GENERIC : choose_kernel(d);
+  // Small head widths on short caches, no forced split: one wave per
+  // (sequence, query head) with one slot per lane (latency-bound steps).
+  if (small && p->kernel == GQA_KERNEL_GENERIC && D <= 16 && d->capacity <= 512 && d->kv_dtype != GQA_I8 &&
+      d->num_splits <= 1) {
+    p->kernel = GQA_KERNEL_SMALL;
+    p->head_chunks = 1;
+    p->block = 256;
+    p->nsplit = 1;
+    p->split_tokens = (int32_t)S;
+    const int64_t waves = B * Hq;
+    p->grid = (int32_t)std::max<int64_t>(1, (waves + 3) / 4);
+    return GQA_OK;
+  }
   // Query-head chunks per kv-head: 8 heads per workgroup in the generic
   // kernel, 16 (one MFMA tile) in MFMA_QK, all G in MFMA_ALL.
   // MFMA_QK takes 16 heads per workgroup (4 waves) for G <= 16, 32 (8 waves
@@ -217,7 +234,7 @@ gqa_status_t check_map(const gqa_decode_desc_t* d, const gqa_cache_map_t* m, con
     if (!mul_ok(d->batch, m->max_blocks, &t)) return GQA_ERR_UNSUPPORTED;
     // The matrix-core kernels take one block per 16-slot tile; other block
     // sizes are planned on the generic kernel (plan_for).
-    if (p.kernel != GQA_KERNEL_GENERIC && m->block_size % 16 != 0) return GQA_ERR_INTERNAL;
+    if (is_matrix_core(p.kernel) && m->block_size % 16 != 0) return GQA_ERR_INTERNAL;
   } else {
     if (!mul_ok(m->num_rows, d->num_kv_heads, &t) || !mul_ok(t, d->capacity, &t) || !mul_ok(t, d->head_dim, &t) ||
         !mul_ok(t, 4, &t))
@@ -334,7 +351,7 @@ gqa_status_t check_attend_ptrs(const gqa_decode_desc_t* d, const gqa_cache_map_t
   if (!aligned(q, eqo) || !aligned(out, eqo) || !aligned(kc, ekv) || !aligned(vc, ekv) || !aligned(lengths, 4))
     return GQA_ERR_INVALID_ARGUMENT;
   if (step && (!aligned(kn, enew) || !aligned(vn, enew))) return GQA_ERR_INVALID_ARGUMENT;
-  if (p.kernel != GQA_KERNEL_GENERIC) {
+  if (is_matrix_core(p.kernel)) {
     // The matrix-core kernels read q, caches and new K/V with 16-byte loads.
     if (!aligned(q, 16) || !aligned(kc, 16) || !aligned(vc, 16) || !aligned(out, 16)) return GQA_ERR_INVALID_ARGUMENT;
     if (step && (!aligned(kn, 16) || !aligned(vn, 16))) return GQA_ERR_INVALID_ARGUMENT;
@@ -384,6 +401,7 @@ gqa_status_t run_attend(const gqa_decode_desc_t* d, const Plan& p, AttnArgs& a, 
   switch (p.kernel) {
     case GQA_KERNEL_MFMA_QK: e = launch_attend_mfma_qk(a, p, s); break;
     case GQA_KERNEL_MFMA_ALL: e = launch_attend_mfma_all(a, p, s); break;
+    case GQA_KERNEL_SMALL: e = launch_attend_small(a, p, s); break;
     default: {
       const size_t ekv = elem_bytes(d->kv_dtype);
       const bool vec = (d->head_dim * ekv) % 16 == 0 && aligned(a.k_cache, 16) && aligned(a.v_cache, 16) &&
@@ -549,12 +567,13 @@ const gqa_decode_opts_t kNoOpts = {nullptr, nullptr, nullptr, nullptr};
 // window's span when one is known, and on the generic kernel for paged caches
 // whose block size is not a multiple of the matrix-core kernels' 16-slot tile.
 gqa_status_t plan_for(const gqa_decode_desc_t* d, const gqa_decode_opts_t* o, Plan* p) {
-  gqa_status_t st = make_plan(d, p, walk_span(o->softmax));
+  const bool small = o->softmax == nullptr;
+  gqa_status_t st = make_plan(d, p, walk_span(o->softmax), false, small);
   if (st != GQA_OK) return st;
   const gqa_cache_map_t* m = o->map;
   if (m != nullptr && m->kind == GQA_MAP_PAGED && m->block_size > 0 && m->block_size % 16 != 0 &&
-      p->kernel != GQA_KERNEL_GENERIC)
-    st = make_plan(d, p, walk_span(o->softmax), true);
+      is_matrix_core(p->kernel))
+    st = make_plan(d, p, walk_span(o->softmax), true, small);
   return st;
 }
 

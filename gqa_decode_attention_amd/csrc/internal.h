@@ -110,6 +110,7 @@ hipError_t launch_rope_append(const AttnArgs& a, void* k_cache, void* v_cache, h
 // Quantizing append into int8 caches (new K/V in a.qo_dtype).
 hipError_t launch_append_q8(const AttnArgs& a, void* k_cache, void* v_cache, hipStream_t s);
 hipError_t launch_attend_generic(const AttnArgs& a, const Plan& p, int vec_path, hipStream_t s);
+hipError_t launch_attend_small(const AttnArgs& a, const Plan& p, hipStream_t s);
 hipError_t launch_attend_mfma_qk(const AttnArgs& a, const Plan& p, hipStream_t s);
 hipError_t launch_attend_mfma_all(const AttnArgs& a, const Plan& p, hipStream_t s);
 hipError_t launch_combine(const AttnArgs& a, const Plan& p, hipStream_t s);

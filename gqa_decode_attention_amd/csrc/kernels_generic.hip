@@ -517,6 +517,114 @@ hipError_t launch_attend_generic(const AttnArgs& a, const Plan& p, int vec_path,
 }
 
 // ---------------------------------------------------------------------------
+// Small head widths (D <= 16, capacity <= 512, plain softmax): one wave per
+// (sequence, query head), four per workgroup; lane j takes slot j of each
+// 64-slot chunk with its whole key and value row (D elements), so a chunk is
+// one dot product per lane, a wave maximum and sum, and the weighted rows
+// summed across lanes at the end -- a short dependent chain for steps whose
+// time is all latency.  The new token of a step (slot lengths[b]) is read
+// from k_new / v_new, and the wave of the kv-head's first query head stores
+// it; no other wave reads that slot.
+// ---------------------------------------------------------------------------
+template <int KV, int QO, int DMAX, bool MAPPED>
+__global__ __launch_bounds__(256) void attend_small_kernel(AttnArgs a) {
+  const int lane = threadIdx.x & 63;
+  // b * Hq + hq (fits 32 bits), uniform over the wave, so lengths and q come by scalar loads.
+  const int bq = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (bq >= a.B * a.Hq) return;  // whole waves only; no workgroup barrier follows
+  const int b = bq / a.Hq;
+  const int hq = bq - b * a.Hq;
+  const int h = hq / a.G;
+  const int D = a.D;
+  const int L0 = a.lengths[b];
+  int n = L0 + a.len_offset;
+  n = n < 0 ? 0 : (n > a.S ? a.S : n);
+  // Elements d >= D of a row read element D - 1 (in bounds, same row) and meet a
+  // zero query element, so every load is unconditional.
+  float q[DMAX];
+#pragma unroll
+  for (int d = 0; d < DMAX; ++d)
+    q[d] = d < D ? Store<QO>::load1_cached(a.q, (int64_t)bq * D + d) : 0.f;
+  const bool fused = a.k_new != nullptr;
+  const int64_t nrow = ((int64_t)b * a.Hkv + h) * D;
+  const int64_t base = MAPPED ? 0 : row_head_offset(a, b, h);
+  float m = kNegInf, l = 0.f, o[DMAX];
+#pragma unroll
+  for (int d = 0; d < DMAX; ++d) o[d] = 0.f;
+  for (int j0 = 0; j0 < n; j0 += 64) {  // uniform over the wave
+    const int j = j0 + lane;
+    float s = kNegInf, v[DMAX];
+#pragma unroll
+    for (int d = 0; d < DMAX; ++d) v[d] = 0.f;
+    if (j < n) {
+      const bool is_new = fused && j == L0;
+      const int64_t off = is_new ? nrow : (MAPPED ? slot_offset(a, b, h, j) : base + (int64_t)j * a.st);
+      const void* kb = is_new ? a.k_new : a.k_cache;
+      const void* vb = is_new ? a.v_new : a.v_cache;
+      float kx[DMAX];
+#pragma unroll
+      for (int d = 0; d < DMAX; ++d) {
+        const int dd = d < D ? d : D - 1;
+        kx[d] = Store<KV>::load1_cached(kb, off + dd);
+        v[d] = Store<KV>::load1_cached(vb, off + dd);
+      }
+      float dot = 0.f;
+#pragma unroll
+      for (int d = 0; d < DMAX; ++d) dot = fmaf(q[d], kx[d], dot);
+      s = dot * a.scale_log2;
+    }
+    const float mn = fmaxf(m, wave_max_dpp(s));
+    const float alpha = m == kNegInf ? 0.f : fast_exp2(m - mn);
+    const float p = j < n ? fast_exp2(s - mn) : 0.f;
+    l = l * alpha + wave_sum_dpp(p);
+#pragma unroll
+    for (int d = 0; d < DMAX; ++d) o[d] = fmaf(p, v[d], o[d] * alpha);
+    m = mn;
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+  for (int d = 0; d < DMAX; ++d) {
+    if (d < D) {  // uniform
+      const float od = wave_sum_dpp(o[d]);
+      if (lane == d) Store<QO>::store1(a.out, (int64_t)bq * D + d, od * inv);
+    }
+  }
+  if (fused && hq == h * a.G && lane < D) {  // the appended slot (raw bits)
+    const int64_t off = (L0 >= 0 && L0 < a.S) ? slot_offset_checked(a, b, h, L0) : -1;
+    if (off >= 0) {
+      Store<KV>::copy1(a.k_cache_w, off + lane, a.k_new, nrow + lane);
+      Store<KV>::copy1(a.v_cache_w, off + lane, a.v_new, nrow + lane);
+    }
+  }
+}
+
+template <int KV, int QO, bool MAPPED>
+static const void* small_kernel(int D) {
+  if (D <= 4) return reinterpret_cast<const void*>(&attend_small_kernel<KV, QO, 4, MAPPED>);
+  if (D <= 8) return reinterpret_cast<const void*>(&attend_small_kernel<KV, QO, 8, MAPPED>);
+  return reinterpret_cast<const void*>(&attend_small_kernel<KV, QO, 16, MAPPED>);
+}
+
+template <int KV, int QO>
+static const void* small_kernel(int D, bool mapped) {
+  return mapped ? small_kernel<KV, QO, true>(D) : small_kernel<KV, QO, false>(D);
+}
+
+hipError_t launch_attend_small(const AttnArgs& a, const Plan& p, hipStream_t s) {
+  if (a.D > 16 || a.kv_dtype == GQA_I8 || p.grid < 1) return hipErrorInvalidValue;
+  AttnArgs arg = a;
+  void* params[] = {&arg};
+  const bool mapped = a.map_kind != 0;
+  const void* fn;
+  if (a.kv_dtype == GQA_F32)
+    fn = a.qo_dtype == GQA_F32 ? small_kernel<GQA_F32, GQA_F32>(a.D, mapped) : small_kernel<GQA_F32, GQA_BF16>(a.D, mapped);
+  else
+    fn = a.qo_dtype == GQA_F32 ? small_kernel<GQA_BF16, GQA_F32>(a.D, mapped)
+                               : small_kernel<GQA_BF16, GQA_BF16>(a.D, mapped);
+  return hipLaunchKernel(fn, dim3(p.grid), dim3(256), params, 0, s);
+}
+
+// ---------------------------------------------------------------------------
 // Combine: one wave per (b, query head), four per workgroup.  Lane i holds
 // split i's maximum and denominator (at most 64 splits), so the merged maximum
 // M, the weights 2^(m_i - M) and the merged denominator are wave reductions;

@@ -112,9 +112,12 @@ typedef struct {
 
 enum {
   GQA_KERNEL_GENERIC = 0,  /* vector ALU, any D <= 256, f32 or bf16 storage                  */
-  GQA_KERNEL_MFMA_QK = 1,  /* bf16 (or int8 caches, bf16 q/out), D = 128, G <= 16: scores and
-                              V sum on MFMA, 16 query heads per 16-slot tile                   */
-  GQA_KERNEL_MFMA_ALL = 2  /* bf16, D = 128, 16 < G <= 64: scores and V sum on MFMA           */
+  GQA_KERNEL_MFMA_QK = 1,  /* bf16 caches with G <= 16, or int8 caches (bf16 q/out) with G <= 64;
+                              D = 128: scores and V sum on MFMA, K/V rows loaded straight into
+                              the MFMA operands                                                */
+  GQA_KERNEL_MFMA_ALL = 2, /* bf16, D = 128, 16 < G <= 64: scores and V sum on MFMA           */
+  GQA_KERNEL_SMALL = 3     /* f32 or bf16, D <= 16, capacity <= 512, no softmax variant and no
+                              forced split: one wave per (sequence, query head)                 */
 };
 
 /* Phase one (CANN operator page, two-phase call convention): validate the

@@ -174,6 +174,9 @@ SHAPES = [
     (2, 32, 8, 128, 2000, "BHSD", "bf16", "bf16", 24),   # many splits: the combine's second loop
     (2, 16, 2, 128, 1500, "BSHD", "f32", "f32", 64),     # 64 splits, float32 combine
     (2, 64, 1, 128, 3000, "BHSD", "bf16", "bf16", 13),   # G = 64, an odd split count above 8
+    (3, 8, 2, 16, 500, "BSHD", "bf16", "bf16", 0),       # small-head-width kernel, several 64-slot chunks
+    (2, 12, 3, 7, 130, "BHSD", "f32", "bf16", 0),        # small kernel, odd D, f32 caches with bf16 out
+    (4, 8, 1, 2, 512, "BHSD", "f32", "f32", 0),          # small kernel at its largest capacity
 ]
 
 
