@@ -459,19 +459,19 @@ gqa_status_t gqa_decode_get_plan(const gqa_decode_desc_t* desc, gqa_decode_plan_
 namespace {
 
 // Int8 caches need their row scales and nothing else does; scales are 4-byte
-// aligned float32 arrays of B * Hkv * S entries that overlap no other buffer
+// aligned float32 arrays with one entry per cache row (the cache's shape
+// without the last axis, mapped caches included) that overlap no other buffer
 // (`others`: the call's other spans).
-gqa_status_t check_scales(const gqa_decode_desc_t* d, const gqa_kv_scales_t* sc, const gqa_cache_map_t* map) {
+gqa_status_t check_scales(const gqa_decode_desc_t* d, const gqa_kv_scales_t* sc) {
   if ((d->kv_dtype == GQA_I8) != (sc != nullptr)) return GQA_ERR_INVALID_ARGUMENT;
-  if (sc != nullptr && map != nullptr) return GQA_ERR_UNSUPPORTED;  // int8 mapped caches: not built
   return GQA_OK;
 }
-gqa_status_t check_scale_ptrs(const gqa_decode_desc_t* d, const gqa_kv_scales_t* sc,
+gqa_status_t check_scale_ptrs(const gqa_decode_desc_t* d, const gqa_cache_map_t* map, const gqa_kv_scales_t* sc,
                               std::initializer_list<Span> others) {
   if (sc == nullptr) return GQA_OK;
   if (!sc->k_scale || !sc->v_scale || !aligned(sc->k_scale, 4) || !aligned(sc->v_scale, 4))
     return GQA_ERR_INVALID_ARGUMENT;
-  const size_t n = (size_t)d->batch * d->num_kv_heads * d->capacity * 4;
+  const size_t n = cache_elems(d, map) / d->head_dim * 4;
   const Span ks = span(sc->k_scale, n), vs = span(sc->v_scale, n);
   if (overlap(ks, vs)) return GQA_ERR_INVALID_ARGUMENT;
   for (const Span& o : others)
@@ -596,7 +596,7 @@ gqa_status_t do_append(const gqa_decode_desc_t* desc, const gqa_decode_opts_t* o
   const gqa_decode_opts_t* o = opts ? opts : &kNoOpts;
   const gqa_cache_map_t* map = o->map;
   const gqa_kv_scales_t* sc = o->scales;
-  if ((st = check_scales(desc, sc, map)) != GQA_OK) return st;
+  if ((st = check_scales(desc, sc)) != GQA_OK) return st;
   if ((st = check_rope(desc, o->rope)) != GQA_OK) return st;
   if (o->softmax != nullptr) return GQA_ERR_INVALID_ARGUMENT;  // the append computes no softmax
   Plan p;
@@ -620,8 +620,8 @@ gqa_status_t do_append(const gqa_decode_desc_t* desc, const gqa_decode_opts_t* o
       overlap(s_vn, s_vc) || overlap(s_len, s_kc) || overlap(s_len, s_vc) || overlap(s_map, s_kc) ||
       overlap(s_map, s_vc))
     return GQA_ERR_INVALID_ARGUMENT;
-  if ((st = check_scale_ptrs(desc, sc, {s_kc, s_vc, s_kn, s_vn, s_len})) != GQA_OK) return st;
-  const size_t sb = sc ? B * Hkv * desc->capacity * 4 : 0;
+  if ((st = check_scale_ptrs(desc, map, sc, {s_kc, s_vc, s_kn, s_vn, s_len, s_map})) != GQA_OK) return st;
+  const size_t sb = sc ? cache_elems(desc, map) / D * 4 : 0;
   if ((st = check_rope_ptrs(desc, o->rope,
                             {s_kc, s_vc, span(sc ? sc->k_scale : nullptr, sb), span(sc ? sc->v_scale : nullptr, sb)})) !=
       GQA_OK)
@@ -659,7 +659,7 @@ gqa_status_t do_attend(const gqa_decode_desc_t* desc, const gqa_decode_opts_t* o
   const gqa_cache_map_t* map = o->map;
   const gqa_kv_scales_t* sc = o->scales;
   const gqa_rope_t* rope = o->rope;
-  if ((st = check_scales(desc, sc, map)) != GQA_OK) return st;
+  if ((st = check_scales(desc, sc)) != GQA_OK) return st;
   if (rope != nullptr && !step) return GQA_ERR_INVALID_ARGUMENT;  // rotation belongs to the append
   if ((st = check_rope(desc, rope)) != GQA_OK) return st;
   if ((st = check_softmax(desc, o->softmax)) != GQA_OK) return st;
@@ -673,15 +673,16 @@ gqa_status_t do_attend(const gqa_decode_desc_t* desc, const gqa_decode_opts_t* o
   const size_t B = desc->batch, Hq = desc->num_q_heads, Hkv = desc->num_kv_heads, D = desc->head_dim;
   const size_t eqo = elem_bytes(desc->qo_dtype), ce = cache_elems(desc, map) * elem_bytes(desc->kv_dtype);
   if (sc != nullptr) {
-    st = check_scale_ptrs(desc, sc,
+    st = check_scale_ptrs(desc, map, sc,
                           {span(q, B * Hq * D * eqo), span(out, B * Hq * D * eqo), span(k_cache, ce),
                            span(v_cache, ce), span(lengths, B * 4), span(workspace, pw.workspace_bytes),
                            span(step ? k_new : nullptr, step ? B * Hkv * D * eqo : 0),
-                           span(step ? v_new : nullptr, step ? B * Hkv * D * eqo : 0)});
+                           span(step ? v_new : nullptr, step ? B * Hkv * D * eqo : 0),
+                           span(map ? map->map : nullptr, map_bytes(desc, map))});
     if (st != GQA_OK) return st;
   }
   if (rope != nullptr) {
-    const size_t sb = sc ? B * Hkv * desc->capacity * 4 : 0;
+    const size_t sb = sc ? cache_elems(desc, map) / D * 4 : 0;
     st = check_rope_ptrs(desc, rope,
                          {span(out, B * Hq * D * eqo), span(k_cache, ce), span(v_cache, ce),
                           span(workspace, pw.workspace_bytes), span(sc ? sc->k_scale : nullptr, sb),
@@ -689,7 +690,7 @@ gqa_status_t do_attend(const gqa_decode_desc_t* desc, const gqa_decode_opts_t* o
     if (st != GQA_OK) return st;
   }
   if (o->softmax != nullptr) {
-    const size_t sb = sc ? B * Hkv * desc->capacity * 4 : 0;
+    const size_t sb = sc ? cache_elems(desc, map) / D * 4 : 0;
     st = check_softmax_ptrs(desc, o->softmax,
                             {span(out, B * Hq * D * eqo), span(workspace, pw.workspace_bytes),
                              span(step ? k_cache : nullptr, step ? ce : 0),

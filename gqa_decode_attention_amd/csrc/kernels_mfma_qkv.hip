@@ -368,12 +368,14 @@ __device__ __forceinline__ void attend_piece(const AttnArgs& a, const Piece& pc,
     const char* vt = vl;
     int tc = 0;       // virtual origin of the tile's block (paged)
     int shift = 0;    // physical - virtual for the whole tile (paged)
+    int64_t sb = sbase;  // int8: scale index of the row the tile's rows count from
     if (PAGED) {
       tc = tile_origin(t0);
       shift = phys(tc) - tc;
-      const int64_t off = (block_head_offset(a, blk, h) + (int64_t)((tc + shift) % a.bs) * rs) * EB;
-      kt = reinterpret_cast<const char*>(a.k_cache) + off + 16 * r;
-      vt = reinterpret_cast<const char*>(a.v_cache) + off + 16 * c;
+      const int64_t eoff = block_head_offset(a, blk, h) + (int64_t)((tc + shift) % a.bs) * rs;
+      kt = reinterpret_cast<const char*>(a.k_cache) + eoff * EB + 16 * r;
+      vt = reinterpret_cast<const char*>(a.v_cache) + eoff * EB + (KV == GQA_BF16 ? 16 : 8) * c;
+      sb = eoff / kDq;  // rows are whole multiples of D elements
     }
     auto row = [&](int tvirt) -> uint32_t {  // row offset from the tile's block (paged) or slot 0
       const int cl = max(min(tvirt, w1 - 1), t_begin);
@@ -397,7 +399,7 @@ __device__ __forceinline__ void attend_piece(const AttnArgs& a, const Piece& pc,
         t.v[i] = load_nt8(vt + (uint64_t)rv * rsb);
     }
     if constexpr (KV == GQA_I8) {
-      const int64_t rsc = sbase + (int64_t)row(t0 + 4 * r + (c & 3)) * sst;
+      const int64_t rsc = sb + (int64_t)row(t0 + 4 * r + (c & 3)) * sst;
       t.ks = __uint_as_float(load_nt4(a.k_scale + rsc));
       t.vs = __uint_as_float(load_nt4(a.v_scale + rsc));
     }
@@ -575,7 +577,6 @@ __device__ __forceinline__ void attend_piece(const AttnArgs& a, const Piece& pc,
 
 template <int KV, int NW, int HB, bool PAGED, bool VAR>
 __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
-  static_assert(!(PAGED && KV == GQA_I8), "int8 caches are dense");
   __shared__ float sm_o[NW][16 * HB][kDq];
   __shared__ float sm_m[NW][16 * HB];
   __shared__ float sm_l[NW][16 * HB];
@@ -675,6 +676,9 @@ const bool kHaveMfmaQkI8 = true;
 
 template <int NW, int HB>
 static const void* qk_kernel(const AttnArgs& a, bool var) {
+  if (a.kv_dtype == GQA_I8 && a.map_kind == GQA_MAP_PAGED)
+    return var ? reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_I8, NW, HB, true, true>)
+               : reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_I8, NW, HB, true, false>);
   if (a.kv_dtype == GQA_I8)
     return var ? reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_I8, NW, HB, false, true>)
                : reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_I8, NW, HB, false, false>);
@@ -687,17 +691,17 @@ static const void* qk_kernel(const AttnArgs& a, bool var) {
   return nullptr;  // bf16 caches with more than 16 heads run on the large-group kernel
 }
 
-// bf16 caches (dense, slot-indexed or paged) with up to 16 query heads per
-// kv-head: 4 waves of one 16-head block each.  Int8 caches (dense): the same
-// for up to 16 heads; for 17..64 heads, 8 waves of two 16-head blocks each (32
-// query heads per workgroup and head chunk).
+// bf16 caches with up to 16 query heads per kv-head: 4 waves of one 16-head
+// block each.  Int8 caches: the same for up to 16 heads; for 17..64 heads, 8
+// waves of two 16-head blocks each (32 query heads per workgroup and head
+// chunk).  Dense, slot-indexed or paged (block size a multiple of 16) caches.
 hipError_t launch_attend_mfma_qk(const AttnArgs& a, const Plan& p, hipStream_t s) {
   const int HB = a.G > 16 ? 2 : 1;
   const int NW = HB == 2 ? 8 : 4;
   if (a.D != qkv::kDq || a.G > 16 * HB * a.head_chunks || p.block != 64 * NW) return hipErrorInvalidValue;
   const bool var = a.window > 0 || a.cap_T > 0.f;  // in-loop variants (the sink is applied at the end)
   if (a.kv_dtype == GQA_I8 &&
-      (a.map_kind != 0 || a.k_scale == nullptr || a.v_scale == nullptr || a.qo_dtype != GQA_BF16 ||
+      (a.k_scale == nullptr || a.v_scale == nullptr || a.qo_dtype != GQA_BF16 ||
        (a.k_new != nullptr && (a.k_cache_w == nullptr || a.k_scale_w == nullptr || a.v_scale_w == nullptr))))
     return hipErrorInvalidValue;
   const void* fn = HB == 2 ? qk_kernel<8, 2>(a, var) : qk_kernel<4, 1>(a, var);

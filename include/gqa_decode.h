@@ -260,8 +260,9 @@ gqa_status_t gqa_decode_step_mapped(const gqa_decode_desc_t* desc, const gqa_cac
  * the descriptor's layout, and every (sequence, kv-head, slot) row has a float32
  * scale; a cached value reads as code * scale.
  *   k_scale, v_scale : float32 (B, Hkv, S) for GQA_LAYOUT_BHSD, (B, S, Hkv) for
- *                      BSHD; read by attend, the appended rows written by
- *                      append and step.
+ *                      BSHD (mapped caches through gqa_decode_*_ex: the pool's
+ *                      shape without the last axis); read by attend, the
+ *                      appended rows written by append and step.
  *   k_new, v_new     : (B, Hkv, D) in desc->qo_dtype (the model's activations);
  *                      each row is quantized on the device: float32 widening,
  *                      scale = max|x| / 127 and code = round-half-even(x / scale)
@@ -362,8 +363,11 @@ typedef struct {
 
 /* Options of the _ex calls; every member may be NULL (the plain behaviour).
  *   map     : mapped caches, as in the _mapped calls
- *   scales  : int8 caches (desc->kv_dtype = GQA_I8), as in the _q8 calls; not
- *             combined with map (GQA_ERR_UNSUPPORTED)
+ *   scales  : int8 caches (desc->kv_dtype = GQA_I8), as in the _q8 calls; with a
+ *             map the scale arrays have the mapped caches' shape without the
+ *             last axis ((num_rows, Hkv, S) / (num_rows, S, Hkv) for slot rows,
+ *             (num_blocks, Hkv, block_size) / (num_blocks, block_size, Hkv) for
+ *             a paged pool): the scale of a row sits at the row's index
  *   rope    : rotary encoding (append and step only)
  *   softmax : softmax variants (attend and step) */
 typedef struct {

@@ -16,6 +16,9 @@ from .oracle import (  # noqa: F401
 )
 from .mapped import (  # noqa: F401
     append_mapped,
+    append_q8_mapped,
+    attend_q8_mapped,
+    step_q8_mapped,
     attend_mapped,
     mapped_rows,
     slot_location,

@@ -43,6 +43,9 @@ __all__ = [
     "append_mapped",
     "attend_mapped",
     "step_mapped",
+    "append_q8_mapped",
+    "attend_q8_mapped",
+    "step_q8_mapped",
 ]
 
 KINDS = ("slots", "paged")
@@ -176,3 +179,74 @@ def step_mapped(kind: str, q, q_dtype: str, k_cache, v_cache, k_new, v_new, kv_d
     out = attend_mapped(kind, q, q_dtype, k_out, v_out, kv_dtype, n_valid, layout, num_q_heads, num_kv_heads,
                         mapping, bs)
     return out, k_out, v_out
+
+
+# ---------------------------------------------------------------------------
+# Int8 caches with per-row scales through a map: the CLIKA page lists kScale /
+# vScale beside slot_ids and the block table as parameters of one operator.
+# The scale arrays have the cache array's shape without the last axis (one
+# float32 per stored row), so slot j of (b, h) has its scale at the same index
+# tuple as its row; values read as code * scale, and an append quantizes the
+# new row by the rule of ``oracle.quant`` (Huawei CANN aclnnMlaPrologV3WeightNz
+# page, dynamic-quantization formula) and stores codes and scale there.
+# ---------------------------------------------------------------------------
+def append_q8_mapped(kind: str, k_cache, v_cache, k_scale, v_scale, k_new, v_new, new_dtype: str, lengths,
+                     layout: str, mapping, bs=None):
+    """Expected int8 caches and scales after the quantizing append at slot ``lengths[b]``."""
+    from .quant import quantize_row
+    B, Hkv, S, D = _dims(kind, k_cache, layout, mapping, bs)
+    if k_cache.dtype != np.int8 or v_cache.shape != k_cache.shape:
+        raise ValueError("int8 caches of one shape")
+    if k_scale.shape != k_cache.shape[:3] or v_scale.shape != k_cache.shape[:3]:
+        raise ValueError("scales have the caches' shape without the last axis")
+    kn = decode(k_new, new_dtype).astype(np.float32)
+    vn = decode(v_new, new_dtype).astype(np.float32)
+    kc, vc, ks, vs = k_cache.copy(), v_cache.copy(), k_scale.copy(), v_scale.copy()
+    lengths = np.asarray(lengths)
+    for b in range(B):
+        pos = int(lengths[b])
+        if not 0 <= pos < S:
+            raise ValueError(f"lengths[{b}]={pos} leaves no free slot in capacity {S}")
+        for h in range(Hkv):
+            idx = slot_location(kind, layout, mapping, b, h, pos, bs)
+            kc[idx], ks[idx] = quantize_row(kn[b, h])
+            vc[idx], vs[idx] = quantize_row(vn[b, h])
+    return kc, vc, ks, vs
+
+
+def attend_q8_mapped(kind: str, q, q_dtype: str, k_cache, v_cache, k_scale, v_scale, lengths, layout: str,
+                     num_q_heads: int, num_kv_heads: int, mapping, bs=None):
+    """Length-masked GQA attention over mapped int8 rows read as code * scale, float64 (B, Hq, D)."""
+    from .quant import dequantize
+    B, Hkv, S, D = _dims(kind, k_cache, layout, mapping, bs)
+    Hq = num_q_heads
+    if num_kv_heads != Hkv or Hq % Hkv != 0 or q.shape != (B, Hq, D):
+        raise ValueError("shape mismatch")
+    G = Hq // Hkv
+    qf = decode(q, q_dtype)
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        n = int(lengths[b])
+        if not 0 <= n <= S:
+            raise ValueError(f"lengths[{b}]={n} outside [0, {S}]")
+        for h in range(Hkv):
+            at = [slot_location(kind, layout, mapping, b, h, j, bs) for j in range(n)]
+            K = dequantize(np.array([k_cache[i] for i in at]).reshape(n, D),
+                           np.array([k_scale[i] for i in at], dtype=np.float32))
+            V = dequantize(np.array([v_cache[i] for i in at]).reshape(n, D),
+                           np.array([v_scale[i] for i in at], dtype=np.float32))
+            for hq in range(h * G, (h + 1) * G):
+                out[b, hq] = attend_one(qf[b, hq], K, V)
+    return out
+
+
+def step_q8_mapped(kind: str, q, q_dtype: str, k_cache, v_cache, k_scale, v_scale, k_new, v_new, lengths,
+                   layout: str, num_q_heads: int, num_kv_heads: int, mapping, bs=None):
+    """Quantizing append at ``lengths[b]`` (new rows stored as ``q_dtype``), then
+    attend over ``lengths[b] + 1`` slots.  Returns (out, k_cache, v_cache,
+    k_scale, v_scale) after the step."""
+    kc, vc, ks, vs = append_q8_mapped(kind, k_cache, v_cache, k_scale, v_scale, k_new, v_new, q_dtype, lengths,
+                                      layout, mapping, bs)
+    n = np.asarray(lengths).astype(np.int64) + 1
+    out = attend_q8_mapped(kind, q, q_dtype, kc, vc, ks, vs, n, layout, num_q_heads, num_kv_heads, mapping, bs)
+    return out, kc, vc, ks, vs

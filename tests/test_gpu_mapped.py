@@ -168,3 +168,57 @@ def test_paged_full_size_llama_layer(g):
         ref = oracle.attend_one(q[b, hq], K, V)
         err = np.abs(got[b, hq] - ref)
         assert np.all(err <= 1e-2 + 1e-2 * np.abs(ref)), (b, hq, err.max())
+
+
+# ---------------------------------------------------------------------------
+# Int8 caches with per-row scales through a map (the CLIKA page lists kScale /
+# vScale beside slot_ids and the block table): codes and scales stored through
+# the same map, the scales of stale, unmapped and padding rows NaN (so a read
+# of any of them shows in the output); appended codes and scales byte-exact.
+# ---------------------------------------------------------------------------
+Q8_CASES = [
+    # B, Hq, Hkv, S, layout, kind, block_size, num_splits, expected kernel
+    (3, 32, 8, 1000, "BHSD", "paged", 16, 0, "mfma_qk"),     # one 16-head block per wave
+    (2, 16, 2, 700, "BSHD", "paged", 32, 3, "mfma_qk"),
+    (2, 64, 1, 900, "BHSD", "paged", 16, 0, "mfma_qk"),      # two 16-head blocks per wave
+    (2, 48, 2, 600, "BSHD", "slots", None, 0, "mfma_qk"),
+    (3, 32, 8, 500, "BHSD", "slots", None, 2, "mfma_qk"),
+    (3, 32, 8, 500, "BHSD", "paged", 7, 0, "generic"),       # block size 7: the generic kernel
+    (2, 8, 2, 300, "BSHD", "paged", 5, 0, "generic"),
+]
+
+
+def _q8_ids(c):
+    return f"{c[5]}{c[6] or ''}-B{c[0]}Hq{c[1]}Hkv{c[2]}S{c[3]}{c[4]}n{c[7]}"
+
+
+@pytest.mark.parametrize("case", Q8_CASES, ids=[_q8_ids(c) for c in Q8_CASES])
+def test_int8_mapped_step_and_attend(g, case):
+    import ctypes
+    from gqa_decode_attention_amd import _lib
+    B, Hq, Hkv, S, layout, kind, bs, ns, kernel = case
+    w = W.custom(B, Hq, Hkv, 128, S, layout, "i8", "bf16", seed=B * 31 + Hq + (bs or 0), stale="pm:1")
+    L = torch.randint(0, S, (B,), generator=torch.Generator().manual_seed(S + 11), dtype=torch.int32)
+    L[0] = S - 1
+    inp = W.make_q8(w, DEV, lengths=L)
+    m = W.make_mapped(inp, w, kind, block_size=bs or 16)
+    table = m["map"].cpu().numpy()
+    say(f"int8 mapped step {_q8_ids(case)} capacity={m['capacity']}")
+    desc, o, keep = _lib._opts((B, Hq, 128, g.I8, g.BF16, ns, None), table=m["map"], kind=kind,
+                               k_scale=m["k_scale"], v_scale=m["v_scale"], k_cache=m["k_cache"], layout=layout)
+    assert g.get_plan_ex(desc, o)["kernel"] == kernel
+    host = {k: np_of(m[k]) for k in ("k_cache", "v_cache", "k_scale", "v_scale")}
+    ref, rk, rv, rks, rvs = oracle.step_q8_mapped(kind, np_of(inp["q"]), "bf16", host["k_cache"], host["v_cache"],
+                                                  host["k_scale"], host["v_scale"], np_of(inp["k_new"]),
+                                                  np_of(inp["v_new"]), L.numpy(), layout, Hq, Hkv, table, bs)
+    out = g.step_ex(inp["q"], m["k_cache"], m["v_cache"], inp["k_new"], inp["v_new"], inp["lengths"], layout=layout,
+                    table=m["map"], kind=kind, k_scale=m["k_scale"], v_scale=m["v_scale"], num_splits=ns)
+    torch.cuda.synchronize()
+    assert_close(out, ref, "bf16", "int8 mapped step")
+    for name, want in (("k_cache", rk), ("v_cache", rv), ("k_scale", rks), ("v_scale", rvs)):
+        assert np_of(m[name]).tobytes() == want.tobytes(), name
+    n = (inp["lengths"] + 1).contiguous()
+    out2 = g.attend_ex(inp["q"], m["k_cache"], m["v_cache"], n, layout=layout, table=m["map"], kind=kind,
+                       k_scale=m["k_scale"], v_scale=m["v_scale"], num_splits=ns)
+    torch.cuda.synchronize()
+    assert_close(out2, ref, "bf16", "int8 mapped attend")

@@ -227,3 +227,102 @@ def test_token_in_unmapped_block_raises():
     with pytest.raises(ValueError):
         oracle.attend_mapped("paged", q, "f32", pool, pool, "f32", np.array([3]), "BHSD", 1, 1,
                              np.array([[0, -1]], np.int32), 2)
+
+
+# ---------------------------------------------------------------------------
+# Int8 caches with per-row scales through a map (the CLIKA page lists kScale /
+# vScale beside slot_ids and the block table).  Pins: the JAX page's printed
+# examples, whose cached values are small integers, stored as codes with
+# scales 1 or 1/2 (exact) in permuted rows / scattered blocks whose other
+# scales are NaN; and equality with the dense int8 oracle on the same logical
+# cache, appended codes and scales included.
+# ---------------------------------------------------------------------------
+def _q8_of(values):
+    """Exact int8 codes and float32 scales for integer-valued rows: code = v and
+    scale 1, or code = 2v and scale 1/2 where that fits."""
+    v = np.asarray(values, dtype=np.float64)
+    fits = (np.abs(v).max(axis=-1) * 2 <= 127)
+    scale = np.where(fits, 0.5, 1.0).astype(np.float32)
+    codes = np.rint(v / scale[..., None]).astype(np.int8)
+    assert np.array_equal(codes.astype(np.float64) * scale[..., None], v)
+    return codes, scale
+
+
+def _scatter_q8(codes, scales, layout, kind, rng, bs=None):
+    """Codes (B, .., D) and scales (B, ..) of a dense cache stored through a map.
+    Unmapped rows / blocks: codes 127, scales NaN.  Returns (codes, scales, map)."""
+    if layout == "BHSD":
+        B, Hkv, S, D = codes.shape
+    else:
+        B, S, Hkv, D = codes.shape
+    if kind == "slots":
+        R = 2 * B + 1
+        slot_ids = rng.permutation(R)[:B].astype(np.int32)
+        c = np.full((R,) + codes.shape[1:], 127, np.int8)
+        s = np.full((R,) + scales.shape[1:], np.nan, np.float32)
+        c[slot_ids], s[slot_ids] = codes, scales
+        return c, s, slot_ids
+    nb = -(-S // bs)
+    total = B * nb + 3
+    table = rng.permutation(total)[: B * nb].reshape(B, nb).astype(np.int32)
+    pshape = (total, Hkv, bs) if layout == "BHSD" else (total, bs, Hkv)
+    c = np.full(pshape + (D,), 127, np.int8)
+    s = np.full(pshape, np.nan, np.float32)
+    for b in range(B):
+        for j in range(S):
+            for h in range(Hkv):
+                src = (b, h, j) if layout == "BHSD" else (b, j, h)
+                dst = oracle.slot_location("paged", layout, table, b, h, j, bs)
+                c[dst], s[dst] = codes[src], scales[src]
+    return c, s, table
+
+
+@pytest.mark.parametrize("kind,bs", [("slots", None), ("paged", 1), ("paged", 3)])
+@pytest.mark.parametrize("case", P2["cases"], ids=[c["name"] for c in P2["cases"]])
+def test_jax_page_examples_int8_through_maps(case, kind, bs):
+    q = f32(case["query"])
+    kc, ks = _q8_of(case["key_cache"])                            # (B, S, Hkv, D) codes, (B, S, Hkv) scales
+    vc, vs = _q8_of(case["value_cache"])
+    S = kc.shape[1]
+    if bs is not None and S % bs:
+        pytest.skip("capacity not a multiple of the block size")
+    kcm, ksm, m = _scatter_q8(kc, ks, "BSHD", kind, np.random.default_rng(17), bs)
+    vcm, vsm, m2 = _scatter_q8(vc, vs, "BSHD", kind, np.random.default_rng(17), bs)
+    assert np.array_equal(m, m2)
+    out = oracle.attend_q8_mapped(kind, q, "f32", kcm, vcm, ksm, vsm, np.array(case["lengths"]), "BSHD",
+                                  case["num_query_heads"], case["num_kv_heads"], m, bs)
+    exp, tol = _printed(case["output"])
+    assert np.all(np.abs(out - exp) <= tol + 1e-7)
+
+
+@pytest.mark.parametrize("layout", ["BHSD", "BSHD"])
+@pytest.mark.parametrize("kind,bs", [("slots", None), ("paged", 1), ("paged", 4), ("paged", 16)])
+def test_int8_mapped_step_equals_dense_int8_step(layout, kind, bs):
+    rng = np.random.default_rng(23)
+    B, Hkv, G, S, D = 3, 2, 3, 37, 8
+    shape = (B, Hkv, S, D) if layout == "BHSD" else (B, S, Hkv, D)
+    kc = rng.integers(-127, 128, shape).astype(np.int8)
+    vc = rng.integers(-127, 128, shape).astype(np.int8)
+    ks = (rng.random(shape[:3]) + 0.5).astype(np.float32) / np.float32(40)
+    vs = (rng.random(shape[:3]) + 0.5).astype(np.float32) / np.float32(40)
+    q = rng.standard_normal((B, Hkv * G, D)).astype(np.float32)
+    kn = rng.standard_normal((B, Hkv, D)).astype(np.float32)
+    vn = rng.standard_normal((B, Hkv, D)).astype(np.float32)
+    L = np.array([0, 17, S - 1], np.int32)
+    want = oracle.step_q8(q, "f32", kc, vc, ks, vs, kn, vn, L, layout, Hkv * G, Hkv)
+    S_map = S if bs is None else -(-S // bs) * bs
+    if bs is not None and S_map != S:       # pad the logical capacity to whole blocks
+        pad = [(0, 0)] * 4
+        pad[2 if layout == "BHSD" else 1] = (0, S_map - S)
+        kc, vc = np.pad(kc, pad), np.pad(vc, pad)
+        ks, vs = np.pad(ks, pad[:3], constant_values=1.0), np.pad(vs, pad[:3], constant_values=1.0)
+    kcm, ksm, m = _scatter_q8(kc, ks, layout, kind, np.random.default_rng(29), bs)
+    vcm, vsm, _ = _scatter_q8(vc, vs, layout, kind, np.random.default_rng(29), bs)
+    got = oracle.step_q8_mapped(kind, q, "f32", kcm, vcm, ksm, vsm, kn, vn, L, layout, Hkv * G, Hkv, m, bs)
+    assert np.array_equal(got[0], want[0])
+    for b in range(B):                       # the appended codes and scales sit at the mapped location
+        for h in range(Hkv):
+            src = (b, h, int(L[b])) if layout == "BHSD" else (b, int(L[b]), h)
+            dst = oracle.slot_location(kind, layout, m, b, h, int(L[b]), bs)
+            assert np.array_equal(got[1][dst], want[1][src]) and np.array_equal(got[2][dst], want[2][src])
+            assert got[3][dst] == want[3][src] and got[4][dst] == want[4][src]

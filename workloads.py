@@ -128,28 +128,36 @@ def make_mapped(inp: dict, w: Workload, kind: str, *, block_size: int = 16, num_
     batch row b lives at row ``map[b]`` of a seeded permutation.  ``"paged"``:
     a pool of ``B * ceil(S / block_size) + spare_blocks`` blocks; the table maps
     each sequence's blocks to a seeded permutation of the pool (``shuffle=False``:
-    to consecutive blocks in order).  Cache rows or
-    blocks that no sequence maps, and the slots past the capacity in the last
-    block, hold NaN bit patterns.  Returns a dict like ``inp`` with
-    k_cache/v_cache replaced, plus ``map`` (int32, same device) and, for a
-    paged cache, ``block_size`` and the mapped capacity (a multiple of it).
+    to consecutive blocks in order).  Cache rows or blocks that no sequence
+    maps, and the slots past the capacity in the last block, hold NaN bit
+    patterns (int8 codes: 127, with NaN scales).  Int8 inputs (``k_scale`` /
+    ``v_scale`` present) have their scale arrays stored through the same map,
+    in the mapped caches' shape without the last axis.  Returns a dict like
+    ``inp`` with the caches (and scales) replaced, plus ``map`` (int32, same
+    device) and, for a paged cache, ``block_size`` and the mapped capacity (a
+    multiple of it).
     """
     gen = torch.Generator().manual_seed(1000 + w.seed * 17 + seed)
     dev = inp["k_cache"].device
     B, Hkv, D, S = w.B, w.Hkv, w.D, w.capacity
-    kc, vc = inp["k_cache"], inp["v_cache"]
-    nan_bits = 0x7FC1 if kc.dtype == torch.bfloat16 else 0x7FC00001
-    itype = torch.int16 if kc.dtype == torch.bfloat16 else torch.int32
 
-    def garbage(shape):
-        return torch.full(shape, nan_bits, dtype=itype, device=dev).view(kc.dtype)
+    def garbage(shape, like):
+        if like.dtype == torch.int8:
+            return torch.full(shape, 127, dtype=torch.int8, device=dev)
+        if like.dtype == torch.bfloat16:
+            return torch.full(shape, 0x7FC1, dtype=torch.int16, device=dev).view(torch.bfloat16)
+        return torch.full(shape, 0x7FC00001, dtype=torch.int32, device=dev).view(torch.float32)
 
+    names = [("k_cache", False), ("v_cache", False)]
+    if "k_scale" in inp:
+        names += [("k_scale", True), ("v_scale", True)]
     out = dict(inp)
     if kind == "slots":
         R = num_rows if num_rows is not None else 2 * B + 1
         slot_ids = torch.randperm(R, generator=gen)[:B].to(torch.int32)
-        for name, c in (("k_cache", kc), ("v_cache", vc)):
-            m = garbage((R,) + tuple(c.shape[1:]))
+        for name, _ in names:
+            c = inp[name]
+            m = garbage((R,) + tuple(c.shape[1:]), c)
             m[slot_ids.to(dev).long()] = c
             out[name] = m
         out["map"] = slot_ids.to(dev)
@@ -164,17 +172,19 @@ def make_mapped(inp: dict, w: Workload, kind: str, *, block_size: int = 16, num_
     table = order[: B * nb].to(torch.int32).view(B, nb)
     idx = table.to(dev).long().flatten()
     pad = nb * bs - S
-    for name, c in (("k_cache", kc), ("v_cache", vc)):
-        if w.layout == "BHSD":                                   # (B, Hkv, S, D) -> blocks (B*nb, Hkv, bs, D)
-            full = torch.cat([c, garbage((B, Hkv, pad, D))], dim=2) if pad else c
-            blocks = full.view(B, Hkv, nb, bs, D).permute(0, 2, 1, 3, 4).reshape(B * nb, Hkv, bs, D)
-            pool = garbage((total, Hkv, bs, D))
-        else:                                                    # (B, S, Hkv, D) -> blocks (B*nb, bs, Hkv, D)
-            full = torch.cat([c, garbage((B, pad, Hkv, D))], dim=1) if pad else c
-            blocks = full.view(B, nb, bs, Hkv, D).reshape(B * nb, bs, Hkv, D)
-            pool = garbage((total, bs, Hkv, D))
+    for name, is_scale in names:
+        c = inp[name].unsqueeze(-1) if is_scale else inp[name]   # scales: a trailing axis of 1
+        E = c.shape[-1]
+        if w.layout == "BHSD":                                   # (B, Hkv, S, E) -> blocks (B*nb, Hkv, bs, E)
+            full = torch.cat([c, garbage((B, Hkv, pad, E), c)], dim=2) if pad else c
+            blocks = full.view(B, Hkv, nb, bs, E).permute(0, 2, 1, 3, 4).reshape(B * nb, Hkv, bs, E)
+            pool = garbage((total, Hkv, bs, E), c)
+        else:                                                    # (B, S, Hkv, E) -> blocks (B*nb, bs, Hkv, E)
+            full = torch.cat([c, garbage((B, pad, Hkv, E), c)], dim=1) if pad else c
+            blocks = full.view(B, nb, bs, Hkv, E).reshape(B * nb, bs, Hkv, E)
+            pool = garbage((total, bs, Hkv, E), c)
         pool[idx] = blocks
-        out[name] = pool
+        out[name] = pool.squeeze(-1) if is_scale else pool
     out["map"] = table.to(dev)
     out["block_size"] = bs
     out["capacity"] = nb * bs
