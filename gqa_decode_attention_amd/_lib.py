@@ -57,6 +57,7 @@ class PlanT(ctypes.Structure):
         ("combine", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
         ("balanced", ctypes.c_int32),
+        ("heads_per_item", ctypes.c_int32),
     ]
 
 
@@ -247,7 +248,7 @@ def get_plan_ex(desc: Desc, opts) -> dict:
 def _plan_dict(p: PlanT) -> dict:
     return dict(kernel=KERNEL_NAMES.get(p.kernel, p.kernel), num_splits=p.num_splits, split_tokens=p.split_tokens,
                 grid=p.grid, block=p.block, combine=bool(p.combine), workspace_bytes=p.workspace_bytes,
-                balanced=bool(p.balanced))
+                balanced=bool(p.balanced), heads_per_item=p.heads_per_item)
 
 
 def _dev(tensors, lengths):

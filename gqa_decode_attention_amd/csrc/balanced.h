@@ -1,20 +1,22 @@
 // Balanced work split of the matrix-core attention kernels (ragged batches).
 //
-// The batch's work is a sequence of units: sequence b holds Hkv items
-// (b, kv-head h) of u_b = C + c_b units each -- C units standing for the
-// fixed cost of a piece (its start-up and merge), then its c_b tiles (its
-// attended slots -- in the sliding window's virtual order when one is set --
-// in tiles of 2^shift slots, at least one tile so an empty sequence still
-// writes its zero rows).  Item (b, h) is units [P_b + h u_b, P_b + (h + 1)
-// u_b), P_b = Hkv * sum of u_b' over b' < b; its tile j is unit P_b + h u_b +
-// C + j.  The units are cut into gridDim.x equal contiguous ranges, one per
-// workgroup, so a workgroup holding many short items gets fewer tiles.  A
-// workgroup attends every item's tiles inside its range: a whole item writes
-// its output rows; an item cut between ranges leaves partial rows (m, l, o of
-// its G heads) at workspace row 2 * blockIdx + 1 if the piece holds the item's
-// first tile (the range's last piece), else 2 * blockIdx (the range's first
-// piece), and the balanced combine pass merges them.  The offsets P_b (and
-// the total) are written to the workspace by workgroup 0 for that pass.
+// The batch's work is a sequence of units: sequence b holds Hkv / hp items of
+// u_b = C + c_b units each, where an item is hp adjacent kv-heads (hp = 1, or
+// the workgroup's wave count when its waves take one kv-head each over the
+// same slots) -- C units standing for the fixed cost of a piece (its start-up
+// and merge), then its c_b tiles (its attended slots -- in the sliding
+// window's virtual order when one is set -- in tiles of 2^shift slots, at
+// least one tile so an empty sequence still writes its zero rows).  Item
+// (b, i) is units [P_b + i u_b, P_b + (i + 1) u_b), P_b = (Hkv / hp) * sum of
+// u_b' over b' < b; its tile j is unit P_b + i u_b + C + j.  The units are cut
+// into gridDim.x equal contiguous ranges, one per workgroup, so a workgroup
+// holding many short items gets fewer tiles.  A workgroup attends every
+// item's tiles inside its range: a whole item writes its output rows; an item
+// cut between ranges leaves partial rows (m, l, o of its G * hp heads) at
+// workspace row 2 * blockIdx + 1 if the piece holds the item's first tile (the
+// range's last piece), else 2 * blockIdx (the range's first piece), and the
+// balanced combine pass merges them.  The offsets P_b (and the total) are
+// written to the workspace by workgroup 0 for that pass.
 #pragma once
 
 #include "device_common.h"
@@ -42,7 +44,7 @@ __device__ __forceinline__ void balanced_scan(const AttnArgs& a, int shift, int3
   int sum = 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    cnt[i] = (i < per_t && b0 + i < B) ? a.Hkv * (a.bal_cost + seq_tiles(a, b0 + i, shift)) : 0;
+    cnt[i] = (i < per_t && b0 + i < B) ? (a.Hkv / a.hp) * (a.bal_cost + seq_tiles(a, b0 + i, shift)) : 0;
     sum += cnt[i];
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -96,7 +98,7 @@ __device__ __forceinline__ BalancedPiece balanced_piece(const AttnArgs& a, const
   }
   BalancedPiece p;
   p.b = l0;
-  const int ub = (pre[l0 + 1] - pre[l0]) / a.Hkv;  // units per item
+  const int ub = (pre[l0 + 1] - pre[l0]) / (a.Hkv / a.hp);  // units per item
   const int cb = ub - a.bal_cost;                  // tiles per item
   p.h = (t - pre[l0]) / ub;
   const int s = pre[l0] + p.h * ub + a.bal_cost;   // unit of the item's tile 0
@@ -104,7 +106,7 @@ __device__ __forceinline__ BalancedPiece balanced_piece(const AttnArgs& a, const
   p.j1 = min(cb, hi - s);
   const bool first = p.j0 == 0, last = p.j1 == cb;
   p.whole = first && last;
-  p.pbase = (2 * (int64_t)blockIdx.x + (first && !last ? 1 : 0)) * a.G;
+  p.pbase = (2 * (int64_t)blockIdx.x + (first && !last ? 1 : 0)) * a.G * a.hp;
   p.next = min(s + cb, hi);
   return p;
 }

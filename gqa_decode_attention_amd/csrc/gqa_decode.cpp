@@ -108,6 +108,7 @@ gqa_status_t make_plan(const gqa_decode_desc_t* d, Plan* p, int64_t span = 0, bo
   gqa_status_t st = check_desc(d);
   if (st != GQA_OK) return st;
   std::memset(p, 0, sizeof(*p));
+  p->hp = 1;
   const int64_t cus = device_cus();
   const int64_t B = d->batch, Hq = d->num_q_heads, Hkv = d->num_kv_heads, D = d->head_dim;
   const int64_t S = span > 0 ? std::min<int64_t>(span, d->capacity) : d->capacity;
@@ -138,7 +139,12 @@ gqa_status_t make_plan(const gqa_decode_desc_t* d, Plan* p, int64_t span = 0, bo
   // MI355X: one 4-wave workgroup per CU streams faster than 8- or 12-wave
   // workgroups or more, shorter splits -- fewer concurrent streams suit HBM.)
   p->block = p->kernel == GQA_KERNEL_MFMA_QK && G > 16 ? 512 : 256;
-  const int64_t units = std::max<int64_t>(1, B * Hkv * p->head_chunks);
+  // Caches (B, S, Hkv, D) hold a slot's kv-heads side by side: MFMA_QK then
+  // gives the four waves of a workgroup four adjacent kv-heads over the same
+  // slots (head-parallel), so the workgroup streams contiguous 1 KB row
+  // segments instead of one head's 256 bytes per 2 KB row.
+  if (p->kernel == GQA_KERNEL_MFMA_QK && G <= 16 && d->layout == GQA_LAYOUT_BSHD && Hkv % 4 == 0) p->hp = 4;
+  const int64_t units = std::max<int64_t>(1, B * (Hkv / p->hp) * p->head_chunks);
   int64_t split_tokens;
   if (d->num_splits > 0) {
     const int64_t ns = std::min<int64_t>(d->num_splits, S);
@@ -191,7 +197,7 @@ gqa_status_t make_plan(const gqa_decode_desc_t* d, Plan* p, int64_t span = 0, bo
   int64_t units_max;
   if (p->kernel == GQA_KERNEL_MFMA_QK && G <= 16 && d->num_splits == 0 && B * Hkv > cus &&
       B <= kMaxBalancedBatch && mul_ok(B * Hkv, S / 16 + 1 + cost, &units_max) && units_max < INT32_MAX) {
-    const size_t rows = (size_t)cus * 2 * G;
+    const size_t rows = (size_t)cus * 2 * G * p->hp;
     p->balanced = 1;
     p->bal_cost = cost;
     p->nsplit = 1;
@@ -312,6 +318,7 @@ void fill_args(const gqa_decode_desc_t* d, const Plan& p, AttnArgs* a) {
   a->nsplit = p.nsplit;
   a->split_tokens = p.split_tokens;
   a->head_chunks = p.head_chunks;
+  a->hp = p.hp;
   a->kv_dtype = d->kv_dtype;
   a->qo_dtype = d->qo_dtype;
   a->scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d->head_dim));
@@ -448,6 +455,7 @@ gqa_status_t gqa_decode_get_plan(const gqa_decode_desc_t* desc, gqa_decode_plan_
     plan->combine = p.combine;
     plan->workspace_bytes = p.workspace_bytes;
     plan->balanced = p.balanced;
+    plan->heads_per_item = p.hp;
     return GQA_OK;
   } catch (...) {
     return GQA_ERR_INTERNAL;
@@ -927,6 +935,7 @@ gqa_status_t gqa_decode_get_plan_ex(const gqa_decode_desc_t* desc, const gqa_dec
     plan->combine = p.combine;
     plan->workspace_bytes = workspace_total(desc, p, o);
     plan->balanced = p.balanced;
+    plan->heads_per_item = p.hp;
     return GQA_OK;
   } catch (...) {
     return GQA_ERR_INTERNAL;

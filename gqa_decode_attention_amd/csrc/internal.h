@@ -62,6 +62,7 @@ struct AttnArgs {
   int32_t* bal_pre;
   int32_t bal_units;     // balanced mode: workgroups of the attention pass
   int32_t bal_cost;      // balanced mode: units charged per item besides its tiles
+  int32_t hp;            // MFMA_QK: kv-heads per work item (4: head-parallel waves, BSHD caches; else 1)
   int32_t nsplit, split_tokens;
   int32_t head_chunks;   // generic kernel: query-head chunks per kv-head
   int32_t len_offset;    // slots attended = lengths[b] + len_offset (1 for a step, 0 for attend)
@@ -81,6 +82,7 @@ struct Plan {
   size_t off_m, off_l;   // byte offsets of part_m / part_l inside the workspace
   int32_t balanced;      // 1: equal unit ranges per workgroup (see AttnArgs::bal_pre)
   int32_t bal_cost;      // balanced mode: units charged per item besides its tiles
+  int32_t hp;            // MFMA_QK: kv-heads per work item (see AttnArgs::hp)
   size_t off_pre;        // byte offset of the tile offsets inside the workspace
 };
 

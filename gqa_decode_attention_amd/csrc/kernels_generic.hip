@@ -732,8 +732,9 @@ __global__ __launch_bounds__(256) void combine128_kernel(AttnArgs a) {
 }
 
 // Balanced-mode combine (head width 128): one wave per (b, hq) row.  Item
-// (b, h) covers tiles [s, e) of the batch's tile sequence (offsets written by
-// the attention pass); workgroup k of `a.bal_units` held tiles
+// (b, i) -- kv-heads [i hp, (i + 1) hp) of sequence b, so query heads
+// [i G hp, (i + 1) G hp) -- covers tiles [s, e) of the batch's tile sequence
+// (offsets written by the attention pass); workgroup k of `a.bal_units` held tiles
 // [k per, (k + 1) per).  An item inside one workgroup's range was written by
 // the attention pass; a cut one left a partial in every workgroup it touched:
 // row 2k + 1 of the first workgroup when the item starts inside its range,
@@ -746,20 +747,21 @@ __global__ __launch_bounds__(256) void combine_balanced_kernel(AttnArgs a) {
   if (bh >= (int64_t)a.B * a.Hq) return;  // whole waves only; no workgroup barrier follows
   const int b = (int)(bh / a.Hq);
   const int hq = (int)(bh - (int64_t)b * a.Hq);
-  const int h = hq / a.G;
-  const int g = hq - h * a.G;
+  const int GI = a.G * a.hp;   // query heads per item
+  const int h = hq / GI;       // item within the sequence
+  const int g = hq - h * GI;
   const int* pre = a.bal_pre;
   const int T = pre[a.B];
   const int W = a.bal_units;  // workgroups of the attention pass
   const int per = (T + W - 1) / W;
-  const int ub = (pre[b + 1] - pre[b]) / a.Hkv;  // units per item
+  const int ub = (pre[b + 1] - pre[b]) / (a.Hkv / a.hp);  // units per item
   const int cb = ub - a.bal_cost;                // tiles per item
   const int s0 = pre[b] + h * ub + a.bal_cost;   // unit of the item's tile 0
   const int k0 = s0 / per, k1 = (s0 + cb - 1) / per;
   if (k0 == k1) return;  // whole in one workgroup: written by the attention pass
   const int np = k1 - k0 + 1;
   auto row = [&](int i) -> int64_t {  // partial row of the i-th piece (the first holds the item's first tile)
-    return (2 * (int64_t)(k0 + i) + (i == 0 ? 1 : 0)) * a.G + g;
+    return (2 * (int64_t)(k0 + i) + (i == 0 ? 1 : 0)) * GI + g;
   };
   // One round of loads: m and l of the first 64 pieces (one per lane) and o
   // of the first eight (half-waves take alternate pieces), then the rest.

@@ -276,15 +276,21 @@ struct Piece {
   int64_t pbase, pstride;
 };
 
-template <int KV, int NW, int HB, bool PAGED, bool VAR>
+// HP = 1: the workgroup's waves share one kv-head and split the piece's tiles
+// into runs.  HP = NW (head-parallel, caches (B, S, Hkv, D)): the piece is a
+// group of NW adjacent kv-heads and wave w takes kv-head w of the group over
+// all of the piece's tiles, so the workgroup reads NW x 256 contiguous bytes
+// of every slot row at once; each wave's heads are its own (no merge).
+template <int KV, int NW, int HB, int HP, bool PAGED, bool VAR>
 __device__ __forceinline__ void attend_piece(const AttnArgs& a, const Piece& pc, float (*sm_o)[16 * HB][kDq],
                                              float (*sm_m)[16 * HB], float (*sm_l)[16 * HB]) {
+  static_assert(HP == 1 || (HP == NW && HB == 1), "head-parallel waves carry one head block");
   constexpr int GW = 16 * HB;               // query heads per wave (and per workgroup)
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r = lane >> 4;
   const int c = lane & 15;
-  const int b = pc.b, h = pc.h, hc = pc.hc;
+  const int b = pc.b, h = HP > 1 ? pc.h * HP + wave : pc.h, hc = pc.hc;
   const int hq0 = h * a.G + GW * hc;       // first query head of this workgroup
   const int G = min(GW, a.G - GW * hc);   // query heads in this workgroup
   const int L = pc.L;
@@ -318,9 +324,11 @@ __device__ __forceinline__ void attend_piece(const AttnArgs& a, const Piece& pc,
   // too; only wave 0's first tile can hold leading rows, and it always holds a
   // valid one.  The new token goes to the last wave.
   const int ntile = t_cache_end > t_begin ? (t_cache_end - tv + 15) >> 4 : 0;
-  const int w0 = tv + 16 * ((wave * ntile + NW - 1) / NW);
-  const int w1 = min(tv + 16 * (((wave + 1) * ntile + NW - 1) / NW), t_cache_end);
-  const bool new_here = own_new && wave == NW - 1;
+  constexpr int RUNS = HP > 1 ? 1 : NW;   // waves sharing the piece's tiles
+  const int run = HP > 1 ? 0 : wave;
+  const int w0 = tv + 16 * ((run * ntile + RUNS - 1) / RUNS);
+  const int w1 = min(tv + 16 * (((run + 1) * ntile + RUNS - 1) / RUNS), t_cache_end);
+  const bool new_here = own_new && run == RUNS - 1;
 
   // Query operand: positions matching the K operand's.
   const int64_t qrow = ((int64_t)b * a.Hq + hq0 + c) * kDq;
@@ -521,6 +529,47 @@ __device__ __forceinline__ void attend_piece(const AttnArgs& a, const Piece& pc,
       }
     }
   }
+  if constexpr (HP > 1) {
+    // Head-parallel: lane (r, c) holds complete sums of head c at positions
+    // 8(4r + i) + e; the wave stores its rows itself.
+    const float lsum = rows_sum(st.l[0]);
+    const int hq = hq0 + c;
+    if (c < G) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = 8 * (4 * r + i);
+        if (pc.whole) {
+          uint32_t w[4];
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            float x0 = st.acc[0][2 * e2][i], x1 = st.acc[0][2 * e2 + 1][i];
+            if (VAR || a.sink != nullptr || a.smooth) {
+              x0 = finish_row(a, hq, st.m[0], x0, lsum);
+              x1 = finish_row(a, hq, st.m[0], x1, lsum);
+            } else {
+              const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+              x0 *= inv;
+              x1 *= inv;
+            }
+            w[e2] = (uint32_t)f32_to_bf16_rne(x0) | ((uint32_t)f32_to_bf16_rne(x1) << 16);
+          }
+          *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.out) + ((int64_t)b * a.Hq + hq) * kDq + d0) =
+              u32x4{w[0], w[1], w[2], w[3]};
+        } else {
+          const int64_t pi = pc.pbase + pc.pstride * (wave * a.G + c);
+          float* po = a.part_o + pi * kDq + d0;
+          *reinterpret_cast<f32x4*>(po) = f32x4{st.acc[0][0][i], st.acc[0][1][i], st.acc[0][2][i], st.acc[0][3][i]};
+          *reinterpret_cast<f32x4*>(po + 4) =
+              f32x4{st.acc[0][4][i], st.acc[0][5][i], st.acc[0][6][i], st.acc[0][7][i]};
+          if (r == 0 && i == 0) {
+            a.part_m[pi] = st.m[0];
+            a.part_l[pi] = lsum;
+          }
+        }
+      }
+    }
+    return;
+  }
   // The merge below overwrites the merge buffers (the int8 new row's codes).
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -575,7 +624,7 @@ __device__ __forceinline__ void attend_piece(const AttnArgs& a, const Piece& pc,
 }
 
 
-template <int KV, int NW, int HB, bool PAGED, bool VAR>
+template <int KV, int NW, int HB, int HP, bool PAGED, bool VAR>
 __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
   __shared__ float sm_o[NW][16 * HB][kDq];
   __shared__ float sm_m[NW][16 * HB];
@@ -620,25 +669,26 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
     int x = blockIdx.x;
     const int split = x % a.nsplit;
     x /= a.nsplit;
+    const int items = a.Hkv / HP;  // work items per sequence
     int hc = 0, bh = x;
     if (a.head_chunks > 1) {
       const int HC = a.head_chunks;
-      const int units = a.B * a.Hkv;
+      const int units = a.B * items;
       const int grp = x / (8 * HC);
       const int gsz = min(8, units - grp * 8);  // the last group may hold fewer (b, kv-head) units
       const int rem = x - grp * 8 * HC;
       hc = rem / gsz;
       bh = grp * 8 + rem % gsz;
     }
-    const int h = bh % a.Hkv;
-    const int b = bh / a.Hkv;
+    const int h = bh % items;
+    const int b = bh / items;
     const int t_begin = split * a.split_tokens;
     Piece pc = piece_of(b, h, hc, t_begin, t_begin + a.split_tokens, false, 0, 0);
     const int nv = pc.view.nv;
     const int nact = nv == 0 ? 0 : min(a.nsplit, (nv + a.split_tokens - 1) / a.split_tokens);
     if (split >= max(nact, 1)) return;
     pc.whole = nact <= 1;
-    pc.pbase = ((int64_t)b * a.Hq + h * a.G + 16 * HB * hc) * a.nsplit + split;
+    pc.pbase = ((int64_t)b * a.Hq + h * HP * a.G + 16 * HB * hc) * a.nsplit + split;
     pc.pstride = a.nsplit;
     split_piece = pc;
   }
@@ -646,7 +696,7 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
   // Split mode: the one piece; balanced mode: the pieces of [lo, hi), in order
   // (a range that holds only cost units of an item has no piece of it).
   if (a.bal_pre == nullptr) {
-    attend_piece<KV, NW, HB, PAGED, VAR>(a, split_piece, sm_o, sm_m, sm_l);
+    attend_piece<KV, NW, HB, HP, PAGED, VAR>(a, split_piece, sm_o, sm_m, sm_l);
     return;
   }
   bool sync = false;
@@ -656,7 +706,7 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
     if (bp.j0 >= bp.j1) continue;
     if (sync) __syncthreads();  // the next piece reuses the merge buffers
     sync = true;
-    attend_piece<KV, NW, HB, PAGED, VAR>(a, piece_of(bp.b, bp.h, 0, 16 * bp.j0, 16 * bp.j1, bp.whole, bp.pbase, 1), sm_o,
+    attend_piece<KV, NW, HB, HP, PAGED, VAR>(a, piece_of(bp.b, bp.h, 0, 16 * bp.j0, 16 * bp.j1, bp.whole, bp.pbase, 1), sm_o,
                                      sm_m, sm_l);
   }
 }
@@ -674,20 +724,20 @@ constexpr unsigned kOneWorkgroupLds = 48u * 1024u;
 const bool kHaveMfmaQk = true;
 const bool kHaveMfmaQkI8 = true;
 
-template <int NW, int HB>
+template <int NW, int HB, int HP>
 static const void* qk_kernel(const AttnArgs& a, bool var) {
   if (a.kv_dtype == GQA_I8 && a.map_kind == GQA_MAP_PAGED)
-    return var ? reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_I8, NW, HB, true, true>)
-               : reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_I8, NW, HB, true, false>);
+    return var ? reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_I8, NW, HB, HP, true, true>)
+               : reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_I8, NW, HB, HP, true, false>);
   if (a.kv_dtype == GQA_I8)
-    return var ? reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_I8, NW, HB, false, true>)
-               : reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_I8, NW, HB, false, false>);
+    return var ? reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_I8, NW, HB, HP, false, true>)
+               : reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_I8, NW, HB, HP, false, false>);
   if (HB == 1 && a.map_kind == GQA_MAP_PAGED)
-    return var ? reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_BF16, NW, HB, true, true>)
-               : reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_BF16, NW, HB, true, false>);
+    return var ? reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_BF16, NW, HB, HP, true, true>)
+               : reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_BF16, NW, HB, HP, true, false>);
   if (HB == 1)
-    return var ? reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_BF16, NW, HB, false, true>)
-               : reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_BF16, NW, HB, false, false>);
+    return var ? reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_BF16, NW, HB, HP, false, true>)
+               : reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_BF16, NW, HB, HP, false, false>);
   return nullptr;  // bf16 caches with more than 16 heads run on the large-group kernel
 }
 
@@ -699,12 +749,13 @@ hipError_t launch_attend_mfma_qk(const AttnArgs& a, const Plan& p, hipStream_t s
   const int HB = a.G > 16 ? 2 : 1;
   const int NW = HB == 2 ? 8 : 4;
   if (a.D != qkv::kDq || a.G > 16 * HB * a.head_chunks || p.block != 64 * NW) return hipErrorInvalidValue;
+  if (a.hp != 1 && (a.hp != NW || HB != 1 || a.Hkv % a.hp != 0)) return hipErrorInvalidValue;
   const bool var = a.window > 0 || a.cap_T > 0.f;  // in-loop variants (the sink is applied at the end)
   if (a.kv_dtype == GQA_I8 &&
       (a.k_scale == nullptr || a.v_scale == nullptr || a.qo_dtype != GQA_BF16 ||
        (a.k_new != nullptr && (a.k_cache_w == nullptr || a.k_scale_w == nullptr || a.v_scale_w == nullptr))))
     return hipErrorInvalidValue;
-  const void* fn = HB == 2 ? qk_kernel<8, 2>(a, var) : qk_kernel<4, 1>(a, var);
+  const void* fn = HB == 2 ? qk_kernel<8, 2, 1>(a, var) : a.hp == 4 ? qk_kernel<4, 1, 4>(a, var) : qk_kernel<4, 1, 1>(a, var);
   if (fn == nullptr) return hipErrorInvalidValue;
   AttnArgs arg = a;
   void* params[] = {&arg};

@@ -108,6 +108,10 @@ typedef struct {
                             fixed cost in tiles), cut on the device from `lengths` (ragged
                             batches with more (b, kv-head) items than CUs); the combine pass
                             then merges the items cut between workgroups                   */
+  int32_t heads_per_item; /* kv-heads one workgroup takes over the same slots: 1, or 4 when the
+                             small-group matrix-core kernel reads a BSHD cache (its four waves
+                             take four adjacent kv-heads, so the workgroup reads whole 1 KB
+                             spans of each slot's row)                                       */
 } gqa_decode_plan_t;
 
 enum {

@@ -242,7 +242,8 @@ def test_plan_is_a_function_of_the_descriptor_only():
             assert p1["kernel"] == "mfma_qk" and p1["grid"] == 256 and p1["num_splits"] == 1
             assert d.batch * d.num_kv_heads > 256
             G = d.num_q_heads // d.num_kv_heads
-            assert p1["workspace_bytes"] >= 256 * 2 * G * (d.head_dim + 2) * 4 + (d.batch + 1) * 4
+            hp = p1["heads_per_item"]
+            assert p1["workspace_bytes"] >= 256 * 2 * G * hp * (d.head_dim + 2) * 4 + (d.batch + 1) * 4
 
 
 def test_balanced_mode_only_where_items_outnumber_cus():
@@ -259,6 +260,26 @@ def test_balanced_mode_only_where_items_outnumber_cus():
     assert g.get_plan(desc(batch=4096, num_q_heads=8, num_kv_heads=1, capacity=64))["balanced"]
     assert not g.get_plan(desc(batch=4097, num_q_heads=8, num_kv_heads=1, capacity=64))["balanced"]
     assert not g.get_plan(desc(batch=300, num_q_heads=8, num_kv_heads=1, kv_dtype=g.F32, qo_dtype=g.F32))["balanced"]
+
+
+def test_head_parallel_items_on_bshd_caches():
+    """The small-group matrix-core kernel takes four adjacent kv-heads per
+    workgroup (one per wave, over the same slots) on BSHD caches whose kv-head
+    count is a multiple of 4; every other plan keeps one kv-head per item."""
+    bshd = dict(layout="BSHD", num_q_heads=32, num_kv_heads=8)
+    four = [bshd, dict(bshd, batch=64, num_q_heads=64, capacity=8192), dict(bshd, num_splits=3),
+            dict(bshd, batch=40, capacity=600), dict(bshd, num_q_heads=64, num_kv_heads=4),
+            dict(bshd, num_q_heads=64, num_kv_heads=4, kv_dtype=g.I8)]
+    one = [dict(bshd, layout="BHSD"), dict(bshd, num_q_heads=16, num_kv_heads=2),
+           dict(bshd, num_q_heads=96, num_kv_heads=4, kv_dtype=g.I8),     # G = 24: two 16-head blocks a wave
+           dict(bshd, num_q_heads=128, num_kv_heads=4),                    # G = 32: large-group kernel
+           dict(bshd, head_dim=64), dict(bshd, kv_dtype=g.F32, qo_dtype=g.F32)]
+    for kw in four:
+        p = g.get_plan(desc(**kw))
+        assert p["kernel"] == "mfma_qk" and p["heads_per_item"] == 4, (kw, p)
+    for kw in one:
+        p = g.get_plan(desc(**kw))
+        assert p["heads_per_item"] == 1, (kw, p)
 
 
 @pytest.mark.parametrize("ns", [1, 2, 3, 7, 64, 10_000])

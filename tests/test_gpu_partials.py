@@ -46,6 +46,8 @@ CASES = {
     "mfma_all_g32_keys3": (2, 64, 2, 1600, "BSHD", "bf16", "bf16", 3, 3.0, [1600, 900], "mfma_all"),
     "mfma_qk_g64_int8": (2, 64, 1, 1800, "BHSD", "i8", "bf16", 3, 1.0, [1800, 1100], "mfma_qk"),
     "mfma_qk_g24_int8_bshd": (2, 48, 2, 1500, "BSHD", "i8", "bf16", 3, 1.0, [1500, 900], "mfma_qk"),
+    "mfma_qk_g4_bshd_four_heads": (2, 32, 8, 1900, "BSHD", "bf16", "bf16", 3, 1.0, [1900, 1000], "mfma_qk"),
+    "mfma_qk_g16_int8_bshd_four_heads": (2, 64, 4, 1500, "BSHD", "i8", "bf16", 3, 1.0, [1500, 700], "mfma_qk"),
     "generic_bf16_caches_f32_out": (2, 16, 4, 1500, "BHSD", "bf16", "f32", 3, 1.0, [1500, 800], "generic"),
 }
 
@@ -61,6 +63,7 @@ def test_split_partials_are_float32_accurate(g, case):
     plan = g.get_plan(desc)
     print(f"partials {case}: plan {plan}", flush=True)
     assert plan["kernel"] == kernel and not plan["balanced"] and plan["num_splits"] == ns
+    assert plan["heads_per_item"] == (4 if case.endswith("four_heads") else 1)
     st = plan["split_tokens"]
     ws = torch.full((plan["workspace_bytes"],), 0xFF, dtype=torch.uint8, device=DEV)
     if kv == "i8":

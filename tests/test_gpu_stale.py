@@ -9,7 +9,8 @@ two outputs must be bitwise equal and finite.  A kernel that loaded a stale
 row and gave it weight 0 would turn the output into NaN (0 * Inf, NaN * 0).
 
 Cases cover the small-group matrix-core kernel (split mode, both layouts,
-forced splits, attend; int8 caches with two 16-head blocks per wave), the
+forced splits, attend, four kv-heads per workgroup on BSHD caches; int8
+caches with two 16-head blocks per wave), the
 large-group matrix-core kernel (G = 24 and 64), the generic vector kernel
 (float32 and bf16 storage, D = 64 and G = 80), the small-head-width kernel
 (D = 4 and 16), the balanced mode, and paged / slot-indexed caches.  Int8 codes cannot hold NaN: there
@@ -51,6 +52,9 @@ CASES = {
     "paged32_mfma_all": (2, 64, 1, 128, 900, "BSHD", "bf16", "bf16", 0, "paged", 32, "mfma_all", False),
     "paged7_generic_f32": (3, 8, 2, 64, 300, "BHSD", "f32", "f32", 0, "paged", 7, "generic", False),
     "slots_mfma_qk": (3, 32, 8, 128, 700, "BSHD", "bf16", "bf16", 0, "slots", 0, "mfma_qk", False),
+    "mfma_qk_bshd_four_heads_splits3": (3, 32, 8, 128, 900, "BSHD", "bf16", "bf16", 3, None, 0, "mfma_qk", False),
+    "mfma_qk_int8_bshd_four_heads": (3, 64, 4, 128, 900, "BSHD", "i8", "bf16", 0, None, 0, "mfma_qk", False),
+    "paged16_bshd_four_heads": (3, 32, 8, 128, 800, "BSHD", "bf16", "bf16", 0, "paged", 16, "mfma_qk", False),
     "small_f32_d4": (3, 4, 2, 4, 200, "BHSD", "f32", "f32", 0, None, 0, "small", False),
     "small_bf16_d16_paged5": (3, 8, 2, 16, 200, "BSHD", "bf16", "bf16", 0, "paged", 5, "small", False),
     "mfma_qk_g32_two_blocks_int8": (3, 64, 2, 128, 900, "BHSD", "i8", "bf16", 0, None, 0, "mfma_qk", False),
