@@ -98,10 +98,12 @@ constexpr int kGenericHeadChunk = 8;  // query heads per workgroup in the generi
 constexpr int kMaxBalancedBatch = 4096;  // most sequences in the balanced mode (16 per thread of its scan)
 // Balanced mode: tiles charged per item besides its own (bf16 / int8 caches;
 // contiguous or strided slots of a kv-head), from sweeps on ragged batches.
+// Strided (BSHD) items are four kv-heads whose tiles carry four times the
+// bytes of a one-head tile, so the same fixed cost is fewer of their tiles.
 constexpr int kBalancedCostBf16 = 12;
 constexpr int kBalancedCostI8 = 28;
-constexpr int kBalancedCostBf16Strided = 4;
-constexpr int kBalancedCostI8Strided = 10;
+constexpr int kBalancedCostBf16Strided = 0;
+constexpr int kBalancedCostI8Strided = 5;
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_append(const AttnArgs& a, void* k_cache, void* v_cache, hipStream_t s);

@@ -67,6 +67,10 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 constexpr float kNegInfQ = -__builtin_inff();
 constexpr int kDq = 128;
 constexpr float kSlackQ = 8.f;  // lazy rescale threshold, log2 units
+// Merge-buffer row pitch in floats: a head's 128 sums plus 16 bytes, so the
+// 16-byte stores of eight lanes holding eight different heads fall on
+// different LDS banks (with a 512-byte pitch they would all share one).
+constexpr int kMergePitch = kDq + 4;
 
 template <int I, int N, typename F>
 __device__ __forceinline__ void unroll(F&& f) {
@@ -282,7 +286,7 @@ struct Piece {
 // all of the piece's tiles, so the workgroup reads NW x 256 contiguous bytes
 // of every slot row at once; each wave's heads are its own (no merge).
 template <int KV, int NW, int HB, int HP, bool PAGED, bool VAR>
-__device__ __forceinline__ void attend_piece(const AttnArgs& a, const Piece& pc, float (*sm_o)[16 * HB][kDq],
+__device__ __forceinline__ void attend_piece(const AttnArgs& a, const Piece& pc, float (*sm_o)[16 * HB][kMergePitch],
                                              float (*sm_m)[16 * HB], float (*sm_l)[16 * HB]) {
   static_assert(HP == 1 || (HP == NW && HB == 1), "head-parallel waves carry one head block");
   constexpr int GW = 16 * HB;               // query heads per wave (and per workgroup)
@@ -473,27 +477,46 @@ __device__ __forceinline__ void attend_piece(const AttnArgs& a, const Piece& pc,
     }
   }
 
-  // Two tile register sets alternate, so the next tile's loads are in flight
-  // during this tile's math.
-  Tile<KV> ta, tb;
-  int32_t eB = entry(w0 + 16), eA = entry(w0 + 32);  // table entries of the first pair's successors
-  load_tile(w0, ta, entry(w0));
+  // DEPTH tile register sets rotate, so the next DEPTH - 1 tiles' loads are
+  // in flight during a tile's math (two sets: one tile ahead, with the
+  // workgroup's waves sharing each CU's SIMDs).  The tile loaded at step d of
+  // an iteration from t0 is t0 + 16 (d + DEPTH - 1), into set
+  // (d + DEPTH - 1) mod DEPTH; en[s] is the table entry of the tile set s loads
+  // next, fetched an iteration ahead.
+  constexpr int DEPTH = 2;
+  auto next_of = [](int s) { return s == DEPTH - 1 ? DEPTH - 1 : DEPTH + s; };  // tile offset set s loads, in tiles
+  Tile<KV> ts[DEPTH];
+  int32_t en[DEPTH];
+#pragma unroll
+  for (int s = 0; s < DEPTH - 1; ++s) load_tile(w0 + 16 * s, ts[s], entry(w0 + 16 * s));
+#pragma unroll
+  for (int s = 0; s < DEPTH; ++s) en[s] = entry(w0 + 16 * next_of(s));
   if (new_here) tile_math<KV, VAR, HB>(st, qf, tn, 0, 1, r, a.scale_log2, TileVar{&a, &view, Lv});
   if (w0 < w1) {
     const int nt = (w1 - w0 + 15) >> 4;
     int t0 = w0;
-    for (int it = 0; it < nt / 2; ++it) {
-      const int32_t nB = entry(t0 + 48), nA = entry(t0 + 64);
-      load_tile(t0 + 16, tb, eB);
-      tile_math<KV, VAR, HB>(st, qf, ta, t_begin - t0, w1 - t0, r, a.scale_log2, TileVar{&a, &view, t0});
-      load_tile(t0 + 32, ta, eA);  // past w1 it re-reads row w1 - 1
-      tile_math<KV, VAR, HB>(st, qf, tb, t_begin - t0 - 16, w1 - t0 - 16, r, a.scale_log2,
-                         TileVar{&a, &view, t0 + 16});
-      eB = nB;
-      eA = nA;
-      t0 += 32;
+    for (int it = 0; it < nt / DEPTH; ++it) {
+      int32_t nx[DEPTH];
+#pragma unroll
+      for (int s = 0; s < DEPTH; ++s) nx[s] = entry(t0 + 16 * (DEPTH + next_of(s)));
+      unroll<0, DEPTH>([&](auto di) {
+        constexpr int d = decltype(di)::value;
+        constexpr int s = (d + DEPTH - 1) % DEPTH;
+        load_tile(t0 + 16 * (d + DEPTH - 1), ts[s], en[s]);  // past w1 it re-reads row w1 - 1
+        tile_math<KV, VAR, HB>(st, qf, ts[d], t_begin - t0 - 16 * d, w1 - t0 - 16 * d, r, a.scale_log2,
+                               TileVar{&a, &view, t0 + 16 * d});
+      });
+#pragma unroll
+      for (int s = 0; s < DEPTH; ++s) en[s] = nx[s];
+      t0 += 16 * DEPTH;
     }
-    if (nt & 1) tile_math<KV, VAR, HB>(st, qf, ta, t_begin - t0, w1 - t0, r, a.scale_log2, TileVar{&a, &view, t0});
+    // The remaining nt mod DEPTH (< DEPTH) tiles are already in sets 0 .. DEPTH - 2.
+    unroll<0, DEPTH - 1>([&](auto di) {
+      constexpr int d = decltype(di)::value;
+      if (d < nt % DEPTH)
+        tile_math<KV, VAR, HB>(st, qf, ts[d], t_begin - t0 - 16 * d, w1 - t0 - 16 * d, r, a.scale_log2,
+                               TileVar{&a, &view, t0 + 16 * d});
+    });
   }
   if constexpr (KV == GQA_BF16) {
     if (new_here && hc == 0) {  // one head chunk writes the appended row: a copy of k_new / v_new
@@ -582,9 +605,12 @@ __device__ __forceinline__ void attend_piece(const AttnArgs& a, const Piece& pc,
     const int g = 16 * hb + c;
     if (g < G) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sm_o[wave][g][8 * (4 * r + i) + e] = st.acc[hb][e][i];
+      for (int i = 0; i < 4; ++i) {  // positions 8(4r + i) .. +7: two 16-byte stores
+        float* row = &sm_o[wave][g][8 * (4 * r + i)];
+        *reinterpret_cast<f32x4*>(row) = f32x4{st.acc[hb][0][i], st.acc[hb][1][i], st.acc[hb][2][i], st.acc[hb][3][i]};
+        *reinterpret_cast<f32x4*>(row + 4) =
+            f32x4{st.acc[hb][4][i], st.acc[hb][5][i], st.acc[hb][6][i], st.acc[hb][7][i]};
+      }
       if (r == 0) {
         sm_m[wave][g] = st.m[hb];
         sm_l[wave][g] = lsum;
@@ -626,7 +652,7 @@ __device__ __forceinline__ void attend_piece(const AttnArgs& a, const Piece& pc,
 
 template <int KV, int NW, int HB, int HP, bool PAGED, bool VAR>
 __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
-  __shared__ float sm_o[NW][16 * HB][kDq];
+  __shared__ __attribute__((aligned(16))) float sm_o[NW][16 * HB][kMergePitch];
   __shared__ float sm_m[NW][16 * HB];
   __shared__ float sm_l[NW][16 * HB];
   extern __shared__ int32_t sm_pre[];  // balanced mode: tile offsets of the sequences (B + 1 entries)
@@ -716,9 +742,9 @@ __global__ __launch_bounds__(64 * NW) void attend_mfma_qkv_kernel(AttnArgs a) {
 
 using qkv::attend_mfma_qkv_kernel;
 
-// Dynamic LDS that, with the 4-wave kernel's 33 KB static arrays, exceeds half
-// of a CU's 160 KB (one workgroup per CU).  The 8-wave kernel's 130 KB of merge
-// buffers already allow only one.
+// Dynamic LDS that, with the one-block kernel's 34 KB static arrays, exceeds
+// half of a CU's 160 KB (one workgroup per CU).  The 135 KB of merge buffers
+// of the two-block kernel already allow only one.
 constexpr unsigned kOneWorkgroupLds = 48u * 1024u;
 
 const bool kHaveMfmaQk = true;
@@ -738,7 +764,9 @@ static const void* qk_kernel(const AttnArgs& a, bool var) {
   if (HB == 1)
     return var ? reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_BF16, NW, HB, HP, false, true>)
                : reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_BF16, NW, HB, HP, false, false>);
-  return nullptr;  // bf16 caches with more than 16 heads run on the large-group kernel
+  // bf16 caches with more than 16 heads run on the large-group kernel (two or
+  // four head blocks per wave, K/V in registers, measured slower there).
+  return nullptr;
 }
 
 // bf16 caches with up to 16 query heads per kv-head: 4 waves of one 16-head
@@ -746,7 +774,10 @@ static const void* qk_kernel(const AttnArgs& a, bool var) {
 // waves of two 16-head blocks each (32 query heads per workgroup and head
 // chunk).  Dense, slot-indexed or paged (block size a multiple of 16) caches.
 hipError_t launch_attend_mfma_qk(const AttnArgs& a, const Plan& p, hipStream_t s) {
-  const int HB = a.G > 16 ? 2 : 1;
+  if (a.head_chunks < 1) return hipErrorInvalidValue;
+  const int per = (a.G + a.head_chunks - 1) / a.head_chunks;  // query heads per workgroup
+  if (per > 32) return hipErrorInvalidValue;
+  const int HB = per > 16 ? 2 : 1;
   const int NW = HB == 2 ? 8 : 4;
   if (a.D != qkv::kDq || a.G > 16 * HB * a.head_chunks || p.block != 64 * NW) return hipErrorInvalidValue;
   if (a.hp != 1 && (a.hp != NW || HB != 1 || a.Hkv % a.hp != 0)) return hipErrorInvalidValue;
@@ -755,7 +786,9 @@ hipError_t launch_attend_mfma_qk(const AttnArgs& a, const Plan& p, hipStream_t s
       (a.k_scale == nullptr || a.v_scale == nullptr || a.qo_dtype != GQA_BF16 ||
        (a.k_new != nullptr && (a.k_cache_w == nullptr || a.k_scale_w == nullptr || a.v_scale_w == nullptr))))
     return hipErrorInvalidValue;
-  const void* fn = HB == 2 ? qk_kernel<8, 2, 1>(a, var) : a.hp == 4 ? qk_kernel<4, 1, 4>(a, var) : qk_kernel<4, 1, 1>(a, var);
+  const void* fn = HB == 2     ? qk_kernel<8, 2, 1>(a, var)
+                   : a.hp == 4 ? qk_kernel<4, 1, 4>(a, var)
+                               : qk_kernel<4, 1, 1>(a, var);
   if (fn == nullptr) return hipErrorInvalidValue;
   AttnArgs arg = a;
   void* params[] = {&arg};
