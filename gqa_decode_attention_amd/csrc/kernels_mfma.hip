@@ -91,8 +91,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 
-template <bool PAGED, bool VAR>
+template <bool PAGED, bool VAR, bool BUF>
 __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
+  static_assert(!BUF || (!PAGED && !VAR), "buffer loads serve dense rows without a window");
   __shared__ __attribute__((aligned(16))) uint16_t sk[2][kTileT * kPitch];
   __shared__ __attribute__((aligned(16))) uint16_t sv[2][kTileT * kPitch];
 
@@ -230,7 +231,33 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
     }
     return en;
   };
+  // Buffer-load path (dense or slot-indexed rows, no window): a tile's
+  // resource starts at its first row and holds its rows up to the split's
+  // end, so a lane's byte offset is the same for every tile and rows past the
+  // end read as zeros without being loaded (their scores are masked).  The
+  // launcher takes this path only when a kv-head's capacity fits the
+  // resource's 31-bit byte count.
+  const uint32_t rsb = (uint32_t)rs * 2u;  // bytes between consecutive slots
+  const uint32_t lane_off0 = (uint32_t)prow * rsb + 16u * (uint32_t)piece;
+  const uint32_t lane_off1 = lane_off0 + 16u * rsb;
+  auto tile_rsrc = [&](const uint16_t* base, int t0) {
+    const int rows = max(0, t_end - t0);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base + (int64_t)t0 * rs), (short)0,
+                                             (int)((uint32_t)rows * rsb), 0x00020000);
+  };
   auto gload = [&](int t0, Regs& R, const Ent& en) {
+    if constexpr (BUF) {
+      const auto rk = tile_rsrc(kb, t0), rv = tile_rsrc(vb, t0);
+      const u32x4 k0 = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)lane_off0, 0, 2);  // 2: non-temporal
+      const u32x4 v0 = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)lane_off0, 0, 2);
+      const u32x4 k1 = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)lane_off1, 0, 2);
+      const u32x4 v1 = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)lane_off1, 0, 2);
+      R.k[0] = k0;
+      R.v[0] = v0;
+      R.k[1] = k1;
+      R.v[1] = v1;
+      return;
+    }
     if constexpr (!PAGED) {
       // Dense or slot-indexed rows (tiles start at t_begin, so only the end
       // clamps): one 32x32->64-bit multiply-add per row address (slot strides
@@ -440,10 +467,13 @@ hipError_t launch_attend_mfma_all(const AttnArgs& a, const Plan& p, hipStream_t 
   const bool var = a.window > 0 || a.cap_T > 0.f;  // in-loop variants (the sink is applied at the end)
   const bool paged = a.map_kind == GQA_MAP_PAGED;
   if (a.kv_dtype != GQA_BF16 || a.qo_dtype != GQA_BF16) return hipErrorInvalidValue;
-  const void* fn = paged ? (var ? reinterpret_cast<const void*>(&attend_mfma_all_kernel<true, true>)
-                                : reinterpret_cast<const void*>(&attend_mfma_all_kernel<true, false>))
-                         : (var ? reinterpret_cast<const void*>(&attend_mfma_all_kernel<false, true>)
-                                : reinterpret_cast<const void*>(&attend_mfma_all_kernel<false, false>));
+  // Buffer loads need every byte offset of a kv-head's rows in 31 bits.
+  const bool buf = !paged && !var && (int64_t)a.S * a.st * 2 <= INT32_MAX;
+  const void* fn = paged ? (var ? reinterpret_cast<const void*>(&attend_mfma_all_kernel<true, true, false>)
+                                : reinterpret_cast<const void*>(&attend_mfma_all_kernel<true, false, false>))
+                   : var ? reinterpret_cast<const void*>(&attend_mfma_all_kernel<false, true, false>)
+                   : buf ? reinterpret_cast<const void*>(&attend_mfma_all_kernel<false, false, true>)
+                         : reinterpret_cast<const void*>(&attend_mfma_all_kernel<false, false, false>);
   return hipLaunchKernel(fn, dim3(p.grid), dim3(256), params, 0, s);
 }
 
