@@ -31,11 +31,11 @@ ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
           "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form=1", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall",
           "-Wno-unused-function"]
-# Per-file flags.  The large-group kernel never has a NaN among its operands
-# (stale rows are never loaded; masked scores are -inf), so its maxima need no
-# NaN-quieting copies: without them the scores' row maxima take a third of
-# the maximum instructions of each tile.
-EXTRA = {"kernels_mfma.hip": ["-fno-honor-nans"]}
+# Per-file flags.  The matrix-core kernels never have a NaN among their
+# operands (stale rows are never loaded; masked scores are -inf), so their
+# maxima need no NaN-quieting copies: without them the large-group kernel's
+# score maxima take a third of the maximum instructions of each tile.
+EXTRA = {"kernels_mfma.hip": ["-fno-honor-nans"], "kernels_mfma_qkv.hip": ["-fno-honor-nans"]}
 
 
 def _run(cmd):
