@@ -37,6 +37,9 @@ KERNEL_SOURCES = sorted(
      if f.endswith((".hip", ".cpp", ".h"))]) + ["include/gqa_decode.h", "gqa_decode_attention_amd/build.py"]
 
 
+PER_CONFIG_PAUSE_S = 3.0  # idle time before each per_config measurement
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
@@ -342,11 +345,14 @@ def main():
     del caches
     torch.cuda.empty_cache()
 
-    # Every workload's plain step, timed the same way in the same run.
+    # Every workload's plain step, timed the same way in the same run.  Each
+    # starts after an idle pause: straight after another workload's sustained
+    # stream the GPU measured up to 6 % slow (long context: 322 vs 303 us).
     per_config = None
     if not args.no_per_config:
         per_config = {}
         for name in ("tiny", "llama3_8b_layer", "ragged_batch", "long_context", "large_group"):
+            time.sleep(PER_CONFIG_PAUSE_S)
             per_config[name] = measure_plain(name, args.steps, args.warmup, graph=not args.no_graph)
             print(json.dumps({"per_config": name, **per_config[name]}), file=sys.stderr, flush=True)
 
