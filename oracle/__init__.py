@@ -14,6 +14,11 @@ from .oracle import (  # noqa: F401
     softmax_weights,
     step,
 )
+from .fp8 import (  # noqa: F401
+    E4M3_MAX,
+    decode_e4m3,
+    encode_e4m3,
+)
 from .mapped import (  # noqa: F401
     append_mapped,
     append_q8_mapped,
@@ -29,6 +34,7 @@ from .mapped import (  # noqa: F401
 from .quant import (  # noqa: F401
     append_q8,
     attend_q8,
+    code_format,
     dequantize,
     quantize_row,
     step_q8,

@@ -192,11 +192,13 @@ def step_mapped(kind: str, q, q_dtype: str, k_cache, v_cache, k_new, v_new, kv_d
 # ---------------------------------------------------------------------------
 def append_q8_mapped(kind: str, k_cache, v_cache, k_scale, v_scale, k_new, v_new, new_dtype: str, lengths,
                      layout: str, mapping, bs=None):
-    """Expected int8 caches and scales after the quantizing append at slot ``lengths[b]``."""
-    from .quant import quantize_row
+    """Expected quantized caches and scales (int8 or fp8 codes) after the quantizing append at slot
+    ``lengths[b]``."""
+    from .quant import code_format, quantize_row
     B, Hkv, S, D = _dims(kind, k_cache, layout, mapping, bs)
-    if k_cache.dtype != np.int8 or v_cache.shape != k_cache.shape:
-        raise ValueError("int8 caches of one shape")
+    fmt = code_format(k_cache)                 # int8 codes, or uint8 fp8 patterns
+    if v_cache.dtype != k_cache.dtype or v_cache.shape != k_cache.shape:
+        raise ValueError("quantized caches of one code format and shape")
     if k_scale.shape != k_cache.shape[:3] or v_scale.shape != k_cache.shape[:3]:
         raise ValueError("scales have the caches' shape without the last axis")
     kn = decode(k_new, new_dtype).astype(np.float32)
@@ -209,14 +211,14 @@ def append_q8_mapped(kind: str, k_cache, v_cache, k_scale, v_scale, k_new, v_new
             raise ValueError(f"lengths[{b}]={pos} leaves no free slot in capacity {S}")
         for h in range(Hkv):
             idx = slot_location(kind, layout, mapping, b, h, pos, bs)
-            kc[idx], ks[idx] = quantize_row(kn[b, h])
-            vc[idx], vs[idx] = quantize_row(vn[b, h])
+            kc[idx], ks[idx] = quantize_row(kn[b, h], fmt)
+            vc[idx], vs[idx] = quantize_row(vn[b, h], fmt)
     return kc, vc, ks, vs
 
 
 def attend_q8_mapped(kind: str, q, q_dtype: str, k_cache, v_cache, k_scale, v_scale, lengths, layout: str,
                      num_q_heads: int, num_kv_heads: int, mapping, bs=None):
-    """Length-masked GQA attention over mapped int8 rows read as code * scale, float64 (B, Hq, D)."""
+    """Length-masked GQA attention over mapped quantized rows read as code * scale, float64 (B, Hq, D)."""
     from .quant import dequantize
     B, Hkv, S, D = _dims(kind, k_cache, layout, mapping, bs)
     Hq = num_q_heads

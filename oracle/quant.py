@@ -13,6 +13,11 @@ row, and reads use ``value = code * scale``.
 Readings (listed with their reasons in the repository's design notes):
 
 * "round" is round-half-to-even;
+* fp8 caches (a format the pages do not define; see ``oracle.fp8``) follow the
+  same rule with the format's largest finite value in place of 127:
+  ``scale = float32(max |x|) / 448``, ``code = encode(clamp(x / scale, -448,
+  448))`` with a correctly rounded float32 division, the code the nearest
+  E4M3 value (ties to even); a row of zeros has scale 0 and codes 0;
 * the code is a decision float arithmetic takes, so it is taken in the
   kernel's precision: the new key/value (stored as ``new_dtype``) is widened
   to float32, ``scale = float32(max |x|) / 127`` and ``code = rne(x / scale)``
@@ -21,41 +26,63 @@ Readings (listed with their reasons in the repository's design notes):
 * attention then runs exactly as in ``oracle.oracle`` on the dequantized rows,
   in float64 (``code * scale`` is exact in float64).
 
-Storage: caches are int8 arrays in the dense layouts ("BHSD" (B, Hkv, S, D),
-"BSHD" (B, S, Hkv, D)); scales are float32 arrays of the same layout without
-the last axis ((B, Hkv, S) or (B, S, Hkv)).
+Storage: caches are int8 arrays (int8 codes) or uint8 arrays (fp8 codes, as
+bit patterns) in the dense layouts ("BHSD" (B, Hkv, S, D), "BSHD" (B, S, Hkv,
+D)); the array's dtype selects the format.  Scales are float32 arrays of the
+same layout without the last axis ((B, Hkv, S) or (B, S, Hkv)).
 """
 
 from __future__ import annotations
 
 import numpy as np
 
+from .fp8 import E4M3_MAX, decode_e4m3, encode_e4m3
 from .oracle import attend_one, decode, kv_index
 
 __all__ = ["quantize_row", "dequantize", "append_q8", "attend_q8", "step_q8"]
 
+CODE_DTYPES = {"i8": np.int8, "fp8": np.uint8}
 
-def quantize_row(x32: np.ndarray):
-    """float32 row -> (int8 codes, float32 scale) by the rule above."""
+
+def quantize_row(x32: np.ndarray, fmt: str = "i8"):
+    """float32 row -> (codes, float32 scale) by the rule above; ``fmt`` "i8"
+    gives int8 codes, "fp8" uint8 E4M3 codes."""
     x32 = np.asarray(x32, dtype=np.float32)
     amax = np.float32(np.max(np.abs(x32))) if x32.size else np.float32(0)
     if amax == 0 or not np.isfinite(amax):
         if amax == 0:
-            return np.zeros(x32.shape, np.int8), np.float32(0)
+            return np.zeros(x32.shape, CODE_DTYPES[fmt]), np.float32(0)
         raise ValueError("non-finite row")
+    if fmt == "fp8":
+        scale = np.float32(amax / np.float32(E4M3_MAX))   # float32 division, correctly rounded
+        q = np.clip(x32 / scale, -E4M3_MAX, E4M3_MAX)     # float32 division, then clamped
+        return encode_e4m3(q), scale
+    if fmt != "i8":
+        raise ValueError(f"unknown code format {fmt!r}")
     scale = np.float32(amax / np.float32(127))            # float32 division, correctly rounded
     q = np.rint(x32 / scale).astype(np.float32)           # float32 division, then half-to-even
     return np.clip(q, -127, 127).astype(np.int8), scale
 
 
+def code_format(codes: np.ndarray) -> str:
+    """The code format of a cache array: int8 -> "i8", uint8 -> "fp8"."""
+    for fmt, dt in CODE_DTYPES.items():
+        if codes.dtype == dt:
+            return fmt
+    raise TypeError("codes are int8 (int8 codes) or uint8 (fp8 bit patterns)")
+
+
 def dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
-    """codes (..., D) int8 and scales (...) float32 -> float64 values (exact)."""
-    return codes.astype(np.float64) * scales.astype(np.float64)[..., None]
+    """codes (..., D) (int8, or uint8 fp8 patterns) and scales (...) float32 ->
+    float64 values ``code * scale`` (exact)."""
+    vals = decode_e4m3(codes) if code_format(codes) == "fp8" else codes.astype(np.float64)
+    return vals * scales.astype(np.float64)[..., None]
 
 
 def _dims(cache, layout):
-    if cache.dtype != np.int8 or cache.ndim != 4:
-        raise TypeError("an int8 cache is a 4-D int8 array")
+    if cache.ndim != 4:
+        raise TypeError("a quantized cache is a 4-D array")
+    code_format(cache)
     if layout == "BHSD":
         B, Hkv, S, D = cache.shape
     elif layout == "BSHD":
@@ -70,6 +97,9 @@ def append_q8(k_cache, v_cache, k_scale, v_scale, k_new, v_new, new_dtype: str, 
 
     Returns new (k_cache, v_cache, k_scale, v_scale); every other byte is kept."""
     B, Hkv, S, D = _dims(k_cache, layout)
+    fmt = code_format(k_cache)
+    if v_cache.dtype != k_cache.dtype:
+        raise TypeError("k_cache and v_cache hold the same code format")
     kn = decode(k_new, new_dtype).astype(np.float32)        # exact: stored values widen to float32
     vn = decode(v_new, new_dtype).astype(np.float32)
     kc, vc, ks, vs = k_cache.copy(), v_cache.copy(), k_scale.copy(), v_scale.copy()
@@ -79,8 +109,8 @@ def append_q8(k_cache, v_cache, k_scale, v_scale, k_new, v_new, new_dtype: str, 
             raise ValueError(f"lengths[{b}]={pos} leaves no free slot in capacity {S}")
         for h in range(Hkv):
             idx = kv_index(layout, b, h, pos)
-            kc[idx], ks[idx] = quantize_row(kn[b, h])
-            vc[idx], vs[idx] = quantize_row(vn[b, h])
+            kc[idx], ks[idx] = quantize_row(kn[b, h], fmt)
+            vc[idx], vs[idx] = quantize_row(vn[b, h], fmt)
     return kc, vc, ks, vs
 
 
