@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     BF16,
     EXPORTS,
     F32,
+    FP8,
     I8,
     LIB_PATH,
     Desc,

@@ -22,7 +22,7 @@ STATUS_NAMES = {
     4: "GQA_ERR_HIP",
     5: "GQA_ERR_INTERNAL",
 }
-F32, BF16, I8 = 0, 1, 2
+F32, BF16, I8, FP8 = 0, 1, 2, 3
 LAYOUTS = {"BHSD": 0, "BSHD": 1}
 KERNEL_NAMES = {0: "generic", 1: "mfma_qk", 2: "mfma_all", 3: "small"}
 
@@ -196,7 +196,9 @@ def _dtype_code(t: torch.dtype) -> int:
         return BF16
     if t == torch.int8:
         return I8
-    raise ValueError(f"unsupported dtype {t}; float32, bfloat16 or int8 (caches only)")
+    if t == torch.float8_e4m3fn:
+        return FP8
+    raise ValueError(f"unsupported dtype {t}; float32, bfloat16, or int8 / float8_e4m3fn (caches only)")
 
 
 def make_desc(batch, num_q_heads, num_kv_heads, head_dim, capacity, layout="BHSD", kv_dtype=BF16, qo_dtype=BF16,
@@ -422,9 +424,10 @@ def step_mapped(q, k_cache, v_cache, k_new, v_new, lengths, table, *, kind, layo
 
 
 def _scales(k_cache, k_scale, v_scale, layout):
-    """gqa_kv_scales_t for int8 caches; scales are float32 of the cache's shape without D."""
-    if k_cache.dtype != torch.int8:
-        raise ValueError("the _q8 calls take int8 caches")
+    """gqa_kv_scales_t for int8 or fp8 (float8_e4m3fn) caches; scales are float32 of the
+    cache's shape without D."""
+    if k_cache.dtype not in (torch.int8, torch.float8_e4m3fn):
+        raise ValueError("the _q8 calls take int8 or float8_e4m3fn caches")
     for t in (k_scale, v_scale):
         if t.dtype != torch.float32 or tuple(t.shape) != tuple(k_cache.shape[:3]):
             raise ValueError(f"scales are float32 of shape {tuple(k_cache.shape[:3])} for {layout} caches")
@@ -433,11 +436,11 @@ def _scales(k_cache, k_scale, v_scale, layout):
 
 def append_q8(k_cache, v_cache, k_scale, v_scale, k_new, v_new, lengths, *, layout="BHSD"):
     """Quantize k_new/v_new (B, Hkv, D; float32 or bfloat16) row by row and store
-    codes and scales at slot lengths[b] of the int8 caches."""
+    codes and scales at slot lengths[b] of the int8 or fp8 caches."""
     dev = _dev([k_cache, v_cache, k_scale, v_scale, k_new, v_new], lengths)
     B, Hkv, D = k_new.shape
     S = k_cache.shape[2] if layout == "BHSD" else k_cache.shape[1]
-    desc = make_desc(B, Hkv, Hkv, D, S, layout, I8, _dtype_code(k_new.dtype))
+    desc = make_desc(B, Hkv, Hkv, D, S, layout, _dtype_code(k_cache.dtype), _dtype_code(k_new.dtype))
     sc = _scales(k_cache, k_scale, v_scale, layout)
     check(lib().gqa_decode_append_q8(ctypes.byref(desc), ctypes.byref(sc), k_cache.data_ptr(), v_cache.data_ptr(),
                                      k_new.data_ptr(), v_new.data_ptr(), lengths.data_ptr(), _stream(dev)),
@@ -446,7 +449,7 @@ def append_q8(k_cache, v_cache, k_scale, v_scale, k_new, v_new, lengths, *, layo
 
 def attend_q8(q, k_cache, v_cache, k_scale, v_scale, lengths, *, layout="BHSD", out=None, workspace=None,
               num_splits=0):
-    """Attention over int8 caches read as code * scale; lengths[b] = valid slots."""
+    """Attention over int8 or fp8 caches read as code * scale; lengths[b] = valid slots."""
     dev = _dev([q, k_cache, v_cache, k_scale, v_scale], lengths)
     desc = desc_for(q, k_cache, layout, num_splits)
     sc = _scales(k_cache, k_scale, v_scale, layout)
@@ -584,7 +587,7 @@ def append_ex(k_cache, v_cache, k_new, v_new, lengths, *, layout="BHSD", table=N
     dev = _dev(tens, lengths)
     B, Hkv, D = k_new.shape
     kv = _dtype_code(k_cache.dtype)
-    qo = _dtype_code(k_new.dtype) if kv == I8 else (kv if qo_dtype is None else _dtype_code(qo_dtype))
+    qo = _dtype_code(k_new.dtype) if kv in (I8, FP8) else (kv if qo_dtype is None else _dtype_code(qo_dtype))
     desc, o, keep = _opts((B, Hkv, D, kv, qo, 0, Hkv), table=table, kind=kind, table_host=table_host,
                           k_scale=k_scale, v_scale=v_scale, k_cache=k_cache, layout=layout, rope=rope)
     check(lib().gqa_decode_append_ex(ctypes.byref(desc), ctypes.byref(o), k_cache.data_ptr(), v_cache.data_ptr(),

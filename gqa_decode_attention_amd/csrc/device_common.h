@@ -150,6 +150,25 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// OCP 8-bit floating-point code (E4M3: bias 7, three mantissa bits,
+// subnormals below 2^-6, largest finite 448) of a float32 value of magnitude at
+// most 448: the nearest representable magnitude, ties to the even code, with
+// the value's sign bit.  Normal range: the top three mantissa bits rounded on
+// the 20 below (a carry moves into the exponent field); below 2^-6 the
+// subnormal step 2^-9, i.e. rint(|x| * 512) (exact scaling, ties to even; 8
+// is the code of 2^-6).
+__device__ __forceinline__ uint32_t e4m3_encode(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (a < 0.015625f) return sign | (uint32_t)__builtin_rintf(a * 512.f);
+  const uint32_t au = u & 0x7fffffffu;
+  uint32_t m3 = (au >> 20) & 7u;
+  const uint32_t rest = au & 0xfffffu;
+  if (rest > 0x80000u || (rest == 0x80000u && (m3 & 1u))) ++m3;
+  return sign | ((((au >> 23) - 120u) << 3) + m3);   // exponent field = unbiased + 7 = biased - 120
+}
+
 // Fast base-2 exponential (v_exp_f32).  exp2(-inf) = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

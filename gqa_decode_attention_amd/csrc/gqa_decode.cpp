@@ -44,7 +44,7 @@ gqa_status_t check_desc(const gqa_decode_desc_t* d) {
     return GQA_ERR_INVALID_ARGUMENT;
   if (d->num_q_heads % d->num_kv_heads != 0) return GQA_ERR_INVALID_ARGUMENT;
   if (d->layout != GQA_LAYOUT_BHSD && d->layout != GQA_LAYOUT_BSHD) return GQA_ERR_INVALID_ARGUMENT;
-  if ((d->kv_dtype != GQA_F32 && d->kv_dtype != GQA_BF16 && d->kv_dtype != GQA_I8) ||
+  if ((d->kv_dtype != GQA_F32 && d->kv_dtype != GQA_BF16 && d->kv_dtype != GQA_I8 && d->kv_dtype != GQA_FP8) ||
       (d->qo_dtype != GQA_F32 && d->qo_dtype != GQA_BF16))
     return GQA_ERR_INVALID_ARGUMENT;
   if (d->num_splits < 0) return GQA_ERR_INVALID_ARGUMENT;
@@ -60,6 +60,9 @@ gqa_status_t check_desc(const gqa_decode_desc_t* d) {
   return GQA_OK;
 }
 
+// Caches of one-byte codes with per-row float32 scales.
+bool quantized(int32_t dt) { return dt == GQA_I8 || dt == GQA_FP8; }
+
 bool is_matrix_core(int32_t kernel) { return kernel == GQA_KERNEL_MFMA_QK || kernel == GQA_KERNEL_MFMA_ALL; }
 
 // Which attention kernel serves the descriptor (pointer alignment is checked
@@ -67,7 +70,9 @@ bool is_matrix_core(int32_t kernel) { return kernel == GQA_KERNEL_MFMA_QK || ker
 int32_t choose_kernel(const gqa_decode_desc_t* d) {
   const int32_t G = d->num_q_heads / d->num_kv_heads;
   const bool bf16 = d->kv_dtype == GQA_BF16 && d->qo_dtype == GQA_BF16;
-  if (d->kv_dtype == GQA_I8) {
+  if (quantized(d->kv_dtype)) {
+    // Fp8 codes are served by the G <= 16 kernel only (the planner refuses
+    // other shapes).
     // G <= 16 on the G <= 16 kernel (which quantizes a step's new rows itself),
     // 16 < G <= 64 on the large-group kernel (codes widened into its LDS tiles).
     // Int8 caches, G <= 64: the G <= 16 kernel (17..64 heads as 32-head chunks
@@ -116,7 +121,8 @@ gqa_status_t make_plan(const gqa_decode_desc_t* d, Plan* p, int64_t span = 0, bo
   p->kernel = generic ? GQA_KERNEL_GENERIC : choose_kernel(d);
   // Small head widths on short caches, no forced split: one wave per
   // (sequence, query head) with one slot per lane (latency-bound steps).
-  if (small && p->kernel == GQA_KERNEL_GENERIC && D <= 16 && d->capacity <= 512 && d->kv_dtype != GQA_I8 &&
+  if (d->kv_dtype == GQA_FP8 && p->kernel != GQA_KERNEL_MFMA_QK) return GQA_ERR_UNSUPPORTED;
+  if (small && p->kernel == GQA_KERNEL_GENERIC && D <= 16 && d->capacity <= 512 && !quantized(d->kv_dtype) &&
       d->num_splits <= 1) {
     p->kernel = GQA_KERNEL_SMALL;
     p->head_chunks = 1;
@@ -191,7 +197,7 @@ gqa_status_t make_plan(const gqa_decode_desc_t* d, Plan* p, int64_t span = 0, bo
   // Less where a kv-head's slots are strided (BSHD): there how fast a tile
   // streams depends on the kv-head, which the charge does not see, and larger
   // charges measured slower.
-  const bool i8 = d->kv_dtype == GQA_I8;
+  const bool i8 = quantized(d->kv_dtype);
   const int32_t cost = d->layout == GQA_LAYOUT_BHSD ? (i8 ? kBalancedCostI8 : kBalancedCostBf16)
                                                     : (i8 ? kBalancedCostI8Strided : kBalancedCostBf16Strided);
   int64_t units_max;
@@ -352,7 +358,7 @@ gqa_status_t check_attend_ptrs(const gqa_decode_desc_t* d, const gqa_cache_map_t
                                const int32_t* lengths, const void* out, const void* ws, size_t ws_bytes,
                                bool step) {
   const size_t ekv = elem_bytes(d->kv_dtype), eqo = elem_bytes(d->qo_dtype);
-  const size_t enew = d->kv_dtype == GQA_I8 ? eqo : ekv;  // int8 caches take new K/V as activations
+  const size_t enew = quantized(d->kv_dtype) ? eqo : ekv;  // quantized caches take new K/V as activations
   if (!q || !kc || !vc || !lengths || !out) return GQA_ERR_INVALID_ARGUMENT;
   if (step && (!kn || !vn)) return GQA_ERR_INVALID_ARGUMENT;
   if (!aligned(q, eqo) || !aligned(out, eqo) || !aligned(kc, ekv) || !aligned(vc, ekv) || !aligned(lengths, 4))
@@ -471,7 +477,7 @@ namespace {
 // without the last axis, mapped caches included) that overlap no other buffer
 // (`others`: the call's other spans).
 gqa_status_t check_scales(const gqa_decode_desc_t* d, const gqa_kv_scales_t* sc) {
-  if ((d->kv_dtype == GQA_I8) != (sc != nullptr)) return GQA_ERR_INVALID_ARGUMENT;
+  if (quantized(d->kv_dtype) != (sc != nullptr)) return GQA_ERR_INVALID_ARGUMENT;
   return GQA_OK;
 }
 gqa_status_t check_scale_ptrs(const gqa_decode_desc_t* d, const gqa_cache_map_t* map, const gqa_kv_scales_t* sc,
@@ -497,7 +503,7 @@ gqa_status_t check_rope(const gqa_decode_desc_t* d, const gqa_rope_t* r) {
   const bool gains = r->q_norm_gain != nullptr || r->k_norm_gain != nullptr;
   const bool eps = r->norm_eps >= 0.f && std::isfinite(r->norm_eps);
   if (gains != eps) return GQA_ERR_INVALID_ARGUMENT;
-  if (gains && d->kv_dtype == GQA_I8) return GQA_ERR_UNSUPPORTED;
+  if (gains && quantized(d->kv_dtype)) return GQA_ERR_UNSUPPORTED;
   int64_t t;
   if (!mul_ok(r->max_pos, d->head_dim, &t) || !mul_ok(t, 2, &t)) return GQA_ERR_UNSUPPORTED;
   return GQA_OK;

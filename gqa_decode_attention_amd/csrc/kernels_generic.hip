@@ -61,32 +61,41 @@ hipError_t launch_append(const AttnArgs& a, void* k_cache, void* v_cache, hipStr
 // dynamic-quantization formula): one wave per (b, kv-head); each new K and V
 // row (D <= 256 elements, in the query/output storage type) gets
 // scale = max|x| / 127 and codes round-half-even(x / scale), with correctly
-// rounded float32 divisions; a zero row stores scale 0 and codes 0.
+// rounded float32 divisions; a zero row stores scale 0 and codes 0.  Fp8
+// caches: scale = max|x| / 448 and codes the E4M3 value nearest to x / scale
+// clamped to [-448, 448] (e4m3_encode).
 // ---------------------------------------------------------------------------
 
 // One row held as elements d = lane + 64 i (i < 4, d < D) of a wave, quantized
-// into int8 codes at dst[off + d] and its scale at sdst[off / D].
-__device__ __forceinline__ void store_q8_row(const float (&x)[4], int lane, int D, int8_t* dst, float* sdst,
+// into one-byte codes (int8, or E4M3 when FP8) at dst[off + d] and its scale at
+// sdst[off / D].
+template <bool FP8>
+__device__ __forceinline__ void store_q8_row(const float (&x)[4], int lane, int D, uint8_t* dst, float* sdst,
                                              int64_t off) {
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(x[i]));  // lanes past D hold 0
   amax = wave_max(amax);
-  const float scale = amax / 127.0f;
+  constexpr float QMAX = FP8 ? 448.f : 127.f;
+  const float scale = amax / QMAX;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int d = lane + 64 * i;
     if (d < D) {
-      const float c = amax > 0.f ? fminf(fmaxf(rintf(x[i] / scale), -127.f), 127.f) : 0.f;
-      dst[off + d] = (int8_t)(int32_t)c;
+      if constexpr (FP8) {
+        dst[off + d] = (uint8_t)(amax > 0.f ? e4m3_encode(fminf(fmaxf(x[i] / scale, -QMAX), QMAX)) : 0u);
+      } else {
+        const float c = amax > 0.f ? fminf(fmaxf(rintf(x[i] / scale), -127.f), 127.f) : 0.f;
+        dst[off + d] = (uint8_t)(int32_t)c;
+      }
     }
   }
   if (lane == 0) sdst[off / D] = scale;
 }
 
 // One wave per (b, kv-head, K or V) row, four per workgroup.
-template <int NEW>
-__global__ __launch_bounds__(256) void append_q8_kernel(AttnArgs a, int8_t* __restrict__ kc, int8_t* __restrict__ vc) {
+template <int NEW, bool FP8>
+__global__ __launch_bounds__(256) void append_q8_kernel(AttnArgs a, uint8_t* __restrict__ kc, uint8_t* __restrict__ vc) {
   const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // 2 (b * Hkv + h) + which
   const int lane = threadIdx.x & 63;
   if (item >= 2 * (int64_t)a.B * a.Hkv) return;  // whole waves; no barrier follows
@@ -106,15 +115,19 @@ __global__ __launch_bounds__(256) void append_q8_kernel(AttnArgs a, int8_t* __re
     const int d = lane + 64 * i;
     x[i] = d < D ? Store<NEW>::load1_cached(src, row * D + d) : 0.f;
   }
-  store_q8_row(x, lane, D, which ? vc : kc, which ? a.v_scale_w : a.k_scale_w, off);
+  store_q8_row<FP8>(x, lane, D, which ? vc : kc, which ? a.v_scale_w : a.k_scale_w, off);
 }
 
 hipError_t launch_append_q8(const AttnArgs& a, void* k_cache, void* v_cache, hipStream_t s) {
   const unsigned blocks = (unsigned)((2 * (int64_t)a.B * a.Hkv + 3) / 4);
   AttnArgs arg = a;
   void* params[] = {&arg, &k_cache, &v_cache};
-  const void* fn = a.qo_dtype == GQA_F32 ? reinterpret_cast<const void*>(&append_q8_kernel<GQA_F32>)
-                                         : reinterpret_cast<const void*>(&append_q8_kernel<GQA_BF16>);
+  const bool fp8 = a.kv_dtype == GQA_FP8;
+  const void* fn = a.qo_dtype == GQA_F32
+                       ? (fp8 ? reinterpret_cast<const void*>(&append_q8_kernel<GQA_F32, true>)
+                              : reinterpret_cast<const void*>(&append_q8_kernel<GQA_F32, false>))
+                       : (fp8 ? reinterpret_cast<const void*>(&append_q8_kernel<GQA_BF16, true>)
+                              : reinterpret_cast<const void*>(&append_q8_kernel<GQA_BF16, false>));
   return hipLaunchKernel(fn, dim3(blocks), dim3(256), params, 0, s);
 }
 
@@ -141,7 +154,8 @@ __device__ __forceinline__ float rope_pair(bool first, float x, float xp, float 
 
 template <int KV, int QO>
 __global__ __launch_bounds__(256) void rope_append_kernel(AttnArgs a, void* __restrict__ kc, void* __restrict__ vc) {
-  constexpr int NEW = KV == GQA_I8 ? QO : KV;  // storage of k_new / v_new
+  constexpr bool QUANT = KV == GQA_I8 || KV == GQA_FP8;  // one-byte codes with row scales
+  constexpr int NEW = QUANT ? QO : KV;                    // storage of k_new / v_new
   const int nrows = 2 + (a.q_rot != nullptr ? a.G : 0);  // k, v, then the query heads
   const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= (int64_t)a.B * a.Hkv * nrows) return;     // whole waves; no barrier follows
@@ -163,7 +177,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(AttnArgs a, void* __re
     const bool isq = row >= 2;
     if (!isq && off < 0) return;               // the map names no valid slot: nothing appended
     const int64_t base = isq ? ((int64_t)b * a.Hq + (int64_t)h * a.G + (row - 2)) * D : (int64_t)bh * D;
-    if (isv && KV != GQA_I8) {
+    if (isv && !QUANT) {
       for (int d = lane; d < D; d += 64) {
         if constexpr (KV == GQA_BF16)
           reinterpret_cast<uint16_t*>(vc)[off + d] = reinterpret_cast<const uint16_t*>(a.v_new)[base + d];
@@ -229,8 +243,9 @@ __global__ __launch_bounds__(256) void rope_append_kernel(AttnArgs a, void* __re
         const int d = lane + 64 * i;
         if (d < D) Store<QO>::store1(a.q_rot, base + d, x[i]);
       }
-    } else if constexpr (KV == GQA_I8) {
-      store_q8_row(x, lane, D, reinterpret_cast<int8_t*>(isv ? vc : kc), isv ? a.v_scale_w : a.k_scale_w, off);
+    } else if constexpr (QUANT) {
+      store_q8_row<KV == GQA_FP8>(x, lane, D, reinterpret_cast<uint8_t*>(isv ? vc : kc),
+                                  isv ? a.v_scale_w : a.k_scale_w, off);
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -249,6 +264,9 @@ hipError_t launch_rope_append(const AttnArgs& a, void* k_cache, void* v_cache, h
   if (a.kv_dtype == GQA_I8)
     fn = f32 ? reinterpret_cast<const void*>(&rope_append_kernel<GQA_I8, GQA_F32>)
              : reinterpret_cast<const void*>(&rope_append_kernel<GQA_I8, GQA_BF16>);
+  else if (a.kv_dtype == GQA_FP8)
+    fn = f32 ? reinterpret_cast<const void*>(&rope_append_kernel<GQA_FP8, GQA_F32>)
+             : reinterpret_cast<const void*>(&rope_append_kernel<GQA_FP8, GQA_BF16>);
   else if (a.kv_dtype == GQA_BF16)
     fn = f32 ? reinterpret_cast<const void*>(&rope_append_kernel<GQA_BF16, GQA_F32>)
              : reinterpret_cast<const void*>(&rope_append_kernel<GQA_BF16, GQA_BF16>);
@@ -507,6 +525,7 @@ static hipError_t dispatch_generic(const AttnArgs& a, const Plan& p, int vec_pat
 }
 
 hipError_t launch_attend_generic(const AttnArgs& a, const Plan& p, int vec_path, hipStream_t s) {
+  if (a.kv_dtype == GQA_FP8) return hipErrorInvalidValue;  // fp8 caches: the matrix-core kernel only
   if (a.kv_dtype == GQA_I8)
     return a.qo_dtype == GQA_F32 ? dispatch_generic<GQA_I8, GQA_F32>(a, p, vec_path, s)
                                  : dispatch_generic<GQA_I8, GQA_BF16>(a, p, vec_path, s);
@@ -611,7 +630,7 @@ static const void* small_kernel(int D, bool mapped) {
 }
 
 hipError_t launch_attend_small(const AttnArgs& a, const Plan& p, hipStream_t s) {
-  if (a.D > 16 || a.kv_dtype == GQA_I8 || p.grid < 1) return hipErrorInvalidValue;
+  if (a.D > 16 || a.kv_dtype == GQA_I8 || a.kv_dtype == GQA_FP8 || p.grid < 1) return hipErrorInvalidValue;
   AttnArgs arg = a;
   void* params[] = {&arg};
   const bool mapped = a.map_kind != 0;

@@ -109,8 +109,8 @@ __device__ __forceinline__ u32x2_t load_nt8(const void* p) {
 }
 
 // One tile's loads.  bf16: k[kk] = A pieces of MFMA kk, v[i] = 16 bytes of slot
-// 4r + i.  int8: k[0..1] = 32 codes, v8[i] = 8 codes of slot 4r + i, ks / vs =
-// the scales of slot 4r + (c & 3).
+// 4r + i.  int8 or fp8 codes: k[0..1] = 32 codes, v[i] = 8 codes of slot
+// 4r + i, ks / vs = the scales of slot 4r + (c & 3).
 template <int KV>
 struct Tile;
 template <>
@@ -124,6 +124,19 @@ struct Tile<GQA_I8> {
   u32x2_t v[4];
   float ks, vs;
 };
+template <>
+struct Tile<GQA_FP8> : Tile<GQA_I8> {};  // fp8 codes: the same bytes, another code
+
+// Caches of one-byte codes with per-row scales (int8 or fp8).
+template <int KV>
+constexpr bool kQuant = KV != GQA_BF16;
+
+// Two fp8 (E4M3) codes, bytes 2 HI .. 2 HI + 1 of w, as a bf16 pair (exact:
+// every E4M3 value is a bf16 value; the conversion's scale is 1).
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
 
 // Online-softmax state of one wave: HB blocks of 16 query heads, each with its
 // running reference maximum m (log2 units), denominator l and the transposed
@@ -153,6 +166,14 @@ __device__ __forceinline__ void tile_math(State<HB>& st, const u32x4 (&qf)[HB][4
   if constexpr (KV == GQA_BF16) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) kf[kk] = t.k[kk];
+  } else if constexpr (KV == GQA_FP8) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t w0 = t.k[j][2 * h], w1 = t.k[j][2 * h + 1];
+        kf[2 * j + h] = u32x4{fp8x2_bf16<false>(w0), fp8x2_bf16<true>(w0), fp8x2_bf16<false>(w1), fp8x2_bf16<true>(w1)};
+      }
   } else {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -186,7 +207,7 @@ __device__ __forceinline__ void tile_math(State<HB>& st, const u32x4 (&qf)[HB][4
     for (int i = 0; i < 4; ++i) dead[i] = dead[i] || 4 * r + i < lo || 4 * r + i >= valid;
   }
   float ksc[4], vsc[4];
-  if constexpr (KV == GQA_I8) {
+  if constexpr (kQuant<KV>) {
     ksc[0] = quad_bcast<0>(t.ks);
     ksc[1] = quad_bcast<1>(t.ks);
     ksc[2] = quad_bcast<2>(t.ks);
@@ -200,7 +221,7 @@ __device__ __forceinline__ void tile_math(State<HB>& st, const u32x4 (&qf)[HB][4
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
     float* sc = sv[hb];
-    if constexpr (KV == GQA_I8) {
+    if constexpr (kQuant<KV>) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) sc[i] *= ksc[i];
     }
@@ -233,7 +254,7 @@ __device__ __forceinline__ void tile_math(State<HB>& st, const u32x4 (&qf)[HB][4
 #pragma unroll
     for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(sc[i], scale_log2, nm));
     st.l[hb] += (p[0] + p[1]) + (p[2] + p[3]);
-    if constexpr (KV == GQA_I8) {
+    if constexpr (kQuant<KV>) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) p[i] *= vsc[i];
     }
@@ -247,11 +268,32 @@ __device__ __forceinline__ void tile_math(State<HB>& st, const u32x4 (&qf)[HB][4
                    pk_bf16(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23))};
   }
   // V sum: A operand of MFMA e = element 8c + e of slots 4r .. 4r + 3 (twice),
-  // shared by the head blocks.
+  // shared by the head blocks.  fp8: one byte permutation gathers element
+  // pairs e, e + 1 of two slots, one conversion each turns them into bf16
+  // pairs (vb[e][0]: slots 0 and 1, vb[e][1]: slots 2 and 3).
+  uint32_t vb[8][2];
+  if constexpr (KV == GQA_FP8) {
+#pragma unroll
+    for (int wd = 0; wd < 2; ++wd)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        constexpr uint32_t sel0 = 0x05010400u, sel1 = 0x07030602u;  // bytes {2k, 4+2k, 2k+1, 4+2k+1}
+        const uint32_t sel = k == 0 ? sel0 : sel1;
+        const uint32_t p01 = __builtin_amdgcn_perm(t.v[1][wd], t.v[0][wd], sel);
+        const uint32_t p23 = __builtin_amdgcn_perm(t.v[3][wd], t.v[2][wd], sel);
+        const int e0 = 4 * wd + 2 * k;
+        vb[e0][0] = fp8x2_bf16<false>(p01);
+        vb[e0 + 1][0] = fp8x2_bf16<true>(p01);
+        vb[e0][1] = fp8x2_bf16<false>(p23);
+        vb[e0 + 1][1] = fp8x2_bf16<true>(p23);
+      }
+  }
   unroll<0, 8>([&](auto ei) {
     constexpr int e = decltype(ei)::value;
     u32x2_t va;
-    if constexpr (KV == GQA_BF16) {
+    if constexpr (KV == GQA_FP8) {
+      va = u32x2_t{vb[e][0], vb[e][1]};
+    } else if constexpr (KV == GQA_BF16) {
       constexpr uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
       va = u32x2_t{__builtin_amdgcn_perm(t.v[1][e >> 1], t.v[0][e >> 1], sel),
                    __builtin_amdgcn_perm(t.v[3][e >> 1], t.v[2][e >> 1], sel)};
@@ -410,7 +452,7 @@ __device__ __forceinline__ void attend_piece(const AttnArgs& a, const Piece& pc,
       else
         t.v[i] = load_nt8(vt + (uint64_t)rv * rsb);
     }
-    if constexpr (KV == GQA_I8) {
+    if constexpr (kQuant<KV>) {
       const int64_t rsc = sb + (int64_t)row(t0 + 4 * r + (c & 3)) * sst;
       t.ks = __uint_as_float(load_nt4(a.k_scale + rsc));
       t.vs = __uint_as_float(load_nt4(a.v_scale + rsc));
@@ -436,7 +478,7 @@ __device__ __forceinline__ void attend_piece(const AttnArgs& a, const Piece& pc,
       for (int i = 1; i < 4; ++i) tn.v[i] = u32x4{0, 0, 0, 0};
     }
   } else {
-    // Int8 caches: the new rows (bf16 activations) are quantized here by the
+    // Int8 (and fp8) caches: the new rows (bf16 activations) are quantized here by the
     // per-row rule (float32 row maximum, scale = max / 127 and codes =
     // round-half-even(x / scale) with correctly rounded divisions, clamped to
     // +-127; a zero row has scale 0 and codes 0).  Lane l quantizes elements
@@ -451,10 +493,17 @@ __device__ __forceinline__ void attend_piece(const AttnArgs& a, const Piece& pc,
       const float k0 = bf16_lo(kp), k1 = bf16_hi(kp), v0 = bf16_lo(vp), v1 = bf16_hi(vp);
       const float kmax = wave_max(fmaxf(fabsf(k0), fabsf(k1)));
       const float vmax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
-      const float ksc = kmax / 127.0f, vsc = vmax / 127.0f;
+      // fp8 caches: the same rule with the code's largest value, 448, and the
+      // E4M3 code of the clamped quotient (ties to even).
+      constexpr float QMAX = KV == GQA_FP8 ? 448.f : 127.f;
+      const float ksc = kmax / QMAX, vsc = vmax / QMAX;
       auto code = [](float x, float amax, float sc) -> uint32_t {
-        const float q = amax > 0.f ? fminf(fmaxf(rintf(x / sc), -127.f), 127.f) : 0.f;
-        return (uint32_t)(int32_t)q & 0xffu;
+        if constexpr (KV == GQA_FP8) {
+          return amax > 0.f ? e4m3_encode(fminf(fmaxf(x / sc, -QMAX), QMAX)) : 0u;
+        } else {
+          const float q = amax > 0.f ? fminf(fmaxf(rintf(x / sc), -127.f), 127.f) : 0.f;
+          return (uint32_t)(int32_t)q & 0xffu;
+        }
       };
       uint16_t* xb = reinterpret_cast<uint16_t*>(&sm_o[wave][0][0]);  // key codes at bytes 0..127, values 128..255
       xb[lane] = (uint16_t)(code(k0, kmax, ksc) | (code(k1, kmax, ksc) << 8));
@@ -758,6 +807,12 @@ static const void* qk_kernel(const AttnArgs& a, bool var) {
   if (a.kv_dtype == GQA_I8)
     return var ? reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_I8, NW, HB, HP, false, true>)
                : reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_I8, NW, HB, HP, false, false>);
+  if (a.kv_dtype == GQA_FP8 && a.map_kind == GQA_MAP_PAGED)
+    return var ? reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_FP8, NW, HB, HP, true, true>)
+               : reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_FP8, NW, HB, HP, true, false>);
+  if (a.kv_dtype == GQA_FP8)
+    return var ? reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_FP8, NW, HB, HP, false, true>)
+               : reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_FP8, NW, HB, HP, false, false>);
   if (HB == 1 && a.map_kind == GQA_MAP_PAGED)
     return var ? reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_BF16, NW, HB, HP, true, true>)
                : reinterpret_cast<const void*>(&attend_mfma_qkv_kernel<GQA_BF16, NW, HB, HP, true, false>);
@@ -782,7 +837,7 @@ hipError_t launch_attend_mfma_qk(const AttnArgs& a, const Plan& p, hipStream_t s
   if (a.D != qkv::kDq || a.G > 16 * HB * a.head_chunks || p.block != 64 * NW) return hipErrorInvalidValue;
   if (a.hp != 1 && (a.hp != NW || HB != 1 || a.Hkv % a.hp != 0)) return hipErrorInvalidValue;
   const bool var = a.window > 0 || a.cap_T > 0.f;  // in-loop variants (the sink is applied at the end)
-  if (a.kv_dtype == GQA_I8 &&
+  if ((a.kv_dtype == GQA_I8 || a.kv_dtype == GQA_FP8) &&
       (a.k_scale == nullptr || a.v_scale == nullptr || a.qo_dtype != GQA_BF16 ||
        (a.k_new != nullptr && (a.k_cache_w == nullptr || a.k_scale_w == nullptr || a.v_scale_w == nullptr))))
     return hipErrorInvalidValue;

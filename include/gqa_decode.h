@@ -70,7 +70,13 @@ typedef enum {
   GQA_ERR_INTERNAL = 5             /* unexpected library error (no C++ exception crosses)       */
 } gqa_status_t;
 
-enum { GQA_F32 = 0, GQA_BF16 = 1, GQA_I8 = 2 /* int8 codes with per-row scales: the _q8 calls only */ };
+enum {
+  GQA_F32 = 0,
+  GQA_BF16 = 1,
+  GQA_I8 = 2,  /* int8 codes with per-row scales: the _q8 calls (and _ex with scales) only            */
+  GQA_FP8 = 3  /* OCP E4M3 codes with per-row scales: as GQA_I8; head_dim 128, bf16 q/out and
+                  Hq/Hkv <= 64 only (GQA_ERR_UNSUPPORTED otherwise)                                    */
+};
 enum {
   GQA_LAYOUT_BHSD = 0,  /* caches (B, Hkv, S, D): KV cache decode step page            */
   GQA_LAYOUT_BSHD = 1   /* caches (B, S, Hkv, D): JAX Grouped-Query Decode Step page   */
@@ -86,7 +92,8 @@ typedef struct {
   int32_t capacity;     /* S >= 1 slots per (sequence, kv-head) in both caches              */
   int32_t layout;       /* GQA_LAYOUT_BHSD or GQA_LAYOUT_BSHD, shared by both caches         */
   int32_t kv_dtype;     /* storage of k_cache, v_cache, k_new, v_new: GQA_F32 or GQA_BF16
-                           (GQA_I8 for the _q8 calls, whose k_new/v_new are in qo_dtype)    */
+                           (GQA_I8 or GQA_FP8 for the _q8 calls, whose k_new/v_new are in
+                           qo_dtype)                                                          */
   int32_t qo_dtype;     /* storage of q and out: GQA_F32 or GQA_BF16                         */
   int32_t num_splits;   /* 0 = library's choice; n > 0 asks for n splits of the token axis
                            (the plan uses at most 64, and fewer when n would leave a split
@@ -272,9 +279,19 @@ gqa_status_t gqa_decode_step_mapped(const gqa_decode_desc_t* desc, const gqa_cac
  *                      scale = max|x| / 127 and code = round-half-even(x / scale)
  *                      with correctly rounded float32 divisions (a zero row has
  *                      scale 0 and codes 0).
+ * desc->kv_dtype = GQA_FP8: the caches hold 8-bit floating-point codes in the
+ * OCP E4M3 format (sign, 4 exponent bits with bias 7, 3 mantissa bits,
+ * subnormals, largest finite magnitude 448; the pages define no fp8 format, so
+ * the rule above is taken over with the code's largest value): scale =
+ * max|x| / 448 and code = the E4M3 value nearest to x / scale clamped to
+ * [-448, 448] (ties to even, the quotient's sign kept), correctly rounded
+ * float32 divisions, a zero row with scale 0 and codes 0; a value reads as
+ * decoded code * scale.  Served for head_dim 128, bf16 q/out and
+ * num_q_heads / num_kv_heads <= 64 (GQA_ERR_UNSUPPORTED otherwise; the append
+ * alone takes any shape).
  * Other arguments, contracts and errors as in the unquantized calls; the
- * unquantized calls refuse GQA_I8 (GQA_ERR_INVALID_ARGUMENT).  Scale arrays must
- * be 4-byte aligned and overlap no other argument.
+ * unquantized calls refuse GQA_I8 and GQA_FP8 (GQA_ERR_INVALID_ARGUMENT).
+ * Scale arrays must be 4-byte aligned and overlap no other argument.
  * ------------------------------------------------------------------------- */
 typedef struct {
   float* k_scale;

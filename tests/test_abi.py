@@ -94,6 +94,28 @@ def test_bad_descriptor_rejected_everywhere(kw, status):
     assert L.gqa_decode_append(ctypes.byref(d), ptrs[1], ptrs[2], ptrs[6], ptrs[7], ptrs[3], None) == status
 
 
+def test_fp8_caches_plan_the_matrix_core_kernel_or_are_refused():
+    """fp8 (E4M3) caches run on the small-group matrix-core kernel (head width
+    128, bf16 q/out, up to 64 query heads per kv-head, dense or mapped with
+    16-slot blocks); any other shape is refused with UNSUPPORTED before anything
+    is enqueued, and the plain (unquantized) calls refuse the type outright."""
+    L = g.lib()
+    for kw in (dict(), dict(num_q_heads=64, num_kv_heads=1), dict(layout="BSHD", num_q_heads=32, num_kv_heads=8),
+               dict(num_q_heads=48, num_kv_heads=2, num_splits=3)):
+        p = g.get_plan(desc(kv_dtype=g.FP8, **kw))
+        assert p["kernel"] == "mfma_qk", (kw, p)
+    for kw in (dict(head_dim=64), dict(qo_dtype=g.F32), dict(num_q_heads=80, num_kv_heads=1)):
+        d = desc(kv_dtype=g.FP8, **kw)
+        pt = _lib.PlanT()
+        assert L.gqa_decode_get_plan(ctypes.byref(d), ctypes.byref(pt)) == UNSUPPORTED, kw
+        n = ctypes.c_size_t(7)
+        assert L.gqa_decode_workspace_size(ctypes.byref(d), ctypes.byref(n)) == UNSUPPORTED and n.value == 7
+    d = desc(kv_dtype=g.FP8)
+    ptrs = [FAKE + i * GAP for i in range(8)]
+    assert L.gqa_decode_attend(ctypes.byref(d), ptrs[0], ptrs[1], ptrs[2], ptrs[3], ptrs[4], ptrs[5], 1 << 30,
+                               None) == INVALID       # no scales: the plain call refuses quantized caches
+
+
 def test_null_desc_and_null_outputs():
     L = g.lib()
     assert L.gqa_decode_workspace_size(None, ctypes.byref(ctypes.c_size_t())) == INVALID

@@ -46,6 +46,8 @@ CASES = {
     "mfma_all_g32_keys3": (2, 64, 2, 1600, "BSHD", "bf16", "bf16", 3, 3.0, [1600, 900], "mfma_all"),
     "mfma_qk_g64_int8": (2, 64, 1, 1800, "BHSD", "i8", "bf16", 3, 1.0, [1800, 1100], "mfma_qk"),
     "mfma_qk_g24_int8_bshd": (2, 48, 2, 1500, "BSHD", "i8", "bf16", 3, 1.0, [1500, 900], "mfma_qk"),
+    "mfma_qk_g8_fp8": (2, 32, 4, 1700, "BHSD", "fp8", "bf16", 3, 1.0, [1700, 1200], "mfma_qk"),
+    "mfma_qk_g16_fp8_bshd_four_heads": (2, 64, 4, 1500, "BSHD", "fp8", "bf16", 3, 1.0, [1500, 700], "mfma_qk"),
     "mfma_qk_g4_bshd_four_heads": (2, 32, 8, 1900, "BSHD", "bf16", "bf16", 3, 1.0, [1900, 1000], "mfma_qk"),
     "mfma_qk_g16_int8_bshd_four_heads": (2, 64, 4, 1500, "BSHD", "i8", "bf16", 3, 1.0, [1500, 700], "mfma_qk"),
     "generic_bf16_caches_f32_out": (2, 16, 4, 1500, "BHSD", "bf16", "f32", 3, 1.0, [1500, 800], "generic"),
@@ -58,7 +60,7 @@ def test_split_partials_are_float32_accurate(g, case):
     D = 128
     w = W.custom(B, Hq, Hkv, D, S, lay, kv, qo, seed=400 + Hq + S, key_scale=ks)
     n = torch.tensor(n_att, dtype=torch.int32)
-    code = {"bf16": g.BF16, "f32": g.F32, "i8": g.I8}
+    code = {"bf16": g.BF16, "f32": g.F32, "i8": g.I8, "fp8": g.FP8}
     desc = g.make_desc(B, Hq, Hkv, D, S, lay, code[kv], code[qo], ns)
     plan = g.get_plan(desc)
     print(f"partials {case}: plan {plan}", flush=True)
@@ -66,7 +68,7 @@ def test_split_partials_are_float32_accurate(g, case):
     assert plan["heads_per_item"] == (4 if case.endswith("four_heads") else 1)
     st = plan["split_tokens"]
     ws = torch.full((plan["workspace_bytes"],), 0xFF, dtype=torch.uint8, device=DEV)
-    if kv == "i8":
+    if kv in ("i8", "fp8"):
         inp = W.make_q8(w, DEV, lengths=n)
         g.attend_q8(inp["q"], inp["k_cache"], inp["v_cache"], inp["k_scale"], inp["v_scale"], inp["lengths"],
                     layout=lay, workspace=ws, num_splits=ns)
@@ -93,10 +95,10 @@ def test_split_partials_are_float32_accurate(g, case):
             idx = (lambda j0, j1: (b, h, slice(j0, j1))) if lay == "BHSD" else (lambda j0, j1: (b, slice(j0, j1), h))
             for s in range(nact):
                 t0, t1 = s * st, min((s + 1) * st, nb)
-                if kv == "i8":
+                if kv in ("i8", "fp8"):
                     sl = idx(t0, t1)
-                    K = oracle.dequantize(inp["k_cache"][sl].cpu().numpy(), inp["k_scale"][sl].cpu().numpy())
-                    V = oracle.dequantize(inp["v_cache"][sl].cpu().numpy(), inp["v_scale"][sl].cpu().numpy())
+                    K = oracle.dequantize(W.to_numpy_storage(inp["k_cache"][sl]), inp["k_scale"][sl].cpu().numpy())
+                    V = oracle.dequantize(W.to_numpy_storage(inp["v_cache"][sl]), inp["v_scale"][sl].cpu().numpy())
                 else:
                     K = oracle.decode(W.to_numpy_storage(inp["k_cache"][idx(t0, t1)]), kv)
                     V = oracle.decode(W.to_numpy_storage(inp["v_cache"][idx(t0, t1)]), kv)

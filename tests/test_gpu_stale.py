@@ -13,8 +13,9 @@ forced splits, attend, four kv-heads per workgroup on BSHD caches; int8
 caches with two 16-head blocks per wave), the
 large-group matrix-core kernel (G = 24 and 64), the generic vector kernel
 (float32 and bf16 storage, D = 64 and G = 80), the small-head-width kernel
-(D = 4 and 16), the balanced mode, and paged / slot-indexed caches.  Int8 codes cannot hold NaN: there
-the refill puts NaN in the stale slots' scales and -127 in their codes.
+(D = 4 and 16), the balanced mode, and paged / slot-indexed caches, int8 and fp8 caches.  Int8 codes cannot hold NaN:
+there the refill puts NaN in the stale slots' scales and -127 in their codes;
+fp8 refills put NaN in both (the E4M3 NaN code 0x7F).
 """
 import pytest
 import torch
@@ -59,17 +60,28 @@ CASES = {
     "small_bf16_d16_paged5": (3, 8, 2, 16, 200, "BSHD", "bf16", "bf16", 0, "paged", 5, "small", False),
     "mfma_qk_g32_two_blocks_int8": (3, 64, 2, 128, 900, "BHSD", "i8", "bf16", 0, None, 0, "mfma_qk", False),
     "mfma_qk_g64_two_blocks_int8": (2, 64, 1, 128, 1100, "BSHD", "i8", "bf16", 3, None, 0, "mfma_qk", False),
+    "mfma_qk_fp8_bhsd": (3, 32, 8, 128, 900, "BHSD", "fp8", "bf16", 0, None, 0, "mfma_qk", False),
+    "mfma_qk_fp8_bshd_four_heads_splits3": (3, 32, 8, 128, 900, "BSHD", "fp8", "bf16", 3, None, 0, "mfma_qk", False),
+    "mfma_qk_fp8_g64_two_blocks": (2, 64, 1, 128, 1100, "BHSD", "fp8", "bf16", 0, None, 0, "mfma_qk", False),
+    "paged16_fp8": (3, 32, 8, 128, 800, "BHSD", "fp8", "bf16", 0, "paged", 16, "mfma_qk", False),
 }
 
 
 def refill(inp, w, n_att):
     """Copies of the caches with every slot j >= n_att[b] set to NaN (K) / +Inf (V);
-    int8 caches: NaN scales and codes of -127 there."""
+    int8 caches: NaN scales and codes of -127 there; fp8 caches: NaN scales and NaN codes."""
     slot = torch.arange(w.capacity, device=DEV)
     stale = slot[None, :] >= n_att.to(DEV).long()[:, None]
     row = stale[:, None, :] if w.layout == "BHSD" else stale[:, :, None]   # the scales' shape
     stale = row[..., None]                                                 # the caches' shape
     out = dict(inp)
+    if w.kv_dtype == "fp8":
+        for name in ("k_cache", "v_cache"):
+            c = inp[name].view(torch.uint8)
+            out[name] = torch.where(stale, torch.tensor(0x7F, dtype=torch.uint8, device=DEV), c).view(torch.float8_e4m3fn)
+        for name in ("k_scale", "v_scale"):
+            out[name] = torch.where(row, torch.tensor(float("nan"), device=DEV), inp[name])
+        return out
     if w.kv_dtype == "i8":
         for name in ("k_cache", "v_cache"):
             out[name] = torch.where(stale, torch.tensor(-127, dtype=torch.int8, device=DEV), inp[name])
@@ -92,35 +104,41 @@ def same_bits(a, b):
 @pytest.mark.parametrize("call", ["step", "attend"])
 def test_stale_slots_never_loaded(g, case, call):
     B, Hq, Hkv, D, S, lay, kv, qo, ns, kind, bs, kernel, balanced = CASES[case]
-    w = W.custom(B, Hq, Hkv, D, S, lay, kv, qo, seed=300 + B + Hq, stale="none" if kv == "i8" else "pm:1000")
+    quant = kv in ("i8", "fp8")
+    w = W.custom(B, Hq, Hkv, D, S, lay, kv, qo, seed=300 + B + Hq, stale="none" if quant else "pm:1000")
     L = torch.randint(0, S, (B,), generator=torch.Generator().manual_seed(S + B), dtype=torch.int32)
     L[0] = S - 1 if call == "step" else S
     L[1] = 0 if call == "step" else 1
     if call == "attend":
         L = L.clamp(min=1)
-    code = {"f32": g.F32, "bf16": g.BF16, "i8": g.I8}
+    code = {"f32": g.F32, "bf16": g.BF16, "i8": g.I8, "fp8": g.FP8}
     desc = g.make_desc(B, Hq, Hkv, D, S, lay, code[kv], code[qo], ns)
     plan = g.get_plan(desc)
     print(f"stale refill {case} {call}: plan {plan}", flush=True)
     assert plan["kernel"] == kernel and plan["balanced"] == balanced
     n_att = L + 1 if call == "step" else L
-    base = W.make_q8(w, DEV, lengths=L) if kv == "i8" else W.make_inputs(w, DEV, lengths=L)
+    base = W.make_q8(w, DEV, lengths=L) if quant else W.make_inputs(w, DEV, lengths=L)
     runs = []
     for inp in (base, refill(base, w, n_att)):
         inp = {k: v.clone() for k, v in inp.items()}
         if kind is not None:
             m = W.make_mapped(inp, w, kind, block_size=bs or 16)    # same seed: the same table both times
             kc, vc, table = m["k_cache"], m["v_cache"], m["map"]
-            if call == "step":
+            if quant:
+                sc = dict(k_scale=m["k_scale"], v_scale=m["v_scale"], table=table, kind=kind, table_host=table.cpu(),
+                          layout=lay, num_splits=ns)
+                out = (g.step_ex(inp["q"], kc, vc, inp["k_new"], inp["v_new"], inp["lengths"], **sc) if call == "step"
+                       else g.attend_ex(inp["q"], kc, vc, inp["lengths"], **sc))
+            elif call == "step":
                 out = g.step_mapped(inp["q"], kc, vc, inp["k_new"], inp["v_new"], inp["lengths"], table, kind=kind,
                                     layout=lay, num_splits=ns)
             else:
                 out = g.attend_mapped(inp["q"], kc, vc, inp["lengths"], table, kind=kind, layout=lay,
                                       num_splits=ns)
-        elif kv == "i8" and call == "step":
+        elif quant and call == "step":
             out = g.step_q8(inp["q"], inp["k_cache"], inp["v_cache"], inp["k_scale"], inp["v_scale"], inp["k_new"],
                             inp["v_new"], inp["lengths"], layout=lay, num_splits=ns)
-        elif kv == "i8":
+        elif quant:
             out = g.attend_q8(inp["q"], inp["k_cache"], inp["v_cache"], inp["k_scale"], inp["v_scale"],
                               inp["lengths"], layout=lay, num_splits=ns)
         elif call == "step":

@@ -37,7 +37,7 @@ class Workload:
     D: int
     capacity: int
     layout: str            # "BHSD" = (B, Hkv, S, D); "BSHD" = (B, S, Hkv, D)
-    kv_dtype: str          # "f32" | "bf16" | "i8" (int8 codes + per-row scales: make_q8)
+    kv_dtype: str          # "f32" | "bf16" | "i8" / "fp8" (int8 / E4M3 codes + per-row scales: make_q8)
     qo_dtype: str          # "f32" | "bf16"
     len_lo: int            # pre-append length range, inclusive
     len_hi: int
@@ -144,6 +144,8 @@ def make_mapped(inp: dict, w: Workload, kind: str, *, block_size: int = 16, num_
     def garbage(shape, like):
         if like.dtype == torch.int8:
             return torch.full(shape, 127, dtype=torch.int8, device=dev)
+        if like.dtype == torch.float8_e4m3fn:       # the E4M3 NaN pattern
+            return torch.full(shape, 0x7F, dtype=torch.uint8, device=dev).view(torch.float8_e4m3fn)
         if like.dtype == torch.bfloat16:
             return torch.full(shape, 0x7FC1, dtype=torch.int16, device=dev).view(torch.bfloat16)
         return torch.full(shape, 0x7FC00001, dtype=torch.int32, device=dev).view(torch.float32)
@@ -192,12 +194,15 @@ def make_mapped(inp: dict, w: Workload, kind: str, *, block_size: int = 16, num_
 
 
 def make_q8(w: Workload, device="cpu", lengths: torch.Tensor | None = None) -> dict:
-    """Seeded inputs for int8 caches with per-row float32 scales.
+    """Seeded inputs for int8 (``w.kv_dtype == "i8"``) or fp8 (``"fp8"``, E4M3
+    codes as torch.float8_e4m3fn) caches with per-row float32 scales.
 
-    The caches hold int8 codes drawn uniformly from [-127, 127] and the scales
-    are drawn uniformly from [0.5, 1.5] * 3 * key_scale / 127 (keys) or
+    Int8 caches hold codes drawn uniformly from [-127, 127] and the scales are
+    drawn uniformly from [0.5, 1.5] * 3 * key_scale / 127 (keys) or
     [0.5, 1.5] * 3 / 127 (values), so cached values span about +-3 like the
-    normal draws of ``make_inputs``.  q and the new key/value rows are normal
+    normal draws of ``make_inputs``.  Fp8 caches hold bytes drawn uniformly
+    over all codes, the two NaN patterns replaced by +-0 (so every finite code,
+    subnormals included, occurs), with 448 in place of 127 in the scales.  q and the new key/value rows are normal
     draws stored as ``w.qo_dtype`` (the step quantizes the new rows itself).
     With ``w.stale != "none"`` the scales of slots >= lengths[b] are NaN, so a
     read past the valid slots shows up in the output.  Draw order (one
@@ -216,10 +221,19 @@ def make_q8(w: Workload, device="cpu", lengths: torch.Tensor | None = None) -> d
         return x.mul_(scale) if scale != 1.0 else x
 
     q = randn((w.B, w.Hq, w.D)).to(qot)
-    k_cache = torch.randint(-127, 128, shape, generator=g, device=device, dtype=torch.int8)
-    v_cache = torch.randint(-127, 128, shape, generator=g, device=device, dtype=torch.int8)
-    k_scale = (torch.rand(sshape, generator=g, device=device) + 0.5).mul_(3.0 * w.key_scale / 127)
-    v_scale = (torch.rand(sshape, generator=g, device=device) + 0.5).mul_(3.0 / 127)
+    fp8 = w.kv_dtype == "fp8"
+    if fp8:
+        def codes():
+            c = torch.randint(0, 256, shape, generator=g, device=device, dtype=torch.int32)
+            c = torch.where((c & 0x7F) == 0x7F, c & 0x80, c)           # NaN patterns -> +-0
+            return c.to(torch.uint8).view(torch.float8_e4m3fn)
+        k_cache, v_cache = codes(), codes()
+    else:
+        k_cache = torch.randint(-127, 128, shape, generator=g, device=device, dtype=torch.int8)
+        v_cache = torch.randint(-127, 128, shape, generator=g, device=device, dtype=torch.int8)
+    qmax = 448.0 if fp8 else 127.0
+    k_scale = (torch.rand(sshape, generator=g, device=device) + 0.5).mul_(3.0 * w.key_scale / qmax)
+    v_scale = (torch.rand(sshape, generator=g, device=device) + 0.5).mul_(3.0 / qmax)
     k_new = randn((w.B, w.Hkv, w.D), w.key_scale).to(qot)
     v_new = randn((w.B, w.Hkv, w.D)).to(qot)
     if w.stale != "none":
@@ -233,10 +247,13 @@ def make_q8(w: Workload, device="cpu", lengths: torch.Tensor | None = None) -> d
 
 
 def to_numpy_storage(t: torch.Tensor) -> np.ndarray:
-    """A tensor's stored bits as the oracle takes them: float32, int8, or uint16 bf16 patterns."""
+    """A tensor's stored bits as the oracle takes them: float32, int8, uint16 bf16
+    patterns, or uint8 E4M3 patterns."""
     t = t.detach().cpu().contiguous()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy()
     if t.dtype in (torch.float32, torch.int8):
         return t.numpy()
     raise TypeError(f"unsupported dtype {t.dtype}")
@@ -244,7 +261,7 @@ def to_numpy_storage(t: torch.Tensor) -> np.ndarray:
 
 def algorithmic_bytes(w: Workload, lengths, window: int = 0, prefix: int = 0) -> int:
     """Bytes one step must move at minimum: valid K+V read (the new token
-    included), Q read, new K/V write, output write.  Int8 caches ("i8") move a
+    included), Q read, new K/V write, output write.  Int8 and fp8 caches move a
     float32 scale with every row and take the new rows in the q/out dtype.  A
     sliding window (with a kept prefix) reads only the slots it attends."""
     e_qo = 4 if w.qo_dtype == "f32" else 2
@@ -252,7 +269,7 @@ def algorithmic_bytes(w: Workload, lengths, window: int = 0, prefix: int = 0) ->
     if window > 0:
         wv = np.minimum(n, window)
         n = wv + np.minimum(prefix, n - wv)
-    if w.kv_dtype == "i8":
+    if w.kv_dtype in ("i8", "fp8"):
         row = w.D + 4
         kv_read = int(n.sum()) * w.Hkv * row * 2
         return kv_read + 2 * w.B * w.Hq * w.D * e_qo + 2 * w.B * w.Hkv * (w.D * e_qo + row)
