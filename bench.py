@@ -74,7 +74,7 @@ def cpu_baseline(w, inp, budget_s=12.0, rope=None, variants=None, window=0, pref
     except Exception:  # pragma: no cover
         threads = 1
     L = inp["lengths"].cpu().numpy()
-    q8 = w.kv_dtype == "i8"
+    q8 = w.kv_dtype in ("i8", "fp8")
     names = ("q", "k_cache", "v_cache", "k_new", "v_new") + (("k_scale", "v_scale") if q8 else ())
 
     def host(nb):
@@ -210,9 +210,9 @@ def main():
     ap.add_argument("--cache", default="dense",
                     help="dense (default), slots (slot-indexed rows), pagedN (pool of N-slot blocks in a "
                          "seeded random order) or pagedNseq (blocks in pool order)")
-    ap.add_argument("--kv", default="native", choices=["native", "int8"],
-                    help="native: the workload's cache dtype; int8: int8 codes with per-row float32 scales "
-                         "(the step quantizes the new rows)")
+    ap.add_argument("--kv", default="native", choices=["native", "int8", "fp8"],
+                    help="native: the workload's cache dtype; int8 / fp8: int8 or fp8 (E4M3) codes with "
+                         "per-row float32 scales (the step quantizes the new rows)")
     ap.add_argument("--rope", default="none", choices=["none", "half", "interleaved"],
                     help="rotate q and the new key with rotary planes in the append (positions = lengths)")
     ap.add_argument("--window", type=int, default=0, help="sliding window of the softmax (0: none)")
@@ -245,11 +245,11 @@ def main():
     g.lib()
     w = W.WORKLOADS[args.workload]
     dev = "cuda"
-    q8 = args.kv == "int8"
+    q8 = args.kv in ("int8", "fp8")
     if q8:
         if args.cache != "dense":
-            raise SystemExit("--kv int8 takes dense caches")
-        w = W.Workload(**{**w.__dict__, "kv_dtype": "i8"})
+            raise SystemExit("--kv int8/fp8 takes dense caches")
+        w = W.Workload(**{**w.__dict__, "kv_dtype": "i8" if args.kv == "int8" else "fp8"})
         inp = W.make_q8(w, dev)
     else:
         inp = W.make_inputs(w, dev)
@@ -362,7 +362,7 @@ def main():
         cpu = cpu_baseline(w, inp_dense, rope=rope_np, variants=smx_np, window=args.window,
                            prefix=args.kept_prefix)   # the dense oracle on the same logical caches
 
-    kv = {"bf16": "bf16", "f32": "f32", "i8": "i8+f32 row scales"}[w.kv_dtype]
+    kv = {"bf16": "bf16", "f32": "f32", "i8": "i8+f32 row scales", "fp8": "fp8 e4m3+f32 row scales"}[w.kv_dtype]
     line = {
         "metric": METRIC,
         "value": round(gbs, 2),

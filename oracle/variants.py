@@ -84,7 +84,7 @@ def attend_variants(q, q_dtype: str, k_cache, v_cache, kv_dtype: str, lengths, l
                     prefix=0, kind: str | None = None, mapping=None, bs=None, scales=None) -> np.ndarray:
     """Length-masked GQA attention with the variants, float64 (B, Hq, D).
     ``prefix`` is one value or one per sequence; ``kind``/``mapping``/``bs``
-    select a mapped cache as in ``oracle.mapped``; ``kv_dtype`` "i8" takes
+    select a mapped cache as in ``oracle.mapped``; ``kv_dtype`` "i8" (or "fp8") takes
     int8 caches read as code * row scale with ``scales = (k_scale, v_scale)``
     (``oracle.quant`` storage)."""
     B, Hq, D = q.shape
@@ -106,7 +106,7 @@ def attend_variants(q, q_dtype: str, k_cache, v_cache, kv_dtype: str, lengths, l
             else:
                 Kr = mapped_rows(k_cache, kind, layout, mapping, b, h, n, bs)
                 Vr = mapped_rows(v_cache, kind, layout, mapping, b, h, n, bs)
-            if kv_dtype == "i8":
+            if kv_dtype in ("i8", "fp8"):
                 K = dequantize(Kr, _scale_rows(scales[0], layout, b, h, n))[idx]
                 V = dequantize(Vr, _scale_rows(scales[1], layout, b, h, n))[idx]
             else:
@@ -121,12 +121,12 @@ def step_variants(q, q_dtype: str, k_cache, v_cache, k_new, v_new, kv_dtype: str
                   **variants):
     """Append at ``lengths[b]``, then attend with the variants over
     ``lengths[b] + 1`` slots.  Returns (out, k_cache_after, v_cache_after);
-    int8 caches ("i8", new rows in ``q_dtype``, ``scales = (k_scale, v_scale)``)
+    int8 or fp8 caches ("i8" / "fp8", new rows in ``q_dtype``, ``scales = (k_scale, v_scale)``)
     return (out, k_cache, v_cache, k_scale, v_scale)."""
-    if kv_dtype == "i8":
+    if kv_dtype in ("i8", "fp8"):
         kc, vc, ks, vs = append_q8(k_cache, v_cache, scales[0], scales[1], k_new, v_new, q_dtype, lengths, layout)
         n = np.asarray(lengths).astype(np.int64) + 1
-        out = attend_variants(q, q_dtype, kc, vc, "i8", n, layout, num_q_heads, num_kv_heads, scales=(ks, vs),
+        out = attend_variants(q, q_dtype, kc, vc, kv_dtype, n, layout, num_q_heads, num_kv_heads, scales=(ks, vs),
                               **variants)
         return out, kc, vc, ks, vs
     if kind is None:

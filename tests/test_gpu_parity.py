@@ -382,22 +382,22 @@ def test_full_size_workload(g, name):
     assert torch.isfinite(out.float()).all()
 
 
-@pytest.mark.parametrize("kind", ["dense", "paged", "int8", "window"])
+@pytest.mark.parametrize("kind", ["dense", "paged", "int8", "fp8", "window"])
 def test_balanced_mode_matches_oracle(g, kind):
     """More (b, kv-head) items than CUs: the plan switches to the balanced mode
     (equal tile ranges per workgroup, cut on the device from the lengths, and a
     combine of the items cut between workgroups).  Shuffled ragged lengths
-    (including 0 and the full capacity) on dense, paged and int8 caches and
+    (including 0 and the full capacity) on dense, paged, int8 and fp8 caches and
     with a sliding window must match the oracle."""
     B, Hq, Hkv, D, S = 40, 32, 8, 128, 300
-    kv = "i8" if kind == "int8" else "bf16"
+    kv = {"int8": "i8", "fp8": "fp8"}.get(kind, "bf16")
     w = W.custom(B, Hq, Hkv, D, S, "BHSD", kv, "bf16", seed=91, stale="pm:1")
     L = torch.randint(0, S, (B,), generator=torch.Generator().manual_seed(92), dtype=torch.int32)
     L[5], L[17], L[30] = 0, S - 1, S - 1
-    desc = g.make_desc(B, Hq, Hkv, D, S, "BHSD", g.I8 if kind == "int8" else g.BF16, g.BF16)
+    desc = g.make_desc(B, Hq, Hkv, D, S, "BHSD", {"i8": g.I8, "fp8": g.FP8}.get(kv, g.BF16), g.BF16)
     assert g.get_plan(desc)["balanced"]
     say(f"balanced {kind}")
-    if kind == "int8":
+    if kv in ("i8", "fp8"):
         inp = W.make_q8(w, DEV, lengths=L)
         ref, rk, rv, rks, rvs = oracle.step_q8(np_of(inp["q"]), "bf16", np_of(inp["k_cache"]), np_of(inp["v_cache"]),
                                                np_of(inp["k_scale"]), np_of(inp["v_scale"]), np_of(inp["k_new"]),
@@ -405,8 +405,9 @@ def test_balanced_mode_matches_oracle(g, kind):
         out = g.step_q8(inp["q"], inp["k_cache"], inp["v_cache"], inp["k_scale"], inp["v_scale"], inp["k_new"],
                         inp["v_new"], inp["lengths"], layout="BHSD")
         torch.cuda.synchronize()
-        assert_close(out, ref, "bf16", "int8 step")
-        assert np_of(inp["k_cache"]).tobytes() == rk.tobytes() and np_of(inp["k_scale"]).tobytes() == rks.tobytes()
+        assert_close(out, ref, "bf16", f"{kind} step")
+        for name, want in (("k_cache", rk), ("v_cache", rv), ("k_scale", rks), ("v_scale", rvs)):
+            assert np_of(inp[name]).tobytes() == want.tobytes(), name
         return
     inp = W.make_inputs(w, DEV, lengths=L)
     if kind == "paged":
@@ -450,7 +451,7 @@ def test_balanced_mode_random_shapes(g, seed):
     B = int(rng.integers(256 // Hkv + 1, 256 // Hkv + 120))
     S = int(rng.integers(40, 1200))
     lay = str(rng.choice(["BHSD", "BSHD"]))
-    kv = "i8" if seed % 2 else "bf16"
+    kv = ("bf16", "i8", "fp8")[(seed // 3 + seed) % 3]
     mix = seed % 3
     if mix == 0:
         L = rng.integers(0, min(S, 48), B)
@@ -463,10 +464,10 @@ def test_balanced_mode_random_shapes(g, seed):
     L = torch.from_numpy(L.astype(np.int32))
     Hq = Hkv * G
     say(f"balanced random seed={seed}: B={B} Hq={Hq} Hkv={Hkv} S={S} {lay} {kv} mix={mix}")
-    desc = g.make_desc(B, Hq, Hkv, 128, S, lay, g.I8 if kv == "i8" else g.BF16, g.BF16)
+    desc = g.make_desc(B, Hq, Hkv, 128, S, lay, {"i8": g.I8, "fp8": g.FP8}.get(kv, g.BF16), g.BF16)
     assert g.get_plan(desc)["balanced"]
     w = W.custom(B, Hq, Hkv, 128, S, lay, kv, "bf16", seed=200 + seed, stale="pm:1")
-    if kv == "i8":
+    if kv in ("i8", "fp8"):
         inp = W.make_q8(w, DEV, lengths=L)
         ref, rk, rv, rks, rvs = oracle.step_q8(np_of(inp["q"]), "bf16", np_of(inp["k_cache"]), np_of(inp["v_cache"]),
                                                np_of(inp["k_scale"]), np_of(inp["v_scale"]), np_of(inp["k_new"]),
@@ -474,7 +475,7 @@ def test_balanced_mode_random_shapes(g, seed):
         out = g.step_q8(inp["q"], inp["k_cache"], inp["v_cache"], inp["k_scale"], inp["v_scale"], inp["k_new"],
                         inp["v_new"], inp["lengths"], layout=lay)
         torch.cuda.synchronize()
-        assert_close(out, ref, "bf16", "int8 step")
+        assert_close(out, ref, "bf16", f"{kv} step")
         for name, want in (("k_cache", rk), ("v_cache", rv), ("k_scale", rks), ("v_scale", rvs)):
             assert np_of(inp[name]).tobytes() == want.tobytes(), name
         return

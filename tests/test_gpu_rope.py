@@ -165,10 +165,13 @@ def test_rope_append_alone(g, mode):
                                   (2, 64, 1, 128, 400, "BHSD", "bf16", "half"),
                                   (3, 48, 2, 128, 300, "BSHD", "bf16", "interleaved")],
                          ids=["G4-bf16-half", "G8-BSHD-interleaved", "generic-f32", "G64-half", "G24-BSHD-interleaved"])
-def test_rope_step_int8(g, case):
+@pytest.mark.parametrize("kv", ["i8", "fp8"])
+def test_rope_step_quantized(g, case, kv):
     B, Hq, Hkv, D, S, layout, qo, mode = case
-    say(f"rope int8 {case}")
-    w = W.custom(B, Hq, Hkv, D, S, layout, "i8", qo, seed=B * 13 + D, stale="pm:1")
+    if kv == "fp8" and (D != 128 or qo != "bf16"):
+        pytest.skip("fp8 caches are served for D = 128 with bf16 q and out only (the plan refuses the rest)")
+    say(f"rope {kv} {case}")
+    w = W.custom(B, Hq, Hkv, D, S, layout, kv, qo, seed=B * 13 + D, stale="pm:1")
     L = torch.randint(0, S, (B,), generator=torch.Generator().manual_seed(S), dtype=torch.int32)
     L[0] = S - 1
     inp = W.make_q8(w, DEV, lengths=L)

@@ -149,21 +149,25 @@ def test_variants_on_mapped_caches(g, case, ns):
     assert np_of(m["v_cache"]).tobytes() == rv.tobytes()
 
 
+@pytest.mark.parametrize("kv", ["i8", "fp8"])
 @pytest.mark.parametrize("vname", ["winpre", "all", "cap", "sink"])
 @pytest.mark.parametrize("ns", [0, 3])
 @pytest.mark.parametrize("shape", [(3, 32, 8), (2, 64, 1)], ids=["G4", "G64"])
-def test_variants_on_int8_caches(g, vname, ns, shape):
+def test_variants_on_quantized_caches(g, vname, ns, shape, kv):
+    """Int8 and fp8 (E4M3) caches with per-row scales under every softmax
+    variant: outputs within the bf16 tolerance, appended codes and scales
+    byte-exact."""
     B, Hq, Hkv = shape
     D, S, layout = 128, 800, "BHSD"
     v = dict(VARIANTS)[vname]
-    say(f"variants int8 {vname} splits={ns} shape={shape}")
-    w = W.custom(B, Hq, Hkv, D, S, layout, "i8", "bf16", seed=77, stale="pm:1")
+    say(f"variants {kv} {vname} splits={ns} shape={shape}")
+    w = W.custom(B, Hq, Hkv, D, S, layout, kv, "bf16", seed=77, stale="pm:1")
     L = _lengths(B, S, 5)
     inp = W.make_q8(w, DEV, lengths=L)
     sm, okw = _softmax(g, v, B, Hq, 21)
     ref, rk, rv, rks, rvs = oracle.step_variants(np_of(inp["q"]), "bf16", np_of(inp["k_cache"]),
                                                  np_of(inp["v_cache"]), np_of(inp["k_new"]), np_of(inp["v_new"]),
-                                                 "i8", L.numpy(), layout, Hq, Hkv,
+                                                 kv, L.numpy(), layout, Hq, Hkv,
                                                  scales=(np_of(inp["k_scale"]), np_of(inp["v_scale"])), **okw)
     out = g.step_ex(inp["q"], inp["k_cache"], inp["v_cache"], inp["k_new"], inp["v_new"], inp["lengths"],
                     layout=layout, k_scale=inp["k_scale"], v_scale=inp["v_scale"], softmax=sm, num_splits=ns)
