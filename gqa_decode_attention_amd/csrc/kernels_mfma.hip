@@ -90,6 +90,139 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
+// One 32-slot tile for the wave's 16 query heads (see the kernel comment
+// below): scores from the K tile in LDS, masking of the slots outside
+// [t_begin, t_end) (and the window's unattended rows), the online softmax
+// update of m, l and O, and the V sum from the V tile in LDS.  Tile slot i is
+// virtual slot t0 + i.
+template <bool VAR>
+__device__ __forceinline__ void all_tile(const AttnArgs& a, const uint16_t* K, const uint16_t* V,
+                                         const u32x4 (&qf)[4], int t0, int t_begin, int t_end,
+                                         const SeqView& view, float& m, float& l, f32x4 (&O)[8]) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane >> 4;
+  const int c = lane & 15;
+  auto phys = [&](int t) { return VAR ? phys_slot(view, t) : t; };
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const u32x4 a0 = *reinterpret_cast<const u32x4*>(&K[c * kPitch + 32 * kk + 8 * r]);
+    const u32x4 a1 = *reinterpret_cast<const u32x4*>(&K[(16 + c) * kPitch + 32 * kk + 8 * r]);
+    s0 = mfma_16x16x32(a0, qf[kk], s0);
+    s1 = mfma_16x16x32(a1, qf[kk], s1);
+  }
+  // Raw scores; the scale log2(e)/sqrt(D) is positive, so the maximum is
+  // taken on raw scores and the scale is folded into the exponent's fma.
+  float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+  if constexpr (VAR) {
+    if (a.cap_T > 0.f) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sc[i] = cap_score(sc[i], a.cap_T, a.cap_invT);
+    }
+    if (a.window > 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (unattended(view, phys(t0 + 4 * r + i))) sc[i] = kNegInfM;
+        if (unattended(view, phys(t0 + 16 + 4 * r + i))) sc[4 + i] = kNegInfM;
+      }
+    }
+  }
+  // A piece's first (paged) or last, partial tile: a real (uniform) branch,
+  // so whole tiles run no per-row compares.
+  if (__builtin_expect(__builtin_amdgcn_readfirstlane(t0 + kTileT > t_end || t0 < t_begin), 0)) {
+    const int valid = t_end - t0;
+    const int lo = t_begin - t0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (4 * r + i >= valid || 4 * r + i < lo) sc[i] = kNegInfM;
+      if (16 + 4 * r + i >= valid || 16 + 4 * r + i < lo) sc[4 + i] = kNegInfM;
+    }
+  }
+  float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+  mx = rows_max(mx);
+  const float mc = mx * a.scale_log2;
+  if (__any(mc > m + kRescaleSlack)) {  // some head's maximum jumped: move the reference
+    const float m_new = fmaxf(m, mc);
+    const float alpha = fast_exp2(m - m_new);  // 0 on the first tile
+    l *= alpha;
+    m = m_new;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float ai = __shfl(alpha, 4 * r + i);  // alpha of head 4r + i
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) O[nb][i] *= ai;
+    }
+  }
+  // With the sliding window a wave can meet tiles with no attended row before
+  // its first attended one (m still -inf): their weights are 0, not NaN.
+  const float nm = VAR && m == kNegInfM ? 0.f : -m;
+  float p[8], ps = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    p[i] = fast_exp2(fmaf(sc[i], a.scale_log2, nm));
+    ps += p[i];
+  }
+  l += ps;
+  // Each weight enters the V sum as bf16 hi = bf16(p) plus lo = bf16(p - hi)
+  // (about 16 significant bits, so the weighted sum keeps float32 accuracy):
+  // one MFMA per part, accumulating into the same float32 output.
+  const u32x4 pa = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                    pack_bf16x2(p[6], p[7])};
+  const u32x4 pl = {pack_bf16x2(p[0] - bf16_lo(pa[0]), p[1] - bf16_hi(pa[0])),
+                    pack_bf16x2(p[2] - bf16_lo(pa[1]), p[3] - bf16_hi(pa[1])),
+                    pack_bf16x2(p[4] - bf16_lo(pa[2]), p[5] - bf16_hi(pa[2])),
+                    pack_bf16x2(p[6] - bf16_lo(pa[3]), p[7] - bf16_hi(pa[3]))};
+  const int trow = 4 * r + (c >> 2);
+  const int tcol = 4 * (c & 3);
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) {
+    const s16x4 lo = lds_read_tr16(&V[trow * kPitch + 16 * nb + tcol]);
+    const s16x4 hi = lds_read_tr16(&V[(16 + trow) * kPitch + 16 * nb + tcol]);
+    const u32x4 vt = {(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
+                      (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
+                      (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
+                      (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
+    O[nb] = mfma_16x16x32(pl, vt, mfma_16x16x32(pa, vt, O[nb]));
+  }
+}
+
+// The end of a piece for the wave's 16 heads hw .. hw + 15 of item (b, h):
+// lane (r, c) holds m and l of head c and the sums of heads 4r .. 4r + 3
+// (O[nb][i] at column 16 nb + c).  A whole piece writes the output rows; a
+// cut one the partial rows pbase + g * pstride of its heads g (m, l, o).
+// `scaled`: the softmax has a sink or the smooth variant, or the window may
+// leave a head with no attended slot (finish_scale covers each).
+__device__ __forceinline__ void all_finish(const AttnArgs& a, int b, int h, int hw, bool whole, int64_t pbase,
+                                           int64_t pstride, float m, float l, const f32x4 (&O)[8], bool scaled) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane >> 4;
+  const int c = lane & 15;
+  const int G = a.G;
+  l = rows_sum(l);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hl = 4 * r + i;  // head within the wave
+    const float li = __shfl(l, hl);
+    const float mi = __shfl(m, hl);
+    if (hw + hl >= G) continue;
+    const int hq = h * G + hw + hl;
+    if (whole) {
+      const float inv = scaled ? finish_scale(a, hq, mi, li) : (li > 0.f ? 1.f / li : 0.f);
+      uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)b * a.Hq + hq) * kD;
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) o[16 * nb + c] = f32_to_bf16_rne(O[nb][i] * inv);
+    } else {
+      const int64_t pi = pbase + (int64_t)(hw + hl) * pstride;
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) a.part_o[pi * kD + 16 * nb + c] = O[nb][i];
+      if (c == 0) {
+        a.part_m[pi] = mi;
+        a.part_l[pi] = li;
+      }
+    }
+  }
+}
+
 
 template <bool PAGED, bool VAR, bool BUF>
 __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
@@ -304,92 +437,8 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
     }
   };
 
-  // One tile: compute on LDS buffer `buf`, then move the next tile (register
-  // set Rn) into the other buffer; Rl receives the tile after that.
   auto compute_tile = [&](int t0, int buf) {
-    const uint16_t* K = sk[buf];
-    const uint16_t* V = sv[buf];
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const u32x4 a0 = *reinterpret_cast<const u32x4*>(&K[c * kPitch + 32 * kk + 8 * r]);
-      const u32x4 a1 = *reinterpret_cast<const u32x4*>(&K[(16 + c) * kPitch + 32 * kk + 8 * r]);
-      s0 = mfma_16x16x32(a0, qf[kk], s0);
-      s1 = mfma_16x16x32(a1, qf[kk], s1);
-    }
-    // Raw scores; the scale log2(e)/sqrt(D) is positive, so the maximum is
-    // taken on raw scores and the scale is folded into the exponent's fma.
-    float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-    if constexpr (VAR) {
-      if (a.cap_T > 0.f) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) sc[i] = cap_score(sc[i], a.cap_T, a.cap_invT);
-      }
-      if (a.window > 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (unattended(view, phys(t0 + 4 * r + i))) sc[i] = kNegInfM;
-          if (unattended(view, phys(t0 + 16 + 4 * r + i))) sc[4 + i] = kNegInfM;
-        }
-      }
-    }
-    // The split's first (paged) or last, partial tile: a real (uniform) branch,
-    // so whole tiles run no per-row compares.
-    if (__builtin_expect(__builtin_amdgcn_readfirstlane(t0 + kTileT > t_end || t0 < t_begin), 0)) {
-      const int valid = t_end - t0;
-      const int lo = t_begin - t0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (4 * r + i >= valid || 4 * r + i < lo) sc[i] = kNegInfM;
-        if (16 + 4 * r + i >= valid || 16 + 4 * r + i < lo) sc[4 + i] = kNegInfM;
-      }
-    }
-    float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-    mx = rows_max(mx);
-    const float mc = mx * a.scale_log2;
-    if (__any(mc > m + kRescaleSlack)) {  // some head's maximum jumped: move the reference
-      const float m_new = fmaxf(m, mc);
-      const float alpha = fast_exp2(m - m_new);  // 0 on the first tile
-      l *= alpha;
-      m = m_new;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float ai = __shfl(alpha, 4 * r + i);  // alpha of head 4r + i
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) O[nb][i] *= ai;
-      }
-    }
-    // With the sliding window a wave can meet tiles with no attended row before
-    // its first attended one (m still -inf): their weights are 0, not NaN.
-    const float nm = VAR && m == kNegInfM ? 0.f : -m;
-    float p[8], ps = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      p[i] = fast_exp2(fmaf(sc[i], a.scale_log2, nm));
-      ps += p[i];
-    }
-    l += ps;
-    // Each weight enters the V sum as bf16 hi = bf16(p) plus lo = bf16(p - hi)
-    // (about 16 significant bits, so the weighted sum keeps float32 accuracy):
-    // one MFMA per part, accumulating into the same float32 output.
-    const u32x4 pa = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                      pack_bf16x2(p[6], p[7])};
-    const u32x4 pl = {pack_bf16x2(p[0] - bf16_lo(pa[0]), p[1] - bf16_hi(pa[0])),
-                      pack_bf16x2(p[2] - bf16_lo(pa[1]), p[3] - bf16_hi(pa[1])),
-                      pack_bf16x2(p[4] - bf16_lo(pa[2]), p[5] - bf16_hi(pa[2])),
-                      pack_bf16x2(p[6] - bf16_lo(pa[3]), p[7] - bf16_hi(pa[3]))};
-    const int trow = 4 * r + (c >> 2);
-    const int tcol = 4 * (c & 3);
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      const s16x4 lo = lds_read_tr16(&V[trow * kPitch + 16 * nb + tcol]);
-      const s16x4 hi = lds_read_tr16(&V[(16 + trow) * kPitch + 16 * nb + tcol]);
-      const u32x4 vt = {(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
-                        (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
-                        (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
-                        (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
-      O[nb] = mfma_16x16x32(pl, vt, mfma_16x16x32(pa, vt, O[nb]));
-    }
+    all_tile<VAR>(a, sk[buf], sv[buf], qf, t0, t_begin, t_end, view, m, l, O);
   };
   // Two register sets keep two tiles in flight: at the top of each iteration
   // tile t0 sits in LDS buffer `buf` and R1 is loading tile t0 + T.  Loads of
@@ -433,31 +482,8 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
     }
   }
 
-  // Denominator and max per head: lane (r, c) holds head c; the output rows of
-  // lane (r, c) are heads 4r + i.
-  l = rows_sum(l);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int hl = 4 * r + i;  // head within the wave
-    const float li = __shfl(l, hl);
-    const float mi = __shfl(m, hl);
-    if (hw + hl >= G) continue;
-    const int hq = h * G + hw + hl;
-    if (nact <= 1) {
-      const float inv = VAR || a.sink != nullptr || a.smooth ? finish_scale(a, hq, mi, li) : (li > 0.f ? 1.f / li : 0.f);
-      uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)b * a.Hq + hq) * kD;
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) o[16 * nb + c] = f32_to_bf16_rne(O[nb][i] * inv);
-    } else {
-      const int64_t pi = ((int64_t)b * a.Hq + hq) * a.nsplit + split;
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) a.part_o[pi * kD + 16 * nb + c] = O[nb][i];
-      if (c == 0) {
-        a.part_m[pi] = mi;
-        a.part_l[pi] = li;
-      }
-    }
-  }
+  all_finish(a, b, h, hw, nact <= 1, ((int64_t)b * a.Hq + (int64_t)h * G) * a.nsplit + split, a.nsplit, m, l, O,
+             VAR || a.sink != nullptr || a.smooth);
 }
 
 hipError_t launch_attend_mfma_all(const AttnArgs& a, const Plan& p, hipStream_t s) {
