@@ -138,10 +138,12 @@ __device__ __forceinline__ void all_tile(const AttnArgs& a, const uint16_t* K, c
       if (16 + 4 * r + i >= valid || 16 + 4 * r + i < lo) sc[4 + i] = kNegInfM;
     }
   }
-  float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-  mx = rows_max(mx);
-  const float mc = mx * a.scale_log2;
-  if (__any(mc > m + kRescaleSlack)) {  // some head's maximum jumped: move the reference
+  // The reference m of head c is the same in its four rows, so a lane can
+  // test its own scores against it: the head's maximum over the tile (the
+  // cross-row reduction) is needed only when some score jumped past it.
+  const float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+  if (__any(mx * a.scale_log2 > m + kRescaleSlack)) {  // some head's maximum jumped: move the reference
+    const float mc = rows_max(mx) * a.scale_log2;
     const float m_new = fmaxf(m, mc);
     const float alpha = fast_exp2(m - m_new);  // 0 on the first tile
     l *= alpha;
@@ -156,13 +158,10 @@ __device__ __forceinline__ void all_tile(const AttnArgs& a, const uint16_t* K, c
   // With the sliding window a wave can meet tiles with no attended row before
   // its first attended one (m still -inf): their weights are 0, not NaN.
   const float nm = VAR && m == kNegInfM ? 0.f : -m;
-  float p[8], ps = 0.f;
+  float p[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    p[i] = fast_exp2(fmaf(sc[i], a.scale_log2, nm));
-    ps += p[i];
-  }
-  l += ps;
+  for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(sc[i], a.scale_log2, nm));
+  l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
   // Each weight enters the V sum as bf16 hi = bf16(p) plus lo = bf16(p - hi)
   // (about 16 significant bits, so the weighted sum keeps float32 accuracy):
   // one MFMA per part, accumulating into the same float32 output.

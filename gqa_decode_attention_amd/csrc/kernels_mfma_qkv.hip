@@ -235,11 +235,13 @@ __device__ __forceinline__ void tile_math(State<HB>& st, const u32x4 (&qf)[HB][4
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (dead[i]) sc[i] = kNegInfQ;
-    // Softmax (per head 16 hb + c = this lane's column).
-    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    mx = rows_max(mx);
-    const float mc = mx * scale_log2;
-    if (__any(mc > st.m[hb] + kSlackQ)) {
+    // Softmax (per head 16 hb + c = this lane's column).  The reference m of
+    // head c is the same in its four rows, so a lane tests its own scores
+    // against it; the head's maximum over the tile (a cross-row reduction) is
+    // needed only when some score jumped past it.
+    const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    if (__any(mx * scale_log2 > st.m[hb] + kSlackQ)) {
+      const float mc = rows_max(mx) * scale_log2;
       const float m_new = fmaxf(st.m[hb], mc);
       const float alpha = fast_exp2(st.m[hb] - m_new);  // 0 on the first tile
       st.l[hb] *= alpha;
