@@ -16,6 +16,7 @@
 // o_i exp(m_i - M); the output is o / l.  Exponentials are base 2 with log2(e)
 // folded into the score scale.
 #include <mutex>
+#include <type_traits>
 
 #include "cache_map.h"
 #include "variants.h"
@@ -689,64 +690,68 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
   }
 }
 
-// Combine for head width 128 with a 16-byte aligned output.  One wave per
-// (b, query head); lane (half, q) = (lane / 32, lane % 32) accumulates output
-// elements 4q .. 4q + 3 over splits half, half + 2, ...  Every load is issued
-// before any result is needed (the sequence length, the split maxima and
-// denominators, the first eight partial rows), so the pass costs about one
-// memory round trip; partial rows of inactive splits are never used.
-template <int QO>
+// Combine for head width 128 with an aligned output.  One wave per
+// (b, query head); lane j merges output columns 2j and 2j + 1.  Every lane
+// reads the splits' maxima and denominators itself (the same values across the
+// wave), so the merge takes no cross-lane step.  NS > 0: the split count is at
+// most NS and the splits are unrolled, every load issued before any result is
+// needed (the sequence length, the (m, l) pairs, the lane's columns of each
+// partial row; indices past the split count repeat the last split), so the pass
+// costs about one memory round trip.  NS = 0: any split count, in loops.
+// Partial rows of inactive splits are never used (their m and l may be stale
+// NaN or Inf: they are selected away, not multiplied by zero).
+template <int QO, int NS>
 __global__ __launch_bounds__(256) void combine128_kernel(AttnArgs a) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
   const int lane = threadIdx.x & 63;
   const int64_t bh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // b * Hq + hq
   if (bh >= (int64_t)a.B * a.Hq) return;  // whole waves only; no workgroup barrier follows
   const int b = (int)(bh / a.Hq);
-  const int64_t pbase = bh * a.nsplit;
-  const int q = lane & 31;
-  const int half = lane >> 5;
-  const int len = a.lengths[b];
-  const float mraw = lane < a.nsplit ? a.part_m[pbase + lane] : kNegInf;
-  const float lraw = lane < a.nsplit ? a.part_l[pbase + lane] : 0.f;
-  const f32x4* po = reinterpret_cast<const f32x4*>(a.part_o + pbase * 128) + q;  // split i: po[32 i]
-  f32x4 o[4];
+  const int ns = a.nsplit;
+  const int64_t pbase = bh * ns;
+  const f32x2* po = reinterpret_cast<const f32x2*>(a.part_o) + lane;  // split i: po[(pbase + i) * 64]
+  float mr[NS > 0 ? NS : 1], lr[NS > 0 ? NS : 1];
+  f32x2 o[NS > 0 ? NS : 1];
+  if constexpr (NS > 0) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int i = half + 2 * j;
-    o[j] = i < a.nsplit ? po[32 * i] : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < NS; ++i) {
+      const int64_t pi = pbase + min(i, ns - 1);
+      mr[i] = a.part_m[pi];
+      lr[i] = a.part_l[pi];
+      o[i] = po[pi * 64];
+    }
   }
-  int n = len + a.len_offset;
+  int n = a.lengths[b] + a.len_offset;
   n = n < 0 ? 0 : (n > a.S ? a.S : n);
   if (a.window > 0) n = seq_view(a, b, n).nv;  // the splits cover the window's virtual slots
-  const int nact = n == 0 ? 0 : min(a.nsplit, (n + a.split_tokens - 1) / a.split_tokens);
+  const int nact = n == 0 ? 0 : min(ns, (n + a.split_tokens - 1) / a.split_tokens);
   if (nact <= 1) return;  // the attention pass wrote this sequence's output itself
-  const float M = wave_max(lane < nact ? mraw : kNegInf);
-  const float w = lane < nact ? fast_exp2(mraw - M) : 0.f;
-  const float L = wave_sum(lane < nact ? w * lraw : 0.f);  // stale l of inactive splits may be NaN or Inf
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float M = kNegInf, L = 0.f;
+  f32x2 acc = {0.f, 0.f};
+  if constexpr (NS > 0) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int i = half + 2 * j;
-    const float wi = __shfl(w, i);
-    if (i < nact) acc += wi * o[j];
-  }
-  for (int i0 = 8; i0 < nact; i0 += 2) {  // more than eight splits
-    const int i = i0 + half;
-    const float wi = __shfl(w, min(i, 63));
-    if (i < nact) acc += wi * po[32 * i];
-  }
+    for (int i = 0; i < NS; ++i) M = i < nact ? fmaxf(M, mr[i]) : M;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], 32);
-  if (half == 0) {
-    const float inv = a.sink != nullptr || a.smooth ? finish_scale(a, (int)(bh - (int64_t)b * a.Hq), M, L)
-                                                    : (L > 0.f ? 1.f / L : 0.f);
-    if (QO == GQA_F32) {
-      reinterpret_cast<f32x4*>(a.out)[bh * 32 + q] = acc * inv;
-    } else {
-      const uint32_t lo = (uint32_t)f32_to_bf16_rne(acc[0] * inv) | ((uint32_t)f32_to_bf16_rne(acc[1] * inv) << 16);
-      const uint32_t hi = (uint32_t)f32_to_bf16_rne(acc[2] * inv) | ((uint32_t)f32_to_bf16_rne(acc[3] * inv) << 16);
-      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-      reinterpret_cast<u32x2*>(a.out)[bh * 32 + q] = u32x2{lo, hi};
+    for (int i = 0; i < NS; ++i) {
+      const float w = i < nact ? fast_exp2(mr[i] - M) : 0.f;
+      L += i < nact ? w * lr[i] : 0.f;
+      acc += i < nact ? w * o[i] : f32x2{0.f, 0.f};
     }
+  } else {
+    for (int i = 0; i < nact; ++i) M = fmaxf(M, a.part_m[pbase + i]);
+    for (int i = 0; i < nact; ++i) {
+      const float w = fast_exp2(a.part_m[pbase + i] - M);
+      L += w * a.part_l[pbase + i];
+      acc += w * po[(pbase + i) * 64];
+    }
+  }
+  const float inv = a.sink != nullptr || a.smooth ? finish_scale(a, (int)(bh - (int64_t)b * a.Hq), M, L)
+                                                  : (L > 0.f ? 1.f / L : 0.f);
+  if (QO == GQA_F32) {
+    reinterpret_cast<f32x2*>(a.out)[bh * 64 + lane] = acc * inv;
+  } else {
+    reinterpret_cast<uint32_t*>(a.out)[bh * 64 + lane] =
+        (uint32_t)f32_to_bf16_rne(acc[0] * inv) | ((uint32_t)f32_to_bf16_rne(acc[1] * inv) << 16);
   }
 }
 
@@ -847,8 +852,16 @@ hipError_t launch_combine(const AttnArgs& a, const Plan& p, hipStream_t s) {
     fn = a.qo_dtype == GQA_F32 ? reinterpret_cast<const void*>(&combine_balanced_kernel<GQA_F32>)
                                : reinterpret_cast<const void*>(&combine_balanced_kernel<GQA_BF16>);
   } else if (fast) {
-    fn = a.qo_dtype == GQA_F32 ? reinterpret_cast<const void*>(&combine128_kernel<GQA_F32>)
-                               : reinterpret_cast<const void*>(&combine128_kernel<GQA_BF16>);
+    const bool f32 = a.qo_dtype == GQA_F32;
+    auto pick = [&](auto ns) -> const void* {
+      constexpr int NS = decltype(ns)::value;
+      return f32 ? reinterpret_cast<const void*>(&combine128_kernel<GQA_F32, NS>)
+                 : reinterpret_cast<const void*>(&combine128_kernel<GQA_BF16, NS>);
+    };
+    fn = a.nsplit <= 2   ? pick(std::integral_constant<int, 2>{})
+         : a.nsplit <= 4 ? pick(std::integral_constant<int, 4>{})
+         : a.nsplit <= 8 ? pick(std::integral_constant<int, 8>{})
+                         : pick(std::integral_constant<int, 0>{});
   } else {
     fn = a.qo_dtype == GQA_F32 ? reinterpret_cast<const void*>(&combine_kernel<GQA_F32>)
                                : reinterpret_cast<const void*>(&combine_kernel<GQA_BF16>);
