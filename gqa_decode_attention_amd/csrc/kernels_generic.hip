@@ -755,17 +755,20 @@ __global__ __launch_bounds__(256) void combine128_kernel(AttnArgs a) {
   }
 }
 
-// Balanced-mode combine (head width 128): one wave per (b, hq) row.  Item
-// (b, i) -- kv-heads [i hp, (i + 1) hp) of sequence b, so query heads
-// [i G hp, (i + 1) G hp) -- covers tiles [s, e) of the batch's tile sequence
-// (offsets written by the attention pass); workgroup k of `a.bal_units` held tiles
-// [k per, (k + 1) per).  An item inside one workgroup's range was written by
-// the attention pass; a cut one left a partial in every workgroup it touched:
-// row 2k + 1 of the first workgroup when the item starts inside its range,
-// row 2k + 0 otherwise.  The partials merge by the same log-sum-exp rule as
-// the split combine, any number of them (64 per round).
+// Balanced-mode combine (head width 128): one wave per (b, hq) row, lane j
+// merging output columns 2j and 2j + 1.  Item (b, i) -- kv-heads
+// [i hp, (i + 1) hp) of sequence b, so query heads [i G hp, (i + 1) G hp) --
+// covers tiles [s, e) of the batch's tile sequence (offsets written by the
+// attention pass); workgroup k of `a.bal_units` held tiles [k per, (k + 1) per).
+// An item inside one workgroup's range was written by the attention pass; a cut
+// one left a partial in every workgroup it touched: row 2k + 1 of the first
+// workgroup when the item starts inside its range, row 2k + 0 otherwise.  The
+// partials merge by the same log-sum-exp rule as the split combine, any number
+// of them: every lane reads the pieces' (m, l) itself (no cross-lane step), the
+// first eight pieces' loads issued together, the rest in loops.
 template <int QO>
 __global__ __launch_bounds__(256) void combine_balanced_kernel(AttnArgs a) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
   const int lane = threadIdx.x & 63;
   const int64_t bh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // b * Hq + hq
   if (bh >= (int64_t)a.B * a.Hq) return;  // whole waves only; no workgroup barrier follows
@@ -787,55 +790,40 @@ __global__ __launch_bounds__(256) void combine_balanced_kernel(AttnArgs a) {
   auto row = [&](int i) -> int64_t {  // partial row of the i-th piece (the first holds the item's first tile)
     return (2 * (int64_t)(k0 + i) + (i == 0 ? 1 : 0)) * GI + g;
   };
-  // One round of loads: m and l of the first 64 pieces (one per lane) and o
-  // of the first eight (half-waves take alternate pieces), then the rest.
-  const int q = lane & 31;
-  const int half = lane >> 5;
-  const float mraw = lane < np ? a.part_m[row(lane)] : kNegInf;
-  const float lraw = lane < np ? a.part_l[row(lane)] : 0.f;
-  f32x4 o[4];
+  const f32x2* po = reinterpret_cast<const f32x2*>(a.part_o) + lane;  // row r: po[r * 64]
+  constexpr int U = 8;
+  float mr[U], lr[U];
+  f32x2 o[U];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int i = half + 2 * j;
-    o[j] = i < np ? reinterpret_cast<const f32x4*>(a.part_o + row(i) * 128)[q] : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < U; ++i) {
+    const int64_t r = row(min(i, np - 1));
+    mr[i] = a.part_m[r];
+    lr[i] = a.part_l[r];
+    o[i] = po[r * 64];
   }
-  float M = wave_max(mraw);
-  for (int i0 = 64; i0 < np; i0 += 64) {
-    const int i = i0 + lane;
-    M = fmaxf(M, wave_max(i < np ? a.part_m[row(i)] : kNegInf));
-  }
-  float w = lane < np ? fast_exp2(mraw - M) : 0.f;
-  float L = wave_sum(w * lraw);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float M = kNegInf, L = 0.f;
+  f32x2 acc = {0.f, 0.f};
 #pragma unroll
-  for (int j = 0; j < 4; ++j) acc += __shfl(w, half + 2 * j) * o[j];
-  // Pieces past the eighth.  Every loop below is uniform over the wave, so all
-  // lanes take part in each cross-lane read of the weights.
-  for (int i0 = 0; i0 < np; i0 += 64) {
-    if (i0 > 0) {
-      const int i = i0 + lane;
-      w = i < np ? fast_exp2(a.part_m[row(i)] - M) : 0.f;
-      L += wave_sum(i < np ? w * a.part_l[row(i)] : 0.f);
-    }
-    const int nr = min(64, np - i0);
-    for (int j0 = i0 == 0 ? 8 : 0; j0 < nr; j0 += 2) {
-      const int j = j0 + half;
-      const float wj = __shfl(w, min(j, 63));
-      if (j < nr) acc += wj * reinterpret_cast<const f32x4*>(a.part_o + row(i0 + j) * 128)[q];
-    }
-  }
+  for (int i = 0; i < U; ++i) M = i < np ? fmaxf(M, mr[i]) : M;
+  for (int i = U; i < np; ++i) M = fmaxf(M, a.part_m[row(i)]);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], 32);
-  if (half == 0) {
-    const float inv = a.sink != nullptr || a.smooth ? finish_scale(a, hq, M, L) : (L > 0.f ? 1.f / L : 0.f);
-    if (QO == GQA_F32) {
-      reinterpret_cast<f32x4*>(a.out)[bh * 32 + q] = acc * inv;
-    } else {
-      const uint32_t lo = (uint32_t)f32_to_bf16_rne(acc[0] * inv) | ((uint32_t)f32_to_bf16_rne(acc[1] * inv) << 16);
-      const uint32_t hi = (uint32_t)f32_to_bf16_rne(acc[2] * inv) | ((uint32_t)f32_to_bf16_rne(acc[3] * inv) << 16);
-      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-      reinterpret_cast<u32x2*>(a.out)[bh * 32 + q] = u32x2{lo, hi};
-    }
+  for (int i = 0; i < U; ++i) {
+    const float w = i < np ? fast_exp2(mr[i] - M) : 0.f;
+    L += i < np ? w * lr[i] : 0.f;
+    acc += i < np ? w * o[i] : f32x2{0.f, 0.f};
+  }
+  for (int i = U; i < np; ++i) {
+    const int64_t r = row(i);
+    const float w = fast_exp2(a.part_m[r] - M);
+    L += w * a.part_l[r];
+    acc += w * po[r * 64];
+  }
+  const float inv = a.sink != nullptr || a.smooth ? finish_scale(a, hq, M, L) : (L > 0.f ? 1.f / L : 0.f);
+  if (QO == GQA_F32) {
+    reinterpret_cast<f32x2*>(a.out)[bh * 64 + lane] = acc * inv;
+  } else {
+    reinterpret_cast<uint32_t*>(a.out)[bh * 64 + lane] =
+        (uint32_t)f32_to_bf16_rne(acc[0] * inv) | ((uint32_t)f32_to_bf16_rne(acc[1] * inv) << 16);
   }
 }
 
