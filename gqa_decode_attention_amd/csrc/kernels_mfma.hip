@@ -1,14 +1,14 @@
 // Matrix-core (MFMA) attention kernel of the GQA decode step for gfx950 for
 // large groups (16 < G <= 64), bf16 storage, head width 128.  (Groups of up to
-// 16 query heads, and int8 caches, run the kernel in kernels_mfma_qkv.hip.)
+// 16 query heads, and int8 and fp8 caches, run the kernel in kernels_mfma_qkv.hip.)
 //
 // What is computed is the JAX "Grouped-Query Decode Step" page's definition
 // (query head h reads cache head floor(h/G); s_j = q.K_j/sqrt(D) over the
 // valid slots; softmax; o = sum_j w_j V_j) with the step of the "KV cache
 // decode step" page (the new token's key/value are attended and appended at
-// slot lengths[b]).  The softmax is evaluated online over 16-slot tiles
+// slot lengths[b]).  The softmax is evaluated online over 32-slot tiles
 // (running maximum m, denominator l, unnormalised output o, rescaled by
-// 2^(m_old - m_new) when the maximum grows); splits of the token axis leave
+// 2^(m_old - m_new) when the maximum grows past a slack); splits of the token axis leave
 // (m, l, o) partials that the combine kernel merges.
 //
 // Fused step: the new token (slot lengths[b]) is not read from the cache; the

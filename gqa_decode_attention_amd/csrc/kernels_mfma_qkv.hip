@@ -1,27 +1,28 @@
 // Matrix-core attention kernel of the GQA decode step, head width 128, bf16
 // q/out: scores and the V sum on MFMA with K/V rows loaded straight into the
 // MFMA operands (no LDS staging).  Serves bf16 caches with up to 16 query
-// heads per kv-head, and int8 caches with per-row float32 scales (Huawei CANN
-// "aclnnMlaPrologV3WeightNz" page, dynamic-quantization formula: a cached
-// value reads as code * row scale) with up to 64.  What is computed is the JAX
-// "Grouped-Query Decode Step" page's definition over the dequantized rows, with
-// the online softmax over 16-slot tiles of the other matrix-core kernels.
+// heads per kv-head, and int8 or fp8 (E4M3) caches with per-row float32 scales
+// (Huawei CANN "aclnnMlaPrologV3WeightNz" page, dynamic-quantization formula: a
+// cached value reads as code * row scale) with up to 64.  What is computed is
+// the JAX "Grouped-Query Decode Step" page's definition over the dequantized
+// rows, with an online softmax over 16-slot tiles.
 //
 // One workgroup = NW waves = one (sequence, kv-head, head chunk, split); each
 // wave walks its own run of 16-slot tiles for HB blocks of 16 query heads:
 // HB = 1 (4 waves) up to 16 heads; HB = 2 (8 waves, 32 heads per chunk) for
-// int8 caches with more, where the widened codes of a tile then serve twice
-// as many heads.  Lane l = 16 r + c.  Per tile and head block:
+// int8 and fp8 caches with more, where the widened codes of a tile then serve
+// twice as many heads.  Lane l = 16 r + c.  Per tile and head block:
 //   scores  S(16 slots x 16 heads) = K(16 x 128) . Q^T as four
 //           v_mfma_f32_16x16x32_bf16: lane (r, c) supplies A-operand pieces of
 //           cache row t0 + c.  bf16 caches: bytes 16r + 64kk of the row for
-//           MFMA kk.  int8: two 16-byte loads (bytes 16r + 64j, j = 0, 1) give
-//           32 codes, widened exactly to bf16 (|code| <= 127); MFMA 2j + h
+//           MFMA kk.  int8 / fp8: two 16-byte loads (bytes 16r + 64j, j = 0,
+//           1) give 32 codes, widened exactly to bf16 (|code| <= 127; every
+//           E4M3 value is a bf16 value); MFMA 2j + h
 //           takes codes 64j + 16r + 8h .. +7, and the query operand holds the
 //           same head-width positions (the dot product does not care how the
 //           positions are dealt, only that both operands agree).  Lane (r, c)
-//           then holds the scores of slots 4r .. 4r + 3 for head c; int8 rows
-//           multiply them by their key scales.
+//           then holds the scores of slots 4r .. 4r + 3 for head c; 8-bit
+//           rows multiply them by their key scales.
 //   softmax per head c, as in the other kernels (lazy rescale, exp2 with the
 //           scale folded in).
 //   V sum   O^T(128 x 16 heads) += V^T(128 x 16 slots) . P'(16 slots x 16
@@ -30,11 +31,11 @@
 //           operand of MFMA e is element 8c + e of its four slots, twice (so
 //           MFMA e covers head-width positions e, 8 + e, ..., 120 + e), and
 //           the B operand is the lane's own four weights of head c (times the
-//           value scales of int8 rows) split into bf16 hi and lo parts, the
+//           value scales of 8-bit rows) split into bf16 hi and lo parts, the
 //           K axis holding each slot once with each part.  Lane (r, c)
 //           receives head c at positions 8(4r + i) + e: complete sums, no
 //           cross-lane reduction.
-// Scores are exact products (bf16 or small integers) summed in float32; each
+// Scores are exact products (bf16 values) summed in float32; each
 // weight reaches the V sum as hi + lo (about 16 significant bits) and the
 // products accumulate in float32, as does the denominator l.
 //
