@@ -33,10 +33,11 @@ constexpr float kNegInfM = -__builtin_inff();
 constexpr int kD = 128;
 
 // Lazy rescaling: a tile whose maximum exceeds the running reference m by at
-// most this much (log2 units) keeps m, so its weights reach at most 2^8; only a
-// larger jump moves m and rescales o and l.  o / l is the same softmax either
-// way, and partials carry their own reference m into the combine.
-constexpr float kRescaleSlack = 8.f;
+// most 8 (log2 units) keeps m, so its weights reach at most 2^8; only a larger
+// jump -- a weight above 2^8 -- moves m and rescales o and l.  o / l is the
+// same softmax either way, and partials carry their own reference m into the
+// combine.
+constexpr float kRescaleJump = 256.f;
 
 __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
@@ -90,98 +91,130 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
-// One 32-slot tile for the wave's 16 query heads (see the kernel comment
-// below): scores from the K tile in LDS, masking of the slots outside
-// [t_begin, t_end) (and the window's unattended rows), the online softmax
-// update of m, l and O, and the V sum from the V tile in LDS.  Tile slot i is
-// virtual slot t0 + i.
-template <bool VAR>
-__device__ __forceinline__ void all_tile(const AttnArgs& a, const uint16_t* K, const uint16_t* V,
+// One step of the tile loop for the wave's 16 query heads (see the kernel
+// comment below).  SCORES: the scores of the K tile in LDS (virtual slots t0
+// ..), masking of the slots outside [t_begin, t_end) (and the window's
+// unattended rows), and their weights, packed as bf16 hi / lo pairs into
+// (pa, pl) for the next step; the running reference m and the denominator l
+// follow.  VSUM: the V sum of the previous tile (V tile in LDS, its weights in
+// (pa, pl) from the step before) into O.  One step does both, so the matrix
+// cores run one tile's V sum while the vector ALU computes the next tile's
+// weights: those are computed against the current reference, and recomputed
+// only when some score jumped past it (O -- the V sum just issued included --
+// and l are then rescaled first).
+template <bool VAR, bool SCORES, bool VSUM>
+__device__ __forceinline__ void all_step(const AttnArgs& a, const uint16_t* K, const uint16_t* V,
                                          const u32x4 (&qf)[4], int t0, int t_begin, int t_end,
-                                         const SeqView& view, float& m, float& l, f32x4 (&O)[8]) {
+                                         const SeqView& view, float& m, float& l, f32x4 (&O)[8], u32x4& pa,
+                                         u32x4& pl) {
   const int lane = threadIdx.x & 63;
   const int r = lane >> 4;
   const int c = lane & 15;
-  auto phys = [&](int t) { return VAR ? phys_slot(view, t) : t; };
-  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  float sc[8];
+  if constexpr (SCORES) {
+    auto phys = [&](int t) { return VAR ? phys_slot(view, t) : t; };
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const u32x4 a0 = *reinterpret_cast<const u32x4*>(&K[c * kPitch + 32 * kk + 8 * r]);
-    const u32x4 a1 = *reinterpret_cast<const u32x4*>(&K[(16 + c) * kPitch + 32 * kk + 8 * r]);
-    s0 = mfma_16x16x32(a0, qf[kk], s0);
-    s1 = mfma_16x16x32(a1, qf[kk], s1);
-  }
-  // Raw scores; the scale log2(e)/sqrt(D) is positive, so the maximum is
-  // taken on raw scores and the scale is folded into the exponent's fma.
-  float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-  if constexpr (VAR) {
-    if (a.cap_T > 0.f) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sc[i] = cap_score(sc[i], a.cap_T, a.cap_invT);
+    for (int kk = 0; kk < 4; ++kk) {
+      const u32x4 a0 = *reinterpret_cast<const u32x4*>(&K[c * kPitch + 32 * kk + 8 * r]);
+      const u32x4 a1 = *reinterpret_cast<const u32x4*>(&K[(16 + c) * kPitch + 32 * kk + 8 * r]);
+      s0 = mfma_16x16x32(a0, qf[kk], s0);
+      s1 = mfma_16x16x32(a1, qf[kk], s1);
     }
-    if (a.window > 0) {
+    // Raw scores; the scale log2(e)/sqrt(D) is positive, so the maximum is
+    // taken on raw scores and the scale is folded into the exponent's fma.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sc[i] = s0[i];
+      sc[4 + i] = s1[i];
+    }
+    if constexpr (VAR) {
+      if (a.cap_T > 0.f) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sc[i] = cap_score(sc[i], a.cap_T, a.cap_invT);
+      }
+      if (a.window > 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (unattended(view, phys(t0 + 4 * r + i))) sc[i] = kNegInfM;
+          if (unattended(view, phys(t0 + 16 + 4 * r + i))) sc[4 + i] = kNegInfM;
+        }
+      }
+    }
+    // A piece's first (paged) or last, partial tile: a real (uniform) branch,
+    // so whole tiles run no per-row compares.
+    if (__builtin_expect(__builtin_amdgcn_readfirstlane(t0 + kTileT > t_end || t0 < t_begin), 0)) {
+      const int valid = t_end - t0;
+      const int lo = t_begin - t0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (unattended(view, phys(t0 + 4 * r + i))) sc[i] = kNegInfM;
-        if (unattended(view, phys(t0 + 16 + 4 * r + i))) sc[4 + i] = kNegInfM;
+        if (4 * r + i >= valid || 4 * r + i < lo) sc[i] = kNegInfM;
+        if (16 + 4 * r + i >= valid || 16 + 4 * r + i < lo) sc[4 + i] = kNegInfM;
       }
     }
   }
-  // A piece's first (paged) or last, partial tile: a real (uniform) branch,
-  // so whole tiles run no per-row compares.
-  if (__builtin_expect(__builtin_amdgcn_readfirstlane(t0 + kTileT > t_end || t0 < t_begin), 0)) {
-    const int valid = t_end - t0;
-    const int lo = t_begin - t0;
+  if constexpr (VSUM) {
+    // O(16 heads x 128) += P(16 x 32 slots) . V(32 x 128), each weight as its
+    // bf16 hi part then its lo part (about 16 significant bits, so the
+    // weighted sum keeps float32 accuracy), accumulating in float32.
+    const int trow = 4 * r + (c >> 2);
+    const int tcol = 4 * (c & 3);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (4 * r + i >= valid || 4 * r + i < lo) sc[i] = kNegInfM;
-      if (16 + 4 * r + i >= valid || 16 + 4 * r + i < lo) sc[4 + i] = kNegInfM;
+    for (int nb = 0; nb < 8; ++nb) {
+      const s16x4 lo = lds_read_tr16(&V[trow * kPitch + 16 * nb + tcol]);
+      const s16x4 hi = lds_read_tr16(&V[(16 + trow) * kPitch + 16 * nb + tcol]);
+      const u32x4 vt = {(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
+                        (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
+                        (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
+                        (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
+      O[nb] = mfma_16x16x32(pl, vt, mfma_16x16x32(pa, vt, O[nb]));
     }
   }
-  // The reference m of head c is the same in its four rows, so a lane can
-  // test its own scores against it: the head's maximum over the tile (the
-  // cross-row reduction) is needed only when some score jumped past it.
-  const float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-  if (__any(mx * a.scale_log2 > m + kRescaleSlack)) {  // some head's maximum jumped: move the reference
-    const float mc = rows_max(mx) * a.scale_log2;
-    const float m_new = fmaxf(m, mc);
-    const float alpha = fast_exp2(m - m_new);  // 0 on the first tile
-    l *= alpha;
-    m = m_new;
+  if constexpr (SCORES) {
+    // The weights against the current reference, and their largest value: a
+    // weight above 2^slack means some score jumped past the reference.  (With
+    // no reference yet, m = -inf, any attended score gives an infinite weight
+    // and so the rescale; masked scores give 0.)  Testing the weights rather
+    // than the scores keeps their computation ahead of the branch, next to
+    // the V sum's MFMAs.
+    auto weights = [&](float nm, u32x4& wa, u32x4& wl, float& pmax) {
+      float p[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float ai = __shfl(alpha, 4 * r + i);  // alpha of head 4r + i
+      for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(sc[i], a.scale_log2, nm));
+      pmax = fmaxf(fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3])), fmaxf(fmaxf(p[4], p[5]), fmaxf(p[6], p[7])));
+      wa = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                 pack_bf16x2(p[6], p[7])};
+      wl = u32x4{pack_bf16x2(p[0] - bf16_lo(wa[0]), p[1] - bf16_hi(wa[0])),
+                 pack_bf16x2(p[2] - bf16_lo(wa[1]), p[3] - bf16_hi(wa[1])),
+                 pack_bf16x2(p[4] - bf16_lo(wa[2]), p[5] - bf16_hi(wa[2])),
+                 pack_bf16x2(p[6] - bf16_lo(wa[3]), p[7] - bf16_hi(wa[3]))};
+      return ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    };
+    u32x4 wa, wl;
+    float pmax;
+    float ps = weights(m == kNegInfM ? __FLT_MAX__ : -m, wa, wl, pmax);
+    if (__any(pmax > kRescaleJump)) {  // some head's maximum jumped: move the reference
+      // The reference m of head c is the same in its four rows; the head's
+      // new maximum over the tile is a cross-row reduction.
+      const float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+      const float mc = rows_max(mx) * a.scale_log2;
+      const float m_new = fmaxf(m, mc);
+      const float alpha = fast_exp2(m - m_new);  // 0 on the first tile
+      l *= alpha;
+      m = m_new;
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) O[nb][i] *= ai;
+      for (int i = 0; i < 4; ++i) {
+        const float ai = __shfl(alpha, 4 * r + i);  // alpha of head 4r + i
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) O[nb][i] *= ai;
+      }
+      // With the sliding window a head can still have no attended row (m
+      // stays -inf): its weights are 0, not NaN.
+      ps = weights(m == kNegInfM ? 0.f : -m, wa, wl, pmax);
     }
-  }
-  // With the sliding window a wave can meet tiles with no attended row before
-  // its first attended one (m still -inf): their weights are 0, not NaN.
-  const float nm = VAR && m == kNegInfM ? 0.f : -m;
-  float p[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(sc[i], a.scale_log2, nm));
-  l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-  // Each weight enters the V sum as bf16 hi = bf16(p) plus lo = bf16(p - hi)
-  // (about 16 significant bits, so the weighted sum keeps float32 accuracy):
-  // one MFMA per part, accumulating into the same float32 output.
-  const u32x4 pa = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                    pack_bf16x2(p[6], p[7])};
-  const u32x4 pl = {pack_bf16x2(p[0] - bf16_lo(pa[0]), p[1] - bf16_hi(pa[0])),
-                    pack_bf16x2(p[2] - bf16_lo(pa[1]), p[3] - bf16_hi(pa[1])),
-                    pack_bf16x2(p[4] - bf16_lo(pa[2]), p[5] - bf16_hi(pa[2])),
-                    pack_bf16x2(p[6] - bf16_lo(pa[3]), p[7] - bf16_hi(pa[3]))};
-  const int trow = 4 * r + (c >> 2);
-  const int tcol = 4 * (c & 3);
-#pragma unroll
-  for (int nb = 0; nb < 8; ++nb) {
-    const s16x4 lo = lds_read_tr16(&V[trow * kPitch + 16 * nb + tcol]);
-    const s16x4 hi = lds_read_tr16(&V[(16 + trow) * kPitch + 16 * nb + tcol]);
-    const u32x4 vt = {(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
-                      (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
-                      (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
-                      (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
-    O[nb] = mfma_16x16x32(pl, vt, mfma_16x16x32(pa, vt, O[nb]));
+    l += ps;
+    pa = wa;
+    pl = wl;
   }
 }
 
@@ -226,8 +259,8 @@ __device__ __forceinline__ void all_finish(const AttnArgs& a, int b, int h, int 
 template <bool PAGED, bool VAR, bool BUF>
 __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
   static_assert(!BUF || (!PAGED && !VAR), "buffer loads serve dense rows without a window");
-  __shared__ __attribute__((aligned(16))) uint16_t sk[2][kTileT * kPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t sv[2][kTileT * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t sk[3][kTileT * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t sv[3][kTileT * kPitch];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -436,41 +469,62 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
     }
   };
 
-  auto compute_tile = [&](int t0, int buf) {
-    all_tile<VAR>(a, sk[buf], sv[buf], qf, t0, t_begin, t_end, view, m, l, O);
-  };
-  // Two register sets keep two tiles in flight: at the top of each iteration
-  // tile t0 sits in LDS buffer `buf` and R1 is loading tile t0 + T.  Loads of
-  // tiles past the end clamp to the last valid row (cache hits, never used), so
-  // every path issues the same loads, the loop has one exit, and each LDS write
-  // waits only for its own tile's loads.
+  // The loop runs one tile behind on the V sum: iteration t issues the V sum
+  // of tile t (LDS buffer t mod 3) with the scores and weights of tile t + 1
+  // (buffer t + 1 mod 3), writes tile t + 2 to buffer t + 2 mod 3 and starts
+  // the loads of tile t + 3.  Two register sets keep two tiles in flight
+  // (tile k in set k mod 2).  Loads of tiles past the end clamp to the last
+  // valid row (cache hits, never used), so every path issues the same loads,
+  // the loop has one exit, and each LDS write waits only for its own tile's
+  // loads.
+  u32x4 pa = {0u, 0u, 0u, 0u}, pl = {0u, 0u, 0u, 0u};  // the weights of the tile whose V sum is next
   if (t_begin < t_end) {
     const int ntile = (t_end - tv + kTileT - 1) / kTileT;
+    auto next3 = [](int x) { return x == 2 ? 0 : x + 1; };
     Regs R0, R1;
     gload(tv, R0, entries(tv));
     gload(tv + kTileT, R1, entries(tv + kTileT));
-    Ent e2 = entries(tv + 2 * kTileT), e3 = entries(tv + 3 * kTileT);
+    const Ent e2 = entries(tv + 2 * kTileT);
+    Ent e3 = entries(tv + 3 * kTileT);
     swrite(tv, 0, R0);
     __syncthreads();
-    int buf = 0;
-    int t0 = tv;
-    for (int it = 0; it < ntile / 2; ++it) {
-      const Ent n2 = entries(t0 + 4 * kTileT), n3 = entries(t0 + 5 * kTileT);
-      gload(t0 + 2 * kTileT, R0, e2);
-      compute_tile(t0, buf);
-      swrite(t0 + kTileT, buf ^ 1, R1);
-      __syncthreads();
-      buf ^= 1;
-      gload(t0 + 3 * kTileT, R1, e3);
-      compute_tile(t0 + kTileT, buf);
-      swrite(t0 + 2 * kTileT, buf ^ 1, R0);
-      __syncthreads();
-      buf ^= 1;
-      e2 = n2;
-      e3 = n3;
-      t0 += 2 * kTileT;
+    gload(tv + 2 * kTileT, R0, e2);
+    all_step<VAR, true, false>(a, sk[0], sv[0], qf, tv, t_begin, t_end, view, m, l, O, pa, pl);
+    swrite(tv + kTileT, 1, R1);
+    __syncthreads();
+    int t0 = tv;  // the tile whose V sum runs next
+    int bt = 0;   // its buffer
+    const int nit = ntile - 1;
+    for (int it = 0; it < nit / 2; ++it) {
+      {
+        const Ent en = entries(t0 + 4 * kTileT);
+        gload(t0 + 3 * kTileT, R1, e3);
+        e3 = en;
+        const int b1 = next3(bt), b2 = next3(b1);
+        all_step<VAR, true, true>(a, sk[b1], sv[bt], qf, t0 + kTileT, t_begin, t_end, view, m, l, O, pa, pl);
+        swrite(t0 + 2 * kTileT, b2, R0);
+        __syncthreads();
+        bt = b1;
+        t0 += kTileT;
+      }
+      {
+        const Ent en = entries(t0 + 4 * kTileT);
+        gload(t0 + 3 * kTileT, R0, e3);
+        e3 = en;
+        const int b1 = next3(bt), b2 = next3(b1);
+        all_step<VAR, true, true>(a, sk[b1], sv[bt], qf, t0 + kTileT, t_begin, t_end, view, m, l, O, pa, pl);
+        swrite(t0 + 2 * kTileT, b2, R1);
+        __syncthreads();
+        bt = b1;
+        t0 += kTileT;
+      }
     }
-    if (ntile & 1) compute_tile(t0, buf);
+    if (nit & 1) {  // the last tile's scores (it is in LDS already)
+      const int b1 = next3(bt);
+      all_step<VAR, true, true>(a, sk[b1], sv[bt], qf, t0 + kTileT, t_begin, t_end, view, m, l, O, pa, pl);
+      bt = b1;
+    }
+    all_step<VAR, false, true>(a, sk[bt], sv[bt], qf, t0, t_begin, t_end, view, m, l, O, pa, pl);
   }
 
   if (own_new && prow == 0) {  // the appended slot (skipped if the map names no valid row/block)
