@@ -4,7 +4,8 @@ Each case draws a kernel family (small-head, generic, register-operand,
 large-group, 8-bit caches, balanced mode), then a batch, group size, head
 width, capacity, layout, cache and q/out storage types, a forced split count
 (or the plan's), a step or an attend call, and ragged lengths that include a
-full sequence and (for B > 1) an empty one.  Only combinations the library
+full sequence and (for B > 1) one attending a single slot (a step from an
+empty cache, or an attend over one valid slot).  Only combinations the library
 serves are drawn (fp8 caches: head width 128, bf16 q/out, G <= 64), so the
 plan the library picks -- small, generic, register-operand or large-group
 kernel, split or balanced, with or without a combine pass -- must run and
