@@ -109,7 +109,7 @@ int32_t device_cus() {
 // matrix-core kernels cannot tile); `small` allows the small-head-width kernel
 // (plain calls: it applies no softmax variant).
 gqa_status_t make_plan(const gqa_decode_desc_t* d, Plan* p, int64_t span = 0, bool generic = false,
-                       bool small = true) {
+                       bool small = true, bool paged = false) {
   gqa_status_t st = check_desc(d);
   if (st != GQA_OK) return st;
   std::memset(p, 0, sizeof(*p));
@@ -141,8 +141,9 @@ gqa_status_t make_plan(const gqa_decode_desc_t* d, Plan* p, int64_t span = 0, bo
   p->head_chunks = p->kernel == GQA_KERNEL_GENERIC ? (int32_t)((G + kGenericHeadChunk - 1) / kGenericHeadChunk)
                    : p->kernel == GQA_KERNEL_MFMA_QK ? (int32_t)((G + qk_heads - 1) / qk_heads)
                                                      : 1;
-  // Four waves per workgroup for every kernel.  (For MFMA_QK, measured on
-  // MI355X: one 4-wave workgroup per CU streams faster than 8- or 12-wave
+  // Four waves per workgroup for every kernel but MFMA_QK on int8 / fp8
+  // caches with G > 16 (two 16-head blocks per wave).  (For MFMA_QK, measured
+  // on MI355X: one 4-wave workgroup per CU streams faster than 8- or 12-wave
   // workgroups or more, shorter splits -- fewer concurrent streams suit HBM.)
   p->block = p->kernel == GQA_KERNEL_MFMA_QK && G > 16 ? 512 : 256;
   // Caches (B, S, Hkv, D) hold a slot's kv-heads side by side: MFMA_QK then
@@ -197,6 +198,22 @@ gqa_status_t make_plan(const gqa_decode_desc_t* d, Plan* p, int64_t span = 0, bo
   // Less where a kv-head's slots are strided (BSHD): there how fast a tile
   // streams depends on the kv-head, which the charge does not see, and larger
   // charges measured slower.
+  // MFMA_ALL on dense or slot-indexed caches without splits (whole-item
+  // form): one 8-wave workgroup per (sequence, kv-head) item holding all G
+  // heads, no partials and no combine pass -- when the items alone fill the
+  // device (measured on MI355X: B = 256, G = 64 and 32, S = 2048, lengths in
+  // [1024, 2048]: 41 and 38 us against 49-57 and 49 us with splits; with 128
+  // items the split form stays ahead), or when one split is asked for.
+  if (p->kernel == GQA_KERNEL_MFMA_ALL && !paged && (d->num_splits == 1 || (d->num_splits == 0 && B * Hkv >= cus))) {
+    p->all8 = G > 32 ? 4 : 2;
+    p->block = 512;
+    p->grid = (int32_t)std::max<int64_t>(1, B * Hkv);
+    p->nsplit = 1;
+    p->split_tokens = (int32_t)S;
+    p->combine = 0;
+    p->workspace_bytes = 0;
+    p->off_m = p->off_l = 0;
+  }
   const bool i8 = quantized(d->kv_dtype);
   const int32_t cost = d->layout == GQA_LAYOUT_BHSD ? (i8 ? kBalancedCostI8 : kBalancedCostBf16)
                                                     : (i8 ? kBalancedCostI8Strided : kBalancedCostBf16Strided);
@@ -587,7 +604,10 @@ gqa_status_t plan_for(const gqa_decode_desc_t* d, const gqa_decode_opts_t* o, Pl
   const gqa_cache_map_t* m = o->map;
   if (m != nullptr && m->kind == GQA_MAP_PAGED && m->block_size > 0 && m->block_size % 16 != 0 &&
       is_matrix_core(p->kernel))
-    st = make_plan(d, p, walk_span(o->softmax), true, small);
+    return make_plan(d, p, walk_span(o->softmax), true, small);
+  // Paged caches: the large-group kernel's split form (tiles of 16-slot halves, one table entry each).
+  if (m != nullptr && m->kind == GQA_MAP_PAGED && p->all8)
+    return make_plan(d, p, walk_span(o->softmax), false, small, true);
   return st;
 }
 

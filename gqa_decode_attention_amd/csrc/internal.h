@@ -84,6 +84,8 @@ struct Plan {
   int32_t bal_cost;      // balanced mode: units charged per item besides its tiles
   int32_t hp;            // MFMA_QK: kv-heads per work item (see AttnArgs::hp)
   size_t off_pre;        // byte offset of the tile offsets inside the workspace
+  int32_t all8;          // MFMA_ALL whole-item form (8-wave workgroups, no split): 16-head blocks
+                         // per workgroup (2 or 4); 0 = the split form
 };
 
 // Which matrix-core kernels this build provides (the planner falls back to the

@@ -218,6 +218,71 @@ __device__ __forceinline__ void all_step(const AttnArgs& a, const uint16_t* K, c
   }
 }
 
+// The wave's query operands: head hw + c (zero past G) at head-width
+// positions 32kk + 8r .. 32kk + 8r + 7, rotated (and normalized) at rotary
+// row rp when `rope`.
+__device__ __forceinline__ void load_q_frags(const AttnArgs& a, int b, int h, int hw, bool rope, int rp,
+                                             u32x4 (&qf)[4]) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane >> 4;
+  const int c = lane & 15;
+  const int G = a.G;
+  const int64_t qrow = ((int64_t)b * a.Hq + (int64_t)h * G + hw + c) * kD;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    qf[kk] = (hw + c < G) ? load16(reinterpret_cast<const uint16_t*>(a.q) + qrow + 32 * kk + 8 * r)
+                          : u32x4{0, 0, 0, 0};
+  if (rope) {
+    float x[4][8];
+    const int pos[4] = {8 * r, 32 + 8 * r, 64 + 8 * r, 96 + 8 * r};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) widen16<GQA_BF16>(qf[kk], x[kk]);
+    rope_chunks(a, rp, pos, x, a.q_gain);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      qf[kk] = hw + c < G ? u32x4{pack_bf16x2(x[kk][0], x[kk][1]), pack_bf16x2(x[kk][2], x[kk][3]),
+                                  pack_bf16x2(x[kk][4], x[kk][5]), pack_bf16x2(x[kk][6], x[kk][7])}
+                          : u32x4{0, 0, 0, 0};
+  }
+}
+
+// The new key and value of kv-head row nrow (element offset), 16-byte piece
+// `piece` (elements 8 piece .. 8 piece + 7); with `rope` the key is rotated
+// (and normalized) at rotary row rp.  Each 16-lane group holds the whole key:
+// the half pairing's partner piece is loaded as well, and the norm reduces
+// over the group.
+__device__ __forceinline__ void load_new_kv(const AttnArgs& a, int64_t nrow, int piece, bool rope, int rp, u32x4& kn,
+                                            u32x4& vn) {
+  kn = load16(reinterpret_cast<const uint16_t*>(a.k_new) + nrow + 8 * piece);
+  vn = load16(reinterpret_cast<const uint16_t*>(a.v_new) + nrow + 8 * piece);
+  if (!rope) return;
+  const u32x4 kp = load16(reinterpret_cast<const uint16_t*>(a.k_new) + nrow + 8 * (piece ^ 8));
+  float x[8], xp[8], y[8];
+  widen16<GQA_BF16>(kn, x);
+  widen16<GQA_BF16>(kp, xp);
+  const float* cs = a.rope_cos + (int64_t)rp * 64;
+  const float* sn = a.rope_sin + (int64_t)rp * 64;
+  const bool half = a.rope_mode == GQA_ROPE_HALF;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int d = 8 * piece + e;
+    const bool first = half ? d < 64 : (e & 1) == 0;
+    const int j = half ? (d & 63) : (d >> 1);
+    y[e] = rope_rot(first, x[e], half ? xp[e] : x[e ^ 1], cs[j], sn[j]);
+  }
+  if (a.k_gain != nullptr) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += y[e] * y[e];
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) ss += __shfl_xor(ss, off);
+    const float rn = 1.0f / sqrtf(ss / 128.f + a.norm_eps);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = (y[e] * rn) * a.k_gain[8 * piece + e];
+  }
+  kn = u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])};
+}
+
 // The end of a piece for the wave's 16 heads hw .. hw + 15 of item (b, h):
 // lane (r, c) holds m and l of head c and the sums of heads 4r .. 4r + 3
 // (O[nb][i] at column 16 nb + c).  A whole piece writes the output rows; a
@@ -263,10 +328,7 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sv[3][kTileT * kPitch];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int r = lane >> 4;
-  const int c = lane & 15;
 
   int x = blockIdx.x;
   const int split = x % a.nsplit;
@@ -292,28 +354,12 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
   const bool own_new = a.k_new != nullptr && L >= t_begin && L < t_end;
 
   const int hw = wave * 16;  // first head of this wave
-  const int64_t qrow = ((int64_t)b * a.Hq + (int64_t)h * G + hw + c) * kD;
-  u32x4 qf[4];
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-    qf[kk] = (hw + c < G) ? load16(reinterpret_cast<const uint16_t*>(a.q) + qrow + 32 * kk + 8 * r)
-                          : u32x4{0, 0, 0, 0};
-  // Rotary step: q (positions 32kk + 8r of head c) and the new key are rotated
-  // (and normalized) here, at the new token's position.
+  // Rotary step: q and the new key are rotated (and normalized) here, at the
+  // new token's position.
   const bool rope = a.rope_cos != nullptr;
   const int rp = rope ? rope_row(a, b, L0) : 0;
-  if (rope) {
-    float x[4][8];
-    const int pos[4] = {8 * r, 32 + 8 * r, 64 + 8 * r, 96 + 8 * r};
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) widen16<GQA_BF16>(qf[kk], x[kk]);
-    rope_chunks(a, rp, pos, x, a.q_gain);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      qf[kk] = hw + c < G ? u32x4{pack_bf16x2(x[kk][0], x[kk][1]), pack_bf16x2(x[kk][2], x[kk][3]),
-                                  pack_bf16x2(x[kk][4], x[kk][5]), pack_bf16x2(x[kk][6], x[kk][7])}
-                          : u32x4{0, 0, 0, 0};
-  }
+  u32x4 qf[4];
+  load_q_frags(a, b, h, hw, rope, rp, qf);
 
   float m = kNegInfM, l = 0.f;
   f32x4 O[8];
@@ -347,39 +393,7 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
     u32x4 k[2], v[2];
   };
   u32x4 kn = {0u, 0u, 0u, 0u}, vn = {0u, 0u, 0u, 0u};  // the new key / value, piece `piece`
-  if (own_new) {
-    kn = load16(reinterpret_cast<const uint16_t*>(a.k_new) + nrow + 8 * piece);
-    vn = load16(reinterpret_cast<const uint16_t*>(a.v_new) + nrow + 8 * piece);
-    if (rope) {
-      // Each 16-lane group holds the whole key (piece = 8 elements); the half
-      // pairing's partner piece is loaded as well, the norm reduces over the group.
-      const u32x4 kp = load16(reinterpret_cast<const uint16_t*>(a.k_new) + nrow + 8 * (piece ^ 8));
-      float x[8], xp[8], y[8];
-      widen16<GQA_BF16>(kn, x);
-      widen16<GQA_BF16>(kp, xp);
-      const float* cs = a.rope_cos + (int64_t)rp * 64;
-      const float* sn = a.rope_sin + (int64_t)rp * 64;
-      const bool half = a.rope_mode == GQA_ROPE_HALF;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = 8 * piece + e;
-        const bool first = half ? d < 64 : (e & 1) == 0;
-        const int j = half ? (d & 63) : (d >> 1);
-        y[e] = rope_rot(first, x[e], half ? xp[e] : x[e ^ 1], cs[j], sn[j]);
-      }
-      if (a.k_gain != nullptr) {
-        float ss = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ss += y[e] * y[e];
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) ss += __shfl_xor(ss, off);
-        const float rn = 1.0f / sqrtf(ss / 128.f + a.norm_eps);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = (y[e] * rn) * a.k_gain[8 * piece + e];
-      }
-      kn = u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])};
-    }
-  }
+  if (own_new) load_new_kv(a, nrow, piece, rope, rp, kn, vn);
   // Paged: the table entries of a tile's two 16-row halves, loaded a tile pair
   // before the tile itself (clamped into the split, like the rows).
   struct Ent {
@@ -539,6 +553,246 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
              VAR || a.sink != nullptr || a.smooth);
 }
 
+// ---------------------------------------------------------------------------
+// Kernel MFMA_ALL, whole-item form: no split of the token axis, so no partials
+// and no combine pass; for batches whose (sequence, kv-head) items fill the
+// device, or when one split is asked for.
+//
+// One workgroup = 8 waves = one item and its G query heads in HB 16-head
+// blocks (HB = 2 for G <= 32, 4 above).  Wave w owns head block w mod HB and
+// sub-tile w / HB of each step: a step stages 8 / HB 32-slot sub-tiles of K
+// and V in LDS (two buffers, loaded by all 512 threads) and each wave runs the
+// tile math above on its sub-tile for its 16 heads (scores, weights as bf16
+// hi / lo pairs, V sum, online softmax with lazy rescale).  The sub-tile waves
+// of a head block end with one (m, l, o) each for their heads, merged through
+// LDS to the block's common maximum before the output rows are written.
+// ---------------------------------------------------------------------------
+constexpr int kMergePitch = 132;  // floats per merge row (16-byte aligned rows, spread over the banks)
+
+template <int HB, bool VAR, bool BUF>
+__global__ __launch_bounds__(512) void attend_mfma_all8_kernel(AttnArgs a) {
+  static_assert(HB == 2 || HB == 4, "two or four 16-head blocks per workgroup");
+  static_assert(!BUF || !VAR, "buffer loads serve dense rows without a window");
+  constexpr int SUB = 8 / HB;            // sub-tiles per step
+  constexpr int STEP = SUB * kTileT;     // slots per step
+  constexpr int HALF = STEP * kPitch;    // bf16 elements of one K (or V) buffer
+  // LDS: K buffers 0, 1 then V buffers 0, 1; after the loop the merge rows.
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * HALF];
+  static_assert(HB * SUB * 16 * kMergePitch * 4 + HB * SUB * 32 * 4 <= 4 * HALF * 2, "merge rows fit the tiles");
+  auto skb = [&](int buf) { return lds + buf * HALF; };
+  auto svb = [&](int buf) { return lds + (2 + buf) * HALF; };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane >> 4;
+  const int c = lane & 15;
+  const int hb = wave % HB;   // head block within the workgroup
+  const int sub = wave / HB;  // sub-tile of each step
+  const int G = a.G;
+
+  const int h = blockIdx.x % a.Hkv;
+  const int b = blockIdx.x / a.Hkv;
+
+  const int L0 = a.lengths[b];
+  int n = L0 + a.len_offset;
+  n = n < 0 ? 0 : (n > a.S ? a.S : n);
+  SeqView view{n, n, 0, 0, 0};
+  if constexpr (VAR) view = seq_view(a, b, n);
+  auto phys = [&](int t) { return VAR ? phys_slot(view, t) : t; };
+  const int nv = view.nv;
+  const int L = L0 - view.gap;
+  const int t_begin = 0, t_end = nv;  // the whole sequence
+  const bool own_new = a.k_new != nullptr && L >= 0 && L < nv;
+
+  const int hw = hb * 16;     // first head of this wave
+  const bool active = hw < G;  // (a head block past G holds no head)
+  const bool rope = a.rope_cos != nullptr;
+  const int rp = rope ? rope_row(a, b, L0) : 0;
+  u32x4 qf[4];
+  load_q_frags(a, b, h, hw, rope, rp, qf);
+
+  float m = kNegInfM, l = 0.f;
+  f32x4 O[8];
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) O[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int64_t base = row_head_offset(a, b, h);  // dense or slot-indexed row
+  const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.k_cache) + base;
+  const uint16_t* vb = reinterpret_cast<const uint16_t*>(a.v_cache) + base;
+  const int64_t rs = a.st;
+  const int64_t nrow = ((int64_t)b * a.Hkv + h) * kD;
+
+  // Cooperative step load: thread t moves 16 bytes (piece t & 15) of row
+  // t >> 4 of each sub-tile.  Rows past the last valid slot are clamped to it
+  // (buffer loads: read as zeros), so every load is unconditional.  The step
+  // holding the new token L takes it for its rows >= L when written to LDS
+  // (rows past L are masked and only need finite values); the new bits go to
+  // the cache slot after the loop.
+  const int prow = tid >> 4;
+  const int piece = tid & 15;
+  struct Regs {
+    u32x4 k[SUB], v[SUB];
+  };
+  u32x4 kn = {0u, 0u, 0u, 0u}, vn = {0u, 0u, 0u, 0u};
+  if (own_new) load_new_kv(a, nrow, piece, rope, rp, kn, vn);
+  const uint32_t rsb = (uint32_t)rs * 2u;  // bytes between consecutive slots
+  const uint32_t lane_off = (uint32_t)prow * rsb + 16u * (uint32_t)piece;
+  auto step_rsrc = [&](const uint16_t* p, int t0) {
+    // (readfirstlane: a resource the compiler cannot prove uniform turns each
+    // load into a loop over the lanes' resources)
+    const int rows = __builtin_amdgcn_readfirstlane(max(0, t_end - t0));
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p + (int64_t)t0 * rs), (short)0,
+                                             (int)((uint32_t)rows * rsb), 0x00020000);
+  };
+  auto gload = [&](int t0, Regs& R) {
+    if constexpr (BUF) {
+      const auto rk = step_rsrc(kb, t0), rv = step_rsrc(vb, t0);
+#pragma unroll
+      for (int q = 0; q < SUB; ++q) {
+        const int so = (int)((uint32_t)(q * kTileT) * rsb);
+        R.k[q] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)lane_off, so, 2);  // 2: non-temporal
+        R.v[q] = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)lane_off, so, 2);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < SUB; ++q) {
+        const int rc = min(t0 + prow + q * kTileT, t_end - 1);
+        const uint64_t off = (uint64_t)(uint32_t)phys(rc) * (uint32_t)rs + (uint32_t)(8 * piece);
+        R.k[q] = load_nt16(kb + off);
+        R.v[q] = load_nt16(vb + off);
+      }
+    }
+  };
+  auto swrite = [&](int t0, int buf, const Regs& R) {
+#pragma unroll
+    for (int q = 0; q < SUB; ++q) {
+      const int row = prow + q * kTileT;
+      *reinterpret_cast<u32x4*>(skb(buf) + row * kPitch + 8 * piece) = R.k[q];
+      *reinterpret_cast<u32x4*>(svb(buf) + row * kPitch + 8 * piece) = R.v[q];
+    }
+    if (own_new && t0 + STEP > L) {  // uniform: the step holding the new token
+#pragma unroll
+      for (int q = 0; q < SUB; ++q) {
+        const int row = prow + q * kTileT;
+        if (t0 + row >= L) {
+          *reinterpret_cast<u32x4*>(skb(buf) + row * kPitch + 8 * piece) = kn;
+          *reinterpret_cast<u32x4*>(svb(buf) + row * kPitch + 8 * piece) = vn;
+        }
+      }
+    }
+  };
+  // The wave's sub-tile of the step in buffer `buf`: scores and weights, then
+  // the V sum with those weights (a sub-tile past the end is skipped).
+  u32x4 pa = {0u, 0u, 0u, 0u}, pl = {0u, 0u, 0u, 0u};
+  auto tile = [&](int buf, int t0) {
+    const int ts = t0 + sub * kTileT;
+    if (active && ts < t_end) {
+      const uint16_t* K = skb(buf) + sub * kTileT * kPitch;
+      const uint16_t* V = svb(buf) + sub * kTileT * kPitch;
+      all_step<VAR, true, false>(a, K, V, qf, ts, t_begin, t_end, view, m, l, O, pa, pl);
+      all_step<VAR, false, true>(a, K, V, qf, ts, t_begin, t_end, view, m, l, O, pa, pl);
+    }
+  };
+
+  // Two register sets keep two steps in flight (step k in set k mod 2); steps
+  // run in pairs with one exit, so each LDS write waits only for its own loads.
+  if (t_begin < t_end) {
+    const int nstep = (t_end - t_begin + STEP - 1) / STEP;
+    Regs R0, R1;
+    gload(t_begin, R0);
+    gload(t_begin + STEP, R1);
+    swrite(t_begin, 0, R0);
+    __syncthreads();
+    gload(t_begin + 2 * STEP, R0);
+    int t0 = t_begin;
+    for (int it = 0; it < nstep / 2; ++it) {
+      tile(0, t0);
+      swrite(t0 + STEP, 1, R1);
+      __syncthreads();
+      gload(t0 + 3 * STEP, R1);
+      tile(1, t0 + STEP);
+      swrite(t0 + 2 * STEP, 0, R0);
+      __syncthreads();
+      gload(t0 + 4 * STEP, R0);
+      t0 += 2 * STEP;
+    }
+    if (nstep & 1) tile(0, t0);
+  }
+
+  if (own_new && prow == 0) {  // the appended slot (skipped if the map names no valid row)
+    const int64_t off = slot_offset_checked(a, b, h, L0);
+    if (off >= 0) {
+      store16(reinterpret_cast<uint16_t*>(a.k_cache_w) + off + 8 * piece, kn);
+      store16(reinterpret_cast<uint16_t*>(a.v_cache_w) + off + 8 * piece, vn);
+    }
+  }
+
+  // Merge of the SUB sub-tile waves of each head block.  Lane (r, c) holds m
+  // of head c, a part of its l, and the sums of heads 4r .. 4r + 3 (O[nb][i]
+  // at column 16 nb + c).  Each wave stores (m, l) of its heads, then its sums
+  // scaled to the block's common maximum; wave (hb, sub) then adds the SUB
+  // waves' sums for its share of the columns and writes those outputs.
+  __syncthreads();  // every wave is done with the tile buffers
+  float* mo = reinterpret_cast<float*>(lds);                          // [hb][sub][16 heads][kMergePitch]
+  float* ml = mo + HB * SUB * 16 * kMergePitch;                       // [hb][sub][m, l][16 heads]
+  auto mrow = [&](int s2, int what) { return ml + ((hb * SUB + s2) * 2 + what) * 16; };
+  const float lw = rows_sum(l);
+  if (r == 0) {
+    mrow(sub, 0)[c] = m;
+    mrow(sub, 1)[c] = lw;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hl = 4 * r + i;
+    float M = kNegInfM;
+#pragma unroll
+    for (int s2 = 0; s2 < SUB; ++s2) M = fmaxf(M, mrow(s2, 0)[hl]);
+    const float alpha = M == kNegInfM ? 0.f : fast_exp2(mrow(sub, 0)[hl] - M);
+    float* row = mo + ((hb * SUB + sub) * 16 + hl) * kMergePitch;
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) row[16 * nb + c] = O[nb][i] * alpha;
+  }
+  __syncthreads();
+  {
+    constexpr int CW = 128 / SUB;  // columns per wave
+    constexpr int CL = CW / 4;     // columns per lane (8 or 16)
+    const int hl = lane >> 2;
+    const int col = CW * sub + CL * (lane & 3);
+    float M = kNegInfM;
+#pragma unroll
+    for (int s2 = 0; s2 < SUB; ++s2) M = fmaxf(M, mrow(s2, 0)[hl]);
+    float lsum = 0.f;
+    float acc[CL];
+#pragma unroll
+    for (int e = 0; e < CL; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < SUB; ++s2) {
+      lsum += (M == kNegInfM ? 0.f : fast_exp2(mrow(s2, 0)[hl] - M)) * mrow(s2, 1)[hl];
+      const float* row = mo + ((hb * SUB + s2) * 16 + hl) * kMergePitch + col;
+#pragma unroll
+      for (int e4 = 0; e4 < CL; e4 += 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(row + e4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e4 + e] += x[e];
+      }
+    }
+    if (hw + hl < G) {
+      const int hq = h * G + hw + hl;
+      const bool scaled = VAR || a.sink != nullptr || a.smooth;
+      const float inv = scaled ? finish_scale(a, hq, M, lsum) : (lsum > 0.f ? 1.f / lsum : 0.f);
+      uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)b * a.Hq + hq) * kD + col;
+#pragma unroll
+      for (int e8 = 0; e8 < CL; e8 += 8)
+        store16(o + e8, u32x4{pack_bf16x2(acc[e8] * inv, acc[e8 + 1] * inv),
+                              pack_bf16x2(acc[e8 + 2] * inv, acc[e8 + 3] * inv),
+                              pack_bf16x2(acc[e8 + 4] * inv, acc[e8 + 5] * inv),
+                              pack_bf16x2(acc[e8 + 6] * inv, acc[e8 + 7] * inv)});
+    }
+  }
+}
+
 hipError_t launch_attend_mfma_all(const AttnArgs& a, const Plan& p, hipStream_t s) {
   if (a.D != kD || a.G > 64) return hipErrorInvalidValue;
   AttnArgs arg = a;
@@ -548,6 +802,23 @@ hipError_t launch_attend_mfma_all(const AttnArgs& a, const Plan& p, hipStream_t 
   if (a.kv_dtype != GQA_BF16 || a.qo_dtype != GQA_BF16) return hipErrorInvalidValue;
   // Buffer loads need every byte offset of a kv-head's rows in 31 bits.
   const bool buf = !paged && !var && (int64_t)a.S * a.st * 2 <= INT32_MAX;
+  if (p.all8) {
+    if (paged || p.all8 != (a.G > 32 ? 4 : 2) || p.nsplit != 1 || (int64_t)p.grid != (int64_t)a.B * a.Hkv)
+      return hipErrorInvalidValue;
+    // Buffer loads: every byte offset of a step's rows, up to two steps past
+    // the capacity, in 31 bits.
+    const bool wbuf = !var && (int64_t)(a.S + 256) * a.st * 2 <= INT32_MAX;
+    const void* wf;
+    if (p.all8 == 4)
+      wf = var ? reinterpret_cast<const void*>(&attend_mfma_all8_kernel<4, true, false>)
+           : wbuf ? reinterpret_cast<const void*>(&attend_mfma_all8_kernel<4, false, true>)
+                  : reinterpret_cast<const void*>(&attend_mfma_all8_kernel<4, false, false>);
+    else
+      wf = var ? reinterpret_cast<const void*>(&attend_mfma_all8_kernel<2, true, false>)
+           : wbuf ? reinterpret_cast<const void*>(&attend_mfma_all8_kernel<2, false, true>)
+                  : reinterpret_cast<const void*>(&attend_mfma_all8_kernel<2, false, false>);
+    return hipLaunchKernel(wf, dim3(p.grid), dim3(512), params, 0, s);
+  }
   const void* fn = paged ? (var ? reinterpret_cast<const void*>(&attend_mfma_all_kernel<true, true, false>)
                                 : reinterpret_cast<const void*>(&attend_mfma_all_kernel<true, false, false>))
                    : var ? reinterpret_cast<const void*>(&attend_mfma_all_kernel<false, true, false>)

@@ -284,6 +284,35 @@ def test_balanced_mode_only_where_items_outnumber_cus():
     assert not g.get_plan(desc(batch=300, num_q_heads=8, num_kv_heads=1, kv_dtype=g.F32, qo_dtype=g.F32))["balanced"]
 
 
+def test_large_group_whole_item_mode_plan():
+    """The large-group kernel (bf16, D = 128, 16 < G <= 64) runs without
+    splits -- one 512-thread workgroup per (sequence, kv-head) item, no
+    partials, no combine pass -- when the items fill the 256 CUs or when one
+    split is forced; otherwise it splits the token axis.  Paged caches keep
+    the split form (256-thread workgroups over its own split count)."""
+    def plan(**kw):
+        return g.get_plan(desc(head_dim=128, **kw))
+    for kw in (dict(batch=256, num_q_heads=64, num_kv_heads=1, capacity=2048),
+               dict(batch=300, num_q_heads=48, num_kv_heads=1, capacity=2048),
+               dict(batch=256, num_q_heads=24, num_kv_heads=1, capacity=900),
+               dict(batch=100, num_q_heads=144, num_kv_heads=3, capacity=900),
+               dict(batch=128, num_q_heads=64, num_kv_heads=1, num_splits=1),
+               dict(batch=3, num_q_heads=48, num_kv_heads=2, num_splits=1)):
+        p = plan(**kw)
+        grid = kw["batch"] * kw["num_kv_heads"]
+        assert (p["kernel"], p["num_splits"], p["block"], p["grid"], p["combine"], p["workspace_bytes"]) == \
+            ("mfma_all", 1, 512, grid, False, 0), (kw, p)
+    for kw in (dict(batch=128, num_q_heads=64, num_kv_heads=1, capacity=2048),   # 128 items: splits
+               dict(batch=128, num_q_heads=32, num_kv_heads=1, capacity=2048),
+               dict(batch=300, num_q_heads=64, num_kv_heads=1, num_splits=4)):
+        p = plan(**kw)
+        assert p["kernel"] == "mfma_all" and p["block"] == 256 and p["num_splits"] > 1 and p["combine"], (kw, p)
+    d = desc(batch=300, num_q_heads=64, num_kv_heads=1, capacity=2048)
+    m, keep = _map("paged", 600, [[2 * b, 2 * b + 1] for b in range(300)], block_size=1024, max_blocks=2)
+    p = g.get_plan_ex(d, _lib.OptsT(ctypes.pointer(m), None, None, None))
+    assert (p["kernel"], p["block"], p["grid"]) == ("mfma_all", 256, 300 * p["num_splits"]), p
+
+
 def test_head_parallel_items_on_bshd_caches():
     """The small-group matrix-core kernel takes four adjacent kv-heads per
     workgroup (one per wave, over the same slots) on BSHD caches whose kv-head

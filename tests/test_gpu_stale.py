@@ -11,7 +11,7 @@ row and gave it weight 0 would turn the output into NaN (0 * Inf, NaN * 0).
 Cases cover the small-group matrix-core kernel (split mode, both layouts,
 forced splits, attend, four kv-heads per workgroup on BSHD caches; int8
 caches with two 16-head blocks per wave), the
-large-group matrix-core kernel (G = 24 and 64), the generic vector kernel
+large-group matrix-core kernel (G = 24 and 64, split and whole-item mode), the generic vector kernel
 (float32 and bf16 storage, D = 64 and G = 80), the small-head-width kernel
 (D = 4 and 16), the balanced mode, and paged / slot-indexed caches, int8 and fp8 caches.  Int8 codes cannot hold NaN:
 there the refill puts NaN in the stale slots' scales and -127 in their codes;
@@ -64,6 +64,12 @@ CASES = {
     "mfma_qk_fp8_bshd_four_heads_splits3": (3, 32, 8, 128, 900, "BSHD", "fp8", "bf16", 3, None, 0, "mfma_qk", False),
     "mfma_qk_fp8_g64_two_blocks": (2, 64, 1, 128, 1100, "BHSD", "fp8", "bf16", 0, None, 0, "mfma_qk", False),
     "paged16_fp8": (3, 32, 8, 128, 800, "BHSD", "fp8", "bf16", 0, "paged", 16, "mfma_qk", False),
+    # the large-group kernel's whole-item mode (one split: no partials, sub-tile waves merged in LDS)
+    "mfma_all_whole_g64": (3, 64, 1, 128, 1500, "BHSD", "bf16", "bf16", 1, None, 0, "mfma_all", False),
+    "mfma_all_whole_g24_bshd": (2, 48, 2, 128, 700, "BSHD", "bf16", "bf16", 1, None, 0, "mfma_all", False),
+    "slots_mfma_all_whole": (3, 64, 1, 128, 700, "BSHD", "bf16", "bf16", 1, "slots", 0, "mfma_all", False),
+    "paged32_mfma_all_one_split": (2, 64, 1, 128, 900, "BSHD", "bf16", "bf16", 1, "paged", 32, "mfma_all", False),
+    "mfma_all_whole_four_blocks": (260, 64, 1, 128, 200, "BHSD", "bf16", "bf16", 0, None, 0, "mfma_all", False),
 }
 
 

@@ -92,6 +92,8 @@ def _lengths(B, S, seed):
 
 CASES = [(s, vn, ns) for s in SHAPES for vn, _ in VARIANTS for ns in (0, 3)
          if not (ns == 3 and vn in ("win1", "smooth"))]
+# The large-group kernel's whole-item mode (one split).
+CASES += [("all64", vn, 1) for vn, _ in VARIANTS]
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"{s}-{v}-n{n}" for s, v, n in CASES])
@@ -121,12 +123,12 @@ def test_variants_step_and_attend(g, case):
 
 MAPPED = [
     ("qk4", "paged", "winpre"), ("qk4", "paged", "all"), ("all64", "paged", "winpre"), ("all64", "paged", "all"),
-    ("qk16", "slots", "all"), ("gen32", "paged", "all"), ("qk4", "paged", "win1"),
+    ("qk16", "slots", "all"), ("gen32", "paged", "all"), ("qk4", "paged", "win1"), ("all64", "slots", "all"),
 ]
 
 
 @pytest.mark.parametrize("case", MAPPED, ids=["-".join(c) for c in MAPPED])
-@pytest.mark.parametrize("ns", [0, 4])
+@pytest.mark.parametrize("ns", [0, 1, 4])
 def test_variants_on_mapped_caches(g, case, ns):
     shape, kind, vname = case
     B, Hq, Hkv, D, S, layout, kv, qo = SHAPES[shape]
