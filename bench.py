@@ -207,6 +207,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama3_8b_layer")
     ap.add_argument("--num-splits", type=int, default=0, help="0 = the library's plan")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="run the workload with this many sequences instead of its own (lengths drawn the same "
+                         "way; the workload is then named <workload>_b<batch>)")
     ap.add_argument("--cache", default="dense",
                     help="dense (default), slots (slot-indexed rows), pagedN (pool of N-slot blocks in a "
                          "seeded random order) or pagedNseq (blocks in pool order)")
@@ -244,6 +247,8 @@ def main():
         return
     g.lib()
     w = W.WORKLOADS[args.workload]
+    if args.batch > 0 and args.batch != w.B:
+        w = W.Workload(**{**w.__dict__, "B": args.batch, "name": f"{w.name}_b{args.batch}"})
     dev = "cuda"
     q8 = args.kv in ("int8", "fp8")
     if q8:
