@@ -484,61 +484,75 @@ __global__ __launch_bounds__(256) void attend_mfma_all_kernel(AttnArgs a) {
   };
 
   // The loop runs one tile behind on the V sum: iteration t issues the V sum
-  // of tile t (LDS buffer t mod 3) with the scores and weights of tile t + 1
-  // (buffer t + 1 mod 3), writes tile t + 2 to buffer t + 2 mod 3 and starts
-  // the loads of tile t + 3.  Two register sets keep two tiles in flight
-  // (tile k in set k mod 2).  Loads of tiles past the end clamp to the last
+  // of the walk's tile t (LDS buffer t mod 3) with the scores and weights of
+  // its tile t + 1 (buffer t + 1 mod 3), writes tile t + 2 to buffer t + 2
+  // mod 3 and starts the loads of tile t + 3.  Two register sets keep two
+  // tiles in flight (tile k in set k mod 2).  Loads of tiles past the end clamp to the last
   // valid row (cache hits, never used), so every path issues the same loads,
   // the loop has one exit, and each LDS write waits only for its own tile's
   // loads.
   u32x4 pa = {0u, 0u, 0u, 0u}, pl = {0u, 0u, 0u, 0u};  // the weights of the tile whose V sum is next
   if (t_begin < t_end) {
     const int ntile = (t_end - tv + kTileT - 1) / kTileT;
+    // The split's tiles are walked from a start tile that moves with the item
+    // (tile k of the walk is tile (k + rot) mod ntile), so the workgroups of
+    // one XCD, which hold consecutive items whose regions are equally aligned,
+    // do not all read the same offset of their regions at the same time
+    // (measured on MI355X: 2-3 % on the large-group shapes).  Positions past
+    // the last tile are the clamped prefetches of the loop's end.
+    const int rot = __builtin_amdgcn_readfirstlane(((b * a.Hkv + h) >> 1) % ntile);
+    auto tp = [&](int k) {
+      if (k >= ntile) return tv + k * kTileT;
+      int x = k + rot;
+      x -= x >= ntile ? ntile : 0;
+      return tv + x * kTileT;
+    };
     auto next3 = [](int x) { return x == 2 ? 0 : x + 1; };
     Regs R0, R1;
-    gload(tv, R0, entries(tv));
-    gload(tv + kTileT, R1, entries(tv + kTileT));
-    const Ent e2 = entries(tv + 2 * kTileT);
-    Ent e3 = entries(tv + 3 * kTileT);
-    swrite(tv, 0, R0);
+    gload(tp(0), R0, entries(tp(0)));
+    gload(tp(1), R1, entries(tp(1)));
+    const Ent e2 = entries(tp(2));
+    Ent e3 = entries(tp(3));
+    swrite(tp(0), 0, R0);
     __syncthreads();
-    gload(tv + 2 * kTileT, R0, e2);
-    all_step<VAR, true, false>(a, sk[0], sv[0], qf, tv, t_begin, t_end, view, m, l, O, pa, pl);
-    swrite(tv + kTileT, 1, R1);
+    gload(tp(2), R0, e2);
+    all_step<VAR, true, false>(a, sk[0], sv[0], qf, tp(0), t_begin, t_end, view, m, l, O, pa, pl);
+    swrite(tp(1), 1, R1);
     __syncthreads();
-    int t0 = tv;  // the tile whose V sum runs next
-    int bt = 0;   // its buffer
+    int k = 0;   // the walk position of the tile whose V sum runs next
+    int bt = 0;  // its buffer
     const int nit = ntile - 1;
     for (int it = 0; it < nit / 2; ++it) {
       {
-        const Ent en = entries(t0 + 4 * kTileT);
-        gload(t0 + 3 * kTileT, R1, e3);
+        const Ent en = entries(tp(k + 4));
+        gload(tp(k + 3), R1, e3);
         e3 = en;
         const int b1 = next3(bt), b2 = next3(b1);
-        all_step<VAR, true, true>(a, sk[b1], sv[bt], qf, t0 + kTileT, t_begin, t_end, view, m, l, O, pa, pl);
-        swrite(t0 + 2 * kTileT, b2, R0);
+        all_step<VAR, true, true>(a, sk[b1], sv[bt], qf, tp(k + 1), t_begin, t_end, view, m, l, O, pa, pl);
+        swrite(tp(k + 2), b2, R0);
         __syncthreads();
         bt = b1;
-        t0 += kTileT;
+        ++k;
       }
       {
-        const Ent en = entries(t0 + 4 * kTileT);
-        gload(t0 + 3 * kTileT, R0, e3);
+        const Ent en = entries(tp(k + 4));
+        gload(tp(k + 3), R0, e3);
         e3 = en;
         const int b1 = next3(bt), b2 = next3(b1);
-        all_step<VAR, true, true>(a, sk[b1], sv[bt], qf, t0 + kTileT, t_begin, t_end, view, m, l, O, pa, pl);
-        swrite(t0 + 2 * kTileT, b2, R1);
+        all_step<VAR, true, true>(a, sk[b1], sv[bt], qf, tp(k + 1), t_begin, t_end, view, m, l, O, pa, pl);
+        swrite(tp(k + 2), b2, R1);
         __syncthreads();
         bt = b1;
-        t0 += kTileT;
+        ++k;
       }
     }
     if (nit & 1) {  // the last tile's scores (it is in LDS already)
       const int b1 = next3(bt);
-      all_step<VAR, true, true>(a, sk[b1], sv[bt], qf, t0 + kTileT, t_begin, t_end, view, m, l, O, pa, pl);
+      all_step<VAR, true, true>(a, sk[b1], sv[bt], qf, tp(k + 1), t_begin, t_end, view, m, l, O, pa, pl);
       bt = b1;
+      ++k;
     }
-    all_step<VAR, false, true>(a, sk[bt], sv[bt], qf, t0, t_begin, t_end, view, m, l, O, pa, pl);
+    all_step<VAR, false, true>(a, sk[bt], sv[bt], qf, tp(k), t_begin, t_end, view, m, l, O, pa, pl);
   }
 
   if (own_new && prow == 0) {  // the appended slot (skipped if the map names no valid row/block)
