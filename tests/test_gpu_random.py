@@ -1,7 +1,7 @@
 """GPU parity on seeded random shapes and options.
 
 Each case draws a kernel family (small-head, generic, register-operand,
-large-group, 8-bit caches, balanced mode), then a batch, group size, head
+large-group split or whole-item, 8-bit caches, balanced mode), then a batch, group size, head
 width, capacity, layout, cache and q/out storage types, a forced split count
 (or the plan's), a step or an attend call, and ragged lengths that include a
 full sequence and (for B > 1) one attending a single slot (a step from an
@@ -54,7 +54,7 @@ def draw(seed):
     """One case: a kernel family first (so every kernel and mode is drawn
     often), then the shape and options within it."""
     rng = np.random.default_rng(7000 + seed)
-    fam = ["small", "generic", "qk", "all", "q8", "balanced"][seed % 6]
+    fam = ["small", "generic", "qk", "all", "q8", "balanced", "whole"][seed % 7]
     Hkv = int(rng.choice([1, 2, 4, 8]))
     B = int(rng.integers(1, 5))
     S = int(rng.integers(1, 420))
@@ -72,11 +72,15 @@ def draw(seed):
     elif fam == "q8":                        # int8 or fp8 codes with row scales
         kv, qo, D, G = str(rng.choice(["i8", "fp8"])), "bf16", 128, int(rng.choice([1, 4, 8, 16, 24, 32, 64]))
         Hkv = min(Hkv, 2)
-    else:                                    # more (sequence, kv-head) items than CUs: balanced mode
+    elif fam == "balanced":                  # more (sequence, kv-head) items than CUs: balanced mode
         kv, qo, D, G = str(rng.choice(["bf16", "i8", "fp8"])), "bf16", 128, int(rng.choice([1, 2, 4, 8]))
         Hkv, B, S = 8, int(rng.integers(33, 48)), int(rng.integers(1, 120))
+    else:                                    # 16 < G <= 64 with items filling the CUs: whole-item form
+        kv, qo, D, G = "bf16", "bf16", 128, int(rng.choice([17, 24, 32, 40, 48, 64]))
+        Hkv = int(rng.choice([1, 2]))
+        B, S = int(rng.integers(256, 300)) // Hkv, int(rng.integers(1, 200))
     layout = str(rng.choice(["BHSD", "BSHD"]))
-    ns = 0 if fam == "balanced" else int(rng.choice([0, 0, 0, 1, 2, 3, 7]))
+    ns = 0 if fam in ("balanced", "whole") else int(rng.choice([0, 0, 0, 1, 2, 3, 7]))
     mode = str(rng.choice(["step", "attend"]))
     if mode == "step":
         L = rng.integers(0, S, B)             # pre-append counts in [0, S - 1]
@@ -92,7 +96,7 @@ def draw(seed):
                 ns=ns, mode=mode, L=torch.from_numpy(L.astype(np.int32)))
 
 
-CASES = [draw(s) for s in range(48)]
+CASES = [draw(s) for s in range(56)]
 
 
 def _id(c):
