@@ -671,7 +671,6 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
   const float L = wave_sum(wi * li);
   const int D = a.D;
   float O[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
   for (int i = 0; i < nact; ++i) {
     const float w = __shfl(wi, i);
     const float* po = a.part_o + (pbase + i) * D;
