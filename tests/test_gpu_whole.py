@@ -331,3 +331,30 @@ def test_large_group_full_size_split_mode(g):
     assert_close(out, ref, w.qo_dtype, "large_group split")
     assert np_of(inp["k_cache"]).tobytes() == rk.tobytes()
     assert np_of(inp["v_cache"]).tobytes() == rv.tobytes()
+
+
+@pytest.mark.parametrize("ns", [1, 0], ids=["whole-item", "split"])
+def test_rows_beyond_buffer_offsets(g, ns):
+    """Rows of a kv-head spanning more than 2^31 bytes (BSHD, 64 kv-heads of 128
+    bf16 elements: a 16 KB slot stride, capacity 131072) are loaded with
+    per-row addresses instead of buffer resources, in both forms of the
+    large-group kernel.  The output against the oracle on the first slots (the
+    only attended ones), the appended row and those slots byte-exact."""
+    B, Hkv, G, S, keep = 1, 64, 17, 131072, 320
+    Hq = Hkv * G
+    assert S * Hkv * 128 * 2 > 2 ** 31 - 1
+    w = W.custom(B, Hq, Hkv, 128, S, "BSHD", "bf16", "bf16", seed=61)
+    L = torch.tensor([300], dtype=torch.int32)
+    inp = W.make_inputs(w, DEV, lengths=L)
+    kc, vc = inp["k_cache"][:, :keep].contiguous(), inp["v_cache"][:, :keep].contiguous()
+    ref, rk, rv = oracle.step(np_of(inp["q"]), "bf16", np_of(kc), np_of(vc), np_of(inp["k_new"]), np_of(inp["v_new"]),
+                              "bf16", L.numpy(), "BSHD", Hq, Hkv)
+    plan = g.get_plan(g.desc_for(inp["q"], inp["k_cache"], "BSHD", ns))
+    say(f"large stride ns={ns}: plan {plan}")
+    assert plan["kernel"] == "mfma_all" and (plan["block"] == 512) == (ns == 1)
+    out = g.step(inp["q"], inp["k_cache"], inp["v_cache"], inp["k_new"], inp["v_new"], inp["lengths"], layout="BSHD",
+                 num_splits=ns)
+    torch.cuda.synchronize()
+    assert_close(out, ref, "bf16", "step")
+    assert np_of(inp["k_cache"][:, :keep].contiguous()).tobytes() == rk.tobytes()
+    assert np_of(inp["v_cache"][:, :keep].contiguous()).tobytes() == rv.tobytes()
