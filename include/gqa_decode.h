@@ -126,7 +126,9 @@ enum {
   GQA_KERNEL_MFMA_QK = 1,  /* bf16 caches with G <= 16, or int8 caches (bf16 q/out) with G <= 64;
                               D = 128: scores and V sum on MFMA, K/V rows loaded straight into
                               the MFMA operands                                                */
-  GQA_KERNEL_MFMA_ALL = 2, /* bf16, D = 128, 16 < G <= 64: scores and V sum on MFMA           */
+  GQA_KERNEL_MFMA_ALL = 2, /* bf16, D = 128, 16 < G <= 64: scores and V sum on MFMA; block 512:
+                              one workgroup per (b, kv-head) item, no split (dense or slot-indexed
+                              caches whose items fill the device, or one split asked for)        */
   GQA_KERNEL_SMALL = 3     /* f32 or bf16, D <= 16, capacity <= 512, no softmax variant and no
                               forced split: one wave per (sequence, query head)                 */
 };
@@ -251,7 +253,8 @@ typedef struct {
  * their meaning (capacity = slots per sequence); the workspace size and plan
  * are gqa_decode_workspace_size_ex / gqa_decode_get_plan_ex with the map (the
  * descriptor's own, unless the block size sends the call to the generic
- * kernel).  B == 0 validates and enqueues nothing. */
+ * kernel, or a paged map sends a large-group call planned without splits to
+ * the split form of its kernel).  B == 0 validates and enqueues nothing. */
 gqa_status_t gqa_decode_append_mapped(const gqa_decode_desc_t* desc, const gqa_cache_map_t* map, void* k_cache,
                                       void* v_cache, const void* k_new, const void* v_new,
                                       const int32_t* lengths, void* stream);
