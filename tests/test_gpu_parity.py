@@ -438,6 +438,40 @@ def test_balanced_mode_matches_oracle(g, kind):
     assert np_of(inp["k_cache"]).tobytes() == rk.tobytes() and np_of(inp["v_cache"]).tobytes() == rv.tobytes()
 
 
+@pytest.mark.parametrize("kv", ["bf16", "i8"])
+@pytest.mark.parametrize("layout", ["BHSD", "BSHD"])
+def test_balanced_mode_largest_batch(g, kv, layout):
+    """The largest batch the balanced mode takes (4096 sequences: 16 per
+    thread of its on-device scan), with empty and full sequences among them:
+    every output against the oracle, appended rows (codes and scales) byte
+    for byte."""
+    B, Hq, Hkv, S = 4096, 8, 1, 64
+    w = W.custom(B, Hq, Hkv, 128, S, layout, kv, "bf16", seed=4096, stale="pm:100" if kv == "bf16" else "none")
+    L = torch.randint(0, S, (B,), generator=torch.Generator().manual_seed(4097), dtype=torch.int32)
+    L[0], L[1], L[4095] = S - 1, 0, S - 1
+    desc = g.make_desc(B, Hq, Hkv, 128, S, layout, g.BF16 if kv == "bf16" else g.I8, g.BF16)
+    plan = g.get_plan(desc)
+    say(f"balanced largest batch {kv} {layout}: plan {plan}")
+    assert plan["balanced"] and plan["kernel"] == "mfma_qk"
+    if kv == "bf16":
+        inp = W.make_inputs(w, DEV, lengths=L)
+        ref, rk, rv = oracle_step(inp, w)
+        out = run_step(g, inp, w)
+        want = {"k_cache": rk, "v_cache": rv}
+    else:
+        inp = W.make_q8(w, DEV, lengths=L)
+        ref, rk, rv, rks, rvs = oracle.step_q8(np_of(inp["q"]), "bf16", np_of(inp["k_cache"]), np_of(inp["v_cache"]),
+                                               np_of(inp["k_scale"]), np_of(inp["v_scale"]), np_of(inp["k_new"]),
+                                               np_of(inp["v_new"]), L.numpy(), layout, Hq, Hkv)
+        out = g.step_q8(inp["q"], inp["k_cache"], inp["v_cache"], inp["k_scale"], inp["v_scale"], inp["k_new"],
+                        inp["v_new"], inp["lengths"], layout=layout)
+        want = {"k_cache": rk, "v_cache": rv, "k_scale": rks, "v_scale": rvs}
+    torch.cuda.synchronize()
+    assert_close(out, ref, "bf16", f"B={B} {kv} {layout}")
+    for name, expect in want.items():
+        assert np_of(inp[name]).tobytes() == expect.tobytes(), name
+
+
 @pytest.mark.parametrize("seed", range(6))
 def test_balanced_mode_random_shapes(g, seed):
     """Balanced mode on seeded random shapes: batch, group size, capacity,
