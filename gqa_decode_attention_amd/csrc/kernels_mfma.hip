@@ -8,8 +8,8 @@
 // decode step" page (the new token's key/value are attended and appended at
 // slot lengths[b]).  The softmax is evaluated online over 32-slot tiles
 // (running maximum m, denominator l, unnormalised output o, rescaled by
-// 2^(m_old - m_new) when the maximum grows past a slack); splits of the token axis leave
-// (m, l, o) partials that the combine kernel merges.
+// 2^(m_old - m_new) when the maximum grows past a slack); splits of the token
+// axis leave (m, l, o) partials that the combine kernel merges.
 //
 // Fused step: the new token (slot lengths[b]) is not read from the cache; the
 // workgroup whose split holds it substitutes k_new/v_new for that row, and
@@ -50,10 +50,11 @@ __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cas
 // ---------------------------------------------------------------------------
 // Kernel MFMA_ALL (16 < G <= 64): scores and the V sum both on MFMA.
 //
-// One workgroup = 4 waves = one (sequence, kv-head, split).  The workgroup
-// stages 32-slot K and V tiles in LDS (double-buffered, rows padded to 288
-// bytes to spread LDS banks); wave w owns query heads 16w .. 16w + 15 and
-// reads every tile from LDS.  Per tile and wave:
+// Split form: one workgroup = 4 waves = one (sequence, kv-head, split).  The
+// workgroup stages 32-slot K and V tiles in LDS (three buffers, rows padded to
+// 288 bytes to spread LDS banks); wave w owns query heads 16w .. 16w + 15 and
+// reads every tile from LDS.  (The whole-item form further below runs the same
+// tile math in 8-wave workgroups over whole items.)  Per tile and wave:
 //   scores  two 16-slot halves, S^T(16 slots x 16 heads) = K(16 x 128) . Q^T,
 //           four v_mfma_f32_16x16x32_bf16 each (A operand: 16-byte LDS reads of
 //           K rows; B operand: the wave's query heads).  Lane (r, c) holds slots
