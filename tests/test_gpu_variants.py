@@ -1,7 +1,8 @@
 """GPU parity for the softmax variants (CLIKA runtime "groupQueryAttention"
 API page: head sink, smooth softmax, softcap, sliding window with a kept
 prefix) on every attention kernel, dense and mapped caches, one split and
-several (the split combine applies the sink and walks the window's slots).
+several (the split combine applies the sink and walks the window's slots),
+and together with the rotary step in one call.
 
 Outputs against the float64 variant oracle within the dense tolerances (fp32
 2e-5, bf16 1e-2, abs + rel); the appended rows byte-exact.  Stale slots hold
@@ -215,3 +216,49 @@ def test_window_skips_the_middle_of_a_long_sequence(g):
     t_win, t_full = ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2])
     say(f"window step {t_win / 20 * 1e3:.1f} us, full step {t_full / 20 * 1e3:.1f} us")
     assert t_win < 0.25 * t_full
+
+
+# Rotary step and softmax variants in one call, on each kernel family that
+# takes both (the options combine in one gqa_decode_opts_t).  The reference
+# composes the two oracles: q and the new key rotated first (rope oracle), then
+# the variant softmax over the appended cache with the rotated query.
+COMBINED = [
+    # B, Hq, Hkv, S, layout, kv/qo, num_splits, map kind
+    (3, 32, 8, 700, "BHSD", "bf16", 0, None),     # G = 4, register-operand kernel (rotated copy of q)
+    (2, 64, 1, 900, "BSHD", "bf16", 0, None),     # G = 64, split form (rotation fused)
+    (260, 64, 1, 200, "BHSD", "bf16", 0, None),   # G = 64, whole-item form
+    (3, 48, 2, 500, "BSHD", "bf16", 1, "slots"),  # G = 24, whole-item form on slot-indexed rows
+    (3, 8, 2, 300, "BHSD", "f32", 3, None),       # D = 64 below: generic kernel
+]
+
+
+@pytest.mark.parametrize("case", COMBINED, ids=[f"B{c[0]}Hq{c[1]}Hkv{c[2]}{c[4]}-{c[5]}-n{c[6]}-{c[7]}" for c in COMBINED])
+def test_rotary_step_with_variants(g, case):
+    B, Hq, Hkv, S, layout, dt, ns, kind = case
+    D = 64 if dt == "f32" else 128
+    say(f"rope + variants {case}")
+    w = W.custom(B, Hq, Hkv, D, S, layout, dt, dt, seed=B + Hq + S, stale="pm:1000")
+    L = _lengths(B, S, S + 11)
+    inp = W.make_inputs(w, DEV, lengths=L)
+    cos, sin = W.rope_tables(S + 8, D, DEV)
+    rope = g.Rope(cos, sin, "half")
+    gen = torch.Generator().manual_seed(12)
+    sink = (torch.randn(Hq, generator=gen) * 2).to(DEV)
+    sm = g.Softmax(sink=sink, softcap=2.0, window=90, kept_prefix=16)
+    qr, kr = oracle.rotate_new(np_of(inp["q"]), dt, np_of(inp["k_new"]), dt, L.numpy(), cos.cpu().numpy(),
+                               sin.cpu().numpy(), "half")
+    kc, vc, table, okw = inp["k_cache"], inp["v_cache"], None, {}
+    if kind is not None:
+        m = W.make_mapped(inp, w, kind)
+        kc, vc, table = m["k_cache"], m["v_cache"], m["map"]
+        okw = dict(kind=kind, mapping=table.cpu().numpy(), bs=m.get("block_size"))
+    ref, rk, rv = oracle.step_variants(qr.astype(np.float32), "f32", np_of(kc), np_of(vc), kr, np_of(inp["v_new"]), dt,
+                                       L.numpy(), layout, Hq, Hkv, sink=sink.cpu().numpy(), softcap=2.0, window=90,
+                                       prefix=16, **okw)
+    out = g.step_ex(inp["q"], kc, vc, inp["k_new"], inp["v_new"], inp["lengths"], layout=layout, table=table,
+                    kind=kind, table_host=None if table is None else table.cpu(), rope=rope, softmax=sm,
+                    num_splits=ns)
+    torch.cuda.synchronize()
+    assert_close(out, ref, dt, "step")
+    assert np_of(kc).tobytes() == rk.tobytes()
+    assert np_of(vc).tobytes() == rv.tobytes()
