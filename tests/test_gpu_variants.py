@@ -262,3 +262,41 @@ def test_rotary_step_with_variants(g, case):
     assert_close(out, ref, dt, "step")
     assert np_of(kc).tobytes() == rk.tobytes()
     assert np_of(vc).tobytes() == rv.tobytes()
+
+
+@pytest.mark.parametrize("kv", ["i8", "fp8"])
+@pytest.mark.parametrize("shape", [(3, 32, 8, 700, "BHSD"), (2, 64, 1, 600, "BSHD")], ids=["G4", "G64"])
+def test_rotary_step_with_variants_on_quantized_caches(g, shape, kv):
+    """The same on int8 and fp8 caches with row scales: the rotated new key
+    (bf16) quantized into the cache, codes and scales byte-exact."""
+    B, Hq, Hkv, S, layout = shape
+    say(f"rope + variants {kv} {shape}")
+    w = W.custom(B, Hq, Hkv, 128, S, layout, kv, "bf16", seed=B + Hq + 5)
+    L = _lengths(B, S, S + 13)
+    inp = W.make_q8(w, DEV, lengths=L)
+    cos, sin = W.rope_tables(S + 8, 128, DEV)
+    rope = g.Rope(cos, sin, "interleaved")
+    gen = torch.Generator().manual_seed(14)
+    sink = (torch.randn(Hq, generator=gen) * 2).to(DEV)
+    sm = g.Softmax(sink=sink, softcap=2.0, window=90, kept_prefix=16)
+    # As the quantized rotary oracle composes it: q and the new key rotated in
+    # float32 (the key quantized from there, q used unrounded), the value exact.
+    cs, sn = cos.cpu().numpy(), sin.cpu().numpy()
+    q32 = oracle.decode(np_of(inp["q"]), "bf16").astype(np.float32)
+    k32 = oracle.decode(np_of(inp["k_new"]), "bf16").astype(np.float32)
+    qr, kr = np.empty_like(q32), np.empty_like(k32)
+    for b in range(B):
+        p = int(L[b])
+        qr[b] = oracle.rope_rotate(q32[b], cs[p], sn[p], "interleaved")
+        kr[b] = oracle.rope_rotate(k32[b], cs[p], sn[p], "interleaved")
+    vn = oracle.decode(np_of(inp["v_new"]), "bf16").astype(np.float32)
+    ref, rk, rv, rks, rvs = oracle.step_variants(qr, "f32", np_of(inp["k_cache"]), np_of(inp["v_cache"]), kr, vn, kv,
+                                                 L.numpy(), layout, Hq, Hkv,
+                                                 scales=(np_of(inp["k_scale"]), np_of(inp["v_scale"])),
+                                                 sink=sink.cpu().numpy(), softcap=2.0, window=90, prefix=16)
+    out = g.step_ex(inp["q"], inp["k_cache"], inp["v_cache"], inp["k_new"], inp["v_new"], inp["lengths"],
+                    layout=layout, k_scale=inp["k_scale"], v_scale=inp["v_scale"], rope=rope, softmax=sm)
+    torch.cuda.synchronize()
+    assert_close(out, ref, "bf16", "step")
+    for name, want in (("k_cache", rk), ("v_cache", rv), ("k_scale", rks), ("v_scale", rvs)):
+        assert np_of(inp[name]).tobytes() == want.tobytes(), name
